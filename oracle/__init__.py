@@ -1,0 +1,112 @@
+"""CPU oracle for segment-masked, non-causal softmax self-attention.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check
+and by the benchmark's CPU-baseline leg, never by the product path.  It shares
+no code with the HIP library.
+
+The arithmetic lives in ``attn_oracle.c`` (scalar fp64, plain definition of
+softmax(scale * Q K^T, masked by segment IDs) V -- vidax paper, section 2
+"3D RoPE, 3D VAEs, and flash attention" with its reference [2], and Appendix A,
+Table 4, group 2 for SegmentIds).  This wrapper only marshals numpy arrays.
+
+Every function here has pins in ``tests/test_oracle.py``; see the module
+docstring there for what pins what.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from .build import LIB_PATH, build_oracle
+
+_lib = None
+
+
+def _load(path: Optional[str] = None):
+    """Load (once) the oracle library; ``path`` swaps in another build of the
+    same source (the mutation tests use this to check that the pins bite)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    if path is None:
+        path = LIB_PATH
+        if not os.path.exists(path):
+            build_oracle()
+    lib = ctypes.CDLL(path)
+    f = lib.vdx_oracle_attn_fwd
+    f.restype = ctypes.c_int
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    f.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double,
+                  p, i64, p, p, p, ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def use_library(path: Optional[str]) -> None:
+    """Point the wrappers at another oracle build (None -> the default one)."""
+    global _lib
+    _lib = None
+    _load(path)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+             seg_q: Optional[np.ndarray], seg_kv: Optional[np.ndarray],
+             scale: float, rows: Optional[np.ndarray] = None,
+             n_threads: Optional[int] = None, want_probs: bool = False
+             ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
+    """fp64 attention on bf16 bit patterns.
+
+    q_bits/k_bits/v_bits: uint16 [B, S, H, D] (bf16 bits).
+    seg_q/seg_kv: int32 [B, S] or both None.
+    rows: optional int64 [n, 3] of (b, h, i); then out is [n, D] and lse [n];
+          else out is [B, S, H, D] and lse [B, H, S].
+    Returns (out fp64, lse fp64, probs fp64 or None).
+    """
+    lib = _load()
+    for a in (q_bits, k_bits, v_bits):
+        assert a.dtype == np.uint16 and a.ndim == 4
+    B, S, H, D = q_bits.shape
+    assert k_bits.shape == q_bits.shape and v_bits.shape == q_bits.shape
+    q_bits = np.ascontiguousarray(q_bits)
+    k_bits = np.ascontiguousarray(k_bits)
+    v_bits = np.ascontiguousarray(v_bits)
+    if (seg_q is None) != (seg_kv is None):
+        raise ValueError("seg_q and seg_kv must both be given or both be None")
+    if seg_q is not None:
+        seg_q = np.ascontiguousarray(seg_q, dtype=np.int32)
+        seg_kv = np.ascontiguousarray(seg_kv, dtype=np.int32)
+        assert seg_q.shape == (B, S) and seg_kv.shape == (B, S)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        out = np.zeros((n, D), dtype=np.float64)
+        lse = np.zeros((n,), dtype=np.float64)
+        n_prob_rows = n
+    else:
+        n = 0
+        out = np.zeros((B, S, H, D), dtype=np.float64)
+        lse = np.zeros((B, H, S), dtype=np.float64)
+        n_prob_rows = B * H * S
+    probs = np.zeros((n_prob_rows, S), dtype=np.float64) if want_probs else None
+    rc = lib.vdx_oracle_attn_fwd(
+        _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(seg_q), _ptr(seg_kv),
+        B, S, H, D, float(scale), _ptr(rows), n, _ptr(out), _ptr(lse), _ptr(probs),
+        int(n_threads if n_threads is not None else default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle returned {rc}")
+    return out, lse, probs

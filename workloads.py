@@ -1,0 +1,194 @@
+"""Seeded synthetic workloads for segment-masked video-DiT self-attention.
+
+This module only *generates inputs*: shapes, seeds, value distributions and
+per-token segment-ID layouts.  It contains none of the attention arithmetic,
+so both the CPU oracle (``oracle/``) and the HIP path may be fed from it.
+
+Provenance of the shapes (vidax paper, arXiv:2609.18077):
+  * the token volume is frames x h x w latent patches flattened into one
+    sequence that reaches tens of thousands of tokens (section 1,
+    "Spatiotemporal constraints in video generation");
+  * padding and packed clips are expressed as per-token SegmentIds instead of a
+    dense (B, H, Sq, Sk) mask (Appendix A, Table 4, group 2, HunyuanVideo-1.5
+    row);
+  * classifier-free guidance doubles the internal batch (section 4,
+    "Experimental setup").
+The latent grids, head counts and head dims below are synthetic stand-ins for
+the layers of Table 5's models; the pages print no activation statistics, so
+Q/K/V are drawn i.i.d. normal and rounded to bf16 (round-to-nearest-even).
+
+Generation recipe (fixed; the same bits go to the oracle and the GPU):
+  Q, K, V are drawn one after the other, each from its own
+  ``torch.Generator().manual_seed(seed_x)`` as float32 ``randn`` of shape
+  [B, S, H, D], multiplied by sigma, then cast to bfloat16.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+# A segment layout is a list of (start, stop, seg_id) runs covering [0, S).
+SegRuns = List[Tuple[int, int, int]]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    S: int
+    H: int
+    D: int
+    scale: float
+    seeds: Tuple[int, int, int]
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    # None -> no segment arrays (unmasked); otherwise the per-batch runs.
+    seg_runs: Optional[SegRuns] = None
+    note: str = ""
+
+    @property
+    def masked(self) -> bool:
+        return self.seg_runs is not None
+
+
+def _runs_cover(runs: SegRuns, S: int) -> bool:
+    pos = 0
+    for a, b, _ in runs:
+        if a != pos or b <= a:
+            return False
+        pos = b
+    return pos == S
+
+
+# --- the five workloads ------------------------------------------------------
+# tiny_ref: 4x16x16 patch grid, small enough for the full oracle in seconds.
+TINY_REF = Workload(
+    name="tiny_ref", B=1, S=1024, H=4, D=64, scale=1.0 / 8.0,
+    seeds=(1000, 1001, 1002), seg_runs=[(0, 1024, 1)],
+    note="4x16x16 patch grid, single segment passed as arrays")
+
+# 480p small-DiT layer: 21x30x52 latent patch grid (Wan2.1 1.3B at 832x480,
+# 81 frames is the page workload it stands for; Table 5).
+SMALL_DIT_480P = Workload(
+    name="dit480p_small", B=1, S=32760, H=12, D=128,
+    scale=1.0 / math.sqrt(128.0), seeds=(2000, 2001, 2002), seg_runs=None,
+    note="21x30x52 latent patch grid, no mask")
+
+# Joint video+text attention with padding (CogVideoX 5B at 720x480, 49 frames,
+# CFG batch 2): 13x30x45 video tokens + 226 text tokens, padded to 17,920.
+JOINT_VIDEO_TEXT = Workload(
+    name="joint_video_text_pad", B=2, S=17920, H=24, D=128,
+    scale=1.0 / math.sqrt(128.0), seeds=(3000, 3001, 3002),
+    seg_runs=[(0, 17550, 1), (17550, 17776, 1), (17776, 17920, 0)],
+    note="17,550 video + 226 text tokens (seg 1), 144 pad tokens (seg 0)")
+
+# 720p large-DiT layer: 21x45x80 latent patch grid, all 40 heads on one GPU
+# (Wan2.1 14B at 1280x720, 81 frames; Table 5 and section 4's offload sweep).
+LARGE_DIT_720P = Workload(
+    name="dit720p_large", B=1, S=75600, H=40, D=128,
+    scale=1.0 / math.sqrt(128.0), seeds=(4000, 4001, 4002), seg_runs=None,
+    note="21x45x80 latent patch grid, no mask")
+
+# Packed variable-length clips: 4 clips + 14 pad tokens, distinct seg IDs,
+# Q/K with sigma 3 to stress the softmax range.
+PACKED_CLIPS = Workload(
+    name="packed_clips", B=1, S=61440, H=16, D=128,
+    scale=1.0 / math.sqrt(128.0), seeds=(5000, 5001, 5002), sigma_qk=3.0,
+    seg_runs=[(0, 4096, 1), (4096, 12286, 2), (12286, 28666, 3),
+              (28666, 61426, 4), (61426, 61440, 0)],
+    note="clips of 4,096 / 8,190 / 16,380 / 32,760 tokens + 14 pad")
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in (TINY_REF, SMALL_DIT_480P, JOINT_VIDEO_TEXT,
+                        LARGE_DIT_720P, PACKED_CLIPS)
+}
+# The workload the throughput line is quoted on.
+HEADLINE = LARGE_DIT_720P.name
+
+for _w in WORKLOADS.values():
+    if _w.seg_runs is not None:
+        assert _runs_cover(_w.seg_runs, _w.S), _w.name
+
+
+# --- generators --------------------------------------------------------------
+def randn_bf16(shape: Sequence[int], seed: int, sigma: float = 1.0) -> torch.Tensor:
+    """float32 N(0, sigma^2) from a seeded CPU generator, rounded to bf16."""
+    g = torch.Generator().manual_seed(int(seed))
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(torch.bfloat16)
+
+
+def seg_from_runs(runs: SegRuns, B: int, S: int) -> torch.Tensor:
+    """int32 [B, S] segment IDs, the same runs in every batch row."""
+    seg = torch.empty(S, dtype=torch.int32)
+    for a, b, sid in runs:
+        seg[a:b] = sid
+    return seg.unsqueeze(0).expand(B, S).contiguous()
+
+
+def make_inputs(w: Workload) -> Dict[str, Optional[torch.Tensor]]:
+    """CPU tensors q, k, v (bf16 [B,S,H,D]) and seg_q, seg_kv (int32 [B,S] or None)."""
+    shape = (w.B, w.S, w.H, w.D)
+    q = randn_bf16(shape, w.seeds[0], w.sigma_qk)
+    k = randn_bf16(shape, w.seeds[1], w.sigma_qk)
+    v = randn_bf16(shape, w.seeds[2], w.sigma_v)
+    seg = seg_from_runs(w.seg_runs, w.B, w.S) if w.seg_runs is not None else None
+    return {"q": q, "k": k, "v": v, "seg_q": seg,
+            "seg_kv": None if seg is None else seg.clone()}
+
+
+def make_random(B: int, S: int, H: int, D: int, seed: int, sigma_qk: float = 1.0,
+                sigma_v: float = 1.0) -> Dict[str, torch.Tensor]:
+    """Ad-hoc seeded q, k, v for shape sweeps (same recipe as the workloads)."""
+    shape = (B, S, H, D)
+    return {"q": randn_bf16(shape, seed, sigma_qk),
+            "k": randn_bf16(shape, seed + 1, sigma_qk),
+            "v": randn_bf16(shape, seed + 2, sigma_v)}
+
+
+def random_segments(B: int, S: int, seed: int, kind: str) -> torch.Tensor:
+    """Seeded int32 [B, S] segment layouts used by the parity sweeps.
+
+    kinds: "single" (all 1), "padded" (ones then a pad tail of 0),
+    "packed" (contiguous runs of random length, IDs 1..n, pad tail),
+    "interleaved" (random IDs in {0,1,2,3} per token, so segments are
+    non-contiguous), "singletons" (every token its own ID),
+    "allpad" (every token 0).
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    seg = torch.zeros(B, S, dtype=torch.int32)
+    for b in range(B):
+        if kind == "single":
+            seg[b] = 1
+        elif kind == "padded":
+            n_pad = int(torch.randint(0, max(1, S // 4) + 1, (1,), generator=g))
+            seg[b, : S - n_pad] = 1
+        elif kind == "packed":
+            pos, sid = 0, 1
+            n_pad = int(torch.randint(0, max(1, S // 8) + 1, (1,), generator=g))
+            real = S - n_pad
+            while pos < real:
+                ln = int(torch.randint(1, max(2, real // 3) + 1, (1,), generator=g))
+                seg[b, pos: min(real, pos + ln)] = sid
+                pos += ln
+                sid += 1
+        elif kind == "interleaved":
+            seg[b] = torch.randint(0, 4, (S,), generator=g, dtype=torch.int32)
+        elif kind == "singletons":
+            seg[b] = torch.arange(1, S + 1, dtype=torch.int32)
+        elif kind == "allpad":
+            pass
+        else:
+            raise ValueError(kind)
+    return seg
+
+
+def bf16_bits(t: torch.Tensor):
+    """uint16 numpy view of a CPU bf16 tensor (the exact bits)."""
+    assert t.dtype == torch.bfloat16 and t.device.type == "cpu"
+    return t.contiguous().view(torch.int16).numpy().view("uint16")
