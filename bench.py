@@ -1,0 +1,232 @@
+"""Throughput of the segment-masked flash-attention forward on one MI355X.
+
+One step = one vdx_attn_fwd call (the whole hot path: tile scheduling,
+segment classification, QK^T, masking, online softmax, PV, epilogue) over one
+batch of seeded synthetic input already resident in HBM.  The default
+workload is the 720p large-DiT layer (B=1, S=75,600 = 21x45x80 latent
+patches, H=40, D=128, bf16, unmasked), the shape the throughput target is
+quoted on.
+
+Prints ONE JSON line:
+  value        valid-pair TFLOP/s = 4*D*H*sum_b #valid(i,j) / (wall time per step)
+  roofline     the attention kernel against the MI355X dense bf16 MFMA peak,
+               with its average launch time from HIP events on its stream and
+               the HBM traffic from rocprofv3 counters when they are current
+  cpu_baseline the fp64 oracle timed on a bounded row sample on the host cores
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline] [--copy-calib]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=75,600 H=40 D=128 (1 GPU)"
+KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
+                  for f in ("attn_fwd_kernel.hip", "attn_fwd_launch.h", "vdx_attn_api.hip")]
+COUNTERS_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def valid_pairs(w: W.Workload) -> int:
+    """Number of (query, key) pairs that take part, summed over the batch."""
+    if w.seg_runs is None:
+        return w.B * w.S * w.S
+    per_id = {}
+    for a, b, sid in w.seg_runs:
+        if sid != 0:
+            per_id[sid] = per_id.get(sid, 0) + (b - a)
+    return w.B * sum(n * n for n in per_id.values())
+
+
+def algorithmic_bytes(w: W.Workload) -> int:
+    """Bytes one call must move at least: read q, k, v (+ segs), write out and lse."""
+    n = w.B * w.S * w.H * w.D
+    b = 4 * 2 * n + 4 * w.B * w.H * w.S
+    if w.seg_runs is not None:
+        b += 2 * 4 * w.B * w.S
+    return b
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on different kernel source."""
+    path = os.path.join(COUNTERS_DIR, f"attn_fwd_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return doc.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+def cpu_baseline(w: W.Workload, x, target_s: float = 15.0):
+    import oracle
+    cores = oracle.default_threads()
+    qb, kb, vb = W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"])
+    sq = None if x["seg_q"] is None else x["seg_q"].numpy()
+    sk = None if x["seg_kv"] is None else x["seg_kv"].numpy()
+    rng = np.random.default_rng(7)
+
+    def rows_for(n):
+        b = rng.integers(0, w.B, n)
+        h = rng.integers(0, w.H, n)
+        i = rng.integers(0, w.S, n)
+        return np.stack([b, h, i], 1).astype(np.int64)
+
+    def flops(rows):
+        if sq is None:
+            return 4.0 * w.D * w.S * len(rows)
+        tot = 0.0
+        for b, _, i in rows:
+            c = sq[b, i]
+            if c != 0:
+                tot += 4.0 * w.D * float(np.count_nonzero(sk[b] == c))
+        return tot
+
+    probe = rows_for(cores)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qb, kb, vb, sq, sk, float(np.float32(w.scale)), rows=probe, n_threads=cores)
+    dt = time.perf_counter() - t0
+    n = max(cores, int(cores * target_s / max(dt, 1e-3)))
+    rows = rows_for(n)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qb, kb, vb, sq, sk, float(np.float32(w.scale)), rows=rows, n_threads=cores)
+    dt = time.perf_counter() - t0
+    rate = flops(rows) / dt / 1e12
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} random (b,h,i) rows of {w.name}, each over its full key set, "
+                      f"{dt:.1f} s on {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU only: the attention kernel runs on one GPU's share "
+              "with every head local; multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import spatiotemporal_attention_amd as vdx
+
+    if args.copy_calib:
+        copy_calibration()
+        return
+
+    w = W.WORKLOADS[args.workload]
+    log(f"workload {w.name}: B={w.B} S={w.S} H={w.H} D={w.D} masked={w.masked}")
+    x = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale,
+                     out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, "
+        f"kernel mean {np.mean(kernel_ms):.3f} ms (min {np.min(kernel_ms):.3f}, "
+        f"median {np.median(kernel_ms):.3f})")
+
+    flop = 4.0 * w.D * w.H * valid_pairs(w)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (float(np.mean(kernel_ms)) * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D,
+                   "segments": "none" if w.seg_runs is None else w.seg_runs,
+                   "flop_per_step": flop, "peak_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(w.name),
+                     "algorithmic_bytes": algorithmic_bytes(w),
+                     "kernel_ms_mean": round(float(np.mean(kernel_ms)), 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

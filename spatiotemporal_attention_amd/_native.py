@@ -1,0 +1,56 @@
+"""ctypes binding of the C ABI in include/vdx_attn.h (argument marshalling only).
+
+Loads the in-tree ``libvdx_attn.so``; there is no fallback path: if the
+library is missing or fails to load, import of the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+VDX_OK = 0
+VDX_ERR_NULL_PTR = 1
+VDX_ERR_SEG_PAIR = 2
+VDX_ERR_SHAPE = 3
+VDX_ERR_HEAD_DIM = 4
+VDX_ERR_SCALE = 5
+VDX_ERR_ALIGN = 6
+VDX_ERR_DEVICE = 7
+VDX_ERR_LAUNCH = 8
+
+EXPORTED = ("vdx_attn_fwd", "vdx_status_str", "vdx_abi_version")
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"HIP library not built: {path} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.vdx_attn_fwd.restype = i
+    lib.vdx_attn_fwd.argtypes = [p, p, p, p, p, p, p, i, i, i, i, ctypes.c_float, p]
+    lib.vdx_status_str.restype = ctypes.c_char_p
+    lib.vdx_status_str.argtypes = [i]
+    lib.vdx_abi_version.restype = i
+    lib.vdx_abi_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def status_str(rc: int) -> str:
+    return lib.vdx_status_str(int(rc)).decode()
+
+
+def abi_version() -> int:
+    return int(lib.vdx_abi_version())
+
+
+def attn_fwd_raw(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale, stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL)."""
+    return int(lib.vdx_attn_fwd(q or None, k or None, v or None, seg_q or None, seg_kv or None,
+                                out or None, lse or None, int(B), int(S), int(H), int(D),
+                                float(scale), stream or None))

@@ -1,0 +1,95 @@
+// vdx_attn_api.hip -- the C ABI declared in include/vdx_attn.h: argument
+// validation (before any HIP call), the per-device architecture check, and
+// the hand-off to the gfx950 launcher.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn_fwd_launch.h"
+#include "vdx_attn.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = something else / query failed.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VDX_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int c = g_arch_ok[dev].load(std::memory_order_acquire);
+        if (c == 1) return VDX_OK;
+        if (c == 2) return VDX_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    int ok = 2;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+        ok = 1;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok, std::memory_order_release);
+    return ok == 1 ? VDX_OK : VDX_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int validate(const void* q, const void* k, const void* v, const int32_t* seg_q,
+             const int32_t* seg_kv, const void* out, const float* lse, int B, int S, int H, int D,
+             float scale) {
+    if (!q || !k || !v || !out || !lse) return VDX_ERR_NULL_PTR;
+    if ((seg_q == nullptr) != (seg_kv == nullptr)) return VDX_ERR_SEG_PAIR;
+    if (B < 1 || S < 1 || H < 1) return VDX_ERR_SHAPE;
+    if (D > 0) {
+        const __int128 n = (__int128)B * S * H * D;
+        if (n > (__int128)INT64_MAX / 2) return VDX_ERR_SHAPE;
+    }
+    const int64_t bq = vdx::queries_per_workgroup();
+    const int64_t n_wg = (int64_t)B * H * ((S + bq - 1) / bq);
+    if (n_wg > INT32_MAX) return VDX_ERR_SHAPE;
+    if (seg_q && (int64_t)S > vdx::max_masked_seq()) return VDX_ERR_SHAPE;
+    if (D != 64 && D != 128) return VDX_ERR_HEAD_DIM;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return VDX_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return VDX_ERR_ALIGN;
+    if (!aligned(lse, 4) || (seg_q && (!aligned(seg_q, 4) || !aligned(seg_kv, 4))))
+        return VDX_ERR_ALIGN;
+    return VDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int vdx_attn_fwd(
+    const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
+    void* out, float* lse, int B, int S, int H, int D, float scale, hipStream_t stream) {
+    int rc = validate(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    vdx::AttnArgs a{q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale};
+    if (vdx::launch_attn_fwd(a, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
+__attribute__((visibility("default"))) const char* vdx_status_str(int status) {
+    switch (status) {
+        case VDX_OK: return "VDX_OK";
+        case VDX_ERR_NULL_PTR: return "VDX_ERR_NULL_PTR: q, k, v, out or lse is NULL";
+        case VDX_ERR_SEG_PAIR: return "VDX_ERR_SEG_PAIR: exactly one of seg_q/seg_kv is NULL";
+        case VDX_ERR_SHAPE: return "VDX_ERR_SHAPE: B, S or H out of range";
+        case VDX_ERR_HEAD_DIM: return "VDX_ERR_HEAD_DIM: D must be 64 or 128";
+        case VDX_ERR_SCALE: return "VDX_ERR_SCALE: scale must be finite and > 0";
+        case VDX_ERR_ALIGN: return "VDX_ERR_ALIGN: q/k/v/out need 16-byte, seg/lse 4-byte alignment";
+        case VDX_ERR_DEVICE: return "VDX_ERR_DEVICE: current device is not gfx950";
+        case VDX_ERR_LAUNCH: return "VDX_ERR_LAUNCH: kernel launch failed";
+        default: return "VDX_ERR_UNKNOWN";
+    }
+}
+
+__attribute__((visibility("default"))) int vdx_abi_version(void) { return VDX_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+"""The C ABI boundary (include/vdx_attn.h): the library loads, exports every
+declared function, reports versions and status strings, and validates
+arguments before any HIP call -- all checkable without a GPU, since
+validation never dereferences the (fake, aligned) device addresses used here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdx_attn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vdx_[a-z0-9_]+)\s*\(", src)))
+
+
+def header_enum():
+    src = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(VDX_[A-Z_]+)\s*=\s*(\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def native():
+    from spatiotemporal_attention_amd import _native
+    return _native
+
+
+def test_exports_every_declared_function(native):
+    names = header_functions()
+    assert names == sorted(["vdx_attn_fwd", "vdx_status_str", "vdx_abi_version"])
+    for n in names:
+        assert hasattr(native.lib, n), n
+
+
+def test_abi_version_matches_header(native):
+    m = re.search(r"#define\s+VDX_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert native.abi_version() == int(m.group(1))
+
+
+def test_status_codes_match_header_and_have_names(native):
+    enum = header_enum()
+    for name, val in enum.items():
+        assert getattr(native, name) == val, name
+        s = native.status_str(val)
+        assert s.startswith(name), (name, s)
+    assert native.status_str(12345) == "VDX_ERR_UNKNOWN"
+
+
+A = 0x10000  # fake, 16-byte aligned device address; never dereferenced here
+
+
+def call(native, q=A, k=A + 0x100, v=A + 0x200, sq=0, sk=0, out=A + 0x300, lse=A + 0x400,
+         B=1, S=128, H=2, D=128, scale=0.125):
+    return native.attn_fwd_raw(q, k, v, sq, sk, out, lse, B, S, H, D, scale, 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out", "lse"])
+def test_null_pointer(native, which):
+    assert call(native, **{which: 0}) == native.VDX_ERR_NULL_PTR
+
+
+def test_segment_pair(native):
+    assert call(native, sq=A + 0x500) == native.VDX_ERR_SEG_PAIR
+    assert call(native, sk=A + 0x500) == native.VDX_ERR_SEG_PAIR
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(S=0), dict(H=0), dict(B=-1), dict(S=-5),
+                                dict(B=2**31 - 1, S=2**31 - 1, H=2**31 - 1),
+                                dict(S=2_097_153, sq=A + 0x500, sk=A + 0x600)])
+def test_shape(native, kw):
+    assert call(native, **kw) == native.VDX_ERR_SHAPE
+
+
+@pytest.mark.parametrize("D", [0, 1, 32, 96, 256, -64])
+def test_head_dim(native, D):
+    assert call(native, D=D) == native.VDX_ERR_HEAD_DIM
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("nan"), float("inf"), float("-inf")])
+def test_scale(native, scale):
+    assert call(native, scale=scale) == native.VDX_ERR_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(q=A + 2), dict(k=A + 8), dict(v=A + 4), dict(out=A + 6),
+                                dict(lse=A + 0x402), dict(sq=A + 0x501, sk=A + 0x600),
+                                dict(sq=A + 0x500, sk=A + 0x602)])
+def test_alignment(native, kw):
+    assert call(native, **kw) == native.VDX_ERR_ALIGN
+
+
+def test_validation_order(native):
+    # NULL beats everything, then segment pair, shape, head dim, scale, alignment.
+    assert call(native, q=0, sq=A, B=0, D=3, scale=-1.0) == native.VDX_ERR_NULL_PTR
+    assert call(native, sq=A + 0x500, B=0, D=3, scale=-1.0) == native.VDX_ERR_SEG_PAIR
+    assert call(native, B=0, D=3, scale=-1.0, q=A + 1) == native.VDX_ERR_SHAPE
+    assert call(native, D=3, scale=-1.0, q=A + 1) == native.VDX_ERR_HEAD_DIM
+    assert call(native, scale=-1.0, q=A + 1) == native.VDX_ERR_SCALE
+
+
+def test_valid_arguments_without_gpu_report_device_error(native):
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this path would launch on fake addresses")
+    assert call(native) == native.VDX_ERR_DEVICE
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    import spatiotemporal_attention_amd as vdx
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vdx.attn_fwd(q, q, q)  # CPU tensors are refused before the C call
+    with pytest.raises(ValueError):
+        vdx.attn_fwd(q.float(), q, q)
+
+
+@pytest.mark.gpu
+def test_error_path_writes_nothing(need_gpu, ):
+    from spatiotemporal_attention_amd import _native
+    q = torch.randn(1, 64, 1, 64, device="cuda").bfloat16()
+    out = torch.full_like(q, 3.0)
+    lse = torch.full((1, 1, 64), 5.0, device="cuda")
+    rc = _native.attn_fwd_raw(q.data_ptr(), q.data_ptr(), q.data_ptr(), 0, 0, out.data_ptr(),
+                              lse.data_ptr(), 1, 64, 1, 64, float("nan"),
+                              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == _native.VDX_ERR_SCALE
+    assert torch.all(out == 3.0) and torch.all(lse == 5.0)
+
+
+@pytest.mark.gpu
+def test_runs_on_side_stream(need_gpu):
+    import spatiotemporal_attention_amd as vdx
+    q = torch.randn(1, 300, 2, 64, device="cuda").bfloat16()
+    ref, ref_lse = vdx.attn_fwd(q, q, q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, l = vdx.attn_fwd(q, q, q)
+    s.synchronize()
+    assert torch.equal(o, ref) and torch.equal(l, ref_lse)

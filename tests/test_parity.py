@@ -1,0 +1,174 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded bf16 inputs, element by element, plus bit-exact properties.
+
+Sizes span several 256-query / 64-key tiles and ragged tails; segment layouts
+cover single, padded, packed, interleaved (non-contiguous), one-token and
+all-padding cases.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import (check_full, run_gpu, run_oracle, valid_rows)
+
+pytestmark = pytest.mark.gpu
+
+SEQS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000]
+KINDS = [None, "single", "padded", "packed", "interleaved", "singletons", "allpad"]
+
+
+def _case(B, S, H, D, kind, seed, sigma_qk=1.0):
+    x = W.make_random(B, S, H, D, seed=seed, sigma_qk=sigma_qk)
+    seg = None if kind is None else W.random_segments(B, S, seed + 7, kind)
+    return x, seg
+
+
+def test_tiny_reference_workload_full(need_gpu):
+    w = W.WORKLOADS["tiny_ref"]
+    x = W.make_inputs(w)
+    print(f"case tiny_ref B={w.B} S={w.S} H={w.H} D={w.D}", flush=True)
+    out_g, lse_g = run_gpu(x, x["seg_q"], x["seg_kv"], w.scale)
+    out_o, lse_o = run_oracle(x, x["seg_q"], x["seg_kv"], w.scale)
+    has = valid_rows(x["seg_q"], x["seg_kv"], w.B, w.S)
+    st = check_full(out_g, lse_g, out_o, lse_o, has)
+    print("tiny_ref", st)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", SEQS)
+@pytest.mark.parametrize("kind", KINDS, ids=[str(k) for k in KINDS])
+def test_shape_and_segment_sweep(need_gpu, S, D, kind):
+    B, H = (2, 2) if S <= 257 else (1, 2)
+    x, seg = _case(B, S, H, D, kind, seed=100 * S + D)
+    print(f"case sweep B={B} S={S} H={H} D={D} kind={kind}", flush=True)
+    scale = 1.0 / math.sqrt(D)
+    out_g, lse_g = run_gpu(x, seg, None if seg is None else seg.clone(), scale)
+    out_o, lse_o = run_oracle(x, seg, None if seg is None else seg.clone(), scale)
+    has = valid_rows(seg, seg, B, S)
+    check_full(out_g, lse_g, out_o, lse_o, has)
+
+
+@pytest.mark.parametrize("kind", [None, "packed", "interleaved"], ids=str)
+def test_long_ragged_sequence(need_gpu, kind):
+    B, S, H, D = 1, 4097, 1, 128
+    x, seg = _case(B, S, H, D, kind, seed=4097, sigma_qk=2.0)
+    print(f"case long B={B} S={S} H={H} D={D} kind={kind}", flush=True)
+    out_g, lse_g = run_gpu(x, seg, None if seg is None else seg.clone(), 1 / math.sqrt(D))
+    out_o, lse_o = run_oracle(x, seg, None if seg is None else seg.clone(), 1 / math.sqrt(D))
+    check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg, seg, B, S))
+
+
+def test_distinct_query_and_key_segments(need_gpu):
+    """seg_q and seg_kv differ: query IDs missing from seg_kv give masked rows."""
+    B, S, H, D = 2, 300, 2, 64
+    x = W.make_random(B, S, H, D, seed=77)
+    seg_q = W.random_segments(B, S, 5, "interleaved")
+    seg_kv = W.random_segments(B, S, 6, "interleaved")
+    seg_kv[seg_kv == 3] = 2  # ID 3 exists only among the queries
+    print("case distinct segs", flush=True)
+    out_g, lse_g = run_gpu(x, seg_q, seg_kv, 0.125)
+    out_o, lse_o = run_oracle(x, seg_q, seg_kv, 0.125)
+    check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg_q, seg_kv, B, S))
+
+
+def test_peaky_softmax_wide_range(need_gpu):
+    """Q, K ~ N(0, 3^2) as in the packed-clips workload: scores span tens of units."""
+    B, S, H, D = 1, 2000, 2, 128
+    x = W.make_random(B, S, H, D, seed=555, sigma_qk=3.0)
+    seg = W.random_segments(B, S, 3, "packed")
+    print("case peaky", flush=True)
+    out_g, lse_g = run_gpu(x, seg, seg.clone(), 1 / math.sqrt(D))
+    out_o, lse_o = run_oracle(x, seg, seg.clone(), 1 / math.sqrt(D))
+    print(check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg, seg, B, S)))
+
+
+# --- bit-exact properties -------------------------------------------------------
+def test_repeated_runs_bit_identical(need_gpu):
+    x, seg = _case(2, 3000, 3, 128, "packed", seed=9)
+    print("case repeat", flush=True)
+    a = run_gpu(x, seg, seg.clone())
+    for _ in range(3):
+        b = run_gpu(x, seg, seg.clone())
+        assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+        assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_batch_split_bit_identical(need_gpu):
+    x, seg = _case(2, 1500, 2, 128, "padded", seed=10)
+    print("case batch split", flush=True)
+    out, lse = run_gpu(x, seg, seg.clone())
+    for b in range(2):
+        xb = {n: x[n][b:b + 1].contiguous() for n in ("q", "k", "v")}
+        sb = seg[b:b + 1].contiguous()
+        o1, l1 = run_gpu(xb, sb, sb.clone())
+        assert torch.equal(o1.view(torch.int16), out[b:b + 1].view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), lse[b:b + 1].view(torch.int32))
+
+
+def test_head_split_bit_identical(need_gpu):
+    x = W.make_random(1, 700, 3, 64, seed=11)
+    print("case head split", flush=True)
+    out, lse = run_gpu(x)
+    for h in range(3):
+        xh = {n: x[n][:, :, h:h + 1].contiguous() for n in ("q", "k", "v")}
+        o1, l1 = run_gpu(xh)
+        assert torch.equal(o1.view(torch.int16), out[:, :, h:h + 1].view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), lse[:, h:h + 1].view(torch.int32))
+
+
+def test_null_segments_equal_all_ones_bitwise(need_gpu):
+    for S in (1000, 1024):
+        x = W.make_random(1, S, 2, 128, seed=12)
+        ones = torch.ones(1, S, dtype=torch.int32)
+        print(f"case null-vs-ones S={S}", flush=True)
+        a = run_gpu(x)
+        b = run_gpu(x, ones, ones.clone())
+        assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+        assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_segment_independence_bitwise(need_gpu):
+    """Re-randomising segment 2 leaves every row of segment 1 bit-identical."""
+    B, S, H, D = 1, 2048, 2, 128
+    x = W.make_random(B, S, H, D, seed=13)
+    seg = torch.tensor([[1, 2] * (S // 2)], dtype=torch.int32)
+    seg[0, 1000:1500] = 1
+    print("case segment independence", flush=True)
+    a_out, a_lse = run_gpu(x, seg, seg.clone())
+    y = W.make_random(B, S, H, D, seed=14, sigma_qk=3.0)
+    z = {n: x[n].clone() for n in ("q", "k", "v")}
+    sel = seg[0] == 2
+    for n in ("q", "k", "v"):
+        z[n][:, sel] = y[n][:, sel]
+    b_out, b_lse = run_gpu(z, seg, seg.clone())
+    s1 = seg[0] == 1
+    assert torch.equal(a_out[:, s1].view(torch.int16), b_out[:, s1].view(torch.int16))
+    assert torch.equal(a_lse[:, :, s1].view(torch.int32), b_lse[:, :, s1].view(torch.int32))
+
+
+def test_masked_rows_and_all_pad_batch(need_gpu):
+    B, S, H, D = 2, 600, 2, 128
+    x = W.make_random(B, S, H, D, seed=15)
+    seg = torch.zeros(B, S, dtype=torch.int32)
+    seg[1, :450] = 7
+    print("case all-pad batch", flush=True)
+    out, lse = run_gpu(x, seg, seg.clone())
+    assert torch.all(out[0].view(torch.int16) == 0)
+    assert torch.all(torch.isneginf(lse[0]))
+    assert torch.all(out[1, 450:].view(torch.int16) == 0)
+    assert torch.all(torch.isneginf(lse[1, :, 450:]))
+    assert torch.all(torch.isfinite(lse[1, :, :450]))
+
+
+def test_singletons_return_value_exactly(need_gpu):
+    B, S, H, D = 1, 900, 2, 128
+    x = W.make_random(B, S, H, D, seed=16)
+    seg = W.random_segments(B, S, 0, "singletons")
+    print("case singletons", flush=True)
+    out, lse = run_gpu(x, seg, seg.clone())
+    assert torch.equal(out.view(torch.int16), x["v"].view(torch.int16))
+    s_ii = (x["q"].double() * x["k"].double()).sum(-1).transpose(1, 2) / math.sqrt(D)
+    assert (lse.double() - s_ii).abs().max() < 1e-4
