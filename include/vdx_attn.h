@@ -49,9 +49,10 @@ enum vdx_status {
     VDX_ERR_NULL_PTR = 1, /* q, k, v, out or lse is NULL                        */
     VDX_ERR_SEG_PAIR = 2, /* exactly one of seg_q / seg_kv is NULL              */
     VDX_ERR_SHAPE = 3,    /* B, S or H < 1, element count overflows int64, the
-                             grid would exceed 2^31-1 workgroups, or a masked
-                             call has S > 2,097,152 (the on-chip key-tile
-                             table holds 32,768 tiles of 64 keys)              */
+                             grid would exceed 2^31-1 workgroups, 64*H*D
+                             exceeds 2^31-1, or a masked call has
+                             S > 1,966,080 (the on-chip key-tile table holds
+                             30,720 tiles of 64 keys)                          */
     VDX_ERR_HEAD_DIM = 4, /* D is not 64 or 128                                 */
     VDX_ERR_SCALE = 5,    /* scale is not finite or is <= 0                     */
     VDX_ERR_ALIGN = 6,    /* q, k, v, out not 16-byte aligned; seg_q, seg_kv or

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libvdx_attn.so")
 SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "vdx_attn_api.hip")]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-               "-fvisibility=hidden", "-Wall",
+               "-fvisibility=hidden", "-Wall", "-fno-honor-nans",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

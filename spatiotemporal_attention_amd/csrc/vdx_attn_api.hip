@@ -50,6 +50,8 @@ int validate(const void* q, const void* k, const void* v, const int32_t* seg_q,
     const int64_t n_wg = (int64_t)B * H * ((S + bq - 1) / bq);
     if (n_wg > INT32_MAX) return VDX_ERR_SHAPE;
     if (seg_q && (int64_t)S > vdx::max_masked_seq()) return VDX_ERR_SHAPE;
+    // Per-tile element offsets (64 tokens x H*D) are kept in 32 bits.
+    if (D > 0 && (int64_t)64 * H * D > INT32_MAX) return VDX_ERR_SHAPE;
     if (D != 64 && D != 128) return VDX_ERR_HEAD_DIM;
     if (!std::isfinite(scale) || !(scale > 0.f)) return VDX_ERR_SCALE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))

@@ -3,7 +3,11 @@ binding, run the oracle on the same bf16 bits, and compare to the tolerances
 of the parity bar.
 
 Tolerances (fixed for bf16 output of fp32-accumulated attention):
-  OUT_ATOL = 1e-2   max |out_gpu - out_oracle| over compared elements;
+  OUT_ATOL = 1e-2   max |out_gpu - out_oracle| over compared elements, plus
+                    BF16_U * |out_oracle| (BF16_U = 2^-8, the unit roundoff of
+                    bf16): rounding the exact value once to bf16 already moves
+                    it by up to that much, which exceeds 1e-2 alone once
+                    |out| > 2.56 (tiny segments, peaky rows);
   LSE_ATOL = 1e-3   max |lse_gpu - lse_oracle| over rows with a valid key;
   REL_L2   = 1e-2   ||out_gpu - out_oracle|| / ||out_oracle|| per case, an extra
                     gate because the absolute bound is loose at long S (output
@@ -20,6 +24,7 @@ import oracle
 import workloads as W
 
 OUT_ATOL = 1e-2
+BF16_U = 2.0 ** -8
 LSE_ATOL = 1e-3
 REL_L2 = 1e-2
 
@@ -70,12 +75,13 @@ def check_full(out_g, lse_g, out_o, lse_o, has):
     if has.any():
         diff = np.abs(og[has] - out_o[has])
         stats["max_abs"] = float(diff.max())
+        stats["max_tol_frac"] = float((diff / (OUT_ATOL + BF16_U * np.abs(out_o[has]))).max())
         ref_n = float(np.linalg.norm(out_o[has]))
         stats["rel_l2"] = float(np.linalg.norm(og[has] - out_o[has]) / max(ref_n, 1e-300))
         lh = np.transpose(lg, (0, 2, 1))[has]
         lo = np.transpose(lse_o, (0, 2, 1))[has]
         stats["max_lse"] = float(np.abs(lh - lo).max())
-        assert stats["max_abs"] <= OUT_ATOL, stats
+        assert stats["max_tol_frac"] <= 1.0, stats
         assert stats["max_lse"] <= LSE_ATOL, stats
         assert stats["rel_l2"] <= REL_L2, stats
     if (~has).any():
@@ -117,10 +123,12 @@ def check_rows(out_g, lse_g, rows, out_o, lse_o, has):
     hv = has[rows[:, 0], rows[:, 2]]
     stats = {"rows": int(len(rows)), "max_abs": 0.0, "max_lse": 0.0, "rel_l2": 0.0}
     if hv.any():
-        stats["max_abs"] = float(np.abs(og[hv] - out_o[hv]).max())
+        diff = np.abs(og[hv] - out_o[hv])
+        stats["max_abs"] = float(diff.max())
+        stats["max_tol_frac"] = float((diff / (OUT_ATOL + BF16_U * np.abs(out_o[hv]))).max())
         stats["max_lse"] = float(np.abs(lg[hv] - lse_o[hv]).max())
         stats["rel_l2"] = float(np.linalg.norm(og[hv] - out_o[hv]) / np.linalg.norm(out_o[hv]))
-        assert stats["max_abs"] <= OUT_ATOL, stats
+        assert stats["max_tol_frac"] <= 1.0, stats
         assert stats["max_lse"] <= LSE_ATOL, stats
         assert stats["rel_l2"] <= REL_L2, stats
     if (~hv).any():

@@ -72,7 +72,8 @@ def test_segment_pair(native):
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(S=0), dict(H=0), dict(B=-1), dict(S=-5),
                                 dict(B=2**31 - 1, S=2**31 - 1, H=2**31 - 1),
-                                dict(S=2_097_153, sq=A + 0x500, sk=A + 0x600)])
+                                dict(S=1_966_081, sq=A + 0x500, sk=A + 0x600),
+                                dict(H=2**18, D=128)])
 def test_shape(native, kw):
     assert call(native, **kw) == native.VDX_ERR_SHAPE
 

@@ -1,5 +1,5 @@
 """GPU probes of the gfx950 instruction semantics the attention kernel relies
-on.  The kernel assumes, for v_mfma_f32_32x32x16_bf16 (D = A B + C, A 32x16,
+on (all single-wave, in-bounds, on buffers of fixed size).  The kernel assumes, for v_mfma_f32_32x32x16_bf16 (D = A B + C, A 32x16,
 B 16x32), that lane l holds A[l%32][8*(l//32)+e] and B[8*(l//32)+e][l%32]
 (e = 0..7), and accumulator register r holds D[8*(r//4)+4*(l//32)+r%4][l%32].
 """
@@ -21,7 +21,8 @@ def probes(need_gpu):
     if not os.path.exists(PROBE_LIB):
         raise RuntimeError(f"probe library not built: {PROBE_LIB}")
     lib = ctypes.CDLL(PROBE_LIB)
-    for name in ("probe_mfma32", "probe_permlane32_swap", "probe_trans"):
+    for name in ("probe_mfma32", "probe_permlane32_swap", "probe_trans", "probe_load_lds",
+                 "probe_read_tr"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -96,3 +97,42 @@ def test_exp2_and_log2_builtins_accuracy(probes):
     bound = np.maximum(np.abs(wl), 1.0) * 4 * 2.0 ** -23
     print(f"v_log_f32 max abs err {err.max():.3e}")
     assert np.all(err <= bound)
+
+
+def test_global_load_lds_dwordx4_places_lane_chunks_contiguously(probes):
+    """global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l."""
+    src = torch.arange(4 * 64, dtype=torch.int32, device="cuda") * 7 + 3
+    perm = torch.tensor([(37 * l + 11) % 64 for l in range(64)], dtype=torch.int32, device="cuda")
+    out = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    assert probes.probe_load_lds(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(perm.data_ptr()),
+                                 ctypes.c_void_p(out.data_ptr()), _stream()) == 0
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().view(np.uint32)
+    srcn = src.cpu().numpy().view(np.uint32)
+    pn = perm.cpu().numpy()
+    want = np.full(1024, 0xDEADBEEF, dtype=np.uint32)
+    for l in range(64):
+        want[128 + 4 * l: 128 + 4 * l + 4] = srcn[4 * pn[l]: 4 * pn[l] + 4]
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("pattern", ["rows_of_4", "strided_rows"])
+def test_ds_read_b64_tr_b16_semantics(probes, pattern):
+    """Within each 16-lane group, with X[j][k] the k-th 16-bit element at lane
+    j's address, lane i receives Y[i][e] = X[4e + i//4][i % 4]."""
+    if pattern == "rows_of_4":
+        addr = [4 * l for l in range(64)]
+    else:
+        addr = [(l % 16) * 64 + (l // 16) * 4 + 1024 * (l % 3 == 0) for l in range(64)]
+        addr = [a & ~3 for a in addr]
+    a_d = torch.tensor(addr, dtype=torch.int32, device="cuda")
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    assert probes.probe_read_tr(ctypes.c_void_p(a_d.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(64, 4)
+    for l in range(64):
+        grp, i = l // 16, l % 16
+        for e in range(4):
+            src_lane = 16 * grp + 4 * e + i // 4
+            assert got[l, e] == addr[src_lane] + (i % 4), (l, e)
