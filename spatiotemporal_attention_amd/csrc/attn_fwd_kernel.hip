@@ -10,27 +10,33 @@
 // invalid key blocks; Table 4, group 1 for masking padding).
 //
 // Design (CDNA4 first; the TPU Pallas kernel of the pages is prior art only):
-//   * one workgroup = 4 wave64s (one per SIMD, 512 registers each) = 256
-//     queries of one (batch, head); a wave owns 64 queries as two 32-query
-//     halves A and B whose Q slices stay in registers for the whole sweep;
+//   * one workgroup = 8 wave64s (two per SIMD) = 256 queries of one
+//     (batch, head); each wave owns 32 queries whose Q slice stays in
+//     registers for the whole sweep;
 //   * scores are formed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: every lane then owns one query column, so the
 //     row max/sum need one v_permlane32_swap with lane^32 only, and the fp32
 //     score registers become the bf16 B operand of O^T += V^T P^T without any
 //     data movement (the key order inside a 32-key block is permuted so the
 //     accumulator rows line up with the operand's contraction index);
-//   * in-wave software pipeline: half B runs half a key tile behind half A.
-//     Each phase issues one half's MFMAs (P V of the previous tile and K Q^T
-//     of the current one) while the VALU runs the other half's online
-//     softmax, so matrix cores and vector ALUs work concurrently inside one
-//     wave;
+//   * ping-pong schedule: the waves form two groups (one wave of each per
+//     SIMD) that run one phase apart -- while one group issues its MFMAs
+//     (P V of the previous key tile and K Q^T of the current one, operands
+//     fetched from LDS a few MFMAs ahead) the other runs the online softmax,
+//     so each SIMD's matrix core and vector ALU are fed by different waves;
+//     a workgroup barrier separates phases;
 //   * K and V arrive in LDS by direct global->LDS DMA (global_load_lds, 16 B
-//     per lane) into three-slot rings, two tiles ahead, with one workgroup
-//     barrier per tile; K rows are XOR-swizzled by 16-byte chunk, V stays
-//     row-major (32-byte chunks XOR-swizzled) and is read transposed with
-//     ds_read_b64_tr_b16, so no VALU work is spent on staging;
+//     per lane) into three-slot rings, issued two phases or more before use;
+//     K rows are XOR-swizzled by 16-byte chunk, V stays row-major (32-byte
+//     chunks XOR-swizzled) and is read transposed with ds_read_b64_tr_b16, so
+//     no VALU work is spent on staging and no LDS bank conflicts occur;
 //   * online softmax in fp32 with exp2 and scale*log2(e) folded into one FMA;
-//     O is rescaled only when some row's running maximum grew;
+//     the O^T accumulators are rescaled only when some row's maximum grew;
+//   * register budget (two waves per SIMD, 256 VGPRs each): the O^T and S^T
+//     accumulators, the Q slice, P and a short operand ring; operand addresses
+//     are one swizzled base per phase (XOR with a constant per MFMA) and the
+//     tile copies take a wave-uniform SGPR base plus a 32-bit lane offset, so
+//     the steady-state loop runs without spills;
 //   * with segment IDs, a prologue classifies every 64-key tile against the
 //     workgroup's query segments as skip / full / partial and compacts the
 //     active ones into an LDS list, so fully masked tiles cost nothing and
@@ -53,11 +59,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBq = 64 * kWaves;  // queries per workgroup
+constexpr int kBq = 32 * kWaves;  // queries per workgroup
 constexpr int kBk = 64;           // keys per tile
 constexpr int kSlots = 3;         // ring depth of the K, V and segment-ID stages
+#ifndef VDX_OPERAND_PREFETCH
+#define VDX_OPERAND_PREFETCH 4
+#endif
+constexpr int kOperandPrefetch = VDX_OPERAND_PREFETCH;  // MFMA operands in flight
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kMaxKvTiles = 30720;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -74,6 +84,7 @@ struct Tile {
     static constexpr int kRingBytes = kSegRegion + kSlots * kBk * 4;
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;        // rows per wave DMA
     static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;
+    static constexpr int kSegLanes = kBk / kWaves;               // seg IDs per wave DMA
     static constexpr int kSteps = D / 16;                        // MFMA k-steps over D
     static constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
     static_assert(kLoadsPerWave >= 1, "tile too small for the workgroup");
@@ -106,31 +117,39 @@ __device__ __forceinline__ void barrier() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 }
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else static_assert(N < 0, "unsupported count");
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    }
 }
 
 // Direct global->LDS copies: lane l's bytes land at LDS address M0 + size*l.
 // Issued as inline asm so that the compiler does not treat every later LDS read
 // as a possible alias of the in-flight copy (it would insert vmcnt(0) waits and
-// serialise the prefetch); completion is tracked by hand with wait_vm<N>() and
-// the workgroup barrier that follows it.
+// serialise the prefetch); completion is tracked by hand with wait_vm() and the
+// workgroup barrier that follows it.
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr(lds)) : "memory");
+__device__ __forceinline__ const char* lds_ptr(uint32_t a) {
+    return (const char*)((const __attribute__((address_space(3))) char*)(uintptr_t)a);
 }
-__device__ __forceinline__ void dma4(const void* g, char* lds) {
-    asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr(lds)) : "memory");
+// The global address is a wave-uniform base (SGPR pair) plus a per-lane
+// 32-bit byte offset.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, char* lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, char* lds) {
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds))
+                 : "memory");
 }
 
 __device__ __forceinline__ bf16x8 tr_read8(const char* p0, const char* p1) {
@@ -171,16 +190,18 @@ struct Attn {
     int64_t tok_stride;
     int S, n_kvt, wave, lane, lr, g;
     float c_log2;
-    int myseg[2];
-    int koff[T::kSteps];               // K operand read offsets (slot base, key block 0)
-    int voff[T::kDBlocks];             // V transposed-read offsets (slot base, key 0)
-    int dmak[T::kLoadsPerWave];        // per-lane element offsets of the K DMA in a tile
-    int dmav[T::kLoadsPerWave];
-    bf16x8 qreg[2][T::kSteps];
-    f32x16 oacc[2][T::kDBlocks];
-    f32x16 sacc[2][2];
-    bf16x8 pb[2][4];
-    float m_run[2], l_run[2], alpha[2];
+    int myseg;
+    // K operand of k-step ks sits at kx ^ (ks << 5) and the transposed V read
+    // of d-block db at vx ^ (db << 6) (offsets within a ring slot): the XOR
+    // swizzles only touch bits that these bases hold no other data in.
+    int kx, vx;
+    uint32_t dmak[T::kLoadsPerWave];   // per-lane byte offsets of the K DMA in a tile
+    uint32_t dmav[T::kLoadsPerWave];
+    bf16x8 qreg[T::kSteps];
+    f32x16 oacc[T::kDBlocks];
+    f32x16 sacc[2];
+    bf16x8 pb[4];
+    float m_run, l_run, alpha;
 
     __device__ __forceinline__ int tile_of(int n, bool& partial) const {
         if (SEG) {
@@ -192,129 +213,130 @@ struct Attn {
             return n;
         }
     }
+    __device__ __forceinline__ bool partial(int n) const {
+        bool p;
+        tile_of(n, p);
+        return p;
+    }
+    // Byte offset of ring slot n % kSlots.  Hidden from the optimiser, which
+    // would otherwise keep one strength-reduced induction variable per operand
+    // address (dozens of VGPRs) instead of adding the slot base per phase.
+    __device__ __forceinline__ static int slot_base(int n) {
+        int o = (n % kSlots) * T::kTileBytes;
+        asm volatile("" : "+s"(o));
+        return o;
+    }
+    __device__ __forceinline__ const int* sslot(int n) const {
+        return reinterpret_cast<const int*>(smem + T::kSegRegion) + (n % kSlots) * kBk;
+    }
 
     // ---- DMA of this wave's share of a K / V tile (rows past S read row S-1,
     // which the masks then exclude) and of a tile's segment IDs ----------------
-    __device__ __forceinline__ void dma_tile(const __bf16* base, const int* off, int t, char* dst) {
+    __device__ __forceinline__ void dma_tile(const __bf16* base, const uint32_t* off, int t,
+                                             char* dst) {
         const __bf16* src = base + (int64_t)t * kBk * tok_stride;
         if (t * kBk + kBk <= S) {
 #pragma unroll
-            for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(src + off[j], dst + j * 1024);
+            for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(src, off[j], dst + j * 1024);
         } else {
 #pragma unroll
             for (int j = 0; j < T::kLoadsPerWave; ++j) {
                 const int i = wave * T::kLoadsPerWave + j;
                 const int r = T::kRowsPerLoad * i + lane / T::kChunks;
                 const int over = max(0, t * kBk + r - (S - 1));
-                dma16(src + off[j] - (int64_t)over * tok_stride, dst + j * 1024);
+                dma16(src, off[j] - (uint32_t)over * (uint32_t)(2 * tok_stride), dst + j * 1024);
             }
         }
     }
-    __device__ __forceinline__ void dma_k(int n, int slot) {
+    __device__ __forceinline__ void dma_k(int n) {
         bool p;
         const int t = tile_of(n, p);
-        dma_tile(kp, dmak, t, smem + T::kKRegion + slot * T::kTileBytes + wave * T::kLoadsPerWave * 1024);
+        dma_tile(kp, dmak, t,
+                 smem + T::kKRegion + (n % kSlots) * T::kTileBytes + wave * T::kLoadsPerWave * 1024);
     }
-    __device__ __forceinline__ void dma_v(int n, int slot) {
+    __device__ __forceinline__ void dma_v(int n) {
         bool p;
         const int t = tile_of(n, p);
-        dma_tile(vp, dmav, t, smem + T::kVRegion + slot * T::kTileBytes + wave * T::kLoadsPerWave * 1024);
+        dma_tile(vp, dmav, t,
+                 smem + T::kVRegion + (n % kSlots) * T::kTileBytes + wave * T::kLoadsPerWave * 1024);
     }
-    __device__ __forceinline__ void dma_seg(int n, int slot) {
-        if (!SEG) return;
+    __device__ __forceinline__ void dma_seg(int n) {
         bool p;
         const int t = tile_of(n, p);
-        char* sdst = smem + T::kSegRegion + slot * kBk * 4 + wave * 64;
-        const int key = min(t * kBk + wave * 16 + (lane & 15), S - 1);
-        if (lane < 16) dma4(segkv + key, sdst);
+        char* sdst = smem + T::kSegRegion + (n % kSlots) * kBk * 4 + wave * T::kSegLanes * 4;
+        const int key = min(t * kBk + wave * T::kSegLanes + (lane % T::kSegLanes), S - 1);
+        if (lane < T::kSegLanes) dma4(segkv, 4u * (uint32_t)key, sdst);
+    }
+    // Loads of global phase p (every wave issues its share once per phase):
+    // even p = 2m: K of tile m+2 and segment IDs of tile m+1; odd p = 2m+1: V of
+    // tile m+1.  Ring slot x%3 of tile x then held tile x-3, whose last reader
+    // finished at phase 2m-1 (K), 2m-2 (seg) or 2m-1 (V).  Returns the number of
+    // loads issued.
+    __device__ __forceinline__ int dma_phase(int p, int n_act) {
+        const int m = p >> 1;
+        int cnt = 0;
+        if ((p & 1) == 0) {
+            if (m + 2 < n_act) {
+                dma_k(m + 2);
+                cnt += T::kLoadsPerWave;
+            }
+            if (SEG && m + 1 < n_act) {
+                dma_seg(m + 1);
+                cnt += 1;
+            }
+        } else if (m + 1 < n_act) {
+            dma_v(m + 1);
+            cnt += T::kLoadsPerWave;
+        }
+        return cnt;
     }
 
-    // ---- MFMA operands ----------------------------------------------------------
-    // MFMA i of a phase: first the P V ones (k-step kst, d-block db), then the
-    // K Q^T ones (k-step ks, key block kb).
+    // ---- MFMA phase ----------------------------------------------------------------
+    // MFMA i: first the P V ones (k-step kst, d-block db), then the K Q^T ones
+    // (k-step ks, key block kb).
     template <bool PV>
     static constexpr int n_pv() { return PV ? 4 * T::kDBlocks : 0; }
+    // vb / kb: LDS byte addresses of this lane's V and K operand bases in the
+    // current ring slots (slot and region offsets are multiples of 1024, so the
+    // swizzle XOR can be applied to the full address).
     template <bool PV, int I>
-    __device__ __forceinline__ bf16x8 operand(const char* vb, const char* kb) const {
+    __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb) const {
         if constexpr (I < n_pv<PV>()) {
             constexpr int kst = I / T::kDBlocks, db = I % T::kDBlocks;
-            const char* p = vb + voff[db] + kst * 16 * T::kRowBytes;
+            const char* p = lds_ptr((vb ^ (db << 6)) + kst * 16 * T::kRowBytes);
             return tr_read8(p, p + 4 * T::kRowBytes);
         } else {
             constexpr int j = I - n_pv<PV>();
             constexpr int ks = j / 2, kbk = j % 2;
-            return *reinterpret_cast<const bf16x8*>(kb + koff[ks] + kbk * 32 * T::kRowBytes);
+            return *reinterpret_cast<const bf16x8*>(lds_ptr((kb ^ (ks << 5)) + kbk * 32 * T::kRowBytes));
         }
     }
-    template <bool PV, int HM, int I>
+    template <bool PV, int I>
     __device__ __forceinline__ void mfma(const bf16x8& a) {
         if constexpr (I < n_pv<PV>()) {
             constexpr int kst = I / T::kDBlocks, db = I % T::kDBlocks;
-            oacc[HM][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[HM][kst], oacc[HM][db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kst], oacc[db], 0, 0, 0);
         } else {
             constexpr int j = I - n_pv<PV>();
             constexpr int ks = j / 2, kbk = j % 2;
             if constexpr (ks == 0)
-                sacc[HM][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[HM][0], f32x16{}, 0, 0, 0);
+                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
             else
-                sacc[HM][kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[HM][ks], sacc[HM][kbk], 0, 0, 0);
+                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kbk], 0, 0, 0);
         }
     }
-
-    // ---- online softmax, cut into slices that ride in the MFMA shadow ----------
-    // Values of half h: v(k) = sacc[h][k / 16][k % 16], k = 0..31.
-    float sm_mx0, sm_mx1, sm_msub, sm_ls[4];
-    __device__ __forceinline__ float sv(int h, int k) const { return sacc[h][k >> 4][k & 15]; }
-    template <int H, int STEP, int NSTEPS>
-    __device__ __forceinline__ void softmax_slice() {
-        if constexpr (STEP == 0) {
-            float m = fmaxf(fmaxf(sv(H, 0), sv(H, 1)), sv(H, 2));
-#pragma unroll
-            for (int k = 3; k < 15; k += 2) m = fmaxf(fmaxf(m, sv(H, k)), sv(H, k + 1));
-            sm_mx0 = fmaxf(m, sv(H, 15));
-        } else if constexpr (STEP == 1) {
-            float m = fmaxf(fmaxf(sv(H, 16), sv(H, 17)), sv(H, 18));
-#pragma unroll
-            for (int k = 19; k < 31; k += 2) m = fmaxf(fmaxf(m, sv(H, k)), sv(H, k + 1));
-            sm_mx1 = fmaxf(m, sv(H, 31));
-        } else if constexpr (STEP == 2) {
-            const float mx = pair_max(fmaxf(sm_mx0, sm_mx1));
-            const float m_old = m_run[H];
-            const float m_new = fmaxf(m_old, mx * c_log2);
-            // alpha == 1 exactly when the maximum did not move (exp2(0) = 1).
-            alpha[H] = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
-            m_run[H] = m_new;
-            sm_msub = (m_new == -INFINITY) ? 0.f : m_new;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm_ls[i] = 0.f;
-        }
-        // 16 pairs of values spread over steps 3 .. NSTEPS-2.
-        static_for<0, 16>([&](auto kc) {
-            constexpr int k = kc;
-            if constexpr (STEP == 3 + k * (NSTEPS - 4) / 16) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv(H, 2 * k), c_log2, -sm_msub));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv(H, 2 * k + 1), c_log2, -sm_msub));
-                sm_ls[(2 * k) & 3] += p0;
-                sm_ls[(2 * k + 1) & 3] += p1;
-                // value k' sits in pb[h][k'/8][k'%8]
-                pb[H][(2 * k) >> 3][(2 * k) & 7] = (__bf16)p0;
-                pb[H][(2 * k + 1) >> 3][(2 * k + 1) & 7] = (__bf16)p1;
-            }
-        });
-        if constexpr (STEP == NSTEPS - 1)
-            l_run[H] = __builtin_fmaf(alpha[H], l_run[H], (sm_ls[0] + sm_ls[1]) + (sm_ls[2] + sm_ls[3]));
-    }
-
-    // One pipeline phase: the MFMAs of half HM (P V of the previous tile if PV,
-    // K Q^T of the current tile if QK) issued one per step with their LDS
-    // operands fetched PF steps ahead, and, if SM, the online softmax of the
-    // other half cut into one slice per step.  A scheduling fence closes every
-    // step so the interleaving survives compilation.
-    template <int HM, bool PV, bool QK, bool SM>
-    __device__ __forceinline__ void phase(const char* vb, const char* kb) {
+    // P V of the previous tile (if PV) and K Q^T of the current tile (if QK): one
+    // MFMA per step, LDS operands fetched kOperandPrefetch steps ahead into a
+    // ring two entries longer, so a register is refilled only after the MFMA
+    // that read it has long issued.  A scheduling fence closes every step.
+    template <bool PV, bool QK>
+    __device__ __forceinline__ void mfma_phase(int vtile, int ktile) {
+        const uint32_t vb = lds_addr(smem) + T::kVRegion + slot_base(vtile) + vx;
+        const uint32_t kb = lds_addr(smem) + T::kKRegion + slot_base(ktile) + kx;
         constexpr int NM = n_pv<PV>() + (QK ? 2 * T::kSteps : 0);
-        constexpr int PF = 3, RING = PF + 1;
+        constexpr int PF = kOperandPrefetch, RING = PF + 2;
         bf16x8 ops[RING];
+        __builtin_amdgcn_s_setprio(1);
         static_for<0, PF>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i < NM) ops[i % RING] = operand<PV, i>(vb, kb);
@@ -322,107 +344,82 @@ struct Attn {
         static_for<0, NM>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i + PF < NM) ops[(i + PF) % RING] = operand<PV, i + PF>(vb, kb);
-            mfma<PV, HM, i>(ops[i % RING]);
-            if constexpr (SM) softmax_slice<1 - HM, i, NM>();
+            mfma<PV, i>(ops[i % RING]);
             __builtin_amdgcn_sched_barrier(0);
         });
-        if constexpr (SM) {
-            // Pin the softmax results inside this phase: without a use here the
-            // optimiser sinks the whole softmax next to its consumers (the next
-            // phase's P V), which would serialise it behind those MFMAs.
-            constexpr int HS = 1 - HM;
-            asm volatile("" ::"v"(pb[HS][0]), "v"(pb[HS][1]), "v"(pb[HS][2]), "v"(pb[HS][3]),
-                         "v"(l_run[HS]), "v"(m_run[HS]), "v"(alpha[HS]));
-        }
+        __builtin_amdgcn_s_setprio(0);
     }
 
-    // Element masks of half h for active tile n (partial tiles only), seg IDs
-    // of the tile at sbase.  Key of register r of block b: b*32 + 16*(r>>3) + 8g + (r&7).
-    __device__ __forceinline__ void mask(int h, int n, const int* sbase) {
+    // ---- VALU phase ----------------------------------------------------------------
+    // Element masks for active tile n (partial tiles only).  Key of accumulator
+    // register r of block b: b*32 + 16*(r>>3) + 8g + (r&7).
+    __device__ __forceinline__ void mask(int n) {
         bool partial;
         const int t = tile_of(n, partial);
         const int lim = S - t * kBk - 8 * g;
-        const int* segt = sbase + 8 * g;
+        const int* segt = sslot(n) + 8 * g;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int jc = b * 32 + 16 * (r >> 3) + (r & 7);
                 bool ok = jc < lim;
-                if (SEG) ok = ok && (segt[jc] == myseg[h]) && (myseg[h] != 0);
-                if (!ok) sacc[h][b][r] = -INFINITY;
+                if (SEG) ok = ok && (segt[jc] == myseg) && (myseg != 0);
+                if (!ok) sacc[b][r] = -INFINITY;
             }
         }
     }
-
-    // O *= alpha for half h when some row's maximum moved.  The accumulators
-    // live in AGPRs; the multiply is spelled out on them so that the compiler
-    // keeps them there for the MFMAs instead of shuttling them through VGPRs.
-    __device__ __forceinline__ void rescale(int h) {
-        if (__ballot(alpha[h] != 1.0f) != 0ull) {
+    // Online softmax of the current scores: running max in the log2 domain,
+    // P = 2^(s*scale*log2(e) - m) in bf16 for the next P V, l += row sum.
+    __device__ __forceinline__ void softmax() {
+        float mx0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+        float mx1 = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
 #pragma unroll
-            for (int db = 0; db < T::kDBlocks; ++db) {
+        for (int r = 3; r < 15; r += 2) {
+            mx0 = fmaxf(fmaxf(mx0, sacc[0][r]), sacc[0][r + 1]);
+            mx1 = fmaxf(fmaxf(mx1, sacc[1][r]), sacc[1][r + 1]);
+        }
+        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15])));
+        const float m_old = m_run;
+        const float m_new = fmaxf(m_old, mx * c_log2);
+        // alpha == 1 exactly when the maximum did not move (exp2(0) = 1).
+        alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
+        m_run = m_new;
+        const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float t;
-                    asm("v_accvgpr_read_b32 %1, %0\n\t"
-                        "v_mul_f32 %1, %1, %2\n\t"
-                        "v_accvgpr_write_b32 %0, %1"
-                        : "+a"(oacc[h][db][r]), "=&v"(t)
-                        : "v"(alpha[h]));
-                }
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][r], c_log2, -msub));
+                ls[r & 3] += p;
+                pb[b * 2 + (r >> 3)][r & 7] = (__bf16)p;
             }
         }
+        l_run = __builtin_fmaf(alpha, l_run, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+        // Pin the results inside this phase: without a use here the optimiser
+        // sinks the softmax next to its consumer (the next MFMA phase), which
+        // would serialise it behind those MFMAs.
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run), "v"(m_run),
+                     "v"(alpha));
     }
-
-    __device__ __forceinline__ const char* kslot(int r) const { return smem + T::kKRegion + r * T::kTileBytes; }
-    __device__ __forceinline__ const char* vslot(int r) const { return smem + T::kVRegion + r * T::kTileBytes; }
-    __device__ __forceinline__ const int* sslot(int r) const {
-        return reinterpret_cast<const int*>(smem + T::kSegRegion) + r * kBk;
-    }
-    __device__ __forceinline__ bool partial(int n) const {
-        bool p;
-        tile_of(n, p);
-        return p;
-    }
-
-    // Steady-state iteration n (1 <= n < n_act), R = n % 3: S(n) of both halves
-    // and P V of tile n-1.  Loads issued here: segment IDs of tile n+1, K of
-    // tile n+2 and V of tile n+1, into ring slots whose previous tiles were last
-    // read in iteration n-1.
-    template <int R>
-    __device__ __forceinline__ void iteration(int n, int n_act) {
-        constexpr int R1 = (R + 1) % kSlots, R2 = (R + 2) % kSlots;
-        const bool ld_v = n + 1 < n_act;
-        const bool ld_k = n + 2 < n_act;
-        if (ld_v) dma_seg(n + 1, R1);
-        if (ld_k) dma_k(n + 2, R2);
-        if (ld_v) dma_v(n + 1, R1);
-        const bool part = partial(n);
-        phase<0, true, true, true>(vslot(R2), kslot(R));   // A: P V(n-1), S(n);  B: softmax(n-1)
-        rescale(1);
-        if (part) mask(0, n, sslot(R));
-        phase<1, true, true, true>(vslot(R2), kslot(R));   // B: P V(n-1), S(n);  A: softmax(n)
-        rescale(0);
-        if (part) mask(1, n, sslot(R));
-        constexpr int kv = T::kLoadsPerWave;
-        if (ld_k)
-            wait_vm<2 * kv>();
-        else if (ld_v)
-            wait_vm<kv>();
-        else
-            wait_vm<0>();
-        barrier();
+    // O *= alpha when some row's maximum moved (rare after the first tiles).
+    __device__ __forceinline__ void rescale() {
+        if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+            for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
     }
 };
 
 template <int D, bool SEG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                     const __bf16* __restrict__ v, const int32_t* __restrict__ seg_q,
-                     const int32_t* __restrict__ seg_kv, __bf16* __restrict__ out,
-                     float* __restrict__ lse, int S, int H, float c_log2, int n_qblk, int n_kvt,
-                     int n_wg) {
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
+    __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
+    int n_kvt, int n_wg) {
     using T = Tile<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -437,9 +434,10 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int b = bh / H;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, g = lane >> 5;
-    const int qbase = qblk * kBq + wave * 64;
+    const int grp = wave >> 2;  // ping-pong group; waves w and w+4 share a SIMD
+    const int qi = qblk * kBq + wave * 32 + lr;
 
     Attn<D, SEG> A;
     A.smem = smem;
@@ -455,32 +453,28 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     A.g = g;
     A.c_log2 = c_log2;
 
-    // ---- Q slices -> registers as the B operand of S^T = K Q^T ----------------
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int qi = qbase + 32 * hh + lr;
+    // ---- Q slice -> registers as the B operand of S^T = K Q^T -----------------
+    {
         const __bf16* qrow = q + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < T::kSteps; ++ks)
-            A.qreg[hh][ks] = (qi < S) ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : bf16x8{};
-        A.myseg[hh] = SEG ? ((qi < S) ? seg_q[(int64_t)b * S + qi] : 0) : 1;
+            A.qreg[ks] = (qi < S) ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : bf16x8{};
+        A.myseg = SEG ? ((qi < S) ? seg_q[(int64_t)b * S + qi] : 0) : 1;
     }
     // ---- per-lane LDS offsets ---------------------------------------------------
     {
+        // K: lane (lr, g) of k-step ks reads chunk 2ks+g of row swap23(lr), stored
+        // at chunk (2ks+g) ^ ksw = (g ^ ksw) ^ 2ks.
         const int ksw = lr & (T::kChunks - 1);  // == k_swz(row) for row = swap23(lr)
-#pragma unroll
-        for (int ks = 0; ks < T::kSteps; ++ks)
-            A.koff[ks] = swap23(lr) * T::kRowBytes + (((2 * ks + g) ^ ksw) << 4);
+        A.kx = swap23(lr) * T::kRowBytes + ((g ^ ksw) << 4);
         // Transposed V read: group q = lane/16 takes d = db*32 + 16(q&1) + 4(j&3)
-        // and keys 8(q>>1) + (j>>2) (+4 for the second half of the operand).
+        // and keys 8(q>>1) + (j>>2) (+4 for the second half of the operand); the
+        // 32-byte chunk 2db + (q&1) sits at (2db + (q&1)) ^ vsw = ((q&1) ^ vsw) ^ 2db
+        // (vsw is even).
         const int qg = lane >> 4, j = lane & 15;
         const int key = 8 * (qg >> 1) + (j >> 2);
         const int vsw = v_swz<D>(key);
-#pragma unroll
-        for (int db = 0; db < T::kDBlocks; ++db) {
-            const int h32 = 2 * db + (qg & 1);  // 32-byte chunk of d
-            A.voff[db] = key * T::kRowBytes + 32 * (h32 ^ vsw) + 16 * ((j & 3) >> 1) + 8 * (j & 1);
-        }
+        A.vx = key * T::kRowBytes + 32 * ((qg & 1) ^ vsw) + 16 * ((j & 3) >> 1) + 8 * (j & 1);
         // DMA: instruction i of the tile covers rows kRowsPerLoad*i .. ; lane lands
         // at LDS position pos of its row and fetches the chunk stored there.
 #pragma unroll
@@ -490,35 +484,31 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const int pos = lane % T::kChunks;
             const int ck = pos ^ k_swz<D>(r);
             const int cv = 2 * ((pos >> 1) ^ v_swz<D>(r)) + (pos & 1);
-            A.dmak[jj] = r * (int)A.tok_stride + ck * 8;
-            A.dmav[jj] = r * (int)A.tok_stride + cv * 8;
+            A.dmak[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + ck * 8);
+            A.dmav[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + cv * 8);
         }
     }
 
     uint16_t* list = reinterpret_cast<uint16_t*>(smem + T::kRingBytes);
     int* meta = reinterpret_cast<int*>(smem + ((T::kRingBytes + 2 * (SEG ? n_kvt : 0) + 15) & ~15));
-    // meta: [0..3] per-wave q min, [4..7] q max, [8..11] q flags, [12] n_active
+    // meta: [0..7] per-wave q min, [8..15] q max, [16..23] q flags, [24] n_active
     A.list = list;
 
     int n_act = n_kvt;
     if (SEG) {
         // ---- query-block segment summary --------------------------------------
         {
-            int mn = INT32_MAX, mx = INT32_MIN, fl = 0;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int s = A.myseg[hh];
-                mn = min(mn, (s != 0) ? s : INT32_MAX);
-                mx = max(mx, (s != 0) ? s : INT32_MIN);
-                fl |= (s == 0) ? 1 : 0;  // pad or out-of-range row present
-            }
+            const int s = A.myseg;
+            int mn = (s != 0) ? s : INT32_MAX;
+            int mx = (s != 0) ? s : INT32_MIN;
+            int fl = (s == 0) ? 1 : 0;  // pad or out-of-range row present
             mn = wave_min(mn);
             mx = wave_max(mx);
             fl = wave_max(fl);
             if (lane == 0) {
                 meta[wave] = mn;
-                meta[4 + wave] = mx;
-                meta[8 + wave] = fl;
+                meta[8 + wave] = mx;
+                meta[16 + wave] = fl;
             }
         }
         __syncthreads();
@@ -526,8 +516,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {
             qmn = min(qmn, meta[i]);
-            qmx = max(qmx, meta[4 + i]);
-            qfl |= meta[8 + i];
+            qmx = max(qmx, meta[8 + i]);
+            qfl |= meta[16 + i];
         }
         // ---- classify every key tile: 0 skip, 1 full, 2 partial ---------------
         uint8_t* cls = reinterpret_cast<uint8_t*>(smem);  // aliases the rings
@@ -563,104 +553,98 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
                 base += __popcll(m);
             }
-            if (lane == 0) meta[12] = base;
+            if (lane == 0) meta[24] = base;
         }
         __syncthreads();
-        n_act = meta[12];
+        n_act = meta[24];
     }
 
     // ---- running softmax state and the O^T accumulators -----------------------
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int i = 0; i < T::kDBlocks; ++i) A.oacc[i] = f32x16{};
 #pragma unroll
-        for (int i = 0; i < T::kDBlocks; ++i) A.oacc[hh][i] = f32x16{};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) A.pb[hh][i] = bf16x8{};
-        A.m_run[hh] = -INFINITY;  // running max of scale*log2(e)*s for this lane's query
-        A.l_run[hh] = 0.f;        // this lane's partial sum (its half of each tile's keys)
-        A.alpha[hh] = 1.f;
-    }
+    for (int i = 0; i < 4; ++i) A.pb[i] = bf16x8{};
+    A.m_run = -INFINITY;  // running max of scale*log2(e)*s for this lane's query
+    A.l_run = 0.f;        // this lane's partial sum (its half of each tile's keys)
+    A.alpha = 1.f;
 
-    // ---- prologue: segment IDs and K of tile 0, K of tile 1, V of tile 0 ---------
+    // ---- prologue: K of tiles 0 and 1, V and segment IDs of tile 0 -------------
     if (n_act > 0) {
-        A.dma_seg(0, 0);
-        A.dma_k(0, 0);
-        A.dma_v(0, 0);
+        A.dma_k(0);
+        A.dma_v(0);
+        if (SEG) A.dma_seg(0);
     }
-    if (n_act > 1) A.dma_k(1, 1);
-    wait_vm<0>();
+    if (n_act > 1) A.dma_k(1);
+    wait_vm(0);
     barrier();
+    // A use of the Q registers (and the query's segment ID) here makes the
+    // compiler wait for their loads before the loop rather than inside it,
+    // where a vmcnt wait would also drain the in-flight tile copies.
+    asm volatile("" ::"v"(A.qreg[0]), "v"(A.qreg[T::kSteps - 1]), "v"(A.myseg));
 
-    // ---- main loop: iteration n computes S(n) and P V of tile n-1 ---------------
-    // Ring slots: K, V and segment IDs of tile n all live in slot n % 3.
-    if (n_act > 0) {
-        // iteration 0: K Q^T of both halves, softmax of half A
-        constexpr int kv = T::kLoadsPerWave;
-        if (n_act > 1) A.dma_seg(1, 1);
-        if (n_act > 2) A.dma_k(2, 2);
-        if (n_act > 1) A.dma_v(1, 1);
-        const bool part = A.partial(0);
-        A.template phase<0, false, true, false>(nullptr, A.kslot(0));
-        if (part) A.mask(0, 0, A.sslot(0));
-        A.template phase<1, false, true, true>(nullptr, A.kslot(0));
-        A.rescale(0);
-        if (part) A.mask(1, 0, A.sslot(0));
-        if (n_act > 2)
-            wait_vm<2 * kv>();
-        else if (n_act > 1)
-            wait_vm<kv>();
-        else
-            wait_vm<0>();
+    // ---- ping-pong main loop --------------------------------------------------------
+    // Local iteration n: MFMA phase (P V of tile n-1, K Q^T of tile n) at global
+    // phase 2n + grp, then the VALU phase (softmax of tile n) at 2n + 1 + grp.
+    // Every wave issues its DMA share for each global phase once and, before
+    // each barrier, waits for the loads of all but the last two phases.
+    int cnt_prev = 0;
+    auto end_phase = [&](int p) {
+        const int c = A.dma_phase(p, n_act);
+        wait_vm(cnt_prev + c);
+        cnt_prev = c;
         barrier();
-    }
-    int n = 1;
-    for (; n + 2 < n_act; n += 3) {
-        A.template iteration<1>(n, n_act);
-        A.template iteration<2>(n + 1, n_act);
-        A.template iteration<0>(n + 2, n_act);
-    }
-    if (n < n_act) A.template iteration<1>(n, n_act);
-    if (n + 1 < n_act) A.template iteration<2>(n + 1, n_act);
+    };
+    // The first and last iterations are peeled so that the steady-state body
+    // has a single MFMA phase shape (no register shuffling at control-flow joins).
+    auto valu_phase = [&](int n) {
+        if (A.partial(n)) A.mask(n);
+        A.softmax();
+        A.rescale();
+        end_phase(2 * n + 1 + grp);
+    };
     if (n_act > 0) {
-        // final iteration: P V of the last tile for both halves
-        const char* vb = A.vslot((n_act - 1) % kSlots);
-        A.template phase<0, true, false, true>(vb, nullptr);
-        A.rescale(1);
-        A.template phase<1, true, false, false>(vb, nullptr);
+        if (grp == 1) end_phase(0);  // group 1 idles in global phase 0
+        A.template mfma_phase<false, true>(0, 0);
+        end_phase(grp);
+        valu_phase(0);
+        for (int n = 1; n < n_act; ++n) {
+            A.template mfma_phase<true, true>(n - 1, n);
+            end_phase(2 * n + grp);
+            valu_phase(n);
+        }
+        A.template mfma_phase<true, false>(n_act - 1, 0);
+        end_phase(2 * n_act + grp);
+        if (grp == 0) end_phase(2 * n_act + 1);  // group 0 idles in the last global phase
     }
 
     // ---- epilogue: normalise, write out (bf16) and lse (fp32) ----------------
+    const float l_tot = pair_sum(A.l_run);
+    if (qi < S) {
+        __bf16* orow = out + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D;
+        float lse_v;
+        if (l_tot > 0.f) {
+            const float inv = 1.0f / l_tot;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int qi = qbase + 32 * hh + lr;
-        const float l_tot = pair_sum(A.l_run[hh]);
-        if (qi < S) {
-            __bf16* orow = out + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D;
-            float lse_v;
-            if (l_tot > 0.f) {
-                const float inv = 1.0f / l_tot;
+            for (int db = 0; db < T::kDBlocks; ++db) {
 #pragma unroll
-                for (int db = 0; db < T::kDBlocks; ++db) {
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = db * 32 + 8 * r4 + 4 * g;
+                    __bf16 o4[4];
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int d = db * 32 + 8 * r4 + 4 * g;
-                        __bf16 o4[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(A.oacc[hh][db][4 * r4 + e] * inv);
-                        *reinterpret_cast<uint2*>(orow + d) = *reinterpret_cast<const uint2*>(o4);
-                    }
+                    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(A.oacc[db][4 * r4 + e] * inv);
+                    *reinterpret_cast<uint2*>(orow + d) = *reinterpret_cast<const uint2*>(o4);
                 }
-                lse_v = (A.m_run[hh] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-            } else {
-#pragma unroll
-                for (int db = 0; db < T::kDBlocks; ++db)
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4)
-                        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * r4 + 4 * g) = uint2{0u, 0u};
-                lse_v = -INFINITY;
             }
-            if (g == 0) lse[((int64_t)b * H + h) * S + qi] = lse_v;
+            lse_v = (A.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        } else {
+#pragma unroll
+            for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<uint2*>(orow + db * 32 + 8 * r4 + 4 * g) = uint2{0u, 0u};
+            lse_v = -INFINITY;
         }
+        if (g == 0) lse[((int64_t)b * H + h) * S + qi] = lse_v;
     }
 }
 
@@ -674,7 +658,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     size_t lds = (size_t)T::kRingBytes;
     if (SEG) lds += 2 * (size_t)n_kvt;
     lds = (lds + 15) & ~(size_t)15;
-    lds += 16 * sizeof(int);  // meta
+    lds += 32 * sizeof(int);  // meta
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, SEG>), dim3(n_wg), dim3(kThreads), lds, stream,
                        reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),

@@ -58,20 +58,27 @@ def test_zero_query_closed_form_every_row(need_gpu, name):
     out, lse = _run(d, w)
     del d
     runs = w.seg_runs if w.seg_runs is not None else [(0, w.S, 1)]
+    # Group the runs by segment ID: runs sharing an ID form one segment.
+    by_id = {}
+    for a, e, sid in runs:
+        by_id.setdefault(sid, []).append((a, e))
     v = x["v"]
     for b in range(w.B):
-        for a, e, sid in runs:
+        for sid, spans in by_id.items():
+            n_tok = sum(e - a for a, e in spans)
             for h in range(w.H):
-                o = out[b, a:e, h].float().cpu().numpy()
-                l = lse[b, h, a:e].cpu().numpy()
                 if sid == 0:
-                    assert np.all(out[b, a:e, h].view(torch.int16).cpu().numpy() == 0)
-                    assert np.all(np.isneginf(l))
+                    for a, e in spans:
+                        assert np.all(out[b, a:e, h].view(torch.int16).cpu().numpy() == 0)
+                        assert np.all(np.isneginf(lse[b, h, a:e].cpu().numpy()))
                     continue
-                mean = v[b, a:e, h].double().mean(0).numpy()
-                err = np.abs(o - mean[None]).max()
-                assert err <= OUT_ATOL, (b, a, e, h, err)
-                # bf16 rounding of the mean itself is the dominant error here
-                assert err <= np.abs(mean).max() * 2.0 ** -8 + 1e-6, (b, a, e, h, err)
-                assert np.abs(l - math.log(e - a)).max() <= LSE_ATOL
+                mean = sum(v[b, a:e, h].double().sum(0) for a, e in spans).numpy() / n_tok
+                for a, e in spans:
+                    o = out[b, a:e, h].float().cpu().numpy()
+                    l = lse[b, h, a:e].cpu().numpy()
+                    err = np.abs(o - mean[None]).max()
+                    assert err <= OUT_ATOL, (b, a, e, h, err)
+                    # bf16 rounding of the mean itself is the dominant error here
+                    assert err <= np.abs(mean).max() * 2.0 ** -8 + 1e-6, (b, a, e, h, err)
+                    assert np.abs(l - math.log(n_tok)).max() <= LSE_ATOL
     del out, lse
