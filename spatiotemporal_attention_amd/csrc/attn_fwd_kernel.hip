@@ -63,6 +63,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBq = 32 * kWaves;  // queries per workgroup
 constexpr int kBk = 64;           // keys per tile
+constexpr int kDmaWaves = kWaves / 2;  // one ping-pong group issues each tile copy
 constexpr int kSlots = 3;         // ring depth of the K, V and segment-ID stages
 #ifndef VDX_OPERAND_PREFETCH
 #define VDX_OPERAND_PREFETCH 4
@@ -83,8 +84,7 @@ struct Tile {
     static constexpr int kSegRegion = kVRegion + kSlots * kTileBytes;
     static constexpr int kRingBytes = kSegRegion + kSlots * kBk * 4;
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;        // rows per wave DMA
-    static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;
-    static constexpr int kSegLanes = kBk / kWaves;               // seg IDs per wave DMA
+    static constexpr int kLoadsPerWave = kTileBytes / 1024 / kDmaWaves;
     static constexpr int kSteps = D / 16;                        // MFMA k-steps over D
     static constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
     static_assert(kLoadsPerWave >= 1, "tile too small for the workgroup");
@@ -142,13 +142,19 @@ __device__ __forceinline__ const char* lds_ptr(uint32_t a) {
     return (const char*)((const __attribute__((address_space(3))) char*)(uintptr_t)a);
 }
 // The global address is a wave-uniform base (SGPR pair) plus a per-lane
-// 32-bit byte offset.
+// 32-bit byte offset.  The s_nop 4 supplies the wait states GFX9 requires
+// before a vector-memory instruction that reads an SGPR (the base pair, M0)
+// written by a VALU instruction (five; the compiler may reload a spilled SGPR
+// with v_readlane right before the asm) or M0 written by SALU (one): the
+// hazard recogniser does not look inside inline asm.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, char* lds) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds))
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                 "{m0}"(lds_addr(lds))
                  : "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, char* lds) {
-    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds))
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+                 "{m0}"(lds_addr(lds))
                  : "memory");
 }
 
@@ -195,12 +201,15 @@ struct Attn {
     // of d-block db at vx ^ (db << 6) (offsets within a ring slot): the XOR
     // swizzles only touch bits that these bases hold no other data in.
     int kx, vx;
-    uint32_t dmak[T::kLoadsPerWave];   // per-lane byte offsets of the K DMA in a tile
-    uint32_t dmav[T::kLoadsPerWave];
+    // Per-lane byte offsets of this wave's share of a tile copy (group 0 waves
+    // copy K tiles and segment IDs, group 1 waves V tiles); w4 = wave & 3.
+    uint32_t dmo[T::kLoadsPerWave];
+    int w4;
     bf16x8 qreg[T::kSteps];
     f32x16 oacc[T::kDBlocks];
     f32x16 sacc[2];
     bf16x8 pb[4];
+    bf16x8 ops[kOperandPrefetch + 2];  // MFMA operand ring
     float m_run, l_run, alpha;
 
     __device__ __forceinline__ int tile_of(int n, bool& partial) const {
@@ -230,121 +239,155 @@ struct Attn {
         return reinterpret_cast<const int*>(smem + T::kSegRegion) + (n % kSlots) * kBk;
     }
 
-    // ---- DMA of this wave's share of a K / V tile (rows past S read row S-1,
-    // which the masks then exclude) and of a tile's segment IDs ----------------
-    __device__ __forceinline__ void dma_tile(const __bf16* base, const uint32_t* off, int t,
-                                             char* dst) {
-        const __bf16* src = base + (int64_t)t * kBk * tok_stride;
-        if (t * kBk + kBk <= S) {
-#pragma unroll
-            for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(src, off[j], dst + j * 1024);
-        } else {
+    // ---- tile copies ---------------------------------------------------------------
+    // In its MFMA phase of local iteration n, a wave of group G copies its share
+    // of K (G = 0) or V (G = 1) of active tile a = n + 2 - G into ring slot
+    // a % 3, and wave 0 of group 0 copies the segment IDs of active tile n + 1.
+    // In global-phase terms (the MFMA phase of iteration n is phase 2n + G):
+    // K of tile m+2 and segment IDs of tile m+1 in phase 2m, V of tile m+1 in
+    // phase 2m+1.  Slot a % 3 then held tile a-3, whose last reader finished
+    // in phase 2m-1 (K, V) or 2m-2 (segment IDs).  Each wave waits for its
+    // copies at the end of its next MFMA phase, before the barrier that
+    // precedes their first reader.
+    struct Copy {
+        const __bf16* src;  // tile base in global memory (wave-uniform)
+        char* dst;          // this wave's share of the ring slot
+        int t;              // key tile index
+        int seg_t, seg_a;   // segment-ID copy (tile, active index), seg_a < 0: none
+        bool spread;        // full tile: the loads go out between MFMAs
+        bool tail;          // last, partial tile: issued at the phase start
+        int cnt;            // loads this wave issues for the copy
+    };
+    // Plans the copies of the MFMA phase of iteration a - 2 + G (run in the
+    // preceding VALU phase: scalar work only, nothing is issued).
+    template <int G>
+    __device__ __forceinline__ void plan(Copy& c, int a, int n_act) {
+        bool part;
+        c.cnt = 0;
+        c.spread = c.tail = false;
+        c.seg_a = -1;
+        if (a < n_act) {
+            c.t = tile_of(a, part);
+            c.src = (G ? vp : kp) + (int64_t)c.t * kBk * tok_stride;
+            c.dst = smem + (G ? T::kVRegion : T::kKRegion) + slot_base(a) +
+                    w4 * T::kLoadsPerWave * 1024;
+            c.spread = c.t * kBk + kBk <= S;
+            c.tail = !c.spread;
+            c.cnt = T::kLoadsPerWave;
+        }
+        if (SEG && G == 0 && w4 == 0 && a >= 1 && a - 1 < n_act) {
+            c.seg_a = a - 1;
+            c.seg_t = tile_of(a - 1, part);
+            c.cnt += 1;
+        }
+    }
+    // Issued at the start of the MFMA phase: the segment IDs (64 keys, one per
+    // lane) and, for the tail tile, the whole K/V share with rows past S
+    // reading row S-1 (the masks exclude them).
+    __device__ __forceinline__ void copy_start(const Copy& c) {
+        if (SEG && c.seg_a >= 0) {
+            char* sdst = smem + T::kSegRegion + (c.seg_a % kSlots) * kBk * 4;
+            const int key = min(c.seg_t * kBk + lane, S - 1);
+            dma4(segkv, 4u * (uint32_t)key, sdst);
+        }
+        if (c.tail) {
 #pragma unroll
             for (int j = 0; j < T::kLoadsPerWave; ++j) {
-                const int i = wave * T::kLoadsPerWave + j;
+                const int i = w4 * T::kLoadsPerWave + j;
                 const int r = T::kRowsPerLoad * i + lane / T::kChunks;
-                const int over = max(0, t * kBk + r - (S - 1));
-                dma16(src, off[j] - (uint32_t)over * (uint32_t)(2 * tok_stride), dst + j * 1024);
+                const int over = max(0, c.t * kBk + r - (S - 1));
+                dma16(c.src, dmo[j] - (uint32_t)over * (uint32_t)(2 * tok_stride), c.dst + j * 1024);
             }
         }
     }
-    __device__ __forceinline__ void dma_k(int n) {
-        bool p;
-        const int t = tile_of(n, p);
-        dma_tile(kp, dmak, t,
-                 smem + T::kKRegion + (n % kSlots) * T::kTileBytes + wave * T::kLoadsPerWave * 1024);
-    }
-    __device__ __forceinline__ void dma_v(int n) {
-        bool p;
-        const int t = tile_of(n, p);
-        dma_tile(vp, dmav, t,
-                 smem + T::kVRegion + (n % kSlots) * T::kTileBytes + wave * T::kLoadsPerWave * 1024);
-    }
-    __device__ __forceinline__ void dma_seg(int n) {
-        bool p;
-        const int t = tile_of(n, p);
-        char* sdst = smem + T::kSegRegion + (n % kSlots) * kBk * 4 + wave * T::kSegLanes * 4;
-        const int key = min(t * kBk + wave * T::kSegLanes + (lane % T::kSegLanes), S - 1);
-        if (lane < T::kSegLanes) dma4(segkv, 4u * (uint32_t)key, sdst);
-    }
-    // Loads of global phase p (every wave issues its share once per phase):
-    // even p = 2m: K of tile m+2 and segment IDs of tile m+1; odd p = 2m+1: V of
-    // tile m+1.  Ring slot x%3 of tile x then held tile x-3, whose last reader
-    // finished at phase 2m-1 (K), 2m-2 (seg) or 2m-1 (V).  Returns the number of
-    // loads issued.
-    __device__ __forceinline__ int dma_phase(int p, int n_act) {
-        const int m = p >> 1;
-        int cnt = 0;
-        if ((p & 1) == 0) {
-            if (m + 2 < n_act) {
-                dma_k(m + 2);
-                cnt += T::kLoadsPerWave;
+    // Load j of a spread copy goes out after MFMA step j*NM/L + 1 of a phase
+    // with NM MFMAs.
+    template <int I, int NM>
+    __device__ __forceinline__ void copy_step(const Copy& c) {
+        constexpr int L = T::kLoadsPerWave;
+        static_assert(NM >= L + 1, "too few MFMA steps to spread the copies over");
+        static_for<0, L>([&](auto jc) {
+            constexpr int j = jc;
+            if constexpr (I == j * NM / L + 1) {
+                if (c.spread) dma16(c.src, dmo[j], c.dst + j * 1024);
             }
-            if (SEG && m + 1 < n_act) {
-                dma_seg(m + 1);
-                cnt += 1;
-            }
-        } else if (m + 1 < n_act) {
-            dma_v(m + 1);
-            cnt += T::kLoadsPerWave;
-        }
-        return cnt;
+        });
     }
 
     // ---- MFMA phase ----------------------------------------------------------------
-    // MFMA i: first the P V ones (k-step kst, d-block db), then the K Q^T ones
-    // (k-step ks, key block kb).
-    template <bool PV>
-    static constexpr int n_pv() { return PV ? 4 * T::kDBlocks : 0; }
+    // MFMA i: first the K Q^T ones of the current tile (k-step ks, key block
+    // kbk), then the P V ones of the previous tile (k-step kst, d-block db).
+    // Starting with K Q^T lets a wave fetch the first K operands before the
+    // barrier that opens the phase: the K tile became visible one phase
+    // earlier, the V tile only at that barrier.
+    template <bool QK>
+    static constexpr int n_qk() { return QK ? 2 * T::kSteps : 0; }
+    template <bool PV, bool QK>
+    static constexpr int n_mfma() { return n_qk<QK>() + (PV ? 4 * T::kDBlocks : 0); }
+    static constexpr int kRing = kOperandPrefetch + 2;
     // vb / kb: LDS byte addresses of this lane's V and K operand bases in the
-    // current ring slots (slot and region offsets are multiples of 1024, so the
-    // swizzle XOR can be applied to the full address).
-    template <bool PV, int I>
+    // ring slots (slot and region offsets are multiples of 1024, so the swizzle
+    // XOR can be applied to the full address).
+    __device__ __forceinline__ uint32_t vbase(int vtile) const {
+        return lds_addr(smem) + T::kVRegion + slot_base(vtile) + vx;
+    }
+    __device__ __forceinline__ uint32_t kbase(int ktile) const {
+        return lds_addr(smem) + T::kKRegion + slot_base(ktile) + kx;
+    }
+    template <bool QK, int I>
     __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb) const {
-        if constexpr (I < n_pv<PV>()) {
-            constexpr int kst = I / T::kDBlocks, db = I % T::kDBlocks;
+        if constexpr (I < n_qk<QK>()) {
+            constexpr int ks = I / 2, kbk = I % 2;
+            return *reinterpret_cast<const bf16x8*>(lds_ptr((kb ^ (ks << 5)) + kbk * 32 * T::kRowBytes));
+        } else {
+            constexpr int j = I - n_qk<QK>();
+            constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
             const char* p = lds_ptr((vb ^ (db << 6)) + kst * 16 * T::kRowBytes);
             return tr_read8(p, p + 4 * T::kRowBytes);
-        } else {
-            constexpr int j = I - n_pv<PV>();
-            constexpr int ks = j / 2, kbk = j % 2;
-            return *reinterpret_cast<const bf16x8*>(lds_ptr((kb ^ (ks << 5)) + kbk * 32 * T::kRowBytes));
         }
     }
-    template <bool PV, int I>
+    template <bool QK, int I>
     __device__ __forceinline__ void mfma(const bf16x8& a) {
-        if constexpr (I < n_pv<PV>()) {
-            constexpr int kst = I / T::kDBlocks, db = I % T::kDBlocks;
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kst], oacc[db], 0, 0, 0);
-        } else {
-            constexpr int j = I - n_pv<PV>();
-            constexpr int ks = j / 2, kbk = j % 2;
+        if constexpr (I < n_qk<QK>()) {
+            constexpr int ks = I / 2, kbk = I % 2;
             if constexpr (ks == 0)
                 sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
             else
                 sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kbk], 0, 0, 0);
+        } else {
+            constexpr int j = I - n_qk<QK>();
+            constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kst], oacc[db], 0, 0, 0);
         }
     }
-    // P V of the previous tile (if PV) and K Q^T of the current tile (if QK): one
-    // MFMA per step, LDS operands fetched kOperandPrefetch steps ahead into a
-    // ring two entries longer, so a register is refilled only after the MFMA
-    // that read it has long issued.  A scheduling fence closes every step.
+    // The first kOperandPrefetch operands of an MFMA phase into the ring.
     template <bool PV, bool QK>
-    __device__ __forceinline__ void mfma_phase(int vtile, int ktile) {
-        const uint32_t vb = lds_addr(smem) + T::kVRegion + slot_base(vtile) + vx;
-        const uint32_t kb = lds_addr(smem) + T::kKRegion + slot_base(ktile) + kx;
-        constexpr int NM = n_pv<PV>() + (QK ? 2 * T::kSteps : 0);
-        constexpr int PF = kOperandPrefetch, RING = PF + 2;
-        bf16x8 ops[RING];
-        __builtin_amdgcn_s_setprio(1);
-        static_for<0, PF>([&](auto ic) {
+    __device__ __forceinline__ void prefetch(int vtile, int ktile) {
+        const uint32_t vb = vbase(vtile), kb = kbase(ktile);
+        static_for<0, kOperandPrefetch>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i < NM) ops[i % RING] = operand<PV, i>(vb, kb);
+            if constexpr (i < n_mfma<PV, QK>()) ops[i % kRing] = operand<QK, i>(vb, kb);
         });
+    }
+    // K Q^T of the current tile (if QK) and P V of the previous tile (if PV):
+    // one MFMA per step, LDS operands fetched kOperandPrefetch steps ahead into
+    // a ring two entries longer, so a register is refilled only after the MFMA
+    // that read it has long issued; the planned tile copy goes out in between.
+    // With PRE the first operands were fetched before the phase began.  A
+    // scheduling fence closes every step.
+    template <bool PV, bool QK, bool PRE>
+    __device__ __forceinline__ void mfma_phase(int vtile, int ktile, const Copy& cp) {
+        constexpr int NM = n_mfma<PV, QK>();
+        constexpr int PF = kOperandPrefetch;
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (!PRE) prefetch<PV, QK>(vtile, ktile);
+        copy_start(cp);
+        const uint32_t vb = vbase(vtile), kb = kbase(ktile);
         static_for<0, NM>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i + PF < NM) ops[(i + PF) % RING] = operand<PV, i + PF>(vb, kb);
-            mfma<PV, i>(ops[i % RING]);
+            if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb);
+            mfma<QK, i>(ops[i % kRing]);
+            copy_step<i, NM>(cp);
             __builtin_amdgcn_sched_barrier(0);
         });
         __builtin_amdgcn_s_setprio(0);
@@ -414,6 +457,52 @@ struct Attn {
     }
 };
 
+// Ping-pong schedule of group G.  Local iteration n: MFMA phase (K Q^T of
+// tile n, P V of tile n-1) at global phase 2n + G, then the VALU phase
+// (softmax of tile n) at 2n + 1 + G; a workgroup barrier closes every global
+// phase.  In its VALU phase a wave also plans the next MFMA phase's tile copy
+// and, once the softmax is done, fetches that phase's first K operands, so
+// the MFMA phase starts issuing right after its barrier.  The MFMA phase
+// issues the copy between its MFMAs and, before its closing barrier, waits for
+// the copy of its previous MFMA phase, so a copy has two phases to land.  The
+// first and last iterations are peeled so that the steady-state body has a
+// single MFMA phase shape.
+template <int G, int D, bool SEG>
+__device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
+    typename Attn<D, SEG>::Copy cp;
+    auto valu_phase = [&](int n) {
+        if (A.partial(n)) A.mask(n);
+        A.softmax();
+        A.rescale();
+        A.template plan<G>(cp, n + 3 - G, n_act);
+        // Operands of the next MFMA phase (K Q^T of tile n+1; stale when n+1 is
+        // past the last tile, and then unused).
+        A.template prefetch<true, true>(n, n + 1);
+        barrier();
+    };
+    A.template plan<G>(cp, 2 - G, n_act);
+    A.template prefetch<false, true>(0, 0);
+    if (G == 1) barrier();  // group 1 idles in global phase 0
+    A.template mfma_phase<false, true, true>(0, 0, cp);
+    wait_vm(cp.cnt);
+    barrier();
+    valu_phase(0);
+    for (int n = 1; n < n_act; ++n) {
+        const int c = cp.cnt;
+        A.template mfma_phase<true, true, true>(n - 1, n, cp);
+        wait_vm(c);
+        barrier();
+        valu_phase(n);
+    }
+    {
+        const int c = cp.cnt;
+        A.template mfma_phase<true, false, false>(n_act - 1, 0, cp);
+        wait_vm(c);
+        barrier();
+    }
+    if (G == 0) barrier();  // group 0 idles in the last global phase
+}
+
 template <int D, bool SEG>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -448,6 +537,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     A.S = S;
     A.n_kvt = n_kvt;
     A.wave = wave;
+    A.w4 = wave & 3;
     A.lane = lane;
     A.lr = lr;
     A.g = g;
@@ -475,17 +565,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
         const int key = 8 * (qg >> 1) + (j >> 2);
         const int vsw = v_swz<D>(key);
         A.vx = key * T::kRowBytes + 32 * ((qg & 1) ^ vsw) + 16 * ((j & 3) >> 1) + 8 * (j & 1);
-        // DMA: instruction i of the tile covers rows kRowsPerLoad*i .. ; lane lands
-        // at LDS position pos of its row and fetches the chunk stored there.
+        // Tile copies: instruction i of a tile covers rows kRowsPerLoad*i .. ; a
+        // lane lands at LDS position pos of its row and fetches the chunk stored
+        // there (K layout for group 0, V layout for group 1).
 #pragma unroll
         for (int jj = 0; jj < T::kLoadsPerWave; ++jj) {
-            const int i = wave * T::kLoadsPerWave + jj;
+            const int i = A.w4 * T::kLoadsPerWave + jj;
             const int r = T::kRowsPerLoad * i + lane / T::kChunks;
             const int pos = lane % T::kChunks;
-            const int ck = pos ^ k_swz<D>(r);
-            const int cv = 2 * ((pos >> 1) ^ v_swz<D>(r)) + (pos & 1);
-            A.dmak[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + ck * 8);
-            A.dmav[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + cv * 8);
+            const int c = grp ? 2 * ((pos >> 1) ^ v_swz<D>(r)) + (pos & 1) : (pos ^ k_swz<D>(r));
+            A.dmo[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + c * 8);
         }
     }
 
@@ -568,13 +657,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     A.l_run = 0.f;        // this lane's partial sum (its half of each tile's keys)
     A.alpha = 1.f;
 
-    // ---- prologue: K of tiles 0 and 1, V and segment IDs of tile 0 -------------
-    if (n_act > 0) {
-        A.dma_k(0);
-        A.dma_v(0);
-        if (SEG) A.dma_seg(0);
+    // ---- prologue: K of tiles 0 and 1, segment IDs of tile 0 (group 0), V of
+    // tile 0 (group 1) ---------------------------------------------------------------
+    {
+        typename Attn<D, SEG>::Copy c;
+        if (grp == 0) {
+            for (int a = 0; a < 2; ++a) {
+                A.template plan<0>(c, a, n_act);  // K tile a, segment IDs of tile a-1
+                A.copy_start(c);
+                if (c.spread) {
+#pragma unroll
+                    for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
+                }
+            }
+        } else {
+            A.template plan<1>(c, 0, n_act);
+            A.copy_start(c);
+            if (c.spread) {
+#pragma unroll
+                for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
+            }
+        }
     }
-    if (n_act > 1) A.dma_k(1);
     wait_vm(0);
     barrier();
     // A use of the Q registers (and the query's segment ID) here makes the
@@ -583,38 +687,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     asm volatile("" ::"v"(A.qreg[0]), "v"(A.qreg[T::kSteps - 1]), "v"(A.myseg));
 
     // ---- ping-pong main loop --------------------------------------------------------
-    // Local iteration n: MFMA phase (P V of tile n-1, K Q^T of tile n) at global
-    // phase 2n + grp, then the VALU phase (softmax of tile n) at 2n + 1 + grp.
-    // Every wave issues its DMA share for each global phase once and, before
-    // each barrier, waits for the loads of all but the last two phases.
-    int cnt_prev = 0;
-    auto end_phase = [&](int p) {
-        const int c = A.dma_phase(p, n_act);
-        wait_vm(cnt_prev + c);
-        cnt_prev = c;
-        barrier();
-    };
-    // The first and last iterations are peeled so that the steady-state body
-    // has a single MFMA phase shape (no register shuffling at control-flow joins).
-    auto valu_phase = [&](int n) {
-        if (A.partial(n)) A.mask(n);
-        A.softmax();
-        A.rescale();
-        end_phase(2 * n + 1 + grp);
-    };
     if (n_act > 0) {
-        if (grp == 1) end_phase(0);  // group 1 idles in global phase 0
-        A.template mfma_phase<false, true>(0, 0);
-        end_phase(grp);
-        valu_phase(0);
-        for (int n = 1; n < n_act; ++n) {
-            A.template mfma_phase<true, true>(n - 1, n);
-            end_phase(2 * n + grp);
-            valu_phase(n);
-        }
-        A.template mfma_phase<true, false>(n_act - 1, 0);
-        end_phase(2 * n_act + grp);
-        if (grp == 0) end_phase(2 * n_act + 1);  // group 0 idles in the last global phase
+        if (grp == 0)
+            main_loop<0>(A, n_act);
+        else
+            main_loop<1>(A, n_act);
     }
 
     // ---- epilogue: normalise, write out (bf16) and lse (fp32) ----------------
