@@ -31,7 +31,8 @@
 //     chunks XOR-swizzled) and is read transposed with ds_read_b64_tr_b16, so
 //     no VALU work is spent on staging and no LDS bank conflicts occur;
 //   * online softmax in fp32 with exp2 and scale*log2(e) folded into one FMA;
-//     the O^T accumulators are rescaled only when some row's maximum grew;
+//     the reference maximum moves lazily (only when a score exceeds it by a
+//     fixed margin), so the O^T accumulators are almost never rescaled;
 //   * register budget (two waves per SIMD, 256 VGPRs each): the O^T and S^T
 //     accumulators, the Q slice, P and a short operand ring; operand addresses
 //     are one swizzled base per phase (XOR with a constant per MFMA) and the
@@ -73,6 +74,11 @@ constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robi
 constexpr int kMaxKvTiles = 30720;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+#ifndef VDX_LAZY_LOG2
+#define VDX_LAZY_LOG2 8.0f
+#endif
+// A row's P may grow to 2^kLazyLog2 before its reference maximum is moved.
+constexpr float kLazyLog2 = VDX_LAZY_LOG2;
 
 template <int D>
 struct Tile {
@@ -210,7 +216,7 @@ struct Attn {
     f32x16 sacc[2];
     bf16x8 pb[4];
     bf16x8 ops[kOperandPrefetch + 2];  // MFMA operand ring
-    float m_run, l_run, alpha;
+    float m_run, l_run;
 
     __device__ __forceinline__ int tile_of(int n, bool& partial) const {
         if (SEG) {
@@ -412,8 +418,14 @@ struct Attn {
             }
         }
     }
-    // Online softmax of the current scores: running max in the log2 domain,
-    // P = 2^(s*scale*log2(e) - m) in bf16 for the next P V, l += row sum.
+    // Online softmax of the current scores in the log2 domain, with a lazily
+    // moved reference: m_run only moves when some row of the wave sees a
+    // scaled score more than kLazyLog2 above it.  Then P = 2^(s*scale*log2(e)
+    // - m_run) <= 2^kLazyLog2, and the rescale of O and l by 2^(m_old - m_new)
+    // (an exp and 64 multiplies per lane) is skipped on nearly every tile.
+    // out = O / l and lse = m_run + log2(l) do not depend on the reference.
+    // l is summed in fp32 from the unrounded P (a sum of the bf16 P would
+    // carry their 2^-9 rounding into lse).
     __device__ __forceinline__ void softmax() {
         float mx0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
         float mx1 = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
@@ -422,13 +434,23 @@ struct Attn {
             mx0 = fmaxf(fmaxf(mx0, sacc[0][r]), sacc[0][r + 1]);
             mx1 = fmaxf(fmaxf(mx1, sacc[1][r]), sacc[1][r + 1]);
         }
-        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15])));
-        const float m_old = m_run;
-        const float m_new = fmaxf(m_old, mx * c_log2);
-        // alpha == 1 exactly when the maximum did not move (exp2(0) = 1).
-        alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
-        m_run = m_new;
-        const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]))) * c_log2;
+        const bool move = mx > m_run + kLazyLog2;
+        if (__ballot(move) != 0ull) {
+            // Per row: only rows past their margin move (alpha = 2^0 = 1
+            // exactly for the others), so a row's arithmetic never depends on
+            // the other rows of the wave.  m_run = -inf (no valid key yet)
+            // gives alpha = 2^-inf = 0.
+            const float m_new = move ? mx : m_run;
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -439,21 +461,11 @@ struct Attn {
                 pb[b * 2 + (r >> 3)][r & 7] = (__bf16)p;
             }
         }
-        l_run = __builtin_fmaf(alpha, l_run, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         // Pin the results inside this phase: without a use here the optimiser
         // sinks the softmax next to its consumer (the next MFMA phase), which
         // would serialise it behind those MFMAs.
-        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run), "v"(m_run),
-                     "v"(alpha));
-    }
-    // O *= alpha when some row's maximum moved (rare after the first tiles).
-    __device__ __forceinline__ void rescale() {
-        if (__ballot(alpha != 1.0f) != 0ull) {
-#pragma unroll
-            for (int db = 0; db < T::kDBlocks; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run), "v"(m_run));
     }
 };
 
@@ -473,7 +485,6 @@ __device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
     auto valu_phase = [&](int n) {
         if (A.partial(n)) A.mask(n);
         A.softmax();
-        A.rescale();
         A.template plan<G>(cp, n + 3 - G, n_act);
         // Operands of the next MFMA phase (K Q^T of tile n+1; stale when n+1 is
         // past the last tile, and then unused).
@@ -655,7 +666,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     for (int i = 0; i < 4; ++i) A.pb[i] = bf16x8{};
     A.m_run = -INFINITY;  // running max of scale*log2(e)*s for this lane's query
     A.l_run = 0.f;        // this lane's partial sum (its half of each tile's keys)
-    A.alpha = 1.f;
 
     // ---- prologue: K of tiles 0 and 1, segment IDs of tile 0 (group 0), V of
     // tile 0 (group 1) ---------------------------------------------------------------
