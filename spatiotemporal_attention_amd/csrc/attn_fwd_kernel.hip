@@ -124,6 +124,22 @@ __device__ __forceinline__ void barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 // Wait until at most n of this wave's vector-memory loads are outstanding.
+// Wait until at most n loads are outstanding, for the counts a phase's
+// copies take (n in {0, 1, L, L+1} with L loads per tile share); the common
+// count is tested first.
+template <int L>
+__device__ __forceinline__ void wait_copies(int n) {
+    static_assert(L >= 2 && L + 1 <= 6, "unsupported copy count");
+    if (n == L) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    } else if (n == L + 1) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L + 1) : "memory");
+    } else if (n == 1) {
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+}
 __device__ __forceinline__ void wait_vm(int n) {
     switch (n) {
         case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
@@ -216,6 +232,7 @@ struct Attn {
     f32x16 sacc[2];
     bf16x8 pb[4];
     bf16x8 ops[kOperandPrefetch + 2];  // MFMA operand ring
+    uint32_t vb_next, kb_next;         // operand bases of the prefetched phase
     float m_run, l_run;
 
     __device__ __forceinline__ int tile_of(int n, bool& partial) const {
@@ -367,12 +384,15 @@ struct Attn {
         }
     }
     // The first kOperandPrefetch operands of an MFMA phase into the ring.
+    // The operand bases are kept for the phase, so that its first MFMA does not
+    // wait behind their computation.
     template <bool PV, bool QK>
     __device__ __forceinline__ void prefetch(int vtile, int ktile) {
-        const uint32_t vb = vbase(vtile), kb = kbase(ktile);
+        vb_next = vbase(vtile);
+        kb_next = kbase(ktile);
         static_for<0, kOperandPrefetch>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i < n_mfma<PV, QK>()) ops[i % kRing] = operand<QK, i>(vb, kb);
+            if constexpr (i < n_mfma<PV, QK>()) ops[i % kRing] = operand<QK, i>(vb_next, kb_next);
         });
     }
     // K Q^T of the current tile (if QK) and P V of the previous tile (if PV):
@@ -387,8 +407,8 @@ struct Attn {
         constexpr int PF = kOperandPrefetch;
         __builtin_amdgcn_s_setprio(1);
         if constexpr (!PRE) prefetch<PV, QK>(vtile, ktile);
+        const uint32_t vb = vb_next, kb = kb_next;
         copy_start(cp);
-        const uint32_t vb = vbase(vtile), kb = kbase(ktile);
         static_for<0, NM>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb);
@@ -495,20 +515,20 @@ __device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
     A.template prefetch<false, true>(0, 0);
     if (G == 1) barrier();  // group 1 idles in global phase 0
     A.template mfma_phase<false, true, true>(0, 0, cp);
-    wait_vm(cp.cnt);
+    wait_copies<Attn<D, SEG>::T::kLoadsPerWave>(cp.cnt);
     barrier();
     valu_phase(0);
     for (int n = 1; n < n_act; ++n) {
         const int c = cp.cnt;
         A.template mfma_phase<true, true, true>(n - 1, n, cp);
-        wait_vm(c);
+        wait_copies<Attn<D, SEG>::T::kLoadsPerWave>(c);
         barrier();
         valu_phase(n);
     }
     {
         const int c = cp.cnt;
         A.template mfma_phase<true, false, false>(n_act - 1, 0, cp);
-        wait_vm(c);
+        wait_copies<Attn<D, SEG>::T::kLoadsPerWave>(c);
         barrier();
     }
     if (G == 0) barrier();  // group 0 idles in the last global phase
