@@ -1,4 +1,5 @@
-"""CPU oracle for segment-masked, non-causal softmax self-attention.
+"""CPU oracles for segment-masked, non-causal softmax self-attention and for
+3D neighbourhood (windowed) self-attention.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check
 and by the benchmark's CPU-baseline leg, never by the product path.  It shares
@@ -7,10 +8,14 @@ no code with the HIP library.
 The arithmetic lives in ``attn_oracle.c`` (scalar fp64, plain definition of
 softmax(scale * Q K^T, masked by segment IDs) V -- vidax paper, section 2
 "3D RoPE, 3D VAEs, and flash attention" with its reference [2], and Appendix A,
-Table 4, group 2 for SegmentIds).  This wrapper only marshals numpy arrays.
+Table 4, group 2 for SegmentIds) and ``natten_oracle.c`` (the same softmax
+restricted to each query's 3D neighbourhood window -- section 2 for the
+windowed-attention fallback of the neighbourhood-attention VAE decoder,
+Appendix A, Table 4, group 4 for its 11 x 11 x 11 window).  This wrapper only
+marshals numpy arrays.
 
-Every function here has pins in ``tests/test_oracle.py``; see the module
-docstring there for what pins what.
+Every function here has pins in ``tests/test_oracle.py`` and
+``tests/test_natten_oracle.py``; their module docstrings say what pins what.
 """
 from __future__ import annotations
 
@@ -42,6 +47,10 @@ def _load(path: Optional[str] = None):
     i64 = ctypes.c_int64
     f.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double,
                   p, i64, p, p, p, ctypes.c_int]
+    g = lib.vdx_oracle_natten3d_fwd
+    g.restype = ctypes.c_int
+    g.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                  p, i64, p, p, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -110,3 +119,44 @@ def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
     return out, lse, probs
+
+
+def natten3d_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                 grid: Tuple[int, int, int], window: Tuple[int, int, int], scale: float,
+                 rows: Optional[np.ndarray] = None, n_threads: Optional[int] = None
+                 ) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 3D neighbourhood attention on bf16 bit patterns.
+
+    q_bits/k_bits/v_bits: uint16 [B, S, H, D], S = NT*NH*NW, tokens (t, y, x)
+    row-major.  grid = (NT, NH, NW); window = (KT, KH, KW), odd sizes.
+    rows: optional int64 [n, 3] of (b, h, i); then out is [n, D] and lse [n];
+    else out is [B, S, H, D] and lse [B, H, S].
+    """
+    lib = _load()
+    for a in (q_bits, k_bits, v_bits):
+        assert a.dtype == np.uint16 and a.ndim == 4
+    B, S, H, D = q_bits.shape
+    NT, NH, NW = (int(x) for x in grid)
+    KT, KH, KW = (int(x) for x in window)
+    if NT * NH * NW != S:
+        raise ValueError("grid does not match the sequence length")
+    assert k_bits.shape == q_bits.shape and v_bits.shape == q_bits.shape
+    q_bits = np.ascontiguousarray(q_bits)
+    k_bits = np.ascontiguousarray(k_bits)
+    v_bits = np.ascontiguousarray(v_bits)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        out = np.zeros((n, D), dtype=np.float64)
+        lse = np.zeros((n,), dtype=np.float64)
+    else:
+        n = 0
+        out = np.zeros((B, S, H, D), dtype=np.float64)
+        lse = np.zeros((B, H, S), dtype=np.float64)
+    rc = lib.vdx_oracle_natten3d_fwd(
+        _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), B, NT, NH, NW, H, D, KT, KH, KW,
+        float(scale), _ptr(rows), n, _ptr(out), _ptr(lse),
+        int(n_threads if n_threads is not None else default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle returned {rc}")
+    return out, lse

@@ -113,6 +113,45 @@ for _w in WORKLOADS.values():
         assert _runs_cover(_w.seg_runs, _w.S), _w.name
 
 
+# --- 3D neighbourhood attention ----------------------------------------------
+@dataclass(frozen=True)
+class NattenWorkload:
+    """A t x h x w token grid (flattened (t, y, x), x fastest) with an odd
+    per-axis window.  The pages give the window of the neighbourhood-attention
+    VAE decoder (11 x 11 x 11, Appendix A, Table 4, group 4) but no grid,
+    head count or head dim, so those are synthetic stand-ins."""
+    name: str
+    B: int
+    grid: Tuple[int, int, int]
+    window: Tuple[int, int, int]
+    H: int
+    D: int
+    scale: float
+    seeds: Tuple[int, int, int]
+    note: str = ""
+
+    @property
+    def S(self) -> int:
+        return self.grid[0] * self.grid[1] * self.grid[2]
+
+
+NATTEN_TINY = NattenWorkload(
+    "natten_tiny", B=1, grid=(4, 6, 40), window=(3, 5, 11), H=2, D=64, scale=1.0 / 8.0,
+    seeds=(6000, 6001, 6002), note="small grid the oracle finishes in seconds; border-heavy")
+NATTEN_VAE = NattenWorkload(
+    "natten_vae_decoder", B=1, grid=(16, 32, 64), window=(11, 11, 11), H=8, D=128,
+    scale=1.0 / math.sqrt(128.0), seeds=(7000, 7001, 7002),
+    note="synthetic stand-in for a video VAE decoder stage with an 11x11x11 window")
+NATTEN_WORKLOADS: Dict[str, NattenWorkload] = {w.name: w for w in (NATTEN_TINY, NATTEN_VAE)}
+
+
+def make_natten_inputs(w: NattenWorkload) -> Dict[str, torch.Tensor]:
+    """CPU tensors q, k, v (bf16 [B, S, H, D]), same recipe as the workloads."""
+    shape = (w.B, w.S, w.H, w.D)
+    return {"q": randn_bf16(shape, w.seeds[0]), "k": randn_bf16(shape, w.seeds[1]),
+            "v": randn_bf16(shape, w.seeds[2])}
+
+
 # --- generators --------------------------------------------------------------
 def randn_bf16(shape: Sequence[int], seed: int, sigma: float = 1.0) -> torch.Tensor:
     """float32 N(0, sigma^2) from a seeded CPU generator, rounded to bf16."""
