@@ -1,6 +1,7 @@
 /*
  * vdx_attn.h -- C ABI of the segment-masked, non-causal flash-attention
- * forward for video-DiT token volumes on gfx950 (MI355X).
+ * forward for video-DiT token volumes on gfx950 (MI355X), and of the 3D
+ * neighbourhood (windowed) attention forward (vdx_natten3d_fwd, below).
  *
  * The operation (vidax paper, arXiv:2609.18077):
  *   - section 1, "Spatiotemporal constraints in video generation": full
@@ -39,7 +40,7 @@
 extern "C" {
 #endif
 
-#define VDX_ABI_VERSION 1
+#define VDX_ABI_VERSION 2
 
 /* Status codes.  Argument validation runs before any HIP call, in the order
  * below (NULL -> segment pair -> shape -> head dim -> scale -> alignment),
@@ -59,7 +60,9 @@ enum vdx_status {
                              lse not 4-byte aligned                              */
     VDX_ERR_DEVICE = 7,   /* the current HIP device is not gfx950, or the
                              device query failed                                */
-    VDX_ERR_LAUNCH = 8    /* the kernel launch reported an error                */
+    VDX_ERR_LAUNCH = 8,   /* the kernel launch reported an error                */
+    VDX_ERR_WINDOW = 9    /* vdx_natten3d_fwd: a window size is even or < 1, or
+                             the effective x window min(KW, NW) exceeds 13      */
 };
 
 /*
@@ -87,6 +90,44 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
                  const int32_t* seg_q, const int32_t* seg_kv,
                  void* out, float* lse,
                  int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/*
+ * vdx_natten3d_fwd -- one forward pass of 3D neighbourhood (windowed)
+ * self-attention over a t x h x w token grid.
+ *
+ * The operation (vidax paper, arXiv:2609.18077):
+ *   - section 2, "3D RoPE, 3D VAEs, and flash attention": models without a
+ *     native kernel for it, such as LTX-2.5's neighbourhood-attention VAE
+ *     decoder, use a windowed-attention primitive;
+ *   - Appendix A, Table 4, group 4 (LTX-2.5 VAE decoder rows): the window
+ *     spans 11 x 11 x 11 grid positions for that model's stage-5 kernel.
+ *
+ * Tokens are the grid flattened (t, y, x), x fastest: S = NT*NH*NW and token
+ * s = (t*NH + y)*NW + x.  Along an axis of length n, a window of odd size k
+ * covers k_eff = min(k, n) positions starting at clamp(c - k/2, 0, n - k_eff)
+ * (it shifts inward at the grid border, so every query sees exactly
+ * k_eff,t * k_eff,h * k_eff,w keys).  For every batch b, head h, query i:
+ *     J    = the keys in the window of i
+ *     out[b,i,h,:] = sum_{j in J} softmax(scale * q_i . k_j)_j * v[b,j,h,:]  (bf16, RNE)
+ *     lse[b,h,i]   = log(sum_{j in J} exp(scale * q_i . k_j))               (fp32)
+ *
+ *   q, k, v   bf16 [B, S, H, D], contiguous, read-only (may alias).
+ *   out, lse  bf16 [B, S, H, D] and fp32 [B, H, S], written in full; they must
+ *             not overlap the inputs or each other.
+ *   NT,NH,NW  grid extents (>= 1), S = NT*NH*NW <= 2^31-1.
+ *   H, D      heads >= 1; D is 64 or 128.
+ *   KT,KH,KW  odd window sizes >= 1; min(KW, NW) <= 13.
+ *   scale     finite, > 0.
+ *   stream    HIP stream; asynchronous, no host synchronisation.
+ * Every pointer is a DEVICE pointer owned by the caller; the library
+ * allocates nothing.  Validation runs before any HIP call, in the order
+ * NULL -> shape -> head dim -> window -> scale -> alignment (q, k, v, out
+ * 16-byte, lse 4-byte), and reports the first failure without touching
+ * device memory.  Results are deterministic.
+ */
+int vdx_natten3d_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int NT, int NH, int NW, int H, int D, int KT, int KH, int KW,
+                     float scale, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* vdx_status_str(int status);

@@ -1,14 +1,24 @@
 """spatiotemporal_attention_amd -- segment-masked, non-causal flash-attention
-forward for video-DiT token volumes on MI355X (gfx950).
+forward for video-DiT token volumes on MI355X (gfx950), and 3D neighbourhood
+(windowed) attention over a t x h x w token grid.
 
 ``attn_fwd`` computes, for q, k, v of shape [B, S, H, D] (bf16):
     out[b,i,h,:] = softmax_j(scale * q[b,i,h,:] . k[b,j,h,:]) v[b,j,h,:]
 over the keys j whose segment ID equals the query's (ID 0 = padding, matched
 by nothing), and lse[b,h,i] = log sum_j exp(scale * q . k) over those keys
 (vidax paper, arXiv:2609.18077: section 2 "3D RoPE, 3D VAEs, and flash
-attention"; Appendix A, Table 4, group 2 for SegmentIds).  Every step runs in
-the hand-written HIP kernel behind the C ABI (include/vdx_attn.h); this module
-only checks arguments and passes device pointers and the current stream.
+attention"; Appendix A, Table 4, group 2 for SegmentIds).
+
+``natten3d_fwd`` computes the same softmax restricted, for each query of a
+t x h x w grid (tokens flattened (t, y, x), x fastest), to its neighbourhood
+window: along an axis of length n an odd window k covers min(k, n) positions
+starting at clamp(c - k//2, 0, n - min(k, n)) (section 2 for the
+windowed-attention primitive of the neighbourhood-attention VAE decoder;
+Appendix A, Table 4, group 4 for its 11 x 11 x 11 window).
+
+Every step runs in the hand-written HIP kernels behind the C ABI
+(include/vdx_attn.h); this module only checks arguments and passes device
+pointers and the current stream.
 """
 from __future__ import annotations
 
@@ -20,7 +30,7 @@ import torch
 from . import _native
 from ._native import abi_version, status_str
 
-__all__ = ["attn_fwd", "abi_version", "status_str", "VdxError"]
+__all__ = ["attn_fwd", "natten3d_fwd", "abi_version", "status_str", "VdxError"]
 
 
 class VdxError(ValueError):
@@ -71,6 +81,50 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                   0 if seg_kv is None else seg_kv.data_ptr(),
                                   out.data_ptr(), lse.data_ptr(), B, S, H, D, scale,
                                   stream.cuda_stream)
+    if rc != 0:
+        raise VdxError(rc)
+    return out, lse
+
+
+def natten3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 grid: Tuple[int, int, int], window: Tuple[int, int, int],
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """3D neighbourhood attention forward on the current (or given) HIP stream.
+
+    q, k, v: bf16 [B, S, H, D] contiguous on one GPU with S = NT*NH*NW for
+    grid = (NT, NH, NW); window = (KT, KH, KW), odd sizes.  Returns
+    (out bf16 [B,S,H,D], lse fp32 [B,H,S]).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S, H, D]")
+    B, S, H, D = q.shape
+    NT, NH, NW = (int(x) for x in grid)
+    KT, KH, KW = (int(x) for x in window)
+    if NT * NH * NW != S:
+        raise ValueError(f"grid {grid} does not hold S={S} tokens")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of shape {tuple(q.shape)}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = _native.natten3d_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), B, NT, NH, NW, H, D, KT, KH, KW, scale,
+                                      stream.cuda_stream)
     if rc != 0:
         raise VdxError(rc)
     return out, lse

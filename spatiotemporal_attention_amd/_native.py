@@ -19,8 +19,9 @@ VDX_ERR_SCALE = 5
 VDX_ERR_ALIGN = 6
 VDX_ERR_DEVICE = 7
 VDX_ERR_LAUNCH = 8
+VDX_ERR_WINDOW = 9
 
-EXPORTED = ("vdx_attn_fwd", "vdx_status_str", "vdx_abi_version")
+EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_status_str", "vdx_abi_version")
 
 
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -31,6 +32,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     i = ctypes.c_int
     lib.vdx_attn_fwd.restype = i
     lib.vdx_attn_fwd.argtypes = [p, p, p, p, p, p, p, i, i, i, i, ctypes.c_float, p]
+    lib.vdx_natten3d_fwd.restype = i
+    lib.vdx_natten3d_fwd.argtypes = [p, p, p, p, p] + [i] * 9 + [ctypes.c_float, p]
     lib.vdx_status_str.restype = ctypes.c_char_p
     lib.vdx_status_str.argtypes = [i]
     lib.vdx_abi_version.restype = i
@@ -54,3 +57,10 @@ def attn_fwd_raw(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale, stream) ->
     return int(lib.vdx_attn_fwd(q or None, k or None, v or None, seg_q or None, seg_kv or None,
                                 out or None, lse or None, int(B), int(S), int(H), int(D),
                                 float(scale), stream or None))
+
+
+def natten3d_fwd_raw(q, k, v, out, lse, B, NT, NH, NW, H, D, KT, KH, KW, scale, stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL)."""
+    return int(lib.vdx_natten3d_fwd(q or None, k or None, v or None, out or None, lse or None,
+                                    int(B), int(NT), int(NH), int(NW), int(H), int(D),
+                                    int(KT), int(KH), int(KW), float(scale), stream or None))

@@ -47,165 +47,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
+#include "attn_common.h"
 #include "attn_fwd_launch.h"
 
 namespace vdx {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBq = 32 * kWaves;  // queries per workgroup
-constexpr int kBk = 64;           // keys per tile
-constexpr int kDmaWaves = kWaves / 2;  // one ping-pong group issues each tile copy
-constexpr int kSlots = 3;         // ring depth of the K, V and segment-ID stages
-#ifndef VDX_OPERAND_PREFETCH
-#define VDX_OPERAND_PREFETCH 4
-#endif
-constexpr int kOperandPrefetch = VDX_OPERAND_PREFETCH;  // MFMA operands in flight
-constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kMaxKvTiles = 30720;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-#ifndef VDX_LAZY_LOG2
-#define VDX_LAZY_LOG2 8.0f
-#endif
-// A row's P may grow to 2^kLazyLog2 before its reference maximum is moved.
-constexpr float kLazyLog2 = VDX_LAZY_LOG2;
-
-template <int D>
-struct Tile {
-    static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
-    static constexpr int kRowBytes = D * 2;
-    static constexpr int kTileBytes = kBk * kRowBytes;           // one K or V tile
-    static constexpr int kKRegion = 0;
-    static constexpr int kVRegion = kSlots * kTileBytes;
-    static constexpr int kSegRegion = kVRegion + kSlots * kTileBytes;
-    static constexpr int kRingBytes = kSegRegion + kSlots * kBk * 4;
-    static constexpr int kRowsPerLoad = 1024 / kRowBytes;        // rows per wave DMA
-    static constexpr int kLoadsPerWave = kTileBytes / 1024 / kDmaWaves;
-    static constexpr int kSteps = D / 16;                        // MFMA k-steps over D
-    static constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
-    static_assert(kLoadsPerWave >= 1, "tile too small for the workgroup");
-};
-
-// Swap bits 2 and 3: maps an MFMA accumulator row inside a 32-key block to the
-// physical key it holds (and back; the map is an involution).
-__device__ __forceinline__ int swap23(int x) {
-    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-// K tile: 16-byte chunk c of row r sits at position c ^ k_swz(r).
-template <int D>
-__device__ __forceinline__ int k_swz(int r) { return swap23(r & 31) & (Tile<D>::kChunks - 1); }
-// V tile: 32-byte chunk h of row r sits at position h ^ v_swz(r).
-template <int D>
-__device__ __forceinline__ int v_swz(int r) { return (2 * (r & 3)) & (Tile<D>::kChunks / 2 - 1); }
-
-__device__ __forceinline__ float pair_max(float x) {
-    // v_permlane32_swap(x, x) yields x[l % 32] and x[l % 32 + 32] in every lane.
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ void barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-}
-// Wait until at most n of this wave's vector-memory loads are outstanding.
-// Wait until at most n loads are outstanding, for the counts a phase's
-// copies take (n in {0, 1, L, L+1} with L loads per tile share); the common
-// count is tested first.
-template <int L>
-__device__ __forceinline__ void wait_copies(int n) {
-    static_assert(L >= 2 && L + 1 <= 6, "unsupported copy count");
-    if (n == L) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-    } else if (n == L + 1) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L + 1) : "memory");
-    } else if (n == 1) {
-        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-}
-__device__ __forceinline__ void wait_vm(int n) {
-    switch (n) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    }
-}
-
-// Direct global->LDS copies: lane l's bytes land at LDS address M0 + size*l.
-// Issued as inline asm so that the compiler does not treat every later LDS read
-// as a possible alias of the in-flight copy (it would insert vmcnt(0) waits and
-// serialise the prefetch); completion is tracked by hand with wait_vm() and the
-// workgroup barrier that follows it.
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
-}
-__device__ __forceinline__ const char* lds_ptr(uint32_t a) {
-    return (const char*)((const __attribute__((address_space(3))) char*)(uintptr_t)a);
-}
-// The global address is a wave-uniform base (SGPR pair) plus a per-lane
-// 32-bit byte offset.  The s_nop 4 supplies the wait states GFX9 requires
-// before a vector-memory instruction that reads an SGPR (the base pair, M0)
-// written by a VALU instruction (five; the compiler may reload a spilled SGPR
-// with v_readlane right before the asm) or M0 written by SALU (one): the
-// hazard recogniser does not look inside inline asm.
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, char* lds) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-                 "{m0}"(lds_addr(lds))
-                 : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t off, char* lds) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
-                 "{m0}"(lds_addr(lds))
-                 : "memory");
-}
-
-__device__ __forceinline__ bf16x8 tr_read8(const char* p0, const char* p1) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
-    return x;
-}
-
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
+constexpr int kMaxKvTiles = 30720;  // capacity of the on-chip active-tile list
 
 template <int D, bool SEG>
 struct Attn {

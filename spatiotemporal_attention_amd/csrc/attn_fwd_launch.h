@@ -29,3 +29,28 @@ int64_t max_masked_seq();
 int64_t queries_per_workgroup();
 
 }  // namespace vdx
+
+namespace vdx {
+
+// 3D neighbourhood attention over a t x h x w grid (tokens (t, y, x), x fastest).
+struct NattenArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int B, NT, NH, NW, H, D;
+    int KT, KH, KW;  // odd window sizes
+    float scale;
+};
+
+// Largest effective window along x the neighbourhood kernel supports.
+constexpr int kNattenMaxWindowX = 13;
+
+// Enqueue the neighbourhood-attention kernel; arguments are already validated.
+hipError_t launch_natten_fwd(const NattenArgs& a, hipStream_t stream);
+
+// Workgroups the neighbourhood kernel launches for a call.
+int64_t natten_workgroups(const NattenArgs& a);
+
+}  // namespace vdx

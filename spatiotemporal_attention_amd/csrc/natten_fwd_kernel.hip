@@ -1,0 +1,460 @@
+// natten_fwd_kernel.hip -- gfx950 forward of 3D neighbourhood (windowed)
+// self-attention over a t x h x w token grid.
+//
+// What it computes: for every query token, softmax(scale * q K^T) V over the
+// keys of its neighbourhood window, plus the natural-log log-sum-exp (vidax
+// paper, arXiv:2609.18077: section 2 "3D RoPE, 3D VAEs, and flash attention"
+// for the windowed-attention primitive of the neighbourhood-attention VAE
+// decoder; Appendix A, Table 4, group 4, LTX-2.5 VAE decoder rows, for its
+// 11 x 11 x 11 window).  Tokens are flattened (t, y, x), x fastest.  Along an
+// axis of length n a window of odd size k covers k_eff = min(k, n) positions
+// starting at clamp(c - k/2, 0, n - k_eff): it shifts inward at the border.
+//
+// Design (same machinery as the segment-masked kernel):
+//   * one workgroup = 8 wave64s (two per SIMD, two ping-pong groups) and a
+//     1 x 8 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
+//     sub-brick at y offset 2(w >> 1), x offset 16(w & 1), lane lr the query
+//     (lr >> 4, lr & 15) of it;
+//   * the workgroup streams one key row (t', y') per tile: 64 consecutive x
+//     positions from X0 (its first query's window start, rounded down to 4),
+//     over every row in the union of its queries' windows -- t' in the common
+//     t window, y' in [start(y0), start(y0 + 7) + kh_eff);
+//   * each wave multiplies only the 32-key block of the tile that holds its
+//     queries' x windows (they span at most 16 + kw_eff - 1 <= 28 keys from a
+//     4-aligned offset, so kw_eff <= 13), i.e. 8 + 8 MFMAs per tile at D=128;
+//   * element masks: key (t', y', x') is valid for a query iff y' and x' lie
+//     in its windows (t' always does); invalid scores become -inf before the
+//     online softmax, which is the segment kernel's;
+//   * copies, operand prefetch, ping-pong schedule and epilogue follow the
+//     segment-masked kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_common.h"
+#include "attn_fwd_launch.h"
+
+namespace vdx {
+namespace {
+
+// First window position along an axis of length n for coordinate c.
+__device__ __forceinline__ int win_start(int c, int k, int n) {
+    const int keff = min(k, n);
+    return min(max(c - k / 2, 0), n - keff);
+}
+
+constexpr int kBrickY = 8;   // query rows per workgroup
+constexpr int kBrickX = 32;  // query columns per workgroup
+
+template <int D>
+struct Nat {
+    using T = Tile<D>;
+    static constexpr int kQk = T::kSteps;         // K Q^T MFMAs per tile (one 32-key block)
+    static constexpr int kPv = 2 * T::kDBlocks;   // P V MFMAs per tile (two 16-key steps)
+    static constexpr int kNm = kQk + kPv;
+    static constexpr int kRing = kOperandPrefetch + 2;
+
+    char* smem;
+    const __bf16* kp;  // K of (b, h), token 0
+    const __bf16* vp;
+    int64_t tok_stride;
+    int NH, NW, lane, lr, g, w4;
+    float c_log2;
+    // workgroup key rows: t' in [ts, ts + kt), y' in [ylo, ylo + ny)
+    int ts, ylo, ny, x0k, kh, kw;
+    bool tail;          // the tile's 64 keys run past the grid row
+    int kx, vx;         // operand bases of this wave's 32-key block (in a ring slot)
+    int xrel;           // X0 + block offset + 8g - xs_q: key register c is x offset xrel + c
+    int ys_q;           // this lane's query y-window start
+    uint32_t dmo[T::kLoadsPerWave];
+    bf16x8 qreg[T::kSteps];
+    f32x16 oacc[T::kDBlocks];
+    f32x16 sacc;
+    bf16x8 pb[2];
+    bf16x8 ops[kRing];
+    uint32_t vb_next, kb_next;
+    float m_run, l_run;
+
+    __device__ __forceinline__ static int slot_base(int n) {
+        int o = (n % kSlots) * T::kTileBytes;
+        asm volatile("" : "+s"(o));
+        return o;
+    }
+    __device__ __forceinline__ uint32_t vbase(int n) const {
+        return lds_addr(smem) + T::kVRegion + slot_base(n) + vx;
+    }
+    __device__ __forceinline__ uint32_t kbase(int n) const {
+        return lds_addr(smem) + T::kKRegion + slot_base(n) + kx;
+    }
+
+    // ---- tile copies --------------------------------------------------------
+    // Tile a is key row (ts + a / ny, ylo + a % ny), keys x' in [x0k, x0k+64).
+    // Group 0 copies K of tile n+2 in its MFMA phase of iteration n, group 1 V
+    // of tile n+1 (the ring discipline of the segment-masked kernel).
+    struct Copy {
+        const __bf16* src;
+        char* dst;
+        int cnt;
+        bool spread;
+    };
+    template <int G>
+    __device__ __forceinline__ void plan(Copy& c, int a, int at, int ay, int n_act) {
+        c.cnt = 0;
+        c.spread = false;
+        if (a < n_act) {
+            const int64_t tok = ((int64_t)(ts + at) * NH + (ylo + ay)) * NW + x0k;
+            c.src = (G ? vp : kp) + tok * tok_stride;
+            c.dst = smem + (G ? T::kVRegion : T::kKRegion) + slot_base(a) + w4 * T::kLoadsPerWave * 1024;
+            c.spread = !tail;
+            c.cnt = T::kLoadsPerWave;
+        }
+    }
+    // Tail rows (x' past the grid row) read the row's last key instead; the x
+    // masks exclude them.
+    __device__ __forceinline__ void copy_start(const Copy& c) {
+        if (tail && c.cnt > 0) {
+            const int lim = NW - 1 - x0k;
+#pragma unroll
+            for (int j = 0; j < T::kLoadsPerWave; ++j) {
+                const int i = w4 * T::kLoadsPerWave + j;
+                const int r = T::kRowsPerLoad * i + lane / T::kChunks;
+                const int over = max(0, r - lim);
+                dma16(c.src, dmo[j] - (uint32_t)over * (uint32_t)(2 * tok_stride), c.dst + j * 1024);
+            }
+        }
+    }
+    // Load j of a spread copy goes out after MFMA step j*NM/L + 1 of a phase
+    // with NM MFMAs.
+    template <int I, int NM>
+    __device__ __forceinline__ void copy_step(const Copy& c) {
+        constexpr int L = T::kLoadsPerWave;
+        static_assert(NM >= L + 1, "too few MFMA steps to spread the copies over");
+        static_for<0, L>([&](auto jc) {
+            constexpr int j = jc;
+            if constexpr (I == j * NM / L + 1) {
+                if (c.spread) dma16(c.src, dmo[j], c.dst + j * 1024);
+            }
+        });
+    }
+
+    // ---- MFMA phase: K Q^T of tile n, then P V of tile n-1 --------------------
+    template <bool QK, int I>
+    __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb) const {
+        if constexpr (QK && I < kQk) {
+            return *reinterpret_cast<const bf16x8*>(lds_ptr(kb ^ (I << 5)));
+        } else {
+            constexpr int j = QK ? I - kQk : I;
+            constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
+            const char* p = lds_ptr((vb ^ (db << 6)) + kst * 16 * T::kRowBytes);
+            return tr_read8(p, p + 4 * T::kRowBytes);
+        }
+    }
+    template <bool QK, int I>
+    __device__ __forceinline__ void mfma(const bf16x8& a) {
+        if constexpr (QK && I < kQk) {
+            if constexpr (I == 0)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
+            else
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[I], sacc, 0, 0, 0);
+        } else {
+            constexpr int j = QK ? I - kQk : I;
+            constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kst], oacc[db], 0, 0, 0);
+        }
+    }
+    template <bool PV, bool QK>
+    __device__ __forceinline__ void prefetch(int vtile, int ktile) {
+        constexpr int NM = (QK ? kQk : 0) + (PV ? kPv : 0);
+        vb_next = vbase(vtile);
+        kb_next = kbase(ktile);
+        static_for<0, kOperandPrefetch>([&](auto ic) {
+            constexpr int i = ic;
+            if constexpr (i < NM) ops[i % kRing] = operand<QK, i>(vb_next, kb_next);
+        });
+    }
+    template <bool PV, bool QK, bool PRE>
+    __device__ __forceinline__ void mfma_phase(int vtile, int ktile, const Copy& cp) {
+        constexpr int NM = (QK ? kQk : 0) + (PV ? kPv : 0);
+        constexpr int PF = kOperandPrefetch;
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (!PRE) prefetch<PV, QK>(vtile, ktile);
+        const uint32_t vb = vb_next, kb = kb_next;
+        copy_start(cp);
+        static_for<0, NM>([&](auto ic) {
+            constexpr int i = ic;
+            if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb);
+            mfma<QK, i>(ops[i % kRing]);
+            copy_step<i, NM>(cp);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        __builtin_amdgcn_s_setprio(0);
+    }
+
+    // ---- VALU phase --------------------------------------------------------------
+    // Masks for key row y' of the current tile: accumulator register r holds
+    // the block key 16 (r >> 3) + 8 g + (r & 7), i.e. x offset xrel + c_r.
+    __device__ __forceinline__ void mask(int yk) {
+        const bool row_ok = (unsigned)(yk - ys_q) < (unsigned)kh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = 16 * (r >> 3) + (r & 7);
+            const bool ok = row_ok && (unsigned)(xrel + c) < (unsigned)kw;
+            if (!ok) sacc[r] = -INFINITY;
+        }
+    }
+    // Online softmax of the tile's 16 scores per lane with the lazily moved
+    // reference of the segment-masked kernel (P <= 2^kLazyLog2).
+    __device__ __forceinline__ void softmax() {
+        float mx0 = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+        float mx1 = fmaxf(fmaxf(sacc[8], sacc[9]), sacc[10]);
+#pragma unroll
+        for (int r = 3; r < 7; r += 2) {
+            mx0 = fmaxf(fmaxf(mx0, sacc[r]), sacc[r + 1]);
+            mx1 = fmaxf(fmaxf(mx1, sacc[8 + r]), sacc[8 + r + 1]);
+        }
+        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[7]), fmaxf(mx1, sacc[15]))) * c_log2;
+        const bool move = mx > m_run + kLazyLog2;
+        if (__ballot(move) != 0ull) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -msub));
+            ls[r & 3] += p;
+            pb[r >> 3][r & 7] = (__bf16)p;
+        }
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(l_run), "v"(m_run));
+    }
+};
+
+// Ping-pong schedule of group G (see the segment-masked kernel): local
+// iteration n = MFMA phase (K Q^T of tile n, P V of tile n-1) at global phase
+// 2n + G, then the VALU phase (masks and softmax of tile n) at 2n + 1 + G.
+// (mt, my) walk the tile being masked, (ct, cy) the tile being planned.
+template <int G, int D>
+__device__ __forceinline__ void natten_loop(Nat<D>& A, int n_act) {
+    typename Nat<D>::Copy cp;
+    int my = 0, ct = 0, cy = 0;
+    auto advance = [&](int& at, int& ay) {
+        if (++ay == A.ny) {
+            ay = 0;
+            ++at;
+        }
+    };
+    // planned tile index a = n + 2 - G: start the walk there
+    for (int i = 0; i < 2 - G; ++i) advance(ct, cy);
+    auto valu_phase = [&](int n) {
+        A.mask(A.ylo + my);
+        {
+            int dummy = 0;
+            advance(dummy, my);
+        }
+        A.softmax();
+        advance(ct, cy);
+        A.template plan<G>(cp, n + 3 - G, ct, cy, n_act);
+        A.template prefetch<true, true>(n, n + 1);
+        barrier();
+    };
+    A.template plan<G>(cp, 2 - G, ct, cy, n_act);
+    A.template prefetch<false, true>(0, 0);
+    if (G == 1) barrier();  // group 1 idles in global phase 0
+    A.template mfma_phase<false, true, true>(0, 0, cp);
+    wait_copies<Nat<D>::T::kLoadsPerWave>(cp.cnt);
+    barrier();
+    valu_phase(0);
+    for (int n = 1; n < n_act; ++n) {
+        const int c = cp.cnt;
+        A.template mfma_phase<true, true, true>(n - 1, n, cp);
+        wait_copies<Nat<D>::T::kLoadsPerWave>(c);
+        barrier();
+        valu_phase(n);
+    }
+    {
+        const int c = cp.cnt;
+        A.template mfma_phase<true, false, false>(n_act - 1, 0, cp);
+        wait_copies<Nat<D>::T::kLoadsPerWave>(c);
+        barrier();
+    }
+    if (G == 0) barrier();  // group 0 idles in the last global phase
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ out, float* __restrict__ lse, int NT, int NH, int NW, int H, int KT, int KH,
+    int KW, float c_log2, int nby, int nbx, int n_wg) {
+    using T = Tile<D>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    // XCD-contiguous renumbering: consecutive bricks of one head share an L2.
+    const int w = blockIdx.x;
+    const int per = n_wg / kXcds, rem = n_wg % kXcds;
+    const int xcd = w % kXcds;
+    const int lid = xcd * per + min(xcd, rem) + w / kXcds;
+    const int bx = lid % nbx;
+    const int by = (lid / nbx) % nby;
+    const int tq = (lid / (nbx * nby)) % NT;
+    const int bh = lid / (nbx * nby * NT);
+    const int h = bh % H;
+    const int b = bh / H;
+    const int S = NT * NH * NW;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 31, g = lane >> 5;
+    const int grp = wave >> 2;
+    const int y0 = by * kBrickY, x0 = bx * kBrickX;
+    const int yq = y0 + 2 * (wave >> 1) + (lr >> 4);
+    const int xq = x0 + 16 * (wave & 1) + (lr & 15);
+    const bool active = yq < NH && xq < NW;
+    const int qi = (tq * NH + min(yq, NH - 1)) * NW + min(xq, NW - 1);
+
+    Nat<D> A;
+    A.smem = smem;
+    A.tok_stride = (int64_t)H * D;
+    A.kp = k + (int64_t)b * S * A.tok_stride + (int64_t)h * D;
+    A.vp = v + (int64_t)b * S * A.tok_stride + (int64_t)h * D;
+    A.NH = NH;
+    A.NW = NW;
+    A.lane = lane;
+    A.lr = lr;
+    A.g = g;
+    A.w4 = wave & 3;
+    A.c_log2 = c_log2;
+    A.kh = min(KH, NH);
+    A.kw = min(KW, NW);
+    const int kt = min(KT, NT);
+
+    // ---- workgroup key rows and the x range of the tiles ----------------------
+    A.ts = win_start(tq, KT, NT);
+    A.ylo = win_start(y0, KH, NH);
+    A.ny = win_start(min(y0 + kBrickY - 1, NH - 1), KH, NH) + A.kh - A.ylo;
+    A.x0k = win_start(x0, KW, NW) & ~3;
+    A.tail = A.x0k + kBk > NW;
+    const int n_act = kt * A.ny;
+    // this wave's 32-key block inside the tile, and the lane's windows
+    const int xw = min(x0 + 16 * (wave & 1), NW - 1);
+    const int boff = min((win_start(xw, KW, NW) & ~3) - A.x0k, kBk - 32);
+    A.ys_q = win_start(min(yq, NH - 1), KH, NH);
+    const int xs_q = win_start(min(xq, NW - 1), KW, NW);
+    A.xrel = A.x0k + boff + 8 * g - xs_q;
+    if (!active) A.ys_q = -(1 << 30);  // no key row passes the row test
+
+    // ---- Q slice -> registers ----------------------------------------------------
+    {
+        const __bf16* qrow = q + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks)
+            A.qreg[ks] = active ? *reinterpret_cast<const bf16x8*>(qrow + ks * 16) : bf16x8{};
+    }
+    // ---- per-lane LDS offsets (operand rows shifted by the block offset) -------
+    {
+        const int krow = boff + swap23(lr);
+        A.kx = krow * T::kRowBytes + ((g ^ k_swz<D>(krow)) << 4);
+        const int qg = lane >> 4, j = lane & 15;
+        const int key = boff + 8 * (qg >> 1) + (j >> 2);
+        const int vsw = v_swz<D>(key);
+        A.vx = key * T::kRowBytes + 32 * ((qg & 1) ^ vsw) + 16 * ((j & 3) >> 1) + 8 * (j & 1);
+#pragma unroll
+        for (int jj = 0; jj < T::kLoadsPerWave; ++jj) {
+            const int i = A.w4 * T::kLoadsPerWave + jj;
+            const int r = T::kRowsPerLoad * i + lane / T::kChunks;
+            const int pos = lane % T::kChunks;
+            const int c = grp ? 2 * ((pos >> 1) ^ v_swz<D>(r)) + (pos & 1) : (pos ^ k_swz<D>(r));
+            A.dmo[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + c * 8);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < T::kDBlocks; ++i) A.oacc[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) A.pb[i] = bf16x8{};
+    A.m_run = -INFINITY;
+    A.l_run = 0.f;
+
+    // ---- prologue: K of tiles 0 and 1 (group 0), V of tile 0 (group 1) ---------
+    {
+        typename Nat<D>::Copy c;
+        if (grp == 0) {
+            int at = 0, ay = 0;
+            for (int a = 0; a < 2; ++a) {
+                A.template plan<0>(c, a, at, ay, n_act);
+                A.copy_start(c);
+                if (c.spread) {
+#pragma unroll
+                    for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
+                }
+                if (++ay == A.ny) ay = 0, ++at;
+            }
+        } else {
+            A.template plan<1>(c, 0, 0, 0, n_act);
+            A.copy_start(c);
+            if (c.spread) {
+#pragma unroll
+                for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
+            }
+        }
+    }
+    wait_vm(0);
+    barrier();
+    asm volatile("" ::"v"(A.qreg[0]), "v"(A.qreg[T::kSteps - 1]));
+
+    if (grp == 0)
+        natten_loop<0>(A, n_act);
+    else
+        natten_loop<1>(A, n_act);
+
+    // ---- epilogue -----------------------------------------------------------------
+    const float l_tot = pair_sum(A.l_run);
+    if (active) {
+        __bf16* orow = out + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D;
+        const float inv = 1.0f / l_tot;
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * g;
+                __bf16 o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(A.oacc[db][4 * r4 + e] * inv);
+                *reinterpret_cast<uint2*>(orow + d) = *reinterpret_cast<const uint2*>(o4);
+            }
+        }
+        if (g == 0) lse[((int64_t)b * H + h) * S + qi] = (A.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+}
+
+template <int D>
+hipError_t launch_t(const NattenArgs& a, hipStream_t stream) {
+    using T = Tile<D>;
+    const int nby = (a.NH + kBrickY - 1) / kBrickY;
+    const int nbx = (a.NW + kBrickX - 1) / kBrickX;
+    const int n_wg = a.B * a.H * a.NT * nby * nbx;
+    const float c_log2 = a.scale * kLog2e;
+    hipLaunchKernelGGL((natten_fwd_kernel<D>), dim3(n_wg), dim3(kThreads), (size_t)T::kRingBytes, stream,
+                       reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
+                       reinterpret_cast<const __bf16*>(a.v), reinterpret_cast<__bf16*>(a.out), a.lse,
+                       a.NT, a.NH, a.NW, a.H, a.KT, a.KH, a.KW, c_log2, nby, nbx, n_wg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t natten_workgroups(const NattenArgs& a) {
+    return (int64_t)a.B * a.H * a.NT * ((a.NH + kBrickY - 1) / kBrickY) *
+           ((a.NW + kBrickX - 1) / kBrickX);
+}
+
+hipError_t launch_natten_fwd(const NattenArgs& a, hipStream_t stream) {
+    return a.D == 128 ? launch_t<128>(a, stream) : launch_t<64>(a, stream);
+}
+
+}  // namespace vdx

@@ -1,6 +1,6 @@
 // vdx_attn_api.hip -- the C ABI declared in include/vdx_attn.h: argument
 // validation (before any HIP call), the per-device architecture check, and
-// the hand-off to the gfx950 launcher.
+// the hand-off to the gfx950 launchers.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -61,6 +61,29 @@ int validate(const void* q, const void* k, const void* v, const int32_t* seg_q,
     return VDX_OK;
 }
 
+int validate_natten(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    int B, int NT, int NH, int NW, int H, int D, int KT, int KH, int KW, float scale) {
+    if (!q || !k || !v || !out || !lse) return VDX_ERR_NULL_PTR;
+    if (B < 1 || NT < 1 || NH < 1 || NW < 1 || H < 1) return VDX_ERR_SHAPE;
+    const int64_t S = (int64_t)NT * NH * NW;
+    if (S > INT32_MAX) return VDX_ERR_SHAPE;
+    if (D > 0) {
+        const __int128 n = (__int128)B * S * H * D;
+        if (n > (__int128)INT64_MAX / 2) return VDX_ERR_SHAPE;
+        if ((int64_t)64 * H * D > INT32_MAX) return VDX_ERR_SHAPE;
+    }
+    vdx::NattenArgs a{q, k, v, nullptr, nullptr, B, NT, NH, NW, H, D, KT, KH, KW, scale};
+    if (vdx::natten_workgroups(a) > INT32_MAX) return VDX_ERR_SHAPE;
+    if (D != 64 && D != 128) return VDX_ERR_HEAD_DIM;
+    if (KT < 1 || KH < 1 || KW < 1 || KT % 2 == 0 || KH % 2 == 0 || KW % 2 == 0) return VDX_ERR_WINDOW;
+    if ((KW < NW ? KW : NW) > vdx::kNattenMaxWindowX) return VDX_ERR_WINDOW;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return VDX_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return VDX_ERR_ALIGN;
+    if (!aligned(lse, 4)) return VDX_ERR_ALIGN;
+    return VDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,17 +100,31 @@ __attribute__((visibility("default"))) int vdx_attn_fwd(
     return VDX_OK;
 }
 
+__attribute__((visibility("default"))) int vdx_natten3d_fwd(
+    const void* q, const void* k, const void* v, void* out, float* lse, int B, int NT, int NH, int NW,
+    int H, int D, int KT, int KH, int KW, float scale, hipStream_t stream) {
+    int rc = validate_natten(q, k, v, out, lse, B, NT, NH, NW, H, D, KT, KH, KW, scale);
+    if (rc != VDX_OK) return rc;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    vdx::NattenArgs a{q, k, v, out, lse, B, NT, NH, NW, H, D, KT, KH, KW, scale};
+    if (vdx::launch_natten_fwd(a, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
 __attribute__((visibility("default"))) const char* vdx_status_str(int status) {
     switch (status) {
         case VDX_OK: return "VDX_OK";
         case VDX_ERR_NULL_PTR: return "VDX_ERR_NULL_PTR: q, k, v, out or lse is NULL";
         case VDX_ERR_SEG_PAIR: return "VDX_ERR_SEG_PAIR: exactly one of seg_q/seg_kv is NULL";
-        case VDX_ERR_SHAPE: return "VDX_ERR_SHAPE: B, S or H out of range";
+        case VDX_ERR_SHAPE: return "VDX_ERR_SHAPE: batch, sequence, grid or head count out of range";
         case VDX_ERR_HEAD_DIM: return "VDX_ERR_HEAD_DIM: D must be 64 or 128";
         case VDX_ERR_SCALE: return "VDX_ERR_SCALE: scale must be finite and > 0";
         case VDX_ERR_ALIGN: return "VDX_ERR_ALIGN: q/k/v/out need 16-byte, seg/lse 4-byte alignment";
         case VDX_ERR_DEVICE: return "VDX_ERR_DEVICE: current device is not gfx950";
         case VDX_ERR_LAUNCH: return "VDX_ERR_LAUNCH: kernel launch failed";
+        case VDX_ERR_WINDOW:
+            return "VDX_ERR_WINDOW: window sizes must be odd and >= 1, the x window at most 13";
         default: return "VDX_ERR_UNKNOWN";
     }
 }

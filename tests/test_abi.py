@@ -33,7 +33,7 @@ def native():
 
 def test_exports_every_declared_function(native):
     names = header_functions()
-    assert names == sorted(["vdx_attn_fwd", "vdx_status_str", "vdx_abi_version"])
+    assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_status_str", "vdx_abi_version"])
     for n in names:
         assert hasattr(native.lib, n), n
 
@@ -144,3 +144,67 @@ def test_runs_on_side_stream(need_gpu):
         o, l = vdx.attn_fwd(q, q, q)
     s.synchronize()
     assert torch.equal(o, ref) and torch.equal(l, ref_lse)
+
+
+# --- vdx_natten3d_fwd validation (no GPU needed) ----------------------------------
+def ncall(native, q=A, k=A + 0x100, v=A + 0x200, out=A + 0x300, lse=A + 0x400, B=1, NT=4, NH=8,
+          NW=32, H=2, D=128, KT=3, KH=5, KW=11, scale=0.125):
+    return native.natten3d_fwd_raw(q, k, v, out, lse, B, NT, NH, NW, H, D, KT, KH, KW, scale, 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out", "lse"])
+def test_natten_null_pointer(native, which):
+    assert ncall(native, **{which: 0}) == native.VDX_ERR_NULL_PTR
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(NT=0), dict(NH=-1), dict(NW=0), dict(H=0),
+                                dict(NT=2048, NH=2048, NW=1024), dict(H=1 << 18)])
+def test_natten_shape(native, kw):
+    assert ncall(native, **kw) == native.VDX_ERR_SHAPE
+
+
+@pytest.mark.parametrize("D", [0, 32, 96, 256])
+def test_natten_head_dim(native, D):
+    assert ncall(native, D=D) == native.VDX_ERR_HEAD_DIM
+
+
+@pytest.mark.parametrize("kw", [dict(KT=0), dict(KH=4), dict(KW=2), dict(KT=-3), dict(KW=15),
+                                dict(KW=21, NW=64)])
+def test_natten_window(native, kw):
+    assert ncall(native, **kw) == native.VDX_ERR_WINDOW
+
+
+def test_natten_wide_window_on_narrow_axis_is_accepted(native):
+    # min(KW, NW) is what counts: a 21-wide window on an 8-wide grid is the
+    # whole axis, so validation passes and only the device check remains
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this path would launch on fake addresses")
+    assert ncall(native, KW=21, NW=8) == native.VDX_ERR_DEVICE
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan"), float("inf")])
+def test_natten_scale(native, scale):
+    assert ncall(native, scale=scale) == native.VDX_ERR_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(q=A + 2), dict(k=A + 8), dict(v=A + 4), dict(out=A + 6),
+                                dict(lse=A + 2)])
+def test_natten_alignment(native, kw):
+    assert ncall(native, **kw) == native.VDX_ERR_ALIGN
+
+
+def test_natten_validation_order(native):
+    # NULL beats shape beats head dim beats window beats scale beats alignment
+    assert ncall(native, q=0, B=0, D=3, KW=2, scale=-1.0) == native.VDX_ERR_NULL_PTR
+    assert ncall(native, B=0, D=3, KW=2, scale=-1.0, k=A + 1) == native.VDX_ERR_SHAPE
+    assert ncall(native, D=3, KW=2, scale=-1.0, k=A + 1) == native.VDX_ERR_HEAD_DIM
+    assert ncall(native, KW=2, scale=-1.0, k=A + 1) == native.VDX_ERR_WINDOW
+    assert ncall(native, scale=-1.0, k=A + 1) == native.VDX_ERR_SCALE
+    assert ncall(native, k=A + 1) == native.VDX_ERR_ALIGN
+
+
+def test_natten_python_wrapper_rejects_bad_grid():
+    import spatiotemporal_attention_amd as vdx
+    q = torch.zeros(1, 10, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vdx.natten3d_fwd(q, q, q, grid=(2, 2, 2), window=(1, 1, 1))
