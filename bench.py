@@ -14,6 +14,10 @@ Prints ONE JSON line:
                the HBM traffic from rocprofv3 counters when they are current
   cpu_baseline the fp64 oracle timed on a bounded row sample on the host cores
 
+With --workload natten_vae_decoder (or natten_tiny) the step is one
+vdx_natten3d_fwd call instead (3D neighbourhood attention over a t x h x w
+grid), and the FLOP count is that of the window pairs: 4*D*H*B*S*|window|.
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--copy-calib]
 """
@@ -38,8 +42,10 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=75,600 H=40 D=128 (1 GPU)"
+NATTEN_METRIC = "3D neighbourhood attention TFLOP/s (window pairs) and % of bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
-                  for f in ("attn_fwd_kernel.hip", "attn_fwd_launch.h", "vdx_attn_api.hip")]
+                  for f in ("attn_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
+                            "vdx_attn_api.hip")]
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -138,12 +144,132 @@ def cpu_baseline(w: W.Workload, x, target_s: float = 15.0):
                       f"{dt:.1f} s on {cores} threads"}
 
 
+def natten_window_volume(w) -> int:
+    return math.prod(min(k, n) for k, n in zip(w.window, w.grid))
+
+
+def natten_executed_flop(w) -> float:
+    """MFMA flops the kernel issues: per workgroup (a 1x8x32 query brick) one
+    64-key row tile per key row of its window union, 8 waves x 32 queries x
+    32 keys x 2 products x 2*D each."""
+    NT, NH, NW = w.grid
+    KT, KH, KW = w.window
+
+    def start(c, k, n):
+        ke = min(k, n)
+        return min(max(c - k // 2, 0), n - ke)
+
+    tiles = 0
+    for by in range((NH + 7) // 8):
+        y0 = 8 * by
+        ny = start(min(y0 + 7, NH - 1), KH, NH) + min(KH, NH) - start(y0, KH, NH)
+        tiles += min(KT, NT) * ny
+    tiles *= NT * ((NW + 31) // 32)
+    return float(tiles) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
+
+
+def natten_cpu_baseline(w, x, target_s: float = 15.0):
+    import oracle
+    cores = oracle.default_threads()
+    qb, kb, vb = W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"])
+    rng = np.random.default_rng(7)
+
+    def rows_for(n):
+        return np.stack([rng.integers(0, w.B, n), rng.integers(0, w.H, n),
+                         rng.integers(0, w.S, n)], 1).astype(np.int64)
+
+    probe = rows_for(cores * 16)
+    t0 = time.perf_counter()
+    oracle.natten3d_fwd(qb, kb, vb, w.grid, w.window, float(np.float32(w.scale)), rows=probe,
+                        n_threads=cores)
+    dt = time.perf_counter() - t0
+    n = max(cores, int(len(probe) * target_s / max(dt, 1e-3)))
+    rows = rows_for(n)
+    t0 = time.perf_counter()
+    oracle.natten3d_fwd(qb, kb, vb, w.grid, w.window, float(np.float32(w.scale)), rows=rows,
+                        n_threads=cores)
+    dt = time.perf_counter() - t0
+    rate = 4.0 * w.D * natten_window_volume(w) * n / dt / 1e12
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} random (b,h,i) rows of {w.name}, each over its full window, "
+                      f"{dt:.1f} s on {cores} threads"}
+
+
+def time_steps(step, stream, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({warmup} steps)")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_per_step = wall * 1e3 / steps
+    log(f"timed {steps} steps: {ms_per_step:.3f} ms/step wall, "
+        f"kernel mean {np.mean(kernel_ms):.3f} ms (min {np.min(kernel_ms):.3f}, "
+        f"median {np.median(kernel_ms):.3f})")
+    return ms_per_step, float(np.mean(kernel_ms))
+
+
+def natten_main(args, vdx):
+    w = W.NATTEN_WORKLOADS[args.workload]
+    log(f"workload {w.name}: B={w.B} grid={w.grid} window={w.window} H={w.H} D={w.D}")
+    x = W.make_natten_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {n: t.to(dev) for n, t in x.items()}
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        vdx.natten3d_fwd(d["q"], d["k"], d["v"], w.grid, w.window, scale=w.scale, out=out,
+                         lse=lse, stream=stream)
+
+    ms_per_step, kernel_ms = time_steps(step, stream, args.steps, args.warmup)
+    flop = 4.0 * w.D * w.H * w.B * w.S * natten_window_volume(w)
+    executed = natten_executed_flop(w)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    n = w.B * w.S * w.H * w.D
+    line = {
+        "metric": NATTEN_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "grid": list(w.grid), "window": list(w.window),
+                   "H": w.H, "D": w.D, "flop_per_step": flop,
+                   "executed_mfma_flop_per_step": executed,
+                   "window_pair_fraction_of_executed": round(flop / executed, 4),
+                   "peak_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "executed_achieved": round(executed / (kernel_ms * 1e-3) / 1e12, 2),
+                     "traffic": None,
+                     "algorithmic_bytes": 4 * 2 * n + 4 * w.B * w.H * w.S,
+                     "kernel_ms_mean": round(kernel_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        line["cpu_baseline"] = natten_cpu_baseline(w, x, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default=W.HEADLINE,
+                    choices=sorted(W.WORKLOADS) + sorted(W.NATTEN_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
@@ -159,6 +285,9 @@ def main():
 
     if args.copy_calib:
         copy_calibration()
+        return
+    if args.workload in W.NATTEN_WORKLOADS:
+        natten_main(args, vdx)
         return
 
     w = W.WORKLOADS[args.workload]
