@@ -24,17 +24,26 @@ VALU_SGPR_WAIT = 5
 SALU_M0_WAIT = 1
 
 
-@pytest.fixture(scope="module")
-def asm_text():
+def _compile(src):
     flags = [f for f in B.HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
         cmd = [B.hipcc(), *flags, "--cuda-device-only", "-S", "-I", B.INCLUDE, "-I", B.CSRC,
-               os.path.join(B.CSRC, "attn_fwd_kernel.hip"), "-o", out]
+               os.path.join(B.CSRC, src), "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         with open(out) as f:
             return f.read()
+
+
+@pytest.fixture(scope="module")
+def asm_text():
+    return _compile("attn_fwd_kernel.hip")
+
+
+@pytest.fixture(scope="module")
+def natten_asm_text():
+    return _compile("natten_fwd_kernel.hip")
 
 
 def _sregs(tok: str):
@@ -110,3 +119,11 @@ def test_no_kernel_spills_to_scratch(asm_text):
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm_text)]
     assert len(sizes) == 4  # D in {64, 128} x {unmasked, segment-masked}
     assert sizes == [0, 0, 0, 0]
+
+
+def test_neighbourhood_kernel_wait_states_and_no_spills(natten_asm_text):
+    n = sum(1 for t in _instructions(natten_asm_text.split("\n")) if t.startswith("global_load_lds"))
+    assert n > 0
+    assert lds_dma_hazards(natten_asm_text) == []
+    sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", natten_asm_text)]
+    assert sizes == [0, 0]  # D in {64, 128}
