@@ -1,5 +1,5 @@
-"""CPU oracles for segment-masked, non-causal softmax self-attention and for
-3D neighbourhood (windowed) self-attention.
+"""CPU oracles for segment-masked, non-causal softmax self-attention (forward
+and gradient) and for 3D neighbourhood (windowed) self-attention.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check
 and by the benchmark's CPU-baseline leg, never by the product path.  It shares
@@ -11,11 +11,14 @@ softmax(scale * Q K^T, masked by segment IDs) V -- vidax paper, section 2
 Table 4, group 2 for SegmentIds) and ``natten_oracle.c`` (the same softmax
 restricted to each query's 3D neighbourhood window -- section 2 for the
 windowed-attention fallback of the neighbourhood-attention VAE decoder,
-Appendix A, Table 4, group 4 for its 11 x 11 x 11 window).  This wrapper only
-marshals numpy arrays.
+Appendix A, Table 4, group 4 for its 11 x 11 x 11 window) and
+``attn_bwd_oracle.c`` (the exact gradients of the segment-masked forward with
+respect to q, k, v -- section 5 lists training as future work).  This
+wrapper only marshals numpy arrays.
 
-Every function here has pins in ``tests/test_oracle.py`` and
-``tests/test_natten_oracle.py``; their module docstrings say what pins what.
+Every function here has pins in ``tests/test_oracle.py``,
+``tests/test_natten_oracle.py`` and ``tests/test_bwd_oracle.py``; their
+module docstrings say what pins what.
 """
 from __future__ import annotations
 
@@ -47,6 +50,9 @@ def _load(path: Optional[str] = None):
     i64 = ctypes.c_int64
     f.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double,
                   p, i64, p, p, p, ctypes.c_int]
+    bw = lib.vdx_oracle_attn_bwd
+    bw.restype = ctypes.c_int
+    bw.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double, p, p, p, ctypes.c_int]
     g = lib.vdx_oracle_natten3d_fwd
     g.restype = ctypes.c_int
     g.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
@@ -160,3 +166,30 @@ def natten3d_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
     return out, lse
+
+
+def attn_bwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dout_bits: np.ndarray,
+             seg_q: Optional[np.ndarray], seg_kv: Optional[np.ndarray], scale: float,
+             n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """fp64 gradients (dq, dk, dv), each [B, S, H, D], of sum(dout * out) for
+    the segment-masked forward, on bf16 bit patterns.  Dense S x S per head:
+    for S up to a few thousand."""
+    lib = _load()
+    for a in (q_bits, k_bits, v_bits, dout_bits):
+        assert a.dtype == np.uint16 and a.ndim == 4
+    B, S, H, D = q_bits.shape
+    arrs = [np.ascontiguousarray(a) for a in (q_bits, k_bits, v_bits, dout_bits)]
+    if (seg_q is None) != (seg_kv is None):
+        raise ValueError("seg_q and seg_kv must both be given or both be None")
+    if seg_q is not None:
+        seg_q = np.ascontiguousarray(seg_q, dtype=np.int32)
+        seg_kv = np.ascontiguousarray(seg_kv, dtype=np.int32)
+    dq = np.zeros((B, S, H, D), dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    rc = lib.vdx_oracle_attn_bwd(*[_ptr(a) for a in arrs], _ptr(seg_q), _ptr(seg_kv),
+                                 B, S, H, D, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 int(n_threads if n_threads is not None else default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle returned {rc}")
+    return dq, dk, dv

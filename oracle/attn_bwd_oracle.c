@@ -1,0 +1,176 @@
+/*
+ * attn_bwd_oracle.c -- plain, slow, scalar fp64 CPU oracle for the gradient
+ * of segment-masked, non-causal softmax self-attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file or the library built from it; only the tests, the
+ * package smoke check and the benchmark's CPU-baseline leg do.  It shares no
+ * code, header, helper or constant with the HIP path.
+ *
+ * What it computes.  The forward is out_i = sum_j P_ij v_j with
+ * P_ij = exp(s_ij) / sum_{j' in J_i} exp(s_ij'), s_ij = scale * q_i . k_j over
+ * the valid keys J_i of row i (segment rule of the forward oracle; a row with
+ * no valid key has out_i = 0).  Given dout, this returns the exact gradients
+ * of sum_i dout_i . out_i (vidax paper, arXiv:2609.18077: section 5 lists
+ * training and fine-tuning as future work; the forward's log-sum-exp output
+ * is what a backward pass reuses):
+ *   dv_j = sum_i P_ij dout_i
+ *   dP_ij = dout_i . v_j,  delta_i = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - delta_i)
+ *   dq_i = scale * sum_j dS_ij k_j,  dk_j = scale * sum_i dS_ij q_i
+ * P, delta and everything else are recomputed here from q, k, v in fp64; the
+ * oracle takes no forward output.  Rows with no valid key contribute nothing
+ * and get dq_i = 0.  Inputs are bf16 bit patterns [B, S, H, D]; outputs fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_EXPORT __attribute__((visibility("default")))
+
+static double b2d(uint16_t bits) {
+    uint32_t w = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    const int32_t *seg_q, *seg_kv;
+    int64_t B, S, H, D;
+    double scale;
+    double *dq, *dk, *dv;
+    int64_t next;
+    pthread_mutex_t mu;
+} bjob_t;
+
+static int64_t at(const bjob_t *J, int64_t b, int64_t s, int64_t h) {
+    return ((b * J->S + s) * J->H + h) * J->D;
+}
+
+static int valid(const bjob_t *J, int64_t b, int64_t i, int64_t j) {
+    if (!J->seg_q) return 1;
+    const int32_t c = J->seg_q[b * J->S + i];
+    return c != 0 && J->seg_kv[b * J->S + j] == c;
+}
+
+/* One (b, h): dense S x S probabilities and score gradients in fp64. */
+static int one_head(const bjob_t *J, int64_t b, int64_t h) {
+    const int64_t S = J->S, D = J->D;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(S * S));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)(S * S));
+    if (!P || !dS) {
+        free(P);
+        free(dS);
+        return 1;
+    }
+    for (int64_t i = 0; i < S; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < S; ++j) {
+            if (!valid(J, b, i, j)) {
+                P[i * S + j] = -INFINITY;
+                continue;
+            }
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                dot += b2d(J->q[at(J, b, i, h) + d]) * b2d(J->k[at(J, b, j, h) + d]);
+            P[i * S + j] = J->scale * dot;
+            if (P[i * S + j] > m) m = P[i * S + j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+            const double w = (m == -INFINITY || P[i * S + j] == -INFINITY) ? 0.0 : exp(P[i * S + j] - m);
+            P[i * S + j] = w;
+            l += w;
+        }
+        for (int64_t j = 0; j < S; ++j) P[i * S + j] = (l > 0.0) ? P[i * S + j] / l : 0.0;
+        /* dP_ij = dout_i . v_j over valid pairs, delta_i = sum_j P_ij dP_ij */
+        double delta = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+            double dp = 0.0;
+            if (valid(J, b, i, j))
+                for (int64_t d = 0; d < D; ++d)
+                    dp += b2d(J->dout[at(J, b, i, h) + d]) * b2d(J->v[at(J, b, j, h) + d]);
+            dS[i * S + j] = dp;
+            delta += P[i * S + j] * dp;
+        }
+        for (int64_t j = 0; j < S; ++j) dS[i * S + j] = P[i * S + j] * (dS[i * S + j] - delta);
+    }
+    for (int64_t i = 0; i < S; ++i)
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < S; ++j) acc += dS[i * S + j] * b2d(J->k[at(J, b, j, h) + d]);
+            J->dq[at(J, b, i, h) + d] = J->scale * acc;
+        }
+    for (int64_t j = 0; j < S; ++j)
+        for (int64_t d = 0; d < D; ++d) {
+            double acck = 0.0, accv = 0.0;
+            for (int64_t i = 0; i < S; ++i) {
+                acck += dS[i * S + j] * b2d(J->q[at(J, b, i, h) + d]);
+                accv += P[i * S + j] * b2d(J->dout[at(J, b, i, h) + d]);
+            }
+            J->dk[at(J, b, j, h) + d] = J->scale * acck;
+            J->dv[at(J, b, j, h) + d] = accv;
+        }
+    free(P);
+    free(dS);
+    return 0;
+}
+
+static void *b_worker(void *arg) {
+    bjob_t *J = (bjob_t *)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        const int64_t r = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (r >= J->B * J->H) break;
+        if (one_head(J, r / J->H, r % J->H)) return (void *)1;
+    }
+    return NULL;
+}
+
+/*
+ * vdx_oracle_attn_bwd
+ *   q, k, v, dout  bf16 bit patterns [B, S, H, D], host memory.
+ *   seg_q/seg_kv   int32 [B, S] or both NULL (unmasked).
+ *   dq, dk, dv     fp64 [B, S, H, D] outputs.
+ *   n_threads      worker threads over (b, h) (<= 0 -> online CPUs).
+ * Memory: two S x S fp64 matrices per thread.  Returns 0 on success, 1 on bad
+ * arguments, 2 on allocation failure.
+ */
+ORACLE_EXPORT int vdx_oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                      const uint16_t *dout, const int32_t *seg_q, const int32_t *seg_kv,
+                                      int64_t B, int64_t S, int64_t H, int64_t D, double scale,
+                                      double *dq, double *dk, double *dv, int n_threads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+    if ((seg_q == NULL) != (seg_kv == NULL)) return 1;
+    if (B < 1 || S < 1 || H < 1 || D < 1 || S > 16384) return 1;
+    if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (n_threads < 1) n_threads = 1;
+    bjob_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dout = dout;
+    J.seg_q = seg_q; J.seg_kv = seg_kv;
+    J.B = B; J.S = S; J.H = H; J.D = D;
+    J.scale = scale;
+    J.dq = dq; J.dk = dk; J.dv = dv;
+    pthread_mutex_init(&J.mu, NULL);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    if (!th) return 2;
+    int started = 0, failed = 0;
+    for (int t = 0; t < n_threads; ++t)
+        if (pthread_create(&th[t], NULL, b_worker, &J) == 0) ++started;
+    if (started == 0) failed = (b_worker(&J) != NULL);
+    for (int t = 0; t < started; ++t) {
+        void *ret = NULL;
+        pthread_join(th[t], &ret);
+        if (ret != NULL) failed = 1;
+    }
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return failed ? 2 : 0;
+}
