@@ -52,7 +52,11 @@ def _load(path: Optional[str] = None):
                   p, i64, p, p, p, ctypes.c_int]
     bw = lib.vdx_oracle_attn_bwd
     bw.restype = ctypes.c_int
-    bw.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double, p, p, p, ctypes.c_int]
+    bw.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double, p, p, p, p, p, p,
+                   ctypes.c_int]
+    br = lib.vdx_oracle_attn_bwd_dq_rows
+    br.restype = ctypes.c_int
+    br.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double, p, i64, p, p, ctypes.c_int]
     g = lib.vdx_oracle_natten3d_fwd
     g.restype = ctypes.c_int
     g.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
@@ -170,10 +174,12 @@ def natten3d_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
 
 def attn_bwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dout_bits: np.ndarray,
              seg_q: Optional[np.ndarray], seg_kv: Optional[np.ndarray], scale: float,
-             n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+             n_threads: Optional[int] = None, sensitivity: bool = False):
     """fp64 gradients (dq, dk, dv), each [B, S, H, D], of sum(dout * out) for
     the segment-masked forward, on bf16 bit patterns.  Dense S x S per head:
-    for S up to a few thousand."""
+    for S up to a few thousand.  With sensitivity=True also returns (tq, tk,
+    tv): per element, the sum of |terms| whose one-time rounding to relative
+    precision u moves the result by at most u * t."""
     lib = _load()
     for a in (q_bits, k_bits, v_bits, dout_bits):
         assert a.dtype == np.uint16 and a.ndim == 4
@@ -187,9 +193,41 @@ def attn_bwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dout_bi
     dq = np.zeros((B, S, H, D), dtype=np.float64)
     dk = np.zeros_like(dq)
     dv = np.zeros_like(dq)
+    ts = [np.zeros_like(dq) for _ in range(3)] if sensitivity else [None] * 3
     rc = lib.vdx_oracle_attn_bwd(*[_ptr(a) for a in arrs], _ptr(seg_q), _ptr(seg_kv),
                                  B, S, H, D, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 *[_ptr(t) for t in ts],
                                  int(n_threads if n_threads is not None else default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
+    if sensitivity:
+        return dq, dk, dv, ts[0], ts[1], ts[2]
     return dq, dk, dv
+
+
+def attn_bwd_dq_rows(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                     dout_bits: np.ndarray, seg_q: Optional[np.ndarray],
+                     seg_kv: Optional[np.ndarray], scale: float, rows: np.ndarray,
+                     n_threads: Optional[int] = None, sensitivity: bool = False):
+    """fp64 dq [n_rows, D] of the listed (b, h, i) rows only, any S (O(S D)
+    per row); with sensitivity=True also tq [n_rows, D] (see attn_bwd)."""
+    lib = _load()
+    for a in (q_bits, k_bits, v_bits, dout_bits):
+        assert a.dtype == np.uint16 and a.ndim == 4
+    B, S, H, D = q_bits.shape
+    arrs = [np.ascontiguousarray(a) for a in (q_bits, k_bits, v_bits, dout_bits)]
+    if (seg_q is None) != (seg_kv is None):
+        raise ValueError("seg_q and seg_kv must both be given or both be None")
+    if seg_q is not None:
+        seg_q = np.ascontiguousarray(seg_q, dtype=np.int32)
+        seg_kv = np.ascontiguousarray(seg_kv, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    dq = np.zeros((rows.shape[0], D), dtype=np.float64)
+    tq = np.zeros_like(dq) if sensitivity else None
+    rc = lib.vdx_oracle_attn_bwd_dq_rows(*[_ptr(a) for a in arrs], _ptr(seg_q), _ptr(seg_kv),
+                                         B, S, H, D, float(scale), _ptr(rows), rows.shape[0],
+                                         _ptr(dq), _ptr(tq),
+                                         int(n_threads if n_threads is not None else default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle returned {rc}")
+    return (dq, tq) if sensitivity else dq

@@ -44,6 +44,7 @@ typedef struct {
     int64_t B, S, H, D;
     double scale;
     double *dq, *dk, *dv;
+    double *tq, *tk, *tv; /* optional rounding-sensitivity sums (NULL: skip) */
     int64_t next;
     pthread_mutex_t mu;
 } bjob_t;
@@ -63,9 +64,11 @@ static int one_head(const bjob_t *J, int64_t b, int64_t h) {
     const int64_t S = J->S, D = J->D;
     double *P = (double *)malloc(sizeof(double) * (size_t)(S * S));
     double *dS = (double *)malloc(sizeof(double) * (size_t)(S * S));
-    if (!P || !dS) {
+    double *E = J->tq ? (double *)malloc(sizeof(double) * (size_t)S) : NULL;
+    if (!P || !dS || (J->tq && !E)) {
         free(P);
         free(dS);
+        free(E);
         return 1;
     }
     for (int64_t i = 0; i < S; ++i) {
@@ -99,12 +102,31 @@ static int one_head(const bjob_t *J, int64_t b, int64_t h) {
             delta += P[i * S + j] * dp;
         }
         for (int64_t j = 0; j < S; ++j) dS[i * S + j] = P[i * S + j] * (dS[i * S + j] - delta);
+        if (E) {
+            /* E_i = sum_j P_ij sum_d |dout_id| |v_jd|: bounds how far delta_i
+             * moves per unit relative error in out_i's terms */
+            double e = 0.0;
+            for (int64_t j = 0; j < S; ++j) {
+                if (P[i * S + j] == 0.0) continue;
+                double a = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    a += fabs(b2d(J->dout[at(J, b, i, h) + d])) * fabs(b2d(J->v[at(J, b, j, h) + d]));
+                e += P[i * S + j] * a;
+            }
+            E[i] = e;
+        }
     }
     for (int64_t i = 0; i < S; ++i)
         for (int64_t d = 0; d < D; ++d) {
             double acc = 0.0;
             for (int64_t j = 0; j < S; ++j) acc += dS[i * S + j] * b2d(J->k[at(J, b, j, h) + d]);
             J->dq[at(J, b, i, h) + d] = J->scale * acc;
+            if (E) {
+                double t = 0.0;
+                for (int64_t j = 0; j < S; ++j)
+                    t += (fabs(dS[i * S + j]) + P[i * S + j] * E[i]) * fabs(b2d(J->k[at(J, b, j, h) + d]));
+                J->tq[at(J, b, i, h) + d] = J->scale * t;
+            }
         }
     for (int64_t j = 0; j < S; ++j)
         for (int64_t d = 0; d < D; ++d) {
@@ -115,9 +137,19 @@ static int one_head(const bjob_t *J, int64_t b, int64_t h) {
             }
             J->dk[at(J, b, j, h) + d] = J->scale * acck;
             J->dv[at(J, b, j, h) + d] = accv;
+            if (E) {
+                double tk = 0.0, tv = 0.0;
+                for (int64_t i = 0; i < S; ++i) {
+                    tk += (fabs(dS[i * S + j]) + P[i * S + j] * E[i]) * fabs(b2d(J->q[at(J, b, i, h) + d]));
+                    tv += P[i * S + j] * fabs(b2d(J->dout[at(J, b, i, h) + d]));
+                }
+                J->tk[at(J, b, j, h) + d] = J->scale * tk;
+                J->tv[at(J, b, j, h) + d] = tv;
+            }
         }
     free(P);
     free(dS);
+    free(E);
     return 0;
 }
 
@@ -133,11 +165,162 @@ static void *b_worker(void *arg) {
     return NULL;
 }
 
+/* dq of listed rows only: the same formulas restricted to one row i, whose
+ * probabilities, dP and delta need row i's scores alone (O(S D) per row). */
+typedef struct {
+    const bjob_t *J;
+    const int64_t *rows;
+    int64_t n_rows;
+    double *dq, *tq;
+    int64_t next;
+    pthread_mutex_t mu;
+} rjob_t;
+
+static int one_row(const bjob_t *J, int64_t b, int64_t h, int64_t i, double *P, double *dP, double *dq,
+                   double *tq) {
+    const int64_t S = J->S, D = J->D;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < S; ++j) {
+        if (!valid(J, b, i, j)) {
+            P[j] = -INFINITY;
+            continue;
+        }
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += b2d(J->q[at(J, b, i, h) + d]) * b2d(J->k[at(J, b, j, h) + d]);
+        P[j] = J->scale * dot;
+        if (P[j] > m) m = P[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < S; ++j) {
+        const double w = (m == -INFINITY || P[j] == -INFINITY) ? 0.0 : exp(P[j] - m);
+        P[j] = w;
+        l += w;
+    }
+    double delta = 0.0;
+    for (int64_t j = 0; j < S; ++j) {
+        P[j] = (l > 0.0) ? P[j] / l : 0.0;
+        double dp = 0.0;
+        if (valid(J, b, i, j))
+            for (int64_t d = 0; d < D; ++d)
+                dp += b2d(J->dout[at(J, b, i, h) + d]) * b2d(J->v[at(J, b, j, h) + d]);
+        dP[j] = dp;
+        delta += P[j] * dp;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < S; ++j) acc += P[j] * (dP[j] - delta) * b2d(J->k[at(J, b, j, h) + d]);
+        dq[d] = J->scale * acc;
+    }
+    if (tq) {
+        double e = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+            if (P[j] == 0.0) continue;
+            double a = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                a += fabs(b2d(J->dout[at(J, b, i, h) + d])) * fabs(b2d(J->v[at(J, b, j, h) + d]));
+            e += P[j] * a;
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            double t = 0.0;
+            for (int64_t j = 0; j < S; ++j)
+                t += (fabs(P[j] * (dP[j] - delta)) + P[j] * e) * fabs(b2d(J->k[at(J, b, j, h) + d]));
+            tq[d] = J->scale * t;
+        }
+    }
+    return 0;
+}
+
+static void *r_worker(void *arg) {
+    rjob_t *R = (rjob_t *)arg;
+    const bjob_t *J = R->J;
+    double *P = (double *)malloc(sizeof(double) * (size_t)J->S);
+    double *dP = (double *)malloc(sizeof(double) * (size_t)J->S);
+    if (!P || !dP) {
+        free(P);
+        free(dP);
+        return (void *)1;
+    }
+    for (;;) {
+        pthread_mutex_lock(&R->mu);
+        const int64_t r = R->next++;
+        pthread_mutex_unlock(&R->mu);
+        if (r >= R->n_rows) break;
+        const int64_t *t = R->rows + 3 * r;
+        one_row(J, t[0], t[1], t[2], P, dP, R->dq + r * J->D, R->tq ? R->tq + r * J->D : NULL);
+    }
+    free(P);
+    free(dP);
+    return NULL;
+}
+
+/*
+ * vdx_oracle_attn_bwd_dq_rows
+ *   Same inputs as vdx_oracle_attn_bwd; rows = n_rows (b, h, i) triples;
+ *   dq = fp64 [n_rows, D], the dq of each listed row; tq = NULL or fp64
+ *   [n_rows, D], its rounding-sensitivity sum (as for vdx_oracle_attn_bwd).
+ *   No limit on S.
+ * Returns 0 on success, 1 on bad arguments, 2 on allocation failure.
+ */
+ORACLE_EXPORT int vdx_oracle_attn_bwd_dq_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                              const uint16_t *dout, const int32_t *seg_q,
+                                              const int32_t *seg_kv, int64_t B, int64_t S, int64_t H,
+                                              int64_t D, double scale, const int64_t *rows,
+                                              int64_t n_rows, double *dq, double *tq, int n_threads) {
+    if (!q || !k || !v || !dout || !dq || !rows) return 1;
+    if ((seg_q == NULL) != (seg_kv == NULL)) return 1;
+    if (B < 1 || S < 1 || H < 1 || D < 1 || n_rows < 0) return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t *t = rows + 3 * r;
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= S) return 1;
+    }
+    if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (n_threads < 1) n_threads = 1;
+    bjob_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k = k; J.v = v; J.dout = dout;
+    J.seg_q = seg_q; J.seg_kv = seg_kv;
+    J.B = B; J.S = S; J.H = H; J.D = D;
+    J.scale = scale;
+    rjob_t R;
+    memset(&R, 0, sizeof R);
+    R.J = &J;
+    R.rows = rows;
+    R.n_rows = n_rows;
+    R.dq = dq;
+    R.tq = tq;
+    pthread_mutex_init(&R.mu, NULL);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    if (!th) return 2;
+    int started = 0, failed = 0;
+    for (int t = 0; t < n_threads; ++t)
+        if (pthread_create(&th[t], NULL, r_worker, &R) == 0) ++started;
+    if (started == 0) failed = (r_worker(&R) != NULL);
+    for (int t = 0; t < started; ++t) {
+        void *ret = NULL;
+        pthread_join(th[t], &ret);
+        if (ret != NULL) failed = 1;
+    }
+    free(th);
+    pthread_mutex_destroy(&R.mu);
+    return failed ? 2 : 0;
+}
+
 /*
  * vdx_oracle_attn_bwd
  *   q, k, v, dout  bf16 bit patterns [B, S, H, D], host memory.
  *   seg_q/seg_kv   int32 [B, S] or both NULL (unmasked).
  *   dq, dk, dv     fp64 [B, S, H, D] outputs.
+ *   tq, tk, tv     fp64 [B, S, H, D] or all NULL: per element, the sum of
+ *                  the absolute values of the terms whose rounding makes up a
+ *                  finite-precision implementation's error --
+ *                    tq_id = scale sum_j (|dS_ij| + P_ij E_i) |k_jd|
+ *                    tk_jd = scale sum_i (|dS_ij| + P_ij E_i) |q_id|
+ *                    tv_jd = sum_i P_ij |dout_id|
+ *                  with E_i = sum_j P_ij sum_d |dout_id| |v_jd| (how far
+ *                  delta_i moves per unit relative error in out_i's terms).
+ *                  A result computed with every term rounded once to
+ *                  relative precision u lies within u * t of the exact one.
  *   n_threads      worker threads over (b, h) (<= 0 -> online CPUs).
  * Memory: two S x S fp64 matrices per thread.  Returns 0 on success, 1 on bad
  * arguments, 2 on allocation failure.
@@ -145,8 +328,10 @@ static void *b_worker(void *arg) {
 ORACLE_EXPORT int vdx_oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const uint16_t *dout, const int32_t *seg_q, const int32_t *seg_kv,
                                       int64_t B, int64_t S, int64_t H, int64_t D, double scale,
-                                      double *dq, double *dk, double *dv, int n_threads) {
+                                      double *dq, double *dk, double *dv, double *tq, double *tk,
+                                      double *tv, int n_threads) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+    if ((tq == NULL) != (tk == NULL) || (tq == NULL) != (tv == NULL)) return 1;
     if ((seg_q == NULL) != (seg_kv == NULL)) return 1;
     if (B < 1 || S < 1 || H < 1 || D < 1 || S > 16384) return 1;
     if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
@@ -158,6 +343,7 @@ ORACLE_EXPORT int vdx_oracle_attn_bwd(const uint16_t *q, const uint16_t *k, cons
     J.B = B; J.S = S; J.H = H; J.D = D;
     J.scale = scale;
     J.dq = dq; J.dk = dk; J.dv = dv;
+    J.tq = tq; J.tk = tk; J.tv = tv;
     pthread_mutex_init(&J.mu, NULL);
     pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
     if (!th) return 2;

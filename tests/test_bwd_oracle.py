@@ -160,3 +160,72 @@ def test_segment_sums_and_masked_rows():
         assert np.abs(dv[0, idx].sum(0) - do[0, idx].sum(0)).max() < 1e-12
     pad = np.nonzero(sg == 0)[0]
     assert np.all(dq[0, pad] == 0) and np.all(dk[0, pad] == 0) and np.all(dv[0, pad] == 0)
+
+
+@pytest.mark.parametrize("kind", [None, "padded", "interleaved"])
+def test_dq_rows_matches_torch_autograd_f64(kind):
+    """The row-restricted dq (any S, used on sampled rows of long sequences)
+    against torch CPU float64 autograd, on every row of a small case."""
+    B, S, H, D = 2, 40, 2, 64
+    x = W.make_random(B, S, H, D, seed=731)
+    dout = W.randn_bf16((B, S, H, D), 733)
+    seg = None if kind is None else W.random_segments(B, S, 735, kind)
+    tq, _, _ = torch_grads(x, dout, seg, 0.3)
+    rows = np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(S)], dtype=np.int64)
+    s = None if seg is None else seg.numpy()
+    got = oracle.attn_bwd_dq_rows(bits(x["q"]), bits(x["k"]), bits(x["v"]), bits(dout), s,
+                                  None if s is None else s.copy(), 0.3, rows)
+    want = tq[rows[:, 0], rows[:, 2], rows[:, 1]]
+    assert np.abs(got - want).max() < 1e-12
+
+
+def test_dq_rows_beyond_the_dense_limit_q_zero_closed_form():
+    """S above the dense routine's limit: with q = 0, dq_i = scale/S *
+    sum_j (dout_i . (v_j - mean v)) k_j (uniform probabilities)."""
+    B, S, H, D = 1, 16500, 1, 64
+    x = W.make_random(B, S, H, D, seed=741)
+    x["q"] = torch.zeros_like(x["q"])
+    dout = W.randn_bf16((B, S, H, D), 743)
+    rows = np.array([(0, 0, i) for i in (0, 1, 8191, S - 1)], dtype=np.int64)
+    got = oracle.attn_bwd_dq_rows(bits(x["q"]), bits(x["k"]), bits(x["v"]), bits(dout), None, None,
+                                  0.125, rows)
+    k = x["k"][0, :, 0].double().numpy()
+    v = x["v"][0, :, 0].double().numpy()
+    M = k.T @ (v - v.mean(0)) / S          # D x D: sum_j k_j (v_j - vbar)^T / S
+    do = dout[0, rows[:, 2], 0].double().numpy()
+    want = 0.125 * do @ M.T
+    assert np.abs(got - want).max() < 1e-11
+
+
+def test_sensitivity_sums_bound_and_reduce():
+    """The rounding-sensitivity sums (tq, tk, tv) leave the gradients
+    untouched, bound them (|sum of terms| <= sum of |terms|), and reduce to
+    the gradient itself where every term is non-negative (dout >= 0 gives
+    tv = dv)."""
+    B, S, H, D = 1, 37, 2, 64
+    x = W.make_random(B, S, H, D, seed=761)
+    dout = W.randn_bf16((B, S, H, D), 763)
+    seg = W.random_segments(B, S, 765, "packed").numpy()
+    b = [bits(x["q"]), bits(x["k"]), bits(x["v"])]
+    g0 = oracle.attn_bwd(*b, bits(dout), seg, seg.copy(), 0.2)
+    g1 = oracle.attn_bwd(*b, bits(dout), seg, seg.copy(), 0.2, sensitivity=True)
+    for a, c in zip(g0, g1[:3]):
+        assert np.array_equal(a, c)
+    for g, t in zip(g1[:3], g1[3:]):
+        assert np.all(t >= np.abs(g) - 1e-12)
+    pos = dout.abs()
+    _, _, dv, _, _, tv = oracle.attn_bwd(*b, bits(pos), seg, seg.copy(), 0.2, sensitivity=True)
+    assert np.allclose(tv, dv, rtol=1e-13, atol=0)
+
+
+def test_dq_rows_sensitivity_matches_dense():
+    B, S, H, D = 1, 45, 2, 64
+    x = W.make_random(B, S, H, D, seed=771)
+    dout = W.randn_bf16((B, S, H, D), 773)
+    seg = W.random_segments(B, S, 775, "interleaved").numpy()
+    b = [bits(x["q"]), bits(x["k"]), bits(x["v"]), bits(dout)]
+    dq, _, _, tq, _, _ = oracle.attn_bwd(*b, seg, seg.copy(), 0.2, sensitivity=True)
+    rows = np.array([(0, h, i) for h in range(H) for i in range(S)], dtype=np.int64)
+    r, t = oracle.attn_bwd_dq_rows(*b, seg, seg.copy(), 0.2, rows, sensitivity=True)
+    assert np.allclose(r, dq[0, rows[:, 2], rows[:, 1]], rtol=0, atol=1e-13)
+    assert np.allclose(t, tq[0, rows[:, 2], rows[:, 1]], rtol=1e-12, atol=1e-14)
