@@ -14,11 +14,17 @@ Prints ONE JSON line:
                the HBM traffic from rocprofv3 counters when they are current
   cpu_baseline the fp64 oracle timed on a bounded row sample on the host cores
 
+With --pass bwd the step is one vdx_attn_bwd call (the gradient: delta/lse
+prep, the key-major dK/dV kernel and the query-major dQ kernel) on the same
+workload, given resident q, k, v, out, lse and a seeded dout; the FLOP count
+is the algorithmic 10*D per valid pair and head (five products of 2*D:
+scores, dP, dV, dK, dQ), of which the two-kernel split executes 14*D.
+
 With --workload natten_vae_decoder (or natten_tiny) the step is one
 vdx_natten3d_fwd call instead (3D neighbourhood attention over a t x h x w
 grid), and the FLOP count is that of the window pairs: 4*D*H*B*S*|window|.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
        [--no-cpu-baseline] [--copy-calib]
 """
 from __future__ import annotations
@@ -42,6 +48,8 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=75,600 H=40 D=128 (1 GPU)"
+BWD_METRIC = ("attention backward TFLOP/s (dq, dk, dv; 10*D flop per valid pair) and % of "
+              "bf16 MFMA peak (1 GPU)")
 NATTEN_METRIC = "3D neighbourhood attention TFLOP/s (window pairs) and % of bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
                   for f in ("attn_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
@@ -218,6 +226,92 @@ def time_steps(step, stream, steps, warmup):
     return ms_per_step, float(np.mean(kernel_ms))
 
 
+def bwd_cpu_baseline(w: W.Workload, x, dout, target_s: float = 15.0):
+    import oracle
+    cores = oracle.default_threads()
+    qb, kb, vb, db = (W.bf16_bits(t) for t in (x["q"], x["k"], x["v"], dout))
+    sq = None if x["seg_q"] is None else x["seg_q"].numpy()
+    sk = None if x["seg_kv"] is None else x["seg_kv"].numpy()
+    rng = np.random.default_rng(11)
+
+    def rows_for(n):
+        return np.stack([rng.integers(0, w.B, n), rng.integers(0, w.H, n),
+                         rng.integers(0, w.S, n)], 1).astype(np.int64)
+
+    def flops(rows):
+        # scores, dP and dq: 6*D per valid key of the row
+        if sq is None:
+            return 6.0 * w.D * w.S * len(rows)
+        return sum(6.0 * w.D * float(np.count_nonzero(sk[b] == sq[b, i]))
+                   for b, _, i in rows if sq[b, i] != 0)
+
+    probe = rows_for(cores)
+    t0 = time.perf_counter()
+    oracle.attn_bwd_dq_rows(qb, kb, vb, db, sq, sk, float(np.float32(w.scale)), probe,
+                            n_threads=cores)
+    dt = time.perf_counter() - t0
+    n = max(cores, int(cores * target_s / max(dt, 1e-3)))
+    rows = rows_for(n)
+    t0 = time.perf_counter()
+    oracle.attn_bwd_dq_rows(qb, kb, vb, db, sq, sk, float(np.float32(w.scale)), rows,
+                            n_threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": flops(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"dq of {n} random (b,h,i) rows of {w.name} (scores, dP and dq over the "
+                      f"row's full key set), {dt:.1f} s on {cores} threads"}
+
+
+def bwd_main(args, vdx):
+    w = W.WORKLOADS[args.workload]
+    log(f"workload {w.name} backward: B={w.B} S={w.S} H={w.H} D={w.D} masked={w.masked}")
+    x = W.make_inputs(w)
+    dout = W.randn_bf16((w.B, w.S, w.H, w.D), w.seeds[2] + 1)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    ddo = dout.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    out, lse = vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale,
+                            stream=stream)
+    dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
+    ws = torch.empty(vdx.attn_bwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device=dev)
+
+    def step():
+        vdx.attn_bwd(d["q"], d["k"], d["v"], out, lse, ddo, d["seg_q"], d["seg_kv"],
+                     scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+
+    ms_per_step, call_ms = time_steps(step, stream, args.steps, args.warmup)
+    pairs = valid_pairs(w)
+    flop = 10.0 * w.D * w.H * pairs
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (call_ms * 1e-3) / 1e12
+    n = w.B * w.S * w.H * w.D
+    line = {
+        "metric": BWD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "bwd", "B": w.B, "S": w.S, "H": w.H, "D": w.D,
+                   "segments": "none" if w.seg_runs is None else w.seg_runs,
+                   "flop_per_step": flop, "executed_mfma_flop_per_step": 14.0 * w.D * w.H * pairs,
+                   "peak_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+        # The three kernels of one call, timed together with HIP events on
+        # their stream; per-kernel durations come from rocprofv3.
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "scope": "vdx_attn_bwd call (prep + dK/dV + dQ kernels)",
+                     "traffic": None,
+                     # reads q, k, v, out, dout, lse; writes dq, dk, dv
+                     "algorithmic_bytes": 2 * 8 * n + 4 * w.B * w.H * w.S,
+                     "kernel_ms_mean": round(call_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        line["cpu_baseline"] = bwd_cpu_baseline(w, x, dout, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def natten_main(args, vdx):
     w = W.NATTEN_WORKLOADS[args.workload]
     log(f"workload {w.name}: B={w.B} grid={w.grid} window={w.window} H={w.H} D={w.D}")
@@ -270,6 +364,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=W.HEADLINE,
                     choices=sorted(W.WORKLOADS) + sorted(W.NATTEN_WORKLOADS))
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
@@ -287,7 +382,12 @@ def main():
         copy_calibration()
         return
     if args.workload in W.NATTEN_WORKLOADS:
+        if args.pass_ != "fwd":
+            ap.error("the neighbourhood-attention workloads have a forward pass only")
         natten_main(args, vdx)
+        return
+    if args.pass_ == "bwd":
+        bwd_main(args, vdx)
         return
 
     w = W.WORKLOADS[args.workload]

@@ -1,7 +1,8 @@
 /*
  * vdx_attn.h -- C ABI of the segment-masked, non-causal flash-attention
  * forward for video-DiT token volumes on gfx950 (MI355X), and of the 3D
- * neighbourhood (windowed) attention forward (vdx_natten3d_fwd, below).
+ * neighbourhood (windowed) attention forward (vdx_natten3d_fwd, below), and
+ * of the attention gradient (vdx_attn_bwd, below).
  *
  * The operation (vidax paper, arXiv:2609.18077):
  *   - section 1, "Spatiotemporal constraints in video generation": full
@@ -33,6 +34,7 @@
 #ifndef VDX_ATTN_H
 #define VDX_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h> /* hipStream_t */
 
@@ -40,7 +42,7 @@
 extern "C" {
 #endif
 
-#define VDX_ABI_VERSION 2
+#define VDX_ABI_VERSION 3
 
 /* Status codes.  Argument validation runs before any HIP call, in the order
  * below (NULL -> segment pair -> shape -> head dim -> scale -> alignment),
@@ -61,8 +63,11 @@ enum vdx_status {
     VDX_ERR_DEVICE = 7,   /* the current HIP device is not gfx950, or the
                              device query failed                                */
     VDX_ERR_LAUNCH = 8,   /* the kernel launch reported an error                */
-    VDX_ERR_WINDOW = 9    /* vdx_natten3d_fwd: a window size is even or < 1, or
+    VDX_ERR_WINDOW = 9,   /* vdx_natten3d_fwd: a window size is even or < 1, or
                              the effective x window min(KW, NW) exceeds 13      */
+    VDX_ERR_WORKSPACE = 10 /* vdx_attn_bwd: workspace NULL, smaller than
+                             vdx_attn_bwd_workspace_size(B, S, H), or not
+                             16-byte aligned                                    */
 };
 
 /*
@@ -128,6 +133,57 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
 int vdx_natten3d_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      int B, int NT, int NH, int NW, int H, int D, int KT, int KH, int KW,
                      float scale, hipStream_t stream);
+
+/*
+ * vdx_attn_bwd -- gradient of vdx_attn_fwd: dq, dk, dv for a given dout.
+ *
+ * The operation (vidax paper, arXiv:2609.18077): section 5, "Conclusions &
+ * Future Work", lists training and fine-tuning (LoRA and full-parameter) of
+ * the video models as future work; training needs this gradient of the
+ * attention of section 2 / Appendix A, Table 4, groups 1 and 2.  With J_i
+ * and s_ij as for vdx_attn_fwd and P_ij = exp(s_ij - lse[b,h,i]) for j in J_i
+ * (0 otherwise), for every batch b and head h:
+ *     dv_j    = sum_i P_ij dout_i
+ *     dP_ij   = dout_i . v_j,     delta_i = dout_i . out_i  (= sum_j P_ij dP_ij)
+ *     dS_ij   = P_ij (dP_ij - delta_i)
+ *     dq_i    = scale * sum_j dS_ij k_j
+ *     dk_j    = scale * sum_i dS_ij q_i
+ *   (vectors over the head dim; all written as bf16, RNE, accumulated in
+ *   fp32).  Rows with empty J_i (lse = -inf) get dq_i = 0 and contribute
+ *   nothing to dk and dv; keys that no query attends get dk_j = dv_j = 0.
+ *
+ *   q, k, v, seg_q, seg_kv, B, S, H, D, scale
+ *             exactly as passed to vdx_attn_fwd.
+ *   out, lse  that call's outputs (bf16 [B, S, H, D], fp32 [B, H, S]).
+ *   dout      bf16 [B, S, H, D], gradient of the loss with respect to out.
+ *   dq,dk,dv  bf16 [B, S, H, D], written in full; they must not overlap any
+ *             input, the workspace or each other.
+ *   workspace device scratch of at least vdx_attn_bwd_workspace_size(B, S, H)
+ *             bytes, 16-byte aligned, owned by the caller; its contents on
+ *             entry do not matter and are overwritten (it holds per-row
+ *             fp32 terms between the kernels of one call, so two calls in
+ *             flight at once need two workspaces).
+ *   stream    HIP stream; the three kernels are enqueued on it in order,
+ *             asynchronous, no host synchronisation.
+ * Every pointer is a DEVICE pointer owned by the caller; the library
+ * allocates nothing.  Validation runs before any HIP call, in the order
+ * NULL (q, k, v, out, lse, dout, dq, dk, dv) -> segment pair -> shape (as for
+ * vdx_attn_fwd, and S <= 2^31 - 65) -> head dim -> scale -> alignment (bf16
+ * tensors 16-byte, lse and segment IDs 4-byte) -> workspace, and reports the
+ * first failure without touching device memory.  Results are deterministic
+ * (no atomics).
+ */
+int vdx_attn_bwd(const void* q, const void* k, const void* v,
+                 const int32_t* seg_q, const int32_t* seg_kv,
+                 const void* out, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/* Bytes of workspace vdx_attn_bwd needs for (B, S, H): 8 * B * H * S rounded
+ * up per (b, h) to a multiple of 64 rows.  0 if B, S or H < 1 or the size
+ * overflows. */
+size_t vdx_attn_bwd_workspace_size(int B, int S, int H);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* vdx_status_str(int status);

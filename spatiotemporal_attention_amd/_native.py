@@ -20,8 +20,10 @@ VDX_ERR_ALIGN = 6
 VDX_ERR_DEVICE = 7
 VDX_ERR_LAUNCH = 8
 VDX_ERR_WINDOW = 9
+VDX_ERR_WORKSPACE = 10
 
-EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_status_str", "vdx_abi_version")
+EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_workspace_size",
+            "vdx_status_str", "vdx_abi_version")
 
 
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -34,6 +36,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vdx_attn_fwd.argtypes = [p, p, p, p, p, p, p, i, i, i, i, ctypes.c_float, p]
     lib.vdx_natten3d_fwd.restype = i
     lib.vdx_natten3d_fwd.argtypes = [p, p, p, p, p] + [i] * 9 + [ctypes.c_float, p]
+    lib.vdx_attn_bwd.restype = i
+    lib.vdx_attn_bwd.argtypes = [p] * 12 + [ctypes.c_size_t] + [i] * 4 + [ctypes.c_float, p]
+    lib.vdx_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.vdx_attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.vdx_status_str.restype = ctypes.c_char_p
     lib.vdx_status_str.argtypes = [i]
     lib.vdx_abi_version.restype = i
@@ -64,3 +70,16 @@ def natten3d_fwd_raw(q, k, v, out, lse, B, NT, NH, NW, H, D, KT, KH, KW, scale, 
     return int(lib.vdx_natten3d_fwd(q or None, k or None, v or None, out or None, lse or None,
                                     int(B), int(NT), int(NH), int(NW), int(H), int(D),
                                     int(KT), int(KH), int(KW), float(scale), stream or None))
+
+
+def attn_bwd_raw(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, ws, ws_bytes, B, S, H, D,
+                 scale, stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL)."""
+    return int(lib.vdx_attn_bwd(q or None, k or None, v or None, seg_q or None, seg_kv or None,
+                                out or None, lse or None, dout or None, dq or None, dk or None,
+                                dv or None, ws or None, int(ws_bytes), int(B), int(S), int(H),
+                                int(D), float(scale), stream or None))
+
+
+def attn_bwd_workspace_size(B, S, H) -> int:
+    return int(lib.vdx_attn_bwd_workspace_size(int(B), int(S), int(H)))

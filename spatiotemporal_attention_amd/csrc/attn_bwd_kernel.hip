@@ -1,0 +1,713 @@
+// attn_bwd_kernel.hip -- gfx950 backward of segment-masked, non-causal
+// softmax attention: dq, dk, dv from q, k, v, out, lse and dout.
+//
+// What it computes (vidax paper, arXiv:2609.18077: section 5 "Conclusions &
+// Future Work" names training and fine-tuning, which need this gradient; the
+// forward and its segment rule are those of section 2 and Appendix A,
+// Table 4, groups 1 and 2).  With P_ij = exp(scale q_i.k_j - lse_i) over the
+// valid pairs (equal, nonzero segment IDs; 0 elsewhere):
+//   dv_j = sum_i P_ij dout_i
+//   dP_ij = dout_i . v_j,  delta_i = sum_j P_ij dP_ij = dout_i . out_i
+//   dS_ij = P_ij (dP_ij - delta_i)
+//   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i
+// P is recomputed from the forward's log-sum-exp, so nothing of size S x S
+// is ever stored.
+//
+// Three kernels, all deterministic (no atomics):
+//   * prep: delta_i = dout_i . out_i in fp32 and lse2_i = lse_i log2(e)
+//     (+inf for rows without a valid key, and for the padding rows up to the
+//     next multiple of 64, so that their P is exactly 0) into a workspace;
+//   * dK/dV (key-major): a workgroup holds 128 keys, 32 per wave, whose K and
+//     V slices stay in registers as MFMA B operands; it sweeps the 64-query
+//     tiles that can hold a valid pair: S = Q K^T and dP = dO V^T (lanes own
+//     key columns), P and dS on the VALU, then dV^T += dO^T P and
+//     dK^T += Q^T dS with the fp32 P / dS registers reused as bf16 B operands
+//     (queries inside a 32-row block are permuted so that the accumulator
+//     rows line up with the operand's contraction index);
+//   * dQ (query-major): a workgroup holds 128 queries, Q and dO slices in
+//     registers; it sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T on
+//     the VALU, dQ^T += K^T dS^T.
+// Both sweeps stage their 64-row tiles in LDS by direct global->LDS DMA into
+// a ring.  One XOR swizzle of 16-byte chunks serves both operand reads of a
+// tile -- row reads (ds_read_b128, A operand of Q K^T-type products) and
+// transposed reads (ds_read_b64_tr_b16, A operand of X^T Y products) -- with
+// no bank conflicts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "attn_common.h"
+#include "attn_fwd_launch.h"
+
+namespace vdx {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kBwdMaxTiles = 30720;       // capacity of the on-chip active-tile list
+constexpr int kPad = 64;                  // workspace rows are padded to this multiple
+
+template <int D>
+struct BTile {
+    static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kTileBytes = 64 * kRowBytes;
+    static constexpr int kSteps = D / 16;   // MFMA k-steps over D
+    static constexpr int kDBlocks = D / 32;
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+    static constexpr int kLoads = kTileBytes / 1024 / kBwdWaves;  // DMAs per wave per tile
+    // One ring stage: two 64-row tiles (Q, dO or K, V), then 64 fp32 lse2,
+    // 64 fp32 delta and 64 int32 segment IDs.
+    static constexpr int kA = 0;
+    static constexpr int kB = kTileBytes;
+    static constexpr int kVec0 = 2 * kTileBytes;
+    static constexpr int kVec1 = kVec0 + 256;
+    static constexpr int kSeg = kVec1 + 256;
+    static constexpr int kStage = (kSeg + 256 + 1023) & ~1023;
+    static_assert(kLoads >= 1, "tile too small for the workgroup");
+};
+
+// 16-byte chunk c of tile row r sits at chunk position c ^ u_swz(r).  The
+// value depends on r & 15 only; it is a bijection on every 16 rows (row
+// reads: 16 lanes fetch 16 different rows' chunk c) and differs in its upper
+// bits across rows {4a..4a+3} (D = 128) or {4a, 4a+2} (D = 64), which
+// spreads the 4 rows x 64 bytes of a transposed read over all banks.
+template <int D>
+__device__ __forceinline__ int u_swz(int r) {
+    if constexpr (D == 128)
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ void wait_vm_upto(int n) {
+    // n is one of the copy counts a wave issues per tile (<= 12).
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    }
+}
+
+// Per-lane LDS offsets (within a 64-row tile) of the two operand reads and
+// the DMA source offsets of this wave's share of a tile copy.
+template <int D>
+struct Lanes {
+    using T = BTile<D>;
+    // Row read, A operand of a 32x32x16 MFMA over rows 32*blk .. +31 and
+    // columns 16*ks .. +15: lane (lr, g) takes row swap23(lr), chunk 2ks + g,
+    // at (rx ^ (ks << 5)) + 32 * blk * kRowBytes.
+    int rx;
+    // Transposed read, A operand over columns 32*db .. +31 (m) and rows
+    // 16*kst .. +15 (k): two ds_read_b64_tr_b16 at (tx0 / tx1 ^ (db << 6)) +
+    // 16 * kst * kRowBytes; lane (q = lane / 16, j = lane % 16) points at row
+    // 8(q >> 1) + (j >> 2) (+4) and columns 16(q & 1) + 4(j & 3) .. +3.
+    int tx0, tx1;
+    uint32_t dmo[T::kLoads];
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t tok_stride) {
+        const int lr = lane & 31, g = lane >> 5;
+        const int sr = swap23(lr);
+        rx = sr * T::kRowBytes + 16 * (g ^ u_swz<D>(sr));
+        const int qg = lane >> 4, j = lane & 15;
+        const int r0 = 8 * g + (j >> 2), r1 = r0 + 4;
+        const int c0 = 2 * (qg & 1) + ((j & 3) >> 1);
+        tx0 = r0 * T::kRowBytes + 16 * (c0 ^ u_swz<D>(r0)) + 8 * (j & 1);
+        tx1 = r1 * T::kRowBytes + 16 * (c0 ^ u_swz<D>(r1)) + 8 * (j & 1);
+        // DMA instruction i covers rows kRowsPerLoad*i ..; lane l lands at
+        // chunk position l % kChunks of its row and fetches the chunk stored
+        // there.
+#pragma unroll
+        for (int jj = 0; jj < T::kLoads; ++jj) {
+            const int i = wave * T::kLoads + jj;
+            const int r = T::kRowsPerLoad * i + lane / T::kChunks;
+            const int c = (lane % T::kChunks) ^ u_swz<D>(r);
+            dmo[jj] = 2u * (uint32_t)(r * (int)tok_stride + 8 * c);
+        }
+    }
+    __device__ __forceinline__ static int dma_row(int wave, int jj, int lane) {
+        return T::kRowsPerLoad * (wave * T::kLoads + jj) + lane / T::kChunks;
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(uint32_t tile, int rx, int ks, int blk) {
+    return *reinterpret_cast<const bf16x8*>(
+        lds_ptr((tile + (uint32_t)(rx ^ (ks << 5))) + blk * 32 * BTile<D>::kRowBytes));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(uint32_t tile, int tx0, int tx1, int kst, int db) {
+    const uint32_t o = tile + kst * 16 * BTile<D>::kRowBytes;
+    return tr_read8(lds_ptr(o + (uint32_t)(tx0 ^ (db << 6))), lds_ptr(o + (uint32_t)(tx1 ^ (db << 6))));
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Classifies every 64-row tile of the opposite side (segment IDs `other`,
+// length S) against this workgroup's rows (ID `mine` per lane; 0 for padding
+// and rows past S) as skip / full / partial, and compacts the active tiles
+// into `list` (bit 15 set: partial).  `cls` is scratch of n_tiles bytes.
+// Returns the number of active tiles.
+__device__ int active_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
+                            uint16_t* list, int* meta, int wave, int lane) {
+    {
+        int mn = (mine != 0) ? mine : INT32_MAX;
+        int mx = (mine != 0) ? mine : INT32_MIN;
+        int fl = (mine == 0) ? 1 : 0;
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        fl = wave_max(fl);
+        if (lane == 0) {
+            meta[wave] = mn;
+            meta[kBwdWaves + wave] = mx;
+            meta[2 * kBwdWaves + wave] = fl;
+        }
+    }
+    __syncthreads();
+    int omn = INT32_MAX, omx = INT32_MIN, ofl = 0;
+#pragma unroll
+    for (int i = 0; i < kBwdWaves; ++i) {
+        omn = min(omn, meta[i]);
+        omx = max(omx, meta[kBwdWaves + i]);
+        ofl |= meta[2 * kBwdWaves + i];
+    }
+    for (int t = wave; t < n_tiles; t += kBwdWaves) {
+        const int r = t * 64 + lane;
+        const int id = (r < S) ? other[r] : 0;
+        int mn = (id != 0) ? id : INT32_MAX;
+        int mx = (id != 0) ? id : INT32_MIN;
+        int fl = (id == 0) ? 1 : 0;
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        fl = wave_max(fl);
+        if (lane == 0) {
+            uint8_t c;
+            if (omn > omx || mn > mx || max(omn, mn) > min(omx, mx))
+                c = 0;
+            else if (!ofl && !fl && omn == omx && mn == mx && omn == mn)
+                c = 1;
+            else
+                c = 2;
+            cls[t] = c;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int base = 0;
+        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+            const int t = t0 + lane;
+            const int c = (t < n_tiles) ? cls[t] : 0;
+            const uint64_t m = __ballot(c != 0);
+            const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+            if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
+            base += __popcll(m);
+        }
+        if (lane == 0) meta[3 * kBwdWaves] = base;
+    }
+    __syncthreads();
+    return meta[3 * kBwdWaves];
+}
+
+// Workgroup id -> (row block, b*H + h), renumbered so that each XCD (own L2)
+// runs consecutive row blocks of one head, which share the swept tiles.
+__device__ __forceinline__ void wg_coords(int n_blk, int n_wg, int& blk, int& bh) {
+    const int w = blockIdx.x;
+    const int per = n_wg / kXcds, rem = n_wg % kXcds;
+    const int xcd = w % kXcds;
+    const int lid = xcd * per + min(xcd, rem) + w / kXcds;
+    blk = lid % n_blk;
+    bh = lid / n_blk;
+}
+
+// ---- prep: delta and lse2 ------------------------------------------------------
+// Rows (b, i, h) in memory order; D/8 lanes per row, 8 elements each.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
+    const __bf16* __restrict__ out, const __bf16* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ ws_lse2, float* __restrict__ ws_delta, int S, int H, int S_pad,
+    int64_t n_rows, int64_t n_items) {
+    constexpr int L = D / 8;
+    const int64_t stride = (int64_t)gridDim.x * (256 / L);
+    const int part = threadIdx.x % L;
+    for (int64_t it = (int64_t)blockIdx.x * (256 / L) + threadIdx.x / L; it < n_items; it += stride) {
+        if (it < n_rows) {
+            const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + it * D + 8 * part);
+            const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + it * D + 8 * part);
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)d[e], acc);
+#pragma unroll
+            for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+            if (part == 0) {
+                const int64_t h = it % H, bi = it / H;
+                const int64_t i = bi % S, b = bi / S;
+                const int64_t w = (b * H + h) * S_pad + i;
+                const float l = lse[(b * H + h) * S + i];
+                ws_delta[w] = acc;
+                ws_lse2[w] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+            }
+        } else if (part == 0) {
+            const int64_t e = it - n_rows, np = S_pad - S;
+            const int64_t w = (e / np) * S_pad + S + e % np;
+            ws_delta[w] = 0.f;
+            ws_lse2[w] = INFINITY;
+        }
+    }
+}
+
+// ---- dK / dV ---------------------------------------------------------------------
+template <int D, bool SEG>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                          const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                          const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
+                          const float* __restrict__ ws_lse2, const float* __restrict__ ws_delta,
+                          __bf16* __restrict__ dk, __bf16* __restrict__ dv, int S, int S_pad,
+                          int H, float c_log2, float scale, int n_blk, int n_qt, int n_wg) {
+    using T = BTile<D>;
+    constexpr int kSlots = 3;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    int blk, bh;
+    wg_coords(n_blk, n_wg, blk, bh);
+    const int h = bh % H, b = bh / H;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 31, g = lane >> 5;
+    const int kj = blk * kBwdRows + wave * 32 + lr;  // this lane's key
+    const int64_t ts = (int64_t)H * D;
+    const int64_t head0 = (int64_t)b * S * ts + (int64_t)h * D;
+    const __bf16* qp = q + head0;
+    const __bf16* dop = dout + head0;
+    const float* l2p = ws_lse2 + (int64_t)bh * S_pad;
+    const float* dlp = ws_delta + (int64_t)bh * S_pad;
+    const int32_t* sqp = SEG ? seg_q + (int64_t)b * S : nullptr;
+
+    // K and V slices of this lane's key as B operands (k = d, n = key).
+    bf16x8 kreg[T::kSteps], vreg[T::kSteps];
+    {
+        const int64_t off = head0 + (int64_t)kj * ts + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) {
+            kreg[ks] = (kj < S) ? *reinterpret_cast<const bf16x8*>(k + off + 16 * ks) : bf16x8{};
+            vreg[ks] = (kj < S) ? *reinterpret_cast<const bf16x8*>(v + off + 16 * ks) : bf16x8{};
+        }
+    }
+    const int myseg = SEG ? ((kj < S) ? seg_kv[(int64_t)b * S + kj] : 0) : 1;
+
+    Lanes<D> L;
+    L.init(wave, lane, ts);
+
+    uint16_t* list = reinterpret_cast<uint16_t*>(smem + kSlots * T::kStage);
+    int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_qt : 0) + 15) & ~15));
+    int n_act = n_qt;
+    if (SEG)
+        n_act = active_tiles(myseg, sqp, S, n_qt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
+                             lane);
+
+    auto tile_of = [&](int n, bool& partial) -> int {
+        if (SEG) {
+            const int e = __builtin_amdgcn_readfirstlane((int)list[n]);
+            partial = (e & 0x8000) != 0;
+            return e & 0x7fff;
+        }
+        partial = false;
+        return n;
+    };
+    // Copies of query tile n of the active list into slot n % 3: this wave's
+    // share of Q and dO (rows past S re-read row S-1; their lse2 is +inf), the
+    // lse2 and delta rows (wave 0) and the query segment IDs (wave 1).
+    const int n_copy = 2 * T::kLoads + (wave == 0 ? 2 : 0) + ((SEG && wave == 1) ? 1 : 0);
+    auto copy = [&](int n) {
+        bool part;
+        const int t = tile_of(n, part);
+        char* st = smem + (n % kSlots) * T::kStage;
+        const int64_t row0 = (int64_t)t * 64;
+        const __bf16* sq = qp + row0 * ts;
+        const __bf16* sd = dop + row0 * ts;
+        const bool tail = row0 + 64 > S;
+#pragma unroll
+        for (int jj = 0; jj < T::kLoads; ++jj) {
+            uint32_t off = L.dmo[jj];
+            if (tail) {
+                const int over = max(0, (int)row0 + Lanes<D>::dma_row(wave, jj, lane) - (S - 1));
+                off -= (uint32_t)over * (uint32_t)(2 * ts);
+            }
+            const int i = wave * T::kLoads + jj;
+            dma16(sq, off, st + T::kA + i * 1024);
+            dma16(sd, off, st + T::kB + i * 1024);
+        }
+        if (wave == 0) {
+            dma4(l2p + row0, 4u * (uint32_t)lane, st + T::kVec0);
+            dma4(dlp + row0, 4u * (uint32_t)lane, st + T::kVec1);
+        }
+        if (SEG && wave == 1) {
+            const int r = min((int)row0 + lane, S - 1);
+            dma4(sqp, 4u * (uint32_t)r, st + T::kSeg);
+        }
+    };
+
+    f32x16 dkacc[T::kDBlocks], dvacc[T::kDBlocks];
+#pragma unroll
+    for (int i = 0; i < T::kDBlocks; ++i) dkacc[i] = dvacc[i] = f32x16{};
+
+    if (n_act > 0) copy(0);
+    if (n_act > 1) copy(1);
+    wait_vm(0);
+    barrier();
+    // Wait for the K/V slices (and the key's segment ID) here rather than in
+    // the loop, where a vmcnt wait would also drain the tile copies.
+    asm volatile("" ::"v"(kreg[0]), "v"(kreg[T::kSteps - 1]), "v"(vreg[0]), "v"(vreg[T::kSteps - 1]),
+                 "v"(myseg));
+
+    for (int n = 0; n < n_act; ++n) {
+        const bool more = n + 2 < n_act;
+        if (more) copy(n + 2);
+        bool partial;
+        tile_of(n, partial);
+        const uint32_t st = lds_addr(smem) + (n % kSlots) * T::kStage;
+        const uint32_t tq = st + T::kA, td = st + T::kB;
+
+        // S = Q K^T and dP = dO V^T over 64 queries (two 32-row blocks).
+        f32x16 sacc[2], pacc[2];
+        static_for<0, T::kSteps>([&](auto kc) {
+            constexpr int ks = kc;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const bf16x8 aq = row_operand<D>(tq, L.rx, ks, bb);
+                const bf16x8 ad = row_operand<D>(td, L.rx, ks, bb);
+                if constexpr (ks == 0) {
+                    sacc[bb] = mfma32(aq, kreg[0], f32x16{});
+                    pacc[bb] = mfma32(ad, vreg[0], f32x16{});
+                } else {
+                    sacc[bb] = mfma32(aq, kreg[ks], sacc[bb]);
+                    pacc[bb] = mfma32(ad, vreg[ks], pacc[bb]);
+                }
+            }
+        });
+
+        // P = 2^(s c - lse2) and dS = P (dP - delta).  Register r of block bb
+        // holds query bb*32 + 16(r >> 3) + 8g + (r & 7) of the tile.
+        bf16x8 pb[4], dsb[4];
+        const float* l2s = reinterpret_cast<const float*>(lds_ptr(st + T::kVec0));
+        const float* dls = reinterpret_cast<const float*>(lds_ptr(st + T::kVec1));
+        const int* sgs = reinterpret_cast<const int*>(lds_ptr(st + T::kSeg));
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int row = bb * 32 + 16 * hh + 8 * g;
+                const float4 la = *reinterpret_cast<const float4*>(l2s + row);
+                const float4 lb = *reinterpret_cast<const float4*>(l2s + row + 4);
+                const float4 da = *reinterpret_cast<const float4*>(dls + row);
+                const float4 db4 = *reinterpret_cast<const float4*>(dls + row + 4);
+                const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+                const float d8[8] = {da.x, da.y, da.z, da.w, db4.x, db4.y, db4.z, db4.w};
+                int s8[8];
+                if (SEG && partial) {
+                    const int4 sa = *reinterpret_cast<const int4*>(sgs + row);
+                    const int4 sb = *reinterpret_cast<const int4*>(sgs + row + 4);
+                    s8[0] = sa.x; s8[1] = sa.y; s8[2] = sa.z; s8[3] = sa.w;
+                    s8[4] = sb.x; s8[5] = sb.y; s8[6] = sb.z; s8[7] = sb.w;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * hh + e;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c_log2, -l8[e]));
+                    if (SEG && partial) p = (s8[e] == myseg && myseg != 0) ? p : 0.f;
+                    const float ds = p * (pacc[bb][r] - d8[e]);
+                    pb[2 * bb + hh][e] = (__bf16)p;
+                    dsb[2 * bb + hh][e] = (__bf16)ds;
+                }
+            }
+        }
+
+        // dV^T += dO^T P and dK^T += Q^T dS (k = queries, 16 per step).
+        static_for<0, 4>([&](auto kc) {
+            constexpr int kst = kc;
+#pragma unroll
+            for (int db = 0; db < T::kDBlocks; ++db) {
+                dvacc[db] = mfma32(tr_operand<D>(td, L.tx0, L.tx1, kst, db), pb[kst], dvacc[db]);
+                dkacc[db] = mfma32(tr_operand<D>(tq, L.tx0, L.tx1, kst, db), dsb[kst], dkacc[db]);
+            }
+        });
+
+        // The copy of tile n+1 (issued one iteration ago) must have landed in
+        // every wave before the barrier that opens iteration n+1; tile n's
+        // slot is refilled only after that barrier.
+        wait_vm_upto(more ? n_copy : 0);
+        barrier();
+    }
+
+    // ---- epilogue: dk = scale dK^T, dv = dV^T (bf16) ----------------------------
+    if (kj < S) {
+        const int64_t o = head0 + (int64_t)kj * ts;
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * g;
+                __bf16 k4[4], v4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    k4[e] = (__bf16)(dkacc[db][4 * r4 + e] * scale);
+                    v4[e] = (__bf16)dvacc[db][4 * r4 + e];
+                }
+                *reinterpret_cast<uint2*>(dk + o + d) = *reinterpret_cast<const uint2*>(k4);
+                *reinterpret_cast<uint2*>(dv + o + d) = *reinterpret_cast<const uint2*>(v4);
+            }
+        }
+    }
+}
+
+// ---- dQ --------------------------------------------------------------------------
+template <int D, bool SEG>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                        const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
+                        const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
+                        const float* __restrict__ ws_lse2, const float* __restrict__ ws_delta,
+                        __bf16* __restrict__ dq, int S, int S_pad, int H, float c_log2, float scale,
+                        int n_blk, int n_kt, int n_wg) {
+    using T = BTile<D>;
+    constexpr int kSlots = 2;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    int blk, bh;
+    wg_coords(n_blk, n_wg, blk, bh);
+    const int h = bh % H, b = bh / H;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 31, g = lane >> 5;
+    const int qi = blk * kBwdRows + wave * 32 + lr;  // this lane's query
+    const int64_t ts = (int64_t)H * D;
+    const int64_t head0 = (int64_t)b * S * ts + (int64_t)h * D;
+    const __bf16* kp = k + head0;
+    const __bf16* vp = v + head0;
+    const int32_t* skp = SEG ? seg_kv + (int64_t)b * S : nullptr;
+
+    // Q and dO slices of this lane's query as B operands (k = d, n = query).
+    bf16x8 qreg[T::kSteps], doreg[T::kSteps];
+    {
+        const int64_t off = head0 + (int64_t)qi * ts + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) {
+            qreg[ks] = (qi < S) ? *reinterpret_cast<const bf16x8*>(q + off + 16 * ks) : bf16x8{};
+            doreg[ks] = (qi < S) ? *reinterpret_cast<const bf16x8*>(dout + off + 16 * ks) : bf16x8{};
+        }
+    }
+    const int myseg = SEG ? ((qi < S) ? seg_q[(int64_t)b * S + qi] : 0) : 1;
+    const float lse2 = (qi < S) ? ws_lse2[(int64_t)bh * S_pad + qi] : INFINITY;
+    const float delta = (qi < S) ? ws_delta[(int64_t)bh * S_pad + qi] : 0.f;
+
+    Lanes<D> L;
+    L.init(wave, lane, ts);
+
+    uint16_t* list = reinterpret_cast<uint16_t*>(smem + kSlots * T::kStage);
+    int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_kt : 0) + 15) & ~15));
+    int n_act = n_kt;
+    if (SEG)
+        n_act = active_tiles(myseg, skp, S, n_kt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
+                             lane);
+
+    auto tile_of = [&](int n, bool& partial) -> int {
+        if (SEG) {
+            const int e = __builtin_amdgcn_readfirstlane((int)list[n]);
+            partial = (e & 0x8000) != 0;
+            return e & 0x7fff;
+        }
+        partial = (n == n_kt - 1) && (S % 64 != 0);
+        return n;
+    };
+    // Copies of key tile n into slot n % 2: this wave's share of K and V (rows
+    // past S re-read row S-1; the masks exclude them) and, from wave 1, the key
+    // segment IDs.  Issued one iteration before the tile is read.
+    auto copy = [&](int n) {
+        bool part;
+        const int t = tile_of(n, part);
+        char* st = smem + (n % kSlots) * T::kStage;
+        const int64_t row0 = (int64_t)t * 64;
+        const __bf16* sk = kp + row0 * ts;
+        const __bf16* sv = vp + row0 * ts;
+        const bool tail = row0 + 64 > S;
+#pragma unroll
+        for (int jj = 0; jj < T::kLoads; ++jj) {
+            uint32_t off = L.dmo[jj];
+            if (tail) {
+                const int over = max(0, (int)row0 + Lanes<D>::dma_row(wave, jj, lane) - (S - 1));
+                off -= (uint32_t)over * (uint32_t)(2 * ts);
+            }
+            const int i = wave * T::kLoads + jj;
+            dma16(sk, off, st + T::kA + i * 1024);
+            dma16(sv, off, st + T::kB + i * 1024);
+        }
+        if (SEG && wave == 1) {
+            const int r = min((int)row0 + lane, S - 1);
+            dma4(skp, 4u * (uint32_t)r, st + T::kSeg);
+        }
+    };
+
+    f32x16 dqacc[T::kDBlocks];
+#pragma unroll
+    for (int i = 0; i < T::kDBlocks; ++i) dqacc[i] = f32x16{};
+
+    if (n_act > 0) copy(0);
+    wait_vm(0);
+    barrier();
+    asm volatile("" ::"v"(qreg[0]), "v"(qreg[T::kSteps - 1]), "v"(doreg[0]), "v"(doreg[T::kSteps - 1]),
+                 "v"(myseg), "v"(lse2), "v"(delta));
+
+    for (int n = 0; n < n_act; ++n) {
+        const bool more = n + 1 < n_act;
+        if (more) copy(n + 1);
+        bool partial;
+        const int t = tile_of(n, partial);
+        const uint32_t st = lds_addr(smem) + (n % kSlots) * T::kStage;
+        const uint32_t tk = st + T::kA, tv = st + T::kB;
+
+        // S^T = K Q^T and dP^T = V dO^T over 64 keys (two 32-row blocks).
+        f32x16 sacc[2], pacc[2];
+        static_for<0, T::kSteps>([&](auto kc) {
+            constexpr int ks = kc;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const bf16x8 ak = row_operand<D>(tk, L.rx, ks, bb);
+                const bf16x8 av = row_operand<D>(tv, L.rx, ks, bb);
+                if constexpr (ks == 0) {
+                    sacc[bb] = mfma32(ak, qreg[0], f32x16{});
+                    pacc[bb] = mfma32(av, doreg[0], f32x16{});
+                } else {
+                    sacc[bb] = mfma32(ak, qreg[ks], sacc[bb]);
+                    pacc[bb] = mfma32(av, doreg[ks], pacc[bb]);
+                }
+            }
+        });
+
+        // dS^T = P^T (dP^T - delta); register r of block bb holds key
+        // t*64 + bb*32 + 16(r >> 3) + 8g + (r & 7).
+        bf16x8 dsb[4];
+        const int lim = S - t * 64 - 8 * g;
+        const int* sgs = reinterpret_cast<const int*>(lds_ptr(st + T::kSeg)) + 8 * g;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int jc = bb * 32 + 16 * (r >> 3) + (r & 7);
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c_log2, -lse2));
+                if (partial) {
+                    bool ok = jc < lim;
+                    if (SEG) ok = ok && (sgs[jc] == myseg) && (myseg != 0);
+                    p = ok ? p : 0.f;
+                }
+                dsb[2 * bb + (r >> 3)][r & 7] = (__bf16)(p * (pacc[bb][r] - delta));
+            }
+        }
+
+        // dQ^T += K^T dS^T (k = keys, 16 per step).
+        static_for<0, 4>([&](auto kc) {
+            constexpr int kst = kc;
+#pragma unroll
+            for (int db = 0; db < T::kDBlocks; ++db)
+                dqacc[db] = mfma32(tr_operand<D>(tk, L.tx0, L.tx1, kst, db), dsb[kst], dqacc[db]);
+        });
+
+        // The copy of tile n+1 must have landed in every wave before the
+        // barrier that opens iteration n+1.
+        wait_vm(0);
+        barrier();
+    }
+
+    // ---- epilogue: dq = scale dQ^T (bf16) ------------------------------------------
+    if (qi < S) {
+        const int64_t o = head0 + (int64_t)qi * ts;
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = db * 32 + 8 * r4 + 4 * g;
+                __bf16 q4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q4[e] = (__bf16)(dqacc[db][4 * r4 + e] * scale);
+                *reinterpret_cast<uint2*>(dq + o + d) = *reinterpret_cast<const uint2*>(q4);
+            }
+        }
+    }
+}
+
+template <int D>
+size_t dkdv_lds(bool seg, int n_tiles) {
+    size_t b = 3 * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
+    return ((b + 15) & ~(size_t)15) + 16 * sizeof(int);
+}
+template <int D>
+size_t dq_lds(bool seg, int n_tiles) {
+    size_t b = 2 * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
+    return ((b + 15) & ~(size_t)15) + 16 * sizeof(int);
+}
+
+template <int D, bool SEG>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+    const int S_pad = (int)(((int64_t)a.S + kPad - 1) / kPad * kPad);
+    float* ws_lse2 = reinterpret_cast<float*>(a.workspace);
+    float* ws_delta = ws_lse2 + (int64_t)a.B * a.H * S_pad;
+    const float c_log2 = a.scale * kLog2e;
+    const auto* q = reinterpret_cast<const __bf16*>(a.q);
+    const auto* k = reinterpret_cast<const __bf16*>(a.k);
+    const auto* v = reinterpret_cast<const __bf16*>(a.v);
+    const auto* dout = reinterpret_cast<const __bf16*>(a.dout);
+    {
+        const int64_t n_rows = (int64_t)a.B * a.S * a.H;
+        const int64_t n_items = n_rows + (int64_t)a.B * a.H * (S_pad - a.S);
+        const int64_t per_block = 256 / (D / 8);
+        const int64_t blocks = std::min<int64_t>((n_items + per_block - 1) / per_block, 1 << 20);
+        hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const __bf16*>(a.out), dout, a.lse, ws_lse2, ws_delta,
+                           a.S, a.H, S_pad, n_rows, n_items);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int n_blk = (a.S + kBwdRows - 1) / kBwdRows;
+    const int n_tiles = (a.S + 63) / 64;
+    const int n_wg = (int)((int64_t)a.B * a.H * n_blk);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, SEG>), dim3(n_wg), dim3(kBwdThreads),
+                       dkdv_lds<D>(SEG, n_tiles), stream, q, k, v, dout, a.seg_q, a.seg_kv, ws_lse2,
+                       ws_delta, reinterpret_cast<__bf16*>(a.dk), reinterpret_cast<__bf16*>(a.dv), a.S,
+                       S_pad, a.H, c_log2, a.scale, n_blk, n_tiles, n_wg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, SEG>), dim3(n_wg), dim3(kBwdThreads),
+                       dq_lds<D>(SEG, n_tiles), stream, q, k, v, dout, a.seg_q, a.seg_kv, ws_lse2,
+                       ws_delta, reinterpret_cast<__bf16*>(a.dq), a.S, S_pad, a.H, c_log2, a.scale,
+                       n_blk, n_tiles, n_wg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t S, int64_t H) {
+    const int64_t S_pad = (S + kPad - 1) / kPad * kPad;
+    return (size_t)(2 * B * H * S_pad) * sizeof(float);
+}
+
+int64_t bwd_max_masked_seq() { return (int64_t)kBwdMaxTiles * 64; }
+int64_t bwd_rows_per_workgroup() { return kBwdRows; }
+
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream) {
+    const bool seg = a.seg_q != nullptr;
+    if (a.D == 128) return seg ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+    return seg ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
+}
+
+}  // namespace vdx

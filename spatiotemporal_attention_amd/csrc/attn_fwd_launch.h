@@ -54,3 +54,36 @@ hipError_t launch_natten_fwd(const NattenArgs& a, hipStream_t stream);
 int64_t natten_workgroups(const NattenArgs& a);
 
 }  // namespace vdx
+
+namespace vdx {
+
+// Backward of segment-masked attention.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* seg_q;  // nullptr together with seg_kv -> unmasked
+    const int32_t* seg_kv;
+    const void* out;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    void* workspace;  // attn_bwd_workspace_bytes(B, S, H) bytes
+    int B, S, H, D;
+    float scale;
+};
+
+// Workspace the backward needs: per (b, h) two fp32 rows (lse2, delta) of S
+// rounded up to a multiple of 64.
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t S, int64_t H);
+
+// Enqueue the three backward kernels; arguments are already validated.
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t stream);
+
+// Largest S accepted with segment IDs, and rows per workgroup (grid size).
+int64_t bwd_max_masked_seq();
+int64_t bwd_rows_per_workgroup();
+
+}  // namespace vdx

@@ -84,6 +84,34 @@ int validate_natten(const void* q, const void* k, const void* v, const void* out
     return VDX_OK;
 }
 
+int validate_bwd(const void* q, const void* k, const void* v, const int32_t* seg_q,
+                 const int32_t* seg_kv, const void* out, const float* lse, const void* dout,
+                 const void* dq, const void* dk, const void* dv, const void* ws, size_t ws_bytes,
+                 int B, int S, int H, int D, float scale) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return VDX_ERR_NULL_PTR;
+    if ((seg_q == nullptr) != (seg_kv == nullptr)) return VDX_ERR_SEG_PAIR;
+    if (B < 1 || S < 1 || H < 1) return VDX_ERR_SHAPE;
+    if (S > INT32_MAX - 64) return VDX_ERR_SHAPE;
+    if (D > 0) {
+        const __int128 n = (__int128)B * S * H * D;
+        if (n > (__int128)INT64_MAX / 2) return VDX_ERR_SHAPE;
+        if ((int64_t)64 * H * D > INT32_MAX) return VDX_ERR_SHAPE;
+    }
+    const int64_t rows = vdx::bwd_rows_per_workgroup();
+    if ((int64_t)B * H * ((S + rows - 1) / rows) > INT32_MAX) return VDX_ERR_SHAPE;
+    if (seg_q && (int64_t)S > vdx::bwd_max_masked_seq()) return VDX_ERR_SHAPE;
+    if (D != 64 && D != 128) return VDX_ERR_HEAD_DIM;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return VDX_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return VDX_ERR_ALIGN;
+    if (!aligned(lse, 4) || (seg_q && (!aligned(seg_q, 4) || !aligned(seg_kv, 4))))
+        return VDX_ERR_ALIGN;
+    if (!ws || !aligned(ws, 16) || ws_bytes < vdx::attn_bwd_workspace_bytes(B, S, H))
+        return VDX_ERR_WORKSPACE;
+    return VDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +140,28 @@ __attribute__((visibility("default"))) int vdx_natten3d_fwd(
     return VDX_OK;
 }
 
+__attribute__((visibility("default"))) int vdx_attn_bwd(
+    const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
+    const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+    void* workspace, size_t workspace_bytes, int B, int S, int H, int D, float scale,
+    hipStream_t stream) {
+    int rc = validate_bwd(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, workspace,
+                          workspace_bytes, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    vdx::BwdArgs a{q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, workspace, B, S, H, D, scale};
+    if (vdx::launch_attn_bwd(a, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
+__attribute__((visibility("default"))) size_t vdx_attn_bwd_workspace_size(int B, int S, int H) {
+    if (B < 1 || S < 1 || H < 1 || S > INT32_MAX - 64) return 0;
+    const __int128 n = (__int128)B * H * (((int64_t)S + 63) / 64 * 64) * 8;
+    if (n > (__int128)INT64_MAX) return 0;
+    return vdx::attn_bwd_workspace_bytes(B, S, H);
+}
+
 __attribute__((visibility("default"))) const char* vdx_status_str(int status) {
     switch (status) {
         case VDX_OK: return "VDX_OK";
@@ -125,6 +175,8 @@ __attribute__((visibility("default"))) const char* vdx_status_str(int status) {
         case VDX_ERR_LAUNCH: return "VDX_ERR_LAUNCH: kernel launch failed";
         case VDX_ERR_WINDOW:
             return "VDX_ERR_WINDOW: window sizes must be odd and >= 1, the x window at most 13";
+        case VDX_ERR_WORKSPACE:
+            return "VDX_ERR_WORKSPACE: workspace NULL, misaligned or smaller than vdx_attn_bwd_workspace_size";
         default: return "VDX_ERR_UNKNOWN";
     }
 }

@@ -33,7 +33,8 @@ def native():
 
 def test_exports_every_declared_function(native):
     names = header_functions()
-    assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_status_str", "vdx_abi_version"])
+    assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd",
+                            "vdx_attn_bwd_workspace_size", "vdx_status_str", "vdx_abi_version"])
     for n in names:
         assert hasattr(native.lib, n), n
 
@@ -208,3 +209,103 @@ def test_natten_python_wrapper_rejects_bad_grid():
     q = torch.zeros(1, 10, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         vdx.natten3d_fwd(q, q, q, grid=(2, 2, 2), window=(1, 1, 1))
+
+
+# --- vdx_attn_bwd validation (no GPU needed) -------------------------------------
+def bcall(native, q=A, k=A + 0x100, v=A + 0x200, sq=0, sk=0, out=A + 0x300, lse=A + 0x400,
+          dout=A + 0x500, dq=A + 0x600, dk=A + 0x700, dv=A + 0x800, ws=A + 0x900, ws_bytes=None,
+          B=1, S=128, H=2, D=128, scale=0.125):
+    if ws_bytes is None:
+        ws_bytes = max(native.attn_bwd_workspace_size(B, S, H), 0)
+    return native.attn_bwd_raw(q, k, v, sq, sk, out, lse, dout, dq, dk, dv, ws, ws_bytes,
+                               B, S, H, D, scale, 0)
+
+
+def test_bwd_workspace_size(native):
+    # two fp32 rows per (b, h), S padded to a multiple of 64
+    assert native.attn_bwd_workspace_size(1, 75600, 40) == 2 * 40 * 75648 * 4
+    assert native.attn_bwd_workspace_size(2, 1, 3) == 2 * 6 * 64 * 4
+    assert native.attn_bwd_workspace_size(1, 64, 1) == 2 * 64 * 4
+    for bad in ((0, 1, 1), (1, 0, 1), (1, 1, 0), (1, 2**31 - 1, 1)):
+        assert native.attn_bwd_workspace_size(*bad) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"])
+def test_bwd_null_pointer(native, which):
+    assert bcall(native, **{which: 0}) == native.VDX_ERR_NULL_PTR
+
+
+def test_bwd_segment_pair(native):
+    assert bcall(native, sq=A + 0xa00) == native.VDX_ERR_SEG_PAIR
+    assert bcall(native, sk=A + 0xa00) == native.VDX_ERR_SEG_PAIR
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(S=0), dict(H=-1), dict(S=2**31 - 64),
+                                dict(S=1_966_081, sq=A + 0xa00, sk=A + 0xb00),
+                                dict(H=2**18, D=128)])
+def test_bwd_shape(native, kw):
+    kw.setdefault("ws_bytes", 1 << 40)
+    assert bcall(native, **kw) == native.VDX_ERR_SHAPE
+
+
+@pytest.mark.parametrize("D", [0, 32, 96, 256])
+def test_bwd_head_dim(native, D):
+    assert bcall(native, D=D) == native.VDX_ERR_HEAD_DIM
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan"), float("inf")])
+def test_bwd_scale(native, scale):
+    assert bcall(native, scale=scale) == native.VDX_ERR_SCALE
+
+
+@pytest.mark.parametrize("kw", [dict(q=A + 2), dict(dout=A + 0x508), dict(dq=A + 0x604),
+                                dict(dk=A + 0x702), dict(dv=A + 0x80a), dict(out=A + 0x306),
+                                dict(lse=A + 0x402), dict(sq=A + 0xa01, sk=A + 0xb00)])
+def test_bwd_alignment(native, kw):
+    assert bcall(native, **kw) == native.VDX_ERR_ALIGN
+
+
+@pytest.mark.parametrize("kw", [dict(ws=0), dict(ws=A + 0x908), dict(ws_bytes=2 * 2 * 128 * 4 - 4)])
+def test_bwd_workspace(native, kw):
+    assert bcall(native, **kw) == native.VDX_ERR_WORKSPACE
+
+
+def test_bwd_validation_order(native):
+    # NULL -> segment pair -> shape -> head dim -> scale -> alignment -> workspace
+    assert bcall(native, dv=0, sq=A, B=0, D=3, scale=-1.0, ws=0) == native.VDX_ERR_NULL_PTR
+    assert bcall(native, sq=A + 0xa00, B=0, D=3, scale=-1.0, ws=0) == native.VDX_ERR_SEG_PAIR
+    assert bcall(native, B=0, D=3, scale=-1.0, q=A + 1, ws=0) == native.VDX_ERR_SHAPE
+    assert bcall(native, D=3, scale=-1.0, q=A + 1, ws=0) == native.VDX_ERR_HEAD_DIM
+    assert bcall(native, scale=-1.0, q=A + 1, ws=0) == native.VDX_ERR_SCALE
+    assert bcall(native, q=A + 1, ws=0) == native.VDX_ERR_ALIGN
+
+
+def test_bwd_valid_arguments_without_gpu_report_device_error(native):
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this path would launch on fake addresses")
+    assert bcall(native) == native.VDX_ERR_DEVICE
+
+
+def test_bwd_python_wrapper_rejects_bad_tensors():
+    import spatiotemporal_attention_amd as vdx
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        vdx.attn_bwd(q, q, q, q, lse, q)  # CPU tensors are refused before the C call
+
+
+@pytest.mark.gpu
+def test_bwd_error_path_writes_nothing(need_gpu):
+    import spatiotemporal_attention_amd as vdx
+    from spatiotemporal_attention_amd import _native
+    q = torch.randn(1, 64, 1, 64, device="cuda").bfloat16()
+    lse = torch.zeros(1, 1, 64, device="cuda")
+    g = [torch.full_like(q, 3.0) for _ in range(3)]
+    ws = torch.full((vdx.attn_bwd_workspace_size(1, 64, 1),), 7, dtype=torch.uint8, device="cuda")
+    rc = _native.attn_bwd_raw(q.data_ptr(), q.data_ptr(), q.data_ptr(), 0, 0, q.data_ptr(),
+                              lse.data_ptr(), q.data_ptr(), g[0].data_ptr(), g[1].data_ptr(),
+                              g[2].data_ptr(), ws.data_ptr(), ws.numel() - 1, 1, 64, 1, 64, 0.125,
+                              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == _native.VDX_ERR_WORKSPACE
+    assert all(torch.all(t == 3.0) for t in g) and torch.all(ws == 7)

@@ -127,3 +127,17 @@ def test_neighbourhood_kernel_wait_states_and_no_spills(natten_asm_text):
     assert lds_dma_hazards(natten_asm_text) == []
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", natten_asm_text)]
     assert sizes == [0, 0]  # D in {64, 128}
+
+
+@pytest.fixture(scope="module")
+def bwd_asm_text():
+    return _compile("attn_bwd_kernel.hip")
+
+
+def test_backward_kernels_wait_states_and_no_spills(bwd_asm_text):
+    n = sum(1 for t in _instructions(bwd_asm_text.split("\n")) if t.startswith("global_load_lds"))
+    assert n > 0
+    assert lds_dma_hazards(bwd_asm_text) == []
+    sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", bwd_asm_text)]
+    assert len(sizes) == 10  # prep x {64, 128}; dK/dV and dQ x {64, 128} x {unmasked, masked}
+    assert sizes == [0] * 10
