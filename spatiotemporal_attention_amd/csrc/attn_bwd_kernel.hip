@@ -46,8 +46,12 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or queries (dQ) per workgroup
-constexpr int kBwdMaxTiles = 30720;       // capacity of the on-chip active-tile list
+constexpr int kBwdMaxTiles = 14000;       // capacity of the on-chip active-tile list
 constexpr int kPad = 64;                  // workspace rows are padded to this multiple
+#ifndef VDX_BWD_PREFETCH
+#define VDX_BWD_PREFETCH 4
+#endif
+constexpr int kPf = VDX_BWD_PREFETCH;     // MFMA operands in flight
 
 template <int D>
 struct BTile {
@@ -155,6 +159,43 @@ __device__ __forceinline__ bf16x8 tr_operand(uint32_t tile, int tx0, int tx1, in
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += a b with acc held in AGPRs (accumulation registers), for
+// accumulators that only MFMAs touch until the epilogue: the register
+// allocator then never moves them between register files.  The hazard
+// recogniser does not look inside inline asm, so the wait states it would
+// insert are explicit: a VALU write (including the v_accvgpr_mov the
+// allocator may place to relocate acc between code paths) of an operand ->
+// MFMA read needs 2, given by the s_nop 1 of every such MFMA (it mostly
+// overlaps the wait for the busy matrix pipe), and 4 when NOP (a VALU
+// instruction may have written b just before); accumulator_fence() supplies
+// the ones between the last MFMA write and a VALU read of the result (an
+// 8-pass XDL write needs 11; 20 are given).
+template <bool NOP>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    if constexpr (NOP)
+        asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void accumulator_fence() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+}
+
+// acc (VGPRs, read by the VALU afterwards) = a b (+ acc unless FIRST), with b
+// held in AGPRs: a K or V slice that only MFMAs read (written there once, by
+// the VALU, before the sweep: NOP gives the first MFMAs their 4 wait states).
+// accumulator_fence() must separate the last such MFMA from the first VALU
+// read of acc.
+template <bool FIRST, bool NOP>
+__device__ __forceinline__ void mfma32_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    if constexpr (FIRST && NOP)
+        asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
+    else if constexpr (FIRST)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
 
 // Classifies every 64-row tile of the opposite side (segment IDs `other`,
@@ -270,6 +311,180 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
 }
 
 // ---- dK / dV ---------------------------------------------------------------------
+// Key-major sweep over the active 64-query tiles, each taken as two 32-query
+// sub-tiles, software-pipelined inside each wave (one wave per SIMD: the K/V
+// slices and the dK/dV accumulators take 192 AGPRs) so that its MFMAs and
+// VALU work overlap.  Sub-iteration u:
+//   step 1: dV^T += dO^T P and dK^T += Q^T dS of sub-tile u-1 (kNB MFMAs);
+//   step 2: S = Q K^T and dP = dO V^T of sub-tile u+1 (kNA MFMAs), with P and
+//           dS of sub-tile u formed on the VALU between them, two elements
+//           per MFMA.
+// A tile iteration (two sub-iterations) reads tiles t-1, t and t+1 while
+// t+2 lands, hence four ring slots and one barrier per tile.  Operands are
+// fetched kPf MFMAs ahead through an 8-entry ring, across step and iteration
+// boundaries (every tile read across the closing barrier is resident).  S/dP
+// and the bf16 P/dS operands alternate between two register buffers (the
+// loop is unrolled by a tile).
+template <int D, bool SEG>
+struct DkDv {
+    using T = BTile<D>;
+    static constexpr int kSlots = 4;
+    static constexpr int kRing = 8;
+    static constexpr int kNA = 2 * T::kSteps;    // S and dP MFMAs per sub-tile
+    static constexpr int kNB = 4 * T::kDBlocks;  // dV and dK MFMAs per sub-tile
+    static constexpr int kPairs = 8;             // softmax element pairs per lane and sub-tile
+    static constexpr int kPairAhead = 2;         // lse2 / delta loads in flight
+    static_assert(kNA % kRing == 0 && kNB % kRing == 0 && kPf <= kRing - 2, "operand ring");
+    static_assert(kNA >= kPairs, "two softmax elements per S/dP MFMA");
+
+    char* smem;
+    Lanes<D> L;
+    int g, myseg;
+    float c_log2;
+    bf16x8 kreg[T::kSteps], vreg[T::kSteps];        // AGPRs (B operands)
+    f32x16 dkacc[T::kDBlocks], dvacc[T::kDBlocks];  // AGPRs (accumulators)
+    f32x16 sc[2], pc[2];                            // S, dP of a sub-tile, by parity
+    bf16x8 pb[2][2], dsb[2][2];                     // P, dS as bf16 B operands [parity][k-step]
+    bf16x8 ring[kRing];
+    float2 lpair[kPairAhead], dpair[kPairAhead];
+    int2 spair[kPairAhead];
+
+    __device__ __forceinline__ static uint32_t slot(int t) {
+        int o = (t % kSlots) * T::kStage;
+        asm volatile("" : "+s"(o));
+        return (uint32_t)o;
+    }
+
+    // MFMA i of the S/dP step of a sub-tile (rows 32*h .. of the tile at st):
+    // k-step i / 2, S (even i, Q rows) or dP (odd i, dO rows).
+    template <int I>
+    __device__ __forceinline__ bf16x8 op_a(uint32_t st, int h) const {
+        return row_operand<D>(st + ((I & 1) ? T::kB : T::kA), L.rx, I / 2, h);
+    }
+    // MFMA i of the dV/dK step of a sub-tile: query k-step 2h + i / (2
+    // kDBlocks), d-block (i / 2) % kDBlocks, dV (even i, dO) or dK (odd, Q).
+    template <int I>
+    __device__ __forceinline__ bf16x8 op_b(uint32_t st, int h) const {
+        return tr_operand<D>(st + ((I & 1) ? T::kA : T::kB), L.tx0, L.tx1,
+                             2 * h + I / (2 * T::kDBlocks), (I / 2) % T::kDBlocks);
+    }
+
+    // Softmax pair j of a sub-tile: accumulator registers r = 2j and 2j+1,
+    // queries row(j), row(j)+1 of the tile (sub-tile h covers rows 32h..).
+    __device__ __forceinline__ int pair_row(int h, int j) const {
+        return 32 * h + 16 * (j / 4) + 8 * g + 2 * (j % 4);
+    }
+    __device__ __forceinline__ void load_pair(uint32_t st, int h, int j, bool partial) {
+        const int row = pair_row(h, j);
+        lpair[j % kPairAhead] = *reinterpret_cast<const float2*>(lds_ptr(st + T::kVec0 + 4 * row));
+        dpair[j % kPairAhead] = *reinterpret_cast<const float2*>(lds_ptr(st + T::kVec1 + 4 * row));
+        // With segment IDs the mask is applied to every tile, full ones
+        // included (they pass it unchanged): a branch on the tile kind here
+        // would split the register assignment of the pipelined loop.
+        if (SEG)
+            spair[j % kPairAhead] = *reinterpret_cast<const int2*>(lds_ptr(st + T::kSeg + 4 * row));
+        (void)partial;
+    }
+    // P = 2^(s c - lse2), dS = P (dP - delta) for pair J of the sub-tile in
+    // buffer B.
+    template <int B, int J>
+    __device__ __forceinline__ void pair(bool partial) {
+        constexpr int r = 2 * J, k = r / 8, e = r % 8;
+        const float2 l = lpair[J % kPairAhead], d = dpair[J % kPairAhead];
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[B][r], c_log2, -l.x));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[B][r + 1], c_log2, -l.y));
+        if (SEG) {
+            const int2 s = spair[J % kPairAhead];
+            p0 = (s.x == myseg && myseg != 0) ? p0 : 0.f;
+            p1 = (s.y == myseg && myseg != 0) ? p1 : 0.f;
+        }
+        (void)partial;
+        pb[B][k][e] = (__bf16)p0;
+        pb[B][k][e + 1] = (__bf16)p1;
+        dsb[B][k][e] = (__bf16)(p0 * (pc[B][r] - d.x));
+        dsb[B][k][e + 1] = (__bf16)(p1 * (pc[B][r + 1] - d.y));
+        // Keep the pair here, between the MFMAs it is meant to overlap: the
+        // optimiser would otherwise sink it towards its consumer, the next
+        // dV/dK step, behind this step's MFMAs.
+        asm volatile("" : "+v"(pb[B][k]), "+v"(dsb[B][k]));
+    }
+
+    __device__ __forceinline__ void prefetch_a(uint32_t st, int h) {
+        static_for<0, kPf>([&](auto ic) { ring[ic] = op_a<ic>(st, h); });
+    }
+    __device__ __forceinline__ void prefetch_pairs(uint32_t sv, int h, bool partial) {
+        static_for<0, kPairAhead>([&](auto jc) { load_pair(sv, h, jc, partial); });
+    }
+
+    // Step 1: dV / dK of the sub-tile (tile at st, half h) whose P / dS are
+    // in buffer B (operands prefetched).  NEXT_A: the last steps fetch the
+    // first operands of the S/dP step of sub-tile (sa, ha).
+    template <int B, bool NEXT_A>
+    __device__ __forceinline__ void step_b(uint32_t st, int h, uint32_t sa, int ha) {
+        static_for<0, kNB>([&](auto ic) {
+            constexpr int i = ic;
+            if constexpr (i + kPf < kNB)
+                ring[(i + kPf) % kRing] = op_b<i + kPf>(st, h);
+            else if constexpr (NEXT_A)
+                ring[(i + kPf) % kRing] = op_a<i + kPf - kNB>(sa, ha);
+            const bf16x8& a = ring[i % kRing];
+            constexpr int kst = i / (2 * T::kDBlocks), db = (i / 2) % T::kDBlocks;
+            if constexpr (i & 1)
+                mfma32_acc<(i < 2)>(dkacc[db], a, dsb[B][kst]);
+            else
+                mfma32_acc<(i < 2)>(dvacc[db], a, pb[B][kst]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+    // Step 2: S / dP of sub-tile (sa, ha) into buffer B ^ 1 (if A) with the
+    // softmax of buffer B (sub-tile (sv, hv)) interleaved; the last steps
+    // fetch the first dV/dK operands of sub-tile (sv, hv).
+    template <int B, bool A>
+    __device__ __forceinline__ void step_a(uint32_t sa, int ha, uint32_t sv, int hv, bool partial) {
+        if constexpr (A) {
+            static_for<0, kNA>([&](auto ic) {
+                constexpr int i = ic;
+                if constexpr (i + kPf < kNA)
+                    ring[(i + kPf) % kRing] = op_a<i + kPf>(sa, ha);
+                else
+                    ring[(i + kPf) % kRing] = op_b<i + kPf - kNA>(sv, hv);
+                const bf16x8& a = ring[i % kRing];
+                constexpr int ks = i / 2;
+                if constexpr (i & 1)
+                    mfma32_vacc<(ks == 0), false>(pc[B ^ 1], a, vreg[ks]);
+                else
+                    mfma32_vacc<(ks == 0), false>(sc[B ^ 1], a, kreg[ks]);
+                if constexpr (i < kPairs) {
+                    pair<B, i>(partial);
+                    if constexpr (i + kPairAhead < kPairs) load_pair(sv, hv, i + kPairAhead, partial);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else {
+            static_for<0, kPairs>([&](auto jc) {
+                constexpr int j = jc;
+                pair<B, j>(partial);
+                if constexpr (j + kPairAhead < kPairs) load_pair(sv, hv, j + kPairAhead, partial);
+            });
+            static_for<0, kPf>([&](auto ic) { ring[ic] = op_b<ic>(sv, hv); });
+        }
+    }
+    // S / dP of the first sub-tile alone, into buffer 0.
+    __device__ __forceinline__ void step_a_only(uint32_t sa) {
+        static_for<0, kNA>([&](auto ic) {
+            constexpr int i = ic;
+            if constexpr (i + kPf < kNA) ring[(i + kPf) % kRing] = op_a<i + kPf>(sa, 0);
+            const bf16x8& a = ring[i % kRing];
+            constexpr int ks = i / 2;
+            if constexpr (i & 1)
+                mfma32_vacc<(ks == 0), (i < 2)>(pc[0], a, vreg[ks]);
+            else
+                mfma32_vacc<(ks == 0), (i < 2)>(sc[0], a, kreg[ks]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+};
+
 template <int D, bool SEG>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -279,7 +494,8 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int S, int S_pad,
                           int H, float c_log2, float scale, int n_blk, int n_qt, int n_wg) {
     using T = BTile<D>;
-    constexpr int kSlots = 3;
+    using K = DkDv<D, SEG>;
+    constexpr int kSlots = K::kSlots;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     int blk, bh;
     wg_coords(n_blk, n_wg, blk, bh);
@@ -296,26 +512,27 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     const float* dlp = ws_delta + (int64_t)bh * S_pad;
     const int32_t* sqp = SEG ? seg_q + (int64_t)b * S : nullptr;
 
+    K A;
+    A.smem = smem;
+    A.g = g;
+    A.c_log2 = c_log2;
     // K and V slices of this lane's key as B operands (k = d, n = key).
-    bf16x8 kreg[T::kSteps], vreg[T::kSteps];
     {
         const int64_t off = head0 + (int64_t)kj * ts + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < T::kSteps; ++ks) {
-            kreg[ks] = (kj < S) ? *reinterpret_cast<const bf16x8*>(k + off + 16 * ks) : bf16x8{};
-            vreg[ks] = (kj < S) ? *reinterpret_cast<const bf16x8*>(v + off + 16 * ks) : bf16x8{};
+            A.kreg[ks] = (kj < S) ? *reinterpret_cast<const bf16x8*>(k + off + 16 * ks) : bf16x8{};
+            A.vreg[ks] = (kj < S) ? *reinterpret_cast<const bf16x8*>(v + off + 16 * ks) : bf16x8{};
         }
     }
-    const int myseg = SEG ? ((kj < S) ? seg_kv[(int64_t)b * S + kj] : 0) : 1;
-
-    Lanes<D> L;
-    L.init(wave, lane, ts);
+    A.myseg = SEG ? ((kj < S) ? seg_kv[(int64_t)b * S + kj] : 0) : 1;
+    A.L.init(wave, lane, ts);
 
     uint16_t* list = reinterpret_cast<uint16_t*>(smem + kSlots * T::kStage);
     int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_qt : 0) + 15) & ~15));
     int n_act = n_qt;
     if (SEG)
-        n_act = active_tiles(myseg, sqp, S, n_qt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
+        n_act = active_tiles(A.myseg, sqp, S, n_qt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
                              lane);
 
     auto tile_of = [&](int n, bool& partial) -> int {
@@ -327,10 +544,9 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         partial = false;
         return n;
     };
-    // Copies of query tile n of the active list into slot n % 3: this wave's
+    // Copies of query tile n of the active list into slot n % 4: this wave's
     // share of Q and dO (rows past S re-read row S-1; their lse2 is +inf), the
     // lse2 and delta rows (wave 0) and the query segment IDs (wave 1).
-    const int n_copy = 2 * T::kLoads + (wave == 0 ? 2 : 0) + ((SEG && wave == 1) ? 1 : 0);
     auto copy = [&](int n) {
         bool part;
         const int t = tile_of(n, part);
@@ -341,7 +557,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         const bool tail = row0 + 64 > S;
 #pragma unroll
         for (int jj = 0; jj < T::kLoads; ++jj) {
-            uint32_t off = L.dmo[jj];
+            uint32_t off = A.L.dmo[jj];
             if (tail) {
                 const int over = max(0, (int)row0 + Lanes<D>::dma_row(wave, jj, lane) - (S - 1));
                 off -= (uint32_t)over * (uint32_t)(2 * ts);
@@ -360,99 +576,66 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         }
     };
 
-    f32x16 dkacc[T::kDBlocks], dvacc[T::kDBlocks];
 #pragma unroll
-    for (int i = 0; i < T::kDBlocks; ++i) dkacc[i] = dvacc[i] = f32x16{};
-
-    if (n_act > 0) copy(0);
-    if (n_act > 1) copy(1);
-    wait_vm(0);
-    barrier();
-    // Wait for the K/V slices (and the key's segment ID) here rather than in
-    // the loop, where a vmcnt wait would also drain the tile copies.
-    asm volatile("" ::"v"(kreg[0]), "v"(kreg[T::kSteps - 1]), "v"(vreg[0]), "v"(vreg[T::kSteps - 1]),
-                 "v"(myseg));
-
-    for (int n = 0; n < n_act; ++n) {
-        const bool more = n + 2 < n_act;
-        if (more) copy(n + 2);
-        bool partial;
-        tile_of(n, partial);
-        const uint32_t st = lds_addr(smem) + (n % kSlots) * T::kStage;
-        const uint32_t tq = st + T::kA, td = st + T::kB;
-
-        // S = Q K^T and dP = dO V^T over 64 queries (two 32-row blocks).
-        f32x16 sacc[2], pacc[2];
-        static_for<0, T::kSteps>([&](auto kc) {
-            constexpr int ks = kc;
+    for (int i = 0; i < T::kDBlocks; ++i) A.dkacc[i] = A.dvacc[i] = f32x16{};
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const bf16x8 aq = row_operand<D>(tq, L.rx, ks, bb);
-                const bf16x8 ad = row_operand<D>(td, L.rx, ks, bb);
-                if constexpr (ks == 0) {
-                    sacc[bb] = mfma32(aq, kreg[0], f32x16{});
-                    pacc[bb] = mfma32(ad, vreg[0], f32x16{});
-                } else {
-                    sacc[bb] = mfma32(aq, kreg[ks], sacc[bb]);
-                    pacc[bb] = mfma32(ad, vreg[ks], pacc[bb]);
-                }
-            }
-        });
+    for (int i = 0; i < T::kDBlocks; ++i) asm volatile("" : "+a"(A.dkacc[i]), "+a"(A.dvacc[i]));
 
-        // P = 2^(s c - lse2) and dS = P (dP - delta).  Register r of block bb
-        // holds query bb*32 + 16(r >> 3) + 8g + (r & 7) of the tile.
-        bf16x8 pb[4], dsb[4];
-        const float* l2s = reinterpret_cast<const float*>(lds_ptr(st + T::kVec0));
-        const float* dls = reinterpret_cast<const float*>(lds_ptr(st + T::kVec1));
-        const int* sgs = reinterpret_cast<const int*>(lds_ptr(st + T::kSeg));
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int row = bb * 32 + 16 * hh + 8 * g;
-                const float4 la = *reinterpret_cast<const float4*>(l2s + row);
-                const float4 lb = *reinterpret_cast<const float4*>(l2s + row + 4);
-                const float4 da = *reinterpret_cast<const float4*>(dls + row);
-                const float4 db4 = *reinterpret_cast<const float4*>(dls + row + 4);
-                const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-                const float d8[8] = {da.x, da.y, da.z, da.w, db4.x, db4.y, db4.z, db4.w};
-                int s8[8];
-                if (SEG && partial) {
-                    const int4 sa = *reinterpret_cast<const int4*>(sgs + row);
-                    const int4 sb = *reinterpret_cast<const int4*>(sgs + row + 4);
-                    s8[0] = sa.x; s8[1] = sa.y; s8[2] = sa.z; s8[3] = sa.w;
-                    s8[4] = sb.x; s8[5] = sb.y; s8[6] = sb.z; s8[7] = sb.w;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * hh + e;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c_log2, -l8[e]));
-                    if (SEG && partial) p = (s8[e] == myseg && myseg != 0) ? p : 0.f;
-                    const float ds = p * (pacc[bb][r] - d8[e]);
-                    pb[2 * bb + hh][e] = (__bf16)p;
-                    dsb[2 * bb + hh][e] = (__bf16)ds;
-                }
-            }
-        }
-
-        // dV^T += dO^T P and dK^T += Q^T dS (k = queries, 16 per step).
-        static_for<0, 4>([&](auto kc) {
-            constexpr int kst = kc;
-#pragma unroll
-            for (int db = 0; db < T::kDBlocks; ++db) {
-                dvacc[db] = mfma32(tr_operand<D>(td, L.tx0, L.tx1, kst, db), pb[kst], dvacc[db]);
-                dkacc[db] = mfma32(tr_operand<D>(tq, L.tx0, L.tx1, kst, db), dsb[kst], dkacc[db]);
-            }
-        });
-
-        // The copy of tile n+1 (issued one iteration ago) must have landed in
-        // every wave before the barrier that opens iteration n+1; tile n's
-        // slot is refilled only after that barrier.
-        wait_vm_upto(more ? n_copy : 0);
+    if (n_act > 0) {
+        copy(0);
+        if (n_act > 1) copy(1);
+        wait_vm(0);
         barrier();
+        // Wait for the K/V slices (and the key's segment ID) here rather than
+        // in the loop, where a vmcnt wait would also drain the tile copies,
+        // and move the slices into AGPRs now, once: the MFMAs read them from
+        // there, and their VALU writes need wait states before the first read.
+        asm volatile("" ::"v"(A.kreg[0]), "v"(A.kreg[T::kSteps - 1]), "v"(A.vreg[0]),
+                     "v"(A.vreg[T::kSteps - 1]), "v"(A.myseg));
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) asm volatile("" : "+a"(A.kreg[ks]), "+a"(A.vreg[ks]));
+        asm volatile("s_nop 3" ::: "memory");
+
+        const uint32_t sm = lds_addr(smem);
+        // Tile iteration t = sub-iterations 2t (half 0) and 2t + 1 (half 1):
+        //   2t:     dV/dK of (t-1, 1); S/dP of (t, 1) with softmax of (t, 0)
+        //   2t + 1: dV/dK of (t, 0); S/dP of (t+1, 0) with softmax of (t, 1)
+        // Every iteration has this one shape (and the register allocator one
+        // assignment, so it never relocates an accumulator next to an
+        // inline-asm MFMA): for t = 0 the dV/dK step of "(t-1, 1)" reads
+        // tile 0 with P = dS = 0 and adds exactly 0, and for the last tile
+        // the S/dP step of "(t+1, 0)" reads the current slot and its result
+        // is never used.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) A.pb[1][kk] = A.dsb[1][kk] = bf16x8{};
+        A.prefetch_a(sm + K::slot(0), 0);
+        A.step_a_only(sm + K::slot(0));
+        accumulator_fence();
+        static_for<0, kPf>([&](auto ic) { A.ring[ic] = A.template op_b<ic>(sm + K::slot(0), 1); });
+        for (int t = 0; t < n_act; ++t) {
+            const bool more = t + 2 < n_act;
+            if (more) copy(t + 2);
+            bool part;
+            tile_of(t, part);
+            part = SEG && part;
+            const uint32_t s0 = sm + K::slot(t);
+            const uint32_t sp = (t > 0) ? sm + K::slot(t - 1) : s0;
+            const uint32_t sn = (t + 1 < n_act) ? sm + K::slot(t + 1) : s0;
+            A.template step_b<1, true>(sp, 1, s0, 1);
+            A.prefetch_pairs(s0, 0, part);
+            A.template step_a<0, true>(s0, 1, s0, 0, part);
+            A.template step_b<0, true>(s0, 0, sn, 0);
+            A.prefetch_pairs(s0, 1, part);
+            A.template step_a<1, true>(sn, 0, s0, 1, part);
+            if (more) wait_vm(0);
+            barrier();
+        }
+        // dV/dK of the last sub-tile (tile n_act - 1, half 1).
+        A.template step_b<1, false>(sm + K::slot(n_act - 1), 1, 0, 0);
     }
 
     // ---- epilogue: dk = scale dK^T, dv = dV^T (bf16) ----------------------------
+    accumulator_fence();
     if (kj < S) {
         const int64_t o = head0 + (int64_t)kj * ts;
 #pragma unroll
@@ -463,8 +646,8 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                 __bf16 k4[4], v4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    k4[e] = (__bf16)(dkacc[db][4 * r4 + e] * scale);
-                    v4[e] = (__bf16)dvacc[db][4 * r4 + e];
+                    k4[e] = (__bf16)(A.dkacc[db][4 * r4 + e] * scale);
+                    v4[e] = (__bf16)A.dvacc[db][4 * r4 + e];
                 }
                 *reinterpret_cast<uint2*>(dk + o + d) = *reinterpret_cast<const uint2*>(k4);
                 *reinterpret_cast<uint2*>(dv + o + d) = *reinterpret_cast<const uint2*>(v4);
@@ -648,7 +831,7 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 
 template <int D>
 size_t dkdv_lds(bool seg, int n_tiles) {
-    size_t b = 3 * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
+    size_t b = DkDv<D, false>::kSlots * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
     return ((b + 15) & ~(size_t)15) + 16 * sizeof(int);
 }
 template <int D>

