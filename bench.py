@@ -54,6 +54,9 @@ NATTEN_METRIC = "3D neighbourhood attention TFLOP/s (window pairs) and % of bf16
 KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
                   for f in ("attn_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
                             "vdx_attn_api.hip")]
+BWD_KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
+                      for f in ("attn_bwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
+                                "vdx_attn_api.hip")]
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -81,25 +84,27 @@ def algorithmic_bytes(w: W.Workload) -> int:
     return b
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the summary is missing or was taken on different kernel source."""
-    path = os.path.join(COUNTERS_DIR, f"attn_fwd_{workload}_hbm_counters.json")
+def load_traffic(workload: str, pass_: str = "fwd"):
+    """HBM bytes per launch (forward) or per call (backward: its three kernels)
+    from the committed rocprofv3 counter summary, or None when the summary is
+    missing or was taken on different kernel source."""
+    path = os.path.join(COUNTERS_DIR, f"attn_{pass_}_{workload}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         doc = json.load(f)
-    if doc.get("kernel_source_sha256") != kernel_source_hash():
+    sources = KERNEL_SOURCES if pass_ == "fwd" else BWD_KERNEL_SOURCES
+    if doc.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
-    return doc.get("traffic_bytes_per_launch")
+    return doc.get("traffic_bytes_per_launch" if pass_ == "fwd" else "traffic_bytes_per_call")
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -299,7 +304,7 @@ def bwd_main(args, vdx):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "scope": "vdx_attn_bwd call (prep + dK/dV + dQ kernels)",
-                     "traffic": None,
+                     "traffic": load_traffic(w.name, "bwd"),
                      # reads q, k, v, out, dout, lse; writes dq, dk, dv
                      "algorithmic_bytes": 2 * 8 * n + 4 * w.B * w.H * w.S,
                      "kernel_ms_mean": round(call_ms, 4)},

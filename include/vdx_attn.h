@@ -168,7 +168,9 @@ int vdx_natten3d_fwd(const void* q, const void* k, const void* v, void* out, flo
  * Every pointer is a DEVICE pointer owned by the caller; the library
  * allocates nothing.  Validation runs before any HIP call, in the order
  * NULL (q, k, v, out, lse, dout, dq, dk, dv) -> segment pair -> shape (as for
- * vdx_attn_fwd, and S <= 2^31 - 65) -> head dim -> scale -> alignment (bf16
+ * vdx_attn_fwd, and S <= 2^31 - 65; a masked call needs S <= 896,000: the
+ * on-chip query-tile table of the dK/dV sweep holds 14,000 tiles of 64)
+ * -> head dim -> scale -> alignment (bf16
  * tensors 16-byte, lse and segment IDs 4-byte) -> workspace, and reports the
  * first failure without touching device memory.  Results are deterministic
  * (no atomics).

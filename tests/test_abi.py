@@ -241,7 +241,7 @@ def test_bwd_segment_pair(native):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(S=0), dict(H=-1), dict(S=2**31 - 64),
-                                dict(S=1_966_081, sq=A + 0xa00, sk=A + 0xb00),
+                                dict(S=896_001, sq=A + 0xa00, sk=A + 0xb00),
                                 dict(H=2**18, D=128)])
 def test_bwd_shape(native, kw):
     kw.setdefault("ws_bytes", 1 << 40)
@@ -284,6 +284,8 @@ def test_bwd_valid_arguments_without_gpu_report_device_error(native):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible; this path would launch on fake addresses")
     assert bcall(native) == native.VDX_ERR_DEVICE
+    # the largest masked sequence passes validation
+    assert bcall(native, S=896_000, sq=A + 0xa00, sk=A + 0xb00, ws_bytes=1 << 40) == native.VDX_ERR_DEVICE
 
 
 def test_bwd_python_wrapper_rejects_bad_tensors():
