@@ -198,71 +198,6 @@ __device__ __forceinline__ void mfma32_vacc(f32x16& acc, const bf16x8& a, const 
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
 
-// Classifies every 64-row tile of the opposite side (segment IDs `other`,
-// length S) against this workgroup's rows (ID `mine` per lane; 0 for padding
-// and rows past S) as skip / full / partial, and compacts the active tiles
-// into `list` (bit 15 set: partial).  `cls` is scratch of n_tiles bytes.
-// Returns the number of active tiles.
-__device__ int active_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
-                            uint16_t* list, int* meta, int wave, int lane) {
-    {
-        int mn = (mine != 0) ? mine : INT32_MAX;
-        int mx = (mine != 0) ? mine : INT32_MIN;
-        int fl = (mine == 0) ? 1 : 0;
-        mn = wave_min(mn);
-        mx = wave_max(mx);
-        fl = wave_max(fl);
-        if (lane == 0) {
-            meta[wave] = mn;
-            meta[kBwdWaves + wave] = mx;
-            meta[2 * kBwdWaves + wave] = fl;
-        }
-    }
-    __syncthreads();
-    int omn = INT32_MAX, omx = INT32_MIN, ofl = 0;
-#pragma unroll
-    for (int i = 0; i < kBwdWaves; ++i) {
-        omn = min(omn, meta[i]);
-        omx = max(omx, meta[kBwdWaves + i]);
-        ofl |= meta[2 * kBwdWaves + i];
-    }
-    for (int t = wave; t < n_tiles; t += kBwdWaves) {
-        const int r = t * 64 + lane;
-        const int id = (r < S) ? other[r] : 0;
-        int mn = (id != 0) ? id : INT32_MAX;
-        int mx = (id != 0) ? id : INT32_MIN;
-        int fl = (id == 0) ? 1 : 0;
-        mn = wave_min(mn);
-        mx = wave_max(mx);
-        fl = wave_max(fl);
-        if (lane == 0) {
-            uint8_t c;
-            if (omn > omx || mn > mx || max(omn, mn) > min(omx, mx))
-                c = 0;
-            else if (!ofl && !fl && omn == omx && mn == mx && omn == mn)
-                c = 1;
-            else
-                c = 2;
-            cls[t] = c;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int base = 0;
-        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
-            const int t = t0 + lane;
-            const int c = (t < n_tiles) ? cls[t] : 0;
-            const uint64_t m = __ballot(c != 0);
-            const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-            if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
-            base += __popcll(m);
-        }
-        if (lane == 0) meta[3 * kBwdWaves] = base;
-    }
-    __syncthreads();
-    return meta[3 * kBwdWaves];
-}
-
 // Workgroup id -> (row block, b*H + h), renumbered so that each XCD (own L2)
 // runs consecutive row blocks of one head, which share the swept tiles.
 __device__ __forceinline__ void wg_coords(int n_blk, int n_wg, int& blk, int& bh) {
@@ -532,7 +467,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_qt : 0) + 15) & ~15));
     int n_act = n_qt;
     if (SEG)
-        n_act = active_tiles(A.myseg, sqp, S, n_qt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
+        n_act = classify_tiles<kBwdWaves>(A.myseg, sqp, S, n_qt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
                              lane);
 
     auto tile_of = [&](int n, bool& partial) -> int {
@@ -702,7 +637,7 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_kt : 0) + 15) & ~15));
     int n_act = n_kt;
     if (SEG)
-        n_act = active_tiles(myseg, skp, S, n_kt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
+        n_act = classify_tiles<kBwdWaves>(myseg, skp, S, n_kt, reinterpret_cast<uint8_t*>(smem), list, meta, wave,
                              lane);
 
     auto tile_of = [&](int n, bool& partial) -> int {

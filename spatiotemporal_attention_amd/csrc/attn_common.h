@@ -157,6 +157,86 @@ __device__ __forceinline__ int wave_max(int x) {
     return x;
 }
 
+// Classifies every 64-row tile of the opposite side (segment IDs `other`, S
+// entries) against this workgroup's rows (ID `mine` per lane; 0 for padding
+// and rows past S) as skip (no valid pair), full (every pair valid: one
+// nonzero ID on both sides, no padding, no rows past S) or partial, and
+// compacts the active tiles, in order, into `list` (bit 15 set: partial).
+// `cls` is scratch of n_tiles bytes, `meta` of 3 NW + 1 ints; every wave of
+// the workgroup (NW of them) must call it.  Returns the number of active
+// tiles.  Each wave loads kUnroll tiles' IDs before reducing any of them, so
+// the loads' latency overlaps instead of adding up tile by tile.
+template <int NW>
+__device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
+                              uint16_t* list, int* meta, int wave, int lane) {
+    constexpr int kUnroll = 4;
+    {
+        int mn = (mine != 0) ? mine : INT32_MAX;
+        int mx = (mine != 0) ? mine : INT32_MIN;
+        int fl = (mine == 0) ? 1 : 0;
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        fl = wave_max(fl);
+        if (lane == 0) {
+            meta[wave] = mn;
+            meta[NW + wave] = mx;
+            meta[2 * NW + wave] = fl;
+        }
+    }
+    __syncthreads();
+    int omn = INT32_MAX, omx = INT32_MIN, ofl = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        omn = min(omn, meta[i]);
+        omx = max(omx, meta[NW + i]);
+        ofl |= meta[2 * NW + i];
+    }
+    for (int t0 = wave; t0 < n_tiles; t0 += NW * kUnroll) {
+        int id[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int t = t0 + u * NW;
+            const int r = t * 64 + lane;
+            id[u] = (t < n_tiles && r < S) ? other[r] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int t = t0 + u * NW;
+            int mn = (id[u] != 0) ? id[u] : INT32_MAX;
+            int mx = (id[u] != 0) ? id[u] : INT32_MIN;
+            int fl = (id[u] == 0) ? 1 : 0;
+            mn = wave_min(mn);
+            mx = wave_max(mx);
+            fl = wave_max(fl);
+            if (lane == 0 && t < n_tiles) {
+                uint8_t c;
+                if (omn > omx || mn > mx || max(omn, mn) > min(omx, mx))
+                    c = 0;
+                else if (!ofl && !fl && omn == omx && mn == mx && omn == mn)
+                    c = 1;
+                else
+                    c = 2;
+                cls[t] = c;
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int base = 0;
+        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+            const int t = t0 + lane;
+            const int c = (t < n_tiles) ? cls[t] : 0;
+            const uint64_t m = __ballot(c != 0);
+            const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+            if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
+            base += __popcll(m);
+        }
+        if (lane == 0) meta[3 * NW] = base;
+    }
+    __syncthreads();
+    return meta[3 * NW];
+}
+
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

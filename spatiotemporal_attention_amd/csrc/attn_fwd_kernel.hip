@@ -275,14 +275,18 @@ struct Attn {
         const int t = tile_of(n, partial);
         const int lim = S - t * kBk - 8 * g;
         const int* segt = sslot(n) + 8 * g;
+        const bool live = myseg != 0;
+        // The segment IDs of every key of the slot are read unconditionally
+        // (the slot always holds 64; past S they repeat key S-1) and combined
+        // with bitwise ands, so the masks compile to selects, not branches.
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int jc = b * 32 + 16 * (r >> 3) + (r & 7);
                 bool ok = jc < lim;
-                if (SEG) ok = ok && (segt[jc] == myseg) && (myseg != 0);
-                if (!ok) sacc[b][r] = -INFINITY;
+                if (SEG) ok = ok & (segt[jc] == myseg) & live;
+                sacc[b][r] = ok ? sacc[b][r] : -INFINITY;
             }
         }
     }
@@ -459,72 +463,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 
     uint16_t* list = reinterpret_cast<uint16_t*>(smem + T::kRingBytes);
     int* meta = reinterpret_cast<int*>(smem + ((T::kRingBytes + 2 * (SEG ? n_kvt : 0) + 15) & ~15));
-    // meta: [0..7] per-wave q min, [8..15] q max, [16..23] q flags, [24] n_active
+    // meta: classify_tiles' scratch (3 kWaves + 1 ints)
     A.list = list;
 
     int n_act = n_kvt;
     if (SEG) {
-        // ---- query-block segment summary --------------------------------------
-        {
-            const int s = A.myseg;
-            int mn = (s != 0) ? s : INT32_MAX;
-            int mx = (s != 0) ? s : INT32_MIN;
-            int fl = (s == 0) ? 1 : 0;  // pad or out-of-range row present
-            mn = wave_min(mn);
-            mx = wave_max(mx);
-            fl = wave_max(fl);
-            if (lane == 0) {
-                meta[wave] = mn;
-                meta[8 + wave] = mx;
-                meta[16 + wave] = fl;
-            }
-        }
-        __syncthreads();
-        int qmn = INT32_MAX, qmx = INT32_MIN, qfl = 0;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            qmn = min(qmn, meta[i]);
-            qmx = max(qmx, meta[8 + i]);
-            qfl |= meta[16 + i];
-        }
-        // ---- classify every key tile: 0 skip, 1 full, 2 partial ---------------
-        uint8_t* cls = reinterpret_cast<uint8_t*>(smem);  // aliases the rings
-        for (int t = wave; t < n_kvt; t += kWaves) {
-            const int key = t * kBk + lane;
-            const int id = (key < S) ? A.segkv[key] : 0;
-            int mn = (id != 0) ? id : INT32_MAX;
-            int mx = (id != 0) ? id : INT32_MIN;
-            int fl = (id == 0) ? 1 : 0;
-            mn = wave_min(mn);
-            mx = wave_max(mx);
-            fl = wave_max(fl);
-            if (lane == 0) {
-                uint8_t c;
-                if (qmn > qmx || mn > mx || max(qmn, mn) > min(qmx, mx))
-                    c = 0;
-                else if (!qfl && !fl && qmn == qmx && mn == mx && qmn == mn)
-                    c = 1;
-                else
-                    c = 2;
-                cls[t] = c;
-            }
-        }
-        __syncthreads();
-        // ---- compact active tiles into the list (wave 0, ballot prefix) -------
-        if (wave == 0) {
-            int base = 0;
-            for (int t0 = 0; t0 < n_kvt; t0 += 64) {
-                const int t = t0 + lane;
-                const int c = (t < n_kvt) ? cls[t] : 0;
-                const uint64_t m = __ballot(c != 0);
-                const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-                if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
-                base += __popcll(m);
-            }
-            if (lane == 0) meta[24] = base;
-        }
-        __syncthreads();
-        n_act = meta[24];
+        // ---- classify the key tiles against this query block (skip / full /
+        // partial) and compact the active ones into the LDS list ----------------
+        n_act = classify_tiles<kWaves>(A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem),
+                                       list, meta, wave, lane);
     }
 
     // ---- running softmax state and the O^T accumulators -----------------------

@@ -209,29 +209,25 @@ def test_dit720p_sampled_dq_rows(need_gpu):
     print(_dq_rows_check(x, dout, None, w.scale, dq, heads=(0, 17, 39), n_rows=24, seed=1))
 
 
-def _closed_form_uniform(x, dout, scale, which):
+def _closed_form_head(x, dout, scale, which, h):
     """q = 0 (which='q') or k = 0 (which='k'): P uniform over all S keys.
-    q = 0: dk = 0, dq_i = scale * M^T-free form scale * dout_i @ M^T with
-    M = sum_j k_j (v_j - vbar)^T / S.  k = 0: dq = 0, dk_j = scale * N (v_j -
-    vbar) with N = sum_i q_i dout_i^T / S.  Both: dv_j = mean_i dout_i."""
-    B, S, H, D = x["q"].shape
-    dq_o = np.zeros((B, S, H, D))
-    dk_o = np.zeros((B, S, H, D))
-    dv_o = np.zeros((B, S, H, D))
-    for h in range(H):
-        q = x["q"][0, :, h].double().numpy()
+    Returns the fp64 closed form of the non-zero gradient of head h (dq for
+    q = 0, dk for k = 0; the other of dq, dk is exactly 0) and dv (every key:
+    the mean of dout over the queries).
+      q = 0: dq_i = scale * M dout_i with M = sum_j k_j (v_j - vbar)^T / S
+      k = 0: dk_j = scale * N (v_j - vbar) with N = sum_i q_i dout_i^T / S"""
+    S = x["q"].shape[1]
+    v = x["v"][0, :, h].double().numpy()
+    do = dout[0, :, h].double().numpy()
+    vc = v - v.mean(0)
+    if which == "q":
         k = x["k"][0, :, h].double().numpy()
-        v = x["v"][0, :, h].double().numpy()
-        do = dout[0, :, h].double().numpy()
-        vc = v - v.mean(0)
-        if which == "q":
-            M = k.T @ vc / S
-            dq_o[0, :, h] = scale * do @ M.T
-        else:
-            N = q.T @ do / S
-            dk_o[0, :, h] = scale * vc @ N.T
-        dv_o[0, :, h] = do.mean(0)[None, :]
-    return dq_o, dk_o, dv_o
+        g = scale * do @ (k.T @ vc / S).T
+    else:
+        q = x["q"][0, :, h].double().numpy()
+        g = scale * vc @ (q.T @ do / S).T
+    dv = np.broadcast_to(do.mean(0), do.shape)
+    return g, dv
 
 
 @pytest.mark.parametrize("which", ["q", "k"])
@@ -241,14 +237,16 @@ def test_dit720p_uniform_closed_forms_every_row(need_gpu, which):
     x[which] = torch.zeros_like(x[which])
     dout = W.randn_bf16((w.B, w.S, w.H, w.D), 4004)
     print(f"case {w.name}: bwd {which}=0 closed form", flush=True)
-    g = run_gpu_bwd(x, dout, None, None, w.scale)
-    o = _closed_form_uniform(x, dout, float(np.float32(w.scale)), which)
-    zero_name = "dk" if which == "q" else "dq"
-    for n, gi, oi in zip(("dq", "dk", "dv"), g, o):
-        if n == zero_name:
-            assert torch.count_nonzero(gi.float()) == 0, f"{n} must be exactly 0 when {which} = 0"
-        else:
-            print(check_grad(n, gi, oi))
+    dq, dk, dv = run_gpu_bwd(x, dout, None, None, w.scale)
+    nonzero, zero = (dq, dk) if which == "q" else (dk, dq)
+    assert torch.count_nonzero(zero.float()) == 0, f"{'dk' if which == 'q' else 'dq'} must be exactly 0"
+    scale = float(np.float32(w.scale))
+    for h in range(w.H):
+        g, gv = _closed_form_head(x, dout, scale, which, h)
+        check_grad("dq" if which == "q" else "dk", nonzero[0, :, h], g)
+        check_grad("dv", dv[0, :, h], gv)
+        if h % 8 == 7:
+            print(f"  heads 0..{h} ok", flush=True)
 
 
 def test_packed_clips_whole_clip_and_sampled_rows(need_gpu):
