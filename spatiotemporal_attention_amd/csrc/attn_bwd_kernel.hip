@@ -677,16 +677,29 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         }
     };
 
+    // dQ^T accumulators in AGPRs; the Q and dO slices move there too (B
+    // operands of the inline-asm MFMAs, see mfma32_vacc / mfma32_acc).
     f32x16 dqacc[T::kDBlocks];
 #pragma unroll
     for (int i = 0; i < T::kDBlocks; ++i) dqacc[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < T::kDBlocks; ++i) asm volatile("" : "+a"(dqacc[i]));
 
     if (n_act > 0) copy(0);
     wait_vm(0);
     barrier();
     asm volatile("" ::"v"(qreg[0]), "v"(qreg[T::kSteps - 1]), "v"(doreg[0]), "v"(doreg[T::kSteps - 1]),
                  "v"(myseg), "v"(lse2), "v"(delta));
+#pragma unroll
+    for (int ks = 0; ks < T::kSteps; ++ks) asm volatile("" : "+a"(qreg[ks]), "+a"(doreg[ks]));
+    asm volatile("s_nop 3" ::: "memory");
+    const bool live = myseg != 0;
 
+    // Operands are fetched kPf MFMAs ahead through a ring two entries longer.
+    constexpr int kRing = kPf + 2;
+    constexpr int kNA = 4 * T::kSteps;    // S^T and dP^T MFMAs per 64-key tile
+    constexpr int kNB = 4 * T::kDBlocks;  // dQ^T MFMAs per tile
+    bf16x8 ring[kRing];
     for (int n = 0; n < n_act; ++n) {
         const bool more = n + 1 < n_act;
         if (more) copy(n + 1);
@@ -695,26 +708,36 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         const uint32_t st = lds_addr(smem) + (n % kSlots) * T::kStage;
         const uint32_t tk = st + T::kA, tv = st + T::kB;
 
-        // S^T = K Q^T and dP^T = V dO^T over 64 keys (two 32-row blocks).
+        // S^T = K Q^T and dP^T = V dO^T over 64 keys: MFMA i takes k-step
+        // i / 4, 32-key block (i / 2) % 2, S^T (even i) or dP^T (odd i).
         f32x16 sacc[2], pacc[2];
-        static_for<0, T::kSteps>([&](auto kc) {
-            constexpr int ks = kc;
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const bf16x8 ak = row_operand<D>(tk, L.rx, ks, bb);
-                const bf16x8 av = row_operand<D>(tv, L.rx, ks, bb);
-                if constexpr (ks == 0) {
-                    sacc[bb] = mfma32(ak, qreg[0], f32x16{});
-                    pacc[bb] = mfma32(av, doreg[0], f32x16{});
-                } else {
-                    sacc[bb] = mfma32(ak, qreg[ks], sacc[bb]);
-                    pacc[bb] = mfma32(av, doreg[ks], pacc[bb]);
-                }
-            }
-        });
+        {
+            auto op = [&](auto ic) -> bf16x8 {
+                constexpr int i = ic;
+                return row_operand<D>((i & 1) ? tv : tk, L.rx, i / 4, (i / 2) % 2);
+            };
+            static_for<0, kPf>([&](auto ic) { ring[ic] = op(ic); });
+            static_for<0, kNA>([&](auto ic) {
+                constexpr int i = ic, ks = i / 4, bb = (i / 2) % 2;
+                if constexpr (i + kPf < kNA) ring[(i + kPf) % kRing] = op(std::integral_constant<int, i + kPf>{});
+                const bf16x8& a = ring[i % kRing];
+                if constexpr (i & 1)
+                    mfma32_vacc<(ks == 0), (i < 2)>(pacc[bb], a, doreg[ks]);
+                else
+                    mfma32_vacc<(ks == 0), (i < 2)>(sacc[bb], a, qreg[ks]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // The wait states between the last MFMA write of S^T / dP^T and
+            // their first VALU read, tied to the registers so that no read is
+            // scheduled above them.
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                         : "+v"(sacc[0]), "+v"(sacc[1]), "+v"(pacc[0]), "+v"(pacc[1]));
+        }
 
         // dS^T = P^T (dP^T - delta); register r of block bb holds key
-        // t*64 + bb*32 + 16(r >> 3) + 8g + (r & 7).
+        // t*64 + bb*32 + 16(r >> 3) + 8g + (r & 7).  Masks (keys past S, and
+        // with segment IDs every key whose ID differs) are selects, applied
+        // to every tile: the slot always holds 64 IDs.
         bf16x8 dsb[4];
         const int lim = S - t * 64 - 8 * g;
         const int* sgs = reinterpret_cast<const int*>(lds_ptr(st + T::kSeg)) + 8 * g;
@@ -724,28 +747,36 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
             for (int r = 0; r < 16; ++r) {
                 const int jc = bb * 32 + 16 * (r >> 3) + (r & 7);
                 float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c_log2, -lse2));
-                if (partial) {
-                    bool ok = jc < lim;
-                    if (SEG) ok = ok && (sgs[jc] == myseg) && (myseg != 0);
-                    p = ok ? p : 0.f;
-                }
+                bool ok = jc < lim;
+                if (SEG) ok = ok & (sgs[jc] == myseg) & live;
+                p = ok ? p : 0.f;
                 dsb[2 * bb + (r >> 3)][r & 7] = (__bf16)(p * (pacc[bb][r] - delta));
             }
         }
+        (void)partial;
 
-        // dQ^T += K^T dS^T (k = keys, 16 per step).
-        static_for<0, 4>([&](auto kc) {
-            constexpr int kst = kc;
-#pragma unroll
-            for (int db = 0; db < T::kDBlocks; ++db)
-                dqacc[db] = mfma32(tr_operand<D>(tk, L.tx0, L.tx1, kst, db), dsb[kst], dqacc[db]);
-        });
+        // dQ^T += K^T dS^T: MFMA i takes key k-step i / kDBlocks, d-block
+        // i % kDBlocks.
+        {
+            auto op = [&](auto ic) -> bf16x8 {
+                constexpr int i = ic;
+                return tr_operand<D>(tk, L.tx0, L.tx1, i / T::kDBlocks, i % T::kDBlocks);
+            };
+            static_for<0, kPf>([&](auto ic) { ring[ic] = op(ic); });
+            static_for<0, kNB>([&](auto ic) {
+                constexpr int i = ic;
+                if constexpr (i + kPf < kNB) ring[(i + kPf) % kRing] = op(std::integral_constant<int, i + kPf>{});
+                mfma32_acc<(i < 2)>(dqacc[i % T::kDBlocks], ring[i % kRing], dsb[i / T::kDBlocks]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
 
         // The copy of tile n+1 must have landed in every wave before the
         // barrier that opens iteration n+1.
         wait_vm(0);
         barrier();
     }
+    accumulator_fence();
 
     // ---- epilogue: dq = scale dQ^T (bf16) ------------------------------------------
     if (qi < S) {
