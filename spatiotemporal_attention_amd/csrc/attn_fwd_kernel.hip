@@ -47,6 +47,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "attn_common.h"
 #include "attn_fwd_launch.h"
 
@@ -386,17 +389,20 @@ __device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
     if (G == 0) barrier();  // group 0 idles in the last global phase
 }
 
+// One query block (256 queries of one (b, h)): work item w of the grid.
 template <int D, bool SEG>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
-    __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
-    int n_kvt, int n_wg) {
+__device__ __forceinline__ void attn_fwd_item(
+    char* smem, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const int32_t* __restrict__ seg_q,
+    const int32_t* __restrict__ seg_kv, __bf16* __restrict__ out, float* __restrict__ lse, int S,
+    int H, float c_log2, int n_qblk, int n_kvt, int n_wg, int w) {
     using T = Tile<D>;
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-    // ---- tile scheduler: XCD-contiguous renumbering of workgroup ids --------
-    const int w = blockIdx.x;
+    // ---- tile scheduler: XCD-contiguous renumbering of work items -----------
+    // Item w runs on XCD w % 8 (workgroups are dealt to the XCDs round-robin
+    // and the persistent grid below is a multiple of 8), and the items of one
+    // XCD are consecutive query blocks of one head, which share K/V tiles in
+    // that XCD's L2.
     const int per = n_wg / kXcds, rem = n_wg % kXcds;
     const int xcd = w % kXcds;
     const int lid = xcd * per + min(xcd, rem) + w / kXcds;
@@ -550,6 +556,49 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     }
 }
 
+// Workgroup p takes items p, p + G, p + 2G, ... (G = the grid size: one per
+// item with segment IDs, else a persistent grid, a multiple of 8).  At every step the G/8 workgroups of an XCD
+// then work on consecutive query blocks of one head, streaming the same K/V
+// tiles at the same time, which keeps them in that XCD's L2; with one
+// workgroup per item, CUs that pick up new items at different times drift
+// apart and each re-fetches the tiles.  Every workgroup's item count is fixed
+// by G and n_wg, so all waves exit.
+template <int D, bool SEG>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
+    __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
+    int n_kvt, int n_wg) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
+        attn_fwd_item<D, SEG>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_qblk, n_kvt,
+                              n_wg, w);
+        // Every wave is done with the LDS of this item before the next one's
+        // copies land there.
+        __syncthreads();
+    }
+}
+
+// Workgroups of the persistent grid: one per CU (the kernel's LDS and
+// registers allow one), rounded down to a multiple of the XCD count; cached
+// per device.
+int64_t persistent_workgroups() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < kMaxDev) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < kXcds)
+        cus = 256;
+    const int g = cus / kXcds * kXcds;
+    if (dev < kMaxDev) cache[dev].store(g, std::memory_order_relaxed);
+    return g;
+}
+
 template <int D, bool SEG>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     using T = Tile<D>;
@@ -562,7 +611,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     lds = (lds + 15) & ~(size_t)15;
     lds += 32 * sizeof(int);  // meta
     const float c_log2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, SEG>), dim3(n_wg), dim3(kThreads), lds, stream,
+    // Unmasked, every item has the same work and the persistent grid keeps
+    // the CUs of an XCD in step; with segment IDs items differ (up to 8x on
+    // packed clips) and one workgroup per item lets the dispatcher balance them.
+    const int grid = SEG ? n_wg : (int)std::min<int64_t>(n_wg64, persistent_workgroups());
+    hipLaunchKernelGGL((attn_fwd_kernel<D, SEG>), dim3(grid), dim3(kThreads), lds, stream,
                        reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                        reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
                        reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, c_log2, n_qblk, n_kvt,
