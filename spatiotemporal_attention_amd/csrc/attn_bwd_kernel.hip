@@ -283,6 +283,10 @@ struct DkDv {
     bf16x8 ring[kRing];
     float2 lpair[kPairAhead], dpair[kPairAhead];
     int2 spair[kPairAhead];
+    // Lane offsets of the operand reads within a stage: row reads of k-step
+    // ks at rxk[ks], the two halves of the transposed reads of d-block db at
+    // txk0[db] / txk1[db].
+    uint32_t rxk[T::kSteps], txk0[T::kDBlocks], txk1[T::kDBlocks];
 
     __device__ __forceinline__ static uint32_t slot(int t) {
         int o = (t % kSlots) * T::kStage;
@@ -290,34 +294,80 @@ struct DkDv {
         return (uint32_t)o;
     }
 
+    // Per-lane LDS addresses of one ring stage, formed once per tile: every
+    // operand read then adds only its region and row offset, as the read's
+    // immediate offset.  The sums are pinned in VGPRs; left alone, the
+    // compiler keeps the stage address in an SGPR and spends a VALU add on
+    // every read.
+    struct RowBases {
+        uint32_t r[T::kSteps];
+    };
+    struct TrBases {
+        uint32_t t0[T::kDBlocks], t1[T::kDBlocks];
+    };
+    __device__ __forceinline__ void init_bases() {
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) rxk[ks] = (uint32_t)(L.rx ^ (ks << 5));
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+            txk0[db] = (uint32_t)(L.tx0 ^ (db << 6));
+            txk1[db] = (uint32_t)(L.tx1 ^ (db << 6));
+        }
+    }
+    __device__ __forceinline__ RowBases rows(uint32_t st) const {
+        RowBases b;
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) {
+            b.r[ks] = st + rxk[ks];
+            asm volatile("" : "+v"(b.r[ks]));
+        }
+        return b;
+    }
+    __device__ __forceinline__ TrBases trs(uint32_t st) const {
+        TrBases b;
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+            b.t0[db] = st + txk0[db];
+            b.t1[db] = st + txk1[db];
+            asm volatile("" : "+v"(b.t0[db]), "+v"(b.t1[db]));
+        }
+        return b;
+    }
+    // Address of this lane's first softmax pair rows in a stage (pair j of
+    // half h is 4 (32h + 16(j/4) + 2(j%4)) bytes further).
+    __device__ __forceinline__ uint32_t pair_base(uint32_t st) const {
+        uint32_t b = st + 32u * (uint32_t)g;
+        asm volatile("" : "+v"(b));
+        return b;
+    }
+
     // MFMA i of the S/dP step of a sub-tile (rows 32*h .. of the tile at st):
     // k-step i / 2, S (even i, Q rows) or dP (odd i, dO rows).
     template <int I>
-    __device__ __forceinline__ bf16x8 op_a(uint32_t st, int h) const {
-        return row_operand<D>(st + ((I & 1) ? T::kB : T::kA), L.rx, I / 2, h);
+    __device__ __forceinline__ bf16x8 op_a(const RowBases& rb, int h) const {
+        return *reinterpret_cast<const bf16x8*>(
+            lds_ptr(rb.r[I / 2] + ((I & 1) ? T::kB : T::kA) + h * 32 * T::kRowBytes));
     }
     // MFMA i of the dV/dK step of a sub-tile: query k-step 2h + i / (2
     // kDBlocks), d-block (i / 2) % kDBlocks, dV (even i, dO) or dK (odd, Q).
     template <int I>
-    __device__ __forceinline__ bf16x8 op_b(uint32_t st, int h) const {
-        return tr_operand<D>(st + ((I & 1) ? T::kA : T::kB), L.tx0, L.tx1,
-                             2 * h + I / (2 * T::kDBlocks), (I / 2) % T::kDBlocks);
+    __device__ __forceinline__ bf16x8 op_b(const TrBases& tb, int h) const {
+        constexpr int db = (I / 2) % T::kDBlocks;
+        const uint32_t o = ((I & 1) ? T::kA : T::kB) + (2 * h + I / (2 * T::kDBlocks)) * 16 * T::kRowBytes;
+        return tr_read8(lds_ptr(tb.t0[db] + o), lds_ptr(tb.t1[db] + o));
     }
 
     // Softmax pair j of a sub-tile: accumulator registers r = 2j and 2j+1,
     // queries row(j), row(j)+1 of the tile (sub-tile h covers rows 32h..).
-    __device__ __forceinline__ int pair_row(int h, int j) const {
-        return 32 * h + 16 * (j / 4) + 8 * g + 2 * (j % 4);
-    }
-    __device__ __forceinline__ void load_pair(uint32_t st, int h, int j, bool partial) {
-        const int row = pair_row(h, j);
-        lpair[j % kPairAhead] = *reinterpret_cast<const float2*>(lds_ptr(st + T::kVec0 + 4 * row));
-        dpair[j % kPairAhead] = *reinterpret_cast<const float2*>(lds_ptr(st + T::kVec1 + 4 * row));
+    // pb: pair_base() of the stage.
+    __device__ __forceinline__ void load_pair(uint32_t pb, int h, int j, bool partial) {
+        const uint32_t o = 4 * (32 * h + 16 * (j / 4) + 2 * (j % 4));
+        lpair[j % kPairAhead] = *reinterpret_cast<const float2*>(lds_ptr(pb + T::kVec0 + o));
+        dpair[j % kPairAhead] = *reinterpret_cast<const float2*>(lds_ptr(pb + T::kVec1 + o));
         // With segment IDs the mask is applied to every tile, full ones
         // included (they pass it unchanged): a branch on the tile kind here
         // would split the register assignment of the pipelined loop.
-        if (SEG)
-            spair[j % kPairAhead] = *reinterpret_cast<const int2*>(lds_ptr(st + T::kSeg + 4 * row));
+        if (SEG) spair[j % kPairAhead] = *reinterpret_cast<const int2*>(lds_ptr(pb + T::kSeg + o));
         (void)partial;
     }
     // P = 2^(s c - lse2), dS = P (dP - delta) for pair J of the sub-tile in
@@ -344,24 +394,24 @@ struct DkDv {
         asm volatile("" : "+v"(pb[B][k]), "+v"(dsb[B][k]));
     }
 
-    __device__ __forceinline__ void prefetch_a(uint32_t st, int h) {
-        static_for<0, kPf>([&](auto ic) { ring[ic] = op_a<ic>(st, h); });
+    __device__ __forceinline__ void prefetch_a(const RowBases& ra, int h) {
+        static_for<0, kPf>([&](auto ic) { ring[ic] = op_a<ic>(ra, h); });
     }
-    __device__ __forceinline__ void prefetch_pairs(uint32_t sv, int h, bool partial) {
-        static_for<0, kPairAhead>([&](auto jc) { load_pair(sv, h, jc, partial); });
+    __device__ __forceinline__ void prefetch_pairs(uint32_t pv, int h, bool partial) {
+        static_for<0, kPairAhead>([&](auto jc) { load_pair(pv, h, jc, partial); });
     }
 
-    // Step 1: dV / dK of the sub-tile (tile at st, half h) whose P / dS are
-    // in buffer B (operands prefetched).  NEXT_A: the last steps fetch the
-    // first operands of the S/dP step of sub-tile (sa, ha).
+    // Step 1: dV / dK of the sub-tile (stage bases tb, half h) whose P / dS
+    // are in buffer B (operands prefetched).  NEXT_A: the last steps fetch the
+    // first operands of the S/dP step of sub-tile (ra, ha).
     template <int B, bool NEXT_A>
-    __device__ __forceinline__ void step_b(uint32_t st, int h, uint32_t sa, int ha) {
+    __device__ __forceinline__ void step_b(const TrBases& tb, int h, const RowBases& ra, int ha) {
         static_for<0, kNB>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i + kPf < kNB)
-                ring[(i + kPf) % kRing] = op_b<i + kPf>(st, h);
+                ring[(i + kPf) % kRing] = op_b<i + kPf>(tb, h);
             else if constexpr (NEXT_A)
-                ring[(i + kPf) % kRing] = op_a<i + kPf - kNB>(sa, ha);
+                ring[(i + kPf) % kRing] = op_a<i + kPf - kNB>(ra, ha);
             const bf16x8& a = ring[i % kRing];
             constexpr int kst = i / (2 * T::kDBlocks), db = (i / 2) % T::kDBlocks;
             if constexpr (i & 1)
@@ -371,18 +421,19 @@ struct DkDv {
             __builtin_amdgcn_sched_barrier(0);
         });
     }
-    // Step 2: S / dP of sub-tile (sa, ha) into buffer B ^ 1 (if A) with the
-    // softmax of buffer B (sub-tile (sv, hv)) interleaved; the last steps
-    // fetch the first dV/dK operands of sub-tile (sv, hv).
+    // Step 2: S / dP of sub-tile (ra, ha) into buffer B ^ 1 (if A) with the
+    // softmax of buffer B (sub-tile (tv / pv, hv)) interleaved; the last steps
+    // fetch the first dV/dK operands of sub-tile (tv, hv).
     template <int B, bool A>
-    __device__ __forceinline__ void step_a(uint32_t sa, int ha, uint32_t sv, int hv, bool partial) {
+    __device__ __forceinline__ void step_a(const RowBases& ra, int ha, const TrBases& tv, uint32_t pv,
+                                           int hv, bool partial) {
         if constexpr (A) {
             static_for<0, kNA>([&](auto ic) {
                 constexpr int i = ic;
                 if constexpr (i + kPf < kNA)
-                    ring[(i + kPf) % kRing] = op_a<i + kPf>(sa, ha);
+                    ring[(i + kPf) % kRing] = op_a<i + kPf>(ra, ha);
                 else
-                    ring[(i + kPf) % kRing] = op_b<i + kPf - kNA>(sv, hv);
+                    ring[(i + kPf) % kRing] = op_b<i + kPf - kNA>(tv, hv);
                 const bf16x8& a = ring[i % kRing];
                 constexpr int ks = i / 2;
                 if constexpr (i & 1)
@@ -391,7 +442,7 @@ struct DkDv {
                     mfma32_vacc<(ks == 0), false>(sc[B ^ 1], a, kreg[ks]);
                 if constexpr (i < kPairs) {
                     pair<B, i>(partial);
-                    if constexpr (i + kPairAhead < kPairs) load_pair(sv, hv, i + kPairAhead, partial);
+                    if constexpr (i + kPairAhead < kPairs) load_pair(pv, hv, i + kPairAhead, partial);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -399,16 +450,16 @@ struct DkDv {
             static_for<0, kPairs>([&](auto jc) {
                 constexpr int j = jc;
                 pair<B, j>(partial);
-                if constexpr (j + kPairAhead < kPairs) load_pair(sv, hv, j + kPairAhead, partial);
+                if constexpr (j + kPairAhead < kPairs) load_pair(pv, hv, j + kPairAhead, partial);
             });
-            static_for<0, kPf>([&](auto ic) { ring[ic] = op_b<ic>(sv, hv); });
+            static_for<0, kPf>([&](auto ic) { ring[ic] = op_b<ic>(tv, hv); });
         }
     }
     // S / dP of the first sub-tile alone, into buffer 0.
-    __device__ __forceinline__ void step_a_only(uint32_t sa) {
+    __device__ __forceinline__ void step_a_only(const RowBases& ra) {
         static_for<0, kNA>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i + kPf < kNA) ring[(i + kPf) % kRing] = op_a<i + kPf>(sa, 0);
+            if constexpr (i + kPf < kNA) ring[(i + kPf) % kRing] = op_a<i + kPf>(ra, 0);
             const bf16x8& a = ring[i % kRing];
             constexpr int ks = i / 2;
             if constexpr (i & 1)
@@ -462,6 +513,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     }
     A.myseg = SEG ? ((kj < S) ? seg_kv[(int64_t)b * S + kj] : 0) : 1;
     A.L.init(wave, lane, ts);
+    A.init_bases();
 
     uint16_t* list = reinterpret_cast<uint16_t*>(smem + kSlots * T::kStage);
     int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_qt : 0) + 15) & ~15));
@@ -543,10 +595,16 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         // is never used.
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) A.pb[1][kk] = A.dsb[1][kk] = bf16x8{};
-        A.prefetch_a(sm + K::slot(0), 0);
-        A.step_a_only(sm + K::slot(0));
+        {
+            const typename K::RowBases r0 = A.rows(sm + K::slot(0));
+            A.prefetch_a(r0, 0);
+            A.step_a_only(r0);
+        }
         accumulator_fence();
-        static_for<0, kPf>([&](auto ic) { A.ring[ic] = A.template op_b<ic>(sm + K::slot(0), 1); });
+        {
+            const typename K::TrBases t0 = A.trs(sm + K::slot(0));
+            static_for<0, kPf>([&](auto ic) { A.ring[ic] = A.template op_b<ic>(t0, 1); });
+        }
         for (int t = 0; t < n_act; ++t) {
             const bool more = t + 2 < n_act;
             if (more) copy(t + 2);
@@ -556,17 +614,23 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             const uint32_t s0 = sm + K::slot(t);
             const uint32_t sp = (t > 0) ? sm + K::slot(t - 1) : s0;
             const uint32_t sn = (t + 1 < n_act) ? sm + K::slot(t + 1) : s0;
-            A.template step_b<1, true>(sp, 1, s0, 1);
-            A.prefetch_pairs(s0, 0, part);
-            A.template step_a<0, true>(s0, 1, s0, 0, part);
-            A.template step_b<0, true>(s0, 0, sn, 0);
-            A.prefetch_pairs(s0, 1, part);
-            A.template step_a<1, true>(sn, 0, s0, 1, part);
+            const typename K::TrBases tp = A.trs(sp), tc = A.trs(s0);
+            const typename K::RowBases rc = A.rows(s0), rn = A.rows(sn);
+            const uint32_t pc = A.pair_base(s0);
+            A.template step_b<1, true>(tp, 1, rc, 1);
+            A.prefetch_pairs(pc, 0, part);
+            A.template step_a<0, true>(rc, 1, tc, pc, 0, part);
+            A.template step_b<0, true>(tc, 0, rn, 0);
+            A.prefetch_pairs(pc, 1, part);
+            A.template step_a<1, true>(rn, 0, tc, pc, 1, part);
             if (more) wait_vm(0);
             barrier();
         }
         // dV/dK of the last sub-tile (tile n_act - 1, half 1).
-        A.template step_b<1, false>(sm + K::slot(n_act - 1), 1, 0, 0);
+        {
+            const typename K::TrBases tl = A.trs(sm + K::slot(n_act - 1));
+            A.template step_b<1, false>(tl, 1, typename K::RowBases{}, 0);
+        }
     }
 
     // ---- epilogue: dk = scale dK^T, dv = dV^T (bf16) ----------------------------
