@@ -146,17 +146,6 @@ struct Lanes {
     }
 };
 
-template <int D>
-__device__ __forceinline__ bf16x8 row_operand(uint32_t tile, int rx, int ks, int blk) {
-    return *reinterpret_cast<const bf16x8*>(
-        lds_ptr((tile + (uint32_t)(rx ^ (ks << 5))) + blk * 32 * BTile<D>::kRowBytes));
-}
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(uint32_t tile, int tx0, int tx1, int kst, int db) {
-    const uint32_t o = tile + kst * 16 * BTile<D>::kRowBytes;
-    return tr_read8(lds_ptr(o + (uint32_t)(tx0 ^ (db << 6))), lds_ptr(o + (uint32_t)(tx1 ^ (db << 6))));
-}
-
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -696,6 +685,16 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 
     Lanes<D> L;
     L.init(wave, lane, ts);
+    // Lane offsets of the operand reads within a stage (row reads per k-step,
+    // the two halves of the transposed reads per d-block).
+    uint32_t rxk[T::kSteps], txk0[T::kDBlocks], txk1[T::kDBlocks];
+#pragma unroll
+    for (int ks = 0; ks < T::kSteps; ++ks) rxk[ks] = (uint32_t)(L.rx ^ (ks << 5));
+#pragma unroll
+    for (int db = 0; db < T::kDBlocks; ++db) {
+        txk0[db] = (uint32_t)(L.tx0 ^ (db << 6));
+        txk1[db] = (uint32_t)(L.tx1 ^ (db << 6));
+    }
 
     uint16_t* list = reinterpret_cast<uint16_t*>(smem + kSlots * T::kStage);
     int* meta = reinterpret_cast<int*>(smem + ((kSlots * T::kStage + 2 * (SEG ? n_kt : 0) + 15) & ~15));
@@ -770,7 +769,16 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         bool partial;
         const int t = tile_of(n, partial);
         const uint32_t st = lds_addr(smem) + (n % kSlots) * T::kStage;
-        const uint32_t tk = st + T::kA, tv = st + T::kB;
+        // Per-lane addresses of this stage, formed once per tile and pinned in
+        // VGPRs, so that each operand read adds its region and row offset as
+        // the instruction's immediate (left alone, the compiler keeps the
+        // stage address in an SGPR and spends a VALU add on every read).
+        uint32_t rb[T::kSteps], tb0[T::kDBlocks], tb1[T::kDBlocks];
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) {
+            rb[ks] = st + rxk[ks];
+            asm volatile("" : "+v"(rb[ks]));
+        }
 
         // S^T = K Q^T and dP^T = V dO^T over 64 keys: MFMA i takes k-step
         // i / 4, 32-key block (i / 2) % 2, S^T (even i) or dP^T (odd i).
@@ -778,7 +786,8 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         {
             auto op = [&](auto ic) -> bf16x8 {
                 constexpr int i = ic;
-                return row_operand<D>((i & 1) ? tv : tk, L.rx, i / 4, (i / 2) % 2);
+                return *reinterpret_cast<const bf16x8*>(
+                    lds_ptr(rb[i / 4] + ((i & 1) ? T::kB : T::kA) + ((i / 2) % 2) * 32 * T::kRowBytes));
             };
             static_for<0, kPf>([&](auto ic) { ring[ic] = op(ic); });
             static_for<0, kNA>([&](auto ic) {
@@ -799,32 +808,49 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
         }
 
         // dS^T = P^T (dP^T - delta); register r of block bb holds key
-        // t*64 + bb*32 + 16(r >> 3) + 8g + (r & 7).  Masks (keys past S, and
-        // with segment IDs every key whose ID differs) are selects, applied
-        // to every tile: the slot always holds 64 IDs.
+        // t*64 + bb*32 + 16(r >> 3) + 8g + (r & 7).  Partial tiles (the ragged
+        // last tile; with segment IDs, tiles with some pair of differing IDs)
+        // mask keys past S and keys whose ID differs with selects (the slot
+        // always holds 64 IDs); on full tiles every pair is valid.
         bf16x8 dsb[4];
-        const int lim = S - t * 64 - 8 * g;
-        const int* sgs = reinterpret_cast<const int*>(lds_ptr(st + T::kSeg)) + 8 * g;
+        auto form_ds = [&](auto maskc) {
+            constexpr bool kMask = decltype(maskc)::value;
+            const int lim = S - t * 64 - 8 * g;
+            const int* sgs = reinterpret_cast<const int*>(lds_ptr(st + T::kSeg)) + 8 * g;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
+            for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int jc = bb * 32 + 16 * (r >> 3) + (r & 7);
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c_log2, -lse2));
-                bool ok = jc < lim;
-                if (SEG) ok = ok & (sgs[jc] == myseg) & live;
-                p = ok ? p : 0.f;
-                dsb[2 * bb + (r >> 3)][r & 7] = (__bf16)(p * (pacc[bb][r] - delta));
+                for (int r = 0; r < 16; ++r) {
+                    const int jc = bb * 32 + 16 * (r >> 3) + (r & 7);
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[bb][r], c_log2, -lse2));
+                    if constexpr (kMask) {
+                        bool ok = jc < lim;
+                        if (SEG) ok = ok & (sgs[jc] == myseg) & live;
+                        p = ok ? p : 0.f;
+                    }
+                    dsb[2 * bb + (r >> 3)][r & 7] = (__bf16)(p * (pacc[bb][r] - delta));
+                }
             }
+        };
+        if (partial)
+            form_ds(std::true_type{});
+        else
+            form_ds(std::false_type{});
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+            tb0[db] = st + txk0[db];
+            tb1[db] = st + txk1[db];
+            asm volatile("" : "+v"(tb0[db]), "+v"(tb1[db]));
         }
-        (void)partial;
 
         // dQ^T += K^T dS^T: MFMA i takes key k-step i / kDBlocks, d-block
         // i % kDBlocks.
         {
             auto op = [&](auto ic) -> bf16x8 {
                 constexpr int i = ic;
-                return tr_operand<D>(tk, L.tx0, L.tx1, i / T::kDBlocks, i % T::kDBlocks);
+                constexpr int db = i % T::kDBlocks;
+                const uint32_t o = T::kA + (i / T::kDBlocks) * 16 * T::kRowBytes;
+                return tr_read8(lds_ptr(tb0[db] + o), lds_ptr(tb1[db] + o));
             };
             static_for<0, kPf>([&](auto ic) { ring[ic] = op(ic); });
             static_for<0, kNB>([&](auto ic) {
