@@ -240,9 +240,10 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
 // slices and the dK/dV accumulators take 192 AGPRs) so that its MFMAs and
 // VALU work overlap.  Sub-iteration u:
 //   step 1: dV^T += dO^T P and dK^T += Q^T dS of sub-tile u-1 (kNB MFMAs);
-//   step 2: S = Q K^T and dP = dO V^T of sub-tile u+1 (kNA MFMAs), with P and
-//           dS of sub-tile u formed on the VALU between them, two elements
-//           per MFMA.
+//   step 2: S = Q K^T and dP = dO V^T of sub-tile u+1 (kNA MFMAs);
+// P and dS of sub-tile u are formed on the VALU between the MFMAs of both
+// steps, two elements at a time, half in each step, so that neither step's
+// MFMA slots run short of issue time.
 // A tile iteration (two sub-iterations) reads tiles t-1, t and t+1 while
 // t+2 lands, hence four ring slots and one barrier per tile.  Operands are
 // fetched kPf MFMAs ahead through an 8-entry ring, across step and iteration
@@ -257,9 +258,20 @@ struct DkDv {
     static constexpr int kNA = 2 * T::kSteps;    // S and dP MFMAs per sub-tile
     static constexpr int kNB = 4 * T::kDBlocks;  // dV and dK MFMAs per sub-tile
     static constexpr int kPairs = 8;             // softmax element pairs per lane and sub-tile
-    static constexpr int kPairAhead = 2;         // lse2 / delta loads in flight
+    static constexpr int kPairAhead = 3;         // lse2 / delta loads in flight
+    // The pairs of a sub-tile are spread over two steps (D = 128): kPairsB in
+    // the dV/dK step before its S/dP step, from MFMA slot kSlotB0 on (the
+    // first slots give the MFMA results they read their wait states), the
+    // rest in the S/dP step from slot kSlotA0 on, one every kSlotStep slots.
+    // With D = 64 the steps have 8 slots and all pairs go to the S/dP step.
+    // A pair's exponentials go one slot before the rest of its arithmetic
+    // (kSplit), so that their latency passes behind an MFMA.
+    static constexpr int kPairsB = kNB >= 16 ? 4 : 0;
+    static constexpr int kSlotB0 = 4, kSlotA0 = kPairsB ? 1 : 0, kSlotStep = kPairsB ? 3 : 1;
+    static constexpr int kSplit = kPairsB ? 1 : 0;
     static_assert(kNA % kRing == 0 && kNB % kRing == 0 && kPf <= kRing - 2, "operand ring");
-    static_assert(kNA >= kPairs, "two softmax elements per S/dP MFMA");
+    static_assert(kPairsB == 0 || kSlotB0 + kSlotStep * (kPairsB - 1) < kNB, "pairs of the dV/dK step");
+    static_assert(kSlotA0 + kSlotStep * (kPairs - kPairsB - 1) < kNA, "pairs of the S/dP step");
 
     char* smem;
     Lanes<D> L;
@@ -272,6 +284,7 @@ struct DkDv {
     bf16x8 ring[kRing];
     float2 lpair[kPairAhead], dpair[kPairAhead];
     int2 spair[kPairAhead];
+    float2 pexp;  // P of the pair between its two halves
     // Lane offsets of the operand reads within a stage: row reads of k-step
     // ks at rxk[ks], the two halves of the transposed reads of d-block db at
     // txk0[db] / txk1[db].
@@ -360,13 +373,21 @@ struct DkDv {
         (void)partial;
     }
     // P = 2^(s c - lse2), dS = P (dP - delta) for pair J of the sub-tile in
-    // buffer B.
+    // buffer B, in two halves: the exponentials, then the masks, dS and the
+    // bf16 operands.
     template <int B, int J>
-    __device__ __forceinline__ void pair(bool partial) {
+    __device__ __forceinline__ void pair_exp() {
+        constexpr int r = 2 * J;
+        const float2 l = lpair[J % kPairAhead];
+        pexp.x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[B][r], c_log2, -l.x));
+        pexp.y = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[B][r + 1], c_log2, -l.y));
+        asm volatile("" : "+v"(pexp.x), "+v"(pexp.y));
+    }
+    template <int B, int J>
+    __device__ __forceinline__ void pair_form(bool partial) {
         constexpr int r = 2 * J, k = r / 8, e = r % 8;
-        const float2 l = lpair[J % kPairAhead], d = dpair[J % kPairAhead];
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[B][r], c_log2, -l.x));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[B][r + 1], c_log2, -l.y));
+        const float2 d = dpair[J % kPairAhead];
+        float p0 = pexp.x, p1 = pexp.y;
         if (SEG) {
             const int2 s = spair[J % kPairAhead];
             p0 = (s.x == myseg && myseg != 0) ? p0 : 0.f;
@@ -390,11 +411,35 @@ struct DkDv {
         static_for<0, kPairAhead>([&](auto jc) { load_pair(pv, h, jc, partial); });
     }
 
+    // Softmax pair of MFMA slot I of a step whose pairs start at slot S0 with
+    // pair J0, or -1.
+    template <int I, int S0, int J0, int N>
+    static constexpr int pair_at() {
+        return (I >= S0 && (I - S0) % kSlotStep == 0 && (I - S0) / kSlotStep < N) ? J0 + (I - S0) / kSlotStep : -1;
+    }
+    // The pair work of MFMA slot I of a step whose pairs start at slot S0
+    // with pair J0 (N of them, buffer PB).
+    template <int PB, int I, int S0, int J0, int N>
+    __device__ __forceinline__ void pairs_at(uint32_t pv, int hv, bool partial) {
+        constexpr int je = pair_at<I, S0, J0, N>();
+        if constexpr (je >= 0) pair_exp<PB, je>();
+        if constexpr (I >= kSplit) {
+            constexpr int jf = pair_at<I - kSplit, S0, J0, N>();
+            if constexpr (jf >= 0) {
+                pair_form<PB, jf>(partial);
+                if constexpr (jf + kPairAhead < kPairs) load_pair(pv, hv, jf + kPairAhead, partial);
+            }
+        }
+    }
+
     // Step 1: dV / dK of the sub-tile (stage bases tb, half h) whose P / dS
     // are in buffer B (operands prefetched).  NEXT_A: the last steps fetch the
-    // first operands of the S/dP step of sub-tile (ra, ha).
-    template <int B, bool NEXT_A>
-    __device__ __forceinline__ void step_b(const TrBases& tb, int h, const RowBases& ra, int ha) {
+    // first operands of the S/dP step of sub-tile (ra, ha).  PB >= 0: the
+    // first kPairsB softmax pairs of buffer PB (sub-tile (pv, hv)) go between
+    // the MFMAs.
+    template <int B, bool NEXT_A, int PB>
+    __device__ __forceinline__ void step_b(const TrBases& tb, int h, const RowBases& ra, int ha, uint32_t pv,
+                                           int hv, bool partial) {
         static_for<0, kNB>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i + kPf < kNB)
@@ -407,12 +452,17 @@ struct DkDv {
                 mfma32_acc<(i < 2)>(dkacc[db], a, dsb[B][kst]);
             else
                 mfma32_acc<(i < 2)>(dvacc[db], a, pb[B][kst]);
+            if constexpr (PB >= 0) pairs_at<PB, i, kSlotB0, 0, kPairsB>(pv, hv, partial);
             __builtin_amdgcn_sched_barrier(0);
         });
+        (void)pv;
+        (void)hv;
+        (void)partial;
     }
     // Step 2: S / dP of sub-tile (ra, ha) into buffer B ^ 1 (if A) with the
-    // softmax of buffer B (sub-tile (tv / pv, hv)) interleaved; the last steps
-    // fetch the first dV/dK operands of sub-tile (tv, hv).
+    // remaining softmax pairs of buffer B (sub-tile (tv / pv, hv))
+    // interleaved; the last steps fetch the first dV/dK operands of sub-tile
+    // (tv, hv).
     template <int B, bool A>
     __device__ __forceinline__ void step_a(const RowBases& ra, int ha, const TrBases& tv, uint32_t pv,
                                            int hv, bool partial) {
@@ -429,16 +479,14 @@ struct DkDv {
                     mfma32_vacc<(ks == 0), false>(pc[B ^ 1], a, vreg[ks]);
                 else
                     mfma32_vacc<(ks == 0), false>(sc[B ^ 1], a, kreg[ks]);
-                if constexpr (i < kPairs) {
-                    pair<B, i>(partial);
-                    if constexpr (i + kPairAhead < kPairs) load_pair(pv, hv, i + kPairAhead, partial);
-                }
+                pairs_at<B, i, kSlotA0, kPairsB, kPairs - kPairsB>(pv, hv, partial);
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else {
-            static_for<0, kPairs>([&](auto jc) {
+            static_for<kPairsB, kPairs>([&](auto jc) {
                 constexpr int j = jc;
-                pair<B, j>(partial);
+                pair_exp<B, j>();
+                pair_form<B, j>(partial);
                 if constexpr (j + kPairAhead < kPairs) load_pair(pv, hv, j + kPairAhead, partial);
             });
             static_for<0, kPf>([&](auto ic) { ring[ic] = op_b<ic>(tv, hv); });
@@ -606,11 +654,11 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
             const typename K::TrBases tp = A.trs(sp), tc = A.trs(s0);
             const typename K::RowBases rc = A.rows(s0), rn = A.rows(sn);
             const uint32_t pc = A.pair_base(s0);
-            A.template step_b<1, true>(tp, 1, rc, 1);
             A.prefetch_pairs(pc, 0, part);
+            A.template step_b<1, true, 0>(tp, 1, rc, 1, pc, 0, part);
             A.template step_a<0, true>(rc, 1, tc, pc, 0, part);
-            A.template step_b<0, true>(tc, 0, rn, 0);
             A.prefetch_pairs(pc, 1, part);
+            A.template step_b<0, true, 1>(tc, 0, rn, 0, pc, 1, part);
             A.template step_a<1, true>(rn, 0, tc, pc, 1, part);
             if (more) wait_vm(0);
             barrier();
@@ -618,7 +666,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
         // dV/dK of the last sub-tile (tile n_act - 1, half 1).
         {
             const typename K::TrBases tl = A.trs(sm + K::slot(n_act - 1));
-            A.template step_b<1, false>(tl, 1, typename K::RowBases{}, 0);
+            A.template step_b<1, false, -1>(tl, 1, typename K::RowBases{}, 0, 0, 0, false);
         }
     }
 
