@@ -157,19 +157,51 @@ __device__ __forceinline__ int wave_max(int x) {
     return x;
 }
 
+// Class of a tile pair from the two sides' summaries (min / max of the
+// nonzero IDs, INT32_MAX / INT32_MIN when there are none, and a flag for an
+// ID 0 or a row past S): 0 skip (no valid pair), 1 full (every pair valid:
+// one nonzero ID on both sides, no padding, no rows past S), 2 partial.
+__device__ __forceinline__ uint8_t tile_class(int omn, int omx, int ofl, int mn, int mx, int fl) {
+    if (omn > omx || mn > mx || max(omn, mn) > min(omx, mx)) return 0;
+    if (!ofl && !fl && omn == omx && mn == mx && omn == mn) return 1;
+    return 2;
+}
+
+// Compacts the active tiles of cls[0, n_tiles), in order, into list (bit 15
+// set: partial); every wave of the workgroup (NW of them) must call it, and
+// all of cls must be written before.  meta[3 NW] holds the count, which is
+// returned to every wave.
+template <int NW>
+__device__ int compact_tiles(const uint8_t* cls, int n_tiles, uint16_t* list, int* meta, int wave, int lane) {
+    __syncthreads();
+    if (wave == 0) {
+        int base = 0;
+        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+            const int t = t0 + lane;
+            const int c = (t < n_tiles) ? cls[t] : 0;
+            const uint64_t m = __ballot(c != 0);
+            const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+            if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
+            base += __popcll(m);
+        }
+        if (lane == 0) meta[3 * NW] = base;
+    }
+    __syncthreads();
+    return meta[3 * NW];
+}
+
 // Classifies every 64-row tile of the opposite side (segment IDs `other`, S
 // entries) against this workgroup's rows (ID `mine` per lane; 0 for padding
-// and rows past S) as skip (no valid pair), full (every pair valid: one
-// nonzero ID on both sides, no padding, no rows past S) or partial, and
-// compacts the active tiles, in order, into `list` (bit 15 set: partial).
-// `cls` is scratch of n_tiles bytes, `meta` of 3 NW + 1 ints; every wave of
-// the workgroup (NW of them) must call it.  Returns the number of active
-// tiles.  Each wave loads kUnroll tiles' IDs before reducing any of them, so
-// the loads' latency overlaps instead of adding up tile by tile.
+// and rows past S) with tile_class() and compacts the active tiles, in
+// order, into `list`.  `cls` is scratch of n_tiles bytes, `meta` of 3 NW + 1
+// ints; every wave of the workgroup (NW of them) must call it.  Returns the
+// number of active tiles.  A wave covers four tiles per step (16 lanes a
+// tile, 4 IDs a lane) and issues kU steps' loads before reducing any of
+// them, so the loads' latency overlaps instead of adding up tile by tile.
 template <int NW>
 __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
                               uint16_t* list, int* meta, int wave, int lane) {
-    constexpr int kUnroll = 4;
+    constexpr int kU = 4;
     {
         int mn = (mine != 0) ? mine : INT32_MAX;
         int mx = (mine != 0) ? mine : INT32_MIN;
@@ -191,50 +223,40 @@ __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles
         omx = max(omx, meta[NW + i]);
         ofl |= meta[2 * NW + i];
     }
-    for (int t0 = wave; t0 < n_tiles; t0 += NW * kUnroll) {
-        int id[kUnroll];
+    const int gq = lane >> 4, sub = lane & 15;
+    const int n_groups = (n_tiles + 3) / 4;
+    for (int g0 = wave; g0 < n_groups; g0 += NW * kU) {
+        int id[kU][4];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int t = t0 + u * NW;
-            const int r = t * 64 + lane;
-            id[u] = (t < n_tiles && r < S) ? other[r] : 0;
-        }
+        for (int u = 0; u < kU; ++u) {
+            const int t = (g0 + u * NW) * 4 + gq;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int t = t0 + u * NW;
-            int mn = (id[u] != 0) ? id[u] : INT32_MAX;
-            int mx = (id[u] != 0) ? id[u] : INT32_MIN;
-            int fl = (id[u] == 0) ? 1 : 0;
-            mn = wave_min(mn);
-            mx = wave_max(mx);
-            fl = wave_max(fl);
-            if (lane == 0 && t < n_tiles) {
-                uint8_t c;
-                if (omn > omx || mn > mx || max(omn, mn) > min(omx, mx))
-                    c = 0;
-                else if (!ofl && !fl && omn == omx && mn == mx && omn == mn)
-                    c = 1;
-                else
-                    c = 2;
-                cls[t] = c;
+            for (int e = 0; e < 4; ++e) {
+                const int r = t * 64 + 4 * sub + e;
+                id[u][e] = (t < n_tiles && r < S) ? other[r] : 0;
             }
         }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int base = 0;
-        for (int t0 = 0; t0 < n_tiles; t0 += 64) {
-            const int t = t0 + lane;
-            const int c = (t < n_tiles) ? cls[t] : 0;
-            const uint64_t m = __ballot(c != 0);
-            const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-            if (c != 0) list[pos] = (uint16_t)(t | ((c == 2) ? 0x8000 : 0));
-            base += __popcll(m);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int t = (g0 + u * NW) * 4 + gq;
+            int mn = INT32_MAX, mx = INT32_MIN, fl = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = id[u][e];
+                mn = (x != 0) ? min(mn, x) : mn;
+                mx = (x != 0) ? max(mx, x) : mx;
+                fl |= (x == 0) ? 1 : 0;
+            }
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                mn = min(mn, __shfl_xor(mn, o));
+                mx = max(mx, __shfl_xor(mx, o));
+                fl |= __shfl_xor(fl, o);
+            }
+            if (sub == 0 && t < n_tiles) cls[t] = tile_class(omn, omx, ofl, mn, mx, fl);
         }
-        if (lane == 0) meta[3 * NW] = base;
     }
-    __syncthreads();
-    return meta[3 * NW];
+    return compact_tiles<NW>(cls, n_tiles, list, meta, wave, lane);
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
