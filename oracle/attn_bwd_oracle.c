@@ -65,12 +65,15 @@ static int one_head(const bjob_t *J, int64_t b, int64_t h) {
     double *P = (double *)malloc(sizeof(double) * (size_t)(S * S));
     double *dS = (double *)malloc(sizeof(double) * (size_t)(S * S));
     double *E = J->tq ? (double *)malloc(sizeof(double) * (size_t)S) : NULL;
-    if (!P || !dS || (J->tq && !E)) {
+    double *acc = (double *)malloc(sizeof(double) * (size_t)(4 * D));
+    if (!P || !dS || (J->tq && !E) || !acc) {
         free(P);
         free(dS);
         free(E);
+        free(acc);
         return 1;
     }
+    double *accv = acc + D, *tacc = acc + 2 * D, *taccv = acc + 3 * D;
     for (int64_t i = 0; i < S; ++i) {
         double m = -INFINITY;
         for (int64_t j = 0; j < S; ++j) {
@@ -116,37 +119,63 @@ static int one_head(const bjob_t *J, int64_t b, int64_t h) {
             E[i] = e;
         }
     }
+    /* The sums below run the index being summed over in ascending order for
+     * each output element; the loops nest with that index outside the head
+     * dimension so P, dS and the operand rows are walked contiguously. */
+    for (int64_t i = 0; i < S; ++i) {
+        for (int64_t d = 0; d < D; ++d) acc[d] = tacc[d] = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+            const double ds = dS[i * S + j];
+            const uint16_t *kj = J->k + at(J, b, j, h);
+            for (int64_t d = 0; d < D; ++d) acc[d] += ds * b2d(kj[d]);
+            if (E) {
+                const double w = fabs(ds) + P[i * S + j] * E[i];
+                for (int64_t d = 0; d < D; ++d) tacc[d] += w * fabs(b2d(kj[d]));
+            }
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            J->dq[at(J, b, i, h) + d] = J->scale * acc[d];
+            if (E) J->tq[at(J, b, i, h) + d] = J->scale * tacc[d];
+        }
+    }
+    /* dk and dv sum over the queries i: transpose P and dS so that key j's
+     * column is contiguous. */
     for (int64_t i = 0; i < S; ++i)
-        for (int64_t d = 0; d < D; ++d) {
-            double acc = 0.0;
-            for (int64_t j = 0; j < S; ++j) acc += dS[i * S + j] * b2d(J->k[at(J, b, j, h) + d]);
-            J->dq[at(J, b, i, h) + d] = J->scale * acc;
-            if (E) {
-                double t = 0.0;
-                for (int64_t j = 0; j < S; ++j)
-                    t += (fabs(dS[i * S + j]) + P[i * S + j] * E[i]) * fabs(b2d(J->k[at(J, b, j, h) + d]));
-                J->tq[at(J, b, i, h) + d] = J->scale * t;
-            }
+        for (int64_t j = 0; j < i; ++j) {
+            const double p = P[i * S + j], g = dS[i * S + j];
+            P[i * S + j] = P[j * S + i];
+            dS[i * S + j] = dS[j * S + i];
+            P[j * S + i] = p;
+            dS[j * S + i] = g;
         }
-    for (int64_t j = 0; j < S; ++j)
-        for (int64_t d = 0; d < D; ++d) {
-            double acck = 0.0, accv = 0.0;
-            for (int64_t i = 0; i < S; ++i) {
-                acck += dS[i * S + j] * b2d(J->q[at(J, b, i, h) + d]);
-                accv += P[i * S + j] * b2d(J->dout[at(J, b, i, h) + d]);
+    /* P and dS now hold P^T and dS^T: P[j * S + i] = P_ij */
+    for (int64_t j = 0; j < S; ++j) {
+        for (int64_t d = 0; d < D; ++d) acc[d] = accv[d] = tacc[d] = taccv[d] = 0.0;
+        for (int64_t i = 0; i < S; ++i) {
+            const double ds = dS[j * S + i], p = P[j * S + i];
+            const uint16_t *qi = J->q + at(J, b, i, h), *oi = J->dout + at(J, b, i, h);
+            for (int64_t d = 0; d < D; ++d) {
+                acc[d] += ds * b2d(qi[d]);
+                accv[d] += p * b2d(oi[d]);
             }
-            J->dk[at(J, b, j, h) + d] = J->scale * acck;
-            J->dv[at(J, b, j, h) + d] = accv;
             if (E) {
-                double tk = 0.0, tv = 0.0;
-                for (int64_t i = 0; i < S; ++i) {
-                    tk += (fabs(dS[i * S + j]) + P[i * S + j] * E[i]) * fabs(b2d(J->q[at(J, b, i, h) + d]));
-                    tv += P[i * S + j] * fabs(b2d(J->dout[at(J, b, i, h) + d]));
+                const double w = fabs(ds) + p * E[i];
+                for (int64_t d = 0; d < D; ++d) {
+                    tacc[d] += w * fabs(b2d(qi[d]));
+                    taccv[d] += p * fabs(b2d(oi[d]));
                 }
-                J->tk[at(J, b, j, h) + d] = J->scale * tk;
-                J->tv[at(J, b, j, h) + d] = tv;
             }
         }
+        for (int64_t d = 0; d < D; ++d) {
+            J->dk[at(J, b, j, h) + d] = J->scale * acc[d];
+            J->dv[at(J, b, j, h) + d] = accv[d];
+            if (E) {
+                J->tk[at(J, b, j, h) + d] = J->scale * tacc[d];
+                J->tv[at(J, b, j, h) + d] = taccv[d];
+            }
+        }
+    }
+    free(acc);
     free(P);
     free(dS);
     free(E);

@@ -20,19 +20,21 @@ import test_bwd_oracle as pins
 MUTANTS = [
     ("delta_dropped", "dS[i * S + j] = P[i * S + j] * (dS[i * S + j] - delta);",
      "dS[i * S + j] = P[i * S + j] * dS[i * S + j];"),
-    ("dq_no_scale", "J->dq[at(J, b, i, h) + d] = J->scale * acc;", "J->dq[at(J, b, i, h) + d] = acc;"),
-    ("dk_uses_k", "acck += dS[i * S + j] * b2d(J->q[at(J, b, i, h) + d]);",
-     "acck += dS[i * S + j] * b2d(J->k[at(J, b, i, h) + d]);"),
-    ("dv_transposed_p", "accv += P[i * S + j] * b2d(J->dout[at(J, b, i, h) + d]);",
-     "accv += P[j * S + i] * b2d(J->dout[at(J, b, i, h) + d]);"),
+    ("dq_no_scale", "J->dq[at(J, b, i, h) + d] = J->scale * acc[d];",
+     "J->dq[at(J, b, i, h) + d] = acc[d];"),
+    ("dk_uses_k", "acc[d] += ds * b2d(qi[d]);",
+     "acc[d] += ds * b2d(J->k[at(J, b, i, h) + d]);"),
+    # after the in-place transpose P[j * S + i] holds P_ij
+    ("dv_transposed_p", "accv[d] += p * b2d(oi[d]);",
+     "accv[d] += P[i * S + j] * b2d(oi[d]);"),
     ("dp_uses_q", "dp += b2d(J->dout[at(J, b, i, h) + d]) * b2d(J->v[at(J, b, j, h) + d]);",
      "dp += b2d(J->q[at(J, b, i, h) + d]) * b2d(J->v[at(J, b, j, h) + d]);"),
     ("softmax_unnormalised", "P[i * S + j] = (l > 0.0) ? P[i * S + j] / l : 0.0;",
      "P[i * S + j] = P[i * S + j];"),
     ("pad_matches_pad", "return c != 0 && J->seg_kv[b * J->S + j] == c;",
      "return J->seg_kv[b * J->S + j] == c;"),
-    ("dq_transposed_ds", "acc += dS[i * S + j] * b2d(J->k[at(J, b, j, h) + d]);",
-     "acc += dS[j * S + i] * b2d(J->k[at(J, b, j, h) + d]);"),
+    ("dq_transposed_ds", "const double ds = dS[i * S + j];",
+     "const double ds = dS[j * S + i];"),
 ]
 
 PIN_FUNCS = [
