@@ -378,7 +378,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py measures one GPU only: the attention kernel runs on one GPU's share "
-              "with every head local; multi-GPU runs are not part of this build", file=sys.stderr)
+              "with every head local; the library has no multi-GPU execution path", file=sys.stderr)
         sys.exit(2)
 
     import spatiotemporal_attention_amd as vdx

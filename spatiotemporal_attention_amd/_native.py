@@ -28,7 +28,7 @@ EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_wo
 
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"HIP library not built: {path} (run __graft_entry__.build())")
+        raise ImportError(f"HIP library not built: {path} (build it with python spatiotemporal_attention_amd/build.py)")
     lib = ctypes.CDLL(path)
     p = ctypes.c_void_p
     i = ctypes.c_int
