@@ -46,7 +46,10 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or queries (dQ) per workgroup
-constexpr int kBwdMaxTiles = 14000;       // capacity of the on-chip active-tile list
+// Capacity of the on-chip active-tile list; with the dK/dV sweep's four-stage
+// ring at D = 128 it fills 163,232 of the 160 KiB of LDS a workgroup may take
+// (checked at compile time with the LDS budgets below).
+constexpr int kBwdMaxTiles = 14000;
 constexpr int kPad = 64;                  // workspace rows are padded to this multiple
 #ifndef VDX_BWD_PREFETCH
 #define VDX_BWD_PREFETCH 4
@@ -934,15 +937,18 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
 }
 
 template <int D>
-size_t dkdv_lds(bool seg, int n_tiles) {
-    size_t b = DkDv<D, false>::kSlots * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
+constexpr size_t dkdv_lds(bool seg, int n_tiles) {
+    const size_t b = DkDv<D, false>::kSlots * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
     return ((b + 15) & ~(size_t)15) + 16 * sizeof(int);
 }
 template <int D>
-size_t dq_lds(bool seg, int n_tiles) {
-    size_t b = 2 * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
+constexpr size_t dq_lds(bool seg, int n_tiles) {
+    const size_t b = 2 * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
     return ((b + 15) & ~(size_t)15) + 16 * sizeof(int);
 }
+static_assert(dkdv_lds<128>(true, kBwdMaxTiles) <= kLdsBytes && dkdv_lds<64>(true, kBwdMaxTiles) <= kLdsBytes &&
+                  dq_lds<128>(true, kBwdMaxTiles) <= kLdsBytes && dq_lds<64>(true, kBwdMaxTiles) <= kLdsBytes,
+              "a full active-tile list must fit in the LDS beside the ring");
 
 template <int D, bool SEG>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {

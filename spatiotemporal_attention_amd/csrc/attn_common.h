@@ -31,6 +31,7 @@ constexpr int kSlots = 3;         // ring depth of the K, V and segment-ID stage
 #endif
 constexpr int kOperandPrefetch = VDX_OPERAND_PREFETCH;  // MFMA operands in flight
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr size_t kLdsBytes = 160 * 1024;  // gfx950: LDS one workgroup may allocate
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 #ifndef VDX_LAZY_LOG2

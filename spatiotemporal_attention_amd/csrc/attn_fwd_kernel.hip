@@ -599,17 +599,25 @@ int64_t persistent_workgroups() {
     return g;
 }
 
+// Dynamic LDS of a launch: the K/V/segment-ID ring, then (masked) the
+// active-tile list of n_kvt entries and classify_tiles' metadata.
+template <int D, bool SEG>
+constexpr size_t fwd_lds(int n_kvt) {
+    size_t lds = (size_t)Tile<D>::kRingBytes;
+    if (SEG) lds += 2 * (size_t)n_kvt;
+    lds = (lds + 15) & ~(size_t)15;
+    return lds + 32 * sizeof(int);  // meta
+}
+static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(kMaxKvTiles) <= kLdsBytes,
+              "a full active-tile list must fit in the LDS beside the ring");
+
 template <int D, bool SEG>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-    using T = Tile<D>;
     const int n_qblk = (a.S + kBq - 1) / kBq;
     const int n_kvt = (a.S + kBk - 1) / kBk;
     const int64_t n_wg64 = (int64_t)a.B * a.H * n_qblk;
     const int n_wg = (int)n_wg64;
-    size_t lds = (size_t)T::kRingBytes;
-    if (SEG) lds += 2 * (size_t)n_kvt;
-    lds = (lds + 15) & ~(size_t)15;
-    lds += 32 * sizeof(int);  // meta
+    const size_t lds = fwd_lds<D, SEG>(n_kvt);
     const float c_log2 = a.scale * kLog2e;
     // Unmasked, every item has the same work and the persistent grid keeps
     // the CUs of an XCD in step; with segment IDs items differ (up to 8x on

@@ -268,3 +268,56 @@ def test_packed_clips_whole_clip_and_sampled_rows(need_gpu):
     for n, gi in zip(("dq", "dk", "dv"), (dq, dk, dv)):
         assert torch.count_nonzero(gi[0, pad].float()) == 0, n
     print(_dq_rows_check(x, dout, seg, w.scale, dq, heads=(0, 15), n_rows=24, seed=2))
+
+
+def test_masked_maximum_sequence(need_gpu):
+    """The largest sequence a masked backward accepts: 14,000 tiles of 64 in
+    its on-chip lists (S = 896,000).  Key tile t carries ID 1 on its first
+    token and the tile-unique ID 2 + t on the others; query block 0 (tokens
+    0..255) has ID 1 and every other query the tile-unique ID of its tile; the
+    last 5 tokens are padding.  So the dQ sweep of query block 0 lists every
+    key tile and the dK/dV sweep of the last key block lists every query tile.
+    dq is compared on sampled rows (all of block 0 among them) with the row
+    oracle; dq, dk and dv of the local segments of the last tiles with the
+    oracle run on each tile as its own sequence (segments are independent; a
+    tile's first key, ID 1, belongs to block 0's segment and is left out)."""
+    B, S, H, D = 1, 896_000, 1, 128
+    assert S // 64 == 14_000
+    tok = torch.arange(S, dtype=torch.int64)
+    seg_kv = torch.where(tok % 64 == 0, 1, 2 + tok // 64).to(torch.int32)
+    seg_q = torch.where(tok < 256, 1, 2 + tok // 64).to(torch.int32)
+    seg_kv[S - 5:] = 0
+    seg_q[S - 5:] = 0
+    seg_q, seg_kv = seg_q[None].contiguous(), seg_kv[None].contiguous()
+    scale = 1.0 / math.sqrt(D)
+    print(f"case bwd masked max S={S}: generating inputs", flush=True)
+    x = W.make_random(B, S, H, D, seed=8960)
+    dout = W.randn_bf16((B, S, H, D), 8967)
+    print(f"case bwd masked max S={S}: gpu run", flush=True)
+    dq, dk, dv = run_gpu_bwd(x, dout, seg_q, seg_kv, scale)
+    # dq rows: block 0 (every key tile), tile edges, the end, seeded random rows.
+    rng = np.random.default_rng(17)
+    idx = sorted(set(range(256)) | {256, 257, 319, 320, S - 65, S - 64, S - 6, S - 5, S - 1}
+                 | set(int(i) for i in rng.choice(S, 40, replace=False)))
+    rows = np.array([(0, 0, i) for i in idx], dtype=np.int64)
+    print(f"case bwd masked max S={S}: dq row oracle on {len(rows)} rows", flush=True)
+    o, t = oracle.attn_bwd_dq_rows(W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"]),
+                                   W.bf16_bits(dout), seg_q.numpy(), seg_kv.numpy(),
+                                   float(np.float32(scale)), rows, sensitivity=True)
+    dead = ~valid_rows(seg_q, seg_kv, B, S)[rows[:, 0], rows[:, 2]]
+    print(check_grad("dq rows", dq[rows[:, 0], rows[:, 2], rows[:, 1]], o, dead, t), flush=True)
+    # Local segments of the last 4 tiles, each as its own 64-token sequence.
+    for k in range(S // 64 - 4, S // 64):
+        a, e = 64 * k, 64 * k + 64
+        xs = {n: x[n][:, a:e].contiguous() for n in ("q", "k", "v")}
+        sq, sk = seg_q[:, a:e].clone(), seg_kv[:, a:e].clone()
+        o = run_oracle_bwd(xs, dout[:, a:e].contiguous(), sq, sk, scale)
+        qd, kd = masks(sq, sk, 1, 64, 1)
+        check_grad(f"dq tile {k}", dq[:, a:e], o[0], qd, o[3])
+        # keys a+1 .. a+63: key a (ID 1) also serves block 0, outside this sub-problem
+        for n, gi, oi, ti in (("dk", dk, o[1], o[4]), ("dv", dv, o[2], o[5])):
+            check_grad(f"{n} tile {k}", gi[:, a + 1:e], oi[:, 1:], kd[:, 1:], ti[:, 1:])
+    pad = slice(S - 5, S)
+    for n, gi in zip(("dq", "dk", "dv"), (dq, dk, dv)):
+        assert torch.count_nonzero(gi[0, pad].float()) == 0, n
+        assert torch.isfinite(gi.float()).all(), n

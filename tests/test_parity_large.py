@@ -82,3 +82,46 @@ def test_zero_query_closed_form_every_row(need_gpu, name):
                     assert err <= np.abs(mean).max() * 2.0 ** -8 + 1e-6, (b, a, e, h, err)
                     assert np.abs(l - math.log(n_tok)).max() <= LSE_ATOL
     del out, lse
+
+
+# The largest sequence a masked call accepts: the on-chip active-tile list
+# holds 30,720 key tiles of 64 (S = 1,966,080).  Key tile t carries ID 1 on its
+# first token and the tile-unique ID 2 + t on the others; the last 5 tokens are
+# padding on both sides.  Query block 0 (tokens 0..255) has ID 1, so every key
+# tile is active (and partial) for it and its list is full; any other query
+# has the tile-unique ID of its own tile and attends the 63 other keys there.
+# The ragged case ends in a partly filled last tile, still 30,720 tiles.
+@pytest.mark.parametrize("S,D", [(1_966_080, 128), (1_966_063, 64)])
+def test_masked_maximum_sequence(need_gpu, S, D):
+    import spatiotemporal_attention_amd as vdx
+    B, H = 1, 1
+    assert (S + 63) // 64 == 30_720
+    tok = torch.arange(S, dtype=torch.int64)
+    seg_kv = torch.where(tok % 64 == 0, 1, 2 + tok // 64).to(torch.int32)
+    seg_q = torch.where(tok < 256, 1, 2 + tok // 64).to(torch.int32)
+    seg_kv[S - 5:] = 0
+    seg_q[S - 5:] = 0
+    seg_q, seg_kv = seg_q[None].contiguous(), seg_kv[None].contiguous()
+    print(f"case masked max S={S} D={D}: generating inputs", flush=True)
+    x = W.make_random(B, S, H, D, seed=S % 100_000)
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    print(f"case masked max S={S} D={D}: gpu run", flush=True)
+    out, lse = vdx.attn_fwd(d["q"], d["k"], d["v"], seg_q.cuda(), seg_kv.cuda(),
+                            scale=1.0 / math.sqrt(D))
+    torch.cuda.synchronize()
+    out_c, lse_c = out.cpu(), lse.cpu()
+    del d, out, lse
+    rows = sample_rows(S, H, B, None, n_random=48, seed=3)
+    extra = [(0, 0, i) for i in (2, 63, 64, 100, 200, 254, 255, 256, 257)]
+    rows = np.unique(np.concatenate([rows, np.array(extra, dtype=np.int64)]), axis=0)
+    print(f"case masked max S={S} D={D}: oracle on {len(rows)} rows", flush=True)
+    out_o, lse_o = run_oracle(x, seg_q, seg_kv, 1.0 / math.sqrt(D), rows=rows)
+    has = valid_rows(seg_q, seg_kv, B, S)
+    assert has[0, :256].all() and not has[0, S - 5:].any()
+    st = check_rows(out_c, lse_c, rows, out_o, lse_o, has)
+    print(st, flush=True)
+    # Every padded row is +0.0 / -inf, every other output is finite.
+    assert np.all(out_c[0, S - 5:].view(torch.int16).numpy() == 0)
+    assert np.all(np.isneginf(lse_c[0, 0, S - 5:].numpy()))
+    assert torch.isfinite(out_c[0, :S - 5].float()).all()
+    assert torch.isfinite(lse_c[0, 0, :S - 5]).all()
