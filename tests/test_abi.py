@@ -311,3 +311,48 @@ def test_bwd_error_path_writes_nothing(need_gpu):
     torch.cuda.synchronize()
     assert rc == _native.VDX_ERR_WORKSPACE
     assert all(torch.all(t == 3.0) for t in g) and torch.all(ws == 7)
+
+
+C_CLIENT = r"""
+#include "vdx_attn.h"
+#include <stdio.h>
+
+/* A plain C99 caller: the header must need no C++ and every entry point must
+ * link; only argument validation runs (NULL tensors), so no GPU is touched. */
+int main(void) {
+    int fails = 0;
+    if (vdx_abi_version() != VDX_ABI_VERSION) fails |= 1;
+    if (vdx_attn_fwd(0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR) fails |= 2;
+    if (vdx_natten3d_fwd(0, 0, 0, 0, 0, 1, 1, 1, 64, 1, 64, 1, 1, 1, 0.125f, 0) != VDX_ERR_NULL_PTR)
+        fails |= 4;
+    if (vdx_attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR)
+        fails |= 8;
+    if (vdx_attn_bwd_workspace_size(1, 64, 1) == 0) fails |= 16;
+    if (vdx_status_str(VDX_OK) == NULL) fails |= 32;
+    printf("%d %s\n", fails, vdx_status_str(VDX_ERR_NULL_PTR));
+    return fails;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """A C99 program includes the header, links the built library and calls
+    every entry point (validation paths only)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    from spatiotemporal_attention_amd import _native
+    libdir = os.path.dirname(_native.LIB_PATH)
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o", str(exe),
+           "-L", libdir, "-lvdx_attn", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr[-2000:])
+    assert "VDX_ERR_NULL_PTR" in r.stdout
