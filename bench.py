@@ -163,8 +163,8 @@ def natten_window_volume(w) -> int:
 
 def natten_executed_flop(w) -> float:
     """MFMA flops the kernel issues: per workgroup (a 1x8x32 query brick) one
-    64-key row tile per key row of its window union, 8 waves x 32 queries x
-    32 keys x 2 products x 2*D each."""
+    step per two key rows of its window union (an odd row count adds a masked
+    row), each row 8 waves x 32 queries x 32 keys x 2 products x 2*D."""
     NT, NH, NW = w.grid
     KT, KH, KW = w.window
 
@@ -172,13 +172,13 @@ def natten_executed_flop(w) -> float:
         ke = min(k, n)
         return min(max(c - k // 2, 0), n - ke)
 
-    tiles = 0
+    rows = 0
     for by in range((NH + 7) // 8):
         y0 = 8 * by
         ny = start(min(y0 + 7, NH - 1), KH, NH) + min(KH, NH) - start(y0, KH, NH)
-        tiles += min(KT, NT) * ny
-    tiles *= NT * ((NW + 31) // 32)
-    return float(tiles) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
+        rows += 2 * ((min(KT, NT) * ny + 1) // 2)
+    rows *= NT * ((NW + 31) // 32)
+    return float(rows) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
 
 
 def natten_cpu_baseline(w, x, target_s: float = 15.0):

@@ -15,13 +15,16 @@
 //     1 x 8 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
 //     sub-brick at y offset 2(w >> 1), x offset 16(w & 1), lane lr the query
 //     (lr >> 4, lr & 15) of it;
-//   * the workgroup streams one key row (t', y') per tile: 64 consecutive x
-//     positions from X0 (its first query's window start, rounded down to 4),
-//     over every row in the union of its queries' windows -- t' in the common
-//     t window, y' in [start(y0), start(y0 + 7) + kh_eff);
-//   * each wave multiplies only the 32-key block of the tile that holds its
+//   * the workgroup walks the key rows (t', y') in the union of its queries'
+//     windows -- t' in the common t window, y' in [start(y0),
+//     start(y0 + 7) + kh_eff) -- two rows per step: a ring slot holds two rows
+//     of 48 consecutive x positions from X0 (the brick's first window start,
+//     rounded down to 4), which cover the x windows of all 32 brick columns;
+//   * each wave multiplies only the 32-key block of each row that holds its
 //     queries' x windows (they span at most 16 + kw_eff - 1 <= 28 keys from a
-//     4-aligned offset, so kw_eff <= 13), i.e. 8 + 8 MFMAs per tile at D=128;
+//     4-aligned offset, so kw_eff <= 13), i.e. 16 K Q^T + 16 P V MFMAs per
+//     step at D = 128 -- the segment kernel's phase length, so the barrier
+//     and operand start-up of a phase are spread over the work of two rows;
 //   * element masks: key (t', y', x') is valid for a query iff y' and x' lie
 //     in its windows (t' always does); invalid scores become -inf before the
 //     online softmax, which is the segment kernel's;
@@ -42,15 +45,38 @@ __device__ __forceinline__ int win_start(int c, int k, int n) {
     return min(max(c - k / 2, 0), n - keff);
 }
 
-constexpr int kBrickY = 8;   // query rows per workgroup
-constexpr int kBrickX = 32;  // query columns per workgroup
+constexpr int kBrickY = 8;    // query rows per workgroup
+constexpr int kBrickX = 32;   // query columns per workgroup
+constexpr int kRowKeys = 48;  // keys of one key row held in LDS
+
+// LDS ring of the neighbourhood kernel: kSlots slots of K and of V, each two
+// key rows of kRowKeys keys (slot rows 0..47 and 48..95), with the K and V
+// swizzles of the segment kernel applied to the slot row.
+template <int D>
+struct NTile {
+    static constexpr int kChunks = D / 8;
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kSlotRows = 2 * kRowKeys;
+    static constexpr int kSlotBytes = kSlotRows * kRowBytes;
+    static constexpr int kKRegion = 0;
+    static constexpr int kVRegion = kSlots * kSlotBytes;
+    static constexpr int kRingBytes = 2 * kSlots * kSlotBytes;
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+    static constexpr int kLoadsPerWave = kSlotBytes / 1024 / kDmaWaves;
+    static constexpr int kSteps = D / 16;
+    static constexpr int kDBlocks = D / 32;
+    // Waves 0-1 of a copying group fill the slot's first row, waves 2-3 its
+    // second: no load straddles the two rows.
+    static_assert(kLoadsPerWave * 2 * kRowsPerLoad == kRowKeys, "one row per wave pair");
+    static_assert(kSlotBytes % 1024 == 0, "slot bases must keep the swizzle bits free");
+    static_assert(kRingBytes <= (int)kLdsBytes, "ring exceeds the LDS");
+};
 
 template <int D>
 struct Nat {
-    using T = Tile<D>;
-    static constexpr int kQk = T::kSteps;         // K Q^T MFMAs per tile (one 32-key block)
-    static constexpr int kPv = 2 * T::kDBlocks;   // P V MFMAs per tile (two 16-key steps)
-    static constexpr int kNm = kQk + kPv;
+    using T = NTile<D>;
+    static constexpr int kQk = 2 * T::kSteps;     // K Q^T MFMAs per step (two rows)
+    static constexpr int kPv = 4 * T::kDBlocks;   // P V MFMAs per step (two rows x two 16-key halves)
     static constexpr int kRing = kOperandPrefetch + 2;
 
     char* smem;
@@ -59,37 +85,39 @@ struct Nat {
     int64_t tok_stride;
     int NH, NW, lane, lr, g, w4;
     float c_log2;
-    // workgroup key rows: t' in [ts, ts + kt), y' in [ylo, ylo + ny)
-    int ts, ylo, ny, x0k, kh, kw;
-    bool tail;          // the tile's 64 keys run past the grid row
-    int kx, vx;         // operand bases of this wave's 32-key block (in a ring slot)
+    // workgroup key rows: t' in [ts, ts + kt), y' in [ylo, ylo + ny); n_rows of them
+    int ts, ylo, ny, n_rows, x0k, kh, kw;
+    bool tail;          // a row's kRowKeys keys run past the grid row
+    int kx[2], vx;      // operand bases of this wave's 32-key block in each row of a slot
     int xrel;           // X0 + block offset + 8g - xs_q: key register c is x offset xrel + c
     int ys_q;           // this lane's query y-window start
     uint32_t dmo[T::kLoadsPerWave];
     bf16x8 qreg[T::kSteps];
     f32x16 oacc[T::kDBlocks];
-    f32x16 sacc;
-    bf16x8 pb[2];
+    f32x16 sacc[2];
+    bf16x8 pb[4];
     bf16x8 ops[kRing];
-    uint32_t vb_next, kb_next;
+    uint32_t vb_next, kb_next[2];
     float m_run, l_run;
 
     __device__ __forceinline__ static int slot_base(int n) {
-        int o = (n % kSlots) * T::kTileBytes;
+        int o = (n % kSlots) * T::kSlotBytes;
         asm volatile("" : "+s"(o));
         return o;
     }
     __device__ __forceinline__ uint32_t vbase(int n) const {
         return lds_addr(smem) + T::kVRegion + slot_base(n) + vx;
     }
-    __device__ __forceinline__ uint32_t kbase(int n) const {
-        return lds_addr(smem) + T::kKRegion + slot_base(n) + kx;
+    __device__ __forceinline__ uint32_t kbase(int n, int j) const {
+        return lds_addr(smem) + T::kKRegion + slot_base(n) + kx[j];
     }
 
     // ---- tile copies --------------------------------------------------------
-    // Tile a is key row (ts + a / ny, ylo + a % ny), keys x' in [x0k, x0k+64).
-    // Group 0 copies K of tile n+2 in its MFMA phase of iteration n, group 1 V
-    // of tile n+1 (the ring discipline of the segment-masked kernel).
+    // Step a holds key rows 2a and 2a+1 of the walk (row r is (ts + r / ny,
+    // ylo + r % ny)); a missing last row repeats row 2a and is masked.  Group 0
+    // copies K of step n+2 in its MFMA phase of iteration n, group 1 V of step
+    // n+1 (the ring discipline of the segment-masked kernel).  (at, ay) is the
+    // key row this wave copies.
     struct Copy {
         const __bf16* src;
         char* dst;
@@ -108,15 +136,15 @@ struct Nat {
             c.cnt = T::kLoadsPerWave;
         }
     }
-    // Tail rows (x' past the grid row) read the row's last key instead; the x
-    // masks exclude them.
+    // Keys past the grid row read the row's last key instead; the x masks
+    // exclude them.
     __device__ __forceinline__ void copy_start(const Copy& c) {
         if (tail && c.cnt > 0) {
             const int lim = NW - 1 - x0k;
 #pragma unroll
             for (int j = 0; j < T::kLoadsPerWave; ++j) {
-                const int i = w4 * T::kLoadsPerWave + j;
-                const int r = T::kRowsPerLoad * i + lane / T::kChunks;
+                const int i = (w4 & 1) * T::kLoadsPerWave + j;
+                const int r = T::kRowsPerLoad * i + lane / T::kChunks;  // key within the row
                 const int over = max(0, r - lim);
                 dma16(c.src, dmo[j] - (uint32_t)over * (uint32_t)(2 * tok_stride), c.dst + j * 1024);
             }
@@ -136,25 +164,32 @@ struct Nat {
         });
     }
 
-    // ---- MFMA phase: K Q^T of tile n, then P V of tile n-1 --------------------
+    // ---- MFMA phase: K Q^T of step n, then P V of step n-1 --------------------
+    // K Q^T MFMA i: k-step i / 2 of row i % 2 (the rows alternate, so
+    // consecutive MFMAs accumulate into different registers).  P V MFMA j:
+    // kst = j / kDBlocks names row kst >> 1 and its 16-key half kst & 1,
+    // d-block j % kDBlocks.
     template <bool QK, int I>
-    __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb) const {
+    __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb0, uint32_t kb1) const {
         if constexpr (QK && I < kQk) {
-            return *reinterpret_cast<const bf16x8*>(lds_ptr(kb ^ (I << 5)));
+            constexpr int ks = I / 2, row = I % 2;
+            return *reinterpret_cast<const bf16x8*>(lds_ptr((row ? kb1 : kb0) ^ (ks << 5)));
         } else {
             constexpr int j = QK ? I - kQk : I;
             constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
-            const char* p = lds_ptr((vb ^ (db << 6)) + kst * 16 * T::kRowBytes);
+            const char* p =
+                lds_ptr((vb ^ (db << 6)) + ((kst >> 1) * kRowKeys + (kst & 1) * 16) * T::kRowBytes);
             return tr_read8(p, p + 4 * T::kRowBytes);
         }
     }
     template <bool QK, int I>
     __device__ __forceinline__ void mfma(const bf16x8& a) {
         if constexpr (QK && I < kQk) {
-            if constexpr (I == 0)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
+            constexpr int ks = I / 2, row = I % 2;
+            if constexpr (ks == 0)
+                sacc[row] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
             else
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[I], sacc, 0, 0, 0);
+                sacc[row] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[row], 0, 0, 0);
         } else {
             constexpr int j = QK ? I - kQk : I;
             constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
@@ -162,26 +197,27 @@ struct Nat {
         }
     }
     template <bool PV, bool QK>
-    __device__ __forceinline__ void prefetch(int vtile, int ktile) {
+    __device__ __forceinline__ void prefetch(int vstep, int kstep) {
         constexpr int NM = (QK ? kQk : 0) + (PV ? kPv : 0);
-        vb_next = vbase(vtile);
-        kb_next = kbase(ktile);
+        vb_next = vbase(vstep);
+        kb_next[0] = kbase(kstep, 0);
+        kb_next[1] = kbase(kstep, 1);
         static_for<0, kOperandPrefetch>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i < NM) ops[i % kRing] = operand<QK, i>(vb_next, kb_next);
+            if constexpr (i < NM) ops[i % kRing] = operand<QK, i>(vb_next, kb_next[0], kb_next[1]);
         });
     }
     template <bool PV, bool QK, bool PRE>
-    __device__ __forceinline__ void mfma_phase(int vtile, int ktile, const Copy& cp) {
+    __device__ __forceinline__ void mfma_phase(int vstep, int kstep, const Copy& cp) {
         constexpr int NM = (QK ? kQk : 0) + (PV ? kPv : 0);
         constexpr int PF = kOperandPrefetch;
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (!PRE) prefetch<PV, QK>(vtile, ktile);
-        const uint32_t vb = vb_next, kb = kb_next;
+        if constexpr (!PRE) prefetch<PV, QK>(vstep, kstep);
+        const uint32_t vb = vb_next, kb0 = kb_next[0], kb1 = kb_next[1];
         copy_start(cp);
         static_for<0, NM>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb);
+            if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb0, kb1);
             mfma<QK, i>(ops[i % kRing]);
             copy_step<i, NM>(cp);
             __builtin_amdgcn_sched_barrier(0);
@@ -190,28 +226,31 @@ struct Nat {
     }
 
     // ---- VALU phase --------------------------------------------------------------
-    // Masks for key row y' of the current tile: accumulator register r holds
-    // the block key 16 (r >> 3) + 8 g + (r & 7), i.e. x offset xrel + c_r.
-    __device__ __forceinline__ void mask(int yk) {
-        const bool row_ok = (unsigned)(yk - ys_q) < (unsigned)kh;
+    // Masks for the step's key rows y0k, y1k (no second row: live1 false).
+    // Accumulator register r holds the block key 16 (r >> 3) + 8 g + (r & 7),
+    // i.e. x offset xrel + c_r, in both rows.
+    __device__ __forceinline__ void mask(int y0k, int y1k, bool live1) {
+        const bool row0 = (unsigned)(y0k - ys_q) < (unsigned)kh;
+        const bool row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c = 16 * (r >> 3) + (r & 7);
-            const bool ok = row_ok && (unsigned)(xrel + c) < (unsigned)kw;
-            if (!ok) sacc[r] = -INFINITY;
+            const bool xok = (unsigned)(xrel + c) < (unsigned)kw;
+            if (!(row0 && xok)) sacc[0][r] = -INFINITY;
+            if (!(row1 && xok)) sacc[1][r] = -INFINITY;
         }
     }
-    // Online softmax of the tile's 16 scores per lane with the lazily moved
+    // Online softmax of the step's 32 scores per lane with the lazily moved
     // reference of the segment-masked kernel (P <= 2^kLazyLog2).
     __device__ __forceinline__ void softmax() {
-        float mx0 = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-        float mx1 = fmaxf(fmaxf(sacc[8], sacc[9]), sacc[10]);
+        float mx0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+        float mx1 = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
 #pragma unroll
-        for (int r = 3; r < 7; r += 2) {
-            mx0 = fmaxf(fmaxf(mx0, sacc[r]), sacc[r + 1]);
-            mx1 = fmaxf(fmaxf(mx1, sacc[8 + r]), sacc[8 + r + 1]);
+        for (int r = 3; r < 15; r += 2) {
+            mx0 = fmaxf(fmaxf(mx0, sacc[0][r]), sacc[0][r + 1]);
+            mx1 = fmaxf(fmaxf(mx1, sacc[1][r]), sacc[1][r + 1]);
         }
-        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[7]), fmaxf(mx1, sacc[15]))) * c_log2;
+        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]))) * c_log2;
         const bool move = mx > m_run + kLazyLog2;
         if (__ballot(move) != 0ull) {
             const float m_new = move ? mx : m_run;
@@ -226,62 +265,77 @@ struct Nat {
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -msub));
-            ls[r & 3] += p;
-            pb[r >> 3][r & 7] = (__bf16)p;
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][r], c_log2, -msub));
+                ls[r & 3] += p;
+                pb[b * 2 + (r >> 3)][r & 7] = (__bf16)p;
+            }
         }
         l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(l_run), "v"(m_run));
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run), "v"(m_run));
+    }
+};
+
+// Position (t, y) of a key row in the workgroup's walk, relative to (ts, ylo).
+struct RowPos {
+    int t, y;
+    __device__ __forceinline__ void advance(int ny, int n) {
+        for (int i = 0; i < n; ++i)
+            if (++y == ny) {
+                y = 0;
+                ++t;
+            }
     }
 };
 
 // Ping-pong schedule of group G (see the segment-masked kernel): local
-// iteration n = MFMA phase (K Q^T of tile n, P V of tile n-1) at global phase
-// 2n + G, then the VALU phase (masks and softmax of tile n) at 2n + 1 + G.
-// (mt, my) walk the tile being masked, (ct, cy) the tile being planned.
+// iteration n = MFMA phase (K Q^T of step n, P V of step n-1) at global phase
+// 2n + G, then the VALU phase (masks and softmax of step n) at 2n + 1 + G.
+// mrow walks the first row of the step being masked; crow the first row of
+// the step being planned, of which waves 0-1 of the group copy the first row
+// and waves 2-3 the second (the first again when the step has one row).
 template <int G, int D>
 __device__ __forceinline__ void natten_loop(Nat<D>& A, int n_act) {
     typename Nat<D>::Copy cp;
-    int my = 0, ct = 0, cy = 0;
-    auto advance = [&](int& at, int& ay) {
-        if (++ay == A.ny) {
-            ay = 0;
-            ++at;
-        }
+    const bool second = (A.w4 >> 1) != 0;
+    RowPos mrow{0, 0}, crow{0, 0};
+    auto plan_step = [&](int a) {
+        RowPos p = crow;
+        if (second && 2 * a + 1 < A.n_rows) p.advance(A.ny, 1);
+        A.template plan<G>(cp, a, p.t, p.y, n_act);
     };
-    // planned tile index a = n + 2 - G: start the walk there
-    for (int i = 0; i < 2 - G; ++i) advance(ct, cy);
     auto valu_phase = [&](int n) {
-        A.mask(A.ylo + my);
-        {
-            int dummy = 0;
-            advance(dummy, my);
-        }
+        RowPos r1 = mrow;
+        r1.advance(A.ny, 1);
+        A.mask(A.ylo + mrow.y, A.ylo + r1.y, 2 * n + 1 < A.n_rows);
+        mrow.advance(A.ny, 2);
         A.softmax();
-        advance(ct, cy);
-        A.template plan<G>(cp, n + 3 - G, ct, cy, n_act);
+        crow.advance(A.ny, 2);
+        plan_step(n + 3 - G);
         A.template prefetch<true, true>(n, n + 1);
         barrier();
     };
-    A.template plan<G>(cp, 2 - G, ct, cy, n_act);
+    crow.advance(A.ny, 2 * (2 - G));  // first planned step: 2 - G
+    plan_step(2 - G);
     A.template prefetch<false, true>(0, 0);
     if (G == 1) barrier();  // group 1 idles in global phase 0
     A.template mfma_phase<false, true, true>(0, 0, cp);
-    wait_copies<Nat<D>::T::kLoadsPerWave>(cp.cnt);
+    wait_vm(cp.cnt);
     barrier();
     valu_phase(0);
     for (int n = 1; n < n_act; ++n) {
         const int c = cp.cnt;
         A.template mfma_phase<true, true, true>(n - 1, n, cp);
-        wait_copies<Nat<D>::T::kLoadsPerWave>(c);
+        wait_vm(c);
         barrier();
         valu_phase(n);
     }
     {
         const int c = cp.cnt;
         A.template mfma_phase<true, false, false>(n_act - 1, 0, cp);
-        wait_copies<Nat<D>::T::kLoadsPerWave>(c);
+        wait_vm(c);
         barrier();
     }
     if (G == 0) barrier();  // group 0 idles in the last global phase
@@ -292,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ out, float* __restrict__ lse, int NT, int NH, int NW, int H, int KT, int KH,
     int KW, float c_log2, int nby, int nbx, int n_wg) {
-    using T = Tile<D>;
+    using T = NTile<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     // XCD-contiguous renumbering: consecutive bricks of one head share an L2.
@@ -334,16 +388,17 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     A.kw = min(KW, NW);
     const int kt = min(KT, NT);
 
-    // ---- workgroup key rows and the x range of the tiles ----------------------
+    // ---- workgroup key rows and the x range of the rows ------------------------
     A.ts = win_start(tq, KT, NT);
     A.ylo = win_start(y0, KH, NH);
     A.ny = win_start(min(y0 + kBrickY - 1, NH - 1), KH, NH) + A.kh - A.ylo;
+    A.n_rows = kt * A.ny;
     A.x0k = win_start(x0, KW, NW) & ~3;
-    A.tail = A.x0k + kBk > NW;
-    const int n_act = kt * A.ny;
-    // this wave's 32-key block inside the tile, and the lane's windows
+    A.tail = A.x0k + kRowKeys > NW;
+    const int n_act = (A.n_rows + 1) / 2;  // steps of two key rows
+    // this wave's 32-key block inside a row, and the lane's windows
     const int xw = min(x0 + 16 * (wave & 1), NW - 1);
-    const int boff = min((win_start(xw, KW, NW) & ~3) - A.x0k, kBk - 32);
+    const int boff = min((win_start(xw, KW, NW) & ~3) - A.x0k, kRowKeys - 32);
     A.ys_q = win_start(min(yq, NH - 1), KH, NH);
     const int xs_q = win_start(min(xq, NW - 1), KW, NW);
     A.xrel = A.x0k + boff + 8 * g - xs_q;
@@ -358,44 +413,59 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     }
     // ---- per-lane LDS offsets (operand rows shifted by the block offset) -------
     {
-        const int krow = boff + swap23(lr);
-        A.kx = krow * T::kRowBytes + ((g ^ k_swz<D>(krow)) << 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int krow = j * kRowKeys + boff + swap23(lr);
+            A.kx[j] = krow * T::kRowBytes + ((g ^ k_swz<D>(krow)) << 4);
+        }
+        // v_swz looks at the slot row mod 4 only, and kRowKeys is a multiple
+        // of 4: one base serves both rows.
         const int qg = lane >> 4, j = lane & 15;
         const int key = boff + 8 * (qg >> 1) + (j >> 2);
         const int vsw = v_swz<D>(key);
         A.vx = key * T::kRowBytes + 32 * ((qg & 1) ^ vsw) + 16 * ((j & 3) >> 1) + 8 * (j & 1);
+        // Tile copies: load jj of this wave covers slot rows kRowsPerLoad*i ..
+        // (i = w4 * L + jj); a lane lands at LDS position pos of its slot row
+        // and fetches the chunk stored there (K layout for group 0, V layout
+        // for group 1) from key r % kRowKeys of its key row.
 #pragma unroll
         for (int jj = 0; jj < T::kLoadsPerWave; ++jj) {
             const int i = A.w4 * T::kLoadsPerWave + jj;
-            const int r = T::kRowsPerLoad * i + lane / T::kChunks;
+            const int r = T::kRowsPerLoad * i + lane / T::kChunks;  // slot row
             const int pos = lane % T::kChunks;
             const int c = grp ? 2 * ((pos >> 1) ^ v_swz<D>(r)) + (pos & 1) : (pos ^ k_swz<D>(r));
-            A.dmo[jj] = 2u * (uint32_t)(r * (int)A.tok_stride + c * 8);
+            A.dmo[jj] = 2u * (uint32_t)((r % kRowKeys) * (int)A.tok_stride + c * 8);
         }
     }
 #pragma unroll
     for (int i = 0; i < T::kDBlocks; ++i) A.oacc[i] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) A.pb[i] = bf16x8{};
+    for (int i = 0; i < 4; ++i) A.pb[i] = bf16x8{};
     A.m_run = -INFINITY;
     A.l_run = 0.f;
 
-    // ---- prologue: K of tiles 0 and 1 (group 0), V of tile 0 (group 1) ---------
+    // ---- prologue: K of steps 0 and 1 (group 0), V of step 0 (group 1) ---------
     {
         typename Nat<D>::Copy c;
+        const bool second = (A.w4 >> 1) != 0;
+        auto row_of = [&](int a) {
+            RowPos p{0, 0};
+            p.advance(A.ny, 2 * a + ((second && 2 * a + 1 < A.n_rows) ? 1 : 0));
+            return p;
+        };
         if (grp == 0) {
-            int at = 0, ay = 0;
             for (int a = 0; a < 2; ++a) {
-                A.template plan<0>(c, a, at, ay, n_act);
+                const RowPos p = row_of(a);
+                A.template plan<0>(c, a, p.t, p.y, n_act);
                 A.copy_start(c);
                 if (c.spread) {
 #pragma unroll
                     for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
                 }
-                if (++ay == A.ny) ay = 0, ++at;
             }
         } else {
-            A.template plan<1>(c, 0, 0, 0, n_act);
+            const RowPos p = row_of(0);
+            A.template plan<1>(c, 0, p.t, p.y, n_act);
             A.copy_start(c);
             if (c.spread) {
 #pragma unroll
@@ -434,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
 
 template <int D>
 hipError_t launch_t(const NattenArgs& a, hipStream_t stream) {
-    using T = Tile<D>;
+    using T = NTile<D>;
     const int nby = (a.NH + kBrickY - 1) / kBrickY;
     const int nbx = (a.NW + kBrickX - 1) / kBrickX;
     const int n_wg = a.B * a.H * a.NT * nby * nbx;
