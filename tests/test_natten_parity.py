@@ -2,7 +2,7 @@
 ABI) against the fp64 oracle on the same seeded bf16 inputs.
 
 Small grids are compared element by element: x extents below, at and above
-the 32-query brick and the 64-key tile (ragged tails), y extents that are not
+the 32-query brick and the 48-key row (ragged tails), y extents that are not
 multiples of the 8-row brick, single-frame grids, windows from 1 to 13 and
 windows wider than their axis (whole axis).  The VAE-decoder-sized grid is
 compared on sampled rows (grid corners, edges and random interior rows) and,
@@ -50,6 +50,10 @@ CASES = [
     ((2, 17, 24), (3, 31, 5), 1, 64),     # y window wider than the axis
     ((5, 4, 12), (9, 3, 21), 1, 128),     # x window wider than the axis (whole axis)
     ((6, 10, 70), (11, 11, 11), 1, 128),
+    # x extents at, below and above the 48-key row the kernel stages per key row
+    ((2, 9, 48), (3, 3, 13), 1, 128),
+    ((1, 8, 47), (1, 5, 11), 2, 64),
+    ((2, 10, 81), (3, 7, 13), 1, 128),
 ]
 
 
