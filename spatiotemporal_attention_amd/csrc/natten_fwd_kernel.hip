@@ -350,14 +350,19 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     // XCD-contiguous renumbering: consecutive bricks of one head share an L2.
+    // Within a head the y-brick index varies slowest, interior bricks first:
+    // the first and last y-bricks (windows clipped at the border, or a
+    // partial brick) walk fewer key rows, and dispatching the long bricks
+    // before the short ones lets the CUs of an XCD finish together.
     const int w = blockIdx.x;
     const int per = n_wg / kXcds, rem = n_wg % kXcds;
     const int xcd = w % kXcds;
     const int lid = xcd * per + min(xcd, rem) + w / kXcds;
     const int bx = lid % nbx;
-    const int by = (lid / nbx) % nby;
-    const int tq = (lid / (nbx * nby)) % NT;
-    const int bh = lid / (nbx * nby * NT);
+    const int tq = (lid / nbx) % NT;
+    const int byi = (lid / (nbx * NT)) % nby;
+    const int by = nby < 3 ? byi : (byi < nby - 2 ? byi + 1 : (byi == nby - 2 ? 0 : nby - 1));
+    const int bh = lid / (nbx * NT * nby);
     const int h = bh % H;
     const int b = bh / H;
     const int S = NT * NH * NW;
