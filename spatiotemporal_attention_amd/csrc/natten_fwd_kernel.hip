@@ -87,7 +87,6 @@ struct Nat {
     float c_log2;
     // workgroup key rows: t' in [ts, ts + kt), y' in [ylo, ylo + ny); n_rows of them
     int ts, ylo, ny, n_rows, x0k, kh, kw;
-    bool tail;          // a row's kRowKeys keys run past the grid row
     int kx[2], vx;      // operand bases of this wave's 32-key block in each row of a slot
     int xrel;           // X0 + block offset + 8g - xs_q: key register c is x offset xrel + c
     int ys_q;           // this lane's query y-window start
@@ -132,22 +131,8 @@ struct Nat {
             const int64_t tok = ((int64_t)(ts + at) * NH + (ylo + ay)) * NW + x0k;
             c.src = (G ? vp : kp) + tok * tok_stride;
             c.dst = smem + (G ? T::kVRegion : T::kKRegion) + slot_base(a) + w4 * T::kLoadsPerWave * 1024;
-            c.spread = !tail;
+            c.spread = true;
             c.cnt = T::kLoadsPerWave;
-        }
-    }
-    // Keys past the grid row read the row's last key instead; the x masks
-    // exclude them.
-    __device__ __forceinline__ void copy_start(const Copy& c) {
-        if (tail && c.cnt > 0) {
-            const int lim = NW - 1 - x0k;
-#pragma unroll
-            for (int j = 0; j < T::kLoadsPerWave; ++j) {
-                const int i = (w4 & 1) * T::kLoadsPerWave + j;
-                const int r = T::kRowsPerLoad * i + lane / T::kChunks;  // key within the row
-                const int over = max(0, r - lim);
-                dma16(c.src, dmo[j] - (uint32_t)over * (uint32_t)(2 * tok_stride), c.dst + j * 1024);
-            }
         }
     }
     // Load j of a spread copy goes out after MFMA step j*NM/L + 1 of a phase
@@ -214,7 +199,6 @@ struct Nat {
         __builtin_amdgcn_s_setprio(1);
         if constexpr (!PRE) prefetch<PV, QK>(vstep, kstep);
         const uint32_t vb = vb_next, kb0 = kb_next[0], kb1 = kb_next[1];
-        copy_start(cp);
         static_for<0, NM>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb0, kb1);
@@ -399,7 +383,6 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     A.ny = win_start(min(y0 + kBrickY - 1, NH - 1), KH, NH) + A.kh - A.ylo;
     A.n_rows = kt * A.ny;
     A.x0k = win_start(x0, KW, NW) & ~3;
-    A.tail = A.x0k + kRowKeys > NW;
     const int n_act = (A.n_rows + 1) / 2;  // steps of two key rows
     // this wave's 32-key block inside a row, and the lane's windows
     const int xw = min(x0 + 16 * (wave & 1), NW - 1);
@@ -432,14 +415,18 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
         // Tile copies: load jj of this wave covers slot rows kRowsPerLoad*i ..
         // (i = w4 * L + jj); a lane lands at LDS position pos of its slot row
         // and fetches the chunk stored there (K layout for group 0, V layout
-        // for group 1) from key r % kRowKeys of its key row.
+        // for group 1) from key r % kRowKeys of its key row.  Keys past the
+        // grid row read the row's last key instead (the x masks exclude them);
+        // every row of the item starts at x0k, so the clamp is folded in here
+        // once and every copy is spread between MFMAs.
 #pragma unroll
         for (int jj = 0; jj < T::kLoadsPerWave; ++jj) {
             const int i = A.w4 * T::kLoadsPerWave + jj;
             const int r = T::kRowsPerLoad * i + lane / T::kChunks;  // slot row
             const int pos = lane % T::kChunks;
             const int c = grp ? 2 * ((pos >> 1) ^ v_swz<D>(r)) + (pos & 1) : (pos ^ k_swz<D>(r));
-            A.dmo[jj] = 2u * (uint32_t)((r % kRowKeys) * (int)A.tok_stride + c * 8);
+            const int xk = min(A.x0k + r % kRowKeys, NW - 1) - A.x0k;  // key within the row
+            A.dmo[jj] = 2u * (uint32_t)(xk * (int)A.tok_stride + c * 8);
         }
     }
 #pragma unroll
@@ -462,7 +449,6 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
             for (int a = 0; a < 2; ++a) {
                 const RowPos p = row_of(a);
                 A.template plan<0>(c, a, p.t, p.y, n_act);
-                A.copy_start(c);
                 if (c.spread) {
 #pragma unroll
                     for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
@@ -471,7 +457,6 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
         } else {
             const RowPos p = row_of(0);
             A.template plan<1>(c, 0, p.t, p.y, n_act);
-            A.copy_start(c);
             if (c.spread) {
 #pragma unroll
                 for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
