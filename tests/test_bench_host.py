@@ -1,0 +1,83 @@
+"""Host logic of bench.py, on the CPU: the multi-GPU refusal, the FLOP and
+byte counts behind `value` and `roofline`, and the rule that ties the
+committed HBM-counter summaries to the kernel sources they were taken on.
+
+The expected FLOP and byte figures were worked out separately from the
+workload definitions (valid-pair FLOP = 4 D H x #valid pairs, algorithmic
+bytes = read q, k, v and segment IDs, write out and lse); the counts here
+come from bench.py's run-length formulas and, independently, from the
+per-token segment arrays the tests and the benchmark feed the kernel.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+
+# name: (valid-pair TFLOP, dense TFLOP, algorithmic GB), 4 significant digits
+EXPECTED = {
+    "tiny_ref": (1.074e-3, 1.074e-3, 2.1e-3),
+    "dit480p_small": (6.594, 6.594, 0.4038),
+    "joint_video_text_pad": (7.766, 7.892, 0.8850),
+    "dit720p_large": (117.05, 117.05, 3.109),
+    "packed_clips": (11.677, 30.924, 1.011),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED))
+def test_flop_and_byte_counts(name):
+    w = W.WORKLOADS[name]
+    valid_t, dense_t, gb = EXPECTED[name]
+    flop = 4.0 * w.D * w.H * bench.valid_pairs(w)
+    assert flop / 1e12 == pytest.approx(valid_t, rel=1e-3)
+    assert 4.0 * w.D * w.H * w.B * w.S * w.S / 1e12 == pytest.approx(dense_t, rel=1e-3)
+    assert bench.algorithmic_bytes(w) / 1e9 == pytest.approx(gb, rel=2e-2)
+
+
+@pytest.mark.parametrize("name", [n for n, w in W.WORKLOADS.items() if w.seg_runs is not None])
+def test_valid_pairs_match_the_token_arrays(name):
+    """Count valid pairs from the per-token ID array (ID 0 matches nothing)."""
+    w = W.WORKLOADS[name]
+    seg = W.seg_from_runs(w.seg_runs, w.B, w.S).numpy()
+    total = 0
+    for b in range(w.B):
+        ids, counts = np.unique(seg[b], return_counts=True)
+        total += int(sum(int(c) * int(c) for i, c in zip(ids, counts) if i != 0))
+    assert bench.valid_pairs(w) == total
+
+
+def test_natten_counts():
+    w = W.NATTEN_WORKLOADS["natten_vae_decoder"]
+    # every query sees the full 11^3 window (it shifts inward at the borders)
+    assert bench.natten_window_volume(w) == 11 ** 3
+    # 8 heads x 10,944 two-row steps per head (bricks of 8 rows walk 18 key
+    # rows in the interior, 13 at the y borders, over 11 frames), each step 2
+    # rows x 8 waves x 32 queries x 32 keys x 2 products x 2 D
+    assert bench.natten_executed_flop(w) == pytest.approx(8 * 10944 * 2 * 8 * 32 * 32 * 4 * 128, rel=0)
+
+
+def test_traffic_served_only_for_matching_sources(tmp_path, monkeypatch):
+    import json
+    doc = {"kernel_source_sha256": bench.kernel_source_hash(), "traffic_bytes_per_launch": 123}
+    (tmp_path / "attn_fwd_dit720p_large_hbm_counters.json").write_text(json.dumps(doc))
+    monkeypatch.setattr(bench, "COUNTERS_DIR", str(tmp_path))
+    assert bench.load_traffic("dit720p_large") == 123
+    doc["kernel_source_sha256"] = "0" * 64
+    (tmp_path / "attn_fwd_dit720p_large_hbm_counters.json").write_text(json.dumps(doc))
+    assert bench.load_traffic("dit720p_large") is None
+    assert bench.load_traffic("packed_clips") is None  # no summary for it
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
