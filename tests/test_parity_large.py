@@ -5,7 +5,10 @@ configuration the benchmark times.
 The oracle evaluates sampled rows one by one (row 0, 1, S-1, tile edges,
 segment boundaries, pad rows and seeded random rows for every head); closed
 forms check every row at full size: with Q = 0 each valid row is the mean of
-V over its segment with lse = ln(segment size), pad rows are zero / -inf.
+V over its segment with lse = ln(segment size), pad rows are zero / -inf;
+with every token its own segment out = V bit for bit and lse = scale q.k;
+with V constant over the tokens every valid row returns that constant.
+Masked calls also run at the largest sequence the on-chip tile list allows.
 """
 import math
 
@@ -125,3 +128,50 @@ def test_masked_maximum_sequence(need_gpu, S, D):
     assert np.all(np.isneginf(lse_c[0, 0, S - 5:].numpy()))
     assert torch.isfinite(out_c[0, :S - 5].float()).all()
     assert torch.isfinite(lse_c[0, 0, :S - 5]).all()
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_distinct_ids_return_value_every_row(need_gpu, name):
+    """Every token its own segment (IDs 1..S): a row's only valid key is
+    itself, so P = 2^0 = 1 exactly and out = v bit for bit, lse = scale q.k."""
+    import spatiotemporal_attention_amd as vdx
+    w = W.WORKLOADS[name]
+    print(f"case {name}: distinct IDs", flush=True)
+    x = W.make_inputs(w)
+    seg = torch.arange(1, w.S + 1, dtype=torch.int32).repeat(w.B, 1).contiguous()
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    out, lse = vdx.attn_fwd(d["q"], d["k"], d["v"], seg.cuda(), seg.cuda(), scale=w.scale)
+    torch.cuda.synchronize()
+    del d
+    assert torch.equal(out.cpu().view(torch.int16), x["v"].view(torch.int16))
+    scale = float(np.float32(w.scale))
+    for b in range(w.B):
+        s_ii = (x["q"][b].double() * x["k"][b].double()).sum(-1).numpy() * scale  # [S, H]
+        err = np.abs(lse[b].cpu().numpy().T.astype(np.float64) - s_ii).max()
+        assert err <= LSE_ATOL, (b, err)
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_constant_value_every_row(need_gpu, name):
+    """V[b, j, h, :] = c_h for every token: each valid row's output is c_h
+    (its probabilities sum to 1).  The GPU weights c by the bf16-rounded
+    probabilities but divides by their unrounded fp32 sum, a ratio within
+    u = 2^-8 of 1 (each term rounds by at most u relative), and rounds the
+    output once more by u: |out - c| <= 2u |c|, plus 1e-4 |c| for the fp32
+    sums.  Padding rows stay +0.0."""
+    import spatiotemporal_attention_amd as vdx
+    w = W.WORKLOADS[name]
+    print(f"case {name}: constant V", flush=True)
+    x = W.make_inputs(w)
+    c = W.randn_bf16((w.H, w.D), 4242)
+    x["v"] = c[None, None].expand(w.B, w.S, w.H, w.D).contiguous()
+    d = {n: (None if t is None else t.cuda()) for n, t in x.items()}
+    out, _ = _run(d, w)
+    del d
+    o = out.float().cpu().numpy()
+    has = valid_rows(x["seg_q"], x["seg_kv"], w.B, w.S)
+    cc = c.double().numpy()[None]
+    err = np.abs(o[has] - cc)
+    assert np.all(err <= (2 * 2.0 ** -8 + 1e-4) * np.abs(cc) + 1e-6), float(err.max())
+    if (~has).any():
+        assert np.all(out.cpu().view(torch.int16).numpy()[~has] == 0)
