@@ -162,9 +162,10 @@ def natten_window_volume(w) -> int:
 
 
 def natten_executed_flop(w) -> float:
-    """MFMA flops the kernel issues: per workgroup (a 1x8x32 query brick) one
-    step per two key rows of its window union (an odd row count adds a masked
-    row), each row 8 waves x 32 queries x 32 keys x 2 products x 2*D."""
+    """MFMA flops the kernel issues: per workgroup (a 2x4x32 (t, y, x) query
+    brick) one step per two key rows of its window union (an odd row count
+    adds a masked row), each row 8 waves x 32 queries x 32 keys x 2 products
+    x 2*D."""
     NT, NH, NW = w.grid
     KT, KH, KW = w.window
 
@@ -172,12 +173,15 @@ def natten_executed_flop(w) -> float:
         ke = min(k, n)
         return min(max(c - k // 2, 0), n - ke)
 
+    def span(c0, brick, k, n):  # window-union length of a brick starting at c0
+        return start(min(c0 + brick - 1, n - 1), k, n) + min(k, n) - start(c0, k, n)
+
     rows = 0
-    for by in range((NH + 7) // 8):
-        y0 = 8 * by
-        ny = start(min(y0 + 7, NH - 1), KH, NH) + min(KH, NH) - start(y0, KH, NH)
-        rows += 2 * ((min(KT, NT) * ny + 1) // 2)
-    rows *= NT * ((NW + 31) // 32)
+    for t0 in range(0, NT, 2):
+        nt = span(t0, 2, KT, NT)
+        for y0 in range(0, NH, 4):
+            rows += 2 * ((nt * span(y0, 4, KH, NH) + 1) // 2)
+    rows *= (NW + 31) // 32
     return float(rows) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
 
 

@@ -12,12 +12,15 @@
 //
 // Design (same machinery as the segment-masked kernel):
 //   * one workgroup = 8 wave64s (two per SIMD, two ping-pong groups) and a
-//     1 x 8 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
-//     sub-brick at y offset 2(w >> 1), x offset 16(w & 1), lane lr the query
-//     (lr >> 4, lr & 15) of it;
+//     2 x 4 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
+//     sub-brick of frame t0 + (w >> 2) at y offset 2((w >> 1) & 1), x offset
+//     16(w & 1), lane lr the query (lr >> 4, lr & 15) of it -- two frames by
+//     four rows, because a brick's window union (12 x 14 key rows for 11^3
+//     windows) then holds fewer rows per query than one frame by eight rows
+//     (11 x 18);
 //   * the workgroup walks the key rows (t', y') in the union of its queries'
-//     windows -- t' in the common t window, y' in [start(y0),
-//     start(y0 + 7) + kh_eff) -- two rows per step: a ring slot holds two rows
+//     windows -- t' in [start(t0), start(t0 + 1) + kt_eff), y' in
+//     [start(y0), start(y0 + 3) + kh_eff) -- two rows per step: a ring slot holds two rows
 //     of 48 consecutive x positions from X0 (the brick's first window start,
 //     rounded down to 4), which cover the x windows of all 32 brick columns;
 //   * each wave multiplies only the 32-key block of each row that holds its
@@ -25,8 +28,8 @@
 //     4-aligned offset, so kw_eff <= 13), i.e. 16 K Q^T + 16 P V MFMAs per
 //     step at D = 128 -- the segment kernel's phase length, so the barrier
 //     and operand start-up of a phase are spread over the work of two rows;
-//   * element masks: key (t', y', x') is valid for a query iff y' and x' lie
-//     in its windows (t' always does); invalid scores become -inf before the
+//   * element masks: key (t', y', x') is valid for a query iff t', y' and x'
+//     lie in its windows; invalid scores become -inf before the
 //     online softmax, which is the segment kernel's;
 //   * copies, operand prefetch, ping-pong schedule and epilogue follow the
 //     segment-masked kernel.
@@ -45,7 +48,8 @@ __device__ __forceinline__ int win_start(int c, int k, int n) {
     return min(max(c - k / 2, 0), n - keff);
 }
 
-constexpr int kBrickY = 8;    // query rows per workgroup
+constexpr int kBrickT = 2;    // query frames per workgroup (one per ping-pong group)
+constexpr int kBrickY = 4;    // query rows per workgroup
 constexpr int kBrickX = 32;   // query columns per workgroup
 constexpr int kRowKeys = 48;  // keys of one key row held in LDS
 
@@ -85,11 +89,11 @@ struct Nat {
     int64_t tok_stride;
     int NH, NW, lane, lr, g, w4;
     float c_log2;
-    // workgroup key rows: t' in [ts, ts + kt), y' in [ylo, ylo + ny); n_rows of them
-    int ts, ylo, ny, n_rows, x0k, kh, kw;
+    // workgroup key rows: t' in [ts, ts + nt), y' in [ylo, ylo + ny); n_rows of them
+    int ts, nt, ylo, ny, n_rows, x0k, kt, kh, kw;
     int kx[2], vx;      // operand bases of this wave's 32-key block in each row of a slot
     int xrel;           // X0 + block offset + 8g - xs_q: key register c is x offset xrel + c
-    int ys_q;           // this lane's query y-window start
+    int ts_q, ys_q;     // this lane's query t- and y-window starts
     uint32_t dmo[T::kLoadsPerWave];
     bf16x8 qreg[T::kSteps];
     f32x16 oacc[T::kDBlocks];
@@ -210,12 +214,13 @@ struct Nat {
     }
 
     // ---- VALU phase --------------------------------------------------------------
-    // Masks for the step's key rows y0k, y1k (no second row: live1 false).
-    // Accumulator register r holds the block key 16 (r >> 3) + 8 g + (r & 7),
-    // i.e. x offset xrel + c_r, in both rows.
-    __device__ __forceinline__ void mask(int y0k, int y1k, bool live1) {
-        const bool row0 = (unsigned)(y0k - ys_q) < (unsigned)kh;
-        const bool row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh;
+    // Masks for the step's key rows (t0k, y0k), (t1k, y1k) (no second row:
+    // live1 false).  Accumulator register r holds the block key
+    // 16 (r >> 3) + 8 g + (r & 7), i.e. x offset xrel + c_r, in both rows.
+    __device__ __forceinline__ void mask(int t0k, int y0k, int t1k, int y1k, bool live1) {
+        const bool row0 = (unsigned)(y0k - ys_q) < (unsigned)kh && (unsigned)(t0k - ts_q) < (unsigned)kt;
+        const bool row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh &&
+                          (unsigned)(t1k - ts_q) < (unsigned)kt;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c = 16 * (r >> 3) + (r & 7);
@@ -293,7 +298,7 @@ __device__ __forceinline__ void natten_loop(Nat<D>& A, int n_act) {
     auto valu_phase = [&](int n) {
         RowPos r1 = mrow;
         r1.advance(A.ny, 1);
-        A.mask(A.ylo + mrow.y, A.ylo + r1.y, 2 * n + 1 < A.n_rows);
+        A.mask(A.ts + mrow.t, A.ylo + mrow.y, A.ts + r1.t, A.ylo + r1.y, 2 * n + 1 < A.n_rows);
         mrow.advance(A.ny, 2);
         A.softmax();
         crow.advance(A.ny, 2);
@@ -329,7 +334,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ out, float* __restrict__ lse, int NT, int NH, int NW, int H, int KT, int KH,
-    int KW, float c_log2, int nby, int nbx, int n_wg) {
+    int KW, float c_log2, int nbt, int nby, int nbx, int n_wg) {
     using T = NTile<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -343,10 +348,10 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const int xcd = w % kXcds;
     const int lid = xcd * per + min(xcd, rem) + w / kXcds;
     const int bx = lid % nbx;
-    const int tq = (lid / nbx) % NT;
-    const int byi = (lid / (nbx * NT)) % nby;
+    const int bt = (lid / nbx) % nbt;
+    const int byi = (lid / (nbx * nbt)) % nby;
     const int by = nby < 3 ? byi : (byi < nby - 2 ? byi + 1 : (byi == nby - 2 ? 0 : nby - 1));
-    const int bh = lid / (nbx * NT * nby);
+    const int bh = lid / (nbx * nbt * nby);
     const int h = bh % H;
     const int b = bh / H;
     const int S = NT * NH * NW;
@@ -355,11 +360,12 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, g = lane >> 5;
     const int grp = wave >> 2;
-    const int y0 = by * kBrickY, x0 = bx * kBrickX;
-    const int yq = y0 + 2 * (wave >> 1) + (lr >> 4);
+    const int t0 = bt * kBrickT, y0 = by * kBrickY, x0 = bx * kBrickX;
+    const int tq = t0 + grp;
+    const int yq = y0 + 2 * ((wave >> 1) & 1) + (lr >> 4);
     const int xq = x0 + 16 * (wave & 1) + (lr & 15);
-    const bool active = yq < NH && xq < NW;
-    const int qi = (tq * NH + min(yq, NH - 1)) * NW + min(xq, NW - 1);
+    const bool active = tq < NT && yq < NH && xq < NW;
+    const int qi = (min(tq, NT - 1) * NH + min(yq, NH - 1)) * NW + min(xq, NW - 1);
 
     Nat<D> A;
     A.smem = smem;
@@ -375,18 +381,20 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     A.c_log2 = c_log2;
     A.kh = min(KH, NH);
     A.kw = min(KW, NW);
-    const int kt = min(KT, NT);
+    A.kt = min(KT, NT);
 
     // ---- workgroup key rows and the x range of the rows ------------------------
-    A.ts = win_start(tq, KT, NT);
+    A.ts = win_start(t0, KT, NT);
+    A.nt = win_start(min(t0 + kBrickT - 1, NT - 1), KT, NT) + A.kt - A.ts;
     A.ylo = win_start(y0, KH, NH);
     A.ny = win_start(min(y0 + kBrickY - 1, NH - 1), KH, NH) + A.kh - A.ylo;
-    A.n_rows = kt * A.ny;
+    A.n_rows = A.nt * A.ny;
     A.x0k = win_start(x0, KW, NW) & ~3;
     const int n_act = (A.n_rows + 1) / 2;  // steps of two key rows
     // this wave's 32-key block inside a row, and the lane's windows
     const int xw = min(x0 + 16 * (wave & 1), NW - 1);
     const int boff = min((win_start(xw, KW, NW) & ~3) - A.x0k, kRowKeys - 32);
+    A.ts_q = win_start(min(tq, NT - 1), KT, NT);
     A.ys_q = win_start(min(yq, NH - 1), KH, NH);
     const int xs_q = win_start(min(xq, NW - 1), KW, NW);
     A.xrel = A.x0k + boff + 8 * g - xs_q;
@@ -495,21 +503,22 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
 template <int D>
 hipError_t launch_t(const NattenArgs& a, hipStream_t stream) {
     using T = NTile<D>;
+    const int nbt = (a.NT + kBrickT - 1) / kBrickT;
     const int nby = (a.NH + kBrickY - 1) / kBrickY;
     const int nbx = (a.NW + kBrickX - 1) / kBrickX;
-    const int n_wg = a.B * a.H * a.NT * nby * nbx;
+    const int n_wg = a.B * a.H * nbt * nby * nbx;
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((natten_fwd_kernel<D>), dim3(n_wg), dim3(kThreads), (size_t)T::kRingBytes, stream,
                        reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                        reinterpret_cast<const __bf16*>(a.v), reinterpret_cast<__bf16*>(a.out), a.lse,
-                       a.NT, a.NH, a.NW, a.H, a.KT, a.KH, a.KW, c_log2, nby, nbx, n_wg);
+                       a.NT, a.NH, a.NW, a.H, a.KT, a.KH, a.KW, c_log2, nbt, nby, nbx, n_wg);
     return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t natten_workgroups(const NattenArgs& a) {
-    return (int64_t)a.B * a.H * a.NT * ((a.NH + kBrickY - 1) / kBrickY) *
+    return (int64_t)a.B * a.H * ((a.NT + kBrickT - 1) / kBrickT) * ((a.NH + kBrickY - 1) / kBrickY) *
            ((a.NW + kBrickX - 1) / kBrickX);
 }
 
