@@ -20,17 +20,18 @@
 //     (11 x 18);
 //   * the workgroup walks the key rows (t', y') in the union of its queries'
 //     windows -- t' in [start(t0), start(t0 + 1) + kt_eff), y' in
-//     [start(y0), start(y0 + 3) + kh_eff) -- two rows per step: a ring slot holds two rows
-//     of 48 consecutive x positions from X0 (the brick's first window start,
-//     rounded down to 4), which cover the x windows of all 32 brick columns;
+//     [start(y0), start(y0 + 3) + kh_eff) -- two rows per step: a ring slot
+//     holds two rows of 48 consecutive x positions from X0 (the brick's first
+//     window start, rounded down to 4), which cover the x windows of all 32
+//     brick columns;
 //   * each wave multiplies only the 32-key block of each row that holds its
 //     queries' x windows (they span at most 16 + kw_eff - 1 <= 28 keys from a
 //     4-aligned offset, so kw_eff <= 13), i.e. 16 K Q^T + 16 P V MFMAs per
 //     step at D = 128 -- the segment kernel's phase length, so the barrier
 //     and operand start-up of a phase are spread over the work of two rows;
 //   * element masks: key (t', y', x') is valid for a query iff t', y' and x'
-//     lie in its windows; invalid scores become -inf before the
-//     online softmax, which is the segment kernel's;
+//     lie in its windows; invalid scores become -inf before the online
+//     softmax, which is the segment kernel's;
 //   * copies, operand prefetch, ping-pong schedule and epilogue follow the
 //     segment-masked kernel.
 #include <hip/hip_runtime.h>
