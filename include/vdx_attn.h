@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define VDX_ABI_VERSION 3
+#define VDX_ABI_VERSION 4
 
 /* Status codes.  Argument validation runs before any HIP call, in the order
  * below (NULL -> segment pair -> shape -> head dim -> scale -> alignment),
@@ -161,10 +161,12 @@ int vdx_natten3d_fwd(const void* q, const void* k, const void* v, void* out, flo
  *   workspace device scratch of at least vdx_attn_bwd_workspace_size(B, S, H)
  *             bytes, 16-byte aligned, owned by the caller; its contents on
  *             entry do not matter and are overwritten (it holds per-row
- *             fp32 terms between the kernels of one call, so two calls in
+ *             fp32 terms and, with segment IDs, per-block work counts and
+ *             orders between the kernels of one call, so two calls in
  *             flight at once need two workspaces).
- *   stream    HIP stream; the three kernels are enqueued on it in order,
- *             asynchronous, no host synchronisation.
+ *   stream    HIP stream; the kernels (three, five with segment IDs) are
+ *             enqueued on it in order, asynchronous, no host
+ *             synchronisation.
  * Every pointer is a DEVICE pointer owned by the caller; the library
  * allocates nothing.  Validation runs before any HIP call, in the order
  * NULL (q, k, v, out, lse, dout, dq, dk, dv) -> segment pair -> shape (as for
@@ -182,9 +184,11 @@ int vdx_attn_bwd(const void* q, const void* k, const void* v,
                  void* workspace, size_t workspace_bytes,
                  int B, int S, int H, int D, float scale, hipStream_t stream);
 
-/* Bytes of workspace vdx_attn_bwd needs for (B, S, H): 8 * B * H * S rounded
- * up per (b, h) to a multiple of 64 rows.  0 if B, S or H < 1 or the size
- * overflows. */
+/* Bytes of workspace vdx_attn_bwd needs for (B, S, H): 8 * B * H * S_pad with
+ * S_pad = S rounded up to a multiple of 64 (two fp32 terms per row), plus
+ * 16 * B * ceil(S / 128) (per batch, the active-tile count and the
+ * longest-first rank of every 128-row block of both sweeps, used with
+ * segment IDs).  0 if B, S or H < 1 or the size overflows. */
 size_t vdx_attn_bwd_workspace_size(int B, int S, int H);
 
 /* Human-readable name of a status code (static storage; never NULL). */

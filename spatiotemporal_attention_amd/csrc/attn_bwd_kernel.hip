@@ -13,7 +13,7 @@
 // P is recomputed from the forward's log-sum-exp, so nothing of size S x S
 // is ever stored.
 //
-// Three kernels, all deterministic (no atomics):
+// Three kernels (five with segment IDs), all deterministic (no atomics):
 //   * prep: delta_i = dout_i . out_i in fp32 and lse2_i = lse_i log2(e)
 //     (+inf for rows without a valid key, and for the padding rows up to the
 //     next multiple of 64, so that their P is exactly 0) into a workspace;
@@ -27,6 +27,11 @@
 //   * dQ (query-major): a workgroup holds 128 queries, Q and dO slices in
 //     registers; it sweeps the key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T on
 //     the VALU, dQ^T += K^T dS^T.
+//   * with segment IDs, a count kernel classifies every row block of both
+//     sweeps as its sweep will (its active-tile count is its cost) and a rank
+//     kernel orders each batch's blocks longest-first, so that the CUs of an
+//     XCD, which take a head's blocks in that order, finish together; the
+//     order of the blocks changes no result.
 // Both sweeps stage their 64-row tiles in LDS by direct global->LDS DMA into
 // a ring.  One XOR swizzle of 16-byte chunks serves both operand reads of a
 // tile -- row reads (ds_read_b128, A operand of Q K^T-type products) and
@@ -518,7 +523,8 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                           const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
                           const float* __restrict__ ws_lse2, const float* __restrict__ ws_delta,
                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int S, int S_pad,
-                          int H, float c_log2, float scale, int n_blk, int n_qt, int n_wg) {
+                          int H, float c_log2, float scale, int n_blk, int n_qt, int n_wg,
+                          const int* __restrict__ ord) {
     using T = BTile<D>;
     using K = DkDv<D, SEG>;
     constexpr int kSlots = K::kSlots;
@@ -526,6 +532,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
     int blk, bh;
     wg_coords(n_blk, n_wg, blk, bh);
     const int h = bh % H, b = bh / H;
+    if (SEG) blk = ord[(int64_t)b * n_blk + blk];  // rank -> key block, longest first
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, g = lane >> 5;
@@ -703,13 +710,14 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
                         const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
                         const float* __restrict__ ws_lse2, const float* __restrict__ ws_delta,
                         __bf16* __restrict__ dq, int S, int S_pad, int H, float c_log2, float scale,
-                        int n_blk, int n_kt, int n_wg) {
+                        int n_blk, int n_kt, int n_wg, const int* __restrict__ ord) {
     using T = BTile<D>;
     constexpr int kSlots = 2;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     int blk, bh;
     wg_coords(n_blk, n_wg, blk, bh);
     const int h = bh % H, b = bh / H;
+    if (SEG) blk = ord[(int64_t)b * n_blk + blk];  // rank -> query block, longest first
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, g = lane >> 5;
@@ -936,6 +944,56 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__
     }
 }
 
+// ---- block order (segment IDs only) ----------------------------------------------
+// Active-tile count of every row block of both sweeps: workgroup
+// (b * n_blk + blk) * 2 + side classifies block blk of batch b -- key rows
+// against query tiles for side 0 (dK/dV), query rows against key tiles for
+// side 1 (dQ) -- exactly as that sweep does, and stores the count at
+// cnt[(side * B + b) * n_blk + blk].
+constexpr size_t count_lds(int n_tiles) {
+    return (((size_t)n_tiles + 15) & ~(size_t)15) + (((size_t)2 * n_tiles + 15) & ~(size_t)15) +
+           16 * sizeof(int);
+}
+__global__ __launch_bounds__(kBwdThreads) void attn_bwd_count_kernel(
+    const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv, int S, int B, int n_blk,
+    int n_tiles, int* __restrict__ cnt) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int side = blockIdx.x & 1;
+    const int blk = (blockIdx.x >> 1) % n_blk, b = (blockIdx.x >> 1) / n_blk;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int row = blk * kBwdRows + wave * 32 + (lane & 31);  // the sweeps' row of this lane
+    const int32_t* mine_ids = (side ? seg_q : seg_kv) + (int64_t)b * S;
+    const int32_t* other = (side ? seg_kv : seg_q) + (int64_t)b * S;
+    const int mine = (row < S) ? mine_ids[row] : 0;
+    const size_t o1 = ((size_t)n_tiles + 15) & ~(size_t)15;
+    const size_t o2 = o1 + (((size_t)2 * n_tiles + 15) & ~(size_t)15);
+    const int n = classify_tiles<kBwdWaves>(mine, other, S, n_tiles, reinterpret_cast<uint8_t*>(smem),
+                                            reinterpret_cast<uint16_t*>(smem + o1),
+                                            reinterpret_cast<int*>(smem + o2), wave, lane);
+    if (tid == 0) cnt[((int64_t)side * B + b) * n_blk + blk] = n;
+}
+
+// Longest-first order of the row blocks of one (side, batch), workgroup
+// side * B + b: ord[r] is the block with the r-th largest count, ties by
+// block index (a permutation of 0 .. n_blk - 1).
+constexpr int kRankThreads = 1024;
+__global__ __launch_bounds__(kRankThreads) void attn_bwd_rank_kernel(const int* __restrict__ cnt,
+                                                                    int* __restrict__ ord, int n_blk) {
+    extern __shared__ int c[];
+    const int64_t base = (int64_t)blockIdx.x * n_blk;
+    for (int i = threadIdx.x; i < n_blk; i += kRankThreads) c[i] = cnt[base + i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_blk; i += kRankThreads) {
+        const int ci = c[i];
+        int r = 0;
+        for (int j = 0; j < n_blk; ++j) r += (c[j] > ci) | ((c[j] == ci) & (j < i));
+        ord[base + r] = i;
+    }
+}
+static_assert(count_lds(kBwdMaxTiles) <= kLdsBytes && (size_t)(kBwdMaxTiles * 64 / kBwdRows) * sizeof(int) <= kLdsBytes,
+              "block-order scratch must fit in the LDS");
+
 template <int D>
 constexpr size_t dkdv_lds(bool seg, int n_tiles) {
     const size_t b = DkDv<D, false>::kSlots * (size_t)BTile<D>::kStage + (seg ? 2 * (size_t)n_tiles : 0);
@@ -974,16 +1032,30 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     const int n_blk = (a.S + kBwdRows - 1) / kBwdRows;
     const int n_tiles = (a.S + 63) / 64;
     const int n_wg = (int)((int64_t)a.B * a.H * n_blk);
+    // Block orders: counts [side][b][blk], then orders [side][b][rank]
+    // (side 0: key blocks of dK/dV, side 1: query blocks of dQ).
+    int* ws_cnt = reinterpret_cast<int*>(ws_delta + (int64_t)a.B * a.H * S_pad);
+    int* ws_ord = ws_cnt + 2 * (int64_t)a.B * n_blk;
+    if (SEG) {
+        hipLaunchKernelGGL(attn_bwd_count_kernel, dim3((unsigned)(2 * (int64_t)a.B * n_blk)), dim3(kBwdThreads),
+                           count_lds(n_tiles), stream, a.seg_q, a.seg_kv, a.S, a.B, n_blk, n_tiles, ws_cnt);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_bwd_rank_kernel, dim3((unsigned)(2 * a.B)), dim3(kRankThreads),
+                           (size_t)n_blk * sizeof(int), stream, ws_cnt, ws_ord, n_blk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, SEG>), dim3(n_wg), dim3(kBwdThreads),
                        dkdv_lds<D>(SEG, n_tiles), stream, q, k, v, dout, a.seg_q, a.seg_kv, ws_lse2,
                        ws_delta, reinterpret_cast<__bf16*>(a.dk), reinterpret_cast<__bf16*>(a.dv), a.S,
-                       S_pad, a.H, c_log2, a.scale, n_blk, n_tiles, n_wg);
+                       S_pad, a.H, c_log2, a.scale, n_blk, n_tiles, n_wg, ws_ord);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, SEG>), dim3(n_wg), dim3(kBwdThreads),
                        dq_lds<D>(SEG, n_tiles), stream, q, k, v, dout, a.seg_q, a.seg_kv, ws_lse2,
                        ws_delta, reinterpret_cast<__bf16*>(a.dq), a.S, S_pad, a.H, c_log2, a.scale,
-                       n_blk, n_tiles, n_wg);
+                       n_blk, n_tiles, n_wg, ws_ord + (int64_t)a.B * n_blk);
     return hipGetLastError();
 }
 
@@ -991,7 +1063,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t S, int64_t H) {
     const int64_t S_pad = (S + kPad - 1) / kPad * kPad;
-    return (size_t)(2 * B * H * S_pad) * sizeof(float);
+    const int64_t n_blk = (S + kBwdRows - 1) / kBwdRows;
+    return (size_t)(2 * B * H * S_pad) * sizeof(float) + (size_t)(4 * B * n_blk) * sizeof(int);
 }
 
 int64_t bwd_max_masked_seq() { return (int64_t)kBwdMaxTiles * 64; }

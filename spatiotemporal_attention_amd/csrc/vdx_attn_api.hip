@@ -157,7 +157,8 @@ __attribute__((visibility("default"))) int vdx_attn_bwd(
 
 __attribute__((visibility("default"))) size_t vdx_attn_bwd_workspace_size(int B, int S, int H) {
     if (B < 1 || S < 1 || H < 1 || S > INT32_MAX - 64) return 0;
-    const __int128 n = (__int128)B * H * (((int64_t)S + 63) / 64 * 64) * 8;
+    const __int128 n = (__int128)B * H * (((int64_t)S + 63) / 64 * 64) * 8 +
+                       (__int128)B * (((int64_t)S + 127) / 128) * 16;
     if (n > (__int128)INT64_MAX) return 0;
     return vdx::attn_bwd_workspace_bytes(B, S, H);
 }

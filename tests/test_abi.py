@@ -222,10 +222,11 @@ def bcall(native, q=A, k=A + 0x100, v=A + 0x200, sq=0, sk=0, out=A + 0x300, lse=
 
 
 def test_bwd_workspace_size(native):
-    # two fp32 rows per (b, h), S padded to a multiple of 64
-    assert native.attn_bwd_workspace_size(1, 75600, 40) == 2 * 40 * 75648 * 4
-    assert native.attn_bwd_workspace_size(2, 1, 3) == 2 * 6 * 64 * 4
-    assert native.attn_bwd_workspace_size(1, 64, 1) == 2 * 64 * 4
+    # two fp32 rows per (b, h), S padded to a multiple of 64, then per batch
+    # four int32 per 128-row block (counts and orders of both sweeps)
+    assert native.attn_bwd_workspace_size(1, 75600, 40) == 2 * 40 * 75648 * 4 + 4 * 591 * 4
+    assert native.attn_bwd_workspace_size(2, 1, 3) == 2 * 6 * 64 * 4 + 2 * 4 * 1 * 4
+    assert native.attn_bwd_workspace_size(1, 64, 1) == 2 * 64 * 4 + 4 * 1 * 4
     for bad in ((0, 1, 1), (1, 0, 1), (1, 1, 0), (1, 2**31 - 1, 1)):
         assert native.attn_bwd_workspace_size(*bad) == 0
 

@@ -245,7 +245,8 @@ def test_backward_kernels_wait_states_and_no_spills_in_loops(bwd_asm_text):
     assert n > 0
     assert lds_dma_hazards(bwd_asm_text) == []
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", bwd_asm_text)]
-    assert len(sizes) == 10  # prep x {64, 128}; dK/dV and dQ x {64, 128} x {unmasked, masked}
+    # prep x {64, 128}; dK/dV and dQ x {64, 128} x {unmasked, masked}; block count and rank
+    assert len(sizes) == 12
     assert max(sizes) <= 128
     for name, lines in _functions(bwd_asm_text).items():
         for h, b in _loops(lines):
