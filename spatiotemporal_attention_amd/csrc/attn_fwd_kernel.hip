@@ -70,6 +70,11 @@ struct Attn {
     int S, n_kvt, wave, lane, lr, g;
     float c_log2;
     int myseg;
+    // Active tile a - 1 of the next plan() call (group 0 plans tiles 0, 1,
+    // 2, ... in order): its index and partial flag, looked up by the
+    // previous call, so the segment-ID copy decision needs no second lookup.
+    int prev_t;
+    bool prev_part;
     // K operand of k-step ks sits at kx ^ (ks << 5) and the transposed V read
     // of d-block db at vx ^ (db << 6) (offsets within a ring slot): the XOR
     // swizzles only touch bits that these bases hold no other data in.
@@ -116,7 +121,8 @@ struct Attn {
     // ---- tile copies ---------------------------------------------------------------
     // In its MFMA phase of local iteration n, a wave of group G copies its share
     // of K (G = 0) or V (G = 1) of active tile a = n + 2 - G into ring slot
-    // a % 3, and wave 0 of group 0 copies the segment IDs of active tile n + 1.
+    // a % 3, and wave 0 of group 0 copies the segment IDs of active tile n + 1
+    // if that tile is partial.
     // In global-phase terms (the MFMA phase of iteration n is phase 2n + G):
     // K of tile m+2 and segment IDs of tile m+1 in phase 2m, V of tile m+1 in
     // phase 2m+1.  Slot a % 3 then held tile a-3, whose last reader finished
@@ -137,6 +143,12 @@ struct Attn {
     template <int G>
     __device__ __forceinline__ void plan(Copy& c, int a, int n_act) {
         bool part;
+        int pt = 0;
+        bool pp = false;
+        if constexpr (SEG && G == 0) {
+            pt = prev_t;
+            pp = prev_part;
+        }
         c.cnt = 0;
         c.spread = c.tail = false;
         c.seg_a = -1;
@@ -148,10 +160,15 @@ struct Attn {
             c.spread = c.t * kBk + kBk <= S;
             c.tail = !c.spread;
             c.cnt = T::kLoadsPerWave;
+            if constexpr (SEG && G == 0) {
+                prev_t = c.t;
+                prev_part = part;
+            }
         }
-        if (SEG && G == 0 && w4 == 0 && a >= 1 && a - 1 < n_act) {
+        // Only a partial tile's masks read its segment IDs.
+        if (SEG && G == 0 && w4 == 0 && a >= 1 && a - 1 < n_act && pp) {
             c.seg_a = a - 1;
-            c.seg_t = tile_of(a - 1, part);
+            c.seg_t = pt;
             c.cnt += 1;
         }
     }
@@ -490,6 +507,10 @@ __device__ __forceinline__ void attn_fwd_item(
 
     // ---- prologue: K of tiles 0 and 1, segment IDs of tile 0 (group 0), V of
     // tile 0 (group 1) ---------------------------------------------------------------
+    if (SEG) {
+        A.prev_t = 0;
+        A.prev_part = false;
+    }
     {
         typename Attn<D, SEG>::Copy c;
         if (grp == 0) {
