@@ -162,7 +162,7 @@ def natten_window_volume(w) -> int:
 
 
 def natten_executed_flop(w) -> float:
-    """MFMA flops the kernel issues: per workgroup (a 2x4x32 (t, y, x) query
+    """MFMA flops the kernel issues: per workgroup (a 4x2x32 (t, y, x) query
     brick) one step per two key rows of its window union (an odd row count
     adds a masked row), each row 8 waves x 32 queries x 32 keys x 2 products
     x 2*D."""
@@ -177,10 +177,10 @@ def natten_executed_flop(w) -> float:
         return start(min(c0 + brick - 1, n - 1), k, n) + min(k, n) - start(c0, k, n)
 
     rows = 0
-    for t0 in range(0, NT, 2):
-        nt = span(t0, 2, KT, NT)
-        for y0 in range(0, NH, 4):
-            rows += 2 * ((nt * span(y0, 4, KH, NH) + 1) // 2)
+    for t0 in range(0, NT, 4):
+        nt = span(t0, 4, KT, NT)
+        for y0 in range(0, NH, 2):
+            rows += 2 * ((nt * span(y0, 2, KH, NH) + 1) // 2)
     rows *= (NW + 31) // 32
     return float(rows) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
 

@@ -12,15 +12,15 @@
 //
 // Design (same machinery as the segment-masked kernel):
 //   * one workgroup = 8 wave64s (two per SIMD, two ping-pong groups) and a
-//     2 x 4 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
-//     sub-brick of frame t0 + (w >> 2) at y offset 2((w >> 1) & 1), x offset
-//     16(w & 1), lane lr the query (lr >> 4, lr & 15) of it -- two frames by
-//     four rows, because a brick's window union (12 x 14 key rows for 11^3
-//     windows) then holds fewer rows per query than one frame by eight rows
-//     (11 x 18);
+//     4 x 2 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
+//     sub-brick of frame t0 + (w >> 1) at x offset 16(w & 1), lane lr the
+//     query (lr >> 4, lr & 15) of it -- four frames by two rows, because a
+//     brick's window union (14 x 12 key rows for 11^3 windows) then holds
+//     fewer rows per query than one frame by eight rows (11 x 18), and fewer
+//     still where the windows clip at the t borders;
 //   * the workgroup walks the key rows (t', y') in the union of its queries'
-//     windows -- t' in [start(t0), start(t0 + 1) + kt_eff), y' in
-//     [start(y0), start(y0 + 3) + kh_eff) -- two rows per step: a ring slot
+//     windows -- t' in [start(t0), start(t0 + 3) + kt_eff), y' in
+//     [start(y0), start(y0 + 1) + kh_eff) -- two rows per step: a ring slot
 //     holds two rows of 48 consecutive x positions from X0 (the brick's first
 //     window start, rounded down to 4), which cover the x windows of all 32
 //     brick columns;
@@ -43,14 +43,21 @@
 namespace vdx {
 namespace {
 
+// k-th of n positions counted from the middle outward (a permutation of
+// 0 .. n-1): middle first, then alternately one step further down and up.
+__device__ __forceinline__ int center_out(int k, int n) {
+    if ((n & 1) == 0) return (k & 1) ? n / 2 + k / 2 : n / 2 - 1 - k / 2;
+    return (k & 1) ? n / 2 - (k + 1) / 2 : n / 2 + k / 2;
+}
+
 // First window position along an axis of length n for coordinate c.
 __device__ __forceinline__ int win_start(int c, int k, int n) {
     const int keff = min(k, n);
     return min(max(c - k / 2, 0), n - keff);
 }
 
-constexpr int kBrickT = 2;    // query frames per workgroup (one per ping-pong group)
-constexpr int kBrickY = 4;    // query rows per workgroup
+constexpr int kBrickT = 4;    // query frames per workgroup (two per ping-pong group)
+constexpr int kBrickY = 2;    // query rows per workgroup
 constexpr int kBrickX = 32;   // query columns per workgroup
 constexpr int kRowKeys = 48;  // keys of one key row held in LDS
 
@@ -340,19 +347,19 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     // XCD-contiguous renumbering: consecutive bricks of one head share an L2.
-    // Within a head the y-brick index varies slowest, interior bricks first:
-    // the first and last y-bricks (windows clipped at the border, or a
-    // partial brick) walk fewer key rows, and dispatching the long bricks
-    // before the short ones lets the CUs of an XCD finish together.
+    // Within a head the bricks go longest first: a brick walks fewer key rows
+    // the nearer it lies to a t or y border (windows clipped there, or a
+    // partial brick), so the frame-brick index runs from the middle outward
+    // (slowest), then the row-brick index from the middle outward, and the
+    // CUs of an XCD, dealt the bricks in that order, finish together.
     const int w = blockIdx.x;
     const int per = n_wg / kXcds, rem = n_wg % kXcds;
     const int xcd = w % kXcds;
     const int lid = xcd * per + min(xcd, rem) + w / kXcds;
     const int bx = lid % nbx;
-    const int bt = (lid / nbx) % nbt;
-    const int byi = (lid / (nbx * nbt)) % nby;
-    const int by = nby < 3 ? byi : (byi < nby - 2 ? byi + 1 : (byi == nby - 2 ? 0 : nby - 1));
-    const int bh = lid / (nbx * nbt * nby);
+    const int by = center_out((lid / nbx) % nby, nby);
+    const int bt = center_out((lid / (nbx * nby)) % nbt, nbt);
+    const int bh = lid / (nbx * nby * nbt);
     const int h = bh % H;
     const int b = bh / H;
     const int S = NT * NH * NW;
@@ -362,8 +369,8 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const int lr = lane & 31, g = lane >> 5;
     const int grp = wave >> 2;
     const int t0 = bt * kBrickT, y0 = by * kBrickY, x0 = bx * kBrickX;
-    const int tq = t0 + grp;
-    const int yq = y0 + 2 * ((wave >> 1) & 1) + (lr >> 4);
+    const int tq = t0 + (wave >> 1);
+    const int yq = y0 + (lr >> 4);
     const int xq = x0 + 16 * (wave & 1) + (lr & 15);
     const bool active = tq < NT && yq < NH && xq < NW;
     const int qi = (min(tq, NT - 1) * NH + min(yq, NH - 1)) * NW + min(xq, NW - 1);

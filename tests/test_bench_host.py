@@ -57,10 +57,10 @@ def test_natten_counts():
     w = W.NATTEN_WORKLOADS["natten_vae_decoder"]
     # every query sees the full 11^3 window (it shifts inward at the borders)
     assert bench.natten_window_volume(w) == 11 ** 3
-    # 8 heads x 9,384 two-row steps per head (2x4x32 bricks walk up to 12
-    # frames x 14 key rows, fewer where windows clip at the borders), each
+    # 8 heads x 8,952 two-row steps per head (4x2x32 bricks walk up to 14
+    # frames x 12 key rows, fewer where windows clip at the borders), each
     # step 2 rows x 8 waves x 32 queries x 32 keys x 2 products x 2 D
-    assert bench.natten_executed_flop(w) == pytest.approx(8 * 9384 * 2 * 8 * 32 * 32 * 4 * 128, rel=0)
+    assert bench.natten_executed_flop(w) == pytest.approx(8 * 8952 * 2 * 8 * 32 * 32 * 4 * 128, rel=0)
 
 
 def test_traffic_served_only_for_matching_sources(tmp_path, monkeypatch):
