@@ -60,6 +60,9 @@ constexpr int kBrickT = 4;    // query frames per workgroup (two per ping-pong g
 constexpr int kBrickY = 2;    // query rows per workgroup
 constexpr int kBrickX = 32;   // query columns per workgroup
 constexpr int kRowKeys = 48;  // keys of one key row held in LDS
+// MFMA operands in flight (the segment kernel keeps 4; here 3 timed about 1%
+// faster and 5 or 6 no better).
+constexpr int kNatPrefetch = 3;
 
 // LDS ring of the neighbourhood kernel: kSlots slots of K and of V, each two
 // key rows of kRowKeys keys (slot rows 0..47 and 48..95), with the K and V
@@ -89,7 +92,7 @@ struct Nat {
     using T = NTile<D>;
     static constexpr int kQk = 2 * T::kSteps;     // K Q^T MFMAs per step (two rows)
     static constexpr int kPv = 4 * T::kDBlocks;   // P V MFMAs per step (two rows x two 16-key halves)
-    static constexpr int kRing = kOperandPrefetch + 2;
+    static constexpr int kRing = kNatPrefetch + 2;
 
     char* smem;
     const __bf16* kp;  // K of (b, h), token 0
@@ -199,7 +202,7 @@ struct Nat {
         vb_next = vbase(vstep);
         kb_next[0] = kbase(kstep, 0);
         kb_next[1] = kbase(kstep, 1);
-        static_for<0, kOperandPrefetch>([&](auto ic) {
+        static_for<0, kNatPrefetch>([&](auto ic) {
             constexpr int i = ic;
             if constexpr (i < NM) ops[i % kRing] = operand<QK, i>(vb_next, kb_next[0], kb_next[1]);
         });
@@ -207,7 +210,7 @@ struct Nat {
     template <bool PV, bool QK, bool PRE>
     __device__ __forceinline__ void mfma_phase(int vstep, int kstep, const Copy& cp) {
         constexpr int NM = (QK ? kQk : 0) + (PV ? kPv : 0);
-        constexpr int PF = kOperandPrefetch;
+        constexpr int PF = kNatPrefetch;
         __builtin_amdgcn_s_setprio(1);
         if constexpr (!PRE) prefetch<PV, QK>(vstep, kstep);
         const uint32_t vb = vb_next, kb0 = kb_next[0], kb1 = kb_next[1];
