@@ -161,13 +161,28 @@ def natten_window_volume(w) -> int:
     return math.prod(min(k, n) for k, n in zip(w.window, w.grid))
 
 
+def natten_brick_frames(NT, NH, KT, KH) -> int:
+    """Frames per query brick the kernel picks (its brick is BT x 8/BT x 32):
+    the fewest window-union key rows per query row, ties to more frames."""
+    kt, kh = min(KT, NT), min(KH, NH)
+    best, best_rows, best_q = 1, 0, 1
+    for bt in (1, 2, 4):
+        by = 8 // bt
+        rows = min(bt + kt - 1, NT) * min(by + kh - 1, NH)
+        q = min(bt, NT) * min(by, NH)
+        if bt == 1 or rows * best_q <= best_rows * q:
+            best, best_rows, best_q = bt, rows, q
+    return best
+
+
 def natten_executed_flop(w) -> float:
-    """MFMA flops the kernel issues: per workgroup (a 4x2x32 (t, y, x) query
-    brick) one step per two key rows of its window union (an odd row count
-    adds a masked row), each row 8 waves x 32 queries x 32 keys x 2 products
-    x 2*D."""
+    """MFMA flops the kernel issues: per workgroup (a BT x 8/BT x 32 (t, y, x)
+    query brick) one step per two key rows of its window union (an odd row
+    count adds a masked row), each row 8 waves x 32 queries x 32 keys x 2
+    products x 2*D."""
     NT, NH, NW = w.grid
     KT, KH, KW = w.window
+    bt, by = natten_brick_frames(NT, NH, KT, KH), 8 // natten_brick_frames(NT, NH, KT, KH)
 
     def start(c, k, n):
         ke = min(k, n)
@@ -177,10 +192,10 @@ def natten_executed_flop(w) -> float:
         return start(min(c0 + brick - 1, n - 1), k, n) + min(k, n) - start(c0, k, n)
 
     rows = 0
-    for t0 in range(0, NT, 4):
-        nt = span(t0, 4, KT, NT)
-        for y0 in range(0, NH, 2):
-            rows += 2 * ((nt * span(y0, 2, KH, NH) + 1) // 2)
+    for t0 in range(0, NT, bt):
+        nt = span(t0, bt, KT, NT)
+        for y0 in range(0, NH, by):
+            rows += 2 * ((nt * span(y0, by, KH, NH) + 1) // 2)
     rows *= (NW + 31) // 32
     return float(rows) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
 

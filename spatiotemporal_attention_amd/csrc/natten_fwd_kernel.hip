@@ -12,15 +12,15 @@
 //
 // Design (same machinery as the segment-masked kernel):
 //   * one workgroup = 8 wave64s (two per SIMD, two ping-pong groups) and a
-//     4 x 2 x 32 (t, y, x) brick of queries; wave w owns the 2 x 16 (y, x)
-//     sub-brick of frame t0 + (w >> 1) at x offset 16(w & 1), lane lr the
-//     query (lr >> 4, lr & 15) of it -- four frames by two rows, because a
-//     brick's window union (14 x 12 key rows for 11^3 windows) then holds
-//     fewer rows per query than one frame by eight rows (11 x 18), and fewer
-//     still where the windows clip at the t borders;
+//     BT x (8 / BT) x 32 (t, y, x) brick of queries, BT in {1, 2, 4} chosen
+//     per call (brick_frames): the shape whose window union holds the fewest
+//     key rows per query row -- 4 x 2 for 11^3 windows (14 x 12 key rows
+//     against 11 x 18 for 1 x 8), 1 x 8 for single frames or 1-frame t
+//     windows; wave w owns the 2 x 16 (y, x) sub-brick of wave-row w >> 1 at
+//     x offset 16(w & 1), lane lr the query (lr >> 4, lr & 15) of it;
 //   * the workgroup walks the key rows (t', y') in the union of its queries'
-//     windows -- t' in [start(t0), start(t0 + 3) + kt_eff), y' in
-//     [start(y0), start(y0 + 1) + kh_eff) -- two rows per step: a ring slot
+//     windows -- t' in [start(t0), start(t0 + BT - 1) + kt_eff), y' in
+//     [start(y0), start(y0 + BY - 1) + kh_eff) -- two rows per step: a ring slot
 //     holds two rows of 48 consecutive x positions from X0 (the brick's first
 //     window start, rounded down to 4), which cover the x windows of all 32
 //     brick columns;
@@ -36,6 +36,8 @@
 //     segment-masked kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "attn_common.h"
 #include "attn_fwd_launch.h"
@@ -56,13 +58,34 @@ __device__ __forceinline__ int win_start(int c, int k, int n) {
     return min(max(c - k / 2, 0), n - keff);
 }
 
-constexpr int kBrickT = 4;    // query frames per workgroup (two per ping-pong group)
-constexpr int kBrickY = 2;    // query rows per workgroup
-constexpr int kBrickX = 32;   // query columns per workgroup
+constexpr int kBrickRows = 8;  // query (t, y) rows per workgroup: BT frames x 8 / BT rows
+constexpr int kBrickX = 32;    // query columns per workgroup
 constexpr int kRowKeys = 48;  // keys of one key row held in LDS
 // MFMA operands in flight (the segment kernel keeps 4; here 3 timed about 1%
 // faster and 5 or 6 no better).
 constexpr int kNatPrefetch = 3;
+
+// Frames per brick, BT in {1, 2, 4} (the brick is BT x 8/BT x 32 queries):
+// the shape whose interior window union, min(BT + kt - 1, NT) frames x
+// min(8/BT + kh - 1, NH) rows, is smallest per query row of the brick; on a
+// tie the one with more frames (its union shrinks more where windows clip at
+// the t borders).
+int brick_frames(int NT, int NH, int KT, int KH) {
+    const int64_t kt = std::min(KT, NT), kh = std::min(KH, NH);
+    int best = 1;
+    int64_t best_rows = 0, best_q = 1;
+    for (int bt = 1; bt <= 4; bt *= 2) {
+        const int64_t by = kBrickRows / bt;
+        const int64_t rows = std::min<int64_t>(bt + kt - 1, NT) * std::min<int64_t>(by + kh - 1, NH);
+        const int64_t q = std::min<int64_t>(bt, NT) * std::min<int64_t>(by, NH);
+        if (bt == 1 || rows * best_q <= best_rows * q) {
+            best = bt;
+            best_rows = rows;
+            best_q = q;
+        }
+    }
+    return best;
+}
 
 // LDS ring of the neighbourhood kernel: kSlots slots of K and of V, each two
 // key rows of kRowKeys keys (slot rows 0..47 and 48..95), with the K and V
@@ -345,7 +368,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ out, float* __restrict__ lse, int NT, int NH, int NW, int H, int KT, int KH,
-    int KW, float c_log2, int nbt, int nby, int nbx, int n_wg) {
+    int KW, float c_log2, int bft, int nbt, int nby, int nbx, int n_wg) {
     using T = NTile<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -371,9 +394,12 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, g = lane >> 5;
     const int grp = wave >> 2;
-    const int t0 = bt * kBrickT, y0 = by * kBrickY, x0 = bx * kBrickX;
-    const int tq = t0 + (wave >> 1);
-    const int yq = y0 + (lr >> 4);
+    // bft frames x bfy rows; wave-row r = wave >> 1 is row pair r % (bfy / 2)
+    // of frame r / (bfy / 2)
+    const int bfy = kBrickRows / bft, pairs = bfy / 2;
+    const int t0 = bt * bft, y0 = by * bfy, x0 = bx * kBrickX;
+    const int tq = t0 + (wave >> 1) / pairs;
+    const int yq = y0 + 2 * ((wave >> 1) % pairs) + (lr >> 4);
     const int xq = x0 + 16 * (wave & 1) + (lr & 15);
     const bool active = tq < NT && yq < NH && xq < NW;
     const int qi = (min(tq, NT - 1) * NH + min(yq, NH - 1)) * NW + min(xq, NW - 1);
@@ -396,9 +422,9 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
 
     // ---- workgroup key rows and the x range of the rows ------------------------
     A.ts = win_start(t0, KT, NT);
-    A.nt = win_start(min(t0 + kBrickT - 1, NT - 1), KT, NT) + A.kt - A.ts;
+    A.nt = win_start(min(t0 + bft - 1, NT - 1), KT, NT) + A.kt - A.ts;
     A.ylo = win_start(y0, KH, NH);
-    A.ny = win_start(min(y0 + kBrickY - 1, NH - 1), KH, NH) + A.kh - A.ylo;
+    A.ny = win_start(min(y0 + bfy - 1, NH - 1), KH, NH) + A.kh - A.ylo;
     A.n_rows = A.nt * A.ny;
     A.x0k = win_start(x0, KW, NW) & ~3;
     const int n_act = (A.n_rows + 1) / 2;  // steps of two key rows
@@ -514,22 +540,24 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
 template <int D>
 hipError_t launch_t(const NattenArgs& a, hipStream_t stream) {
     using T = NTile<D>;
-    const int nbt = (a.NT + kBrickT - 1) / kBrickT;
-    const int nby = (a.NH + kBrickY - 1) / kBrickY;
+    const int bft = brick_frames(a.NT, a.NH, a.KT, a.KH), bfy = kBrickRows / bft;
+    const int nbt = (a.NT + bft - 1) / bft;
+    const int nby = (a.NH + bfy - 1) / bfy;
     const int nbx = (a.NW + kBrickX - 1) / kBrickX;
     const int n_wg = a.B * a.H * nbt * nby * nbx;
     const float c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((natten_fwd_kernel<D>), dim3(n_wg), dim3(kThreads), (size_t)T::kRingBytes, stream,
                        reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                        reinterpret_cast<const __bf16*>(a.v), reinterpret_cast<__bf16*>(a.out), a.lse,
-                       a.NT, a.NH, a.NW, a.H, a.KT, a.KH, a.KW, c_log2, nbt, nby, nbx, n_wg);
+                       a.NT, a.NH, a.NW, a.H, a.KT, a.KH, a.KW, c_log2, bft, nbt, nby, nbx, n_wg);
     return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t natten_workgroups(const NattenArgs& a) {
-    return (int64_t)a.B * a.H * ((a.NT + kBrickT - 1) / kBrickT) * ((a.NH + kBrickY - 1) / kBrickY) *
+    const int bft = brick_frames(a.NT, a.NH, a.KT, a.KH), bfy = kBrickRows / bft;
+    return (int64_t)a.B * a.H * ((a.NT + bft - 1) / bft) * ((a.NH + bfy - 1) / bfy) *
            ((a.NW + kBrickX - 1) / kBrickX);
 }
 

@@ -57,6 +57,9 @@ def test_natten_counts():
     w = W.NATTEN_WORKLOADS["natten_vae_decoder"]
     # every query sees the full 11^3 window (it shifts inward at the borders)
     assert bench.natten_window_volume(w) == 11 ** 3
+    assert bench.natten_brick_frames(16, 32, 11, 11) == 4   # 14 x 12 rows beat 11 x 18
+    assert bench.natten_brick_frames(1, 32, 11, 11) == 1    # single frame: 1 x 8 bricks
+    assert bench.natten_brick_frames(16, 32, 1, 11) == 1    # 1-frame t window
     # 8 heads x 8,952 two-row steps per head (4x2x32 bricks walk up to 14
     # frames x 12 key rows, fewer where windows clip at the borders), each
     # step 2 rows x 8 waves x 32 queries x 32 keys x 2 products x 2 D
