@@ -9,7 +9,10 @@ workgroups with ragged tails, every segment layout of the forward sweep, and
 D = 64 / 128.  The 720p DiT shape (B=1, S=75,600, H=40, D=128) is compared on
 sampled dq rows and, on every row, against the closed forms of q = 0 and
 k = 0; the packed-clips shape (S=61,440, H=16) on a whole clip computed by
-the oracle as its own sequence (clips are independent) and on sampled dq rows.
+the oracle as its own sequence (clips are independent) and on sampled dq rows;
+the padded joint video+text shape (B=2, S=17,920, H=24) on sampled dq rows
+of both batch rows and, with k = 0, every dk and dv row against the closed
+form over its valid tokens.
 
 Tolerances for a gradient g (bf16) against the oracle o (fp64):
   |g - o| <= 2 * BF16_U * t + BF16_U * |o| + G_ATOL    element by element
@@ -268,6 +271,57 @@ def test_packed_clips_whole_clip_and_sampled_rows(need_gpu):
     for n, gi in zip(("dq", "dk", "dv"), (dq, dk, dv)):
         assert torch.count_nonzero(gi[0, pad].float()) == 0, n
     print(_dq_rows_check(x, dout, seg, w.scale, dq, heads=(0, 15), n_rows=24, seed=2))
+
+
+def test_joint_video_text_padding_full_size(need_gpu):
+    """Joint video+text layer with padding (B=2, S=17,920, H=24, one segment
+    of 17,776 tokens and 144 pad tokens in each batch row).  Random inputs:
+    dq on sampled rows of both batch rows (pad rows among them) against the
+    row oracle, and pad tokens exactly 0 in dq, dk and dv.  Then k = 0, so P
+    is uniform over the valid keys: dq must be exactly 0, and every row of dk
+    and dv is compared with the closed form over the valid tokens
+    (dk_j = scale (sum_i q_i dout_i^T / n)(v_j - vbar), dv_j = mean_i dout_i,
+    sums and means over the n valid tokens)."""
+    w = W.WORKLOADS["joint_video_text_pad"]
+    x = W.make_inputs(w)
+    seg = x["seg_q"]
+    dout = W.randn_bf16((w.B, w.S, w.H, w.D), 3007)
+    print(f"case {w.name}: bwd sampled dq rows, both batch rows", flush=True)
+    dq, dk, dv = run_gpu_bwd(x, dout, seg, x["seg_kv"], w.scale)
+    rng = np.random.default_rng(3)
+    idx = sorted({0, 127, 128, 17549, 17550, 17775, 17776, w.S - 1}
+                 | set(int(i) for i in rng.choice(w.S, 16, replace=False)))
+    rows = np.array([(b, h, i) for b in range(w.B) for h in (0, 23) for i in idx], dtype=np.int64)
+    o, t = oracle.attn_bwd_dq_rows(W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"]),
+                                   W.bf16_bits(dout), seg.numpy(), x["seg_kv"].numpy(),
+                                   float(np.float32(w.scale)), rows, sensitivity=True)
+    dead = ~valid_rows(seg, seg, w.B, w.S)[rows[:, 0], rows[:, 2]]
+    assert dead.sum() == 2 * 2 * 2  # rows 17776 and S-1 of both heads and batch rows
+    print(check_grad("dq rows", dq[rows[:, 0], rows[:, 2], rows[:, 1]], o, dead, t), flush=True)
+    pad = seg[0] == 0
+    for n, gi in zip(("dq", "dk", "dv"), (dq, dk, dv)):
+        assert torch.count_nonzero(gi[:, pad].float()) == 0, n
+        assert torch.isfinite(gi.float()).all(), n
+
+    print(f"case {w.name}: bwd k=0 closed form over the valid tokens", flush=True)
+    x["k"] = torch.zeros_like(x["k"])
+    dq, dk, dv = run_gpu_bwd(x, dout, seg, x["seg_kv"], w.scale)
+    assert torch.count_nonzero(dq.float()) == 0, "dq must be exactly 0"
+    scale = float(np.float32(w.scale))
+    ok = ~pad
+    n = int(ok.sum())
+    for b in range(w.B):
+        for h in range(w.H):
+            q = x["q"][b, ok, h].double().numpy()
+            v = x["v"][b, ok, h].double().numpy()
+            do = dout[b, ok, h].double().numpy()
+            gk = scale * (v - v.mean(0)) @ (q.T @ do / n).T
+            gv = np.broadcast_to(do.mean(0), do.shape)
+            check_grad("dk", dk[b, ok, h], gk)
+            check_grad("dv", dv[b, ok, h], gv)
+        print(f"  batch row {b}: {w.H} heads ok", flush=True)
+    for n_, gi in zip(("dk", "dv"), (dk, dv)):
+        assert torch.count_nonzero(gi[:, pad].float()) == 0, n_
 
 
 def test_masked_maximum_sequence(need_gpu):
