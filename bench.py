@@ -57,6 +57,9 @@ KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
                       for f in ("attn_bwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
                                 "vdx_attn_api.hip")]
+NATTEN_KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
+                         for f in ("natten_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
+                                   "vdx_attn_api.hip")]
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -93,18 +96,24 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
 
 
 def load_traffic(workload: str, pass_: str = "fwd"):
-    """HBM bytes per launch (forward) or per call (backward: its three kernels)
-    from the committed rocprofv3 counter summary, or None when the summary is
-    missing or was taken on different kernel source."""
-    path = os.path.join(COUNTERS_DIR, f"attn_{pass_}_{workload}_hbm_counters.json")
+    """HBM bytes per launch (forward, neighbourhood forward) or per call
+    (backward: its three kernels) from the committed rocprofv3 counter
+    summary, or None when the summary is missing or was taken on different
+    kernel source.  pass_ is "fwd", "bwd" or "natten"."""
+    prefix, sources, key = {
+        "fwd": ("attn_fwd", KERNEL_SOURCES, "traffic_bytes_per_launch"),
+        "bwd": ("attn_bwd", BWD_KERNEL_SOURCES, "traffic_bytes_per_call"),
+        "natten": ("natten_fwd", NATTEN_KERNEL_SOURCES, "traffic_bytes_per_launch"),
+    }[pass_]
+    name = workload.removeprefix("natten_") if pass_ == "natten" else workload
+    path = os.path.join(COUNTERS_DIR, f"{prefix}_{name}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         doc = json.load(f)
-    sources = KERNEL_SOURCES if pass_ == "fwd" else BWD_KERNEL_SOURCES
     if doc.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
-    return doc.get("traffic_bytes_per_launch" if pass_ == "fwd" else "traffic_bytes_per_call")
+    return doc.get(key)
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -369,7 +378,7 @@ def natten_main(args, vdx):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "executed_achieved": round(executed / (kernel_ms * 1e-3) / 1e12, 2),
-                     "traffic": None,
+                     "traffic": load_traffic(w.name, "natten"),
                      "algorithmic_bytes": 4 * 2 * n + 4 * w.B * w.H * w.S,
                      "kernel_ms_mean": round(kernel_ms, 4)},
     }

@@ -76,6 +76,14 @@ def test_traffic_served_only_for_matching_sources(tmp_path, monkeypatch):
     (tmp_path / "attn_fwd_dit720p_large_hbm_counters.json").write_text(json.dumps(doc))
     assert bench.load_traffic("dit720p_large") is None
     assert bench.load_traffic("packed_clips") is None  # no summary for it
+    # the neighbourhood kernel's summary is keyed on its own sources
+    doc = {"kernel_source_sha256": bench.kernel_source_hash(bench.NATTEN_KERNEL_SOURCES),
+           "traffic_bytes_per_launch": 456}
+    (tmp_path / "natten_fwd_vae_decoder_hbm_counters.json").write_text(json.dumps(doc))
+    assert bench.load_traffic("natten_vae_decoder", "natten") == 456
+    doc["kernel_source_sha256"] = bench.kernel_source_hash()
+    (tmp_path / "natten_fwd_vae_decoder_hbm_counters.json").write_text(json.dumps(doc))
+    assert bench.load_traffic("natten_vae_decoder", "natten") is None
 
 
 def test_more_than_one_gpu_is_refused():
