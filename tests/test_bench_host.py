@@ -92,3 +92,49 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _counter_docs():
+    import glob
+    import json
+    return [(os.path.basename(p), json.load(open(p)))
+            for p in sorted(glob.glob(os.path.join(bench.COUNTERS_DIR, "*_hbm_counters.json")))]
+
+
+@pytest.mark.parametrize("name,doc", _counter_docs(), ids=[n for n, _ in _counter_docs()])
+def test_counter_summaries_are_consistent(name, doc):
+    """Each committed FETCH_SIZE/WRITE_SIZE summary: the copy calibration gives
+    its scale factors, the per-launch bytes are the per-dispatch KiB times
+    1024 times those factors, the traffic is their sum, the algorithmic bytes
+    are bench.py's, and the stored commands run committed files only."""
+    cal = doc["copy_calibration"]
+    copy_kib = cal["copy_bytes"] / 1024
+    assert cal["fetch_factor"] == pytest.approx(copy_kib / cal["fetch_size_kib"], rel=1e-3)
+    assert cal["write_factor"] == pytest.approx(copy_kib / cal["write_size_kib"], rel=1e-3)
+    if "kernels" in doc:  # backward: every kernel of a call
+        fb = sum(k["fetch_bytes"] for k in doc["kernels"].values())
+        wb = sum(k["write_bytes"] for k in doc["kernels"].values())
+        for k in doc["kernels"].values():  # the KiB figures are stored to 0.1 KiB
+            for c in ("fetch", "write"):
+                f = cal[c + "_factor"]
+                assert k[c + "_bytes"] == pytest.approx(k[c + "_size_kib_per_dispatch"] * 1024 * f,
+                                                        rel=1e-6, abs=0.06 * 1024 * f)
+        assert doc["traffic_bytes_per_call"] == pytest.approx(fb + wb, rel=1e-9)
+        wl = name[len("attn_bwd_"):-len("_hbm_counters.json")]
+        w = W.WORKLOADS[wl]
+        n = w.B * w.S * w.H * w.D
+        assert doc["algorithmic_bytes_per_call"] == 2 * 8 * n + 4 * w.B * w.H * w.S
+    else:
+        fb = doc["fetch_size_kib_per_dispatch"] * 1024 * cal["fetch_factor"]
+        wb = doc["write_size_kib_per_dispatch"] * 1024 * cal["write_factor"]
+        assert doc["traffic_bytes_per_launch"] == pytest.approx(fb + wb, rel=1e-6)
+        if name.startswith("natten_fwd_"):
+            w = W.NATTEN_WORKLOADS["natten_" + name[len("natten_fwd_"):-len("_hbm_counters.json")]]
+            n = w.B * w.S * w.H * w.D
+            assert doc["algorithmic_bytes_per_launch"] == 4 * 2 * n + 4 * w.B * w.H * w.S
+        else:
+            w = W.WORKLOADS[name[len("attn_fwd_"):-len("_hbm_counters.json")]]
+            assert doc["algorithmic_bytes_per_launch"] == bench.algorithmic_bytes(w)
+    for c in doc["commands"]:
+        assert "rocprofv3 --pmc" in c and "-- python3 /root/repo/bench.py" in c
+        assert "_work" not in c
