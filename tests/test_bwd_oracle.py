@@ -52,7 +52,8 @@ def torch_grads(x, dout, seg, scale):
     return f(q), f(k), f(v)
 
 
-@pytest.mark.parametrize("kind", [None, "single", "padded", "packed", "interleaved", "allpad"])
+@pytest.mark.parametrize("kind", [None, "single", "padded", "packed", "interleaved", "allpad", "negative",
+                                  "extreme"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_matches_torch_autograd_f64(kind, D):
     B, S, H = 2, 48, 2
@@ -229,3 +230,96 @@ def test_dq_rows_sensitivity_matches_dense():
     r, t = oracle.attn_bwd_dq_rows(*b, seg, seg.copy(), 0.2, rows, sensitivity=True)
     assert np.allclose(r, dq[0, rows[:, 2], rows[:, 1]], rtol=0, atol=1e-13)
     assert np.allclose(t, tq[0, rows[:, 2], rows[:, 1]], rtol=1e-12, atol=1e-14)
+
+
+# ---- the sensitivity sums, characterised from above ----------------------------------
+# A separately written fp64 model of the gradient in which every term that a
+# finite-precision implementation rounds carries its own relative
+# perturbation: term j of dq_id (scale dS_ij k_jd), term i of dk_jd
+# (scale dS_ij q_id) and of dv_jd (P_ij dout_id), and term (j, d') of out_id'
+# (P_ij v_jd') where out feeds delta_i = dout_i . out_i.  Every output is
+# linear in each single perturbation, so one-hot evaluations give its
+# partial derivatives exactly, and the sign-aligned first-order deviation for
+# perturbations of size u is u times the sum of their magnitudes.  tk and tv
+# must equal that sum; so must tq where every k_jd has one sign (its P E term
+# takes |k_jd| inside the sum over j, a bound on |sum_j P_ij k_jd| E_i),
+# and tq must bound it otherwise.
+
+def _perturbed_grads(q, k, v, do, valid, scale, eq, ek, ev, eo):
+    """dq, dk, dv [S, D] of one (b, h) with relative term perturbations:
+    eq[i, j, d] on term j of dq[i, d]; ek[j, i, d] on term i of dk[j, d];
+    ev[j, i, d] on term i of dv[j, d]; eo[i, j, d] on term (j, d) of out[i, d]
+    as it enters delta_i."""
+    S = q.shape[0]
+    P = np.zeros((S, S))
+    for i in range(S):
+        js = np.nonzero(valid[i])[0]
+        if len(js) == 0:
+            continue
+        s = np.array([scale * float(np.dot(q[i], k[j])) for j in js])
+        w = np.exp(s - s.max())
+        P[i, js] = w / w.sum()
+    dP = do @ v.T
+    out_terms = P[:, :, None] * v[None, :, :] * (1.0 + eo)
+    delta = np.array([float(np.sum(do[i][None, :] * out_terms[i])) for i in range(S)])
+    dS = P * (dP - delta[:, None])
+    dq = (scale * dS[:, :, None] * k[None, :, :] * (1.0 + eq)).sum(axis=1)
+    dk = (scale * dS.T[:, :, None] * q[None, :, :] * (1.0 + ek)).sum(axis=1)
+    dv = (P.T[:, :, None] * do[None, :, :] * (1.0 + ev)).sum(axis=1)
+    return dq, dk, dv
+
+
+def _first_order_sums(q, k, v, do, valid, scale):
+    """Per element of dq, dk, dv: sum over every term perturbation of
+    |d output / d perturbation|, from one-hot evaluations of the model."""
+    S, D = q.shape
+    zero = np.zeros((S, S, D))
+    base = _perturbed_grads(q, k, v, do, valid, scale, zero, zero, zero, zero)
+    sums = [np.zeros((S, D)) for _ in range(3)]
+    for slot in range(4):
+        for idx in np.ndindex(S, S, D):
+            e = [zero, zero, zero, zero]
+            one = np.zeros((S, S, D))
+            one[idx] = 1.0
+            e[slot] = one
+            got = _perturbed_grads(q, k, v, do, valid, scale, *e)
+            for n in range(3):
+                sums[n] += np.abs(got[n] - base[n])
+    return sums
+
+
+@pytest.mark.parametrize("case", ["unmasked_signed", "packed_signed", "packed_nonneg_k"])
+def test_sensitivity_sums_equal_first_order_deviation(case):
+    B, S, H, D = 1, 7, 2, 5
+    scale = 0.375
+    x = W.make_random(B, S, H, D, seed=781)
+    dout = W.randn_bf16((B, S, H, D), 783)
+    if case == "packed_nonneg_k":
+        x["k"] = x["k"].abs()
+    seg = None
+    if case != "unmasked_signed":
+        seg = torch.tensor([[2, 2, 2, 0, -5, -5, 2]], dtype=torch.int32)
+    s = None if seg is None else seg.numpy()
+    dq, dk, dv, tq, tk, tv = oracle.attn_bwd(bits(x["q"]), bits(x["k"]), bits(x["v"]), bits(dout), s,
+                                             None if s is None else s.copy(), scale, sensitivity=True)
+    for h in range(H):
+        f = lambda t: t[0, :, h].double().numpy()
+        q, k, v, do = f(x["q"]), f(x["k"]), f(x["v"]), f(dout)
+        if seg is None:
+            valid = np.ones((S, S), dtype=bool)
+        else:
+            sg = seg[0].numpy()
+            valid = (sg[:, None] == sg[None, :]) & (sg[:, None] != 0)
+        zero = np.zeros((S, S, D))
+        g = _perturbed_grads(q, k, v, do, valid, scale, zero, zero, zero, zero)
+        for a, b in zip(g, (dq, dk, dv)):
+            assert np.abs(a - b[0, :, h]).max() < 1e-12
+        sq, sk, sv = _first_order_sums(q, k, v, do, valid, scale)
+        close = lambda a, b: np.all(np.abs(a - b) <= 1e-9 * np.abs(b) + 1e-13)
+        assert close(tk[0, :, h], sk), (h, np.abs(tk[0, :, h] - sk).max())
+        assert close(tv[0, :, h], sv), (h, np.abs(tv[0, :, h] - sv).max())
+        if case == "packed_nonneg_k":
+            assert close(tq[0, :, h], sq), (h, np.abs(tq[0, :, h] - sq).max())
+        else:
+            assert np.all(tq[0, :, h] >= sq * (1 - 1e-12) - 1e-13)
+            assert np.any(tq[0, :, h] > sq * (1 + 1e-6))  # signed k: a strict bound somewhere

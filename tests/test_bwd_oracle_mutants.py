@@ -5,7 +5,10 @@ dropped, a missing scale, a transposed probability or score-gradient index,
 the wrong operand in a product, an unnormalised softmax, padding matching
 padding), compiled on the CPU with the other oracle sources unchanged,
 swapped in and run against the pins of ``test_bwd_oracle.py``: at least one
-pin must fail for every mutant.  Nothing here touches a GPU.
+pin must fail for every mutant.  The slips in the rounding-sensitivity sums
+(which set the GPU backward's per-element tolerance) are made the same way in
+the dense and the row function, so that the two still agree with each other.
+Nothing here touches a GPU.
 """
 import os
 import shutil
@@ -35,6 +38,39 @@ MUTANTS = [
      "return J->seg_kv[b * J->S + j] == c;"),
     ("dq_transposed_ds", "const double ds = dS[i * S + j];",
      "const double ds = dS[j * S + i];"),
+    # rounding-sensitivity sums, each slip in both the dense and the row function
+    ("sens_e_doubled", [("E[i] = e;", "E[i] = 2.0 * e;"),
+                        ("+ P[j] * e) * fabs", "+ 2.0 * P[j] * e) * fabs")]),
+    ("sens_e_dropped", [("const double w = fabs(ds) + P[i * S + j] * E[i];", "const double w = fabs(ds);"),
+                        ("const double w = fabs(ds) + p * E[i];", "const double w = fabs(ds);"),
+                        ("+ P[j] * e) * fabs", ") * fabs")]),
+    ("sens_no_scale", [("if (E) J->tq[at(J, b, i, h) + d] = J->scale * tacc[d];",
+                        "if (E) J->tq[at(J, b, i, h) + d] = tacc[d];"),
+                       ("J->tk[at(J, b, j, h) + d] = J->scale * tacc[d];", "J->tk[at(J, b, j, h) + d] = tacc[d];"),
+                       ("tq[d] = J->scale * t;", "tq[d] = t;")]),
+    # E_i from |dout_i . v_j| instead of sum_d |dout_id| |v_jd|
+    ("sens_e_abs_of_dot", [("a += fabs(b2d(J->dout[at(J, b, i, h) + d])) * fabs(b2d(J->v[at(J, b, j, h) + d]));\n"
+                            "                e += P[i * S + j] * a;",
+                            "a += b2d(J->dout[at(J, b, i, h) + d]) * b2d(J->v[at(J, b, j, h) + d]);\n"
+                            "                e += P[i * S + j] * fabs(a);"),
+                           ("a += fabs(b2d(J->dout[at(J, b, i, h) + d])) * fabs(b2d(J->v[at(J, b, j, h) + d]));\n"
+                            "            e += P[j] * a;",
+                            "a += b2d(J->dout[at(J, b, i, h) + d]) * b2d(J->v[at(J, b, j, h) + d]);\n"
+                            "            e += P[j] * fabs(a);")]),
+    # |dS_ij| replaced by P_ij |dP_ij| (delta left out of the magnitude)
+    ("sens_ds_without_delta", [("const double w = fabs(ds) + P[i * S + j] * E[i];",
+                                "const double w = fabs(ds + P[i * S + j] * dl[i]) + P[i * S + j] * E[i];"),
+                               ("const double w = fabs(ds) + p * E[i];",
+                                "const double w = fabs(ds + p * dl[i]) + p * E[i];"),
+                               ("E[i] = e;", "E[i] = e;\n            dl[i] = delta;"),
+                               ("double *acc = (double *)malloc(sizeof(double) * (size_t)(4 * D));",
+                                "double *acc = (double *)malloc(sizeof(double) * (size_t)(4 * D));\n"
+                                "    static __thread double dl[4096];"),
+                               ("t += (fabs(P[j] * (dP[j] - delta)) + P[j] * e)", "t += (P[j] * fabs(dP[j]) + P[j] * e)")]),
+    # |k_jd| without the absolute value in tq
+    ("sens_k_signed", [("for (int64_t d = 0; d < D; ++d) tacc[d] += w * fabs(b2d(kj[d]));",
+                        "for (int64_t d = 0; d < D; ++d) tacc[d] += w * b2d(kj[d]);"),
+                       ("+ P[j] * e) * fabs(b2d(J->k[at(J, b, j, h) + d]));", "+ P[j] * e) * b2d(J->k[at(J, b, j, h) + d]);")]),
 ]
 
 PIN_FUNCS = [
@@ -45,6 +81,10 @@ PIN_FUNCS = [
     pins.test_constant_value_gives_zero_dq_dk,
     pins.test_zero_query_closed_form,
     pins.test_segment_sums_and_masked_rows,
+    pins.test_sensitivity_sums_bound_and_reduce,
+    pins.test_dq_rows_sensitivity_matches_dense,
+    lambda: pins.test_sensitivity_sums_equal_first_order_deviation("packed_signed"),
+    lambda: pins.test_sensitivity_sums_equal_first_order_deviation("packed_nonneg_k"),
 ]
 
 
@@ -56,13 +96,21 @@ def workdir():
     shutil.rmtree(d, ignore_errors=True)
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(workdir, name, old, new):
+def _edits(m):
+    """(name, old, new) or (name, [(old, new), ...]) -> [(old, new), ...]."""
+    return [(m[1], m[2])] if len(m) == 3 else list(m[1])
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(workdir, mutant):
+    name = mutant[0]
     src = open(BWD_SRC).read()
-    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    for old, new in _edits(mutant):
+        assert src.count(old) >= 1, f"mutation site for {name} not found: {old!r}"
+        src = src.replace(old, new, 1)
     path = os.path.join(workdir, f"{name}.c")
     with open(path, "w") as f:
-        f.write(src.replace(old, new, 1))
+        f.write(src)
     lib = os.path.join(workdir, f"lib_{name}.so")
     build_oracle(bwd_src=path, out=lib)
     oracle.use_library(lib)

@@ -75,7 +75,8 @@ def sdpa_ref(x, seg, scale):
 
 # --- library routine ----------------------------------------------------------
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("kind", ["single", "padded", "packed", "interleaved", "singletons"])
+@pytest.mark.parametrize("kind", ["single", "padded", "packed", "interleaved", "singletons", "negative",
+                                  "extreme"])
 def test_matches_torch_sdpa_f64(D, kind):
     B, S, H = 2, 97, 2
     x = W.make_random(B, S, H, D, seed=11 + D)

@@ -197,7 +197,12 @@ def random_segments(B: int, S: int, seed: int, kind: str) -> torch.Tensor:
     "packed" (contiguous runs of random length, IDs 1..n, pad tail),
     "interleaved" (random IDs in {0,1,2,3} per token, so segments are
     non-contiguous), "singletons" (every token its own ID),
-    "allpad" (every token 0).
+    "allpad" (every token 0), "negative" (contiguous runs of random length
+    with negative IDs -1, -2, ..., interrupted by pad runs of 0, and a run of
+    ID 1 that shares no token with a negative run), "extreme" (runs of the
+    int32 extremes -2^31 and 2^31 - 1, their neighbours -2^31 + 1 and
+    2^31 - 2, -1, 1 and 0 in random order and lengths, each ID possibly in
+    several non-adjacent runs).
     """
     g = torch.Generator().manual_seed(int(seed))
     seg = torch.zeros(B, S, dtype=torch.int32)
@@ -222,6 +227,24 @@ def random_segments(B: int, S: int, seed: int, kind: str) -> torch.Tensor:
             seg[b] = torch.arange(1, S + 1, dtype=torch.int32)
         elif kind == "allpad":
             pass
+        elif kind == "negative":
+            pos, sid = 0, -1
+            while pos < S:
+                ln = int(torch.randint(1, max(2, S // 4) + 1, (1,), generator=g))
+                r = int(torch.randint(0, 5, (1,), generator=g))
+                seg[b, pos: pos + ln] = 0 if r == 0 else (1 if r == 1 else sid)
+                if r >= 2:
+                    sid -= 1
+                pos += ln
+        elif kind == "extreme":
+            ids = torch.tensor([-2 ** 31, 2 ** 31 - 1, -2 ** 31 + 1, 2 ** 31 - 2, -1, 1, 0],
+                               dtype=torch.int64)
+            pos = 0
+            while pos < S:
+                ln = int(torch.randint(1, max(2, S // 6) + 1, (1,), generator=g))
+                sid = int(ids[int(torch.randint(0, len(ids), (1,), generator=g))])
+                seg[b, pos: pos + ln] = sid
+                pos += ln
         else:
             raise ValueError(kind)
     return seg
@@ -231,3 +254,4 @@ def bf16_bits(t: torch.Tensor):
     """uint16 numpy view of a CPU bf16 tensor (the exact bits)."""
     assert t.dtype == torch.bfloat16 and t.device.type == "cpu"
     return t.contiguous().view(torch.int16).numpy().view("uint16")
+
