@@ -13,12 +13,15 @@ restricted to each query's 3D neighbourhood window -- section 2 for the
 windowed-attention fallback of the neighbourhood-attention VAE decoder,
 Appendix A, Table 4, group 4 for its 11 x 11 x 11 window) and
 ``attn_bwd_oracle.c`` (the exact gradients of the segment-masked forward with
-respect to q, k, v -- section 5 lists training as future work).  This
-wrapper only marshals numpy arrays.
+respect to q, k, v -- section 5 lists training as future work) and
+``rope_oracle.c`` (the 3D rotary position embedding of queries and keys that
+section 2 places right before attention, with the per-axis angle tables and
+section widths, the pairing of features and the positions all given by the
+caller).  This wrapper only marshals numpy arrays.
 
 Every function here has pins in ``tests/test_oracle.py``,
-``tests/test_natten_oracle.py`` and ``tests/test_bwd_oracle.py``; their
-module docstrings say what pins what.
+``tests/test_natten_oracle.py``, ``tests/test_bwd_oracle.py`` and
+``tests/test_rope_oracle.py``; their module docstrings say what pins what.
 """
 from __future__ import annotations
 
@@ -57,6 +60,13 @@ def _load(path: Optional[str] = None):
     br = lib.vdx_oracle_attn_bwd_dq_rows
     br.restype = ctypes.c_int
     br.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double, p, i64, p, p, ctypes.c_int]
+    r = lib.vdx_oracle_rope3d
+    r.restype = ctypes.c_int
+    r.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                  i64, i64, i64, i64, p, p]
+    rb = lib.vdx_oracle_round_bf16
+    rb.restype = None
+    rb.argtypes = [p, i64, p]
     g = lib.vdx_oracle_natten3d_fwd
     g.restype = ctypes.c_int
     g.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
@@ -231,3 +241,56 @@ def attn_bwd_dq_rows(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
     return (dq, tq) if sensitivity else dq
+
+
+def rope3d(x_bits: np.ndarray, pos: np.ndarray, cos: Tuple[np.ndarray, np.ndarray, np.ndarray],
+           sin: Tuple[np.ndarray, np.ndarray, np.ndarray], dims: Tuple[int, int, int],
+           interleaved: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """3D rotary position embedding of bf16 bit patterns x [B, S, H, D].
+
+    pos: int32 [B, S, 3], the (t, y, x) of every token; cos / sin: per axis
+    (t, y, x) fp32 tables [n_a, d_a / 2]; dims: the section widths (d_t, d_h,
+    d_w); interleaved: pairs (2p, 2p + 1) of a section, else (p, p + d_a / 2).
+    Returns (bf16 bits uint16 [B, S, H, D], the fp64 values before rounding)."""
+    lib = _load()
+    assert x_bits.dtype == np.uint16 and x_bits.ndim == 4
+    B, S, H, D = x_bits.shape
+    x_bits = np.ascontiguousarray(x_bits)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    assert pos.shape == (B, S, 3)
+    cs = [np.ascontiguousarray(c, dtype=np.float32) for c in cos]
+    sn = [np.ascontiguousarray(c, dtype=np.float32) for c in sin]
+    for a in range(3):
+        assert cs[a].ndim == 2 and cs[a].shape == sn[a].shape and cs[a].shape[1] == dims[a] // 2
+    y = np.zeros((B, S, H, D), dtype=np.uint16)
+    yd = np.zeros((B, S, H, D), dtype=np.float64)
+    tabs = []
+    for a in range(3):
+        tabs += [_ptr(cs[a]) if cs[a].size else None, _ptr(sn[a]) if sn[a].size else None]
+    rc = lib.vdx_oracle_rope3d(_ptr(x_bits), _ptr(pos), *tabs, cs[0].shape[0], cs[1].shape[0],
+                               cs[2].shape[0], int(dims[0]), int(dims[1]), int(dims[2]),
+                               1 if interleaved else 0, B, S, H, D, _ptr(y), _ptr(yd))
+    if rc != 0:
+        raise RuntimeError(f"oracle returned {rc}")
+    return y, yd
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) of fp64 values, rounded to nearest, ties to even."""
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, dtype=np.uint16)
+    lib.vdx_oracle_round_bf16(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def rope3d_attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, pos: np.ndarray,
+                    cos, sin, dims, interleaved: bool, seg_q: Optional[np.ndarray],
+                    seg_kv: Optional[np.ndarray], scale: float, rows: Optional[np.ndarray] = None,
+                    n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention (attn_fwd) of the 3D-rotary-embedded queries and keys: q and
+    k go through rope3d (rounded to bf16), v is used as given."""
+    qr, _ = rope3d(q_bits, pos, cos, sin, dims, interleaved)
+    kr, _ = rope3d(k_bits, pos, cos, sin, dims, interleaved)
+    out, lse, _ = attn_fwd(qr, kr, v_bits, seg_q, seg_kv, scale, rows=rows, n_threads=n_threads)
+    return out, lse

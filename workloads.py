@@ -255,3 +255,100 @@ def bf16_bits(t: torch.Tensor):
     assert t.dtype == torch.bfloat16 and t.device.type == "cpu"
     return t.contiguous().view(torch.int16).numpy().view("uint16")
 
+
+# --- 3D rotary position embedding of queries and keys -----------------------------
+# The pages say the video DiTs rotate queries and keys by a 3D rotary position
+# embedding over (t, y, x) before attention, with per-family conventions
+# (vidax paper, section 2, "3D RoPE, 3D VAEs, and flash attention"), and give
+# no formula, head-dim split or frequency schedule.  The inputs below are
+# synthetic: per-axis angle tables from the geometric frequency schedule of
+# the rotary position embedding (angle(pos, p) = pos * theta^(-2p / d_a),
+# theta = 10,000), a split of the head dim into three even sections whose pair
+# counts are not multiples of 8, and the (t, y, x) of every video token of
+# each clip's latent grid; other tokens (text, padding) get (-1, -1, -1) and
+# stay unrotated.
+
+@dataclass(frozen=True)
+class Rope3D:
+    """Per-token positions and per-axis tables of a 3D rotary embedding."""
+    pos: torch.Tensor                 # int32 [B, S, 3]
+    cos: Tuple[torch.Tensor, ...]     # fp32 [n_a, d_a / 2] for a = t, y, x
+    sin: Tuple[torch.Tensor, ...]
+    dims: Tuple[int, int, int]        # (d_t, d_h, d_w)
+    interleaved: bool = True
+
+    def numpy(self):
+        """(pos, cos, sin) as numpy arrays, for the oracle."""
+        return (self.pos.numpy(), tuple(c.numpy() for c in self.cos),
+                tuple(s.numpy() for s in self.sin))
+
+
+ROPE_DIMS = {64: (20, 22, 22), 128: (44, 42, 42)}
+ROPE_THETA = 10000.0
+
+# Latent grids (t, y, x) of the video tokens of each workload: (first token, grid).
+ROPE_GRIDS: Dict[str, List[Tuple[int, Tuple[int, int, int]]]] = {
+    "tiny_ref": [(0, (4, 16, 16))],
+    "dit480p_small": [(0, (21, 30, 52))],
+    "joint_video_text_pad": [(0, (13, 30, 45))],     # the 226 text tokens and the padding stay unrotated
+    "dit720p_large": [(0, (21, 45, 80))],
+    "packed_clips": [(0, (16, 16, 16)), (4096, (7, 30, 39)), (12286, (13, 30, 42)),
+                     (28666, (21, 30, 52))],
+}
+
+
+def rope3d_tables(n: int, d: int, theta: float = ROPE_THETA) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp32 cos / sin [n, d/2] of angle(pos, p) = pos * theta^(-2p/d),
+    evaluated in fp64 and rounded to fp32."""
+    half = d // 2
+    p = torch.arange(half, dtype=torch.float64)
+    freq = theta ** (-2.0 * p / d) if d > 0 else p
+    ang = torch.arange(n, dtype=torch.float64)[:, None] * freq[None, :]
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
+
+
+def grid_positions(B: int, S: int, grids: Sequence[Tuple[int, Tuple[int, int, int]]]) -> torch.Tensor:
+    """int32 [B, S, 3]: (t, y, x) of token start + (t*NH + y)*NW + x of each
+    grid, (-1, -1, -1) for every other token; the same in every batch row."""
+    pos = torch.full((S, 3), -1, dtype=torch.int32)
+    for start, (nt, nh, nw) in grids:
+        n = nt * nh * nw
+        assert start + n <= S
+        idx = torch.arange(n, dtype=torch.int32)
+        pos[start:start + n, 0] = idx // (nh * nw)
+        pos[start:start + n, 1] = (idx // nw) % nh
+        pos[start:start + n, 2] = idx % nw
+    return pos.unsqueeze(0).expand(B, S, 3).contiguous()
+
+
+def make_rope3d(B: int, S: int, D: int, grids: Sequence[Tuple[int, Tuple[int, int, int]]],
+                interleaved: bool = True, dims: Optional[Tuple[int, int, int]] = None) -> Rope3D:
+    """Positions of the given grids and tables covering the largest extent of
+    each axis."""
+    dims = ROPE_DIMS[D] if dims is None else tuple(dims)
+    n = [max(g[1][a] for g in grids) if grids else 1 for a in range(3)]
+    tabs = [rope3d_tables(n[a], dims[a]) for a in range(3)]
+    return Rope3D(pos=grid_positions(B, S, grids), cos=tuple(t[0] for t in tabs),
+                  sin=tuple(t[1] for t in tabs), dims=dims, interleaved=interleaved)
+
+
+def workload_rope3d(w: "Workload", interleaved: bool = True) -> Rope3D:
+    return make_rope3d(w.B, w.S, w.D, ROPE_GRIDS[w.name], interleaved)
+
+
+def random_positions(B: int, S: int, n: Tuple[int, int, int], seed: int,
+                     outside: float = 0.1) -> torch.Tensor:
+    """int32 [B, S, 3] seeded positions inside tables of n = (n_t, n_h, n_w)
+    rows, with about a fraction `outside` of the tokens given a coordinate
+    outside them (negative or >= n_a) on one random axis."""
+    g = torch.Generator().manual_seed(int(seed))
+    pos = torch.stack([torch.randint(0, max(1, n[a]), (B, S), generator=g, dtype=torch.int32)
+                       for a in range(3)], dim=-1)
+    sel = torch.rand(B, S, generator=g) < outside
+    axis = torch.randint(0, 3, (B, S), generator=g)
+    big = torch.rand(B, S, generator=g) < 0.5
+    for a in range(3):
+        m = sel & (axis == a)
+        pos[..., a] = torch.where(m & big, torch.tensor(n[a] + 3, dtype=torch.int32), pos[..., a])
+        pos[..., a] = torch.where(m & ~big, torch.tensor(-1 - a, dtype=torch.int32), pos[..., a])
+    return pos.contiguous()
