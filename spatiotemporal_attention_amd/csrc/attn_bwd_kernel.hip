@@ -207,37 +207,39 @@ __device__ __forceinline__ void wg_coords(int n_blk, int n_wg, int& blk, int& bh
 }
 
 // ---- prep: delta and lse2 ------------------------------------------------------
-// Rows (b, i, h) in memory order; D/8 lanes per row, 8 elements each.
+// Items walk the workspace order (b, h, i) with i fastest over S_pad rows, so
+// the 4-byte results of a block's rows land in one contiguous run per array
+// (walking the rows in [B, S, H] memory order instead put neighbouring stores
+// S_pad * 4 bytes apart, each in a write burst of its own).  A row's out and
+// dout (D bf16 each) are read by D/8 lanes, 16 bytes a lane.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
     const __bf16* __restrict__ out, const __bf16* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ ws_lse2, float* __restrict__ ws_delta, int S, int H, int S_pad,
-    int64_t n_rows, int64_t n_items) {
+    int64_t n_items) {
     constexpr int L = D / 8;
     const int64_t stride = (int64_t)gridDim.x * (256 / L);
     const int part = threadIdx.x % L;
     for (int64_t it = (int64_t)blockIdx.x * (256 / L) + threadIdx.x / L; it < n_items; it += stride) {
-        if (it < n_rows) {
-            const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + it * D + 8 * part);
-            const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + it * D + 8 * part);
+        const int64_t i = it % S_pad, bh = it / S_pad;
+        if (i < S) {
+            const int64_t h = bh % H, b = bh / H;
+            const int64_t row = (b * S + i) * H + h;
+            const bf16x8 o = *reinterpret_cast<const bf16x8*>(out + row * D + 8 * part);
+            const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + row * D + 8 * part);
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)d[e], acc);
 #pragma unroll
             for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
             if (part == 0) {
-                const int64_t h = it % H, bi = it / H;
-                const int64_t i = bi % S, b = bi / S;
-                const int64_t w = (b * H + h) * S_pad + i;
-                const float l = lse[(b * H + h) * S + i];
-                ws_delta[w] = acc;
-                ws_lse2[w] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+                const float l = lse[bh * S + i];
+                ws_delta[it] = acc;
+                ws_lse2[it] = (l == -INFINITY) ? INFINITY : l * kLog2e;
             }
         } else if (part == 0) {
-            const int64_t e = it - n_rows, np = S_pad - S;
-            const int64_t w = (e / np) * S_pad + S + e % np;
-            ws_delta[w] = 0.f;
-            ws_lse2[w] = INFINITY;
+            ws_delta[it] = 0.f;
+            ws_lse2[it] = INFINITY;
         }
     }
 }
@@ -1019,13 +1021,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     const auto* v = reinterpret_cast<const __bf16*>(a.v);
     const auto* dout = reinterpret_cast<const __bf16*>(a.dout);
     {
-        const int64_t n_rows = (int64_t)a.B * a.S * a.H;
-        const int64_t n_items = n_rows + (int64_t)a.B * a.H * (S_pad - a.S);
+        const int64_t n_items = (int64_t)a.B * a.H * S_pad;
         const int64_t per_block = 256 / (D / 8);
         const int64_t blocks = std::min<int64_t>((n_items + per_block - 1) / per_block, 1 << 20);
         hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
                            reinterpret_cast<const __bf16*>(a.out), dout, a.lse, ws_lse2, ws_delta,
-                           a.S, a.H, S_pad, n_rows, n_items);
+                           a.S, a.H, S_pad, n_items);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
