@@ -52,7 +52,7 @@ def _load(path: Optional[str] = None):
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
     f.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double,
-                  p, i64, p, p, p, ctypes.c_int]
+                  p, i64, p, p, p, p, ctypes.c_int]
     bw = lib.vdx_oracle_attn_bwd
     bw.restype = ctypes.c_int
     bw.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_double, p, p, p, p, p, p,
@@ -70,7 +70,7 @@ def _load(path: Optional[str] = None):
     g = lib.vdx_oracle_natten3d_fwd
     g.restype = ctypes.c_int
     g.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
-                  p, i64, p, p, ctypes.c_int]
+                  p, i64, p, p, p, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -96,7 +96,8 @@ def _ptr(a: Optional[np.ndarray]):
 def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
              seg_q: Optional[np.ndarray], seg_kv: Optional[np.ndarray],
              scale: float, rows: Optional[np.ndarray] = None,
-             n_threads: Optional[int] = None, want_probs: bool = False
+             n_threads: Optional[int] = None, want_probs: bool = False,
+             sens: Optional[np.ndarray] = None
              ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
     """fp64 attention on bf16 bit patterns.
 
@@ -104,6 +105,8 @@ def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     seg_q/seg_kv: int32 [B, S] or both None.
     rows: optional int64 [n, 3] of (b, h, i); then out is [n, D] and lse [n];
           else out is [B, S, H, D] and lse [B, H, S].
+    sens: optional fp64 array shaped like out, filled with the rounding
+          sensitivity sum_j P_ij |v_jd| of each output element.
     Returns (out fp64, lse fp64, probs fp64 or None).
     """
     lib = _load()
@@ -132,9 +135,11 @@ def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         lse = np.zeros((B, H, S), dtype=np.float64)
         n_prob_rows = B * H * S
     probs = np.zeros((n_prob_rows, S), dtype=np.float64) if want_probs else None
+    if sens is not None:
+        assert sens.shape == out.shape and sens.dtype == np.float64 and sens.flags.c_contiguous
     rc = lib.vdx_oracle_attn_fwd(
         _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(seg_q), _ptr(seg_kv),
-        B, S, H, D, float(scale), _ptr(rows), n, _ptr(out), _ptr(lse), _ptr(probs),
+        B, S, H, D, float(scale), _ptr(rows), n, _ptr(out), _ptr(lse), _ptr(probs), _ptr(sens),
         int(n_threads if n_threads is not None else default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
@@ -143,14 +148,15 @@ def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
 
 def natten3d_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
                  grid: Tuple[int, int, int], window: Tuple[int, int, int], scale: float,
-                 rows: Optional[np.ndarray] = None, n_threads: Optional[int] = None
-                 ) -> Tuple[np.ndarray, np.ndarray]:
+                 rows: Optional[np.ndarray] = None, n_threads: Optional[int] = None,
+                 sens: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 3D neighbourhood attention on bf16 bit patterns.
 
     q_bits/k_bits/v_bits: uint16 [B, S, H, D], S = NT*NH*NW, tokens (t, y, x)
     row-major.  grid = (NT, NH, NW); window = (KT, KH, KW), odd sizes.
     rows: optional int64 [n, 3] of (b, h, i); then out is [n, D] and lse [n];
-    else out is [B, S, H, D] and lse [B, H, S].
+    else out is [B, S, H, D] and lse [B, H, S].  sens: optional fp64 array
+    shaped like out, filled with sum over the window of P_ij |v_jd|.
     """
     lib = _load()
     for a in (q_bits, k_bits, v_bits):
@@ -173,9 +179,11 @@ def natten3d_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         n = 0
         out = np.zeros((B, S, H, D), dtype=np.float64)
         lse = np.zeros((B, H, S), dtype=np.float64)
+    if sens is not None:
+        assert sens.shape == out.shape and sens.dtype == np.float64 and sens.flags.c_contiguous
     rc = lib.vdx_oracle_natten3d_fwd(
         _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), B, NT, NH, NW, H, D, KT, KH, KW,
-        float(scale), _ptr(rows), n, _ptr(out), _ptr(lse),
+        float(scale), _ptr(rows), n, _ptr(out), _ptr(lse), _ptr(sens),
         int(n_threads if n_threads is not None else default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
@@ -287,10 +295,12 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
 def rope3d_attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, pos: np.ndarray,
                     cos, sin, dims, interleaved: bool, seg_q: Optional[np.ndarray],
                     seg_kv: Optional[np.ndarray], scale: float, rows: Optional[np.ndarray] = None,
-                    n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+                    n_threads: Optional[int] = None,
+                    sens: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention (attn_fwd) of the 3D-rotary-embedded queries and keys: q and
-    k go through rope3d (rounded to bf16), v is used as given."""
+    k go through rope3d (rounded to bf16), v is used as given; sens as for
+    attn_fwd."""
     qr, _ = rope3d(q_bits, pos, cos, sin, dims, interleaved)
     kr, _ = rope3d(k_bits, pos, cos, sin, dims, interleaved)
-    out, lse, _ = attn_fwd(qr, kr, v_bits, seg_q, seg_kv, scale, rows=rows, n_threads=n_threads)
+    out, lse, _ = attn_fwd(qr, kr, v_bits, seg_q, seg_kv, scale, rows=rows, n_threads=n_threads, sens=sens)
     return out, lse

@@ -33,6 +33,12 @@
  *
  * Layouts: q, k, v are bf16 bit patterns [B, S, H, D]; seg arrays int32 [B, S].
  * Output is fp64 and is never rounded to bf16 here.
+ *
+ * Optionally it also returns, per output element, the sum of the magnitudes
+ * of the terms that make it up, sens_id = sum_j P_ij |v_jd|: a finite-precision
+ * result whose every probability carries its own relative error up to u lies
+ * within u * sens_id of the exact one (to first order), which sets the parity
+ * tolerance of elements where that exceeds the fixed bound.
  */
 #include <math.h>
 #include <pthread.h>
@@ -60,6 +66,7 @@ typedef struct {
     int64_t n_rows;
     double *out, *lse;
     double *probs;       /* optional: per-row probability vector [n_rows, S] */
+    double *sens;        /* optional: sum_j P_ij |v_jd|, shaped like out */
     int64_t next;        /* shared work counter */
     pthread_mutex_t mu;
 } job_t;
@@ -70,7 +77,7 @@ static int64_t tok_index(const job_t *J, int64_t b, int64_t s, int64_t h) {
 
 /* One output row: fixed (b, h, i). */
 static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
-                    double *out_row, double *lse_row, double *probs_row,
+                    double *out_row, double *lse_row, double *probs_row, double *sens_row,
                     double *s_buf, unsigned char *valid) {
     const int64_t S = J->S, D = J->D;
     int any = 0;
@@ -88,6 +95,8 @@ static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
     }
     if (!any) {
         for (int64_t d = 0; d < D; ++d) out_row[d] = 0.0;
+        if (sens_row)
+            for (int64_t d = 0; d < D; ++d) sens_row[d] = 0.0;
         *lse_row = -INFINITY;
         if (probs_row)
             for (int64_t j = 0; j < S; ++j) probs_row[j] = 0.0;
@@ -109,6 +118,8 @@ static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
     /* Softmax weights relative to the maximum, their sum, and the weighted V. */
     double l = 0.0;
     for (int64_t d = 0; d < D; ++d) out_row[d] = 0.0;
+    if (sens_row)
+        for (int64_t d = 0; d < D; ++d) sens_row[d] = 0.0;
     for (int64_t j = 0; j < S; ++j) {
         if (!valid[j]) continue;
         const double w = exp(s_buf[j] - m);
@@ -116,8 +127,12 @@ static void one_row(const job_t *J, int64_t b, int64_t h, int64_t i,
         l += w;
         const uint16_t *vj = J->v + tok_index(J, b, j, h);
         for (int64_t d = 0; d < D; ++d) out_row[d] += w * bf16_to_f64(vj[d]);
+        if (sens_row)
+            for (int64_t d = 0; d < D; ++d) sens_row[d] += w * fabs(bf16_to_f64(vj[d]));
     }
     for (int64_t d = 0; d < D; ++d) out_row[d] /= l;
+    if (sens_row)
+        for (int64_t d = 0; d < D; ++d) sens_row[d] /= l;
     *lse_row = m + log(l);
     if (probs_row)
         for (int64_t j = 0; j < S; ++j) probs_row[j] = valid[j] ? s_buf[j] / l : 0.0;
@@ -139,7 +154,7 @@ static void *worker(void *arg) {
         pthread_mutex_unlock(&J->mu);
         if (r >= total) break;
         int64_t b, h, i;
-        double *out_row, *lse_row, *probs_row = NULL;
+        double *out_row, *lse_row, *probs_row = NULL, *sens_row = NULL;
         if (J->rows) {
             b = J->rows[3 * r + 0];
             h = J->rows[3 * r + 1];
@@ -147,6 +162,7 @@ static void *worker(void *arg) {
             out_row = J->out + r * J->D;
             lse_row = J->lse + r;
             if (J->probs) probs_row = J->probs + r * J->S;
+            if (J->sens) sens_row = J->sens + r * J->D;
         } else {
             /* r enumerates (b, h, i) with i fastest; out is [B,S,H,D], lse [B,H,S]. */
             i = r % J->S;
@@ -155,8 +171,9 @@ static void *worker(void *arg) {
             out_row = J->out + tok_index(J, b, i, h);
             lse_row = J->lse + (b * J->H + h) * J->S + i;
             if (J->probs) probs_row = J->probs + r * J->S;
+            if (J->sens) sens_row = J->sens + tok_index(J, b, i, h);
         }
-        one_row(J, b, h, i, out_row, lse_row, probs_row, s_buf, valid);
+        one_row(J, b, h, i, out_row, lse_row, probs_row, sens_row, s_buf, valid);
     }
     free(s_buf);
     free(valid);
@@ -171,6 +188,7 @@ static void *worker(void *arg) {
  *   rows         NULL -> every row; out is [B,S,H,D] and lse is [B,H,S].
  *                else n_rows (b, h, i) triples; out is [n_rows, D], lse [n_rows].
  *   probs        optional [n_rows or B*H*S, S] softmax rows (tiny cases only).
+ *   sens         optional, shaped like out: sum_j P_ij |v_jd| per element.
  *   n_threads    worker threads (<= 0 -> online CPUs).
  * Returns 0 on success, 1 on bad arguments, 2 on allocation failure.
  */
@@ -178,7 +196,8 @@ ORACLE_EXPORT int vdx_oracle_attn_fwd(const uint16_t *q, const uint16_t *k, cons
                                       const int32_t *seg_q, const int32_t *seg_kv,
                                       int64_t B, int64_t S, int64_t H, int64_t D, double scale,
                                       const int64_t *rows, int64_t n_rows,
-                                      double *out, double *lse, double *probs, int n_threads) {
+                                      double *out, double *lse, double *probs, double *sens,
+                                      int n_threads) {
     if (!q || !k || !v || !out || !lse) return 1;
     if ((seg_q == NULL) != (seg_kv == NULL)) return 1;
     if (B < 1 || S < 1 || H < 1 || D < 1) return 1;
@@ -199,7 +218,7 @@ ORACLE_EXPORT int vdx_oracle_attn_fwd(const uint16_t *q, const uint16_t *k, cons
     J.B = B; J.S = S; J.H = H; J.D = D;
     J.scale = scale;
     J.rows = rows; J.n_rows = n_rows;
-    J.out = out; J.lse = lse; J.probs = probs;
+    J.out = out; J.lse = lse; J.probs = probs; J.sens = sens;
     J.next = 0;
     pthread_mutex_init(&J.mu, NULL);
 

@@ -66,6 +66,7 @@ typedef struct {
     const int64_t *rows;
     int64_t n_rows;
     double *out, *lse;
+    double *sens; /* optional: sum over the window of P_ij |v_jd|, shaped like out */
     int64_t next;
     pthread_mutex_t mu;
 } njob_t;
@@ -77,7 +78,7 @@ static int64_t elem(const njob_t *J, int64_t b, int64_t s, int64_t h) {
 }
 
 static void n_row(const njob_t *J, int64_t b, int64_t h, int64_t i, double *out_row, double *lse_row,
-                  double *s_buf) {
+                  double *sens_row, double *s_buf) {
     const int64_t D = J->D;
     const int64_t x = i % J->NW, y = (i / J->NW) % J->NH, t = i / (J->NW * J->NH);
     const int64_t kt = J->KT < J->NT ? J->KT : J->NT;
@@ -105,6 +106,8 @@ static void n_row(const njob_t *J, int64_t b, int64_t h, int64_t i, double *out_
 
     double l = 0.0;
     for (int64_t d = 0; d < D; ++d) out_row[d] = 0.0;
+    if (sens_row)
+        for (int64_t d = 0; d < D; ++d) sens_row[d] = 0.0;
     n = 0;
     for (int64_t a = 0; a < kt; ++a)
         for (int64_t c = 0; c < kh; ++c)
@@ -114,9 +117,13 @@ static void n_row(const njob_t *J, int64_t b, int64_t h, int64_t i, double *out_
                 l += w;
                 const uint16_t *vj = J->v + elem(J, b, j, h);
                 for (int64_t d = 0; d < D; ++d) out_row[d] += w * bf16_bits_to_f64(vj[d]);
+                if (sens_row)
+                    for (int64_t d = 0; d < D; ++d) sens_row[d] += w * fabs(bf16_bits_to_f64(vj[d]));
                 ++n;
             }
     for (int64_t d = 0; d < D; ++d) out_row[d] /= l;
+    if (sens_row)
+        for (int64_t d = 0; d < D; ++d) sens_row[d] /= l;
     *lse_row = m + log(l);
 }
 
@@ -134,21 +141,23 @@ static void *n_worker(void *arg) {
         pthread_mutex_unlock(&J->mu);
         if (r >= total) break;
         int64_t b, h, i;
-        double *out_row, *lse_row;
+        double *out_row, *lse_row, *sens_row = NULL;
         if (J->rows) {
             b = J->rows[3 * r + 0];
             h = J->rows[3 * r + 1];
             i = J->rows[3 * r + 2];
             out_row = J->out + r * J->D;
             lse_row = J->lse + r;
+            if (J->sens) sens_row = J->sens + r * J->D;
         } else {
             i = r % S;
             h = (r / S) % J->H;
             b = r / (S * J->H);
             out_row = J->out + elem(J, b, i, h);
             lse_row = J->lse + (b * J->H + h) * S + i;
+            if (J->sens) sens_row = J->sens + elem(J, b, i, h);
         }
-        n_row(J, b, h, i, out_row, lse_row, s_buf);
+        n_row(J, b, h, i, out_row, lse_row, sens_row, s_buf);
     }
     free(s_buf);
     return NULL;
@@ -162,6 +171,8 @@ static void *n_worker(void *arg) {
  *   scale          multiplies q . k (fp64).
  *   rows           NULL -> every row; out is [B,S,H,D] and lse is [B,H,S].
  *                  else n_rows (b, h, i) triples; out is [n_rows, D], lse [n_rows].
+ *   sens           optional, shaped like out: sum over the window of P_ij |v_jd|
+ *                  (first-order rounding sensitivity of each output element).
  *   n_threads      worker threads (<= 0 -> online CPUs).
  * Returns 0 on success, 1 on bad arguments, 2 on allocation failure.
  */
@@ -169,7 +180,7 @@ ORACLE_EXPORT int vdx_oracle_natten3d_fwd(const uint16_t *q, const uint16_t *k, 
                                           int64_t B, int64_t NT, int64_t NH, int64_t NW, int64_t H,
                                           int64_t D, int64_t KT, int64_t KH, int64_t KW, double scale,
                                           const int64_t *rows, int64_t n_rows, double *out, double *lse,
-                                          int n_threads) {
+                                          double *sens, int n_threads) {
     if (!q || !k || !v || !out || !lse) return 1;
     if (B < 1 || NT < 1 || NH < 1 || NW < 1 || H < 1 || D < 1) return 1;
     if (KT < 1 || KH < 1 || KW < 1 || KT % 2 == 0 || KH % 2 == 0 || KW % 2 == 0) return 1;
@@ -191,7 +202,7 @@ ORACLE_EXPORT int vdx_oracle_natten3d_fwd(const uint16_t *q, const uint16_t *k, 
     J.KT = KT; J.KH = KH; J.KW = KW;
     J.scale = scale;
     J.rows = rows; J.n_rows = n_rows;
-    J.out = out; J.lse = lse;
+    J.out = out; J.lse = lse; J.sens = sens;
     J.next = 0;
     pthread_mutex_init(&J.mu, NULL);
 

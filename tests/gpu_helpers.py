@@ -2,12 +2,19 @@
 binding, run the oracle on the same bf16 bits, and compare to the tolerances
 of the parity bar.
 
-Tolerances (fixed for bf16 output of fp32-accumulated attention):
-  OUT_ATOL = 1e-2   max |out_gpu - out_oracle| over compared elements, plus
-                    BF16_U * |out_oracle| (BF16_U = 2^-8, the unit roundoff of
-                    bf16): rounding the exact value once to bf16 already moves
-                    it by up to that much, which exceeds 1e-2 alone once
-                    |out| > 2.56 (tiny segments, peaky rows);
+Tolerances (bf16 output of fp32-accumulated attention):
+  OUT_ATOL = 1e-2   |out_gpu - out_oracle| on every compared element (the
+                    acceptance bound of the product, max |err| <= 1e-2),
+                    except where the first-order rounding bound of the
+                    arithmetic itself is larger (out_tol): the P V product
+                    takes each probability rounded once to bf16 (relative
+                    error up to BF16_U = 2^-8) and the output is rounded once
+                    to bf16, so an element may be off by
+                    BF16_U * sens + half a bf16 ULP of |out| + BF16_U * sens,
+                    with sens = sum_j P_ij |v_jd| from the oracle.  That only
+                    exceeds 1e-2 on peaky rows with a large |out|; each case
+                    also reports its plain max |err| and how many elements
+                    are above 1e-2;
   LSE_ATOL = 1e-3   max |lse_gpu - lse_oracle| over rows with a valid key;
   REL_L2   = 1e-2   ||out_gpu - out_oracle|| / ||out_oracle|| per case, an extra
                     gate because the absolute bound is loose at long S (output
@@ -29,6 +36,26 @@ LSE_ATOL = 1e-3
 REL_L2 = 1e-2
 
 
+def half_ulp_bf16(x):
+    """Half a bf16 ULP of |x| (elementwise): bf16 keeps 8 significant bits,
+    so a value in [2^e, 2^(e+1)) has ULP 2^(e-7); below 2^-126 the spacing
+    is 2^-133."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.ldexp(1.0, (np.maximum(e, -126) - 8).astype(np.int64))
+
+
+def out_tol(ref, sens):
+    """Per-element bound on |out_gpu - out_oracle|: OUT_ATOL, or where larger
+    the first-order rounding bound BF16_U * sens (each probability rounded
+    once to bf16) plus half a bf16 ULP of the value before the final
+    rounding, plus 1e-5 for the fp32 score and sum arithmetic."""
+    ref = np.asarray(ref, dtype=np.float64)
+    sens = np.asarray(sens, dtype=np.float64)
+    pre = np.abs(ref) + BF16_U * sens
+    return np.maximum(OUT_ATOL, BF16_U * sens + half_ulp_bf16(pre) + 1e-5)
+
+
 def to_dev(x, seg_q=None, seg_kv=None):
     d = {n: x[n].cuda() for n in ("q", "k", "v")}
     d["seg_q"] = None if seg_q is None else seg_q.cuda()
@@ -45,13 +72,17 @@ def run_gpu(x, seg_q=None, seg_kv=None, scale=None):
 
 
 def run_oracle(x, seg_q=None, seg_kv=None, scale=None, rows=None):
-    D = x["q"].shape[-1]
+    """(out, lse, sens) of the oracle: fp64 [B,S,H,D] / [B,H,S] / [B,S,H,D], or
+    [n, D] / [n] / [n, D] for listed (b, h, i) rows."""
+    B, S, H, D = x["q"].shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    return oracle.attn_fwd(W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"]),
-                           None if seg_q is None else seg_q.numpy(),
-                           None if seg_kv is None else seg_kv.numpy(), float(np.float32(scale)),
-                           rows=rows)[:2]
+    sens = np.zeros((B, S, H, D) if rows is None else (len(rows), D), dtype=np.float64)
+    out, lse, _ = oracle.attn_fwd(W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"]),
+                                  None if seg_q is None else seg_q.numpy(),
+                                  None if seg_kv is None else seg_kv.numpy(), float(np.float32(scale)),
+                                  rows=rows, sens=sens)
+    return out, lse, sens
 
 
 def valid_rows(seg_q, seg_kv, B, S):
@@ -66,16 +97,28 @@ def valid_rows(seg_q, seg_kv, B, S):
     return out
 
 
-def check_full(out_g, lse_g, out_o, lse_o, has):
-    """Compare full outputs ([B,S,H,D] / [B,H,S]); returns a stats dict."""
+def _out_stats(stats, diff, ref, sens):
+    tol = out_tol(ref, sens)
+    stats["max_abs"] = float(diff.max())
+    stats["max_tol_frac"] = float((diff / tol).max())
+    stats["n_over_1e-2"] = int((diff > OUT_ATOL).sum())
+    over = diff > OUT_ATOL
+    if over.any():
+        # how much of the rounding bound the elements above 1e-2 use
+        stats["max_over_frac_of_rounding_bound"] = float(
+            ((diff[over] - half_ulp_bf16(ref[over])) / (BF16_U * sens[over] + 1e-300)).max())
+
+
+def check_full(out_g, lse_g, out_o, lse_o, has, sens):
+    """Compare full outputs ([B,S,H,D] / [B,H,S]); sens: the oracle's
+    rounding-sensitivity sums; returns a stats dict."""
     og = out_g.float().numpy().astype(np.float64)
     lg = lse_g.numpy().astype(np.float64)
     B, S, H, D = og.shape
     stats = {"max_abs": 0.0, "max_lse": 0.0, "rel_l2": 0.0}
     if has.any():
         diff = np.abs(og[has] - out_o[has])
-        stats["max_abs"] = float(diff.max())
-        stats["max_tol_frac"] = float((diff / (OUT_ATOL + BF16_U * np.abs(out_o[has]))).max())
+        _out_stats(stats, diff, out_o[has], sens[has])
         ref_n = float(np.linalg.norm(out_o[has]))
         stats["rel_l2"] = float(np.linalg.norm(og[has] - out_o[has]) / max(ref_n, 1e-300))
         lh = np.transpose(lg, (0, 2, 1))[has]
@@ -117,15 +160,14 @@ def sample_rows(S, H, B, seg_runs=None, n_random=64, tile=64, seed=0, heads=None
     return np.array(rows, dtype=np.int64)
 
 
-def check_rows(out_g, lse_g, rows, out_o, lse_o, has):
+def check_rows(out_g, lse_g, rows, out_o, lse_o, has, sens):
     og = out_g[rows[:, 0], rows[:, 2], rows[:, 1]].float().numpy().astype(np.float64)
     lg = lse_g[rows[:, 0], rows[:, 1], rows[:, 2]].numpy().astype(np.float64)
     hv = has[rows[:, 0], rows[:, 2]]
     stats = {"rows": int(len(rows)), "max_abs": 0.0, "max_lse": 0.0, "rel_l2": 0.0}
     if hv.any():
         diff = np.abs(og[hv] - out_o[hv])
-        stats["max_abs"] = float(diff.max())
-        stats["max_tol_frac"] = float((diff / (OUT_ATOL + BF16_U * np.abs(out_o[hv]))).max())
+        _out_stats(stats, diff, out_o[hv], sens[hv])
         stats["max_lse"] = float(np.abs(lg[hv] - lse_o[hv]).max())
         stats["rel_l2"] = float(np.linalg.norm(og[hv] - out_o[hv]) / np.linalg.norm(out_o[hv]))
         assert stats["max_tol_frac"] <= 1.0, stats

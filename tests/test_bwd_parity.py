@@ -123,7 +123,8 @@ def compare_all(x, dout, seg_q, seg_kv, scale):
 
 
 SEQS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 257, 1000]
-KINDS = [None, "single", "padded", "packed", "interleaved", "singletons", "allpad"]
+KINDS = [None, "single", "padded", "packed", "interleaved", "singletons", "allpad", "negative",
+         "extreme"]
 
 
 @pytest.mark.parametrize("D", [64, 128])

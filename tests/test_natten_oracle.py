@@ -206,3 +206,29 @@ def test_matches_40_digit_decimal_evaluation():
         for d in range(D):
             want = float(sum(e[j] * Decimal(float(v[j, d])) for j in J) / tot)
             assert abs(out[0, i, 0, d] - want) < 1e-14
+
+
+def test_output_sensitivity_bounds_reduces_and_sums_window_terms():
+    """sum over the window of P_ij |v_jd|: >= |out|, == out bit for bit when
+    v >= 0, and equal to the sum computed here from the probabilities of the
+    whole-grid-masked reference on a small grid."""
+    grid, window = (3, 4, 5), (3, 3, 3)
+    B, H, D = 1, 2, 8
+    S = grid[0] * grid[1] * grid[2]
+    x = W.make_random(B, S, H, D, seed=181)
+    b3 = [W.bf16_bits(x[n]) for n in ("q", "k", "v")]
+    sens = np.zeros((B, S, H, D))
+    out, _ = oracle.natten3d_fwd(*b3, grid, window, 0.2, sens=sens)
+    assert np.all(sens >= np.abs(out) - 1e-15)
+    sens2 = np.zeros_like(sens)
+    out2, _ = oracle.natten3d_fwd(b3[0], b3[1], W.bf16_bits(x["v"].abs()), grid, window, 0.2, sens=sens2)
+    assert np.array_equal(sens2, out2)
+    # the same sums from an independent window mask and softmax in numpy
+    mask = window_mask(grid, window)
+    for h in range(H):
+        q, k, v = (x[n][0, :, h].double().numpy() for n in ("q", "k", "v"))
+        sc = 0.2 * q @ k.T
+        sc[~mask] = -np.inf
+        p = np.exp(sc - sc.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        assert np.abs(p @ np.abs(v) - sens[0, :, h]).max() < 1e-12

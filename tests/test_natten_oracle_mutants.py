@@ -29,6 +29,9 @@ MUTANTS = [
     ("value_of_query_token", "const uint16_t *vj = J->v + elem(J, b, j, h);",
      "const uint16_t *vj = J->v + elem(J, b, i, h);"),
     ("lse_drops_max", "*lse_row = m + log(l);", "*lse_row = log(l);"),
+    ("sens_signed", "sens_row[d] += w * fabs(bf16_bits_to_f64(vj[d]));",
+     "sens_row[d] += w * bf16_bits_to_f64(vj[d]);"),
+    ("sens_unnormalised", "for (int64_t d = 0; d < D; ++d) sens_row[d] /= l;", ""),
 ]
 
 PIN_FUNCS = [
@@ -40,6 +43,7 @@ PIN_FUNCS = [
     lambda: pins.test_reflection_along_an_axis_reflects_the_output(0),
     lambda: pins.test_reflection_along_an_axis_reflects_the_output(2),
     pins.test_matches_40_digit_decimal_evaluation,
+    pins.test_output_sensitivity_bounds_reduces_and_sums_window_terms,
 ]
 
 

@@ -395,3 +395,72 @@ def test_matches_40_digit_decimal_evaluation():
         for d in range(D):
             want = float(sum(e[j] * Decimal(float(v[j, d])) for j in J) / tot)
             assert abs(out[0, i, 0, d] - want) < 1e-14
+
+
+# --- the output rounding-sensitivity sums ------------------------------------------------
+# sens_id = sum_j P_ij |v_jd| sets the per-element parity tolerance where the
+# first-order rounding bound of a bf16-probability kernel exceeds the fixed
+# one.  Pinned against a separately written model in which every probability
+# carries its own relative perturbation (the normaliser kept exact, as a
+# kernel that sums the unrounded weights does): the sum over keys of the
+# magnitudes of the one-hot derivatives of out_id must equal sens_id.
+
+def _perturbed_out(x, seg, scale, b, h, eps):
+    """out[b, :, h, :] with P_ij -> P_ij (1 + eps[i, j]), numpy fp64."""
+    q, k, v = (x[n][b, :, h].double().numpy() for n in ("q", "k", "v"))
+    S = q.shape[0]
+    out = np.zeros_like(q)
+    for i in range(S):
+        js = [j for j in range(S) if seg is None or (seg[b, i] != 0 and seg[b, j] == seg[b, i])]
+        if not js:
+            continue
+        s = np.array([scale * float(np.dot(q[i], k[j])) for j in js])
+        w = np.exp(s - s.max())
+        p = w / w.sum()
+        for t, j in enumerate(js):
+            out[i] += p[t] * (1.0 + eps[i, j]) * v[j]
+    return out
+
+
+@pytest.mark.parametrize("kind", [None, "packed", "interleaved"])
+def test_output_sensitivity_equals_first_order_deviation(kind):
+    B, S, H, D = 1, 11, 2, 6
+    x = W.make_random(B, S, H, D, seed=171, sigma_qk=2.0)
+    seg = None if kind is None else W.random_segments(B, S, 172, kind)
+    sens = np.zeros((B, S, H, D))
+    s = None if seg is None else seg.numpy()
+    out, _, _ = oracle.attn_fwd(bits(x["q"]), bits(x["k"]), bits(x["v"]), s, None if s is None else s.copy(),
+                                0.3, sens=sens)
+    for h in range(H):
+        base = _perturbed_out(x, s, 0.3, 0, h, np.zeros((S, S)))
+        assert np.abs(base - out[0, :, h]).max() < 1e-12
+        tot = np.zeros((S, D))
+        for i in range(S):
+            for j in range(S):
+                e = np.zeros((S, S))
+                e[i, j] = 1.0
+                tot += np.abs(_perturbed_out(x, s, 0.3, 0, h, e) - base)
+        assert np.all(np.abs(sens[0, :, h] - tot) <= 1e-12 * np.maximum(tot, 1.0)), np.abs(sens[0, :, h] - tot).max()
+
+
+def test_output_sensitivity_bounds_and_reduces():
+    """sens >= |out|; with v >= 0 every term is non-negative and sens == out
+    bit for bit; rows without a valid key give 0; the row-subset evaluation
+    gives the same values."""
+    B, S, H, D = 2, 40, 2, 64
+    x = W.make_random(B, S, H, D, seed=173)
+    seg = W.random_segments(B, S, 174, "packed").numpy()
+    sens = np.zeros((B, S, H, D))
+    b3 = [bits(x[n]) for n in ("q", "k", "v")]
+    out, lse, _ = oracle.attn_fwd(*b3, seg, seg.copy(), 0.125, sens=sens)
+    assert np.all(sens >= np.abs(out) - 1e-15)
+    dead = np.isneginf(np.transpose(lse, (0, 2, 1)))
+    assert np.all(sens[dead] == 0.0)
+    vpos = bits(x["v"].abs())
+    sens2 = np.zeros_like(sens)
+    out2, _, _ = oracle.attn_fwd(b3[0], b3[1], vpos, seg, seg.copy(), 0.125, sens=sens2)
+    assert np.array_equal(sens2, out2)
+    rows = np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(0, S, 3)], dtype=np.int64)
+    sr = np.zeros((len(rows), D))
+    oracle.attn_fwd(*b3, seg, seg.copy(), 0.125, rows=rows, sens=sr)
+    assert np.array_equal(sr, sens[rows[:, 0], rows[:, 2], rows[:, 1]])

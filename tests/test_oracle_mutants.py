@@ -40,6 +40,11 @@ MUTANTS = [
     ("bf16_low_bits", "uint32_t w = ((uint32_t)bits) << 16;", "uint32_t w = ((uint32_t)bits) << 15;"),
     ("out_overwritten_not_summed", "out_row[d] += w * bf16_to_f64(vj[d]);",
      "out_row[d] = w * bf16_to_f64(vj[d]);"),
+    # the output rounding-sensitivity sums
+    ("sens_signed", "sens_row[d] += w * fabs(bf16_to_f64(vj[d]));", "sens_row[d] += w * bf16_to_f64(vj[d]);"),
+    ("sens_unnormalised", "for (int64_t d = 0; d < D; ++d) sens_row[d] /= l;", ""),
+    ("sens_weight_squared", "sens_row[d] += w * fabs(bf16_to_f64(vj[d]));",
+     "sens_row[d] += w * w * fabs(bf16_to_f64(vj[d]));"),
 ]
 
 PIN_FUNCS = [
@@ -57,6 +62,8 @@ PIN_FUNCS = [
     pins.test_other_segment_does_not_leak,
     pins.test_lse_bounds,
     pins.test_matches_40_digit_decimal_evaluation,
+    lambda: pins.test_output_sensitivity_equals_first_order_deviation("packed"),
+    pins.test_output_sensitivity_bounds_and_reduces,
 ]
 
 

@@ -3,7 +3,8 @@ same seeded bf16 inputs, element by element, plus bit-exact properties.
 
 Sizes span several 256-query / 64-key tiles and ragged tails; segment layouts
 cover single, padded, packed, interleaved (non-contiguous), one-token and
-all-padding cases.
+all-padding cases, negative IDs, and the int32 extremes (-2^31, 2^31 - 1 and
+their neighbours, which sit next to the tile classifier's empty-set values).
 """
 import math
 
@@ -17,7 +18,8 @@ from gpu_helpers import (check_full, run_gpu, run_oracle, valid_rows)
 pytestmark = pytest.mark.gpu
 
 SEQS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000]
-KINDS = [None, "single", "padded", "packed", "interleaved", "singletons", "allpad"]
+KINDS = [None, "single", "padded", "packed", "interleaved", "singletons", "allpad", "negative",
+         "extreme"]
 
 
 def _case(B, S, H, D, kind, seed, sigma_qk=1.0):
@@ -31,9 +33,9 @@ def test_tiny_reference_workload_full(need_gpu):
     x = W.make_inputs(w)
     print(f"case tiny_ref B={w.B} S={w.S} H={w.H} D={w.D}", flush=True)
     out_g, lse_g = run_gpu(x, x["seg_q"], x["seg_kv"], w.scale)
-    out_o, lse_o = run_oracle(x, x["seg_q"], x["seg_kv"], w.scale)
+    out_o, lse_o, sens_o = run_oracle(x, x["seg_q"], x["seg_kv"], w.scale)
     has = valid_rows(x["seg_q"], x["seg_kv"], w.B, w.S)
-    st = check_full(out_g, lse_g, out_o, lse_o, has)
+    st = check_full(out_g, lse_g, out_o, lse_o, has, sens_o)
     print("tiny_ref", st)
 
 
@@ -46,9 +48,9 @@ def test_shape_and_segment_sweep(need_gpu, S, D, kind):
     print(f"case sweep B={B} S={S} H={H} D={D} kind={kind}", flush=True)
     scale = 1.0 / math.sqrt(D)
     out_g, lse_g = run_gpu(x, seg, None if seg is None else seg.clone(), scale)
-    out_o, lse_o = run_oracle(x, seg, None if seg is None else seg.clone(), scale)
+    out_o, lse_o, sens_o = run_oracle(x, seg, None if seg is None else seg.clone(), scale)
     has = valid_rows(seg, seg, B, S)
-    check_full(out_g, lse_g, out_o, lse_o, has)
+    check_full(out_g, lse_g, out_o, lse_o, has, sens_o)
 
 
 @pytest.mark.parametrize("kind", [None, "packed", "interleaved"], ids=str)
@@ -57,8 +59,8 @@ def test_long_ragged_sequence(need_gpu, kind):
     x, seg = _case(B, S, H, D, kind, seed=4097, sigma_qk=2.0)
     print(f"case long B={B} S={S} H={H} D={D} kind={kind}", flush=True)
     out_g, lse_g = run_gpu(x, seg, None if seg is None else seg.clone(), 1 / math.sqrt(D))
-    out_o, lse_o = run_oracle(x, seg, None if seg is None else seg.clone(), 1 / math.sqrt(D))
-    check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg, seg, B, S))
+    out_o, lse_o, sens_o = run_oracle(x, seg, None if seg is None else seg.clone(), 1 / math.sqrt(D))
+    check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg, seg, B, S), sens_o)
 
 
 def test_distinct_query_and_key_segments(need_gpu):
@@ -70,8 +72,8 @@ def test_distinct_query_and_key_segments(need_gpu):
     seg_kv[seg_kv == 3] = 2  # ID 3 exists only among the queries
     print("case distinct segs", flush=True)
     out_g, lse_g = run_gpu(x, seg_q, seg_kv, 0.125)
-    out_o, lse_o = run_oracle(x, seg_q, seg_kv, 0.125)
-    check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg_q, seg_kv, B, S))
+    out_o, lse_o, sens_o = run_oracle(x, seg_q, seg_kv, 0.125)
+    check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg_q, seg_kv, B, S), sens_o)
 
 
 def test_peaky_softmax_wide_range(need_gpu):
@@ -81,8 +83,8 @@ def test_peaky_softmax_wide_range(need_gpu):
     seg = W.random_segments(B, S, 3, "packed")
     print("case peaky", flush=True)
     out_g, lse_g = run_gpu(x, seg, seg.clone(), 1 / math.sqrt(D))
-    out_o, lse_o = run_oracle(x, seg, seg.clone(), 1 / math.sqrt(D))
-    print(check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg, seg, B, S)))
+    out_o, lse_o, sens_o = run_oracle(x, seg, seg.clone(), 1 / math.sqrt(D))
+    print(check_full(out_g, lse_g, out_o, lse_o, valid_rows(seg, seg, B, S), sens_o))
 
 
 # --- bit-exact properties -------------------------------------------------------

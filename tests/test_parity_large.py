@@ -45,9 +45,9 @@ def test_sampled_rows_vs_oracle(need_gpu, name):
     heads = list(range(w.H)) if w.H <= 16 else list(range(0, w.H, 3))
     rows = sample_rows(w.S, w.H, w.B, w.seg_runs, n_random=48, seed=1, heads=heads)
     print(f"case {name}: oracle on {len(rows)} rows", flush=True)
-    out_o, lse_o = run_oracle(x, x["seg_q"], x["seg_kv"], w.scale, rows=rows)
+    out_o, lse_o, sens_o = run_oracle(x, x["seg_q"], x["seg_kv"], w.scale, rows=rows)
     has = valid_rows(x["seg_q"], x["seg_kv"], w.B, w.S)
-    st = check_rows(out_c, lse_c, rows, out_o, lse_o, has)
+    st = check_rows(out_c, lse_c, rows, out_o, lse_o, has, sens_o)
     print(name, st, flush=True)
 
 
@@ -118,10 +118,10 @@ def test_masked_maximum_sequence(need_gpu, S, D):
     extra = [(0, 0, i) for i in (2, 63, 64, 100, 200, 254, 255, 256, 257)]
     rows = np.unique(np.concatenate([rows, np.array(extra, dtype=np.int64)]), axis=0)
     print(f"case masked max S={S} D={D}: oracle on {len(rows)} rows", flush=True)
-    out_o, lse_o = run_oracle(x, seg_q, seg_kv, 1.0 / math.sqrt(D), rows=rows)
+    out_o, lse_o, sens_o = run_oracle(x, seg_q, seg_kv, 1.0 / math.sqrt(D), rows=rows)
     has = valid_rows(seg_q, seg_kv, B, S)
     assert has[0, :256].all() and not has[0, S - 5:].any()
-    st = check_rows(out_c, lse_c, rows, out_o, lse_o, has)
+    st = check_rows(out_c, lse_c, rows, out_o, lse_o, has, sens_o)
     print(st, flush=True)
     # Every padded row is +0.0 / -inf, every other output is finite.
     assert np.all(out_c[0, S - 5:].view(torch.int16).numpy() == 0)
@@ -175,3 +175,34 @@ def test_constant_value_every_row(need_gpu, name):
     assert np.all(err <= (2 * 2.0 ** -8 + 1e-4) * np.abs(cc) + 1e-6), float(err.max())
     if (~has).any():
         assert np.all(out.cpu().view(torch.int16).numpy()[~has] == 0)
+
+
+# Bit canaries at the 480p layer's size (B=1, S=32,760, H=12): 1,536 query
+# blocks, so the unmasked call's persistent grid of 256 workgroups runs six
+# items per workgroup (reusing its LDS and registers after each), while a
+# masked call runs one workgroup per item and a one-head call 128 items on
+# 128 workgroups.  Every route must give the same bits.
+def test_full_size_bit_canaries(need_gpu):
+    import spatiotemporal_attention_amd as vdx
+    w = W.WORKLOADS["dit480p_small"]
+    print(f"case {w.name}: bit canaries (repeat, all-ones IDs, head split)", flush=True)
+    x = W.make_inputs(w)
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    a_out, a_lse = vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale)
+    b_out, b_lse = vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16)), "repeat run"
+    assert torch.equal(a_lse.view(torch.int32), b_lse.view(torch.int32)), "repeat run"
+    del b_out, b_lse
+    ones = torch.ones(w.B, w.S, dtype=torch.int32, device="cuda")
+    c_out, c_lse = vdx.attn_fwd(d["q"], d["k"], d["v"], ones, ones.clone(), scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out.view(torch.int16), c_out.view(torch.int16)), "NULL vs all-ones IDs"
+    assert torch.equal(a_lse.view(torch.int32), c_lse.view(torch.int32)), "NULL vs all-ones IDs"
+    del c_out, c_lse
+    for h in (0, 5, w.H - 1):
+        dh = {n: d[n][:, :, h:h + 1].contiguous() for n in ("q", "k", "v")}
+        o1, l1 = vdx.attn_fwd(dh["q"], dh["k"], dh["v"], scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), a_out[:, :, h:h + 1].contiguous().view(torch.int16)), h
+        assert torch.equal(l1.view(torch.int32), a_lse[:, h:h + 1].contiguous().view(torch.int32)), h
