@@ -24,8 +24,18 @@ With --workload natten_vae_decoder (or natten_tiny) the step is one
 vdx_natten3d_fwd call instead (3D neighbourhood attention over a t x h x w
 grid), and the FLOP count is that of the window pairs: 4*D*H*B*S*|window|.
 
+With --rope the step is one vdx_rope3d_attn_fwd call on the workload: the 3D
+rotary position embedding of the keys (a pre-pass into a resident buffer) and
+of the queries (in the attention kernel's prologue), then the same attention;
+the FLOP count is the attention's.
+
+Every line also carries the graphics clock and socket power sampled with
+amdsmi during the timed steps (null where amdsmi cannot read them), and the
+CPU baseline's row rate with the extrapolated time of the whole workload on
+the oracle (labelled as an extrapolation).
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
-       [--no-cpu-baseline] [--copy-calib]
+       [--rope] [--no-cpu-baseline] [--copy-calib]
 """
 from __future__ import annotations
 
@@ -35,6 +45,7 @@ import json
 import math
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -161,9 +172,13 @@ def cpu_baseline(w: W.Workload, x, target_s: float = 15.0):
     oracle.attn_fwd(qb, kb, vb, sq, sk, float(np.float32(w.scale)), rows=rows, n_threads=cores)
     dt = time.perf_counter() - t0
     rate = flops(rows) / dt / 1e12
+    full = 4.0 * w.D * w.H * valid_pairs(w)
     return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} random (b,h,i) rows of {w.name}, each over its full key set, "
-                      f"{dt:.1f} s on {cores} threads"}
+                      f"{dt:.1f} s on {cores} threads",
+            "rows_per_s": round(n / dt, 2),
+            "extrapolated_full_workload_s": round(full / (rate * 1e12), 1),
+            "extrapolation": "whole-workload oracle time = the workload's valid-pair FLOP / the sampled rate"}
 
 
 def natten_window_volume(w) -> int:
@@ -231,9 +246,86 @@ def natten_cpu_baseline(w, x, target_s: float = 15.0):
                         n_threads=cores)
     dt = time.perf_counter() - t0
     rate = 4.0 * w.D * natten_window_volume(w) * n / dt / 1e12
+    full = 4.0 * w.D * w.H * w.B * w.S * natten_window_volume(w)
     return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} random (b,h,i) rows of {w.name}, each over its full window, "
-                      f"{dt:.1f} s on {cores} threads"}
+                      f"{dt:.1f} s on {cores} threads",
+            "rows_per_s": round(n / dt, 2),
+            "extrapolated_full_workload_s": round(full / (rate * 1e12), 1),
+            "extrapolation": "whole-workload oracle time = the workload's window-pair FLOP / the sampled rate"}
+
+
+class ClockSampler:
+    """Reads the GPU's current graphics clock (MHz) and socket power (W) with
+    amdsmi every `period` seconds from a background thread while the timed
+    steps run.  Any amdsmi failure leaves the summary null."""
+
+    def __init__(self, period: float = 0.05):
+        self.period = period
+        self.clk, self.pwr = [], []
+        self.err = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            bus = None
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            if hasattr(props, "pci_bus_id"):
+                bus = int(props.pci_bus_id)
+            for h in handles:
+                try:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                        self._handle = h
+                except Exception:  # pragma: no cover
+                    pass
+            if self._handle is None and len(handles) == 1:
+                self._handle = handles[0]
+            self._smi = amdsmi
+        except Exception as e:  # pragma: no cover - no driver here
+            self.err = f"{type(e).__name__}: {e}"
+
+    def _run(self):
+        smi = self._smi
+        while not self._stop.is_set():
+            try:
+                c = smi.amdsmi_get_clock_info(self._handle, smi.AmdSmiClkType.GFX)
+                self.clk.append(float(c["clk"]))
+                p = smi.amdsmi_get_power_info(self._handle)
+                w = p.get("current_socket_power", p.get("average_socket_power"))
+                if isinstance(w, (int, float)):
+                    self.pwr.append(float(w))
+            except Exception as e:  # pragma: no cover
+                self.err = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.clk:
+            return {"gfx_clock_mhz_median": None, "source": "amdsmi", "error": self.err or "no handle"}
+        return {"gfx_clock_mhz_median": float(np.median(self.clk)),
+                "gfx_clock_mhz_mean": round(float(np.mean(self.clk)), 1),
+                "socket_power_w_median": float(np.median(self.pwr)) if self.pwr else None,
+                "samples": len(self.clk),
+                "source": f"amdsmi current GFX clock and socket power, every {self.period * 1e3:.0f} ms "
+                          f"during the timed steps"}
+
+
+CLOCK = {"summary": None}
 
 
 def time_steps(step, stream, steps, warmup):
@@ -244,13 +336,16 @@ def time_steps(step, stream, steps, warmup):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    sampler = ClockSampler()
+    with sampler:
+        t0 = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    CLOCK["summary"] = sampler.summary()
     kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     ms_per_step = wall * 1e3 / steps
     log(f"timed {steps} steps: {ms_per_step:.3f} ms/step wall, "
@@ -289,9 +384,14 @@ def bwd_cpu_baseline(w: W.Workload, x, dout, target_s: float = 15.0):
     oracle.attn_bwd_dq_rows(qb, kb, vb, db, sq, sk, float(np.float32(w.scale)), rows,
                             n_threads=cores)
     dt = time.perf_counter() - t0
-    return {"value": flops(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    rate = flops(rows) / dt / 1e12
+    full = 6.0 * w.D * w.H * valid_pairs(w)
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"dq of {n} random (b,h,i) rows of {w.name} (scores, dP and dq over the "
-                      f"row's full key set), {dt:.1f} s on {cores} threads"}
+                      f"row's full key set), {dt:.1f} s on {cores} threads",
+            "rows_per_s": round(n / dt, 2),
+            "extrapolated_full_workload_s": round(full / (rate * 1e12), 1),
+            "extrapolation": "dq of every row (6*D FLOP per valid pair) at the sampled rate"}
 
 
 def bwd_main(args, vdx):
@@ -336,6 +436,7 @@ def bwd_main(args, vdx):
                      # reads q, k, v, out, dout, lse; writes dq, dk, dv
                      "algorithmic_bytes": 2 * 8 * n + 4 * w.B * w.H * w.S,
                      "kernel_ms_mean": round(call_ms, 4)},
+        "clock": CLOCK["summary"],
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
@@ -381,6 +482,7 @@ def natten_main(args, vdx):
                      "traffic": load_traffic(w.name, "natten"),
                      "algorithmic_bytes": 4 * 2 * n + 4 * w.B * w.H * w.S,
                      "kernel_ms_mean": round(kernel_ms, 4)},
+        "clock": CLOCK["summary"],
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
@@ -398,6 +500,8 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE,
                     choices=sorted(W.WORKLOADS) + sorted(W.NATTEN_WORKLOADS))
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--rope", action="store_true",
+                    help="time vdx_rope3d_attn_fwd (3D rotary embedding of q and k, then attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
@@ -414,6 +518,8 @@ def main():
     if args.copy_calib:
         copy_calibration()
         return
+    if args.rope and (args.workload in W.NATTEN_WORKLOADS or args.pass_ != "fwd"):
+        ap.error("--rope applies to the forward of the segment-masked workloads")
     if args.workload in W.NATTEN_WORKLOADS:
         if args.pass_ != "fwd":
             ap.error("the neighbourhood-attention workloads have a forward pass only")
@@ -424,42 +530,46 @@ def main():
         return
 
     w = W.WORKLOADS[args.workload]
-    log(f"workload {w.name}: B={w.B} S={w.S} H={w.H} D={w.D} masked={w.masked}")
+    log(f"workload {w.name}: B={w.B} S={w.S} H={w.H} D={w.D} masked={w.masked} rope={args.rope}")
     x = W.make_inputs(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
     out = torch.empty_like(d["q"])
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    rope_cfg = None
+    if args.rope:
+        r = W.workload_rope3d(w)
+        rr = dict(pos=r.pos.to(dev), cos=[c.to(dev) for c in r.cos], sin=[t.to(dev) for t in r.sin],
+                  dims=r.dims, interleaved=r.interleaved)
+        k_rot = torch.empty_like(d["k"])
+        rope_cfg = {"dims": list(r.dims), "interleaved": r.interleaved, "grids": W.ROPE_GRIDS[w.name],
+                    "theta": W.ROPE_THETA}
 
-    def step():
-        vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale,
-                     out=out, lse=lse, stream=stream)
+        def step():
+            vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=d["seg_q"], seg_kv=d["seg_kv"],
+                                scale=w.scale, k_rot=k_rot, out=out, lse=lse, stream=stream)
+    else:
+        def step():
+            vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale,
+                         out=out, lse=lse, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    ms_per_step = wall * 1e3 / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, "
-        f"kernel mean {np.mean(kernel_ms):.3f} ms (min {np.min(kernel_ms):.3f}, "
-        f"median {np.median(kernel_ms):.3f})")
+    ms_per_step, kernel_ms = time_steps(step, stream, args.steps, args.warmup)
+    clock = CLOCK["summary"]
+    prepass_ms = None
+    if args.rope:
+        # the key pre-pass alone, timed the same way
+        prepass_ms = time_steps(lambda: vdx.rope3d_apply(d["k"], **rr, out=k_rot, stream=stream), stream,
+                                max(3, args.steps), 1)[1]
 
     flop = 4.0 * w.D * w.H * valid_pairs(w)
     value = flop / (ms_per_step * 1e-3) / 1e12
-    achieved = flop / (float(np.mean(kernel_ms)) * 1e-3) / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    config = {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D,
+              "segments": "none" if w.seg_runs is None else w.seg_runs,
+              "flop_per_step": flop, "peak_frac": round(value / PEAK_BF16_TFLOPS, 4)}
+    if rope_cfg is not None:
+        config["rope3d"] = rope_cfg
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -473,15 +583,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D,
-                   "segments": "none" if w.seg_runs is None else w.seg_runs,
-                   "flop_per_step": flop, "peak_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+        "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(w.name),
+                     "traffic": None if args.rope else load_traffic(w.name),
                      "algorithmic_bytes": algorithmic_bytes(w),
-                     "kernel_ms_mean": round(float(np.mean(kernel_ms)), 4)},
+                     "kernel_ms_mean": round(kernel_ms, 4)},
+        "clock": clock,
     }
+    if args.rope:
+        line["roofline"]["scope"] = "vdx_rope3d_attn_fwd call (key pre-pass + attention kernel)"
+        line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

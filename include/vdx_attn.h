@@ -1,8 +1,10 @@
 /*
  * vdx_attn.h -- C ABI of the segment-masked, non-causal flash-attention
- * forward for video-DiT token volumes on gfx950 (MI355X), and of the 3D
- * neighbourhood (windowed) attention forward (vdx_natten3d_fwd, below), and
- * of the attention gradient (vdx_attn_bwd, below).
+ * forward for video-DiT token volumes on gfx950 (MI355X), of the 3D
+ * neighbourhood (windowed) attention forward (vdx_natten3d_fwd, below), of
+ * the attention gradient (vdx_attn_bwd, below), and of the 3D rotary
+ * position embedding of queries and keys, alone (vdx_rope3d_apply) and fused
+ * into the attention forward (vdx_rope3d_attn_fwd).
  *
  * The operation (vidax paper, arXiv:2609.18077):
  *   - section 1, "Spatiotemporal constraints in video generation": full
@@ -42,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VDX_ABI_VERSION 4
+#define VDX_ABI_VERSION 5
 
 /* Status codes.  Argument validation runs before any HIP call, in the order
  * below (NULL -> segment pair -> shape -> head dim -> scale -> alignment),
@@ -65,9 +67,14 @@ enum vdx_status {
     VDX_ERR_LAUNCH = 8,   /* the kernel launch reported an error                */
     VDX_ERR_WINDOW = 9,   /* vdx_natten3d_fwd: a window size is even or < 1, or
                              the effective x window min(KW, NW) exceeds 13      */
-    VDX_ERR_WORKSPACE = 10 /* vdx_attn_bwd: workspace NULL, smaller than
+    VDX_ERR_WORKSPACE = 10, /* vdx_attn_bwd: workspace NULL, smaller than
                              vdx_attn_bwd_workspace_size(B, S, H), or not
                              16-byte aligned                                    */
+    VDX_ERR_ROPE = 11     /* vdx_rope3d_*: the embedding description is NULL,
+                             its pos is NULL, a section width is odd or < 0,
+                             the widths add up to more than D, a row count is
+                             < 0, a table of a section of nonzero width is
+                             NULL, or pos / a table is not 4-byte aligned      */
 };
 
 /*
@@ -190,6 +197,77 @@ int vdx_attn_bwd(const void* q, const void* k, const void* v,
  * longest-first rank of every 128-row block of both sweeps, used with
  * segment IDs).  0 if B, S or H < 1 or the size overflows. */
 size_t vdx_attn_bwd_workspace_size(int B, int S, int H);
+
+/*
+ * 3D rotary position embedding of queries and keys.
+ *
+ * The operation (vidax paper, arXiv:2609.18077): section 2, "3D RoPE, 3D VAEs,
+ * and flash attention", places a rotary position embedding over time, height
+ * and width on the queries and keys right before attention and notes that
+ * the families' conventions differ and are kept exactly; section 3.1 names
+ * Wan and CogVideoX1.5 as 3D-RoPE DiTs.  No formula is printed, so every
+ * family-specific choice is an argument:
+ *   - features [0, dims[0]), [dims[0], dims[0] + dims[1]) and
+ *     [dims[0] + dims[1], dims[0] + dims[1] + dims[2]) of the head dim belong
+ *     to the t, y and x axes; later features are not rotated;
+ *   - pair p of an axis section at offset o and width w is the features
+ *     (o + 2p, o + 2p + 1) if interleaved, else (o + p, o + p + w / 2);
+ *   - its angle is c = cos_tab[a][pos_a * (w / 2) + p],
+ *     s = sin_tab[a][pos_a * (w / 2) + p] at the token's coordinate pos_a;
+ *   - (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c), formed exactly up to one
+ *     rounding in fp64 and rounded once to bf16 (to nearest, ties to even);
+ *   - a token with a coordinate outside its axis's table (< 0 or >= n[a]:
+ *     text tokens, padding) is not rotated.
+ */
+typedef struct vdx_rope3d {
+    const int32_t* pos;        /* DEVICE int32 [B, S, 3]: (t, y, x) per token     */
+    const float* cos_tab[3];   /* DEVICE fp32 [n[a], dims[a] / 2] per axis (t, y,
+                                  x); may be NULL where dims[a] == 0              */
+    const float* sin_tab[3];   /* DEVICE fp32, same shapes                       */
+    int n[3];                  /* table rows per axis, >= 0                      */
+    int dims[3];               /* even section widths, sum <= D                  */
+    int interleaved;           /* nonzero: pairs (2p, 2p + 1), else (p, p + w/2) */
+} vdx_rope3d;
+
+/*
+ * vdx_rope3d_apply -- y = the 3D rotary embedding of x.
+ *
+ *   x, y      bf16 [B, S, H, D], contiguous, 16-byte aligned; y may be x (in
+ *             place), otherwise they must not overlap.
+ *   rope      host pointer to the description above (read during the call
+ *             only); the tensors it points to must stay alive until the
+ *             stream work completes.
+ *   B, S, H   >= 1; D is 64 or 128.
+ * Validation runs before any HIP call, in the order NULL (x, y) -> shape ->
+ * head dim -> alignment -> rope, and reports the first failure without
+ * touching device memory.  Asynchronous on `stream`; deterministic.
+ */
+int vdx_rope3d_apply(const void* x, void* y, const vdx_rope3d* rope,
+                     int B, int S, int H, int D, hipStream_t stream);
+
+/*
+ * vdx_rope3d_attn_fwd -- vdx_attn_fwd on the 3D-rotary-embedded queries and
+ * keys (v is used as given): out and lse are bit for bit those of
+ * vdx_attn_fwd called on vdx_rope3d_apply(q) and vdx_rope3d_apply(k).  The
+ * keys are rotated once into k_rot by a pre-pass on `stream`; the queries are
+ * rotated in registers as each workgroup loads them.
+ *
+ *   q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale, stream
+ *             as for vdx_attn_fwd.
+ *   rope      as for vdx_rope3d_apply.
+ *   k_rot     DEVICE bf16 [B, S, H, D], 16-byte aligned, owned by the caller:
+ *             receives the rotated keys.  It may be k itself (the keys are
+ *             then rotated in place); otherwise it must not overlap q, k, v,
+ *             out or lse.
+ * Validation: NULL (q, k, v, out, lse, k_rot) -> segment pair -> shape -> head
+ * dim -> scale -> alignment (k_rot 16-byte as well) -> rope, before any HIP
+ * call and without touching device memory.
+ */
+int vdx_rope3d_attn_fwd(const void* q, const void* k, const void* v,
+                        const int32_t* seg_q, const int32_t* seg_kv,
+                        const vdx_rope3d* rope, void* k_rot,
+                        void* out, float* lse,
+                        int B, int S, int H, int D, float scale, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* vdx_status_str(int status);

@@ -20,6 +20,13 @@ Appendix A, Table 4, group 4 for its 11 x 11 x 11 window).
 dout, recomputing the probabilities from the forward's lse (section 5 lists
 training and fine-tuning, which need them).
 
+``rope3d_apply`` rotates a [B, S, H, D] tensor by a 3D rotary position
+embedding over (t, y, x) whose conventions the caller gives (per-axis
+cos/sin tables, head-dim section widths, pairing, per-token positions);
+``rope3d_attn_fwd`` is ``attn_fwd`` on the rotated queries and keys, with the
+queries rotated as the attention kernel loads them (section 2 places the 3D
+RoPE right before attention and keeps each family's convention).
+
 Every step runs in the hand-written HIP kernels behind the C ABI
 (include/vdx_attn.h); this module only checks arguments and passes device
 pointers and the current stream.
@@ -34,13 +41,33 @@ import torch
 from . import _native
 from ._native import abi_version, status_str
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "natten3d_fwd", "abi_version", "status_str", "VdxError"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "natten3d_fwd", "rope3d_apply",
+           "rope3d_attn_fwd", "abi_version", "status_str", "VdxError"]
 
 
 class VdxError(ValueError):
     def __init__(self, rc: int):
         super().__init__(status_str(rc))
         self.rc = rc
+
+
+def _outputs(q: torch.Tensor, out: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+             stream: torch.cuda.Stream) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Checks caller-given out / lse, or allocates them on the launch stream
+    (so the caching allocator orders their reuse after the kernel)."""
+    B, S, H, D = q.shape
+    if out is not None and (out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous()
+                            or out.device != q.device):
+        raise ValueError("out must be a contiguous bf16 tensor like q")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S)
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    return out, lse
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -69,16 +96,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError(f"{name} must be a contiguous int32 CUDA tensor of shape {(B, S)}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous bf16 tensor like q")
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    out, lse = _outputs(q, out, lse, stream)
     with torch.cuda.device(q.device):
         rc = _native.attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   0 if seg_q is None else seg_q.data_ptr(),
@@ -115,16 +135,9 @@ def natten3d_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous bf16 tensor like q")
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    out, lse = _outputs(q, out, lse, stream)
     with torch.cuda.device(q.device):
         rc = _native.natten3d_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       lse.data_ptr(), B, NT, NH, NW, H, D, KT, KH, KW, scale,
@@ -167,21 +180,25 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
             raise ValueError(f"{name} must be a contiguous int32 CUDA tensor of shape {(B, S)}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    grads = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t is None:
-            t = torch.empty_like(q)
-        elif t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous bf16 tensor like q")
-        grads.append(t)
-    need = _native.attn_bwd_workspace_size(B, S, H)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    elif not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
-        raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
-    ws_bytes = workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None and (t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor like q")
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()
+                                  or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+    need = _native.attn_bwd_workspace_size(B, S, H)
+    # Tensors made here belong to the launch stream: the caching allocator
+    # then hands a freed block (the workspace, when this function allocated
+    # it, is freed on return) to later work only in that stream's order, never
+    # while the kernels still use it.
+    with torch.cuda.stream(stream):
+        grads = [torch.empty_like(q) if t is None else t for t in (dq, dk, dv)]
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         rc = _native.attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   0 if seg_q is None else seg_q.data_ptr(),
@@ -198,3 +215,101 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
 def attn_bwd_workspace_size(B: int, S: int, H: int) -> int:
     """Bytes of workspace ``attn_bwd`` needs for (B, S, H)."""
     return _native.attn_bwd_workspace_size(B, S, H)
+
+
+def _rope_desc(q: torch.Tensor, pos: torch.Tensor, cos, sin, dims, interleaved: bool):
+    """Checks the rotary-embedding tensors against q [B, S, H, D] and returns
+    the C description (the tensors must outlive the call's stream work)."""
+    B, S, H, D = q.shape
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B, S, 3) or not pos.is_cuda or not pos.is_contiguous() \
+            or pos.device != q.device:
+        raise ValueError(f"pos must be a contiguous int32 CUDA tensor of shape {(B, S, 3)}")
+    if len(cos) != 3 or len(sin) != 3 or len(dims) != 3:
+        raise ValueError("cos, sin and dims need one entry per axis (t, y, x)")
+    n = []
+    for a in range(3):
+        c, s_ = cos[a], sin[a]
+        for name, t in (("cos", c), ("sin", s_)):
+            if t.dtype != torch.float32 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous() \
+                    or t.device != q.device or t.shape[1] != int(dims[a]) // 2:
+                raise ValueError(f"{name}[{a}] must be a contiguous fp32 CUDA tensor [n, dims[{a}] / 2]")
+        if c.shape != s_.shape:
+            raise ValueError(f"cos[{a}] and sin[{a}] differ in shape")
+        n.append(int(c.shape[0]))
+    ptr = lambda t: t.data_ptr() if t.numel() else 0
+    return _native.rope3d_desc(pos.data_ptr(), [ptr(c) for c in cos], [ptr(s_) for s_ in sin], n,
+                               [int(d) for d in dims], interleaved)
+
+
+def rope3d_apply(x: torch.Tensor, pos: torch.Tensor, cos, sin, dims, interleaved: bool = True,
+                 out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """3D rotary position embedding of x (bf16 [B, S, H, D], contiguous).
+
+    pos: int32 [B, S, 3], the (t, y, x) of every token (a token outside the
+    tables is left as is); cos / sin: per axis (t, y, x) an fp32 [n_a, d_a / 2]
+    table; dims: section widths (d_t, d_h, d_w); interleaved: pairs
+    (2p, 2p + 1) of a section, else (p, p + d_a / 2).  out may be x (in place).
+    """
+    if x.dim() != 4 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 CUDA tensor [B, S, H, D]")
+    B, S, H, D = x.shape
+    desc = _rope_desc(x, pos, cos, sin, dims, interleaved)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    if out is None:
+        with torch.cuda.stream(stream):
+            out = torch.empty_like(x)
+    elif out.dtype != torch.bfloat16 or out.shape != x.shape or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous bf16 tensor like x")
+    with torch.cuda.device(x.device):
+        rc = _native.rope3d_apply_raw(x.data_ptr(), out.data_ptr(), desc, B, S, H, D, stream.cuda_stream)
+    if rc != 0:
+        raise VdxError(rc)
+    return out
+
+
+def rope3d_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, cos, sin, dims,
+                    interleaved: bool = True, seg_q: Optional[torch.Tensor] = None,
+                    seg_kv: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                    k_rot: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``attn_fwd`` on the 3D-rotary-embedded queries and keys (see
+    ``rope3d_apply``; v is used as given).  k_rot: bf16 like k, receives the
+    rotated keys (allocated here if None; may be k itself).  Returns
+    (out bf16 [B,S,H,D], lse fp32 [B,H,S])."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S, H, D]")
+    B, S, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of shape {tuple(q.shape)}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if (seg_q is None) != (seg_kv is None):
+        raise VdxError(_native.VDX_ERR_SEG_PAIR)
+    for name, t in (("seg_q", seg_q), ("seg_kv", seg_kv)):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (B, S) or not t.is_cuda
+                              or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous int32 CUDA tensor of shape {(B, S)}")
+    desc = _rope_desc(q, pos, cos, sin, dims, interleaved)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    out, lse = _outputs(q, out, lse, stream)
+    if k_rot is None:
+        with torch.cuda.stream(stream):
+            k_rot = torch.empty_like(k)
+    elif k_rot.dtype != torch.bfloat16 or k_rot.shape != k.shape or not k_rot.is_contiguous() \
+            or k_rot.device != q.device:
+        raise ValueError("k_rot must be a contiguous bf16 tensor like k")
+    with torch.cuda.device(q.device):
+        rc = _native.rope3d_attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         0 if seg_q is None else seg_q.data_ptr(),
+                                         0 if seg_kv is None else seg_kv.data_ptr(), desc, k_rot.data_ptr(),
+                                         out.data_ptr(), lse.data_ptr(), B, S, H, D, scale, stream.cuda_stream)
+    if rc != 0:
+        raise VdxError(rc)
+    return out, lse

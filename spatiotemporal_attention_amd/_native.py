@@ -21,9 +21,16 @@ VDX_ERR_DEVICE = 7
 VDX_ERR_LAUNCH = 8
 VDX_ERR_WINDOW = 9
 VDX_ERR_WORKSPACE = 10
+VDX_ERR_ROPE = 11
 
 EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_workspace_size",
-            "vdx_status_str", "vdx_abi_version")
+            "vdx_rope3d_apply", "vdx_rope3d_attn_fwd", "vdx_status_str", "vdx_abi_version")
+
+
+class Rope3D(ctypes.Structure):
+    """struct vdx_rope3d of include/vdx_attn.h (device pointers as integers)."""
+    _fields_ = [("pos", ctypes.c_void_p), ("cos_tab", ctypes.c_void_p * 3), ("sin_tab", ctypes.c_void_p * 3),
+                ("n", ctypes.c_int * 3), ("dims", ctypes.c_int * 3), ("interleaved", ctypes.c_int)]
 
 
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -40,6 +47,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vdx_attn_bwd.argtypes = [p] * 12 + [ctypes.c_size_t] + [i] * 4 + [ctypes.c_float, p]
     lib.vdx_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.vdx_attn_bwd_workspace_size.argtypes = [i, i, i]
+    lib.vdx_rope3d_apply.restype = i
+    lib.vdx_rope3d_apply.argtypes = [p, p, ctypes.POINTER(Rope3D), i, i, i, i, p]
+    lib.vdx_rope3d_attn_fwd.restype = i
+    lib.vdx_rope3d_attn_fwd.argtypes = [p, p, p, p, p, ctypes.POINTER(Rope3D), p, p, p, i, i, i, i,
+                                        ctypes.c_float, p]
     lib.vdx_status_str.restype = ctypes.c_char_p
     lib.vdx_status_str.argtypes = [i]
     lib.vdx_abi_version.restype = i
@@ -83,3 +95,31 @@ def attn_bwd_raw(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, ws, ws_byte
 
 def attn_bwd_workspace_size(B, S, H) -> int:
     return int(lib.vdx_attn_bwd_workspace_size(int(B), int(S), int(H)))
+
+
+def rope3d_desc(pos, cos, sin, n, dims, interleaved) -> Rope3D:
+    """A struct vdx_rope3d from integer device addresses (0 for NULL)."""
+    r = Rope3D()
+    r.pos = pos or None
+    for a in range(3):
+        r.cos_tab[a] = cos[a] or None
+        r.sin_tab[a] = sin[a] or None
+        r.n[a] = int(n[a])
+        r.dims[a] = int(dims[a])
+    r.interleaved = 1 if interleaved else 0
+    return r
+
+
+def rope3d_apply_raw(x, y, rope: Rope3D, B, S, H, D, stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL); rope may be None."""
+    return int(lib.vdx_rope3d_apply(x or None, y or None, None if rope is None else ctypes.byref(rope),
+                                    int(B), int(S), int(H), int(D), stream or None))
+
+
+def rope3d_attn_fwd_raw(q, k, v, seg_q, seg_kv, rope: Rope3D, k_rot, out, lse, B, S, H, D, scale,
+                        stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL); rope may be None."""
+    return int(lib.vdx_rope3d_attn_fwd(q or None, k or None, v or None, seg_q or None, seg_kv or None,
+                                       None if rope is None else ctypes.byref(rope), k_rot or None,
+                                       out or None, lse or None, int(B), int(S), int(H), int(D),
+                                       float(scale), stream or None))

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libvdx_attn.so")
 SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "natten_fwd_kernel.hip"),
-           os.path.join(CSRC, "attn_bwd_kernel.hip"), os.path.join(CSRC, "vdx_attn_api.hip")]
+           os.path.join(CSRC, "attn_bwd_kernel.hip"), os.path.join(CSRC, "rope3d_kernel.hip"),
+           os.path.join(CSRC, "vdx_attn_api.hip")]
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-fvisibility=hidden", "-Wall", "-fno-honor-nans",

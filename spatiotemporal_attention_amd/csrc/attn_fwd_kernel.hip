@@ -52,6 +52,7 @@
 
 #include "attn_common.h"
 #include "attn_fwd_launch.h"
+#include "rope3d.h"
 
 namespace vdx {
 namespace {
@@ -406,13 +407,67 @@ __device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
     if (G == 0) barrier();  // group 0 idles in the last global phase
 }
 
+// 3D rotary embedding of a workgroup's query block, staged in LDS before the
+// K/V ring is in use: the block's kBq rows (D bf16 each, row-major) are copied
+// in, each rotated feature pair is rewritten in place by one thread, and each
+// lane then reads its Q slice from there.  The rule and its rounding are those
+// of the key pre-pass (rope3d.h), so the bits equal a rotated copy of q.  The
+// loops stay rolled, which keeps this prologue's registers far below the main
+// loop's.  Rows past S stay zero.
+template <int D>
+__device__ void rope_stage_q(char* smem, const __bf16* __restrict__ q, const Rope3DDev& r, int b, int h,
+                             int S, int64_t tok_stride, int q0, int tid) {
+    constexpr int kRowChunks = D / 8;
+    static_assert(kBq * D * 2 <= Tile<D>::kRingBytes, "the staged query block must fit in the ring");
+#pragma unroll 1
+    for (int c = tid; c < kBq * kRowChunks; c += kThreads) {
+        const int row = c / kRowChunks, ch = c % kRowChunks;
+        const int tok = q0 + row;
+        bf16x8 x = {};
+        if (tok < S)
+            x = *reinterpret_cast<const bf16x8*>(q + ((int64_t)b * S + tok) * tok_stride + (int64_t)h * D + 8 * ch);
+        *reinterpret_cast<bf16x8*>(smem + (row * D + 8 * ch) * 2) = x;
+    }
+    __syncthreads();
+    const int h0 = r.d[0] >> 1, h1 = r.d[1] >> 1, h2 = r.d[2] >> 1;
+    const int P = h0 + h1 + h2;  // rotated pairs per row
+    uint16_t* sb = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll 1
+    for (int k = tid; k < kBq * P; k += kThreads) {
+        const int row = k / P, pp = k - row * P;
+        const int tok = q0 + row;
+        if (tok >= S) continue;
+        int pos[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) pos[a] = r.pos[((int64_t)b * S + tok) * 3 + a];
+        if (!rope_inside(r, pos)) continue;
+        int a, p, off, half;
+        if (pp < h0) {
+            a = 0, p = pp, off = 0, half = h0;
+        } else if (pp < h0 + h1) {
+            a = 1, p = pp - h0, off = r.d[0], half = h1;
+        } else {
+            a = 2, p = pp - h0 - h1, off = r.d[0] + r.d[1], half = h2;
+        }
+        const int i0 = r.interleaved ? off + 2 * p : off + p;
+        const int i1 = r.interleaved ? off + 2 * p + 1 : off + p + half;
+        const int e = (a == 0 ? pos[0] : (a == 1 ? pos[1] : pos[2])) * half + p;
+        const float c = (a == 0 ? r.cs[0] : (a == 1 ? r.cs[1] : r.cs[2]))[e];
+        const float sn = (a == 0 ? r.sn[0] : (a == 1 ? r.sn[1] : r.sn[2]))[e];
+        const float x0 = bf16_bits_to_f32(sb[row * D + i0]), x1 = bf16_bits_to_f32(sb[row * D + i1]);
+        sb[row * D + i0] = rope_rotate(x0, x1, c, sn, true);
+        sb[row * D + i1] = rope_rotate(x1, x0, c, sn, false);
+    }
+    __syncthreads();
+}
+
 // One query block (256 queries of one (b, h)): work item w of the grid.
-template <int D, bool SEG>
+template <int D, bool SEG, bool ROPE>
 __device__ __forceinline__ void attn_fwd_item(
     char* smem, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const int32_t* __restrict__ seg_q,
     const int32_t* __restrict__ seg_kv, __bf16* __restrict__ out, float* __restrict__ lse, int S,
-    int H, float c_log2, int n_qblk, int n_kvt, int n_wg, int w) {
+    int H, float c_log2, int n_qblk, int n_kvt, int n_wg, int w, const Rope3DDev& rope) {
     using T = Tile<D>;
 
     // ---- tile scheduler: XCD-contiguous renumbering of work items -----------
@@ -450,7 +505,15 @@ __device__ __forceinline__ void attn_fwd_item(
     A.c_log2 = c_log2;
 
     // ---- Q slice -> registers as the B operand of S^T = K Q^T -----------------
-    {
+    if constexpr (ROPE) {
+        rope_stage_q<D>(smem, q, rope, b, h, S, A.tok_stride, qblk * kBq, tid);
+        const char* st = smem + ((wave * 32 + lr) * D + 8 * g) * 2;
+#pragma unroll
+        for (int ks = 0; ks < T::kSteps; ++ks) A.qreg[ks] = *reinterpret_cast<const bf16x8*>(st + ks * 32);
+        A.myseg = SEG ? ((qi < S) ? seg_q[(int64_t)b * S + qi] : 0) : 1;
+        // The classifier's scratch and the ring copies reuse this LDS.
+        __syncthreads();
+    } else {
         const __bf16* qrow = q + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < T::kSteps; ++ks)
@@ -493,8 +556,11 @@ __device__ __forceinline__ void attn_fwd_item(
     if (SEG) {
         // ---- classify the key tiles against this query block (skip / full /
         // partial) and compact the active ones into the LDS list ----------------
-        n_act = classify_tiles<kWaves>(A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem),
-                                       list, meta, wave, lane);
+        // Every lane reads the same count from the LDS; readfirstlane states
+        // that it is wave-uniform, so the loop bounds and ring-slot offsets
+        // derived from it stay in scalar registers.
+        n_act = __builtin_amdgcn_readfirstlane(classify_tiles<kWaves>(
+            A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
     }
 
     // ---- running softmax state and the O^T accumulators -----------------------
@@ -584,16 +650,16 @@ __device__ __forceinline__ void attn_fwd_item(
 // workgroup per item, CUs that pick up new items at different times drift
 // apart and each re-fetches the tiles.  Every workgroup's item count is fixed
 // by G and n_wg, so all waves exit.
-template <int D, bool SEG>
+template <int D, bool SEG, bool ROPE>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
     __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
-    int n_kvt, int n_wg) {
+    int n_kvt, int n_wg, Rope3DDev rope) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
-        attn_fwd_item<D, SEG>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_qblk, n_kvt,
-                              n_wg, w);
+        attn_fwd_item<D, SEG, ROPE>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_qblk,
+                                    n_kvt, n_wg, w, rope);
         // Every wave is done with the LDS of this item before the next one's
         // copies land there.
         __syncthreads();
@@ -632,8 +698,8 @@ constexpr size_t fwd_lds(int n_kvt) {
 static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(kMaxKvTiles) <= kLdsBytes,
               "a full active-tile list must fit in the LDS beside the ring");
 
-template <int D, bool SEG>
-hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+template <int D, bool SEG, bool ROPE>
+hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream) {
     const int n_qblk = (a.S + kBq - 1) / kBq;
     const int n_kvt = (a.S + kBk - 1) / kBk;
     const int64_t n_wg64 = (int64_t)a.B * a.H * n_qblk;
@@ -644,11 +710,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     // the CUs of an XCD in step; with segment IDs items differ (up to 8x on
     // packed clips) and one workgroup per item lets the dispatcher balance them.
     const int grid = SEG ? n_wg : (int)std::min<int64_t>(n_wg64, persistent_workgroups());
-    hipLaunchKernelGGL((attn_fwd_kernel<D, SEG>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, SEG, ROPE>), dim3(grid), dim3(kThreads), lds, stream,
                        reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                        reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
                        reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, c_log2, n_qblk, n_kvt,
-                       n_wg);
+                       n_wg, rope);
     return hipGetLastError();
 }
 
@@ -659,8 +725,17 @@ int64_t queries_per_workgroup() { return kBq; }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     const bool seg = a.seg_q != nullptr;
-    if (a.D == 128) return seg ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
-    return seg ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    const Rope3DDev none{};
+    if (a.D == 128)
+        return seg ? launch_t<128, true, false>(a, none, stream) : launch_t<128, false, false>(a, none, stream);
+    return seg ? launch_t<64, true, false>(a, none, stream) : launch_t<64, false, false>(a, none, stream);
+}
+
+hipError_t launch_rope3d_attn_fwd(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream) {
+    const bool seg = a.seg_q != nullptr;
+    if (a.D == 128)
+        return seg ? launch_t<128, true, true>(a, rope, stream) : launch_t<128, false, true>(a, rope, stream);
+    return seg ? launch_t<64, true, true>(a, rope, stream) : launch_t<64, false, true>(a, rope, stream);
 }
 
 }  // namespace vdx

@@ -7,6 +7,17 @@
 
 namespace vdx {
 
+// Kernel-argument form of a 3D rotary position embedding (device pointers;
+// the rule is stated in rope3d.h).
+struct Rope3DDev {
+    const int32_t* pos;  // [B, S, 3]: (t, y, x) of every token
+    const float* cs[3];  // cos tables [n_a][d_a / 2] of the t, y, x axes
+    const float* sn[3];  // sin tables, same shape
+    int n[3];            // table rows per axis
+    int d[3];            // even section widths, d[0] + d[1] + d[2] <= D
+    int interleaved;     // 1: pairs (2p, 2p + 1); 0: (p, p + d_a / 2)
+};
+
 struct AttnArgs {
     const void* q;
     const void* k;
@@ -21,6 +32,14 @@ struct AttnArgs {
 
 // Enqueue the forward kernel; arguments are already validated.
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+
+// The forward kernel on 3D-rotary-embedded queries (rotated in registers as
+// they are loaded) and keys (a.k must already hold the rotated keys).
+hipError_t launch_rope3d_attn_fwd(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream);
+
+// y = the 3D rotary embedding of x (bf16 [B, S, H, D]; y may be x).
+hipError_t launch_rope3d_apply(const void* x, void* y, const Rope3DDev& r, int B, int S, int H, int D,
+                               hipStream_t stream);
 
 // Largest S accepted with segment IDs (the LDS key-tile table bound).
 int64_t max_masked_seq();

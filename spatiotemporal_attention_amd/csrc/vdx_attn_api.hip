@@ -84,10 +84,10 @@ int validate_natten(const void* q, const void* k, const void* v, const void* out
     return VDX_OK;
 }
 
-int validate_bwd(const void* q, const void* k, const void* v, const int32_t* seg_q,
-                 const int32_t* seg_kv, const void* out, const float* lse, const void* dout,
-                 const void* dq, const void* dk, const void* dv, const void* ws, size_t ws_bytes,
-                 int B, int S, int H, int D, float scale) {
+int validate_bwd_args(const void* q, const void* k, const void* v, const int32_t* seg_q,
+                      const int32_t* seg_kv, const void* out, const float* lse, const void* dout,
+                      const void* dq, const void* dk, const void* dv, int B, int S, int H, int D,
+                      float scale) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return VDX_ERR_NULL_PTR;
     if ((seg_q == nullptr) != (seg_kv == nullptr)) return VDX_ERR_SEG_PAIR;
     if (B < 1 || S < 1 || H < 1) return VDX_ERR_SHAPE;
@@ -107,6 +107,15 @@ int validate_bwd(const void* q, const void* k, const void* v, const int32_t* seg
         return VDX_ERR_ALIGN;
     if (!aligned(lse, 4) || (seg_q && (!aligned(seg_q, 4) || !aligned(seg_kv, 4))))
         return VDX_ERR_ALIGN;
+    return VDX_OK;
+}
+
+int validate_bwd(const void* q, const void* k, const void* v, const int32_t* seg_q,
+                 const int32_t* seg_kv, const void* out, const float* lse, const void* dout,
+                 const void* dq, const void* dk, const void* dv, const void* ws, size_t ws_bytes,
+                 int B, int S, int H, int D, float scale) {
+    const int rc = validate_bwd_args(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
     if (!ws || !aligned(ws, 16) || ws_bytes < vdx::attn_bwd_workspace_bytes(B, S, H))
         return VDX_ERR_WORKSPACE;
     return VDX_OK;
@@ -155,6 +164,36 @@ __attribute__((visibility("default"))) int vdx_attn_bwd(
     return VDX_OK;
 }
 
+__attribute__((visibility("default"))) int vdx_rope3d_apply(const void* x, void* y, const vdx_rope3d* rope,
+                                                            int B, int S, int H, int D, hipStream_t stream) {
+    vdx::Rope3DDev dev{};
+    int rc = validate_rope_apply(x, y, rope, B, S, H, D, dev);
+    if (rc != VDX_OK) return rc;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    if (vdx::launch_rope3d_apply(x, y, dev, B, S, H, D, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
+__attribute__((visibility("default"))) int vdx_rope3d_attn_fwd(
+    const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
+    const vdx_rope3d* rope, void* k_rot, void* out, float* lse, int B, int S, int H, int D, float scale,
+    hipStream_t stream) {
+    if (!k_rot && q && k && v && out && lse) return VDX_ERR_NULL_PTR;
+    int rc = validate(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
+    if (!aligned(k_rot, 16)) return VDX_ERR_ALIGN;
+    vdx::Rope3DDev dev{};
+    rc = validate_rope(rope, D, dev);
+    if (rc != VDX_OK) return rc;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    if (vdx::launch_rope3d_apply(k, k_rot, dev, B, S, H, D, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    vdx::AttnArgs a{q, k_rot, v, seg_q, seg_kv, out, lse, B, S, H, D, scale};
+    if (vdx::launch_rope3d_attn_fwd(a, dev, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
 __attribute__((visibility("default"))) size_t vdx_attn_bwd_workspace_size(int B, int S, int H) {
     if (B < 1 || S < 1 || H < 1 || S > INT32_MAX - 64) return 0;
     const __int128 n = (__int128)B * H * (((int64_t)S + 63) / 64 * 64) * 8 +
@@ -178,6 +217,9 @@ __attribute__((visibility("default"))) const char* vdx_status_str(int status) {
             return "VDX_ERR_WINDOW: window sizes must be odd and >= 1, the x window at most 13";
         case VDX_ERR_WORKSPACE:
             return "VDX_ERR_WORKSPACE: workspace NULL, misaligned or smaller than vdx_attn_bwd_workspace_size";
+        case VDX_ERR_ROPE:
+            return "VDX_ERR_ROPE: rotary embedding description NULL, or a section width, row count, table or "
+                   "position pointer invalid";
         default: return "VDX_ERR_UNKNOWN";
     }
 }

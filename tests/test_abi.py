@@ -34,7 +34,8 @@ def native():
 def test_exports_every_declared_function(native):
     names = header_functions()
     assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd",
-                            "vdx_attn_bwd_workspace_size", "vdx_status_str", "vdx_abi_version"])
+                            "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd",
+                            "vdx_status_str", "vdx_abi_version"])
     for n in names:
         assert hasattr(native.lib, n), n
 
@@ -145,6 +146,33 @@ def test_runs_on_side_stream(need_gpu):
         o, l = vdx.attn_fwd(q, q, q)
     s.synchronize()
     assert torch.equal(o, ref) and torch.equal(l, ref_lse)
+
+
+@pytest.mark.gpu
+def test_bwd_on_side_stream_with_own_workspace(need_gpu):
+    """attn_bwd on a stream other than the current one, allocating its
+    workspace and gradients itself: the caller's next allocations on the
+    current stream (filled at once) must not land in memory the backward still
+    uses, so the gradients equal those of the same call on the current
+    stream, bit for bit."""
+    import spatiotemporal_attention_amd as vdx
+    B, S, H, D = 1, 8192, 4, 128
+    g = torch.Generator(device="cuda").manual_seed(31)
+    q, k, v, dout = (torch.randn(B, S, H, D, device="cuda", generator=g).bfloat16() for _ in range(4))
+    seg = torch.ones(B, S, dtype=torch.int32, device="cuda")
+    seg[:, S - 100:] = 0
+    out, lse = vdx.attn_fwd(q, k, v, seg, seg)
+    ref = vdx.attn_bwd(q, k, v, out, lse, dout, seg, seg)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    got = vdx.attn_bwd(q, k, v, out, lse, dout, seg, seg, stream=s)
+    junk = [torch.full((1 << 22,), float("nan"), device="cuda") for _ in range(8)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 # --- vdx_natten3d_fwd validation (no GPU needed) ----------------------------------
@@ -314,6 +342,86 @@ def test_bwd_error_path_writes_nothing(need_gpu):
     assert all(torch.all(t == 3.0) for t in g) and torch.all(ws == 7)
 
 
+# --- vdx_rope3d_apply / vdx_rope3d_attn_fwd validation (no GPU needed) ----------------
+def rdesc(native, pos=A + 0x800, cos=(A + 0x900, A + 0xa00, A + 0xb00), sin=(A + 0xc00, A + 0xd00, A + 0xe00),
+          n=(4, 5, 6), dims=(44, 42, 42), interleaved=True):
+    return native.rope3d_desc(pos, cos, sin, n, dims, interleaved)
+
+
+def rapply(native, x=A, y=A + 0x100, rope="default", B=1, S=64, H=2, D=128):
+    r = rdesc(native) if rope == "default" else rope
+    return native.rope3d_apply_raw(x, y, r, B, S, H, D, 0)
+
+
+def rattn(native, q=A, k=A + 0x100, v=A + 0x200, sq=0, sk=0, rope="default", k_rot=A + 0x600,
+          out=A + 0x300, lse=A + 0x400, B=1, S=128, H=2, D=128, scale=0.125):
+    r = rdesc(native) if rope == "default" else rope
+    return native.rope3d_attn_fwd_raw(q, k, v, sq, sk, r, k_rot, out, lse, B, S, H, D, scale, 0)
+
+
+@pytest.mark.parametrize("kw", [dict(pos=0), dict(pos=A + 0x802), dict(dims=(43, 43, 42)),
+                                dict(dims=(-2, 66, 64)), dict(dims=(44, 44, 42)), dict(n=(4, -1, 6)),
+                                dict(cos=(A + 0x900, 0, A + 0xb00)), dict(sin=(A + 0xc00, A + 0xd00, 0)),
+                                dict(cos=(A + 0x902, A + 0xa00, A + 0xb00))])
+def test_rope_description_rejected(native, kw):
+    assert rapply(native, rope=rdesc(native, **kw)) == native.VDX_ERR_ROPE
+    assert rattn(native, rope=rdesc(native, **kw)) == native.VDX_ERR_ROPE
+
+
+def test_rope_missing_description(native):
+    assert rapply(native, rope=None) == native.VDX_ERR_ROPE
+    assert rattn(native, rope=None) == native.VDX_ERR_ROPE
+
+
+def test_rope_zero_width_section_needs_no_table(native):
+    r = rdesc(native, cos=(A + 0x900, 0, A + 0xb00), sin=(A + 0xc00, 0, A + 0xe00), dims=(64, 0, 64))
+    want = native.VDX_ERR_DEVICE if not torch.cuda.is_available() else None
+    if want is None:
+        pytest.skip("a GPU is visible; this path would launch on fake addresses")
+    assert rapply(native, rope=r) == want
+    assert rattn(native, rope=r) == want
+
+
+def test_rope_apply_validation(native):
+    assert rapply(native, x=0) == native.VDX_ERR_NULL_PTR
+    assert rapply(native, y=0) == native.VDX_ERR_NULL_PTR
+    assert rapply(native, S=0) == native.VDX_ERR_SHAPE
+    assert rapply(native, D=96) == native.VDX_ERR_HEAD_DIM
+    assert rapply(native, D=64) == native.VDX_ERR_ROPE  # 44 + 42 + 42 > 64
+    assert rapply(native, x=A + 4) == native.VDX_ERR_ALIGN
+    # order: NULL -> shape -> head dim -> alignment -> rope
+    assert rapply(native, x=0, S=0, D=3, rope=None) == native.VDX_ERR_NULL_PTR
+    assert rapply(native, S=0, D=3, y=A + 2, rope=None) == native.VDX_ERR_SHAPE
+    assert rapply(native, D=3, y=A + 2, rope=None) == native.VDX_ERR_HEAD_DIM
+    assert rapply(native, y=A + 2, rope=None) == native.VDX_ERR_ALIGN
+
+
+def test_rope_attn_validation(native):
+    for w in ("q", "k", "v", "out", "lse", "k_rot"):
+        assert rattn(native, **{w: 0}) == native.VDX_ERR_NULL_PTR, w
+    assert rattn(native, sq=A + 0x500) == native.VDX_ERR_SEG_PAIR
+    assert rattn(native, B=0) == native.VDX_ERR_SHAPE
+    assert rattn(native, D=32) == native.VDX_ERR_HEAD_DIM
+    assert rattn(native, scale=0.0) == native.VDX_ERR_SCALE
+    assert rattn(native, k_rot=A + 0x608) == native.VDX_ERR_ALIGN
+    # order: NULL -> segment pair -> shape -> head dim -> scale -> alignment -> rope
+    assert rattn(native, k_rot=0, sq=A, B=0, rope=None) == native.VDX_ERR_NULL_PTR
+    assert rattn(native, sq=A, B=0, rope=None) == native.VDX_ERR_SEG_PAIR
+    assert rattn(native, B=0, D=3, rope=None) == native.VDX_ERR_SHAPE
+    assert rattn(native, D=3, scale=-1.0, rope=None) == native.VDX_ERR_HEAD_DIM
+    assert rattn(native, scale=-1.0, k_rot=A + 2, rope=None) == native.VDX_ERR_SCALE
+    assert rattn(native, k_rot=A + 2, rope=None) == native.VDX_ERR_ALIGN
+
+
+def test_rope_valid_arguments_without_gpu_report_device_error(native):
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this path would launch on fake addresses")
+    assert rapply(native) == native.VDX_ERR_DEVICE
+    assert rattn(native) == native.VDX_ERR_DEVICE
+    assert rapply(native, rope=rdesc(native, dims=(0, 0, 0), cos=(0, 0, 0), sin=(0, 0, 0))) == \
+        native.VDX_ERR_DEVICE
+
+
 C_CLIENT = r"""
 #include "vdx_attn.h"
 #include <stdio.h>
@@ -330,6 +438,12 @@ int main(void) {
         fails |= 8;
     if (vdx_attn_bwd_workspace_size(1, 64, 1) == 0) fails |= 16;
     if (vdx_status_str(VDX_OK) == NULL) fails |= 32;
+    {
+        vdx_rope3d r = {0};
+        if (vdx_rope3d_apply(0, 0, &r, 1, 64, 1, 64, 0) != VDX_ERR_NULL_PTR) fails |= 64;
+        if (vdx_rope3d_attn_fwd(0, 0, 0, 0, 0, &r, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR)
+            fails |= 128;
+    }
     printf("%d %s\n", fails, vdx_status_str(VDX_ERR_NULL_PTR));
     return fails;
 }
