@@ -121,6 +121,43 @@ int validate_bwd(const void* q, const void* k, const void* v, const int32_t* seg
     return VDX_OK;
 }
 
+int validate_rope(const vdx_rope3d* r, int D, vdx::Rope3DDev& dev) {
+    if (!r || !r->pos || !aligned(r->pos, 4)) return VDX_ERR_ROPE;
+    int64_t sum = 0;
+    for (int a = 0; a < 3; ++a) {
+        if (r->dims[a] < 0 || r->dims[a] % 2 != 0 || r->n[a] < 0) return VDX_ERR_ROPE;
+        if (r->dims[a] > 0 && (!r->cos_tab[a] || !r->sin_tab[a] || !aligned(r->cos_tab[a], 4) ||
+                               !aligned(r->sin_tab[a], 4)))
+            return VDX_ERR_ROPE;
+        sum += r->dims[a];
+    }
+    if (sum > D) return VDX_ERR_ROPE;
+    dev.pos = r->pos;
+    for (int a = 0; a < 3; ++a) {
+        dev.cs[a] = r->cos_tab[a];
+        dev.sn[a] = r->sin_tab[a];
+        // A section of width 0 reads no table; its rows only decide which
+        // tokens are inside.
+        dev.n[a] = r->n[a];
+        dev.d[a] = r->dims[a];
+    }
+    dev.interleaved = r->interleaved ? 1 : 0;
+    return VDX_OK;
+}
+
+int validate_rope_apply(const void* x, const void* y, const vdx_rope3d* r, int B, int S, int H, int D,
+                        vdx::Rope3DDev& dev) {
+    if (!x || !y) return VDX_ERR_NULL_PTR;
+    if (B < 1 || S < 1 || H < 1) return VDX_ERR_SHAPE;
+    if (D > 0) {
+        const __int128 n = (__int128)B * S * H * D;
+        if (n > (__int128)INT64_MAX / 2) return VDX_ERR_SHAPE;
+    }
+    if (D != 64 && D != 128) return VDX_ERR_HEAD_DIM;
+    if (!aligned(x, 16) || !aligned(y, 16)) return VDX_ERR_ALIGN;
+    return validate_rope(r, D, dev);
+}
+
 }  // namespace
 
 extern "C" {
