@@ -70,11 +70,13 @@ enum vdx_status {
     VDX_ERR_WORKSPACE = 10, /* vdx_attn_bwd: workspace NULL, smaller than
                              vdx_attn_bwd_workspace_size(B, S, H), or not
                              16-byte aligned                                    */
-    VDX_ERR_ROPE = 11     /* vdx_rope3d_*: the embedding description is NULL,
+    VDX_ERR_ROPE = 11,    /* vdx_rope3d_*: the embedding description is NULL,
                              its pos is NULL, a section width is odd or < 0,
                              the widths add up to more than D, a row count is
                              < 0, a table of a section of nonzero width is
                              NULL, or pos / a table is not 4-byte aligned      */
+    VDX_ERR_SCRATCH = 12  /* vdx_attn_bwd_noalloc: vdx_attn_bwd_workspace_size
+                             (B, S, H) exceeds VDX_BWD_NOALLOC_SCRATCH_BYTES   */
 };
 
 /*
@@ -190,6 +192,33 @@ int vdx_attn_bwd(const void* q, const void* k, const void* v,
                  void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/*
+ * vdx_attn_bwd_noalloc -- vdx_attn_bwd with no workspace argument and no
+ * allocation of any kind, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, semantics and results as vdx_attn_bwd (bit for
+ * bit) without workspace / workspace_bytes.
+ *
+ * The scratch vdx_attn_bwd would take from its workspace lives in one static
+ * device array of VDX_BWD_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held by the
+ * library until the process ends; a call needs
+ * vdx_attn_bwd_workspace_size(B, S, H) bytes of it (the 720p layer, B=1,
+ * S=75,600, H=40, needs 24.2 MB) and returns VDX_ERR_SCRATCH, before any HIP
+ * call, if that is more.  Every call on a GPU shares that GPU's array, which
+ * keeps the last call's contents (nothing in it needs clearing: each call
+ * writes what it reads): calls that overlap in time on one GPU -- on
+ * different streams, or from different threads -- race and give wrong
+ * results; serialise them.  The first call on a device looks up the array's
+ * address there (the call's current device).
+ * Validation order: as vdx_attn_bwd up to alignment, then the scratch size.
+ */
+#define VDX_BWD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int vdx_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                         const int32_t* seg_q, const int32_t* seg_kv,
+                         const void* out, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv,
+                         int B, int S, int H, int D, float scale, hipStream_t stream);
 
 /* Bytes of workspace vdx_attn_bwd needs for (B, S, H): 8 * B * H * S_pad with
  * S_pad = S rounded up to a multiple of 64 (two fp32 terms per row), plus

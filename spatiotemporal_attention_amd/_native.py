@@ -22,9 +22,11 @@ VDX_ERR_LAUNCH = 8
 VDX_ERR_WINDOW = 9
 VDX_ERR_WORKSPACE = 10
 VDX_ERR_ROPE = 11
+VDX_ERR_SCRATCH = 12
 
-EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_workspace_size",
-            "vdx_rope3d_apply", "vdx_rope3d_attn_fwd", "vdx_status_str", "vdx_abi_version")
+EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
+            "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd", "vdx_status_str",
+            "vdx_abi_version")
 
 
 class Rope3D(ctypes.Structure):
@@ -45,6 +47,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vdx_natten3d_fwd.argtypes = [p, p, p, p, p] + [i] * 9 + [ctypes.c_float, p]
     lib.vdx_attn_bwd.restype = i
     lib.vdx_attn_bwd.argtypes = [p] * 12 + [ctypes.c_size_t] + [i] * 4 + [ctypes.c_float, p]
+    lib.vdx_attn_bwd_noalloc.restype = i
+    lib.vdx_attn_bwd_noalloc.argtypes = [p] * 11 + [i] * 4 + [ctypes.c_float, p]
     lib.vdx_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.vdx_attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.vdx_rope3d_apply.restype = i
@@ -91,6 +95,18 @@ def attn_bwd_raw(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, ws, ws_byte
                                 out or None, lse or None, dout or None, dq or None, dk or None,
                                 dv or None, ws or None, int(ws_bytes), int(B), int(S), int(H),
                                 int(D), float(scale), stream or None))
+
+
+def attn_bwd_noalloc_raw(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, B, S, H, D, scale,
+                        stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL)."""
+    return int(lib.vdx_attn_bwd_noalloc(q or None, k or None, v or None, seg_q or None, seg_kv or None,
+                                        out or None, lse or None, dout or None, dq or None, dk or None,
+                                        dv or None, int(B), int(S), int(H), int(D), float(scale),
+                                        stream or None))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def attn_bwd_workspace_size(B, S, H) -> int:

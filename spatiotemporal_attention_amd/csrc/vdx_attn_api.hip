@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn_fwd_launch.h"
 #include "vdx_attn.h"
@@ -121,6 +122,33 @@ int validate_bwd(const void* q, const void* k, const void* v, const int32_t* seg
     return VDX_OK;
 }
 
+// ---- the allocation-free backward's scratch ---------------------------------------
+// One file-scope device array: every GPU the library runs on holds its own copy
+// (at its own address) until the process ends.  Host code never uses the
+// array's name as an address: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) unsigned char scratch[VDX_BWD_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VDX_ERR_DEVICE;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return VDX_ERR_DEVICE;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return VDX_OK;
+}
+
 int validate_rope(const vdx_rope3d* r, int D, vdx::Rope3DDev& dev) {
     if (!r || !r->pos || !aligned(r->pos, 4)) return VDX_ERR_ROPE;
     int64_t sum = 0;
@@ -231,6 +259,23 @@ __attribute__((visibility("default"))) int vdx_rope3d_attn_fwd(
     return VDX_OK;
 }
 
+__attribute__((visibility("default"))) int vdx_attn_bwd_noalloc(
+    const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
+    const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int S,
+    int H, int D, float scale, hipStream_t stream) {
+    int rc = validate_bwd_args(q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
+    if (vdx::attn_bwd_workspace_bytes(B, S, H) > (size_t)VDX_BWD_NOALLOC_SCRATCH_BYTES) return VDX_ERR_SCRATCH;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != VDX_OK) return rc;
+    vdx::BwdArgs a{q, k, v, seg_q, seg_kv, out, lse, dout, dq, dk, dv, ws, B, S, H, D, scale};
+    if (vdx::launch_attn_bwd(a, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
 __attribute__((visibility("default"))) size_t vdx_attn_bwd_workspace_size(int B, int S, int H) {
     if (B < 1 || S < 1 || H < 1 || S > INT32_MAX - 64) return 0;
     const __int128 n = (__int128)B * H * (((int64_t)S + 63) / 64 * 64) * 8 +
@@ -254,6 +299,8 @@ __attribute__((visibility("default"))) const char* vdx_status_str(int status) {
             return "VDX_ERR_WINDOW: window sizes must be odd and >= 1, the x window at most 13";
         case VDX_ERR_WORKSPACE:
             return "VDX_ERR_WORKSPACE: workspace NULL, misaligned or smaller than vdx_attn_bwd_workspace_size";
+        case VDX_ERR_SCRATCH:
+            return "VDX_ERR_SCRATCH: the call needs more scratch than vdx_attn_bwd_noalloc's static buffer holds";
         case VDX_ERR_ROPE:
             return "VDX_ERR_ROPE: rotary embedding description NULL, or a section width, row count, table or "
                    "position pointer invalid";

@@ -33,7 +33,7 @@ def native():
 
 def test_exports_every_declared_function(native):
     names = header_functions()
-    assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd",
+    assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
                             "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd",
                             "vdx_status_str", "vdx_abi_version"])
     for n in names:
@@ -342,6 +342,35 @@ def test_bwd_error_path_writes_nothing(need_gpu):
     assert all(torch.all(t == 3.0) for t in g) and torch.all(ws == 7)
 
 
+# --- vdx_attn_bwd_noalloc validation (no GPU needed) ------------------------------------
+def ncall_bwd(native, q=A, k=A + 0x100, v=A + 0x200, sq=0, sk=0, out=A + 0x300, lse=A + 0x400,
+              dout=A + 0x500, dq=A + 0x600, dk=A + 0x700, dv=A + 0x800, B=1, S=128, H=2, D=128, scale=0.125):
+    return native.attn_bwd_noalloc_raw(q, k, v, sq, sk, out, lse, dout, dq, dk, dv, B, S, H, D, scale, 0)
+
+
+def test_bwd_noalloc_validation(native):
+    for w in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert ncall_bwd(native, **{w: 0}) == native.VDX_ERR_NULL_PTR, w
+    assert ncall_bwd(native, sq=A + 0x900) == native.VDX_ERR_SEG_PAIR
+    assert ncall_bwd(native, S=0) == native.VDX_ERR_SHAPE
+    assert ncall_bwd(native, D=96) == native.VDX_ERR_HEAD_DIM
+    assert ncall_bwd(native, scale=-1.0) == native.VDX_ERR_SCALE
+    assert ncall_bwd(native, dq=A + 0x602) == native.VDX_ERR_ALIGN
+
+
+def test_bwd_noalloc_rejects_calls_beyond_its_scratch(native):
+    """The 720p layer fits the 32 MiB array; a call needing more is refused
+    before any HIP call (and after the alignment check)."""
+    import spatiotemporal_attention_amd as vdx
+    assert vdx.attn_bwd_workspace_size(1, 75600, 40) <= native.NOALLOC_SCRATCH_BYTES
+    B, S, H = 1, 1 << 20, 4
+    assert vdx.attn_bwd_workspace_size(B, S, H) > native.NOALLOC_SCRATCH_BYTES
+    assert ncall_bwd(native, B=B, S=S, H=H) == native.VDX_ERR_SCRATCH
+    assert ncall_bwd(native, B=B, S=S, H=H, dq=A + 0x602) == native.VDX_ERR_ALIGN
+    if not torch.cuda.is_available():
+        assert ncall_bwd(native) == native.VDX_ERR_DEVICE
+
+
 # --- vdx_rope3d_apply / vdx_rope3d_attn_fwd validation (no GPU needed) ----------------
 def rdesc(native, pos=A + 0x800, cos=(A + 0x900, A + 0xa00, A + 0xb00), sin=(A + 0xc00, A + 0xd00, A + 0xe00),
           n=(4, 5, 6), dims=(44, 42, 42), interleaved=True):
@@ -437,6 +466,8 @@ int main(void) {
     if (vdx_attn_bwd(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR)
         fails |= 8;
     if (vdx_attn_bwd_workspace_size(1, 64, 1) == 0) fails |= 16;
+    if (vdx_attn_bwd_noalloc(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR)
+        fails |= 256;
     if (vdx_status_str(VDX_OK) == NULL) fails |= 32;
     {
         vdx_rope3d r = {0};
