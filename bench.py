@@ -30,7 +30,8 @@ of the queries (in the attention kernel's prologue), then the same attention;
 the FLOP count is the attention's.
 
 Every line also carries the graphics clock and socket power sampled with
-amdsmi during the timed steps (null where amdsmi cannot read them), and the
+amdsmi while the same step runs back to back for a few seconds after the
+timed ones (null where amdsmi cannot read them), and the
 CPU baseline's row rate with the extrapolated time of the whole workload on
 the oracle (labelled as an extrapolation).
 
@@ -314,21 +315,39 @@ class ClockSampler:
         if self._thread is not None:
             self._thread.join()
 
-    def summary(self):
+    def summary(self, skip: float = 0.5):
+        """Median over the samples after the first `skip` fraction (the
+        readings lag the load by a few hundred ms)."""
         if not self.clk:
             return {"gfx_clock_mhz_median": None, "source": "amdsmi", "error": self.err or "no handle"}
-        return {"gfx_clock_mhz_median": float(np.median(self.clk)),
-                "gfx_clock_mhz_mean": round(float(np.mean(self.clk)), 1),
-                "socket_power_w_median": float(np.median(self.pwr)) if self.pwr else None,
-                "samples": len(self.clk),
-                "source": f"amdsmi current GFX clock and socket power, every {self.period * 1e3:.0f} ms "
-                          f"during the timed steps"}
+        k = int(len(self.clk) * skip)
+        clk, pwr = self.clk[k:], self.pwr[k:]
+        return {"gfx_clock_mhz_median": float(np.median(clk)),
+                "socket_power_w_median": float(np.median(pwr)) if pwr else None,
+                "samples": len(clk),
+                "source": f"amdsmi current GFX clock and socket power every {self.period * 1e3:.0f} ms, "
+                          f"over the second half of {CLOCK_WINDOW_S:.0f} s of back-to-back steps after "
+                          f"the timed ones"}
 
 
 CLOCK = {"summary": None}
+CLOCK_WINDOW_S = 3.0
 
 
-def time_steps(step, stream, steps, warmup):
+def clock_window(step, seconds: float = CLOCK_WINDOW_S):
+    """Runs steps back to back for about `seconds` while sampling the clock
+    (outside the timed region, so the sampling thread cannot disturb it)."""
+    sampler = ClockSampler()
+    with sampler:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
+    CLOCK["summary"] = sampler.summary()
+
+
+def time_steps(step, stream, steps, warmup, sample_clock=True):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -336,16 +355,15 @@ def time_steps(step, stream, steps, warmup):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
-    sampler = ClockSampler()
-    with sampler:
-        t0 = time.perf_counter()
-        for e0, e1 in ev:
-            e0.record(stream)
-            step()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    CLOCK["summary"] = sampler.summary()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if sample_clock:
+        clock_window(step)
     kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     ms_per_step = wall * 1e3 / steps
     log(f"timed {steps} steps: {ms_per_step:.3f} ms/step wall, "
@@ -560,7 +578,7 @@ def main():
     if args.rope:
         # the key pre-pass alone, timed the same way
         prepass_ms = time_steps(lambda: vdx.rope3d_apply(d["k"], **rr, out=k_rot, stream=stream), stream,
-                                max(3, args.steps), 1)[1]
+                                max(3, args.steps), 1, sample_clock=False)[1]
 
     flop = 4.0 * w.D * w.H * valid_pairs(w)
     value = flop / (ms_per_step * 1e-3) / 1e12

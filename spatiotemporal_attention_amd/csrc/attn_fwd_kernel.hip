@@ -408,17 +408,26 @@ __device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
 }
 
 // 3D rotary embedding of a workgroup's query block, staged in LDS before the
-// K/V ring is in use: the block's kBq rows (D bf16 each, row-major) are copied
-// in, each rotated feature pair is rewritten in place by one thread, and each
-// lane then reads its Q slice from there.  The rule and its rounding are those
-// of the key pre-pass (rope3d.h), so the bits equal a rotated copy of q.  The
-// loops stay rolled, which keeps this prologue's registers far below the main
-// loop's.  Rows past S stay zero.
+// K/V ring is in use: the block's kBq rows (D bf16 each, rows kQStage bytes
+// apart so that neighbouring rows start in different banks) are copied in,
+// two threads per row rewrite its rotated feature pairs in place (alternate
+// pairs; the row's position is read once), and each lane then reads its Q
+// slice from there.  The rule and its rounding are those of the key pre-pass
+// (rope3d.h), so the bits equal a rotated copy of q.  The loops stay rolled,
+// which keeps this prologue's registers far below the main loop's.  Rows past
+// S stay zero.
+template <int D>
+struct QStage {
+    static constexpr int kRowBytes = D * 2 + 16;
+    static_assert(kBq * kRowBytes <= Tile<D>::kRingBytes, "the staged query block must fit in the ring");
+    static_assert(kThreads == 2 * kBq, "two threads per staged row");
+};
+
 template <int D>
 __device__ void rope_stage_q(char* smem, const __bf16* __restrict__ q, const Rope3DDev& r, int b, int h,
                              int S, int64_t tok_stride, int q0, int tid) {
     constexpr int kRowChunks = D / 8;
-    static_assert(kBq * D * 2 <= Tile<D>::kRingBytes, "the staged query block must fit in the ring");
+    constexpr int kStride = QStage<D>::kRowBytes;
 #pragma unroll 1
     for (int c = tid; c < kBq * kRowChunks; c += kThreads) {
         const int row = c / kRowChunks, ch = c % kRowChunks;
@@ -426,37 +435,42 @@ __device__ void rope_stage_q(char* smem, const __bf16* __restrict__ q, const Rop
         bf16x8 x = {};
         if (tok < S)
             x = *reinterpret_cast<const bf16x8*>(q + ((int64_t)b * S + tok) * tok_stride + (int64_t)h * D + 8 * ch);
-        *reinterpret_cast<bf16x8*>(smem + (row * D + 8 * ch) * 2) = x;
+        *reinterpret_cast<bf16x8*>(smem + row * kStride + 16 * ch) = x;
     }
     __syncthreads();
-    const int h0 = r.d[0] >> 1, h1 = r.d[1] >> 1, h2 = r.d[2] >> 1;
-    const int P = h0 + h1 + h2;  // rotated pairs per row
-    uint16_t* sb = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll 1
-    for (int k = tid; k < kBq * P; k += kThreads) {
-        const int row = k / P, pp = k - row * P;
-        const int tok = q0 + row;
-        if (tok >= S) continue;
-        int pos[3];
+    const int row = tid % kBq, hf = tid / kBq;
+    const int tok = q0 + row;
+    int pos[3] = {-1, -1, -1};
+    if (tok < S) {
 #pragma unroll
         for (int a = 0; a < 3; ++a) pos[a] = r.pos[((int64_t)b * S + tok) * 3 + a];
-        if (!rope_inside(r, pos)) continue;
-        int a, p, off, half;
-        if (pp < h0) {
-            a = 0, p = pp, off = 0, half = h0;
-        } else if (pp < h0 + h1) {
-            a = 1, p = pp - h0, off = r.d[0], half = h1;
-        } else {
-            a = 2, p = pp - h0 - h1, off = r.d[0] + r.d[1], half = h2;
+    }
+    if (tok < S && rope_inside(r, pos)) {
+        uint16_t* sb = reinterpret_cast<uint16_t*>(smem + row * kStride);
+        const int h0 = r.d[0] >> 1, h1 = r.d[1] >> 1, h2 = r.d[2] >> 1;
+        // walk pairs hf, hf + 2, ... of the concatenated sections: (a, p) is
+        // the axis and the pair within it, off the section's first feature
+        int a = 0, p = hf, off = 0;
+#pragma unroll 1
+        for (;;) {
+            const int half = a == 0 ? h0 : (a == 1 ? h1 : h2);
+            if (p >= half) {
+                if (a == 2) break;
+                p -= half;
+                off += 2 * half;
+                ++a;
+                continue;
+            }
+            const int i0 = r.interleaved ? off + 2 * p : off + p;
+            const int i1 = r.interleaved ? off + 2 * p + 1 : off + p + half;
+            const int e = (a == 0 ? pos[0] : (a == 1 ? pos[1] : pos[2])) * half + p;
+            const float c = (a == 0 ? r.cs[0] : (a == 1 ? r.cs[1] : r.cs[2]))[e];
+            const float sn = (a == 0 ? r.sn[0] : (a == 1 ? r.sn[1] : r.sn[2]))[e];
+            const float x0 = bf16_bits_to_f32(sb[i0]), x1 = bf16_bits_to_f32(sb[i1]);
+            sb[i0] = rope_rotate(x0, x1, c, sn, true);
+            sb[i1] = rope_rotate(x1, x0, c, sn, false);
+            p += 2;
         }
-        const int i0 = r.interleaved ? off + 2 * p : off + p;
-        const int i1 = r.interleaved ? off + 2 * p + 1 : off + p + half;
-        const int e = (a == 0 ? pos[0] : (a == 1 ? pos[1] : pos[2])) * half + p;
-        const float c = (a == 0 ? r.cs[0] : (a == 1 ? r.cs[1] : r.cs[2]))[e];
-        const float sn = (a == 0 ? r.sn[0] : (a == 1 ? r.sn[1] : r.sn[2]))[e];
-        const float x0 = bf16_bits_to_f32(sb[row * D + i0]), x1 = bf16_bits_to_f32(sb[row * D + i1]);
-        sb[row * D + i0] = rope_rotate(x0, x1, c, sn, true);
-        sb[row * D + i1] = rope_rotate(x1, x0, c, sn, false);
     }
     __syncthreads();
 }
@@ -507,7 +521,7 @@ __device__ __forceinline__ void attn_fwd_item(
     // ---- Q slice -> registers as the B operand of S^T = K Q^T -----------------
     if constexpr (ROPE) {
         rope_stage_q<D>(smem, q, rope, b, h, S, A.tok_stride, qblk * kBq, tid);
-        const char* st = smem + ((wave * 32 + lr) * D + 8 * g) * 2;
+        const char* st = smem + (wave * 32 + lr) * QStage<D>::kRowBytes + 16 * g;
 #pragma unroll
         for (int ks = 0; ks < T::kSteps; ++ks) A.qreg[ks] = *reinterpret_cast<const bf16x8*>(st + ks * 32);
         A.myseg = SEG ? ((qi < S) ? seg_q[(int64_t)b * S + qi] : 0) : 1;

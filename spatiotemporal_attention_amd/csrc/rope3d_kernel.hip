@@ -2,12 +2,14 @@
 // tensor (the rule is stated in rope3d.h), and the key pre-pass of the
 // rotary-embedded attention forward.
 //
-// One (token, head) row of D features is handled by D/2 lanes, two adjacent
-// features (4 bytes) a lane, so a row is one coalesced D*2-byte load and store.
-// A feature's pair partner is fetched from the lane that holds it with a
-// cross-lane permute; the row groups never straddle a wave (64 is a multiple
-// of D/2), so every lane of a row has its inputs before any lane stores, and
-// the output may be the input itself.
+// A wave takes one token at a time: its position and each lane's angles are
+// looked up once and serve all H heads of the token (the tables are read per
+// token, not per element).  The heads go 64/(D/8) at a time, D/8 lanes a head
+// and 8 features (16 bytes) a lane, so every head row is one coalesced load
+// and one store.  A feature's pair partner is in the lane's own 16 bytes when
+// pairs are interleaved (sections start at even offsets); for split halves it
+// is read back from a per-wave copy of the rows in LDS.  Each row is read in
+// full before it is written, so the output may be the input itself.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,44 +21,70 @@
 namespace vdx {
 namespace {
 
+constexpr int kRopeWaves = 4;  // waves per block
+
 template <int D>
-__global__ __launch_bounds__(256) void rope3d_apply_kernel(const uint32_t* x, uint32_t* y,
-                                                           Rope3DDev r, int S, int H, int64_t n_rows) {
-    constexpr int L = D / 2;  // lanes per row
+__global__ __launch_bounds__(64 * kRopeWaves) void rope3d_apply_kernel(const uint4* x, uint4* y, Rope3DDev r,
+                                                                       int H, int64_t n_tok) {
+    constexpr int L = D / 8;   // lanes per head row
+    constexpr int R = 64 / L;  // head rows per wave step
+    __shared__ uint4 stage[kRopeWaves][64];
     const int lane = threadIdx.x & 63;
-    const int sub = lane % L;            // this lane's feature pair (2 sub, 2 sub + 1)
-    const int base = lane - sub;         // first lane of the row within the wave
-    const int64_t rows_per_block = 256 / L;
-    for (int64_t row0 = (int64_t)blockIdx.x * rows_per_block; row0 < n_rows;
-         row0 += (int64_t)gridDim.x * rows_per_block) {
-        const int64_t row = row0 + threadIdx.x / L;
-        const bool live = row < n_rows;
-        const uint32_t w = live ? x[row * L + sub] : 0u;
-        // Every lane of the wave takes part in the permutes below.
-        int pos[3] = {-1, -1, -1};
-        if (live) {
-            const int64_t tok = row / H;  // b * S + s
+    const int wave = threadIdx.x >> 6;
+    const int c = lane % L, rr = lane / L;
+    const uint16_t* sh = reinterpret_cast<const uint16_t*>(&stage[wave][rr * L]);  // this lane's row
+    for (int64_t tok = (int64_t)blockIdx.x * kRopeWaves + wave; tok < n_tok;
+         tok += (int64_t)gridDim.x * kRopeWaves) {
+        int pos[3];
 #pragma unroll
-            for (int a = 0; a < 3; ++a) pos[a] = r.pos[tok * 3 + a];
-        }
-        const bool inside = live && rope_inside(r, pos);
-        uint32_t outw = w;
-        uint32_t half[2];
+        for (int a = 0; a < 3; ++a) pos[a] = r.pos[tok * 3 + a];
+        const bool inside = rope_inside(r, pos);
+        RopeFeature ft[8];
+        float cs[8], sn[8];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int f = 2 * sub + e;
-            const RopeFeature ft = rope_feature(r, f, pos);
-            const int src = base + (ft.partner >> 1);
-            const uint32_t pw = (uint32_t)__shfl((int)w, src, 64);
-            half[e] = (w >> (16 * e)) & 0xffffu;
-            if (inside && ft.rot) {
-                const uint32_t pb = (pw >> (16 * (ft.partner & 1))) & 0xffffu;
-                const float c = rope_cos(r, ft), s = rope_sin(r, ft);
-                half[e] = rope_rotate(bf16_bits_to_f32(half[e]), bf16_bits_to_f32(pb), c, s, ft.first);
+        for (int e = 0; e < 8; ++e) {
+            ft[e] = rope_feature(r, 8 * c + e, pos);
+            cs[e] = 1.f;
+            sn[e] = 0.f;
+            if (inside && ft[e].rot) {
+                cs[e] = rope_cos(r, ft[e]);
+                sn[e] = rope_sin(r, ft[e]);
             }
         }
-        outw = half[0] | (half[1] << 16);
-        if (live) y[row * L + sub] = outw;
+        for (int h0 = 0; h0 < H; h0 += R) {
+            const int h = h0 + rr;
+            const bool live = h < H;
+            const int64_t idx = (tok * H + h) * L + c;
+            uint4 w = live ? x[idx] : uint4{0u, 0u, 0u, 0u};
+            if (inside) {
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+                uint16_t v[8], pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
+                if (r.interleaved) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pv[e] = v[e ^ 1];
+                } else {
+                    stage[wave][lane] = w;
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pv[e] = sh[ft[e].partner];
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                }
+                uint16_t o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[e] = ft[e].rot ? rope_rotate(bf16_bits_to_f32(v[e]), bf16_bits_to_f32(pv[e]), cs[e], sn[e],
+                                                   ft[e].first)
+                                     : v[e];
+                w = uint4{o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16),
+                          o[4] | ((uint32_t)o[5] << 16), o[6] | ((uint32_t)o[7] << 16)};
+            }
+            if (live) y[idx] = w;
+        }
     }
 }
 
@@ -64,17 +92,14 @@ __global__ __launch_bounds__(256) void rope3d_apply_kernel(const uint32_t* x, ui
 
 hipError_t launch_rope3d_apply(const void* x, void* y, const Rope3DDev& r, int B, int S, int H, int D,
                                hipStream_t stream) {
-    const int64_t n_rows = (int64_t)B * S * H;
-    const int64_t rows_per_block = 256 / (D / 2);
-    const int64_t blocks = std::min<int64_t>((n_rows + rows_per_block - 1) / rows_per_block, 1 << 16);
+    const int64_t n_tok = (int64_t)B * S;
+    const int64_t blocks = std::min<int64_t>((n_tok + kRopeWaves - 1) / kRopeWaves, 1 << 16);
     if (D == 128)
-        hipLaunchKernelGGL(rope3d_apply_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const uint32_t*>(x), reinterpret_cast<uint32_t*>(y), r, S, H,
-                           n_rows);
+        hipLaunchKernelGGL(rope3d_apply_kernel<128>, dim3((unsigned)blocks), dim3(64 * kRopeWaves), 0, stream,
+                           reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), r, H, n_tok);
     else
-        hipLaunchKernelGGL(rope3d_apply_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const uint32_t*>(x), reinterpret_cast<uint32_t*>(y), r, S, H,
-                           n_rows);
+        hipLaunchKernelGGL(rope3d_apply_kernel<64>, dim3((unsigned)blocks), dim3(64 * kRopeWaves), 0, stream,
+                           reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), r, H, n_tok);
     return hipGetLastError();
 }
 
