@@ -191,7 +191,7 @@ def natten_brick_frames(NT, NH, KT, KH) -> int:
     the fewest window-union key rows per query row, ties to more frames."""
     kt, kh = min(KT, NT), min(KH, NH)
     best, best_rows, best_q = 1, 0, 1
-    for bt in (1, 2, 4):
+    for bt in (1, 2, 4, 8):
         by = 8 // bt
         rows = min(bt + kt - 1, NT) * min(by + kh - 1, NH)
         q = min(bt, NT) * min(by, NH)
@@ -203,7 +203,7 @@ def natten_brick_frames(NT, NH, KT, KH) -> int:
 def natten_executed_flop(w) -> float:
     """MFMA flops the kernel issues: per workgroup (a BT x 8/BT x 32 (t, y, x)
     query brick) one step per two key rows of its window union (an odd row
-    count adds a masked row), each row 8 waves x 32 queries x 32 keys x 2
+    count adds a masked row), each row 8 waves x 32 queries x 16 keys x 2
     products x 2*D."""
     NT, NH, NW = w.grid
     KT, KH, KW = w.window
@@ -222,7 +222,7 @@ def natten_executed_flop(w) -> float:
         for y0 in range(0, NH, by):
             rows += 2 * ((nt * span(y0, by, KH, NH) + 1) // 2)
     rows *= (NW + 31) // 32
-    return float(rows) * w.B * w.H * 8 * 32 * 32 * 4 * w.D
+    return float(rows) * w.B * w.H * 8 * 32 * 16 * 4 * w.D
 
 
 def natten_cpu_baseline(w, x, target_s: float = 15.0):

@@ -12,26 +12,29 @@
 //
 // Design (same machinery as the segment-masked kernel):
 //   * one workgroup = 8 wave64s (two per SIMD, two ping-pong groups) and a
-//     BT x (8 / BT) x 32 (t, y, x) brick of queries, BT in {1, 2, 4} chosen
-//     per call (brick_frames): the shape whose window union holds the fewest
-//     key rows per query row -- 4 x 2 for 11^3 windows (14 x 12 key rows
-//     against 11 x 18 for 1 x 8), 1 x 8 for single frames or 1-frame t
-//     windows; wave w owns the 2 x 16 (y, x) sub-brick of wave-row w >> 1 at
-//     x offset 16(w & 1), lane lr the query (lr >> 4, lr & 15) of it;
+//     BT x (8 / BT) x 32 (t, y, x) brick of queries, BT in {1, 2, 4, 8}
+//     chosen per call (brick_frames): the shape whose window union holds the
+//     fewest key rows per query row -- 4 x 2 for 11^3 windows (14 x 12 key
+//     rows against 11 x 18 for 1 x 8), 1 x 8 for single frames or 1-frame t
+//     windows; wave w owns the BT x (8 / BT) x 4 patch of the brick at x
+//     offset 4w (lane lr the query (lr / (4 BY), (lr / 4) % BY, lr % 4) of it),
+//     so a wave's 32 queries span only 4 columns and their x windows at most
+//     3 + kw_eff <= 16 keys;
 //   * the workgroup walks the key rows (t', y') in the union of its queries'
 //     windows -- t' in [start(t0), start(t0 + BT - 1) + kt_eff), y' in
 //     [start(y0), start(y0 + BY - 1) + kh_eff) -- two rows per step: a ring slot
 //     holds two rows of 48 consecutive x positions from X0 (the brick's first
 //     window start, rounded down to 4), which cover the x windows of all 32
 //     brick columns;
-//   * each wave multiplies only the 32-key block of each row that holds its
-//     queries' x windows (they span at most 16 + kw_eff - 1 <= 28 keys from a
-//     4-aligned offset, so kw_eff <= 13), i.e. 16 K Q^T + 16 P V MFMAs per
-//     step at D = 128 -- the segment kernel's phase length, so the barrier
-//     and operand start-up of a phase are spread over the work of two rows;
+//   * each wave multiplies one 32-key block per step: the 16 keys of each of
+//     the step's two rows that hold its queries' x windows (so kw_eff <= 13),
+//     i.e. 8 K Q^T + 8 P V MFMAs per step at D = 128, of which about half
+//     the pairs lie in the windows (11 of 16 keys in x); a block of 32 keys
+//     of one row for a 16-column patch kept a third;
 //   * element masks: key (t', y', x') is valid for a query iff t', y' and x'
-//     lie in its windows; invalid scores become -inf before the online
-//     softmax, which is the segment kernel's;
+//     lie in its windows; the x test is fixed for the item (one byte per
+//     lane), the row tests change per step; invalid scores become -inf
+//     before the online softmax, which is the segment kernel's;
 //   * copies, operand prefetch, ping-pong schedule and epilogue follow the
 //     segment-masked kernel.
 #include <hip/hip_runtime.h>
@@ -60,12 +63,14 @@ __device__ __forceinline__ int win_start(int c, int k, int n) {
 
 constexpr int kBrickRows = 8;  // query (t, y) rows per workgroup: BT frames x 8 / BT rows
 constexpr int kBrickX = 32;    // query columns per workgroup
-constexpr int kRowKeys = 48;  // keys of one key row held in LDS
+constexpr int kPatchX = 4;     // query columns per wave
+constexpr int kRowKeys = 48;   // keys of one key row held in LDS
+constexpr int kBlockKeys = 16; // keys of one row a wave multiplies
 // MFMA operands in flight (the segment kernel keeps 4; here 3 timed about 1%
 // faster and 5 or 6 no better).
 constexpr int kNatPrefetch = 3;
 
-// Frames per brick, BT in {1, 2, 4} (the brick is BT x 8/BT x 32 queries):
+// Frames per brick, BT in {1, 2, 4, 8} (the brick is BT x 8/BT x 32 queries):
 // the shape whose interior window union, min(BT + kt - 1, NT) frames x
 // min(8/BT + kh - 1, NH) rows, is smallest per query row of the brick; on a
 // tie the one with more frames (its union shrinks more where windows clip at
@@ -74,7 +79,7 @@ int brick_frames(int NT, int NH, int KT, int KH) {
     const int64_t kt = std::min(KT, NT), kh = std::min(KH, NH);
     int best = 1;
     int64_t best_rows = 0, best_q = 1;
-    for (int bt = 1; bt <= 4; bt *= 2) {
+    for (int bt = 1; bt <= kBrickRows; bt *= 2) {
         const int64_t by = kBrickRows / bt;
         const int64_t rows = std::min<int64_t>(bt + kt - 1, NT) * std::min<int64_t>(by + kh - 1, NH);
         const int64_t q = std::min<int64_t>(bt, NT) * std::min<int64_t>(by, NH);
@@ -113,8 +118,8 @@ struct NTile {
 template <int D>
 struct Nat {
     using T = NTile<D>;
-    static constexpr int kQk = 2 * T::kSteps;     // K Q^T MFMAs per step (two rows)
-    static constexpr int kPv = 4 * T::kDBlocks;   // P V MFMAs per step (two rows x two 16-key halves)
+    static constexpr int kQk = T::kSteps;         // K Q^T MFMAs per step (one 32-key block)
+    static constexpr int kPv = 2 * T::kDBlocks;   // P V MFMAs per step (its two 16-key rows)
     static constexpr int kRing = kNatPrefetch + 2;
 
     char* smem;
@@ -125,16 +130,16 @@ struct Nat {
     float c_log2;
     // workgroup key rows: t' in [ts, ts + nt), y' in [ylo, ylo + ny); n_rows of them
     int ts, nt, ylo, ny, n_rows, x0k, kt, kh, kw;
-    int kx[2], vx;      // operand bases of this wave's 32-key block in each row of a slot
-    int xrel;           // X0 + block offset + 8g - xs_q: key register c is x offset xrel + c
+    int kx, vx;         // operand bases of this wave's block (16 keys of each row of a slot)
+    uint32_t xmask;     // bit e: block key 8g + e of a row lies in this lane's x window
     int ts_q, ys_q;     // this lane's query t- and y-window starts
     uint32_t dmo[T::kLoadsPerWave];
     bf16x8 qreg[T::kSteps];
     f32x16 oacc[T::kDBlocks];
-    f32x16 sacc[2];
-    bf16x8 pb[4];
+    f32x16 sacc;
+    bf16x8 pb[2];
     bf16x8 ops[kRing];
-    uint32_t vb_next, kb_next[2];
+    uint32_t vb_next, kb_next;
     float m_run, l_run;
 
     __device__ __forceinline__ static int slot_base(int n) {
@@ -145,8 +150,8 @@ struct Nat {
     __device__ __forceinline__ uint32_t vbase(int n) const {
         return lds_addr(smem) + T::kVRegion + slot_base(n) + vx;
     }
-    __device__ __forceinline__ uint32_t kbase(int n, int j) const {
-        return lds_addr(smem) + T::kKRegion + slot_base(n) + kx[j];
+    __device__ __forceinline__ uint32_t kbase(int n) const {
+        return lds_addr(smem) + T::kKRegion + slot_base(n) + kx;
     }
 
     // ---- tile copies --------------------------------------------------------
@@ -188,31 +193,27 @@ struct Nat {
     }
 
     // ---- MFMA phase: K Q^T of step n, then P V of step n-1 --------------------
-    // K Q^T MFMA i: k-step i / 2 of row i % 2 (the rows alternate, so
-    // consecutive MFMAs accumulate into different registers).  P V MFMA j:
-    // kst = j / kDBlocks names row kst >> 1 and its 16-key half kst & 1,
-    // d-block j % kDBlocks.
+    // K Q^T MFMA i: k-step i of the block (block key m < 16 from the step's
+    // first row, m >= 16 from its second).  P V MFMA j: kst = j / kDBlocks
+    // names the row (its 16 keys are one k-step), d-block j % kDBlocks.
     template <bool QK, int I>
-    __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb0, uint32_t kb1) const {
+    __device__ __forceinline__ bf16x8 operand(uint32_t vb, uint32_t kb) const {
         if constexpr (QK && I < kQk) {
-            constexpr int ks = I / 2, row = I % 2;
-            return *reinterpret_cast<const bf16x8*>(lds_ptr((row ? kb1 : kb0) ^ (ks << 5)));
+            return *reinterpret_cast<const bf16x8*>(lds_ptr(kb ^ (I << 5)));
         } else {
             constexpr int j = QK ? I - kQk : I;
             constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
-            const char* p =
-                lds_ptr((vb ^ (db << 6)) + ((kst >> 1) * kRowKeys + (kst & 1) * 16) * T::kRowBytes);
+            const char* p = lds_ptr((vb ^ (db << 6)) + kst * kRowKeys * T::kRowBytes);
             return tr_read8(p, p + 4 * T::kRowBytes);
         }
     }
     template <bool QK, int I>
     __device__ __forceinline__ void mfma(const bf16x8& a) {
         if constexpr (QK && I < kQk) {
-            constexpr int ks = I / 2, row = I % 2;
-            if constexpr (ks == 0)
-                sacc[row] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
+            if constexpr (I == 0)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
             else
-                sacc[row] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[row], 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[I], sacc, 0, 0, 0);
         } else {
             constexpr int j = QK ? I - kQk : I;
             constexpr int kst = j / T::kDBlocks, db = j % T::kDBlocks;
@@ -223,11 +224,10 @@ struct Nat {
     __device__ __forceinline__ void prefetch(int vstep, int kstep) {
         constexpr int NM = (QK ? kQk : 0) + (PV ? kPv : 0);
         vb_next = vbase(vstep);
-        kb_next[0] = kbase(kstep, 0);
-        kb_next[1] = kbase(kstep, 1);
+        kb_next = kbase(kstep);
         static_for<0, kNatPrefetch>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i < NM) ops[i % kRing] = operand<QK, i>(vb_next, kb_next[0], kb_next[1]);
+            if constexpr (i < NM) ops[i % kRing] = operand<QK, i>(vb_next, kb_next);
         });
     }
     template <bool PV, bool QK, bool PRE>
@@ -236,10 +236,10 @@ struct Nat {
         constexpr int PF = kNatPrefetch;
         __builtin_amdgcn_s_setprio(1);
         if constexpr (!PRE) prefetch<PV, QK>(vstep, kstep);
-        const uint32_t vb = vb_next, kb0 = kb_next[0], kb1 = kb_next[1];
+        const uint32_t vb = vb_next, kb = kb_next;
         static_for<0, NM>([&](auto ic) {
             constexpr int i = ic;
-            if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb0, kb1);
+            if constexpr (i + PF < NM) ops[(i + PF) % kRing] = operand<QK, i + PF>(vb, kb);
             mfma<QK, i>(ops[i % kRing]);
             copy_step<i, NM>(cp);
             __builtin_amdgcn_sched_barrier(0);
@@ -249,31 +249,31 @@ struct Nat {
 
     // ---- VALU phase --------------------------------------------------------------
     // Masks for the step's key rows (t0k, y0k), (t1k, y1k) (no second row:
-    // live1 false).  Accumulator register r holds the block key
-    // 16 (r >> 3) + 8 g + (r & 7), i.e. x offset xrel + c_r, in both rows.
+    // live1 false).  Accumulator register r holds block key
+    // 16 (r >> 3) + 8 g + (r & 7): row r >> 3 of the step, key 8g + (r & 7)
+    // of that row's 16, whose x test is bit r & 7 of xmask.
     __device__ __forceinline__ void mask(int t0k, int y0k, int t1k, int y1k, bool live1) {
         const bool row0 = (unsigned)(y0k - ys_q) < (unsigned)kh && (unsigned)(t0k - ts_q) < (unsigned)kt;
         const bool row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh &&
                           (unsigned)(t1k - ts_q) < (unsigned)kt;
+        const uint32_t m0 = row0 ? xmask : 0u, m1 = row1 ? xmask : 0u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int c = 16 * (r >> 3) + (r & 7);
-            const bool xok = (unsigned)(xrel + c) < (unsigned)kw;
-            if (!(row0 && xok)) sacc[0][r] = -INFINITY;
-            if (!(row1 && xok)) sacc[1][r] = -INFINITY;
+            const uint32_t m = (r < 8) ? m0 : m1;
+            if (((m >> (r & 7)) & 1u) == 0u) sacc[r] = -INFINITY;
         }
     }
-    // Online softmax of the step's 32 scores per lane with the lazily moved
+    // Online softmax of the step's 16 scores per lane with the lazily moved
     // reference of the segment-masked kernel (P <= 2^kLazyLog2).
     __device__ __forceinline__ void softmax() {
-        float mx0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
-        float mx1 = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
+        float mx0 = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+        float mx1 = fmaxf(fmaxf(sacc[8], sacc[9]), sacc[10]);
 #pragma unroll
-        for (int r = 3; r < 15; r += 2) {
-            mx0 = fmaxf(fmaxf(mx0, sacc[0][r]), sacc[0][r + 1]);
-            mx1 = fmaxf(fmaxf(mx1, sacc[1][r]), sacc[1][r + 1]);
+        for (int r = 3; r < 7; r += 2) {
+            mx0 = fmaxf(fmaxf(mx0, sacc[r]), sacc[r + 1]);
+            mx1 = fmaxf(fmaxf(mx1, sacc[8 + r]), sacc[8 + r + 1]);
         }
-        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]))) * c_log2;
+        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[7]), fmaxf(mx1, sacc[15]))) * c_log2;
         const bool move = mx > m_run + kLazyLog2;
         if (__ballot(move) != 0ull) {
             const float m_new = move ? mx : m_run;
@@ -288,16 +288,13 @@ struct Nat {
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][r], c_log2, -msub));
-                ls[r & 3] += p;
-                pb[b * 2 + (r >> 3)][r & 7] = (__bf16)p;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -msub));
+            ls[r & 3] += p;
+            pb[r >> 3][r & 7] = (__bf16)p;
         }
         l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(l_run), "v"(m_run));
+        asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(l_run), "v"(m_run));
     }
 };
 
@@ -394,13 +391,14 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, g = lane >> 5;
     const int grp = wave >> 2;
-    // bft frames x bfy rows; wave-row r = wave >> 1 is row pair r % (bfy / 2)
-    // of frame r / (bfy / 2)
-    const int bfy = kBrickRows / bft, pairs = bfy / 2;
+    // bft frames x bfy rows x 32 columns; wave w takes columns 4w .. 4w + 3 of
+    // every (t, y) row of the brick, lane lr the query (lr / (4 bfy),
+    // (lr / 4) % bfy, lr % 4) of that patch
+    const int bfy = kBrickRows / bft;
     const int t0 = bt * bft, y0 = by * bfy, x0 = bx * kBrickX;
-    const int tq = t0 + (wave >> 1) / pairs;
-    const int yq = y0 + 2 * ((wave >> 1) % pairs) + (lr >> 4);
-    const int xq = x0 + 16 * (wave & 1) + (lr & 15);
+    const int tq = t0 + lr / (kPatchX * bfy);
+    const int yq = y0 + (lr / kPatchX) % bfy;
+    const int xq = x0 + kPatchX * wave + (lr % kPatchX);
     const bool active = tq < NT && yq < NH && xq < NW;
     const int qi = (min(tq, NT - 1) * NH + min(yq, NH - 1)) * NW + min(xq, NW - 1);
 
@@ -428,13 +426,20 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     A.n_rows = A.nt * A.ny;
     A.x0k = win_start(x0, KW, NW) & ~3;
     const int n_act = (A.n_rows + 1) / 2;  // steps of two key rows
-    // this wave's 32-key block inside a row, and the lane's windows
-    const int xw = min(x0 + 16 * (wave & 1), NW - 1);
-    const int boff = min((win_start(xw, KW, NW) & ~3) - A.x0k, kRowKeys - 32);
+    // this wave's 16-key block inside a row (from its first column's window
+    // start), and the lane's windows
+    const int xw = min(x0 + kPatchX * wave, NW - 1);
+    const int boff = min(win_start(xw, KW, NW) - A.x0k, kRowKeys - kBlockKeys);
     A.ts_q = win_start(min(tq, NT - 1), KT, NT);
     A.ys_q = win_start(min(yq, NH - 1), KH, NH);
     const int xs_q = win_start(min(xq, NW - 1), KW, NW);
-    A.xrel = A.x0k + boff + 8 * g - xs_q;
+    {
+        const int xrel = A.x0k + boff + 8 * g - xs_q;  // block key 8g + e is x offset xrel + e
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m |= ((unsigned)(xrel + e) < (unsigned)A.kw ? 1u : 0u) << e;
+        A.xmask = m;
+    }
     if (!active) A.ys_q = -(1 << 30);  // no key row passes the row test
 
     // ---- Q slice -> registers ----------------------------------------------------
@@ -446,11 +451,11 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     }
     // ---- per-lane LDS offsets (operand rows shifted by the block offset) -------
     {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int krow = j * kRowKeys + boff + swap23(lr);
-            A.kx[j] = krow * T::kRowBytes + ((g ^ k_swz<D>(krow)) << 4);
-        }
+        // K Q^T: accumulator row lr holds block key m = swap23(lr), i.e. key
+        // m & 15 of the block in the step's row m >> 4
+        const int m = swap23(lr);
+        const int krow = (m >> 4) * kRowKeys + boff + (m & 15);
+        A.kx = krow * T::kRowBytes + ((g ^ k_swz<D>(krow)) << 4);
         // v_swz looks at the slot row mod 4 only, and kRowKeys is a multiple
         // of 4: one base serves both rows.
         const int qg = lane >> 4, j = lane & 15;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < T::kDBlocks; ++i) A.oacc[i] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) A.pb[i] = bf16x8{};
+    for (int i = 0; i < 2; ++i) A.pb[i] = bf16x8{};
     A.m_run = -INFINITY;
     A.l_run = 0.f;
 

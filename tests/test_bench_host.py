@@ -62,8 +62,8 @@ def test_natten_counts():
     assert bench.natten_brick_frames(16, 32, 1, 11) == 1    # 1-frame t window
     # 8 heads x 8,952 two-row steps per head (4x2x32 bricks walk up to 14
     # frames x 12 key rows, fewer where windows clip at the borders), each
-    # step 2 rows x 8 waves x 32 queries x 32 keys x 2 products x 2 D
-    assert bench.natten_executed_flop(w) == pytest.approx(8 * 8952 * 2 * 8 * 32 * 32 * 4 * 128, rel=0)
+    # step 2 rows x 8 waves x 32 queries x 16 keys x 2 products x 2 D
+    assert bench.natten_executed_flop(w) == pytest.approx(8 * 8952 * 2 * 8 * 32 * 16 * 4 * 128, rel=0)
 
 
 def test_traffic_served_only_for_matching_sources(tmp_path, monkeypatch):

@@ -1,14 +1,15 @@
 """Geometry of the neighbourhood-attention kernel, on the CPU.
 
 A restatement of the kernel's index rules (natten_fwd_kernel.hip): the
-per-call brick shape (BT frames x 8/BT rows x 32 columns), the walk over the
-key rows of a brick's window union two rows per step, the 48-key rows staged
-from the brick's first window start rounded down to 4, each wave's 32-key
-block within a row, the clamp of keys past the grid row, the LDS slot
-layout, and the work-item decode (XCD renumbering, then bricks counted from
-the middle outward).
+per-call brick shape (BT frames x 8/BT rows x 32 columns, BT in 1, 2, 4, 8),
+each wave's BT x 8/BT x 4 patch of it, the walk over the key rows of a
+brick's window union two rows per step, the 48-key rows staged from the
+brick's first window start rounded down to 4, each wave's 16-key block
+within each row, the clamp of keys past the grid row, the LDS slot layout,
+and the work-item decode (XCD renumbering, then bricks counted from the
+middle outward).
 For many grids and windows it checks what the kernel relies on: every
-query's window lies inside its wave's 32-key block and inside the walked
+query's window lies inside its wave's 16-key block and inside the walked
 rows, every copied key and every LDS access is in bounds, the two copying
 waves of a row pair fetch rows 2a and 2a + 1 (or repeat row 2a), and the
 decode visits every brick once.  No GPU is involved.
@@ -20,6 +21,8 @@ import pytest
 ROW_KEYS = 48        # keys of one staged key row
 BRICK_ROWS = 8       # (t, y) query rows of a brick
 BRICK_X = 32         # query columns of a brick
+PATCH_X = 4          # query columns of a wave
+BLOCK_KEYS = 16      # keys of one row a wave multiplies
 
 
 def win_start(c, k, n):
@@ -34,7 +37,7 @@ def swap23(x):
 def brick_frames(NT, NH, KT, KH):
     kt, kh = min(KT, NT), min(KH, NH)
     best, best_rows, best_q = 1, 0, 1
-    for bt in (1, 2, 4):
+    for bt in (1, 2, 4, 8):
         by = BRICK_ROWS // bt
         rows = min(bt + kt - 1, NT) * min(by + kh - 1, NH)
         q = min(bt, NT) * min(by, NH)
@@ -56,7 +59,6 @@ def check_grid(grid, window, D, BT=None):
     assert kw <= 13, "the kernel rejects wider x windows"
     BT = brick_frames(NT, NH, KT, KH) if BT is None else BT
     BY = BRICK_ROWS // BT
-    pairs = BY // 2
     row_bytes = 2 * D
     rows_per_load = 1024 // row_bytes
     loads = 2 * ROW_KEYS * row_bytes // 1024 // 4
@@ -73,24 +75,31 @@ def check_grid(grid, window, D, BT=None):
         for r in range(n_rows):
             assert 0 <= ts + r // ny < NT and 0 <= ylo + r % ny < NH
         for wave in range(8):
-            xw = min(x0 + 16 * (wave & 1), NW - 1)
-            boff = min((win_start(xw, KW, NW) & ~3) - x0k, ROW_KEYS - 32)
-            assert 0 <= boff <= ROW_KEYS - 32 and boff % 4 == 0
+            xw = min(x0 + PATCH_X * wave, NW - 1)
+            boff = min(win_start(xw, KW, NW) - x0k, ROW_KEYS - BLOCK_KEYS)
+            assert 0 <= boff <= ROW_KEYS - BLOCK_KEYS
             for lane in range(64):
-                lr = lane & 31
-                # K operand row and transposed V rows inside the two-row slot
-                for j in range(2):
-                    assert j * ROW_KEYS + boff + swap23(lr) < 2 * ROW_KEYS
+                lr, g = lane & 31, lane >> 5
+                # K operand row (block key swap23(lr): row m >> 4, key m & 15)
+                # and the transposed V rows of both k-steps, inside the slot
+                m = swap23(lr)
+                assert 0 <= (m >> 4) * ROW_KEYS + boff + (m & 15) < 2 * ROW_KEYS
                 key = boff + 8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)
-                for kst in range(4):
-                    assert key + (kst >> 1) * ROW_KEYS + (kst & 1) * 16 + 4 < 2 * ROW_KEYS
-                tq = t0 + (wave >> 1) // pairs
-                yq = y0 + 2 * ((wave >> 1) % pairs) + (lr >> 4)
-                xq = x0 + 16 * (wave & 1) + (lr & 15)
+                for kst in range(2):
+                    assert key + kst * ROW_KEYS + 4 < 2 * ROW_KEYS
+                    assert key % 4 == (key + kst * ROW_KEYS) % 4  # one V swizzle base serves both rows
+                tq = t0 + lr // (PATCH_X * BY)
+                yq = y0 + (lr // PATCH_X) % BY
+                xq = x0 + PATCH_X * wave + lr % PATCH_X
                 if not (tq < NT and yq < NH and xq < NW):
                     continue
                 xs, ys, tsq = win_start(xq, KW, NW), win_start(yq, KH, NH), win_start(tq, KT, NT)
-                assert x0k + boff <= xs and xs + kw <= x0k + boff + 32
+                # the lane's x window is its 16-key block's keys whose bit is set in xmask
+                assert x0k + boff <= xs and xs + kw <= x0k + boff + BLOCK_KEYS
+                xrel = x0k + boff + 8 * g - xs
+                in_block = [e for e in range(8) if 0 <= xrel + e < kw]
+                assert len(in_block) == sum(1 for x in range(x0k + boff + 8 * g, x0k + boff + 8 * g + 8)
+                                            if xs <= x < xs + kw)
                 assert ylo <= ys and ys + kh <= ylo + ny
                 assert ts <= tsq and tsq + kt <= ts + nt
             # the rows this wave copies for each step (waves 0-1 of a copying
@@ -116,7 +125,7 @@ CASES = [((1, 1, 1), (1, 1, 1)), ((1, 3, 5), (3, 3, 3)), ((2, 8, 32), (3, 3, 3))
 
 
 @pytest.mark.parametrize("grid,window", CASES, ids=[f"{g}-{w}" for g, w in CASES])
-@pytest.mark.parametrize("BT", [None, 1, 2, 4], ids=["chosen", "bt1", "bt2", "bt4"])
+@pytest.mark.parametrize("BT", [None, 1, 2, 4, 8], ids=["chosen", "bt1", "bt2", "bt4", "bt8"])
 def test_windows_covered_and_accesses_in_bounds(grid, window, BT):
     check_grid(grid, window, 128, BT)
 
@@ -131,7 +140,7 @@ def test_x_widths_and_frame_counts():
 
 
 def test_brick_shape_choice():
-    assert brick_frames(16, 32, 11, 11) == 4   # 14 x 12 key rows beat 11 x 18
+    assert brick_frames(16, 32, 11, 11) == 4   # 14 x 12 key rows beat 11 x 18 (ties with 12 x 14: more frames)
     assert brick_frames(1, 32, 11, 11) == 1    # a single frame
     assert brick_frames(16, 32, 1, 11) == 1    # a one-frame t window
 
