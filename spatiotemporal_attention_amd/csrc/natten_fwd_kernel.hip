@@ -130,8 +130,9 @@ struct Nat {
     float c_log2;
     // workgroup key rows: t' in [ts, ts + nt), y' in [ylo, ylo + ny); n_rows of them
     int ts, nt, ylo, ny, n_rows, x0k, kt, kh, kw;
+    int wrap_add;       // token step from the last row of a frame's y range to the first of the next
     int kx, vx;         // operand bases of this wave's block (16 keys of each row of a slot)
-    uint32_t xmask;     // bit e: block key 8g + e of a row lies in this lane's x window
+    bool xok[8];        // block key 8g + e of a row lies in this lane's x window
     int ts_q, ys_q;     // this lane's query t- and y-window starts
     uint32_t dmo[T::kLoadsPerWave];
     bf16x8 qreg[T::kSteps];
@@ -158,8 +159,8 @@ struct Nat {
     // Step a holds key rows 2a and 2a+1 of the walk (row r is (ts + r / ny,
     // ylo + r % ny)); a missing last row repeats row 2a and is masked.  Group 0
     // copies K of step n+2 in its MFMA phase of iteration n, group 1 V of step
-    // n+1 (the ring discipline of the segment-masked kernel).  (at, ay) is the
-    // key row this wave copies.
+    // n+1 (the ring discipline of the segment-masked kernel).  tok is the
+    // token (in the head) of the first staged key of the row this wave copies.
     struct Copy {
         const __bf16* src;
         char* dst;
@@ -167,16 +168,22 @@ struct Nat {
         bool spread;
     };
     template <int G>
-    __device__ __forceinline__ void plan(Copy& c, int a, int at, int ay, int n_act) {
+    __device__ __forceinline__ void plan(Copy& c, int a, int tok, int n_act) {
         c.cnt = 0;
         c.spread = false;
         if (a < n_act) {
-            const int64_t tok = ((int64_t)(ts + at) * NH + (ylo + ay)) * NW + x0k;
-            c.src = (G ? vp : kp) + tok * tok_stride;
+            c.src = (G ? vp : kp) + (int64_t)tok * tok_stride;
             c.dst = smem + (G ? T::kVRegion : T::kKRegion) + slot_base(a) + w4 * T::kLoadsPerWave * 1024;
             c.spread = true;
             c.cnt = T::kLoadsPerWave;
         }
+    }
+    // Wait for the copies issued before this phase's (c: 0 or kLoadsPerWave).
+    __device__ __forceinline__ static void wait_own(int c) {
+        if (c != 0)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(T::kLoadsPerWave) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     // Load j of a spread copy goes out after MFMA step j*NM/L + 1 of a phase
     // with NM MFMAs.
@@ -256,11 +263,10 @@ struct Nat {
         const bool row0 = (unsigned)(y0k - ys_q) < (unsigned)kh && (unsigned)(t0k - ts_q) < (unsigned)kt;
         const bool row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh &&
                           (unsigned)(t1k - ts_q) < (unsigned)kt;
-        const uint32_t m0 = row0 ? xmask : 0u, m1 = row1 ? xmask : 0u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const uint32_t m = (r < 8) ? m0 : m1;
-            if (((m >> (r & 7)) & 1u) == 0u) sacc[r] = -INFINITY;
+            const bool ok = ((r < 8) ? row0 : row1) && xok[r & 7];
+            sacc[r] = ok ? sacc[r] : -INFINITY;
         }
     }
     // Online softmax of the step's 16 scores per lane with the lazily moved
@@ -298,17 +304,26 @@ struct Nat {
     }
 };
 
-// Position (t, y) of a key row in the workgroup's walk, relative to (ts, ylo).
-struct RowPos {
-    int t, y;
-    __device__ __forceinline__ void advance(int ny, int n) {
-        for (int i = 0; i < n; ++i)
-            if (++y == ny) {
-                y = 0;
-                ++t;
-            }
+// A key row of the workgroup's walk: ry = y' - ylo, rt = t' - ts, and tok =
+// the token of its first staged key.  step() moves to the next row (y'
+// fastest) with integer selects only: stay = -1 while the row stays in its
+// frame, 0 when it wraps to the first row of the next frame.
+struct Walk {
+    int ry, rt, tok;
+    __device__ __forceinline__ void step(int ny, int NW, int wrap_add) {
+        const int y1 = ry + 1;
+        const int stay = (y1 - ny) >> 31;
+        ry = y1 & stay;
+        rt += 1 + stay;
+        tok += (NW & stay) | (wrap_add & ~stay);
     }
 };
+
+// The token of the row a wave copies: the step's second row (b) when it has
+// one and the wave copies second rows, else its first (a); wave-uniform.
+__device__ __forceinline__ int pick_row(bool use_b, int a, int b) {
+    return __builtin_amdgcn_readfirstlane(a ^ ((a ^ b) & -(int)use_b));
+}
 
 // Ping-pong schedule of group G (see the segment-masked kernel): local
 // iteration n = MFMA phase (K Q^T of step n, P V of step n-1) at global phase
@@ -317,45 +332,48 @@ struct RowPos {
 // the step being planned, of which waves 0-1 of the group copy the first row
 // and waves 2-3 the second (the first again when the step has one row).
 template <int G, int D>
-__device__ __forceinline__ void natten_loop(Nat<D>& A, int n_act) {
+__device__ __forceinline__ void natten_loop(Nat<D>& A, int n_act, const Walk& w0) {
     typename Nat<D>::Copy cp;
     const bool second = (A.w4 >> 1) != 0;
-    RowPos mrow{0, 0}, crow{0, 0};
+    Walk mw = w0, cw = w0;
+    // plan the copy of step a (cw at its first row), then move cw two rows on
     auto plan_step = [&](int a) {
-        RowPos p = crow;
-        if (second && 2 * a + 1 < A.n_rows) p.advance(A.ny, 1);
-        A.template plan<G>(cp, a, p.t, p.y, n_act);
+        Walk w1 = cw;
+        w1.step(A.ny, A.NW, A.wrap_add);
+        A.template plan<G>(cp, a, pick_row(second && 2 * a + 1 < A.n_rows, cw.tok, w1.tok), n_act);
+        cw = w1;
+        cw.step(A.ny, A.NW, A.wrap_add);
     };
     auto valu_phase = [&](int n) {
-        RowPos r1 = mrow;
-        r1.advance(A.ny, 1);
-        A.mask(A.ts + mrow.t, A.ylo + mrow.y, A.ts + r1.t, A.ylo + r1.y, 2 * n + 1 < A.n_rows);
-        mrow.advance(A.ny, 2);
+        Walk m1 = mw;
+        m1.step(A.ny, A.NW, A.wrap_add);
+        A.mask(A.ts + mw.rt, A.ylo + mw.ry, A.ts + m1.rt, A.ylo + m1.ry, 2 * n + 1 < A.n_rows);
+        mw = m1;
+        mw.step(A.ny, A.NW, A.wrap_add);
         A.softmax();
-        crow.advance(A.ny, 2);
         plan_step(n + 3 - G);
         A.template prefetch<true, true>(n, n + 1);
         barrier();
     };
-    crow.advance(A.ny, 2 * (2 - G));  // first planned step: 2 - G
+    for (int i = 0; i < 2 * (2 - G); ++i) cw.step(A.ny, A.NW, A.wrap_add);  // first planned step: 2 - G
     plan_step(2 - G);
     A.template prefetch<false, true>(0, 0);
     if (G == 1) barrier();  // group 1 idles in global phase 0
     A.template mfma_phase<false, true, true>(0, 0, cp);
-    wait_vm(cp.cnt);
+    A.wait_own(cp.cnt);
     barrier();
     valu_phase(0);
     for (int n = 1; n < n_act; ++n) {
         const int c = cp.cnt;
         A.template mfma_phase<true, true, true>(n - 1, n, cp);
-        wait_vm(c);
+        A.wait_own(c);
         barrier();
         valu_phase(n);
     }
     {
         const int c = cp.cnt;
         A.template mfma_phase<true, false, false>(n_act - 1, 0, cp);
-        wait_vm(c);
+        A.wait_own(c);
         barrier();
     }
     if (G == 0) barrier();  // group 0 idles in the last global phase
@@ -426,6 +444,8 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     A.n_rows = A.nt * A.ny;
     A.x0k = win_start(x0, KW, NW) & ~3;
     const int n_act = (A.n_rows + 1) / 2;  // steps of two key rows
+    A.wrap_add = NW * (NH - A.ny + 1);
+    const Walk w0{0, 0, (A.ts * NH + A.ylo) * NW + A.x0k};
     // this wave's 16-key block inside a row (from its first column's window
     // start), and the lane's windows
     const int xw = min(x0 + kPatchX * wave, NW - 1);
@@ -435,10 +455,8 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     const int xs_q = win_start(min(xq, NW - 1), KW, NW);
     {
         const int xrel = A.x0k + boff + 8 * g - xs_q;  // block key 8g + e is x offset xrel + e
-        uint32_t m = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m |= ((unsigned)(xrel + e) < (unsigned)A.kw ? 1u : 0u) << e;
-        A.xmask = m;
+        for (int e = 0; e < 8; ++e) A.xok[e] = (unsigned)(xrel + e) < (unsigned)A.kw;
     }
     if (!active) A.ys_q = -(1 << 30);  // no key row passes the row test
 
@@ -490,27 +508,21 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     {
         typename Nat<D>::Copy c;
         const bool second = (A.w4 >> 1) != 0;
-        auto row_of = [&](int a) {
-            RowPos p{0, 0};
-            p.advance(A.ny, 2 * a + ((second && 2 * a + 1 < A.n_rows) ? 1 : 0));
-            return p;
-        };
-        if (grp == 0) {
-            for (int a = 0; a < 2; ++a) {
-                const RowPos p = row_of(a);
-                A.template plan<0>(c, a, p.t, p.y, n_act);
-                if (c.spread) {
-#pragma unroll
-                    for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
-                }
-            }
-        } else {
-            const RowPos p = row_of(0);
-            A.template plan<1>(c, 0, p.t, p.y, n_act);
+        Walk w = w0;
+        for (int a = 0; a < 2 - grp; ++a) {
+            Walk w1 = w;
+            w1.step(A.ny, A.NW, A.wrap_add);
+            const int tok = pick_row(second && 2 * a + 1 < A.n_rows, w.tok, w1.tok);
+            if (grp == 0)
+                A.template plan<0>(c, a, tok, n_act);
+            else
+                A.template plan<1>(c, a, tok, n_act);
             if (c.spread) {
 #pragma unroll
                 for (int j = 0; j < T::kLoadsPerWave; ++j) dma16(c.src, A.dmo[j], c.dst + j * 1024);
             }
+            w = w1;
+            w.step(A.ny, A.NW, A.wrap_add);
         }
     }
     wait_vm(0);
@@ -518,9 +530,9 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     asm volatile("" ::"v"(A.qreg[0]), "v"(A.qreg[T::kSteps - 1]));
 
     if (grp == 0)
-        natten_loop<0>(A, n_act);
+        natten_loop<0>(A, n_act, w0);
     else
-        natten_loop<1>(A, n_act);
+        natten_loop<1>(A, n_act, w0);
 
     // ---- epilogue -----------------------------------------------------------------
     const float l_tot = pair_sum(A.l_run);
