@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VDX_ABI_VERSION 5
+#define VDX_ABI_VERSION 6
 
 /* Status codes.  Argument validation runs before any HIP call, in the order
  * below (NULL -> segment pair -> shape -> head dim -> scale -> alignment),
@@ -67,8 +67,9 @@ enum vdx_status {
     VDX_ERR_LAUNCH = 8,   /* the kernel launch reported an error                */
     VDX_ERR_WINDOW = 9,   /* vdx_natten3d_fwd: a window size is even or < 1, or
                              the effective x window min(KW, NW) exceeds 13      */
-    VDX_ERR_WORKSPACE = 10, /* vdx_attn_bwd: workspace NULL, smaller than
-                             vdx_attn_bwd_workspace_size(B, S, H), or not
+    VDX_ERR_WORKSPACE = 10, /* vdx_attn_bwd, or vdx_attn_fwd_ws with segment
+                             IDs: workspace NULL, smaller than the call's
+                             vdx_attn_*_workspace_size(B, S, H), or not
                              16-byte aligned                                    */
     VDX_ERR_ROPE = 11,    /* vdx_rope3d_*: the embedding description is NULL,
                              its pos is NULL, a section width is odd or < 0,
@@ -104,6 +105,44 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
                  const int32_t* seg_q, const int32_t* seg_kv,
                  void* out, float* lse,
                  int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/*
+ * vdx_attn_fwd_ws -- vdx_attn_fwd with a caller workspace, which the masked
+ * (segment-ID) path uses to balance its uneven work; same operation and
+ * results, bit for bit.
+ *
+ * The pages motivate it (vidax paper, arXiv:2609.18077, Appendix A, Table 4,
+ * group 2): with SegmentIds a query block skips every key block of other
+ * segments, so blocks of short and long clips packed into one sequence do
+ * very different amounts of work.  With segment IDs this call enqueues four
+ * kernels: a summary of every 64-key tile's IDs, the active-tile count of
+ * every 256-query block, each batch's blocks ordered longest first, then a
+ * persistent forward whose workgroups pull (block, head) items in that order
+ * from per-XCD work counters and classify tiles from the summaries.  The
+ * counters change only which workgroup computes an item, never its result.
+ *
+ *   q ... scale, stream   exactly as for vdx_attn_fwd.
+ *   workspace  with segment IDs: device scratch of at least
+ *              vdx_attn_fwd_workspace_size(B, S, H) bytes, 16-byte aligned,
+ *              owned by the caller; its contents on entry do not matter and
+ *              are overwritten (two calls in flight at once need two
+ *              workspaces).  Without segment IDs it is not used (it may be
+ *              NULL) and the call is vdx_attn_fwd.
+ * Validation: as vdx_attn_fwd, then (segment IDs only) the workspace ->
+ * VDX_ERR_WORKSPACE; the first failure is reported before any HIP call.
+ * Results are deterministic.
+ */
+int vdx_attn_fwd_ws(const void* q, const void* k, const void* v,
+                    const int32_t* seg_q, const int32_t* seg_kv,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/* Bytes of workspace vdx_attn_fwd_ws needs with segment IDs for (B, S, H):
+ * 256 (work counters) + R(16 * B * ceil(S / 64)) (tile summaries) +
+ * R(4 * B * ceil(S / 256)) (block counts) + 4 * B * ceil(S / 256) (block
+ * orders), R() rounding up to a multiple of 256.  H does not enter.  0 if
+ * B, S or H < 1. */
+size_t vdx_attn_fwd_workspace_size(int B, int S, int H);
 
 /*
  * vdx_natten3d_fwd -- one forward pass of 3D neighbourhood (windowed)

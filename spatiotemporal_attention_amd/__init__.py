@@ -41,7 +41,7 @@ import torch
 from . import _native
 from ._native import abi_version, status_str
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "natten3d_fwd", "rope3d_apply",
+__all__ = ["attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size", "natten3d_fwd", "rope3d_apply",
            "rope3d_attn_fwd", "abi_version", "status_str", "VdxError"]
 
 
@@ -70,15 +70,29 @@ def _outputs(q: torch.Tensor, out: Optional[torch.Tensor], lse: Optional[torch.T
     return out, lse
 
 
+def attn_fwd_workspace_size(B: int, S: int, H: int) -> int:
+    """Bytes of workspace the masked forward (vdx_attn_fwd_ws) needs."""
+    return int(_native.lib.vdx_attn_fwd_workspace_size(int(B), int(S), int(H)))
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              seg_q: Optional[torch.Tensor] = None, seg_kv: Optional[torch.Tensor] = None,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
-             stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+             stream: Optional[torch.cuda.Stream] = None,
+             workspace: Optional[torch.Tensor] = None,
+             scheduled: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
     """Segment-masked attention forward on the current (or given) HIP stream.
 
     q, k, v: bf16 [B, S, H, D] contiguous on one GPU.  seg_q, seg_kv: int32
     [B, S] or both None (unmasked).  Returns (out bf16 [B,S,H,D], lse fp32 [B,H,S]).
+
+    With segment IDs the call goes to vdx_attn_fwd_ws (work counters and a
+    longest-first block order in a workspace; ``workspace``, a uint8 CUDA
+    tensor of at least attn_fwd_workspace_size(B, S, H) bytes, or one
+    allocated here on the launch stream); ``scheduled=False`` calls
+    vdx_attn_fwd, one workgroup per block in index order.  Both give the
+    same bits.
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, S, H, D]")
@@ -99,12 +113,21 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     out, lse = _outputs(q, out, lse, stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if seg_q is None else seg_q.data_ptr(),
+            0 if seg_kv is None else seg_kv.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
-        rc = _native.attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                  0 if seg_q is None else seg_q.data_ptr(),
-                                  0 if seg_kv is None else seg_kv.data_ptr(),
-                                  out.data_ptr(), lse.data_ptr(), B, S, H, D, scale,
-                                  stream.cuda_stream)
+        if seg_q is not None and scheduled:
+            need = attn_fwd_workspace_size(B, S, H)
+            if workspace is None:
+                with torch.cuda.stream(stream):
+                    workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif (workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.numel() < need
+                  or workspace.device != q.device):
+                raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {need} bytes on {q.device}")
+            rc = _native.attn_fwd_ws_raw(*ptrs, workspace.data_ptr(), workspace.numel(), B, S, H, D, scale,
+                                         stream.cuda_stream)
+        else:
+            rc = _native.attn_fwd_raw(*ptrs, B, S, H, D, scale, stream.cuda_stream)
     if rc != 0:
         raise VdxError(rc)
     return out, lse

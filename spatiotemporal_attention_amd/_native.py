@@ -24,7 +24,7 @@ VDX_ERR_WORKSPACE = 10
 VDX_ERR_ROPE = 11
 VDX_ERR_SCRATCH = 12
 
-EXPORTED = ("vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
+EXPORTED = ("vdx_attn_fwd", "vdx_attn_fwd_ws", "vdx_attn_fwd_workspace_size", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
             "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd", "vdx_status_str",
             "vdx_abi_version")
 
@@ -43,6 +43,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     i = ctypes.c_int
     lib.vdx_attn_fwd.restype = i
     lib.vdx_attn_fwd.argtypes = [p, p, p, p, p, p, p, i, i, i, i, ctypes.c_float, p]
+    lib.vdx_attn_fwd_ws.restype = i
+    lib.vdx_attn_fwd_ws.argtypes = [p] * 8 + [ctypes.c_size_t] + [i] * 4 + [ctypes.c_float, p]
+    lib.vdx_attn_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.vdx_attn_fwd_workspace_size.argtypes = [i, i, i]
     lib.vdx_natten3d_fwd.restype = i
     lib.vdx_natten3d_fwd.argtypes = [p, p, p, p, p] + [i] * 9 + [ctypes.c_float, p]
     lib.vdx_attn_bwd.restype = i
@@ -79,6 +83,13 @@ def attn_fwd_raw(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale, stream) ->
     return int(lib.vdx_attn_fwd(q or None, k or None, v or None, seg_q or None, seg_kv or None,
                                 out or None, lse or None, int(B), int(S), int(H), int(D),
                                 float(scale), stream or None))
+
+
+def attn_fwd_ws_raw(q, k, v, seg_q, seg_kv, out, lse, ws, ws_bytes, B, S, H, D, scale, stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL)."""
+    return int(lib.vdx_attn_fwd_ws(q or None, k or None, v or None, seg_q or None, seg_kv or None,
+                                   out or None, lse or None, ws or None, int(ws_bytes), int(B), int(S),
+                                   int(H), int(D), float(scale), stream or None))
 
 
 def natten3d_fwd_raw(q, k, v, out, lse, B, NT, NH, NW, H, D, KT, KH, KW, scale, stream) -> int:

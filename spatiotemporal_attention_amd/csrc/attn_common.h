@@ -191,18 +191,13 @@ __device__ int compact_tiles(const uint8_t* cls, int n_tiles, uint16_t* list, in
     return meta[3 * NW];
 }
 
-// Classifies every 64-row tile of the opposite side (segment IDs `other`, S
-// entries) against this workgroup's rows (ID `mine` per lane; 0 for padding
-// and rows past S) with tile_class() and compacts the active tiles, in
-// order, into `list`.  `cls` is scratch of n_tiles bytes, `meta` of 3 NW + 1
-// ints; every wave of the workgroup (NW of them) must call it.  Returns the
-// number of active tiles.  A wave covers four tiles per step (16 lanes a
-// tile, 4 IDs a lane) and issues kU steps' loads before reducing any of
-// them, so the loads' latency overlaps instead of adding up tile by tile.
+// Summary of the workgroup's rows (ID `mine` per lane of every wave; 0 for
+// padding and rows past S): min and max of the nonzero IDs (INT32_MAX /
+// INT32_MIN when there are none) and a flag for an ID 0.  Every wave of the
+// workgroup (NW of them) must call it; meta[3 NW] is scratch.
 template <int NW>
-__device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
-                              uint16_t* list, int* meta, int wave, int lane) {
-    constexpr int kU = 4;
+__device__ __forceinline__ void block_summary(int mine, int* meta, int wave, int lane, int& omn, int& omx,
+                                              int& ofl) {
     {
         int mn = (mine != 0) ? mine : INT32_MAX;
         int mx = (mine != 0) ? mine : INT32_MIN;
@@ -217,13 +212,31 @@ __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles
         }
     }
     __syncthreads();
-    int omn = INT32_MAX, omx = INT32_MIN, ofl = 0;
+    omn = INT32_MAX;
+    omx = INT32_MIN;
+    ofl = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         omn = min(omn, meta[i]);
         omx = max(omx, meta[NW + i]);
         ofl |= meta[2 * NW + i];
     }
+}
+
+// Classifies every 64-row tile of the opposite side (segment IDs `other`, S
+// entries) against this workgroup's rows (ID `mine` per lane; 0 for padding
+// and rows past S) with tile_class() and compacts the active tiles, in
+// order, into `list`.  `cls` is scratch of n_tiles bytes, `meta` of 3 NW + 1
+// ints; every wave of the workgroup (NW of them) must call it.  Returns the
+// number of active tiles.  A wave covers four tiles per step (16 lanes a
+// tile, 4 IDs a lane) and issues kU steps' loads before reducing any of
+// them, so the loads' latency overlaps instead of adding up tile by tile.
+template <int NW>
+__device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
+                              uint16_t* list, int* meta, int wave, int lane) {
+    constexpr int kU = 4;
+    int omn, omx, ofl;
+    block_summary<NW>(mine, meta, wave, lane, omn, omx, ofl);
     const int gq = lane >> 4, sub = lane & 15;
     const int n_groups = (n_tiles + 3) / 4;
     for (int g0 = wave; g0 < n_groups; g0 += NW * kU) {
@@ -255,6 +268,33 @@ __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles
                 fl |= __shfl_xor(fl, o);
             }
             if (sub == 0 && t < n_tiles) cls[t] = tile_class(omn, omx, ofl, mn, mx, fl);
+        }
+    }
+    return compact_tiles<NW>(cls, n_tiles, list, meta, wave, lane);
+}
+
+// classify_tiles from the opposite side's per-tile summaries instead of its
+// IDs: sum[t] = {min nonzero ID, max nonzero ID, flag, 0} of tile t, as the
+// loop above reduces them.  One lane per tile, four tiles' loads in flight
+// per lane.
+template <int NW>
+__device__ int classify_tiles_sum(int mine, const int4* sum, int n_tiles, uint8_t* cls, uint16_t* list,
+                                  int* meta, int wave, int lane) {
+    constexpr int kU = 4;
+    int omn, omx, ofl;
+    block_summary<NW>(mine, meta, wave, lane, omn, omx, ofl);
+    const int tid = wave * 64 + lane;
+    for (int t0 = 0; t0 < n_tiles; t0 += NW * 64 * kU) {
+        int4 s[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int t = t0 + u * NW * 64 + tid;
+            s[u] = (t < n_tiles) ? sum[t] : int4{INT32_MAX, INT32_MIN, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int t = t0 + u * NW * 64 + tid;
+            if (t < n_tiles) cls[t] = tile_class(omn, omx, ofl, s[u].x, s[u].y, s[u].z);
         }
     }
     return compact_tiles<NW>(cls, n_tiles, list, meta, wave, lane);

@@ -475,27 +475,33 @@ __device__ void rope_stage_q(char* smem, const __bf16* __restrict__ q, const Rop
     __syncthreads();
 }
 
-// One query block (256 queries of one (b, h)): work item w of the grid.
-template <int D, bool SEG, bool ROPE>
+// Work item w of a grid of n_wg items -> (b, h, query block), renumbered
+// XCD-contiguously: item w runs on XCD w % 8 (workgroups are dealt to the
+// XCDs round-robin and the persistent grid is a multiple of 8), and the
+// items of one XCD are consecutive query blocks of one head, which share K/V
+// tiles in that XCD's L2.
+struct ItemPos {
+    int b, h, qblk;
+};
+__device__ __forceinline__ ItemPos decode_item(int w, int n_wg, int n_qblk, int H) {
+    const int per = n_wg / kXcds, rem = n_wg % kXcds;
+    const int xcd = w % kXcds;
+    const int lid = xcd * per + min(xcd, rem) + w / kXcds;
+    const int bh = lid / n_qblk;
+    return ItemPos{bh / H, bh % H, lid % n_qblk};
+}
+
+// One query block (256 queries of one (b, h)).  With segment IDs the key
+// tiles are classified from the IDs themselves (SUM false) or from the
+// per-tile summaries tsum of the batch (SUM true, see attn_fwd_tilesum_kernel).
+template <int D, bool SEG, bool ROPE, bool SUM>
 __device__ __forceinline__ void attn_fwd_item(
     char* smem, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const int32_t* __restrict__ seg_q,
     const int32_t* __restrict__ seg_kv, __bf16* __restrict__ out, float* __restrict__ lse, int S,
-    int H, float c_log2, int n_qblk, int n_kvt, int n_wg, int w, const Rope3DDev& rope) {
+    int H, float c_log2, int n_kvt, ItemPos it, const int4* __restrict__ tsum, const Rope3DDev& rope) {
     using T = Tile<D>;
-
-    // ---- tile scheduler: XCD-contiguous renumbering of work items -----------
-    // Item w runs on XCD w % 8 (workgroups are dealt to the XCDs round-robin
-    // and the persistent grid below is a multiple of 8), and the items of one
-    // XCD are consecutive query blocks of one head, which share K/V tiles in
-    // that XCD's L2.
-    const int per = n_wg / kXcds, rem = n_wg % kXcds;
-    const int xcd = w % kXcds;
-    const int lid = xcd * per + min(xcd, rem) + w / kXcds;
-    const int qblk = lid % n_qblk;
-    const int bh = lid / n_qblk;
-    const int h = bh % H;
-    const int b = bh / H;
+    const int qblk = it.qblk, h = it.h, b = it.b;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -573,8 +579,12 @@ __device__ __forceinline__ void attn_fwd_item(
         // Every lane reads the same count from the LDS; readfirstlane states
         // that it is wave-uniform, so the loop bounds and ring-slot offsets
         // derived from it stay in scalar registers.
-        n_act = __builtin_amdgcn_readfirstlane(classify_tiles<kWaves>(
-            A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
+        if constexpr (SUM)
+            n_act = __builtin_amdgcn_readfirstlane(classify_tiles_sum<kWaves>(
+                A.myseg, tsum, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
+        else
+            n_act = __builtin_amdgcn_readfirstlane(classify_tiles<kWaves>(
+                A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
     }
 
     // ---- running softmax state and the O^T accumulators -----------------------
@@ -672,10 +682,171 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     int n_kvt, int n_wg, Rope3DDev rope) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
-        attn_fwd_item<D, SEG, ROPE>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_qblk,
-                                    n_kvt, n_wg, w, rope);
+        attn_fwd_item<D, SEG, ROPE, false>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt,
+                                           decode_item(w, n_wg, n_qblk, H), nullptr, rope);
         // Every wave is done with the LDS of this item before the next one's
         // copies land there.
+        __syncthreads();
+    }
+}
+
+// Dynamic LDS of a launch: the K/V/segment-ID ring, then (masked) the
+// active-tile list of n_kvt entries and classify_tiles' metadata.
+template <int D, bool SEG>
+constexpr size_t fwd_lds(int n_kvt) {
+    size_t lds = (size_t)Tile<D>::kRingBytes;
+    if (SEG) lds += 2 * (size_t)n_kvt;
+    lds = (lds + 15) & ~(size_t)15;
+    return lds + 32 * sizeof(int);  // meta
+}
+static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(kMaxKvTiles) <= kLdsBytes,
+              "a full active-tile list must fit in the LDS beside the ring");
+
+// ---- scheduled masked forward (caller workspace) -------------------------------------
+// With segment IDs, item lengths differ by up to ~10x (a query block of a
+// short clip skips most key tiles), and the hardware dispatcher, which hands
+// workgroups to the XCDs round-robin in index order, leaves CUs idle behind a
+// long item.  The scheduled path instead runs a persistent grid whose
+// workgroups pull items from eight work counters (one per XCD) in
+// longest-first order, and classifies key tiles from per-tile summaries
+// instead of every workgroup re-reading all of the batch's key IDs.
+// Workspace: eight counters (256 bytes), then int4 tile summaries
+// [B][n_kvt], active-tile counts [B][n_qblk] and the longest-first block
+// orders [B][n_qblk].
+struct FwdWs {
+    uint32_t* ctr;
+    int4* tsum;
+    int* cnt;
+    int* ord;
+};
+__host__ __device__ inline size_t fwd_ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
+FwdWs fwd_ws_layout(void* ws, int64_t B, int64_t n_kvt, int64_t n_qblk) {
+    char* p = reinterpret_cast<char*>(ws);
+    FwdWs w;
+    w.ctr = reinterpret_cast<uint32_t*>(p);
+    p += 256;
+    w.tsum = reinterpret_cast<int4*>(p);
+    p += fwd_ws_align((size_t)(B * n_kvt) * sizeof(int4));
+    w.cnt = reinterpret_cast<int*>(p);
+    p += fwd_ws_align((size_t)(B * n_qblk) * sizeof(int));
+    w.ord = reinterpret_cast<int*>(p);
+    return w;
+}
+
+// Summary of every 64-key tile of every batch: {min nonzero ID, max nonzero
+// ID, flag (an ID 0 or a key past S), 0}, the quantities classify_tiles
+// reduces; 16 lanes a tile, 4 IDs a lane.  Workgroup 0 also zeroes the work
+// counters of the launch that follows on the stream.
+__global__ __launch_bounds__(256) void attn_fwd_tilesum_kernel(const int32_t* __restrict__ seg_kv, int S,
+                                                               int n_kvt, int64_t n_all, int4* __restrict__ tsum,
+                                                               uint32_t* __restrict__ ctr) {
+    if (blockIdx.x == 0 && threadIdx.x < kXcds) ctr[threadIdx.x] = 0u;
+    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int sub = threadIdx.x & 15;
+    int mn = INT32_MAX, mx = INT32_MIN, fl = 0;
+    if (t < n_all) {
+        const int64_t b = t / n_kvt;
+        const int tt = (int)(t - b * n_kvt);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = tt * kBk + 4 * sub + e;
+            const int x = (r < S) ? seg_kv[b * S + r] : 0;
+            mn = (x != 0) ? min(mn, x) : mn;
+            mx = (x != 0) ? max(mx, x) : mx;
+            fl |= (x == 0) ? 1 : 0;
+        }
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+        mn = min(mn, __shfl_xor(mn, o));
+        mx = max(mx, __shfl_xor(mx, o));
+        fl |= __shfl_xor(fl, o);
+    }
+    if (sub == 0 && t < n_all) tsum[t] = int4{mn, mx, fl, 0};
+}
+
+// Active-tile count of every query block, workgroup b * n_qblk + blk: the
+// block's rows are summarised as the forward summarises them and every key
+// tile is classified from its summary.
+constexpr int kCountWaves = kBq / 64;  // one thread per query row of the block
+__global__ __launch_bounds__(kBq) void attn_fwd_count_kernel(const int32_t* __restrict__ seg_q,
+                                                            const int4* __restrict__ tsum, int S, int n_qblk,
+                                                            int n_kvt, int* __restrict__ cnt) {
+    __shared__ int meta[4 * kCountWaves];
+    const int blk = blockIdx.x % n_qblk, b = blockIdx.x / n_qblk;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int row = blk * kBq + tid;
+    const int mine = (row < S) ? seg_q[(int64_t)b * S + row] : 0;
+    int omn, omx, ofl;
+    block_summary<kCountWaves>(mine, meta, wave, lane, omn, omx, ofl);
+    const int4* ts = tsum + (int64_t)b * n_kvt;
+    int c = 0;
+    for (int t = tid; t < n_kvt; t += kBq) {
+        const int4 x = ts[t];
+        c += tile_class(omn, omx, ofl, x.x, x.y, x.z) != 0 ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) meta[3 * kCountWaves + wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < kCountWaves; ++i) n += meta[3 * kCountWaves + i];
+        cnt[(int64_t)b * n_qblk + blk] = n;
+    }
+}
+
+// Longest-first order of the query blocks of batch b (workgroup b): ord[r]
+// is the block with the r-th largest count, ties by block index (a
+// permutation of 0 .. n_qblk - 1).
+constexpr int kFwdRankThreads = 1024;
+__global__ __launch_bounds__(kFwdRankThreads) void attn_fwd_rank_kernel(const int* __restrict__ cnt,
+                                                                       int* __restrict__ ord, int n_qblk) {
+    extern __shared__ int c[];
+    const int64_t base = (int64_t)blockIdx.x * n_qblk;
+    for (int i = threadIdx.x; i < n_qblk; i += kFwdRankThreads) c[i] = cnt[base + i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_qblk; i += kFwdRankThreads) {
+        const int ci = c[i];
+        int r = 0;
+        for (int j = 0; j < n_qblk; ++j) r += (c[j] > ci) | ((c[j] == ci) & (j < i));
+        ord[base + r] = i;
+    }
+}
+
+// Persistent masked forward: workgroup p (on XCD p % 8) pulls slot k of its
+// XCD's counter and runs item e = p % 8 + 8 k of the list that walks the
+// batches, then the query blocks longest first, then the heads:
+// e = (b * n_qblk + r) * H + h, block ord[b][r].  An XCD thus takes every
+// eighth item -- all of its heads h = x (mod 8) when 8 divides H -- longest
+// first, and its workgroups stay busy until its list runs out.  Every item is
+// pulled exactly once (each counter hands out 0, 1, 2, ... and only items of
+// its residue), and a workgroup exits at the first slot past the list, so
+// every wave exits.  Requires a grid that is a multiple of 8.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
+    __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
+    int n_kvt, int n_items, FwdWs ws) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    int* slot = reinterpret_cast<int*>(smem + fwd_lds<D, true>(n_kvt) - sizeof(int));
+    const int xcd = blockIdx.x % kXcds;
+    for (;;) {
+        if (threadIdx.x == 0) *slot = (int)atomicAdd(ws.ctr + xcd, 1u);
+        __syncthreads();
+        const int64_t e = xcd + (int64_t)kXcds * __builtin_amdgcn_readfirstlane(*slot);
+        __syncthreads();  // every wave has the slot before it is reused
+        if (e >= n_items) break;
+        const int ie = (int)e;
+        const int h = ie % H, rb = ie / H;
+        const int r = rb % n_qblk, b = rb / n_qblk;
+        const int o = ws.ord[(int64_t)b * n_qblk + r];
+        const ItemPos it{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};  // a permutation; the test keeps it in range
+        attn_fwd_item<D, true, false, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
+                                            ws.tsum + (int64_t)b * n_kvt, Rope3DDev{});
         __syncthreads();
     }
 }
@@ -700,17 +871,6 @@ int64_t persistent_workgroups() {
     return g;
 }
 
-// Dynamic LDS of a launch: the K/V/segment-ID ring, then (masked) the
-// active-tile list of n_kvt entries and classify_tiles' metadata.
-template <int D, bool SEG>
-constexpr size_t fwd_lds(int n_kvt) {
-    size_t lds = (size_t)Tile<D>::kRingBytes;
-    if (SEG) lds += 2 * (size_t)n_kvt;
-    lds = (lds + 15) & ~(size_t)15;
-    return lds + 32 * sizeof(int);  // meta
-}
-static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(kMaxKvTiles) <= kLdsBytes,
-              "a full active-tile list must fit in the LDS beside the ring");
 
 template <int D, bool SEG, bool ROPE>
 hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream) {
@@ -734,7 +894,46 @@ hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream
 
 }  // namespace
 
+template <int D>
+hipError_t launch_sched_t(const AttnArgs& a, void* workspace, hipStream_t stream) {
+    const int n_qblk = (a.S + kBq - 1) / kBq;
+    const int n_kvt = (a.S + kBk - 1) / kBk;
+    const int64_t n_items64 = (int64_t)a.B * a.H * n_qblk;
+    const FwdWs ws = fwd_ws_layout(workspace, a.B, n_kvt, n_qblk);
+    const int64_t n_all = (int64_t)a.B * n_kvt;
+    hipLaunchKernelGGL(attn_fwd_tilesum_kernel, dim3((unsigned)((n_all + 15) / 16)), dim3(256), 0, stream,
+                       a.seg_kv, a.S, n_kvt, n_all, ws.tsum, ws.ctr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_fwd_count_kernel, dim3((unsigned)((int64_t)a.B * n_qblk)), dim3(kBq), 0, stream,
+                       a.seg_q, ws.tsum, a.S, n_qblk, n_kvt, ws.cnt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_fwd_rank_kernel, dim3((unsigned)a.B), dim3(kFwdRankThreads),
+                       (size_t)n_qblk * sizeof(int), stream, ws.cnt, ws.ord, n_qblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // A multiple of 8 (every XCD counter has workgroups), at most one per CU.
+    const int64_t grid = std::min<int64_t>(persistent_workgroups(), (n_items64 + kXcds - 1) / kXcds * kXcds);
+    hipLaunchKernelGGL((attn_fwd_sched_kernel<D>), dim3((unsigned)grid), dim3(kThreads), (fwd_lds<D, true>(n_kvt)),
+                       stream, reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
+                       reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv, reinterpret_cast<__bf16*>(a.out),
+                       a.lse, a.S, a.H, a.scale * kLog2e, n_qblk, n_kvt, (int)n_items64, ws);
+    return hipGetLastError();
+}
+
 int64_t max_masked_seq() { return (int64_t)kMaxKvTiles * kBk; }
+
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t S) {
+    const int64_t n_qblk = (S + kBq - 1) / kBq, n_kvt = (S + kBk - 1) / kBk;
+    return 256 + fwd_ws_align((size_t)(B * n_kvt) * sizeof(int4)) + fwd_ws_align((size_t)(B * n_qblk) * sizeof(int)) +
+           (size_t)(B * n_qblk) * sizeof(int);
+}
+
+hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t stream) {
+    if (a.seg_q == nullptr) return launch_attn_fwd(a, stream);
+    return a.D == 128 ? launch_sched_t<128>(a, workspace, stream) : launch_sched_t<64>(a, workspace, stream);
+}
 int64_t queries_per_workgroup() { return kBq; }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {

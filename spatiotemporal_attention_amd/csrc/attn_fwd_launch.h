@@ -33,6 +33,14 @@ struct AttnArgs {
 // Enqueue the forward kernel; arguments are already validated.
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 
+// The masked forward on a persistent grid with per-XCD work counters and
+// longest-first block order, with its scratch in a caller workspace of
+// attn_fwd_workspace_bytes(B, S) bytes (16-byte aligned); unmasked calls
+// ignore it and run launch_attn_fwd.
+hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t stream);
+
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t S);
+
 // The forward kernel on 3D-rotary-embedded queries (rotated in registers as
 // they are loaded) and keys (a.k must already hold the rotated keys).
 hipError_t launch_rope3d_attn_fwd(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream);

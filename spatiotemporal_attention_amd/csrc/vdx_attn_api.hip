@@ -202,6 +202,26 @@ __attribute__((visibility("default"))) int vdx_attn_fwd(
     return VDX_OK;
 }
 
+__attribute__((visibility("default"))) int vdx_attn_fwd_ws(
+    const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
+    void* out, float* lse, void* workspace, size_t workspace_bytes, int B, int S, int H, int D, float scale,
+    hipStream_t stream) {
+    int rc = validate(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
+    if (seg_q && (!workspace || !aligned(workspace, 16) || workspace_bytes < vdx::attn_fwd_workspace_bytes(B, S)))
+        return VDX_ERR_WORKSPACE;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    vdx::AttnArgs a{q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale};
+    if (vdx::launch_attn_fwd_sched(a, workspace, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
+__attribute__((visibility("default"))) size_t vdx_attn_fwd_workspace_size(int B, int S, int H) {
+    if (B < 1 || S < 1 || H < 1) return 0;
+    return vdx::attn_fwd_workspace_bytes(B, S);
+}
+
 __attribute__((visibility("default"))) int vdx_natten3d_fwd(
     const void* q, const void* k, const void* v, void* out, float* lse, int B, int NT, int NH, int NW,
     int H, int D, int KT, int KH, int KW, float scale, hipStream_t stream) {
@@ -298,7 +318,7 @@ __attribute__((visibility("default"))) const char* vdx_status_str(int status) {
         case VDX_ERR_WINDOW:
             return "VDX_ERR_WINDOW: window sizes must be odd and >= 1, the x window at most 13";
         case VDX_ERR_WORKSPACE:
-            return "VDX_ERR_WORKSPACE: workspace NULL, misaligned or smaller than vdx_attn_bwd_workspace_size";
+            return "VDX_ERR_WORKSPACE: workspace NULL, misaligned or smaller than the call's workspace size";
         case VDX_ERR_SCRATCH:
             return "VDX_ERR_SCRATCH: the call needs more scratch than vdx_attn_bwd_noalloc's static buffer holds";
         case VDX_ERR_ROPE:

@@ -33,7 +33,7 @@ def native():
 
 def test_exports_every_declared_function(native):
     names = header_functions()
-    assert names == sorted(["vdx_attn_fwd", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
+    assert names == sorted(["vdx_attn_fwd", "vdx_attn_fwd_ws", "vdx_attn_fwd_workspace_size", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
                             "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd",
                             "vdx_status_str", "vdx_abi_version"])
     for n in names:
@@ -237,6 +237,44 @@ def test_natten_python_wrapper_rejects_bad_grid():
     q = torch.zeros(1, 10, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         vdx.natten3d_fwd(q, q, q, grid=(2, 2, 2), window=(1, 1, 1))
+
+
+# --- vdx_attn_fwd_ws validation (no GPU needed) ---------------------------------------
+def wcall(native, ws=A + 0x900, ws_bytes=None, q=A, k=A + 0x100, v=A + 0x200, sq=A + 0x500, sk=A + 0x600,
+          out=A + 0x300, lse=A + 0x400, B=1, S=128, H=2, D=128, scale=0.125):
+    if ws_bytes is None:
+        ws_bytes = native.lib.vdx_attn_fwd_workspace_size(B, S, H)
+    return native.attn_fwd_ws_raw(q, k, v, sq, sk, out, lse, ws, ws_bytes, B, S, H, D, scale, 0)
+
+
+def test_fwd_workspace_size(native):
+    size = native.lib.vdx_attn_fwd_workspace_size
+    r = lambda x: (x + 255) // 256 * 256
+    # counters, then per batch int4 tile summaries, block counts, block orders
+    assert size(1, 61440, 16) == 256 + r(16 * 960) + r(4 * 240) + 4 * 240
+    assert size(2, 17920, 24) == 256 + r(16 * 2 * 280) + r(4 * 2 * 70) + 4 * 2 * 70
+    assert size(1, 1, 1) == 256 + 256 + 256 + 4
+    assert size(3, 1000, 1) == size(3, 1000, 40)  # H does not enter
+    for bad in ((0, 1, 1), (1, 0, 1), (1, 1, 0)):
+        assert size(*bad) == 0
+
+
+def test_fwd_ws_validation(native):
+    # the checks of vdx_attn_fwd, in its order, then the workspace (masked calls only)
+    assert wcall(native, q=0, ws=0) == native.VDX_ERR_NULL_PTR
+    assert wcall(native, sk=0, ws=0) == native.VDX_ERR_SEG_PAIR
+    assert wcall(native, B=0, ws=0) == native.VDX_ERR_SHAPE
+    assert wcall(native, D=96, ws=0) == native.VDX_ERR_HEAD_DIM
+    assert wcall(native, scale=0.0, ws=0) == native.VDX_ERR_SCALE
+    assert wcall(native, sq=A + 0x502, ws=0) == native.VDX_ERR_ALIGN
+    assert wcall(native, ws=0) == native.VDX_ERR_WORKSPACE
+    assert wcall(native, ws=A + 0x908) == native.VDX_ERR_WORKSPACE
+    need = native.lib.vdx_attn_fwd_workspace_size(1, 128, 2)
+    assert wcall(native, ws_bytes=need - 1) == native.VDX_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert wcall(native) == native.VDX_ERR_DEVICE
+        # without segment IDs the workspace is not used and may be NULL
+        assert wcall(native, sq=0, sk=0, ws=0, ws_bytes=0) == native.VDX_ERR_DEVICE
 
 
 # --- vdx_attn_bwd validation (no GPU needed) -------------------------------------
@@ -469,6 +507,8 @@ int main(void) {
     if (vdx_attn_bwd_noalloc(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR)
         fails |= 256;
     if (vdx_status_str(VDX_OK) == NULL) fails |= 32;
+    if (vdx_attn_fwd_ws(0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR) fails |= 512;
+    if (vdx_attn_fwd_workspace_size(1, 64, 1) == 0) fails |= 1024;
     {
         vdx_rope3d r = {0};
         if (vdx_rope3d_apply(0, 0, &r, 1, 64, 1, 64, 0) != VDX_ERR_NULL_PTR) fails |= 64;

@@ -1,0 +1,100 @@
+"""The scheduled masked forward (vdx_attn_fwd_ws: a persistent grid pulling
+(block, head) items longest first from per-XCD work counters, with key tiles
+classified from per-tile summaries) against the plain one (vdx_attn_fwd: one
+workgroup per query block, index order, tiles classified from the IDs): the
+same bits for every segment layout and size, whatever the workspace holds on
+entry.  Against the oracle it is checked by the parity sweeps, which call
+attn_fwd and so take this path for every masked case.
+"""
+import math
+
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["single", "padded", "packed", "interleaved", "singletons", "allpad", "negative", "extreme"]
+
+
+def _dev(x, seg_q, seg_kv):
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    return d, seg_q.cuda(), seg_kv.cuda()
+
+
+def run_both(x, seg_q, seg_kv, scale, workspace=None):
+    import spatiotemporal_attention_amd as vdx
+    d, sq, sk = _dev(x, seg_q, seg_kv)
+    o1, l1 = vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=scale, workspace=workspace)
+    o2, l2 = vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=scale, scheduled=False)
+    torch.cuda.synchronize()
+    return (o1, l1), (o2, l2)
+
+
+def assert_same_bits(a, b):
+    (o1, l1), (o2, l2) = a, b
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", [1, 65, 257, 1000, 4097])
+@pytest.mark.parametrize("kind", KINDS)
+def test_scheduled_equals_plain(need_gpu, S, D, kind):
+    B, H = (2, 3) if S <= 1000 else (1, 2)
+    seed = 31 * S + D
+    x = W.make_random(B, S, H, D, seed=seed)
+    seg = W.random_segments(B, S, seed + 5, kind)
+    print(f"case sched B={B} S={S} H={H} D={D} kind={kind}", flush=True)
+    assert_same_bits(*run_both(x, seg, seg.clone(), 1.0 / math.sqrt(D)))
+
+
+def test_distinct_query_and_key_segments(need_gpu):
+    B, S, H, D = 2, 700, 2, 128
+    x = W.make_random(B, S, H, D, seed=91)
+    seg_q = W.random_segments(B, S, 92, "interleaved")
+    seg_kv = W.random_segments(B, S, 93, "packed")
+    print("case sched distinct segs", flush=True)
+    assert_same_bits(*run_both(x, seg_q, seg_kv, 0.1))
+
+
+def test_workspace_contents_do_not_matter(need_gpu):
+    """A workspace full of garbage, then the same one again (its counters left
+    at the previous call's values), then a smaller call in it: every call
+    matches the plain path."""
+    import spatiotemporal_attention_amd as vdx
+    B, S, H, D = 1, 5000, 3, 128
+    ws = torch.full((vdx.attn_fwd_workspace_size(B, S, H),), 0xA5, dtype=torch.uint8, device="cuda")
+    for i, (s, kind) in enumerate([(S, "packed"), (S, "packed"), (1300, "interleaved")]):
+        x = W.make_random(B, s, H, D, seed=300 + i)
+        seg = W.random_segments(B, s, 310 + i, kind)
+        print(f"case sched workspace reuse {i} S={s}", flush=True)
+        assert_same_bits(*run_both(x, seg, seg.clone(), 0.125, workspace=ws))
+
+
+@pytest.mark.parametrize("name", ["packed_clips", "joint_video_text_pad"])
+def test_full_size_scheduled_equals_plain(need_gpu, name):
+    """At the workload's full size (thousands of items, so every workgroup of
+    the persistent grid runs many), in the launch configuration the benchmark
+    times."""
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    print(f"case sched full size {name}", flush=True)
+    assert_same_bits(*run_both(x, x["seg_q"], x["seg_kv"], w.scale))
+
+
+def test_all_ones_at_480p_size_equals_unmasked(need_gpu):
+    """All IDs 1 at the 480p layer's size: every tile is full, every block has
+    the same count, and the result is the unmasked call's, bit for bit."""
+    import spatiotemporal_attention_amd as vdx
+    w = W.WORKLOADS["dit480p_small"]
+    x = W.make_inputs(w)
+    ones = torch.ones((w.B, w.S), dtype=torch.int32)
+    print("case sched all-ones 480p", flush=True)
+    (o1, l1), (o2, l2) = run_both(x, ones, ones.clone(), w.scale)
+    assert_same_bits((o1, l1), (o2, l2))
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    o3, l3 = vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert_same_bits((o1, l1), (o3, l3))

@@ -103,6 +103,12 @@ int main(void) {
     if (vdx_attn_fwd(A, A, A, 0, 0, A, (float*)A, 1, 64, 1, 64, -1.0f, 0) != VDX_ERR_SCALE) bad |= 16;
     if (vdx_attn_fwd(A + 2, A, A, 0, 0, A, (float*)A, 1, 64, 1, 64, 0.1f, 0) != VDX_ERR_ALIGN) bad |= 32;
     if (vdx_attn_fwd(A, A, A, 0, 0, A, (float*)A, 1, 64, 1, 64, 0.1f, 0) != VDX_ERR_DEVICE) bad |= 64;
+    if (vdx_attn_fwd_ws(A, A, A, (int*)A, (int*)A, A, (float*)A, 0, 0, 1, 64, 1, 64, 0.1f, 0) != VDX_ERR_WORKSPACE)
+        bad |= 131072;
+    if (vdx_attn_fwd_ws(A, A, A, (int*)A, (int*)A, A, (float*)A, A, vdx_attn_fwd_workspace_size(1, 64, 1), 1, 64, 1,
+                        64, 0.1f, 0) != VDX_ERR_DEVICE)
+        bad |= 262144;
+    if (vdx_attn_fwd_workspace_size(0, 5, 5) != 0) bad |= 524288;
     /* neighbourhood */
     if (vdx_natten3d_fwd(A, A, A, A, (float*)A, 1, 4, 8, 32, 2, 128, 4, 3, 3, 0.1f, 0) != VDX_ERR_WINDOW) bad |= 128;
     if (vdx_natten3d_fwd(A, A, A, A, (float*)A, 1, 4, 8, 32, 2, 128, 3, 3, 3, 0.1f, 0) != VDX_ERR_DEVICE) bad |= 256;
@@ -133,6 +139,11 @@ LAUNCH_STUBS = r"""
 #include "attn_fwd_launch.h"
 namespace vdx {
 hipError_t launch_attn_fwd(const AttnArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_attn_fwd_sched(const AttnArgs&, void*, hipStream_t) { return hipErrorInvalidValue; }
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t S) {
+    const int64_t nq = (S + 255) / 256, nk = (S + 63) / 64;
+    return 256 + (size_t)((16 * B * nk + 255) / 256 * 256) + (size_t)((4 * B * nq + 255) / 256 * 256) + (size_t)(4 * B * nq);
+}
 hipError_t launch_rope3d_attn_fwd(const AttnArgs&, const Rope3DDev&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_rope3d_apply(const void*, void*, const Rope3DDev&, int, int, int, int, hipStream_t) {
     return hipErrorInvalidValue;
