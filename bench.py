@@ -1,8 +1,12 @@
 """Throughput of the segment-masked flash-attention forward on one MI355X.
 
-One step = one vdx_attn_fwd call (the whole hot path: tile scheduling,
-segment classification, QK^T, masking, online softmax, PV, epilogue) over one
-batch of seeded synthetic input already resident in HBM.  The default
+One step = one vdx_attn_fwd call (vdx_attn_fwd_ws with segment IDs; the
+whole hot path: tile scheduling, segment classification, QK^T, masking,
+online softmax, PV, epilogue) over one batch of seeded synthetic input already
+resident in HBM.  Steps call the C ABI through the binding with their
+arguments prepared once (the tensor-level wrappers check them on a first,
+untimed call), and the warm-up runs until the clock has settled (at least 3
+steps and 1 s unless --warmup is given).  The default
 workload is the 720p large-DiT layer (B=1, S=75,600 = 21x45x80 latent
 patches, H=40, D=128, bf16, unmasked), the shape the throughput target is
 quoted on.
@@ -63,15 +67,14 @@ METRIC = "attention TFLOP/s and % of bf16 MFMA peak at S=75,600 H=40 D=128 (1 GP
 BWD_METRIC = ("attention backward TFLOP/s (dq, dk, dv; 10*D flop per valid pair) and % of "
               "bf16 MFMA peak (1 GPU)")
 NATTEN_METRIC = "3D neighbourhood attention TFLOP/s (window pairs) and % of bf16 MFMA peak (1 GPU)"
+# The device code and launch configuration of each path (the C-ABI file only
+# validates arguments and calls the launchers, so it is not part of them).
 KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
-                  for f in ("attn_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
-                            "vdx_attn_api.hip")]
+                  for f in ("attn_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
-                      for f in ("attn_bwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
-                                "vdx_attn_api.hip")]
+                      for f in ("attn_bwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h")]
 NATTEN_KERNEL_SOURCES = [os.path.join(ROOT, "spatiotemporal_attention_amd", "csrc", f)
-                         for f in ("natten_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h",
-                                   "vdx_attn_api.hip")]
+                         for f in ("natten_fwd_kernel.hip", "attn_common.h", "attn_fwd_launch.h")]
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -347,10 +350,45 @@ def clock_window(step, seconds: float = CLOCK_WINDOW_S):
     CLOCK["summary"] = sampler.summary()
 
 
+def c_step(fn, *args):
+    """One timed step: a direct call of a C-ABI entry point through the binding
+    with every argument prepared beforehand (device addresses, sizes, the
+    stream handle), so that the host issues launches faster than the GPU runs
+    them and the events around a step time the launch, not the Python
+    argument checks of the tensor-level wrappers."""
+    def step():
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"{fn.__name__}: {status_str(rc)}")
+    return step
+
+
+WARMUP_SECONDS = 1.0
+
+
+def warm_up(step, warmup):
+    """Runs the untimed warm-up steps and returns how many ran: exactly
+    `warmup` when given, else at least 3 and at least WARMUP_SECONDS of
+    back-to-back steps, so that the shader clock and power have settled to
+    their sustained values before the timed region (a short kernel's first
+    launches run at a lower clock; a long power-limited one's at a higher)."""
+    if warmup is not None:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        return warmup
+    n, t0 = 0, time.perf_counter()
+    while n < 3 or time.perf_counter() - t0 < WARMUP_SECONDS:
+        for _ in range(max(1, n)):
+            step()
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(step, stream, steps, warmup, sample_clock=True):
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    """(wall ms per step, mean kernel ms per step, warm-up steps run)."""
+    warmup = warm_up(step, warmup)
     log(f"warmup done ({warmup} steps)")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -369,7 +407,7 @@ def time_steps(step, stream, steps, warmup, sample_clock=True):
     log(f"timed {steps} steps: {ms_per_step:.3f} ms/step wall, "
         f"kernel mean {np.mean(kernel_ms):.3f} ms (min {np.min(kernel_ms):.3f}, "
         f"median {np.median(kernel_ms):.3f})")
-    return ms_per_step, float(np.mean(kernel_ms))
+    return ms_per_step, float(np.mean(kernel_ms)), warmup
 
 
 def bwd_cpu_baseline(w: W.Workload, x, dout, target_s: float = 15.0):
@@ -426,11 +464,16 @@ def bwd_main(args, vdx):
     dq, dk, dv = (torch.empty_like(d["q"]) for _ in range(3))
     ws = torch.empty(vdx.attn_bwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device=dev)
 
-    def step():
-        vdx.attn_bwd(d["q"], d["k"], d["v"], out, lse, ddo, d["seg_q"], d["seg_kv"],
-                     scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+    # the first call through the tensor-level wrapper checks the arguments
+    vdx.attn_bwd(d["q"], d["k"], d["v"], out, lse, ddo, d["seg_q"], d["seg_kv"],
+                 scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+    sp = lambda t: 0 if t is None else t.data_ptr()
+    step = c_step(_native.attn_bwd_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                  sp(d["seg_q"]), sp(d["seg_kv"]), out.data_ptr(), lse.data_ptr(), ddo.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                  w.B, w.S, w.H, w.D, w.scale, stream.cuda_stream)
 
-    ms_per_step, call_ms = time_steps(step, stream, args.steps, args.warmup)
+    ms_per_step, call_ms, n_warm = time_steps(step, stream, args.steps, args.warmup)
     pairs = valid_pairs(w)
     flop = 10.0 * w.D * w.H * pairs
     value = flop / (ms_per_step * 1e-3) / 1e12
@@ -438,7 +481,7 @@ def bwd_main(args, vdx):
     n = w.B * w.S * w.H * w.D
     line = {
         "metric": BWD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": n_warm, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "pass": "bwd", "B": w.B, "S": w.S, "H": w.H, "D": w.D,
@@ -474,11 +517,13 @@ def natten_main(args, vdx):
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        vdx.natten3d_fwd(d["q"], d["k"], d["v"], w.grid, w.window, scale=w.scale, out=out,
-                         lse=lse, stream=stream)
+    vdx.natten3d_fwd(d["q"], d["k"], d["v"], w.grid, w.window, scale=w.scale, out=out, lse=lse,
+                     stream=stream)
+    step = c_step(_native.natten3d_fwd_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                  out.data_ptr(), lse.data_ptr(), w.B, *w.grid, w.H, w.D, *w.window, w.scale,
+                  stream.cuda_stream)
 
-    ms_per_step, kernel_ms = time_steps(step, stream, args.steps, args.warmup)
+    ms_per_step, kernel_ms, n_warm = time_steps(step, stream, args.steps, args.warmup)
     flop = 4.0 * w.D * w.H * w.B * w.S * natten_window_volume(w)
     executed = natten_executed_flop(w)
     value = flop / (ms_per_step * 1e-3) / 1e12
@@ -486,7 +531,7 @@ def natten_main(args, vdx):
     n = w.B * w.S * w.H * w.D
     line = {
         "metric": NATTEN_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": n_warm, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "grid": list(w.grid), "window": list(w.window),
@@ -514,7 +559,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3 and at least 1 s of steps)")
     ap.add_argument("--workload", default=W.HEADLINE,
                     choices=sorted(W.WORKLOADS) + sorted(W.NATTEN_WORKLOADS))
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
@@ -532,6 +578,9 @@ def main():
         sys.exit(2)
 
     import spatiotemporal_attention_amd as vdx
+    global _native, status_str
+    from spatiotemporal_attention_amd import _native
+    from spatiotemporal_attention_amd import status_str
 
     if args.copy_calib:
         copy_calibration()
@@ -556,6 +605,7 @@ def main():
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     rope_cfg = None
+    sp = lambda t: 0 if t is None else t.data_ptr()
     if args.rope:
         r = W.workload_rope3d(w)
         rr = dict(pos=r.pos.to(dev), cos=[c.to(dev) for c in r.cos], sin=[t.to(dev) for t in r.sin],
@@ -564,20 +614,32 @@ def main():
         rope_cfg = {"dims": list(r.dims), "interleaved": r.interleaved, "grids": W.ROPE_GRIDS[w.name],
                     "theta": W.ROPE_THETA}
 
-        def step():
-            vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=d["seg_q"], seg_kv=d["seg_kv"],
-                                scale=w.scale, k_rot=k_rot, out=out, lse=lse, stream=stream)
+        vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=d["seg_q"], seg_kv=d["seg_kv"],
+                            scale=w.scale, k_rot=k_rot, out=out, lse=lse, stream=stream)
+        desc = vdx._rope_desc(d["q"], rr["pos"], rr["cos"], rr["sin"], rr["dims"], rr["interleaved"])
+        step = c_step(_native.rope3d_attn_fwd_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                      sp(d["seg_q"]), sp(d["seg_kv"]), desc, k_rot.data_ptr(), out.data_ptr(),
+                      lse.data_ptr(), w.B, w.S, w.H, w.D, w.scale, stream.cuda_stream)
+    elif w.masked:
+        ws = torch.empty(vdx.attn_fwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device=dev)
+        vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale, out=out, lse=lse,
+                     stream=stream, workspace=ws)
+        step = c_step(_native.attn_fwd_ws_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                      sp(d["seg_q"]), sp(d["seg_kv"]), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                      ws.numel(), w.B, w.S, w.H, w.D, w.scale, stream.cuda_stream)
     else:
-        def step():
-            vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale,
-                         out=out, lse=lse, stream=stream)
+        vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale, out=out, lse=lse, stream=stream)
+        step = c_step(_native.attn_fwd_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                      0, 0, out.data_ptr(), lse.data_ptr(), w.B, w.S, w.H, w.D, w.scale,
+                      stream.cuda_stream)
 
-    ms_per_step, kernel_ms = time_steps(step, stream, args.steps, args.warmup)
+    ms_per_step, kernel_ms, n_warm = time_steps(step, stream, args.steps, args.warmup)
     clock = CLOCK["summary"]
     prepass_ms = None
     if args.rope:
         # the key pre-pass alone, timed the same way
-        prepass_ms = time_steps(lambda: vdx.rope3d_apply(d["k"], **rr, out=k_rot, stream=stream), stream,
+        prepass_ms = time_steps(c_step(_native.rope3d_apply_raw, d["k"].data_ptr(), k_rot.data_ptr(), desc,
+                                       w.B, w.S, w.H, w.D, stream.cuda_stream), stream,
                                 max(3, args.steps), 1, sample_clock=False)[1]
 
     flop = 4.0 * w.D * w.H * valid_pairs(w)
@@ -594,7 +656,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
