@@ -31,10 +31,13 @@
 //     i.e. 8 K Q^T + 8 P V MFMAs per step at D = 128, of which about half
 //     the pairs lie in the windows (11 of 16 keys in x); a block of 32 keys
 //     of one row for a 16-column patch kept a third;
-//   * element masks: key (t', y', x') is valid for a query iff t', y' and x'
-//     lie in its windows; the x test is fixed for the item (one byte per
-//     lane), the row tests change per step; invalid scores become -inf
-//     before the online softmax, which is the segment kernel's;
+//   * window tests: key (t', y', x') is valid for a query iff t', y' and x'
+//     lie in its windows.  The x test is fixed for the item, so the K Q^T
+//     chain starts from a per-lane bias of 0 / -inf instead of zero and
+//     out-of-window keys score -inf with no per-step work; the t and y tests
+//     are two per step (one per key row), applied to the row maxima and to
+//     the exponent's offset, so an out-of-window row gets probability 0;
+//     the online softmax is otherwise the segment kernel's;
 //   * copies, operand prefetch, ping-pong schedule and epilogue follow the
 //     segment-masked kernel.
 #include <hip/hip_runtime.h>
@@ -132,7 +135,8 @@ struct Nat {
     int ts, nt, ylo, ny, n_rows, x0k, kt, kh, kw;
     int wrap_add;       // token step from the last row of a frame's y range to the first of the next
     int kx, vx;         // operand bases of this wave's block (16 keys of each row of a slot)
-    bool xok[8];        // block key 8g + e of a row lies in this lane's x window
+    f32x16 xbias;       // 0 where block key 8g + (r & 7) of a row lies in this lane's x window, else -inf
+    bool row0, row1;    // the step's two key rows lie in this lane's t and y windows
     int ts_q, ys_q;     // this lane's query t- and y-window starts
     uint32_t dmo[T::kLoadsPerWave];
     bf16x8 qreg[T::kSteps];
@@ -218,7 +222,7 @@ struct Nat {
     __device__ __forceinline__ void mfma(const bf16x8& a) {
         if constexpr (QK && I < kQk) {
             if constexpr (I == 0)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], f32x16{}, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], xbias, 0, 0, 0);
             else
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[I], sacc, 0, 0, 0);
         } else {
@@ -255,19 +259,16 @@ struct Nat {
     }
 
     // ---- VALU phase --------------------------------------------------------------
-    // Masks for the step's key rows (t0k, y0k), (t1k, y1k) (no second row:
-    // live1 false).  Accumulator register r holds block key
+    // Window tests of the step's key rows (t0k, y0k), (t1k, y1k) (no second
+    // row: live1 false).  Accumulator register r holds block key
     // 16 (r >> 3) + 8 g + (r & 7): row r >> 3 of the step, key 8g + (r & 7)
-    // of that row's 16, whose x test is bit r & 7 of xmask.
-    __device__ __forceinline__ void mask(int t0k, int y0k, int t1k, int y1k, bool live1) {
-        const bool row0 = (unsigned)(y0k - ys_q) < (unsigned)kh && (unsigned)(t0k - ts_q) < (unsigned)kt;
-        const bool row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh &&
-                          (unsigned)(t1k - ts_q) < (unsigned)kt;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const bool ok = ((r < 8) ? row0 : row1) && xok[r & 7];
-            sacc[r] = ok ? sacc[r] : -INFINITY;
-        }
+    // of that row's 16.  The x test is in the scores already (the K Q^T chain
+    // starts from xbias, so keys outside the lane's x window score -inf); a row
+    // outside the lane's t or y window is left out of the maximum and given
+    // -inf in the exponent, so its probabilities are exactly 0.
+    __device__ __forceinline__ void row_tests(int t0k, int y0k, int t1k, int y1k, bool live1) {
+        row0 = (unsigned)(y0k - ys_q) < (unsigned)kh && (unsigned)(t0k - ts_q) < (unsigned)kt;
+        row1 = live1 && (unsigned)(y1k - ys_q) < (unsigned)kh && (unsigned)(t1k - ts_q) < (unsigned)kt;
     }
     // Online softmax of the step's 16 scores per lane with the lazily moved
     // reference of the segment-masked kernel (P <= 2^kLazyLog2).
@@ -279,7 +280,9 @@ struct Nat {
             mx0 = fmaxf(fmaxf(mx0, sacc[r]), sacc[r + 1]);
             mx1 = fmaxf(fmaxf(mx1, sacc[8 + r]), sacc[8 + r + 1]);
         }
-        const float mx = pair_max(fmaxf(fmaxf(mx0, sacc[7]), fmaxf(mx1, sacc[15]))) * c_log2;
+        mx0 = row0 ? fmaxf(mx0, sacc[7]) : -INFINITY;
+        mx1 = row1 ? fmaxf(mx1, sacc[15]) : -INFINITY;
+        const float mx = pair_max(fmaxf(mx0, mx1)) * c_log2;
         const bool move = mx > m_run + kLazyLog2;
         if (__ballot(move) != 0ull) {
             const float m_new = move ? mx : m_run;
@@ -292,10 +295,11 @@ struct Nat {
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+        const float a0 = row0 ? -msub : -INFINITY, a1 = row1 ? -msub : -INFINITY;
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -msub));
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, r < 8 ? a0 : a1));
             ls[r & 3] += p;
             pb[r >> 3][r & 7] = (__bf16)p;
         }
@@ -347,7 +351,7 @@ __device__ __forceinline__ void natten_loop(Nat<D>& A, int n_act, const Walk& w0
     auto valu_phase = [&](int n) {
         Walk m1 = mw;
         m1.step(A.ny, A.NW, A.wrap_add);
-        A.mask(A.ts + mw.rt, A.ylo + mw.ry, A.ts + m1.rt, A.ylo + m1.ry, 2 * n + 1 < A.n_rows);
+        A.row_tests(A.ts + mw.rt, A.ylo + mw.ry, A.ts + m1.rt, A.ylo + m1.ry, 2 * n + 1 < A.n_rows);
         mw = m1;
         mw.step(A.ny, A.NW, A.wrap_add);
         A.softmax();
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void natten_fwd_kernel(
     {
         const int xrel = A.x0k + boff + 8 * g - xs_q;  // block key 8g + e is x offset xrel + e
 #pragma unroll
-        for (int e = 0; e < 8; ++e) A.xok[e] = (unsigned)(xrel + e) < (unsigned)A.kw;
+        for (int r = 0; r < 16; ++r) A.xbias[r] = (unsigned)(xrel + (r & 7)) < (unsigned)A.kw ? 0.f : -INFINITY;
     }
     if (!active) A.ys_q = -(1 << 30);  // no key row passes the row test
 
