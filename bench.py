@@ -28,7 +28,7 @@ With --workload natten_vae_decoder (or natten_tiny) the step is one
 vdx_natten3d_fwd call instead (3D neighbourhood attention over a t x h x w
 grid), and the FLOP count is that of the window pairs: 4*D*H*B*S*|window|.
 
-With --rope the step is one vdx_rope3d_attn_fwd call on the workload: the 3D
+With --rope the step is one vdx_rope3d_attn_fwd_ws call on the workload: the 3D
 rotary position embedding of the keys (a pre-pass into a resident buffer) and
 of the queries (in the attention kernel's prologue), then the same attention;
 the FLOP count is the attention's.
@@ -565,7 +565,7 @@ def main():
                     choices=sorted(W.WORKLOADS) + sorted(W.NATTEN_WORKLOADS))
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--rope", action="store_true",
-                    help="time vdx_rope3d_attn_fwd (3D rotary embedding of q and k, then attention)")
+                    help="time vdx_rope3d_attn_fwd_ws (3D rotary embedding of q and k, then attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
@@ -617,9 +617,11 @@ def main():
         vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=d["seg_q"], seg_kv=d["seg_kv"],
                             scale=w.scale, k_rot=k_rot, out=out, lse=lse, stream=stream)
         desc = vdx._rope_desc(d["q"], rr["pos"], rr["cos"], rr["sin"], rr["dims"], rr["interleaved"])
-        step = c_step(_native.rope3d_attn_fwd_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+        ws = torch.empty(vdx.attn_fwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device=dev)
+        step = c_step(_native.rope3d_attn_fwd_ws_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
                       sp(d["seg_q"]), sp(d["seg_kv"]), desc, k_rot.data_ptr(), out.data_ptr(),
-                      lse.data_ptr(), w.B, w.S, w.H, w.D, w.scale, stream.cuda_stream)
+                      lse.data_ptr(), ws.data_ptr(), ws.numel(), w.B, w.S, w.H, w.D, w.scale,
+                      stream.cuda_stream)
     elif w.masked:
         ws = torch.empty(vdx.attn_fwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device=dev)
         vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale, out=out, lse=lse,
@@ -672,7 +674,7 @@ def main():
         "clock": clock,
     }
     if args.rope:
-        line["roofline"]["scope"] = "vdx_rope3d_attn_fwd call (key pre-pass + attention kernel)"
+        line["roofline"]["scope"] = "vdx_rope3d_attn_fwd_ws call (key pre-pass + attention kernels)"
         line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")

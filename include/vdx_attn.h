@@ -31,7 +31,9 @@
  * beyond a per-device, once-cached architecture check.  Calls are
  * asynchronous on `stream` (0 = null stream); buffers must stay alive until
  * the stream work completes.  Results are deterministic: the same inputs give
- * bit-identical outputs (fixed reduction order, no atomics).
+ * bit-identical outputs (fixed reduction order, no atomics in the arithmetic;
+ * the *_ws entry points hand out work items with atomic counters in their
+ * workspace, which decides only which workgroup computes an item).
  */
 #ifndef VDX_ATTN_H
 #define VDX_ATTN_H
@@ -67,7 +69,7 @@ enum vdx_status {
     VDX_ERR_LAUNCH = 8,   /* the kernel launch reported an error                */
     VDX_ERR_WINDOW = 9,   /* vdx_natten3d_fwd: a window size is even or < 1, or
                              the effective x window min(KW, NW) exceeds 13      */
-    VDX_ERR_WORKSPACE = 10, /* vdx_attn_bwd, or vdx_attn_fwd_ws with segment
+    VDX_ERR_WORKSPACE = 10, /* vdx_attn_bwd, or a *_ws forward with segment
                              IDs: workspace NULL, smaller than the call's
                              vdx_attn_*_workspace_size(B, S, H), or not
                              16-byte aligned                                    */
@@ -336,6 +338,21 @@ int vdx_rope3d_attn_fwd(const void* q, const void* k, const void* v,
                         const vdx_rope3d* rope, void* k_rot,
                         void* out, float* lse,
                         int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/*
+ * vdx_rope3d_attn_fwd_ws -- vdx_rope3d_attn_fwd with the masked path of
+ * vdx_attn_fwd_ws: with segment IDs the attention runs on the persistent,
+ * longest-first schedule of vdx_attn_fwd_ws (same workspace layout and size,
+ * vdx_attn_fwd_workspace_size(B, S, H)); without them the workspace is not
+ * used (it may be NULL).  Same results as vdx_rope3d_attn_fwd, bit for bit.
+ * Validation: as vdx_rope3d_attn_fwd, then (segment IDs only) the workspace
+ * -> VDX_ERR_WORKSPACE.
+ */
+int vdx_rope3d_attn_fwd_ws(const void* q, const void* k, const void* v,
+                           const int32_t* seg_q, const int32_t* seg_kv,
+                           const vdx_rope3d* rope, void* k_rot,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           int B, int S, int H, int D, float scale, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* vdx_status_str(int status);

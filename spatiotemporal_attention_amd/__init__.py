@@ -75,6 +75,18 @@ def attn_fwd_workspace_size(B: int, S: int, H: int) -> int:
     return int(_native.lib.vdx_attn_fwd_workspace_size(int(B), int(S), int(H)))
 
 
+def _workspace(workspace: Optional[torch.Tensor], B: int, S: int, H: int, device, stream) -> torch.Tensor:
+    """Checks a caller's forward workspace, or allocates one on the launch stream."""
+    need = attn_fwd_workspace_size(B, S, H)
+    if workspace is None:
+        with torch.cuda.stream(stream):
+            return torch.empty(need, dtype=torch.uint8, device=device)
+    if (workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.numel() < need
+            or workspace.device != device):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {need} bytes on {device}")
+    return workspace
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
              seg_q: Optional[torch.Tensor] = None, seg_kv: Optional[torch.Tensor] = None,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
@@ -117,13 +129,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             0 if seg_kv is None else seg_kv.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
         if seg_q is not None and scheduled:
-            need = attn_fwd_workspace_size(B, S, H)
-            if workspace is None:
-                with torch.cuda.stream(stream):
-                    workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            elif (workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.numel() < need
-                  or workspace.device != q.device):
-                raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {need} bytes on {q.device}")
+            workspace = _workspace(workspace, B, S, H, q.device, stream)
             rc = _native.attn_fwd_ws_raw(*ptrs, workspace.data_ptr(), workspace.numel(), B, S, H, D, scale,
                                          stream.cuda_stream)
         else:
@@ -297,11 +303,15 @@ def rope3d_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torc
                     seg_kv: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                     k_rot: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None,
-                    stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    stream: Optional[torch.cuda.Stream] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    scheduled: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
     """``attn_fwd`` on the 3D-rotary-embedded queries and keys (see
     ``rope3d_apply``; v is used as given).  k_rot: bf16 like k, receives the
-    rotated keys (allocated here if None; may be k itself).  Returns
-    (out bf16 [B,S,H,D], lse fp32 [B,H,S])."""
+    rotated keys (allocated here if None; may be k itself).  With segment IDs
+    the call goes to vdx_rope3d_attn_fwd_ws with ``workspace`` (as for
+    ``attn_fwd``) unless ``scheduled=False``.  Returns (out bf16 [B,S,H,D],
+    lse fp32 [B,H,S])."""
     if q.dim() != 4:
         raise ValueError("q must be [B, S, H, D]")
     B, S, H, D = q.shape
@@ -328,11 +338,15 @@ def rope3d_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torc
     elif k_rot.dtype != torch.bfloat16 or k_rot.shape != k.shape or not k_rot.is_contiguous() \
             or k_rot.device != q.device:
         raise ValueError("k_rot must be a contiguous bf16 tensor like k")
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if seg_q is None else seg_q.data_ptr(),
+            0 if seg_kv is None else seg_kv.data_ptr(), desc, k_rot.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
-        rc = _native.rope3d_attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                         0 if seg_q is None else seg_q.data_ptr(),
-                                         0 if seg_kv is None else seg_kv.data_ptr(), desc, k_rot.data_ptr(),
-                                         out.data_ptr(), lse.data_ptr(), B, S, H, D, scale, stream.cuda_stream)
+        if seg_q is not None and scheduled:
+            workspace = _workspace(workspace, B, S, H, q.device, stream)
+            rc = _native.rope3d_attn_fwd_ws_raw(*ptrs, workspace.data_ptr(), workspace.numel(), B, S, H, D, scale,
+                                                stream.cuda_stream)
+        else:
+            rc = _native.rope3d_attn_fwd_raw(*ptrs, B, S, H, D, scale, stream.cuda_stream)
     if rc != 0:
         raise VdxError(rc)
     return out, lse

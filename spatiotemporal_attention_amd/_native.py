@@ -24,9 +24,9 @@ VDX_ERR_WORKSPACE = 10
 VDX_ERR_ROPE = 11
 VDX_ERR_SCRATCH = 12
 
-EXPORTED = ("vdx_attn_fwd", "vdx_attn_fwd_ws", "vdx_attn_fwd_workspace_size", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
-            "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd", "vdx_status_str",
-            "vdx_abi_version")
+EXPORTED = ("vdx_attn_fwd", "vdx_attn_fwd_ws", "vdx_attn_fwd_workspace_size", "vdx_natten3d_fwd",
+            "vdx_attn_bwd", "vdx_attn_bwd_noalloc", "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply",
+            "vdx_rope3d_attn_fwd", "vdx_rope3d_attn_fwd_ws", "vdx_status_str", "vdx_abi_version")
 
 
 class Rope3D(ctypes.Structure):
@@ -60,6 +60,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vdx_rope3d_attn_fwd.restype = i
     lib.vdx_rope3d_attn_fwd.argtypes = [p, p, p, p, p, ctypes.POINTER(Rope3D), p, p, p, i, i, i, i,
                                         ctypes.c_float, p]
+    lib.vdx_rope3d_attn_fwd_ws.restype = i
+    lib.vdx_rope3d_attn_fwd_ws.argtypes = [p, p, p, p, p, ctypes.POINTER(Rope3D), p, p, p, p, ctypes.c_size_t,
+                                           i, i, i, i, ctypes.c_float, p]
     lib.vdx_status_str.restype = ctypes.c_char_p
     lib.vdx_status_str.argtypes = [i]
     lib.vdx_abi_version.restype = i
@@ -150,3 +153,12 @@ def rope3d_attn_fwd_raw(q, k, v, seg_q, seg_kv, rope: Rope3D, k_rot, out, lse, B
                                        None if rope is None else ctypes.byref(rope), k_rot or None,
                                        out or None, lse or None, int(B), int(S), int(H), int(D),
                                        float(scale), stream or None))
+
+
+def rope3d_attn_fwd_ws_raw(q, k, v, seg_q, seg_kv, rope: Rope3D, k_rot, out, lse, ws, ws_bytes, B, S, H, D,
+                           scale, stream) -> int:
+    """Direct C call with integer device addresses (0 for NULL); rope may be None."""
+    return int(lib.vdx_rope3d_attn_fwd_ws(q or None, k or None, v or None, seg_q or None, seg_kv or None,
+                                          None if rope is None else ctypes.byref(rope), k_rot or None,
+                                          out or None, lse or None, ws or None, int(ws_bytes), int(B), int(S),
+                                          int(H), int(D), float(scale), stream or None))

@@ -824,13 +824,14 @@ __global__ __launch_bounds__(kFwdRankThreads) void attn_fwd_rank_kernel(const in
 // first, and its workgroups stay busy until its list runs out.  Every item is
 // pulled exactly once (each counter hands out 0, 1, 2, ... and only items of
 // its residue), and a workgroup exits at the first slot past the list, so
-// every wave exits.  Requires a grid that is a multiple of 8.
-template <int D>
+// every wave exits.  Requires a grid that is a multiple of 8.  ROPE: the
+// queries are rotated in the item prologue, as in attn_fwd_kernel.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
     __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
-    int n_kvt, int n_items, FwdWs ws) {
+    int n_kvt, int n_items, FwdWs ws, Rope3DDev rope) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     int* slot = reinterpret_cast<int*>(smem + fwd_lds<D, true>(n_kvt) - sizeof(int));
     const int xcd = blockIdx.x % kXcds;
@@ -845,8 +846,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
         const int r = rb % n_qblk, b = rb / n_qblk;
         const int o = ws.ord[(int64_t)b * n_qblk + r];
         const ItemPos it{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};  // a permutation; the test keeps it in range
-        attn_fwd_item<D, true, false, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
-                                            ws.tsum + (int64_t)b * n_kvt, Rope3DDev{});
+        attn_fwd_item<D, true, ROPE, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
+                                           ws.tsum + (int64_t)b * n_kvt, rope);
         __syncthreads();
     }
 }
@@ -894,8 +895,8 @@ hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream
 
 }  // namespace
 
-template <int D>
-hipError_t launch_sched_t(const AttnArgs& a, void* workspace, hipStream_t stream) {
+template <int D, bool ROPE>
+hipError_t launch_sched_t(const AttnArgs& a, const Rope3DDev& rope, void* workspace, hipStream_t stream) {
     const int n_qblk = (a.S + kBq - 1) / kBq;
     const int n_kvt = (a.S + kBk - 1) / kBk;
     const int64_t n_items64 = (int64_t)a.B * a.H * n_qblk;
@@ -915,10 +916,11 @@ hipError_t launch_sched_t(const AttnArgs& a, void* workspace, hipStream_t stream
     if (e != hipSuccess) return e;
     // A multiple of 8 (every XCD counter has workgroups), at most one per CU.
     const int64_t grid = std::min<int64_t>(persistent_workgroups(), (n_items64 + kXcds - 1) / kXcds * kXcds);
-    hipLaunchKernelGGL((attn_fwd_sched_kernel<D>), dim3((unsigned)grid), dim3(kThreads), (fwd_lds<D, true>(n_kvt)),
-                       stream, reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
-                       reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv, reinterpret_cast<__bf16*>(a.out),
-                       a.lse, a.S, a.H, a.scale * kLog2e, n_qblk, n_kvt, (int)n_items64, ws);
+    hipLaunchKernelGGL((attn_fwd_sched_kernel<D, ROPE>), dim3((unsigned)grid), dim3(kThreads),
+                       (fwd_lds<D, true>(n_kvt)), stream, reinterpret_cast<const __bf16*>(a.q),
+                       reinterpret_cast<const __bf16*>(a.k), reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
+                       reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, a.scale * kLog2e, n_qblk, n_kvt,
+                       (int)n_items64, ws, rope);
     return hipGetLastError();
 }
 
@@ -932,7 +934,16 @@ size_t attn_fwd_workspace_bytes(int64_t B, int64_t S) {
 
 hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t stream) {
     if (a.seg_q == nullptr) return launch_attn_fwd(a, stream);
-    return a.D == 128 ? launch_sched_t<128>(a, workspace, stream) : launch_sched_t<64>(a, workspace, stream);
+    const Rope3DDev none{};
+    return a.D == 128 ? launch_sched_t<128, false>(a, none, workspace, stream)
+                      : launch_sched_t<64, false>(a, none, workspace, stream);
+}
+
+hipError_t launch_rope3d_attn_fwd_sched(const AttnArgs& a, const Rope3DDev& rope, void* workspace,
+                                        hipStream_t stream) {
+    if (a.seg_q == nullptr) return launch_rope3d_attn_fwd(a, rope, stream);
+    return a.D == 128 ? launch_sched_t<128, true>(a, rope, workspace, stream)
+                      : launch_sched_t<64, true>(a, rope, workspace, stream);
 }
 int64_t queries_per_workgroup() { return kBq; }
 

@@ -45,6 +45,11 @@ size_t attn_fwd_workspace_bytes(int64_t B, int64_t S);
 // they are loaded) and keys (a.k must already hold the rotated keys).
 hipError_t launch_rope3d_attn_fwd(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream);
 
+// launch_rope3d_attn_fwd with the masked path of launch_attn_fwd_sched (same
+// workspace); unmasked calls ignore the workspace.
+hipError_t launch_rope3d_attn_fwd_sched(const AttnArgs& a, const Rope3DDev& rope, void* workspace,
+                                        hipStream_t stream);
+
 // y = the 3D rotary embedding of x (bf16 [B, S, H, D]; y may be x).
 hipError_t launch_rope3d_apply(const void* x, void* y, const Rope3DDev& r, int B, int S, int H, int D,
                                hipStream_t stream);

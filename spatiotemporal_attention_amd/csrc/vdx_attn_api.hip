@@ -279,6 +279,27 @@ __attribute__((visibility("default"))) int vdx_rope3d_attn_fwd(
     return VDX_OK;
 }
 
+__attribute__((visibility("default"))) int vdx_rope3d_attn_fwd_ws(
+    const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
+    const vdx_rope3d* rope, void* k_rot, void* out, float* lse, void* workspace, size_t workspace_bytes, int B,
+    int S, int H, int D, float scale, hipStream_t stream) {
+    if (!k_rot && q && k && v && out && lse) return VDX_ERR_NULL_PTR;
+    int rc = validate(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale);
+    if (rc != VDX_OK) return rc;
+    if (!aligned(k_rot, 16)) return VDX_ERR_ALIGN;
+    vdx::Rope3DDev dev{};
+    rc = validate_rope(rope, D, dev);
+    if (rc != VDX_OK) return rc;
+    if (seg_q && (!workspace || !aligned(workspace, 16) || workspace_bytes < vdx::attn_fwd_workspace_bytes(B, S)))
+        return VDX_ERR_WORKSPACE;
+    rc = check_device();
+    if (rc != VDX_OK) return rc;
+    if (vdx::launch_rope3d_apply(k, k_rot, dev, B, S, H, D, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    vdx::AttnArgs a{q, k_rot, v, seg_q, seg_kv, out, lse, B, S, H, D, scale};
+    if (vdx::launch_rope3d_attn_fwd_sched(a, dev, workspace, stream) != hipSuccess) return VDX_ERR_LAUNCH;
+    return VDX_OK;
+}
+
 __attribute__((visibility("default"))) int vdx_attn_bwd_noalloc(
     const void* q, const void* k, const void* v, const int32_t* seg_q, const int32_t* seg_kv,
     const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int S,

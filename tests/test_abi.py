@@ -33,8 +33,9 @@ def native():
 
 def test_exports_every_declared_function(native):
     names = header_functions()
-    assert names == sorted(["vdx_attn_fwd", "vdx_attn_fwd_ws", "vdx_attn_fwd_workspace_size", "vdx_natten3d_fwd", "vdx_attn_bwd", "vdx_attn_bwd_noalloc",
-                            "vdx_attn_bwd_workspace_size", "vdx_rope3d_apply", "vdx_rope3d_attn_fwd",
+    assert names == sorted(["vdx_attn_fwd", "vdx_attn_fwd_ws", "vdx_attn_fwd_workspace_size", "vdx_natten3d_fwd",
+                            "vdx_attn_bwd", "vdx_attn_bwd_noalloc", "vdx_attn_bwd_workspace_size",
+                            "vdx_rope3d_apply", "vdx_rope3d_attn_fwd", "vdx_rope3d_attn_fwd_ws",
                             "vdx_status_str", "vdx_abi_version"])
     for n in names:
         assert hasattr(native.lib, n), n
@@ -480,6 +481,34 @@ def test_rope_attn_validation(native):
     assert rattn(native, k_rot=A + 2, rope=None) == native.VDX_ERR_ALIGN
 
 
+def rattn_ws(native, ws=A + 0xe00, ws_bytes=None, sq=A + 0x500, sk=A + 0x700, rope="default", k_rot=A + 0x600,
+             B=1, S=128, H=2, D=128, **kw):
+    r = rdesc(native) if rope == "default" else rope
+    if ws_bytes is None:
+        ws_bytes = native.lib.vdx_attn_fwd_workspace_size(B, S, H)
+    return native.rope3d_attn_fwd_ws_raw(kw.get("q", A), kw.get("k", A + 0x100), kw.get("v", A + 0x200), sq, sk, r,
+                                         k_rot, kw.get("out", A + 0x300), kw.get("lse", A + 0x400), ws, ws_bytes,
+                                         B, S, H, D, kw.get("scale", 0.125), 0)
+
+
+def test_rope_attn_ws_validation(native):
+    # vdx_rope3d_attn_fwd's checks in its order, then the workspace (masked calls only)
+    assert rattn_ws(native, k_rot=0, ws=0) == native.VDX_ERR_NULL_PTR
+    assert rattn_ws(native, sk=0, ws=0) == native.VDX_ERR_SEG_PAIR
+    assert rattn_ws(native, B=0, ws=0) == native.VDX_ERR_SHAPE
+    assert rattn_ws(native, D=32, ws=0) == native.VDX_ERR_HEAD_DIM
+    assert rattn_ws(native, scale=0.0, ws=0) == native.VDX_ERR_SCALE
+    assert rattn_ws(native, k_rot=A + 0x608, ws=0) == native.VDX_ERR_ALIGN
+    assert rattn_ws(native, rope=None, ws=0) == native.VDX_ERR_ROPE
+    assert rattn_ws(native, ws=0) == native.VDX_ERR_WORKSPACE
+    assert rattn_ws(native, ws=A + 0xe04) == native.VDX_ERR_WORKSPACE
+    need = native.lib.vdx_attn_fwd_workspace_size(1, 128, 2)
+    assert rattn_ws(native, ws_bytes=need - 1) == native.VDX_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert rattn_ws(native) == native.VDX_ERR_DEVICE
+        assert rattn_ws(native, sq=0, sk=0, ws=0, ws_bytes=0) == native.VDX_ERR_DEVICE
+
+
 def test_rope_valid_arguments_without_gpu_report_device_error(native):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible; this path would launch on fake addresses")
@@ -509,6 +538,11 @@ int main(void) {
     if (vdx_status_str(VDX_OK) == NULL) fails |= 32;
     if (vdx_attn_fwd_ws(0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR) fails |= 512;
     if (vdx_attn_fwd_workspace_size(1, 64, 1) == 0) fails |= 1024;
+    {
+        vdx_rope3d r = {0};
+        if (vdx_rope3d_attn_fwd_ws(0, 0, 0, 0, 0, &r, 0, 0, 0, 0, 0, 1, 64, 1, 64, 0.125f, 0) != VDX_ERR_NULL_PTR)
+            fails |= 2048;
+    }
     {
         vdx_rope3d r = {0};
         if (vdx_rope3d_apply(0, 0, &r, 1, 64, 1, 64, 0) != VDX_ERR_NULL_PTR) fails |= 64;

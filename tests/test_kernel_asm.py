@@ -198,10 +198,10 @@ def test_checker_flags_a_planted_hazard():
 def test_no_kernel_spills_to_scratch(asm_text):
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm_text)]
     # D in {64, 128} x {unmasked, segment-masked} x {plain, 3D-rotary-embedded queries},
-    # the scheduled masked kernel for D in {64, 128}, and its three set-up kernels
-    # (tile summaries, block counts, block order)
-    assert len(sizes) == 13
-    assert sizes == [0] * 13
+    # the scheduled masked kernel for the same D and query variants, and its three
+    # set-up kernels (tile summaries, block counts, block order)
+    assert len(sizes) == 15
+    assert sizes == [0] * 15
 
 
 def test_neighbourhood_kernel_wait_states_and_no_spills(natten_asm_text):

@@ -182,3 +182,37 @@ def test_full_size_fused_equals_composed_and_sampled_rows(need_gpu, name):
     lg = l1[:, heads].contiguous()
     st = check_rows(og, lg, rows, out_o, lse_o, valid_rows(seg, seg, w.B, w.S), sens)
     print(name, st, flush=True)
+
+
+# --- the scheduled masked path (vdx_rope3d_attn_fwd_ws) ------------------------------------------
+def fused_both_schedules(x, r, seg, scale):
+    import spatiotemporal_attention_amd as vdx
+    d = {k_: x[k_].cuda() for k_ in ("q", "k", "v")}
+    sd = seg.cuda()
+    rr = dev_rope(r)
+    o1, l1 = vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=sd, seg_kv=sd, scale=scale)
+    o2, l2 = vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=sd, seg_kv=sd, scale=scale, scheduled=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+@pytest.mark.parametrize("interleaved", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["packed", "padded", "negative", "interleaved"])
+def test_fused_scheduled_equals_plain(need_gpu, kind, D, interleaved):
+    """vdx_rope3d_attn_fwd_ws (persistent, longest-first) and vdx_rope3d_attn_fwd
+    (one workgroup per block) give the same bits."""
+    B, S, H = 2, 2100, 2
+    x = W.make_random(B, S, H, D, seed=400 + D)
+    r = random_rope(B, S, D, 401 + D, interleaved=interleaved)
+    seg = W.random_segments(B, S, 402 + D, kind)
+    print(f"case rope scheduled B={B} S={S} H={H} D={D} kind={kind} interleaved={interleaved}", flush=True)
+    fused_both_schedules(x, r, seg, 1.0 / math.sqrt(D))
+
+
+def test_full_size_packed_clips_scheduled_equals_plain(need_gpu):
+    w = W.WORKLOADS["packed_clips"]
+    print("case packed_clips: rope scheduled vs plain, full size", flush=True)
+    x = W.make_inputs(w)
+    fused_both_schedules(x, W.workload_rope3d(w), x["seg_q"], w.scale)

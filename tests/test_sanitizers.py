@@ -109,6 +109,13 @@ int main(void) {
                         64, 0.1f, 0) != VDX_ERR_DEVICE)
         bad |= 262144;
     if (vdx_attn_fwd_workspace_size(0, 5, 5) != 0) bad |= 524288;
+    {
+        vdx_rope3d rw = {(const int*)A, {(float*)A, (float*)A, (float*)A}, {(float*)A, (float*)A, (float*)A},
+                         {4, 5, 6}, {20, 22, 22}, 1};
+        if (vdx_rope3d_attn_fwd_ws(A, A, A, (int*)A, (int*)A, &rw, A, A, (float*)A, 0, 0, 1, 64, 1, 64, 0.1f, 0) !=
+            VDX_ERR_WORKSPACE)
+            bad |= 1048576;
+    }
     /* neighbourhood */
     if (vdx_natten3d_fwd(A, A, A, A, (float*)A, 1, 4, 8, 32, 2, 128, 4, 3, 3, 0.1f, 0) != VDX_ERR_WINDOW) bad |= 128;
     if (vdx_natten3d_fwd(A, A, A, A, (float*)A, 1, 4, 8, 32, 2, 128, 3, 3, 3, 0.1f, 0) != VDX_ERR_DEVICE) bad |= 256;
@@ -140,6 +147,9 @@ LAUNCH_STUBS = r"""
 namespace vdx {
 hipError_t launch_attn_fwd(const AttnArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_attn_fwd_sched(const AttnArgs&, void*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_rope3d_attn_fwd_sched(const AttnArgs&, const Rope3DDev&, void*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t S) {
     const int64_t nq = (S + 255) / 256, nk = (S + 63) / 64;
     return 256 + (size_t)((16 * B * nk + 255) / 256 * 256) + (size_t)((4 * B * nq + 255) / 256 * 256) + (size_t)(4 * B * nq);
