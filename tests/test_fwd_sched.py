@@ -98,3 +98,40 @@ def test_all_ones_at_480p_size_equals_unmasked(need_gpu):
     o3, l3 = vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale)
     torch.cuda.synchronize()
     assert_same_bits((o1, l1), (o3, l3))
+
+
+def test_graph_replays_reset_the_work_counters(need_gpu):
+    """The scheduled call captured in a HIP graph (its counters are zeroed by
+    a kernel, not a memset), replayed three times with eager work between the
+    replays: every replay equals the eager call, bit for bit."""
+    import spatiotemporal_attention_amd as vdx
+    B, S, H, D = 1, 6000, 2, 128
+    x = W.make_random(B, S, H, D, seed=500)
+    seg = W.random_segments(B, S, 501, "packed")
+    d, sq, sk = _dev(x, seg, seg.clone())
+    ref_o, ref_l = vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, scheduled=False)
+    ws = torch.empty(vdx.attn_fwd_workspace_size(B, S, H), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, out=out, lse=lse, workspace=ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("case sched graph capture", flush=True)
+    with torch.cuda.graph(g):
+        vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, out=out, lse=lse, workspace=ws,
+                     stream=torch.cuda.current_stream())
+    for i in range(3):
+        out.zero_()
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"case sched graph replay {i}", flush=True)
+        assert_same_bits((out, lse), (ref_o, ref_l))
+        # eager work between replays, reusing the same workspace
+        vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, workspace=ws)
+        torch.cuda.synchronize()
