@@ -162,9 +162,13 @@ __device__ __forceinline__ int wave_max(int x) {
 // nonzero IDs, INT32_MAX / INT32_MIN when there are none, and a flag for an
 // ID 0 or a row past S): 0 skip (no valid pair), 1 full (every pair valid:
 // one nonzero ID on both sides, no padding, no rows past S), 2 partial.
+// kOwnPadFree: the caller overwrites the results of its own padding rows (ID
+// 0 or past S), so their pairs need no mask and only the other side's
+// padding keeps a tile from being full.
+template <bool kOwnPadFree = false>
 __device__ __forceinline__ uint8_t tile_class(int omn, int omx, int ofl, int mn, int mx, int fl) {
     if (omn > omx || mn > mx || max(omn, mn) > min(omx, mx)) return 0;
-    if (!ofl && !fl && omn == omx && mn == mx && omn == mn) return 1;
+    if ((kOwnPadFree || !ofl) && !fl && omn == omx && mn == mx && omn == mn) return 1;
     return 2;
 }
 
@@ -231,7 +235,7 @@ __device__ __forceinline__ void block_summary(int mine, int* meta, int wave, int
 // number of active tiles.  A wave covers four tiles per step (16 lanes a
 // tile, 4 IDs a lane) and issues kU steps' loads before reducing any of
 // them, so the loads' latency overlaps instead of adding up tile by tile.
-template <int NW>
+template <int NW, bool kOwnPadFree = false>
 __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles, uint8_t* cls,
                               uint16_t* list, int* meta, int wave, int lane) {
     constexpr int kU = 4;
@@ -267,7 +271,7 @@ __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles
                 mx = max(mx, __shfl_xor(mx, o));
                 fl |= __shfl_xor(fl, o);
             }
-            if (sub == 0 && t < n_tiles) cls[t] = tile_class(omn, omx, ofl, mn, mx, fl);
+            if (sub == 0 && t < n_tiles) cls[t] = tile_class<kOwnPadFree>(omn, omx, ofl, mn, mx, fl);
         }
     }
     return compact_tiles<NW>(cls, n_tiles, list, meta, wave, lane);
@@ -277,7 +281,7 @@ __device__ int classify_tiles(int mine, const int32_t* other, int S, int n_tiles
 // IDs: sum[t] = {min nonzero ID, max nonzero ID, flag, 0} of tile t, as the
 // loop above reduces them.  One lane per tile, four tiles' loads in flight
 // per lane.
-template <int NW>
+template <int NW, bool kOwnPadFree = false>
 __device__ int classify_tiles_sum(int mine, const int4* sum, int n_tiles, uint8_t* cls, uint16_t* list,
                                   int* meta, int wave, int lane) {
     constexpr int kU = 4;
@@ -294,7 +298,7 @@ __device__ int classify_tiles_sum(int mine, const int4* sum, int n_tiles, uint8_
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int t = t0 + u * NW * 64 + tid;
-            if (t < n_tiles) cls[t] = tile_class(omn, omx, ofl, s[u].x, s[u].y, s[u].z);
+            if (t < n_tiles) cls[t] = tile_class<kOwnPadFree>(omn, omx, ofl, s[u].x, s[u].y, s[u].z);
         }
     }
     return compact_tiles<NW>(cls, n_tiles, list, meta, wave, lane);

@@ -580,10 +580,10 @@ __device__ __forceinline__ void attn_fwd_item(
         // that it is wave-uniform, so the loop bounds and ring-slot offsets
         // derived from it stay in scalar registers.
         if constexpr (SUM)
-            n_act = __builtin_amdgcn_readfirstlane(classify_tiles_sum<kWaves>(
+            n_act = __builtin_amdgcn_readfirstlane(classify_tiles_sum<kWaves, true>(
                 A.myseg, tsum, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
         else
-            n_act = __builtin_amdgcn_readfirstlane(classify_tiles<kWaves>(
+            n_act = __builtin_amdgcn_readfirstlane(classify_tiles<kWaves, true>(
                 A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
     }
 
@@ -641,7 +641,10 @@ __device__ __forceinline__ void attn_fwd_item(
     if (qi < S) {
         __bf16* orow = out + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D;
         float lse_v;
-        if (l_tot > 0.f) {
+        // A padding row (ID 0) may have run through full tiles unmasked (the
+        // classifier does not let a block's own padding make a tile partial):
+        // it is written as a row without valid keys.
+        if (l_tot > 0.f && A.myseg != 0) {
             const float inv = 1.0f / l_tot;
 #pragma unroll
             for (int db = 0; db < T::kDBlocks; ++db) {
@@ -784,7 +787,7 @@ __global__ __launch_bounds__(kBq) void attn_fwd_count_kernel(const int32_t* __re
     int c = 0;
     for (int t = tid; t < n_kvt; t += kBq) {
         const int4 x = ts[t];
-        c += tile_class(omn, omx, ofl, x.x, x.y, x.z) != 0 ? 1 : 0;
+        c += tile_class<true>(omn, omx, ofl, x.x, x.y, x.z) != 0 ? 1 : 0;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
