@@ -1,9 +1,11 @@
 """Throughput of the segment-masked flash-attention forward on one MI355X.
 
-One step = one vdx_attn_fwd call (vdx_attn_fwd_ws with segment IDs; the
-whole hot path: tile scheduling, segment classification, QK^T, masking,
-online softmax, PV, epilogue) over one batch of seeded synthetic input already
-resident in HBM.  Steps call the C ABI through the binding with their
+One step = one vdx_attn_fwd_ws call (the forward with a resident workspace;
+the whole hot path: tile scheduling, segment classification, QK^T, masking,
+online softmax, PV, epilogue, and the merge of the split last round's parts)
+over one batch of seeded synthetic input already resident in HBM; with
+--plain, one vdx_attn_fwd call (no workspace: unmasked launches never split,
+masked ones run one workgroup per query block).  Steps call the C ABI through the binding with their
 arguments prepared once (the tensor-level wrappers check them on a first,
 untimed call), and the warm-up runs until the clock has settled (at least 3
 steps and 1 s unless --warmup is given).  The default
@@ -40,7 +42,7 @@ CPU baseline's row rate with the extrapolated time of the whole workload on
 the oracle (labelled as an extrapolation).
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
-       [--rope] [--no-cpu-baseline] [--copy-calib]
+       [--rope] [--plain] [--no-cpu-baseline] [--copy-calib]
 """
 from __future__ import annotations
 
@@ -566,6 +568,8 @@ def main():
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--rope", action="store_true",
                     help="time vdx_rope3d_attn_fwd_ws (3D rotary embedding of q and k, then attention)")
+    ap.add_argument("--plain", action="store_true",
+                    help="time vdx_attn_fwd (no workspace) instead of vdx_attn_fwd_ws")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
@@ -587,6 +591,8 @@ def main():
         return
     if args.rope and (args.workload in W.NATTEN_WORKLOADS or args.pass_ != "fwd"):
         ap.error("--rope applies to the forward of the segment-masked workloads")
+    if args.plain and (args.rope or args.workload in W.NATTEN_WORKLOADS or args.pass_ != "fwd"):
+        ap.error("--plain applies to the attention forward without --rope")
     if args.workload in W.NATTEN_WORKLOADS:
         if args.pass_ != "fwd":
             ap.error("the neighbourhood-attention workloads have a forward pass only")
@@ -622,7 +628,7 @@ def main():
                       sp(d["seg_q"]), sp(d["seg_kv"]), desc, k_rot.data_ptr(), out.data_ptr(),
                       lse.data_ptr(), ws.data_ptr(), ws.numel(), w.B, w.S, w.H, w.D, w.scale,
                       stream.cuda_stream)
-    elif w.masked:
+    elif not args.plain:
         ws = torch.empty(vdx.attn_fwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device=dev)
         vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale, out=out, lse=lse,
                      stream=stream, workspace=ws)
@@ -630,9 +636,10 @@ def main():
                       sp(d["seg_q"]), sp(d["seg_kv"]), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
                       ws.numel(), w.B, w.S, w.H, w.D, w.scale, stream.cuda_stream)
     else:
-        vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale, out=out, lse=lse, stream=stream)
+        vdx.attn_fwd(d["q"], d["k"], d["v"], d["seg_q"], d["seg_kv"], scale=w.scale, out=out, lse=lse,
+                     stream=stream, scheduled=False)
         step = c_step(_native.attn_fwd_raw, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
-                      0, 0, out.data_ptr(), lse.data_ptr(), w.B, w.S, w.H, w.D, w.scale,
+                      sp(d["seg_q"]), sp(d["seg_kv"]), out.data_ptr(), lse.data_ptr(), w.B, w.S, w.H, w.D, w.scale,
                       stream.cuda_stream)
 
     ms_per_step, kernel_ms, n_warm = time_steps(step, stream, args.steps, args.warmup)
@@ -647,7 +654,8 @@ def main():
     flop = 4.0 * w.D * w.H * valid_pairs(w)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kernel_ms * 1e-3) / 1e12
-    config = {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "D": w.D,
+    entry = "vdx_rope3d_attn_fwd_ws" if args.rope else ("vdx_attn_fwd" if args.plain else "vdx_attn_fwd_ws")
+    config = {"workload": w.name, "entry": entry, "B": w.B, "S": w.S, "H": w.H, "D": w.D,
               "segments": "none" if w.seg_runs is None else w.seg_runs,
               "flop_per_step": flop, "peak_frac": round(value / PEAK_BF16_TFLOPS, 4)}
     if rope_cfg is not None:
@@ -675,6 +683,9 @@ def main():
     }
     if args.rope:
         line["roofline"]["scope"] = "vdx_rope3d_attn_fwd_ws call (key pre-pass + attention kernels)"
+    elif not args.plain:
+        line["roofline"]["scope"] = ("vdx_attn_fwd_ws call (" + ("tile summaries, block counts and order, "
+                                     if w.masked else "") + "the forward, the merge of a split last round)")
         line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")

@@ -30,10 +30,12 @@
  * allocates nothing, keeps no pointer after returning and holds no state
  * beyond a per-device, once-cached architecture check.  Calls are
  * asynchronous on `stream` (0 = null stream); buffers must stay alive until
- * the stream work completes.  Results are deterministic: the same inputs give
- * bit-identical outputs (fixed reduction order, no atomics in the arithmetic;
- * the *_ws entry points hand out work items with atomic counters in their
- * workspace, which decides only which workgroup computes an item).
+ * the stream work completes.  Results are deterministic: the same inputs on
+ * the same device give bit-identical outputs (fixed reduction order, no
+ * atomics in the arithmetic; the *_ws entry points hand out work items with
+ * atomic counters in their workspace, which decides only which workgroup
+ * computes an item, and split their last round by a rule fixed by the shape
+ * and the device's CU count).
  */
 #ifndef VDX_ATTN_H
 #define VDX_ATTN_H
@@ -46,7 +48,7 @@
 extern "C" {
 #endif
 
-#define VDX_ABI_VERSION 6
+#define VDX_ABI_VERSION 7
 
 /* Status codes.  Argument validation runs before any HIP call, in the order
  * below (NULL -> segment pair -> shape -> head dim -> scale -> alignment),
@@ -109,41 +111,53 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
                  int B, int S, int H, int D, float scale, hipStream_t stream);
 
 /*
- * vdx_attn_fwd_ws -- vdx_attn_fwd with a caller workspace, which the masked
- * (segment-ID) path uses to balance its uneven work; same operation and
- * results, bit for bit.
+ * vdx_attn_fwd_ws -- vdx_attn_fwd with a caller workspace, which the call
+ * uses to balance uneven work and to split the last round of a persistent
+ * launch; the same operation.
  *
  * The pages motivate it (vidax paper, arXiv:2609.18077, Appendix A, Table 4,
  * group 2): with SegmentIds a query block skips every key block of other
  * segments, so blocks of short and long clips packed into one sequence do
- * very different amounts of work.  With segment IDs this call enqueues four
- * kernels: a summary of every 64-key tile's IDs, the active-tile count of
- * every 256-query block, each batch's blocks ordered longest first, then a
+ * very different amounts of work.  With segment IDs this call enqueues a
+ * summary of every 64-key tile's IDs, the active-tile count of every
+ * 256-query block, each batch's blocks ordered longest first, then a
  * persistent forward whose workgroups pull (block, head) items in that order
  * from per-XCD work counters and classify tiles from the summaries.  The
  * counters change only which workgroup computes an item, never its result.
  *
+ * Split last round (with or without segment IDs): a persistent launch of G
+ * workgroups (the CU count rounded down to a multiple of 8; W = G / 8 per
+ * XCD) runs the n_x items of each XCD in rounds of W.  When n_x > W and
+ * R = n_x mod W leaves room for P = min(8, W / R) >= 2 parts, each of the
+ * last R items of the XCD is split along its active key tiles into P parts
+ * run side by side, and a last kernel merges each item's parts (their
+ * running maxima, sums and unnormalised outputs, added in part order).
+ * Every other query block gives vdx_attn_fwd's bits; a split block equals
+ * them up to rounding (each part rounds its probabilities to bf16 against
+ * its own running maximum), within the same accuracy bound.
+ *
  *   q ... scale, stream   exactly as for vdx_attn_fwd.
- *   workspace  with segment IDs: device scratch of at least
- *              vdx_attn_fwd_workspace_size(B, S, H) bytes, 16-byte aligned,
- *              owned by the caller; its contents on entry do not matter and
- *              are overwritten (two calls in flight at once need two
- *              workspaces).  Without segment IDs it is not used (it may be
- *              NULL) and the call is vdx_attn_fwd.
- * Validation: as vdx_attn_fwd, then (segment IDs only) the workspace ->
- * VDX_ERR_WORKSPACE; the first failure is reported before any HIP call.
- * Results are deterministic.
+ *   workspace  device scratch of at least vdx_attn_fwd_workspace_size(B, S,
+ *              H) bytes, 16-byte aligned, owned by the caller; its contents
+ *              on entry do not matter and are overwritten (two calls in
+ *              flight at once need two workspaces).  Required with segment
+ *              IDs.  Without them it may be NULL, and the call is then
+ *              vdx_attn_fwd (no split).
+ * Validation: as vdx_attn_fwd, then the workspace (with segment IDs, or
+ * whenever it is not NULL) -> VDX_ERR_WORKSPACE; the first failure is
+ * reported before any HIP call.  Results are deterministic.
  */
 int vdx_attn_fwd_ws(const void* q, const void* k, const void* v,
                     const int32_t* seg_q, const int32_t* seg_kv,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     int B, int S, int H, int D, float scale, hipStream_t stream);
 
-/* Bytes of workspace vdx_attn_fwd_ws needs with segment IDs for (B, S, H):
- * 256 (work counters) + R(16 * B * ceil(S / 64)) (tile summaries) +
- * R(4 * B * ceil(S / 256)) (block counts) + 4 * B * ceil(S / 256) (block
- * orders), R() rounding up to a multiple of 256.  H does not enter.  0 if
- * B, S or H < 1. */
+/* Bytes of workspace vdx_attn_fwd_ws needs for (B, S, H): 256 (work
+ * counters) + R(16 * B * ceil(S / 64)) (tile summaries) + R(4 * B *
+ * ceil(S / 256)) (block counts) + R(4 * B * ceil(S / 256)) (block orders) +
+ * 256 * 256 * 130 * 4 (part records of the split last round: per part the
+ * fp32 unnormalised output, maximum and sum of 256 rows at D <= 128), R()
+ * rounding up to a multiple of 256.  H does not enter.  0 if B, S or H < 1. */
 size_t vdx_attn_fwd_workspace_size(int B, int S, int H);
 
 /*
@@ -340,13 +354,14 @@ int vdx_rope3d_attn_fwd(const void* q, const void* k, const void* v,
                         int B, int S, int H, int D, float scale, hipStream_t stream);
 
 /*
- * vdx_rope3d_attn_fwd_ws -- vdx_rope3d_attn_fwd with the masked path of
- * vdx_attn_fwd_ws: with segment IDs the attention runs on the persistent,
- * longest-first schedule of vdx_attn_fwd_ws (same workspace layout and size,
- * vdx_attn_fwd_workspace_size(B, S, H)); without them the workspace is not
- * used (it may be NULL).  Same results as vdx_rope3d_attn_fwd, bit for bit.
- * Validation: as vdx_rope3d_attn_fwd, then (segment IDs only) the workspace
- * -> VDX_ERR_WORKSPACE.
+ * vdx_rope3d_attn_fwd_ws -- vdx_rope3d_attn_fwd on the schedule of
+ * vdx_attn_fwd_ws (same workspace layout and size,
+ * vdx_attn_fwd_workspace_size(B, S, H)): with segment IDs the persistent,
+ * longest-first launch, and with or without them the split last round.
+ * Without segment IDs the workspace may be NULL (then no split).  Results
+ * relate to vdx_rope3d_attn_fwd's as vdx_attn_fwd_ws's to vdx_attn_fwd's.
+ * Validation: as vdx_rope3d_attn_fwd, then the workspace (with segment IDs,
+ * or whenever it is not NULL) -> VDX_ERR_WORKSPACE.
  */
 int vdx_rope3d_attn_fwd_ws(const void* q, const void* k, const void* v,
                            const int32_t* seg_q, const int32_t* seg_kv,

@@ -99,12 +99,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     q, k, v: bf16 [B, S, H, D] contiguous on one GPU.  seg_q, seg_kv: int32
     [B, S] or both None (unmasked).  Returns (out bf16 [B,S,H,D], lse fp32 [B,H,S]).
 
-    With segment IDs the call goes to vdx_attn_fwd_ws (work counters and a
-    longest-first block order in a workspace; ``workspace``, a uint8 CUDA
-    tensor of at least attn_fwd_workspace_size(B, S, H) bytes, or one
-    allocated here on the launch stream); ``scheduled=False`` calls
-    vdx_attn_fwd, one workgroup per block in index order.  Both give the
-    same bits.
+    With segment IDs the call goes to vdx_attn_fwd_ws (work counters, a
+    longest-first block order and the split last round's partial results in
+    a workspace; ``workspace``, a uint8 CUDA tensor of at least
+    attn_fwd_workspace_size(B, S, H) bytes, or one allocated here on the
+    launch stream); ``scheduled=False`` calls vdx_attn_fwd, one workgroup per
+    block in index order.  Without segment IDs the call goes to
+    vdx_attn_fwd_ws only when a ``workspace`` is given (and ``scheduled``).
+    The two entry points give the same bits except on the query blocks whose
+    keys the split last round divides (equal up to rounding).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, S, H, D]")
@@ -128,7 +131,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if seg_q is None else seg_q.data_ptr(),
             0 if seg_kv is None else seg_kv.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
-        if seg_q is not None and scheduled:
+        if scheduled and (seg_q is not None or workspace is not None):
             workspace = _workspace(workspace, B, S, H, q.device, stream)
             rc = _native.attn_fwd_ws_raw(*ptrs, workspace.data_ptr(), workspace.numel(), B, S, H, D, scale,
                                          stream.cuda_stream)
@@ -341,7 +344,7 @@ def rope3d_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos: torc
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if seg_q is None else seg_q.data_ptr(),
             0 if seg_kv is None else seg_kv.data_ptr(), desc, k_rot.data_ptr(), out.data_ptr(), lse.data_ptr())
     with torch.cuda.device(q.device):
-        if seg_q is not None and scheduled:
+        if scheduled and (seg_q is not None or workspace is not None):
             workspace = _workspace(workspace, B, S, H, q.device, stream)
             rc = _native.rope3d_attn_fwd_ws_raw(*ptrs, workspace.data_ptr(), workspace.numel(), B, S, H, D, scale,
                                                 stream.cuda_stream)

@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <tuple>
 
 #include "attn_common.h"
 #include "attn_fwd_launch.h"
@@ -59,7 +60,7 @@ namespace {
 
 constexpr int kMaxKvTiles = 30720;  // capacity of the on-chip active-tile list
 
-template <int D, bool SEG>
+template <int D, bool SEG, bool PART>
 struct Attn {
     using T = Tile<D>;
     char* smem;
@@ -69,6 +70,11 @@ struct Attn {
     const uint16_t* list;
     int64_t tok_stride;
     int S, n_kvt, wave, lane, lr, g;
+    // Unmasked: a part of a split item sees tiles t0 .. t0 + n_kvt - 1 of
+    // the head (n_kvt then counts that range), and holds the ragged last
+    // tile only if its range ends the sequence (last_view).
+    int t0;
+    bool last_view;
     float c_log2;
     int myseg;
     // Active tile a - 1 of the next plan() call (group 0 plans tiles 0, 1,
@@ -98,8 +104,13 @@ struct Attn {
             partial = (e & 0x8000) != 0;
             return e & 0x7fff;
         } else {
-            partial = (n == n_kvt - 1) && (S % kBk != 0);
-            return n;
+            if constexpr (PART) {
+                partial = (n == n_kvt - 1) && (S % kBk != 0) && last_view;
+                return n + t0;
+            } else {
+                partial = (n == n_kvt - 1) && (S % kBk != 0);
+                return n;
+            }
         }
     }
     __device__ __forceinline__ bool partial(int n) const {
@@ -372,9 +383,9 @@ struct Attn {
 // the copy of its previous MFMA phase, so a copy has two phases to land.  The
 // first and last iterations are peeled so that the steady-state body has a
 // single MFMA phase shape.
-template <int G, int D, bool SEG>
-__device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
-    typename Attn<D, SEG>::Copy cp;
+template <int G, class AT>
+__device__ __forceinline__ void main_loop(AT& A, int n_act) {
+    typename AT::Copy cp;
     auto valu_phase = [&](int n) {
         if (A.partial(n)) A.mask(n);
         A.softmax();
@@ -388,20 +399,20 @@ __device__ __forceinline__ void main_loop(Attn<D, SEG>& A, int n_act) {
     A.template prefetch<false, true>(0, 0);
     if (G == 1) barrier();  // group 1 idles in global phase 0
     A.template mfma_phase<false, true, true>(0, 0, cp);
-    wait_copies<Attn<D, SEG>::T::kLoadsPerWave>(cp.cnt);
+    wait_copies<AT::T::kLoadsPerWave>(cp.cnt);
     barrier();
     valu_phase(0);
     for (int n = 1; n < n_act; ++n) {
         const int c = cp.cnt;
         A.template mfma_phase<true, true, true>(n - 1, n, cp);
-        wait_copies<Attn<D, SEG>::T::kLoadsPerWave>(c);
+        wait_copies<AT::T::kLoadsPerWave>(c);
         barrier();
         valu_phase(n);
     }
     {
         const int c = cp.cnt;
         A.template mfma_phase<true, false, false>(n_act - 1, 0, cp);
-        wait_copies<Attn<D, SEG>::T::kLoadsPerWave>(c);
+        wait_copies<AT::T::kLoadsPerWave>(c);
         barrier();
     }
     if (G == 0) barrier();  // group 0 idles in the last global phase
@@ -491,15 +502,62 @@ __device__ __forceinline__ ItemPos decode_item(int w, int n_wg, int n_qblk, int 
     return ItemPos{bh / H, bh % H, lid % n_qblk};
 }
 
+// ---- split tail of a persistent launch ----------------------------------------------
+// A persistent grid of G workgroups (W = G / 8 per XCD) runs the n_x items of
+// an XCD in rounds of W.  When n_x is not a multiple of W, the last round
+// holds R = n_x mod W items and leaves W - R workgroups idle for a whole
+// item's time.  With a workspace for partial results, each of those R items
+// is instead split along its active key tiles into P = min(8, W / R) parts,
+// which the XCD's workgroups run side by side; a combine kernel then merges
+// the parts of each item.  Local index j of an XCD (its j-th item, or unit
+// once split): j < n_x - R is the whole item j; otherwise u = j - (n_x - R)
+// is part u / R of item n_x - R + u % R, with its partial results in record
+// x * W + u.  An XCD runs n_x - R + R * P units.
+constexpr int kTailMaxParts = 8;
+constexpr int kTailRecords = 256;  // part records a workspace holds (one per workgroup of a 256-CU grid)
+struct TailPlan {
+    int n_x;    // items of the XCD
+    int R, P;   // split items and parts per item (R = 0: no split)
+    __host__ __device__ int units() const { return n_x - R + R * P; }
+};
+__host__ __device__ inline TailPlan tail_plan(int x, int n_items, int W, bool on) {
+    TailPlan t{n_items / kXcds + (x < n_items % kXcds ? 1 : 0), 0, 1};
+    if (on && t.n_x > W) {
+        const int R = t.n_x % W;
+        const int P = R > 0 ? min(kTailMaxParts, W / R) : 1;
+        if (P >= 2) {
+            t.R = R;
+            t.P = P;
+        }
+    }
+    return t;
+}
+// Floats of one part record: the unnormalised O^T of the block's kBq rows as
+// [D / 8][kBq][8] (row-contiguous 8-float chunks of d), then the reference
+// maximum m (log2 units of the scaled score) and the key sum l of every row
+// (l = 0: no valid key in the part).  A multiple of 64 floats.
+template <int D>
+constexpr size_t tail_record_floats() { return (size_t)kBq * D + 2 * kBq; }
+static_assert(tail_record_floats<128>() % 64 == 0 && tail_record_floats<64>() % 64 == 0, "records stay 256-byte aligned");
+
+// What one workgroup of a persistent launch runs: query block it, whole
+// (rec == nullptr) or part p of P of its active key tiles with its partial
+// results in record rec.
+struct TailPart {
+    float* rec;
+    int p, P;
+};
+
 // One query block (256 queries of one (b, h)).  With segment IDs the key
 // tiles are classified from the IDs themselves (SUM false) or from the
 // per-tile summaries tsum of the batch (SUM true, see attn_fwd_tilesum_kernel).
-template <int D, bool SEG, bool ROPE, bool SUM>
+template <int D, bool SEG, bool ROPE, bool SUM, bool PART>
 __device__ __forceinline__ void attn_fwd_item(
     char* smem, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, const int32_t* __restrict__ seg_q,
     const int32_t* __restrict__ seg_kv, __bf16* __restrict__ out, float* __restrict__ lse, int S,
-    int H, float c_log2, int n_kvt, ItemPos it, const int4* __restrict__ tsum, const Rope3DDev& rope) {
+    int H, float c_log2, int n_kvt, ItemPos it, const int4* __restrict__ tsum, const Rope3DDev& rope,
+    TailPart part = TailPart{nullptr, 0, 1}) {
     using T = Tile<D>;
     const int qblk = it.qblk, h = it.h, b = it.b;
 
@@ -509,7 +567,7 @@ __device__ __forceinline__ void attn_fwd_item(
     const int grp = wave >> 2;  // ping-pong group; waves w and w+4 share a SIMD
     const int qi = qblk * kBq + wave * 32 + lr;
 
-    Attn<D, SEG> A;
+    Attn<D, SEG, PART> A;
     A.smem = smem;
     A.tok_stride = (int64_t)H * D;
     A.kp = k + (int64_t)b * S * A.tok_stride + (int64_t)h * D;
@@ -517,6 +575,8 @@ __device__ __forceinline__ void attn_fwd_item(
     A.segkv = SEG ? seg_kv + (int64_t)b * S : nullptr;
     A.S = S;
     A.n_kvt = n_kvt;
+    A.t0 = 0;
+    A.last_view = true;
     A.wave = wave;
     A.w4 = wave & 3;
     A.lane = lane;
@@ -586,6 +646,26 @@ __device__ __forceinline__ void attn_fwd_item(
             n_act = __builtin_amdgcn_readfirstlane(classify_tiles<kWaves, true>(
                 A.myseg, A.segkv, S, n_kvt, reinterpret_cast<uint8_t*>(smem), list, meta, wave, lane));
     }
+    if constexpr (PART) {
+        if (part.rec != nullptr) {
+            // Part p of P: active tiles [n_act p / P, n_act (p + 1) / P).
+            const int a0 = (int)((int64_t)n_act * part.p / part.P);
+            const int a1 = (int)((int64_t)n_act * (part.p + 1) / part.P);
+            n_act = a1 - a0;
+            if (SEG) {
+                A.list = list + a0;
+            } else {
+                A.t0 = a0;
+                A.n_kvt = n_act;
+                A.last_view = a1 == n_kvt;
+            }
+        }
+        // The record address waits in the LDS (meta[28..29], past the
+        // classifier's scratch) until the epilogue, so that it holds no
+        // registers through the main loop; the barrier after the prologue
+        // copies makes it visible.
+        if (tid == 0) *reinterpret_cast<float**>(meta + 28) = part.rec;
+    }
 
     // ---- running softmax state and the O^T accumulators -----------------------
 #pragma unroll
@@ -602,7 +682,7 @@ __device__ __forceinline__ void attn_fwd_item(
         A.prev_part = false;
     }
     {
-        typename Attn<D, SEG>::Copy c;
+        typename Attn<D, SEG, PART>::Copy c;
         if (grp == 0) {
             for (int a = 0; a < 2; ++a) {
                 A.template plan<0>(c, a, n_act);  // K tile a, segment IDs of tile a-1
@@ -638,7 +718,30 @@ __device__ __forceinline__ void attn_fwd_item(
 
     // ---- epilogue: normalise, write out (bf16) and lse (fp32) ----------------
     const float l_tot = pair_sum(A.l_run);
-    if (qi < S) {
+    float* ro = nullptr;
+    if constexpr (PART) {
+        ro = *reinterpret_cast<float* const volatile*>(meta + 28);
+        uint64_t rv = reinterpret_cast<uint64_t>(ro);
+        rv = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(rv >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((int)rv);
+        ro = reinterpret_cast<float*>(rv);
+    }
+    if (PART && ro != nullptr) {
+        // A part writes its unnormalised state; attn_fwd_combine_kernel
+        // finishes the row.  Padding rows (ID 0) report no valid key.
+        const int row = wave * 32 + lr;
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<float4*>(ro + ((size_t)(db * 4 + r4) * kBq + row) * 8 + 4 * g) =
+                    float4{A.oacc[db][4 * r4], A.oacc[db][4 * r4 + 1], A.oacc[db][4 * r4 + 2],
+                           A.oacc[db][4 * r4 + 3]};
+        if (g == 0) {
+            ro[(size_t)kBq * D + row] = A.m_run;
+            ro[(size_t)kBq * D + kBq + row] = A.myseg != 0 ? l_tot : 0.f;
+        }
+    } else if (qi < S) {
         __bf16* orow = out + ((int64_t)b * S + qi) * A.tok_stride + (int64_t)h * D;
         float lse_v;
         // A padding row (ID 0) may have run through full tiles unmasked (the
@@ -675,21 +778,127 @@ __device__ __forceinline__ void attn_fwd_item(
 // then work on consecutive query blocks of one head, streaming the same K/V
 // tiles at the same time, which keeps them in that XCD's L2; with one
 // workgroup per item, CUs that pick up new items at different times drift
-// apart and each re-fetches the tiles.  Every workgroup's item count is fixed
-// by G and n_wg, so all waves exit.
-template <int D, bool SEG, bool ROPE>
+// apart and each re-fetches the tiles.  With part records (recs, a persistent
+// grid only) the last round's items are split (tail_plan): workgroup p then
+// runs local units p / 8, p / 8 + G / 8, ... of its XCD.  Every workgroup's
+// unit count is fixed by G and n_wg, so all waves exit.
+template <int D, bool SEG, bool ROPE, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
     __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
-    int n_kvt, int n_wg, Rope3DDev rope) {
+    int n_kvt, int n_wg, Rope3DDev rope, float* __restrict__ recs) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
-        attn_fwd_item<D, SEG, ROPE, false>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt,
-                                           decode_item(w, n_wg, n_qblk, H), nullptr, rope);
-        // Every wave is done with the LDS of this item before the next one's
-        // copies land there.
-        __syncthreads();
+    if constexpr (!SPLIT) {
+        for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
+            attn_fwd_item<D, SEG, ROPE, false, false>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2,
+                                                      n_kvt, decode_item(w, n_wg, n_qblk, H), nullptr, rope);
+            // Every wave is done with the LDS of this item before the next
+            // one's copies land there.
+            __syncthreads();
+        }
+    } else {
+        // The schedule is recomputed every iteration (the empty asm keeps the
+        // compiler from hoisting it), so that only the iteration count is
+        // carried through the item, as in the loop above.
+        for (int s = 0;; ++s) {
+            int x = blockIdx.x % kXcds, W = gridDim.x / kXcds;
+            asm volatile("" : "+s"(x), "+s"(W));
+            const TailPlan tp = tail_plan(x, n_wg, W, true);
+            const int n_whole = tp.n_x - tp.R;
+            int j = (int)(blockIdx.x / kXcds) + s * W;
+            if (j >= tp.units()) break;
+            TailPart part{nullptr, 0, 1};
+            if (j >= n_whole) {
+                const int u = j - n_whole;
+                part = TailPart{recs + (size_t)(x * W + u) * tail_record_floats<D>(), u / tp.R, tp.P};
+                j = n_whole + u % tp.R;
+            }
+            attn_fwd_item<D, SEG, ROPE, false, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt,
+                                                     decode_item(x + kXcds * j, n_wg, n_qblk, H), nullptr, rope,
+                                                     part);
+            __syncthreads();
+        }
+    }
+}
+
+// Merges the P parts of every split item of XCD blockIdx.y (item
+// blockIdx.x of its R): per row, M = the largest reference maximum among the
+// parts with valid keys, L = sum_p l_p 2^(m_p - M), O = sum_p O_p 2^(m_p - M);
+// out = O / L (bf16) and lse = (M + log2 L) ln 2, or +0 / -inf when L = 0.
+// One thread per row; parts are added in index order, so the result is
+// deterministic.  SCHED: the items are those of attn_fwd_sched_kernel
+// (longest-first block order ord), else those of attn_fwd_kernel.
+template <int D, bool SCHED>
+__global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __restrict__ recs,
+                                                               const int* __restrict__ ord,
+                                                               __bf16* __restrict__ out, float* __restrict__ lse,
+                                                               int S, int H, int n_qblk, int n_items, int W) {
+    const int x = blockIdx.y, r = blockIdx.x;
+    const TailPlan tp = tail_plan(x, n_items, W, true);
+    if (r >= tp.R) return;
+    const int j = tp.n_x - tp.R + r;
+    ItemPos it;
+    if (SCHED) {
+        const int e = x + kXcds * j;
+        const int h = e % H, rb = e / H;
+        const int rr = rb % n_qblk, b = rb / n_qblk;
+        const int o = ord[(int64_t)b * n_qblk + rr];
+        it = ItemPos{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};
+    } else {
+        it = decode_item(x + kXcds * j, n_items, n_qblk, H);
+    }
+    const int row = threadIdx.x;
+    const int qi = it.qblk * kBq + row;
+    if (qi >= S) return;
+    constexpr size_t RF = tail_record_floats<D>();
+    const float* rec0 = recs + (size_t)(x * W + r) * RF;
+    const size_t pstride = (size_t)tp.R * RF;  // part p of this item: record x W + r + p R
+    float M = -INFINITY;
+    for (int p = 0; p < tp.P; ++p) {
+        const float* rp = rec0 + p * pstride;
+        if (rp[(size_t)kBq * D + kBq + row] > 0.f) M = fmaxf(M, rp[(size_t)kBq * D + row]);
+    }
+    float wgt[kTailMaxParts];
+    float L = 0.f;
+    for (int p = 0; p < kTailMaxParts; ++p) {
+        wgt[p] = 0.f;
+        if (p < tp.P) {
+            const float* rp = rec0 + p * pstride;
+            const float l = rp[(size_t)kBq * D + kBq + row];
+            if (l > 0.f) {
+                wgt[p] = __builtin_amdgcn_exp2f(rp[(size_t)kBq * D + row] - M);
+                L += wgt[p] * l;
+            }
+        }
+    }
+    __bf16* orow = out + ((int64_t)it.b * S + qi) * H * D + (int64_t)it.h * D;
+    if (L > 0.f) {
+        const float inv = 1.0f / L;
+        for (int c = 0; c < D / 8; ++c) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < tp.P; ++p) {
+                if (wgt[p] == 0.f) continue;
+                const float4* src = reinterpret_cast<const float4*>(rec0 + p * pstride + ((size_t)c * kBq + row) * 8);
+                const float4 lo = src[0], hi = src[1];
+                acc[0] += wgt[p] * lo.x;
+                acc[1] += wgt[p] * lo.y;
+                acc[2] += wgt[p] * lo.z;
+                acc[3] += wgt[p] * lo.w;
+                acc[4] += wgt[p] * hi.x;
+                acc[5] += wgt[p] * hi.y;
+                acc[6] += wgt[p] * hi.z;
+                acc[7] += wgt[p] * hi.w;
+            }
+            __bf16 o8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(acc[e] * inv);
+            *reinterpret_cast<uint4*>(orow + 8 * c) = *reinterpret_cast<const uint4*>(o8);
+        }
+        lse[((int64_t)it.b * H + it.h) * S + qi] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+    } else {
+        for (int c = 0; c < D / 8; ++c) *reinterpret_cast<uint4*>(orow + 8 * c) = uint4{0u, 0u, 0u, 0u};
+        lse[((int64_t)it.b * H + it.h) * S + qi] = -INFINITY;
     }
 }
 
@@ -714,13 +923,15 @@ static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(
 // longest-first order, and classifies key tiles from per-tile summaries
 // instead of every workgroup re-reading all of the batch's key IDs.
 // Workspace: eight counters (256 bytes), then int4 tile summaries
-// [B][n_kvt], active-tile counts [B][n_qblk] and the longest-first block
-// orders [B][n_qblk].
+// [B][n_kvt], active-tile counts [B][n_qblk], the longest-first block orders
+// [B][n_qblk] and kTailRecords part records of the split tail (sized for
+// D = 128).  An unmasked call uses only the part records.
 struct FwdWs {
     uint32_t* ctr;
     int4* tsum;
     int* cnt;
     int* ord;
+    float* recs;  // kTailRecords part records of the split tail
 };
 __host__ __device__ inline size_t fwd_ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 FwdWs fwd_ws_layout(void* ws, int64_t B, int64_t n_kvt, int64_t n_qblk) {
@@ -733,6 +944,8 @@ FwdWs fwd_ws_layout(void* ws, int64_t B, int64_t n_kvt, int64_t n_qblk) {
     w.cnt = reinterpret_cast<int*>(p);
     p += fwd_ws_align((size_t)(B * n_qblk) * sizeof(int));
     w.ord = reinterpret_cast<int*>(p);
+    p += fwd_ws_align((size_t)(B * n_qblk) * sizeof(int));
+    w.recs = reinterpret_cast<float*>(p);
     return w;
 }
 
@@ -829,7 +1042,7 @@ __global__ __launch_bounds__(kFwdRankThreads) void attn_fwd_rank_kernel(const in
 // its residue), and a workgroup exits at the first slot past the list, so
 // every wave exits.  Requires a grid that is a multiple of 8.  ROPE: the
 // queries are rotated in the item prologue, as in attn_fwd_kernel.
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
@@ -837,20 +1050,31 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
     int n_kvt, int n_items, FwdWs ws, Rope3DDev rope) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     int* slot = reinterpret_cast<int*>(smem + fwd_lds<D, true>(n_kvt) - sizeof(int));
-    const int xcd = blockIdx.x % kXcds;
     for (;;) {
+        // Recomputed every iteration (see attn_fwd_kernel), so that nothing
+        // but the kernel arguments is carried through an item.
+        int xcd = blockIdx.x % kXcds, W = gridDim.x / kXcds;
+        asm volatile("" : "+s"(xcd), "+s"(W));
+        const TailPlan tp = tail_plan(xcd, n_items, W, SPLIT);
+        const int n_whole = tp.n_x - tp.R;
         if (threadIdx.x == 0) *slot = (int)atomicAdd(ws.ctr + xcd, 1u);
         __syncthreads();
-        const int64_t e = xcd + (int64_t)kXcds * __builtin_amdgcn_readfirstlane(*slot);
+        int j = __builtin_amdgcn_readfirstlane(*slot);
         __syncthreads();  // every wave has the slot before it is reused
-        if (e >= n_items) break;
-        const int ie = (int)e;
+        if (j >= tp.units()) break;
+        TailPart part{nullptr, 0, 1};
+        if (SPLIT && j >= n_whole) {
+            const int u = j - n_whole;
+            part = TailPart{ws.recs + (size_t)(xcd * W + u) * tail_record_floats<D>(), u / tp.R, tp.P};
+            j = n_whole + u % tp.R;
+        }
+        const int ie = xcd + kXcds * j;
         const int h = ie % H, rb = ie / H;
         const int r = rb % n_qblk, b = rb / n_qblk;
         const int o = ws.ord[(int64_t)b * n_qblk + r];
         const ItemPos it{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};  // a permutation; the test keeps it in range
-        attn_fwd_item<D, true, ROPE, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
-                                           ws.tsum + (int64_t)b * n_kvt, rope);
+        attn_fwd_item<D, true, ROPE, true, SPLIT>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
+                                                  ws.tsum + (int64_t)b * n_kvt, rope, part);
         __syncthreads();
     }
 }
@@ -876,8 +1100,28 @@ int64_t persistent_workgroups() {
 }
 
 
+// Largest split-item count R over the XCDs of a persistent grid (0: no item
+// is split, and no combine launch is needed).
+int tail_max_r(int n_items, int grid) {
+    int m = 0;
+    for (int x = 0; x < kXcds; ++x) m = std::max(m, tail_plan(x, n_items, grid / kXcds, true).R);
+    return m;
+}
+
+template <int D, bool SCHED>
+hipError_t launch_combine(const AttnArgs& a, const float* recs, const int* ord, int n_qblk, int n_items, int grid,
+                          hipStream_t stream) {
+    const int max_r = tail_max_r(n_items, grid);
+    if (max_r == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, kXcds), dim3(kBq), 0, stream,
+                       recs, ord, reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, n_qblk, n_items,
+                       grid / kXcds);
+    return hipGetLastError();
+}
+
+// recs: part records for a split tail (unmasked calls only), or nullptr.
 template <int D, bool SEG, bool ROPE>
-hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream) {
+hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream, float* recs = nullptr) {
     const int n_qblk = (a.S + kBq - 1) / kBq;
     const int n_kvt = (a.S + kBk - 1) / kBk;
     const int64_t n_wg64 = (int64_t)a.B * a.H * n_qblk;
@@ -887,13 +1131,30 @@ hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream
     // Unmasked, every item has the same work and the persistent grid keeps
     // the CUs of an XCD in step; with segment IDs items differ (up to 8x on
     // packed clips) and one workgroup per item lets the dispatcher balance them.
-    const int grid = SEG ? n_wg : (int)std::min<int64_t>(n_wg64, persistent_workgroups());
-    hipLaunchKernelGGL((attn_fwd_kernel<D, SEG, ROPE>), dim3(grid), dim3(kThreads), lds, stream,
-                       reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
-                       reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
-                       reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, c_log2, n_qblk, n_kvt,
-                       n_wg, rope);
-    return hipGetLastError();
+    const int64_t pg = persistent_workgroups();
+    const int grid = SEG ? n_wg : (int)std::min<int64_t>(n_wg64, pg);
+    // A split tail needs the persistent grid (a multiple of 8) with more than
+    // one round, a record per workgroup, and a ragged last round.
+    if (SEG || n_wg64 <= pg || pg > kTailRecords || tail_max_r(n_wg, grid) == 0) recs = nullptr;
+    const auto args = std::make_tuple(reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
+                                      reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
+                                      reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, c_log2, n_qblk, n_kvt,
+                                      n_wg, rope, recs);
+    if (recs == nullptr) {
+        std::apply([&](auto... x) {
+            hipLaunchKernelGGL((attn_fwd_kernel<D, SEG, ROPE, false>), dim3(grid), dim3(kThreads), lds, stream, x...);
+        }, args);
+        return hipGetLastError();
+    }
+    if constexpr (!SEG) {
+        std::apply([&](auto... x) {
+            hipLaunchKernelGGL((attn_fwd_kernel<D, false, ROPE, true>), dim3(grid), dim3(kThreads), lds, stream, x...);
+        }, args);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_combine<D, false>(a, recs, nullptr, n_qblk, n_wg, grid, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -919,12 +1180,26 @@ hipError_t launch_sched_t(const AttnArgs& a, const Rope3DDev& rope, void* worksp
     if (e != hipSuccess) return e;
     // A multiple of 8 (every XCD counter has workgroups), at most one per CU.
     const int64_t grid = std::min<int64_t>(persistent_workgroups(), (n_items64 + kXcds - 1) / kXcds * kXcds);
-    hipLaunchKernelGGL((attn_fwd_sched_kernel<D, ROPE>), dim3((unsigned)grid), dim3(kThreads),
-                       (fwd_lds<D, true>(n_kvt)), stream, reinterpret_cast<const __bf16*>(a.q),
-                       reinterpret_cast<const __bf16*>(a.k), reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
-                       reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, a.scale * kLog2e, n_qblk, n_kvt,
-                       (int)n_items64, ws, rope);
-    return hipGetLastError();
+    const bool split = grid <= kTailRecords && tail_max_r((int)n_items64, (int)grid) > 0;
+    const auto args = std::make_tuple(reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
+                                      reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
+                                      reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, a.scale * kLog2e, n_qblk,
+                                      n_kvt, (int)n_items64, ws, rope);
+    const size_t lds = fwd_lds<D, true>(n_kvt);
+    if (!split) {
+        std::apply([&](auto... x) {
+            hipLaunchKernelGGL((attn_fwd_sched_kernel<D, ROPE, false>), dim3((unsigned)grid), dim3(kThreads), lds,
+                               stream, x...);
+        }, args);
+        return hipGetLastError();
+    }
+    std::apply([&](auto... x) {
+        hipLaunchKernelGGL((attn_fwd_sched_kernel<D, ROPE, true>), dim3((unsigned)grid), dim3(kThreads), lds,
+                           stream, x...);
+    }, args);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_combine<D, true>(a, ws.recs, ws.ord, n_qblk, (int)n_items64, (int)grid, stream);
 }
 
 int64_t max_masked_seq() { return (int64_t)kMaxKvTiles * kBk; }
@@ -932,19 +1207,29 @@ int64_t max_masked_seq() { return (int64_t)kMaxKvTiles * kBk; }
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t S) {
     const int64_t n_qblk = (S + kBq - 1) / kBq, n_kvt = (S + kBk - 1) / kBk;
     return 256 + fwd_ws_align((size_t)(B * n_kvt) * sizeof(int4)) + fwd_ws_align((size_t)(B * n_qblk) * sizeof(int)) +
-           (size_t)(B * n_qblk) * sizeof(int);
+           fwd_ws_align((size_t)(B * n_qblk) * sizeof(int)) + (size_t)kTailRecords * tail_record_floats<128>() * 4;
 }
 
 hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t stream) {
-    if (a.seg_q == nullptr) return launch_attn_fwd(a, stream);
     const Rope3DDev none{};
+    if (a.seg_q == nullptr) {
+        if (workspace == nullptr) return launch_attn_fwd(a, stream);
+        const FwdWs ws = fwd_ws_layout(workspace, a.B, (a.S + kBk - 1) / kBk, (a.S + kBq - 1) / kBq);
+        return a.D == 128 ? launch_t<128, false, false>(a, none, stream, ws.recs)
+                          : launch_t<64, false, false>(a, none, stream, ws.recs);
+    }
     return a.D == 128 ? launch_sched_t<128, false>(a, none, workspace, stream)
                       : launch_sched_t<64, false>(a, none, workspace, stream);
 }
 
 hipError_t launch_rope3d_attn_fwd_sched(const AttnArgs& a, const Rope3DDev& rope, void* workspace,
                                         hipStream_t stream) {
-    if (a.seg_q == nullptr) return launch_rope3d_attn_fwd(a, rope, stream);
+    if (a.seg_q == nullptr) {
+        if (workspace == nullptr) return launch_rope3d_attn_fwd(a, rope, stream);
+        const FwdWs ws = fwd_ws_layout(workspace, a.B, (a.S + kBk - 1) / kBk, (a.S + kBq - 1) / kBq);
+        return a.D == 128 ? launch_t<128, false, true>(a, rope, stream, ws.recs)
+                          : launch_t<64, false, true>(a, rope, stream, ws.recs);
+    }
     return a.D == 128 ? launch_sched_t<128, true>(a, rope, workspace, stream)
                       : launch_sched_t<64, true>(a, rope, workspace, stream);
 }

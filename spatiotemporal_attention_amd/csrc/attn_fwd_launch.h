@@ -33,10 +33,11 @@ struct AttnArgs {
 // Enqueue the forward kernel; arguments are already validated.
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 
-// The masked forward on a persistent grid with per-XCD work counters and
-// longest-first block order, with its scratch in a caller workspace of
-// attn_fwd_workspace_bytes(B, S) bytes (16-byte aligned); unmasked calls
-// ignore it and run launch_attn_fwd.
+// The forward with a caller workspace of attn_fwd_workspace_bytes(B, S)
+// bytes (16-byte aligned): masked calls run on a persistent grid with per-XCD
+// work counters and longest-first block order; masked and unmasked calls
+// split a ragged last round along the keys and merge the parts.  An unmasked
+// call with a NULL workspace is launch_attn_fwd.
 hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t stream);
 
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t S);
@@ -45,8 +46,8 @@ size_t attn_fwd_workspace_bytes(int64_t B, int64_t S);
 // they are loaded) and keys (a.k must already hold the rotated keys).
 hipError_t launch_rope3d_attn_fwd(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream);
 
-// launch_rope3d_attn_fwd with the masked path of launch_attn_fwd_sched (same
-// workspace); unmasked calls ignore the workspace.
+// launch_rope3d_attn_fwd on the schedule of launch_attn_fwd_sched (same
+// workspace; an unmasked call with a NULL workspace is launch_rope3d_attn_fwd).
 hipError_t launch_rope3d_attn_fwd_sched(const AttnArgs& a, const Rope3DDev& rope, void* workspace,
                                         hipStream_t stream);
 

@@ -208,7 +208,8 @@ __attribute__((visibility("default"))) int vdx_attn_fwd_ws(
     hipStream_t stream) {
     int rc = validate(q, k, v, seg_q, seg_kv, out, lse, B, S, H, D, scale);
     if (rc != VDX_OK) return rc;
-    if (seg_q && (!workspace || !aligned(workspace, 16) || workspace_bytes < vdx::attn_fwd_workspace_bytes(B, S)))
+    if ((seg_q || workspace) &&
+        (!workspace || !aligned(workspace, 16) || workspace_bytes < vdx::attn_fwd_workspace_bytes(B, S)))
         return VDX_ERR_WORKSPACE;
     rc = check_device();
     if (rc != VDX_OK) return rc;
@@ -290,7 +291,8 @@ __attribute__((visibility("default"))) int vdx_rope3d_attn_fwd_ws(
     vdx::Rope3DDev dev{};
     rc = validate_rope(rope, D, dev);
     if (rc != VDX_OK) return rc;
-    if (seg_q && (!workspace || !aligned(workspace, 16) || workspace_bytes < vdx::attn_fwd_workspace_bytes(B, S)))
+    if ((seg_q || workspace) &&
+        (!workspace || !aligned(workspace, 16) || workspace_bytes < vdx::attn_fwd_workspace_bytes(B, S)))
         return VDX_ERR_WORKSPACE;
     rc = check_device();
     if (rc != VDX_OK) return rc;

@@ -178,3 +178,92 @@ def check_rows(out_g, lse_g, rows, out_o, lse_o, has, sens):
         assert np.all(bits == 0)
         assert np.all(np.isneginf(lg[~hv]))
     return stats
+
+
+# --- the split last round of vdx_attn_fwd_ws -----------------------------------------
+# The schedule only (which query blocks are split into parts), restated from
+# the library's documented rule: a persistent grid of G workgroups (the CU
+# count rounded down to a multiple of 8, W = G / 8 per XCD) runs the n_x items
+# of XCD x in rounds of W; when more than one round remains ragged, the last
+# R = n_x mod W items are split into P = min(8, W // R) >= 2 parts each.
+def persistent_grid():
+    return torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+
+
+def tail_plan(x, n_items, W):
+    n_x = n_items // 8 + (1 if x < n_items % 8 else 0)
+    if n_x > W:
+        R = n_x % W
+        P = min(8, W // R) if R else 1
+        if P >= 2:
+            return n_x, R, P
+    return n_x, 0, 1
+
+
+def n_split_items(n_items, grid):
+    if grid > 256:
+        return 0
+    return sum(tail_plan(x, n_items, grid // 8)[1] for x in range(8))
+
+
+def split_unmasked_blocks(B, S, H, grid):
+    """(b, h, block) of every 256-query block the unmasked vdx_attn_fwd_ws
+    splits: XCD x owns a contiguous run of items (item = (b H + h) n_qblk +
+    block), its local item j being run number x * per + min(x, rem) + j."""
+    n_qblk = (S + 255) // 256
+    n = B * H * n_qblk
+    if n <= grid or grid > 256:
+        return []
+    per, rem = n // 8, n % 8
+    out = []
+    for x in range(8):
+        n_x, R, _ = tail_plan(x, n, grid // 8)
+        for j in range(n_x - R, n_x):
+            lid = x * per + min(x, rem) + j
+            bh = lid // n_qblk
+            out.append((bh // H, bh % H, lid % n_qblk))
+    return out
+
+
+def block_mask(B, H, S, blocks):
+    """bool [B, S, H]: rows of the listed (b, h, block) query blocks."""
+    m = np.zeros((B, S, H), dtype=bool)
+    for b, h, blk in blocks:
+        m[b, blk * 256:min(S, (blk + 1) * 256), h] = True
+    return m
+
+
+def differing_blocks(o1, l1, o2, l2):
+    """(b, h, block) of the 256-query blocks where two results differ in any bit."""
+    B, S, H, _ = o1.shape
+    ob = (o1.view(torch.int16) != o2.view(torch.int16)).any(dim=3).cpu().numpy()  # [B, S, H]
+    lb = (l1.view(torch.int32) != l2.view(torch.int32)).cpu().numpy().transpose(0, 2, 1)
+    rows = ob | lb
+    out = set()
+    for b, i, h in zip(*np.nonzero(rows)):
+        out.add((int(b), int(h), int(i) // 256))
+    return sorted(out)
+
+
+def assert_split_close(o1, l1, o2, l2):
+    """A split block against the same block computed whole.  The parts round
+    their probabilities to bf16 against their own reference maxima, so the
+    outputs differ at the level of that rounding (each within the oracle
+    bound, which the callers check on sampled rows): every element within
+    OUT_ATOL of the other and a relative L2 distance within REL_L2.  The
+    sums l are taken from the unrounded probabilities in fp32, so lse agrees
+    to 1e-5 (+1e-6 relative); empty rows (+0.0, -inf) are the same."""
+    a = o1.float().cpu().numpy().astype(np.float64)
+    b = o2.float().cpu().numpy().astype(np.float64)
+    assert np.abs(a - b).max() <= OUT_ATOL, float(np.abs(a - b).max())
+    nb = np.linalg.norm(b)
+    if nb > 0:
+        assert np.linalg.norm(a - b) / nb <= REL_L2
+    la = l1.cpu().numpy().astype(np.float64)
+    lb = l2.cpu().numpy().astype(np.float64)
+    fa, fb = np.isfinite(la), np.isfinite(lb)
+    assert np.array_equal(fa, fb)
+    assert np.array_equal(la[~fa], lb[~fb])
+    assert np.all(np.abs(la[fa] - lb[fa]) <= 1e-5 + 1e-6 * np.abs(la[fa]))
+    dead = torch.from_numpy(~fa.transpose(0, 2, 1).copy())  # [B, S, H]
+    assert torch.all(o1.view(torch.int16).cpu()[dead] == 0)

@@ -251,10 +251,12 @@ def wcall(native, ws=A + 0x900, ws_bytes=None, q=A, k=A + 0x100, v=A + 0x200, sq
 def test_fwd_workspace_size(native):
     size = native.lib.vdx_attn_fwd_workspace_size
     r = lambda x: (x + 255) // 256 * 256
-    # counters, then per batch int4 tile summaries, block counts, block orders
-    assert size(1, 61440, 16) == 256 + r(16 * 960) + r(4 * 240) + 4 * 240
-    assert size(2, 17920, 24) == 256 + r(16 * 2 * 280) + r(4 * 2 * 70) + 4 * 2 * 70
-    assert size(1, 1, 1) == 256 + 256 + 256 + 4
+    # counters, then per batch int4 tile summaries, block counts, block orders,
+    # then 256 part records of the split last round (256 rows x (128 + 2) fp32)
+    recs = 256 * 256 * (128 + 2) * 4
+    assert size(1, 61440, 16) == 256 + r(16 * 960) + r(4 * 240) + r(4 * 240) + recs
+    assert size(2, 17920, 24) == 256 + r(16 * 2 * 280) + r(4 * 2 * 70) + r(4 * 2 * 70) + recs
+    assert size(1, 1, 1) == 256 + 256 + 256 + 256 + recs
     assert size(3, 1000, 1) == size(3, 1000, 40)  # H does not enter
     for bad in ((0, 1, 1), (1, 0, 1), (1, 1, 0)):
         assert size(*bad) == 0
@@ -272,10 +274,13 @@ def test_fwd_ws_validation(native):
     assert wcall(native, ws=A + 0x908) == native.VDX_ERR_WORKSPACE
     need = native.lib.vdx_attn_fwd_workspace_size(1, 128, 2)
     assert wcall(native, ws_bytes=need - 1) == native.VDX_ERR_WORKSPACE
+    # without segment IDs a workspace is optional, but one that is given is checked
+    assert wcall(native, sq=0, sk=0, ws_bytes=need - 1) == native.VDX_ERR_WORKSPACE
+    assert wcall(native, sq=0, sk=0, ws=A + 0x908) == native.VDX_ERR_WORKSPACE
     if not torch.cuda.is_available():
         assert wcall(native) == native.VDX_ERR_DEVICE
-        # without segment IDs the workspace is not used and may be NULL
         assert wcall(native, sq=0, sk=0, ws=0, ws_bytes=0) == native.VDX_ERR_DEVICE
+        assert wcall(native, sq=0, sk=0) == native.VDX_ERR_DEVICE
 
 
 # --- vdx_attn_bwd validation (no GPU needed) -------------------------------------
@@ -504,9 +509,11 @@ def test_rope_attn_ws_validation(native):
     assert rattn_ws(native, ws=A + 0xe04) == native.VDX_ERR_WORKSPACE
     need = native.lib.vdx_attn_fwd_workspace_size(1, 128, 2)
     assert rattn_ws(native, ws_bytes=need - 1) == native.VDX_ERR_WORKSPACE
+    assert rattn_ws(native, sq=0, sk=0, ws_bytes=need - 1) == native.VDX_ERR_WORKSPACE
     if not torch.cuda.is_available():
         assert rattn_ws(native) == native.VDX_ERR_DEVICE
         assert rattn_ws(native, sq=0, sk=0, ws=0, ws_bytes=0) == native.VDX_ERR_DEVICE
+        assert rattn_ws(native, sq=0, sk=0) == native.VDX_ERR_DEVICE
 
 
 def test_rope_valid_arguments_without_gpu_report_device_error(native):

@@ -1,0 +1,152 @@
+"""The split last round of vdx_attn_fwd_ws: when a persistent launch's items
+do not fill its last round, the items of that round are divided along their
+active key tiles into parts that run side by side, and a combine kernel
+merges the parts' (O, m, l).
+
+Against vdx_attn_fwd (which never splits): every query block that is not
+split gives the same bits; the split ones round their probabilities against
+each part's own reference maximum, so they agree to within that rounding
+(lse, summed from unrounded probabilities, to about 1e-6).  Against the oracle: rows of the split blocks at
+the parity bar, with the blocks and parts chosen so that parts with no key
+tile, padding rows and ragged tails all occur.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import (assert_split_close, block_mask, check_rows, differing_blocks, n_split_items,
+                         persistent_grid, run_oracle, split_unmasked_blocks, valid_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, seg_q, seg_kv, scale, split):
+    import spatiotemporal_attention_amd as vdx
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    sq = None if seg_q is None else seg_q.cuda()
+    sk = None if seg_kv is None else seg_kv.cuda()
+    B, S, H, _ = x["q"].shape
+    ws = torch.empty(vdx.attn_fwd_workspace_size(B, S, H), dtype=torch.uint8, device="cuda") if split else None
+    o, l = vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=scale, workspace=ws, scheduled=split)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def _rows_of(blocks, S, per_block, seed):
+    g = np.random.default_rng(seed)
+    rows = []
+    for b, h, blk in blocks:
+        lo, hi = blk * 256, min(S, (blk + 1) * 256)
+        picks = {lo, hi - 1} | set(int(i) for i in g.integers(lo, hi, size=per_block))
+        rows += [(b, h, i) for i in sorted(picks)]
+    return np.array(rows, dtype=np.int64)
+
+
+def _check_against_oracle(x, seg_q, seg_kv, scale, o, l, blocks, per_block, seed):
+    B, S, H, D = x["q"].shape
+    rows = _rows_of(blocks, S, per_block, seed)
+    oo, lo, sens = run_oracle(x, seg_q, seg_kv, scale, rows=rows)
+    has = valid_rows(seg_q, seg_kv, B, S)
+    return check_rows(o.cpu(), l.cpu(), rows, oo, lo, has, sens)
+
+
+@pytest.mark.parametrize("B,S,H,D", [(1, 8192, 9, 128), (1, 8192, 9, 64), (2, 4000, 10, 128), (1, 75600, 40, 128)])
+def test_unmasked_split_blocks(need_gpu, B, S, H, D):
+    """Unmasked: only the blocks the schedule splits differ from vdx_attn_fwd,
+    within rounding; their rows match the oracle."""
+    grid = persistent_grid()
+    blocks = split_unmasked_blocks(B, S, H, grid)
+    if not blocks:
+        pytest.skip(f"{B * H * ((S + 255) // 256)} items on a {grid}-workgroup grid leave no ragged round")
+    if S == 75600:
+        w = W.WORKLOADS["dit720p_large"]
+        x, scale = W.make_inputs(w), w.scale
+    else:
+        x, scale = W.make_random(B, S, H, D, seed=S + H + D), 1.0 / math.sqrt(D)
+    print(f"case split unmasked B={B} S={S} H={H} D={D} split blocks={len(blocks)}", flush=True)
+    o1, l1 = _run(x, None, None, scale, split=True)
+    o2, l2 = _run(x, None, None, scale, split=False)
+    diff = differing_blocks(o1, l1, o2, l2)
+    assert set(diff) <= set(blocks), sorted(set(diff) - set(blocks))[:8]
+    m = block_mask(B, H, S, blocks)
+    keep = torch.from_numpy(~m)
+    assert torch.equal(o1.view(torch.int16).cpu()[keep], o2.view(torch.int16).cpu()[keep])
+    assert_split_close(o1, l1, o2, l2)
+    sample = blocks[::max(1, len(blocks) // 16)]
+    stats = _check_against_oracle(x, None, None, scale, o1, l1, sample, 4 if S > 20000 else 16, S)
+    print(stats, flush=True)
+
+
+@pytest.mark.parametrize("kind", ["singletons", "packed", "padded", "allpad", "negative"])
+def test_masked_split_blocks(need_gpu, kind):
+    """Masked (the scheduled persistent kernel): 288 items on a 256-workgroup
+    grid leave 4 items per XCD for its last round, split 8 ways; with one-
+    token segments a block has about 4 active tiles, so most parts get none.
+    At most the split items' blocks differ from vdx_attn_fwd; their rows
+    match the oracle and padding rows stay +0.0 / -inf."""
+    B, S, H, D = 1, 8192, 9, 128
+    grid = persistent_grid()
+    n_items = B * H * ((S + 255) // 256)
+    n_split = n_split_items(n_items, grid)
+    if n_split == 0:
+        pytest.skip(f"{n_items} items on a {grid}-workgroup grid leave no ragged round")
+    x = W.make_random(B, S, H, D, seed=7000 + len(kind))
+    seg = W.random_segments(B, S, 7100 + len(kind), kind)
+    print(f"case split masked kind={kind} items={n_items} split={n_split}", flush=True)
+    o1, l1 = _run(x, seg, seg.clone(), 0.1, split=True)
+    o2, l2 = _run(x, seg, seg.clone(), 0.1, split=False)
+    diff = differing_blocks(o1, l1, o2, l2)
+    assert len(diff) <= n_split, (len(diff), n_split)
+    assert_split_close(o1, l1, o2, l2)
+    if diff:
+        print(_check_against_oracle(x, seg, seg, 0.1, o1, l1, diff, 16, 11), flush=True)
+    has = valid_rows(seg, seg, B, S)
+    dead = torch.from_numpy(~has)
+    assert torch.all(o1.view(torch.int16).cpu()[dead] == 0)
+    assert torch.all(torch.isneginf(l1.cpu().permute(0, 2, 1)[dead]))
+
+
+def test_joint_video_text_split_tail(need_gpu):
+    """The padded joint video+text workload at full size (3,360 items: 13
+    rounds of 256 and 32 items left, split 8 ways): at most 32 blocks differ
+    from vdx_attn_fwd, within rounding, and their rows (text, video and pad
+    rows among them) match the oracle."""
+    w = W.WORKLOADS["joint_video_text_pad"]
+    x = W.make_inputs(w)
+    n_items = w.B * w.H * ((w.S + 255) // 256)
+    n_split = n_split_items(n_items, persistent_grid())
+    print(f"case split joint video+text split={n_split}", flush=True)
+    o1, l1 = _run(x, x["seg_q"], x["seg_kv"], w.scale, split=True)
+    o2, l2 = _run(x, x["seg_q"], x["seg_kv"], w.scale, split=False)
+    diff = differing_blocks(o1, l1, o2, l2)
+    assert len(diff) <= n_split, (len(diff), n_split)
+    assert_split_close(o1, l1, o2, l2)
+    if diff:
+        print(_check_against_oracle(x, x["seg_q"], x["seg_kv"], w.scale, o1, l1, diff, 4, 13), flush=True)
+
+
+def test_split_workspace_reuse_and_smaller_call(need_gpu):
+    """One workspace, garbage on entry, used by a split unmasked call, a split
+    masked call and a smaller unsplit call: each equals a fresh-workspace run
+    bit for bit (the part records are written before the combine reads them)."""
+    import spatiotemporal_attention_amd as vdx
+    B, S, H, D = 1, 8192, 9, 128
+    ws = torch.full((vdx.attn_fwd_workspace_size(B, S, H),), 0x7F, dtype=torch.uint8, device="cuda")
+    x = W.make_random(B, S, H, D, seed=8100)
+    seg = W.random_segments(B, S, 8101, "packed")
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    for i, (sq, s_len) in enumerate([(None, S), (seg, S), (None, 3000)]):
+        dd = {n: t[:, :s_len].contiguous() for n, t in d.items()}
+        sqd = None if sq is None else sq[:, :s_len].contiguous().cuda()
+        print(f"case split workspace reuse {i}", flush=True)
+        o1, l1 = vdx.attn_fwd(dd["q"], dd["k"], dd["v"], sqd, None if sqd is None else sqd.clone(), scale=0.1,
+                              workspace=ws)
+        fresh = torch.empty_like(ws)
+        o2, l2 = vdx.attn_fwd(dd["q"], dd["k"], dd["v"], sqd, None if sqd is None else sqd.clone(), scale=0.1,
+                              workspace=fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))

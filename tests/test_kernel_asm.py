@@ -198,10 +198,12 @@ def test_checker_flags_a_planted_hazard():
 def test_no_kernel_spills_to_scratch(asm_text):
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm_text)]
     # D in {64, 128} x {unmasked, segment-masked} x {plain, 3D-rotary-embedded queries},
-    # the scheduled masked kernel for the same D and query variants, and its three
-    # set-up kernels (tile summaries, block counts, block order)
-    assert len(sizes) == 15
-    assert sizes == [0] * 15
+    # the unmasked ones again with a split last round, the scheduled masked
+    # kernel for the same D and query variants with and without a split last
+    # round, its three set-up kernels (tile summaries, block counts, block
+    # order), and the split-tail combine kernel for each D and item order
+    assert len(sizes) == 27
+    assert sizes == [0] * 27
 
 
 def test_neighbourhood_kernel_wait_states_and_no_spills(natten_asm_text):
