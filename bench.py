@@ -683,10 +683,10 @@ def main():
     }
     if args.rope:
         line["roofline"]["scope"] = "vdx_rope3d_attn_fwd_ws call (key pre-pass + attention kernels)"
+        line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     elif not args.plain:
         line["roofline"]["scope"] = ("vdx_attn_fwd_ws call (" + ("tile summaries, block counts and order, "
                                      if w.masked else "") + "the forward, the merge of a split last round)")
-        line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -823,18 +823,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 }
 
 // Merges the P parts of every split item of XCD blockIdx.y (item
-// blockIdx.x of its R): per row, M = the largest reference maximum among the
-// parts with valid keys, L = sum_p l_p 2^(m_p - M), O = sum_p O_p 2^(m_p - M);
-// out = O / L (bf16) and lse = (M + log2 L) ln 2, or +0 / -inf when L = 0.
-// One thread per row; parts are added in index order, so the result is
-// deterministic.  SCHED: the items are those of attn_fwd_sched_kernel
-// (longest-first block order ord), else those of attn_fwd_kernel.
+// blockIdx.x of its R), d columns 32 blockIdx.z .. 32 blockIdx.z + 31: per
+// row, M = the largest reference maximum among the parts with valid keys,
+// L = sum_p l_p 2^(m_p - M), O = sum_p O_p 2^(m_p - M); out = O / L (bf16)
+// and lse = (M + log2 L) ln 2, or +0 / -inf when L = 0.  One thread per row;
+// parts are added in index order, so the result is deterministic.  SCHED: the
+// items are those of attn_fwd_sched_kernel (longest-first block order ord),
+// else those of attn_fwd_kernel.
 template <int D, bool SCHED>
 __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __restrict__ recs,
                                                                const int* __restrict__ ord,
                                                                __bf16* __restrict__ out, float* __restrict__ lse,
                                                                int S, int H, int n_qblk, int n_items, int W) {
-    const int x = blockIdx.y, r = blockIdx.x;
+    const int x = blockIdx.y, r = blockIdx.x, c0 = 4 * blockIdx.z;
     const TailPlan tp = tail_plan(x, n_items, W, true);
     if (r >= tp.R) return;
     const int j = tp.n_x - tp.R + r;
@@ -859,47 +860,44 @@ __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __re
         const float* rp = rec0 + p * pstride;
         if (rp[(size_t)kBq * D + kBq + row] > 0.f) M = fmaxf(M, rp[(size_t)kBq * D + row]);
     }
-    float wgt[kTailMaxParts];
     float L = 0.f;
-    for (int p = 0; p < kTailMaxParts; ++p) {
-        wgt[p] = 0.f;
-        if (p < tp.P) {
-            const float* rp = rec0 + p * pstride;
-            const float l = rp[(size_t)kBq * D + kBq + row];
-            if (l > 0.f) {
-                wgt[p] = __builtin_amdgcn_exp2f(rp[(size_t)kBq * D + row] - M);
-                L += wgt[p] * l;
-            }
-        }
-    }
-    __bf16* orow = out + ((int64_t)it.b * S + qi) * H * D + (int64_t)it.h * D;
-    if (L > 0.f) {
-        const float inv = 1.0f / L;
-        for (int c = 0; c < D / 8; ++c) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int p = 0; p < tp.P; ++p) {
-                if (wgt[p] == 0.f) continue;
-                const float4* src = reinterpret_cast<const float4*>(rec0 + p * pstride + ((size_t)c * kBq + row) * 8);
-                const float4 lo = src[0], hi = src[1];
-                acc[0] += wgt[p] * lo.x;
-                acc[1] += wgt[p] * lo.y;
-                acc[2] += wgt[p] * lo.z;
-                acc[3] += wgt[p] * lo.w;
-                acc[4] += wgt[p] * hi.x;
-                acc[5] += wgt[p] * hi.y;
-                acc[6] += wgt[p] * hi.z;
-                acc[7] += wgt[p] * hi.w;
-            }
-            __bf16 o8[8];
+    float acc[4][8] = {};
+    for (int p = 0; p < tp.P; ++p) {
+        const float* rp = rec0 + p * pstride;
+        const float l = rp[(size_t)kBq * D + kBq + row];
+        if (!(l > 0.f)) continue;
+        const float w = __builtin_amdgcn_exp2f(rp[(size_t)kBq * D + row] - M);
+        L += w * l;
+        float4 v[4][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(acc[e] * inv);
-            *reinterpret_cast<uint4*>(orow + 8 * c) = *reinterpret_cast<const uint4*>(o8);
+        for (int cc = 0; cc < 4; ++cc) {
+            const float4* src = reinterpret_cast<const float4*>(rp + ((size_t)(c0 + cc) * kBq + row) * 8);
+            v[cc][0] = src[0];
+            v[cc][1] = src[1];
         }
-        lse[((int64_t)it.b * H + it.h) * S + qi] = (M + __builtin_amdgcn_logf(L)) * kLn2;
-    } else {
-        for (int c = 0; c < D / 8; ++c) *reinterpret_cast<uint4*>(orow + 8 * c) = uint4{0u, 0u, 0u, 0u};
-        lse[((int64_t)it.b * H + it.h) * S + qi] = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            acc[cc][0] += w * v[cc][0].x;
+            acc[cc][1] += w * v[cc][0].y;
+            acc[cc][2] += w * v[cc][0].z;
+            acc[cc][3] += w * v[cc][0].w;
+            acc[cc][4] += w * v[cc][1].x;
+            acc[cc][5] += w * v[cc][1].y;
+            acc[cc][6] += w * v[cc][1].z;
+            acc[cc][7] += w * v[cc][1].w;
+        }
     }
+    __bf16* orow = out + ((int64_t)it.b * S + qi) * H * D + (int64_t)it.h * D + 8 * c0;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+        __bf16 o8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(acc[cc][e] * inv);
+        *reinterpret_cast<uint4*>(orow + 8 * cc) = *reinterpret_cast<const uint4*>(o8);
+    }
+    if (blockIdx.z == 0)
+        lse[((int64_t)it.b * H + it.h) * S + qi] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
 // Dynamic LDS of a launch: the K/V/segment-ID ring, then (masked) the
@@ -1113,7 +1111,7 @@ hipError_t launch_combine(const AttnArgs& a, const float* recs, const int* ord, 
                           hipStream_t stream) {
     const int max_r = tail_max_r(n_items, grid);
     if (max_r == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, kXcds), dim3(kBq), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, kXcds, D / 32), dim3(kBq), 0, stream,
                        recs, ord, reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, n_qblk, n_items,
                        grid / kXcds);
     return hipGetLastError();
