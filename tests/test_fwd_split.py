@@ -150,3 +150,98 @@ def test_split_workspace_reuse_and_smaller_call(need_gpu):
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
         assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def _rope_run(x, r, seg, scale, split):
+    import spatiotemporal_attention_amd as vdx
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    sd = None if seg is None else seg.cuda()
+    rr = dict(pos=r.pos.cuda(), cos=[c.cuda() for c in r.cos], sin=[s.cuda() for s in r.sin], dims=r.dims,
+              interleaved=r.interleaved)
+    B, S, H, _ = x["q"].shape
+    ws = torch.empty(vdx.attn_fwd_workspace_size(B, S, H), dtype=torch.uint8, device="cuda") if split else None
+    o, l = vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, seg_q=sd, seg_kv=sd, scale=scale, workspace=ws,
+                               scheduled=split)
+    torch.cuda.synchronize()
+    return o, l
+
+
+@pytest.mark.parametrize("D,kind", [(128, None), (64, None), (128, "packed"), (64, "padded")])
+def test_rope_split_blocks(need_gpu, D, kind):
+    """vdx_rope3d_attn_fwd_ws with a split last round (288 items on a
+    256-workgroup grid) against vdx_rope3d_attn_fwd: at most the split
+    blocks differ, within rounding, and their rows match the oracle
+    (rotation, then attention)."""
+    import oracle
+    B, S, H = 1, 8192, 9
+    grid = persistent_grid()
+    n_items = B * H * ((S + 255) // 256)
+    n_split = n_split_items(n_items, grid)
+    if n_split == 0:
+        pytest.skip(f"{n_items} items on a {grid}-workgroup grid leave no ragged round")
+    x = W.make_random(B, S, H, D, seed=9000 + D)
+    dims = W.ROPE_DIMS[D]
+    n = (8, 16, 64)
+    tabs = [W.rope3d_tables(n[a], dims[a]) for a in range(3)]
+    r = W.Rope3D(pos=W.random_positions(B, S, n, 9001 + D, 0.05), cos=tuple(t[0] for t in tabs),
+                 sin=tuple(t[1] for t in tabs), dims=tuple(dims), interleaved=True)
+    seg = None if kind is None else W.random_segments(B, S, 9002 + D, kind)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case split rope D={D} kind={kind} split={n_split}", flush=True)
+    o1, l1 = _rope_run(x, r, seg, scale, split=True)
+    o2, l2 = _rope_run(x, r, seg, scale, split=False)
+    diff = differing_blocks(o1, l1, o2, l2)
+    assert len(diff) <= n_split, (len(diff), n_split)
+    if kind is None:
+        assert set(diff) <= set(split_unmasked_blocks(B, S, H, grid))
+    assert_split_close(o1, l1, o2, l2)
+    if diff:
+        rows = _rows_of(diff, S, 8, 17)
+        pos, cos, sin = r.numpy()
+        s = None if seg is None else seg.numpy()
+        sens = np.zeros((len(rows), D))
+        out_o, lse_o = oracle.rope3d_attn_fwd(W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"]),
+                                              pos, cos, sin, r.dims, r.interleaved, s,
+                                              None if s is None else s.copy(), float(np.float32(scale)),
+                                              rows=rows, sens=sens)
+        print(check_rows(o1.cpu(), l1.cpu(), rows, out_o, lse_o, valid_rows(seg, seg, B, S), sens), flush=True)
+
+
+def test_split_graph_replays(need_gpu):
+    """A split call (unmasked and masked) captured in a HIP graph and
+    replayed three times, with eager calls on the same workspace in between:
+    every replay equals the eager call, bit for bit."""
+    import spatiotemporal_attention_amd as vdx
+    B, S, H, D = 1, 8192, 9, 128
+    if n_split_items(B * H * ((S + 255) // 256), persistent_grid()) == 0:
+        pytest.skip("no ragged round on this grid")
+    x = W.make_random(B, S, H, D, seed=9100)
+    seg = W.random_segments(B, S, 9101, "packed").cuda()
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    for sq in (None, seg):
+        sk = None if sq is None else sq.clone()
+        ws = torch.empty(vdx.attn_fwd_workspace_size(B, S, H), dtype=torch.uint8, device="cuda")
+        ref_o, ref_l = vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, workspace=ws)
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, out=out, lse=lse, workspace=ws, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        print(f"case split graph capture masked={sq is not None}", flush=True)
+        with torch.cuda.graph(g):
+            vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, out=out, lse=lse, workspace=ws,
+                         stream=torch.cuda.current_stream())
+        for i in range(3):
+            out.zero_()
+            lse.fill_(7.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+            assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
+            vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, workspace=ws)
+            torch.cuda.synchronize()
