@@ -63,6 +63,7 @@ constexpr int kMaxKvTiles = 30720;  // capacity of the on-chip active-tile list
 template <int D, bool SEG, bool PART>
 struct Attn {
     using T = Tile<D>;
+    static constexpr bool kSeg = SEG;
     char* smem;
     const __bf16* kp;   // K of (b, h), token 0
     const __bf16* vp;
@@ -82,6 +83,10 @@ struct Attn {
     // previous call, so the segment-ID copy decision needs no second lookup.
     int prev_t;
     bool prev_part;
+    // With segment IDs the partial flags of the planned tiles are kept as
+    // bits (the latest plan() call's in bit 0), so that the VALU phase's
+    // partial test does not wait on an LDS read of the tile list.
+    uint32_t phist;
     // K operand of k-step ks sits at kx ^ (ks << 5) and the transposed V read
     // of d-block db at vx ^ (db << 6) (offsets within a ring slot): the XOR
     // swizzles only touch bits that these bases hold no other data in.
@@ -111,6 +116,18 @@ struct Attn {
                 partial = (n == n_kvt - 1) && (S % kBk != 0);
                 return n;
             }
+        }
+    }
+    // Partial test of tile n in the VALU phase of iteration n of group G: the
+    // last plan() call of G was for tile n + 2 - G.
+    template <int G>
+    __device__ __forceinline__ bool partial_planned(int n) const {
+        if constexpr (SEG) {
+            return ((phist >> (2 - G)) & 1u) != 0;
+        } else {
+            bool p;
+            tile_of(n, p);
+            return p;
         }
     }
     __device__ __forceinline__ bool partial(int n) const {
@@ -150,10 +167,17 @@ struct Attn {
         bool tail;          // last, partial tile: issued at the phase start
         int cnt;            // loads this wave issues for the copy
     };
+    // Tile-list entry of active tile a for plan() (SEG; read at the start of
+    // a VALU phase, so that its latency passes under the softmax), or 0.
+    __device__ __forceinline__ int list_entry(int a, int n_act) const {
+        if constexpr (SEG) return a < n_act ? (int)list[a] : 0;
+        return 0;
+    }
     // Plans the copies of the MFMA phase of iteration a - 2 + G (run in the
-    // preceding VALU phase: scalar work only, nothing is issued).
+    // preceding VALU phase: scalar work only, nothing is issued); ent is
+    // list_entry(a, n_act).
     template <int G>
-    __device__ __forceinline__ void plan(Copy& c, int a, int n_act) {
+    __device__ __forceinline__ void plan(Copy& c, int a, int n_act, int ent) {
         bool part;
         int pt = 0;
         bool pp = false;
@@ -164,8 +188,16 @@ struct Attn {
         c.cnt = 0;
         c.spread = c.tail = false;
         c.seg_a = -1;
+        if constexpr (SEG) phist <<= 1;
         if (a < n_act) {
-            c.t = tile_of(a, part);
+            if constexpr (SEG) {
+                const int e = __builtin_amdgcn_readfirstlane(ent);
+                part = (e & 0x8000) != 0;
+                c.t = e & 0x7fff;
+                phist |= part ? 1u : 0u;
+            } else {
+                c.t = tile_of(a, part);
+            }
             c.src = (G ? vp : kp) + (int64_t)c.t * kBk * tok_stride;
             c.dst = smem + (G ? T::kVRegion : T::kKRegion) + slot_base(a) +
                     w4 * T::kLoadsPerWave * 1024;
@@ -387,15 +419,19 @@ template <int G, class AT>
 __device__ __forceinline__ void main_loop(AT& A, int n_act) {
     typename AT::Copy cp;
     auto valu_phase = [&](int n) {
-        if (A.partial(n)) A.mask(n);
+        // The tile-list read for this phase's plan goes out first; the fence
+        // keeps the scheduler from sinking it next to its use.
+        const int ent = A.list_entry(n + 3 - G, n_act);
+        if (AT::kSeg) __builtin_amdgcn_sched_barrier(0);
+        if (A.template partial_planned<G>(n)) A.mask(n);
         A.softmax();
-        A.template plan<G>(cp, n + 3 - G, n_act);
+        A.template plan<G>(cp, n + 3 - G, n_act, ent);
         // Operands of the next MFMA phase (K Q^T of tile n+1; stale when n+1 is
         // past the last tile, and then unused).
         A.template prefetch<true, true>(n, n + 1);
         barrier();
     };
-    A.template plan<G>(cp, 2 - G, n_act);
+    A.template plan<G>(cp, 2 - G, n_act, A.list_entry(2 - G, n_act));
     A.template prefetch<false, true>(0, 0);
     if (G == 1) barrier();  // group 1 idles in global phase 0
     A.template mfma_phase<false, true, true>(0, 0, cp);
@@ -680,12 +716,13 @@ __device__ __forceinline__ void attn_fwd_item(
     if (SEG) {
         A.prev_t = 0;
         A.prev_part = false;
+        A.phist = 0u;
     }
     {
         typename Attn<D, SEG, PART>::Copy c;
         if (grp == 0) {
             for (int a = 0; a < 2; ++a) {
-                A.template plan<0>(c, a, n_act);  // K tile a, segment IDs of tile a-1
+                A.template plan<0>(c, a, n_act, A.list_entry(a, n_act));  // K tile a, segment IDs of tile a-1
                 A.copy_start(c);
                 if (c.spread) {
 #pragma unroll
@@ -693,7 +730,7 @@ __device__ __forceinline__ void attn_fwd_item(
                 }
             }
         } else {
-            A.template plan<1>(c, 0, n_act);
+            A.template plan<1>(c, 0, n_act, A.list_entry(0, n_act));
             A.copy_start(c);
             if (c.spread) {
 #pragma unroll
