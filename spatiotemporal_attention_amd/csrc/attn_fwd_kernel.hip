@@ -540,12 +540,12 @@ __device__ __forceinline__ ItemPos decode_item(int w, int n_wg, int n_qblk, int 
 
 // ---- split tail of a persistent launch ----------------------------------------------
 // A persistent grid of G workgroups (W = G / 8 per XCD) runs the n_x items of
-// an XCD in rounds of W.  When n_x is not a multiple of W, the last round
+// an XCD in rounds of W.  When n_x > W is not a multiple of W, the last round
 // holds R = n_x mod W items and leaves W - R workgroups idle for a whole
 // item's time.  With a workspace for partial results, each of those R items
-// is instead split along its active key tiles into P = min(8, W / R) parts,
-// which the XCD's workgroups run side by side; a combine kernel then merges
-// the parts of each item.  Local index j of an XCD (its j-th item, or unit
+// is instead split along its active key tiles into P = min(8, W / R) parts
+// (when that makes at least 2), which the XCD's workgroups run side by side;
+// a combine kernel then merges the parts of each item.  Local index j of an XCD (its j-th item, or unit
 // once split): j < n_x - R is the whole item j; otherwise u = j - (n_x - R)
 // is part u / R of item n_x - R + u % R, with its partial results in record
 // x * W + u.  An XCD runs n_x - R + R * P units.
