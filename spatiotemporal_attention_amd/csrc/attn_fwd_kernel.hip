@@ -538,6 +538,29 @@ __device__ __forceinline__ ItemPos decode_item(int w, int n_wg, int n_qblk, int 
     return ItemPos{bh / H, bh % H, lid % n_qblk};
 }
 
+// Item j of XCD x in the scheduled order -> batch b, head h and longest-first
+// rank r of its query block.  When 8 divides H, XCD x takes its heads x,
+// x + 8, ... one after the other, each head's blocks batch by batch, longest
+// first, so that its workgroups stream one head's K/V at a time; otherwise
+// item e = x + 8 j of the list that walks the batches, then the blocks
+// longest first, then the heads.
+__device__ __forceinline__ void sched_coords(int x, int j, int H, int n_qblk, int n_items, int& b, int& h,
+                                             int& r) {
+    if (H % kXcds == 0) {
+        const int per_head = n_items / H;  // B * n_qblk
+        const int hi = j / per_head, rem = j - hi * per_head;
+        h = x + kXcds * hi;
+        b = rem / n_qblk;
+        r = rem - b * n_qblk;
+    } else {
+        const int e = x + kXcds * j;
+        h = e % H;
+        const int rb = e / H;
+        r = rb % n_qblk;
+        b = rb / n_qblk;
+    }
+}
+
 // ---- split tail of a persistent launch ----------------------------------------------
 // A persistent grid of G workgroups (W = G / 8 per XCD) runs the n_x items of
 // an XCD in rounds of W.  When n_x > W is not a multiple of W, the last round
@@ -878,9 +901,8 @@ __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __re
     const int j = tp.n_x - tp.R + r;
     ItemPos it;
     if (SCHED) {
-        const int e = x + kXcds * j;
-        const int h = e % H, rb = e / H;
-        const int rr = rb % n_qblk, b = rb / n_qblk;
+        int b, h, rr;
+        sched_coords(x, j, H, n_qblk, n_items, b, h, rr);
         const int o = ord[(int64_t)b * n_qblk + rr];
         it = ItemPos{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};
     } else {
@@ -1067,16 +1089,18 @@ __global__ __launch_bounds__(kFwdRankThreads) void attn_fwd_rank_kernel(const in
     }
 }
 
-// Persistent masked forward: workgroup p (on XCD p % 8) pulls slot k of its
-// XCD's counter and runs item e = p % 8 + 8 k of the list that walks the
-// batches, then the query blocks longest first, then the heads:
-// e = (b * n_qblk + r) * H + h, block ord[b][r].  An XCD thus takes every
-// eighth item -- all of its heads h = x (mod 8) when 8 divides H -- longest
-// first, and its workgroups stay busy until its list runs out.  Every item is
-// pulled exactly once (each counter hands out 0, 1, 2, ... and only items of
-// its residue), and a workgroup exits at the first slot past the list, so
-// every wave exits.  Requires a grid that is a multiple of 8.  ROPE: the
-// queries are rotated in the item prologue, as in attn_fwd_kernel.
+// Persistent masked forward: workgroup p (on XCD x = p % 8) pulls slot k of
+// its XCD's counter and runs item k of the XCD's list (sched_coords): when 8
+// divides H, its heads x, x + 8, ... one after the other, each head's blocks
+// batch by batch, longest first (block ord[b][r]), so that the XCD's
+// workgroups stream one head's K/V at a time; otherwise every eighth item of
+// the list that walks the batches, then the blocks longest first, then the
+// heads.  Either way the XCD takes an eighth of the work, longest first within
+// a head, and its workgroups stay busy until its list runs out.  Every item is
+// pulled exactly once (each counter hands out 0, 1, 2, ...), and a workgroup
+// exits at the first slot past the list, so every wave exits.  Requires a grid
+// that is a multiple of 8.  ROPE: the queries are rotated in the item
+// prologue, as in attn_fwd_kernel.
 template <int D, bool ROPE, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -1103,9 +1127,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
             part = TailPart{ws.recs + (size_t)(xcd * W + u) * tail_record_floats<D>(), u / tp.R, tp.P};
             j = n_whole + u % tp.R;
         }
-        const int ie = xcd + kXcds * j;
-        const int h = ie % H, rb = ie / H;
-        const int r = rb % n_qblk, b = rb / n_qblk;
+        int b, h, r;
+        sched_coords(xcd, j, H, n_qblk, n_items, b, h, r);
         const int o = ws.ord[(int64_t)b * n_qblk + r];
         const ItemPos it{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};  // a permutation; the test keeps it in range
         attn_fwd_item<D, true, ROPE, true, SPLIT>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
