@@ -137,3 +137,16 @@ def test_counter_summaries_are_consistent(name, doc):
     for c in doc["commands"]:
         assert "rocprofv3 --pmc" in c and "-- python3 /root/repo/bench.py" in c
         assert "_work" not in c
+
+
+@pytest.mark.parametrize("args", [["--plain", "--rope"], ["--plain", "--pass", "bwd"],
+                                  ["--plain", "--workload", "natten_vae_decoder"]])
+def test_plain_entry_only_for_the_attention_forward(args):
+    """--plain (time vdx_attn_fwd instead of vdx_attn_fwd_ws) is refused with
+    the rotary call, the backward and the neighbourhood kernel, before any GPU
+    work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--plain applies to the attention forward" in r.stderr
+    assert r.stdout == ""
