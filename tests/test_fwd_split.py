@@ -245,3 +245,26 @@ def test_split_graph_replays(need_gpu):
             assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
             vdx.attn_fwd(d["q"], d["k"], d["v"], sq, sk, scale=0.1, workspace=ws)
             torch.cuda.synchronize()
+
+
+def test_rope_split_at_720p_equals_composed_split(need_gpu):
+    """At the 720p layer's size, in the launch configuration the benchmark
+    times with --rope: vdx_rope3d_attn_fwd_ws (split last round) equals
+    vdx_attn_fwd_ws on separately rotated q and k, bit for bit (the same split
+    schedule on the same rotated bits)."""
+    import spatiotemporal_attention_amd as vdx
+    w = W.WORKLOADS["dit720p_large"]
+    x = W.make_inputs(w)
+    r = W.workload_rope3d(w)
+    d = {n: x[n].cuda() for n in ("q", "k", "v")}
+    rr = dict(pos=r.pos.cuda(), cos=[c.cuda() for c in r.cos], sin=[s.cuda() for s in r.sin], dims=r.dims,
+              interleaved=r.interleaved)
+    ws = torch.empty(vdx.attn_fwd_workspace_size(w.B, w.S, w.H), dtype=torch.uint8, device="cuda")
+    print("case split rope 720p: fused vs composed", flush=True)
+    o1, l1 = vdx.rope3d_attn_fwd(d["q"], d["k"], d["v"], **rr, scale=w.scale, workspace=ws)
+    qr = vdx.rope3d_apply(d["q"], **rr)
+    kr = vdx.rope3d_apply(d["k"], **rr)
+    o2, l2 = vdx.attn_fwd(qr, kr, d["v"], scale=w.scale, workspace=torch.empty_like(ws))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
