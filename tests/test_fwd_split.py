@@ -268,3 +268,48 @@ def test_rope_split_at_720p_equals_composed_split(need_gpu):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def _random_split_cases(n=10, seed=2024):
+    """Seeded shapes whose item count leaves a ragged last round on a
+    256-workgroup grid (so that the call splits), with random segment kinds."""
+    g = np.random.default_rng(seed)
+    kinds = [None, "single", "padded", "packed", "interleaved", "singletons", "negative", "extreme"]
+    cases = []
+    while len(cases) < n:
+        B = int(g.integers(1, 4))
+        D = int(g.choice([64, 128]))
+        S = int(g.integers(700, 6000))
+        n_qblk = (S + 255) // 256
+        H = int(g.integers(1, 40))
+        n_items = B * H * n_qblk
+        if n_items > 2000 or n_split_items(n_items, 256) == 0:
+            continue
+        cases.append((B, S, H, D, kinds[int(g.integers(0, len(kinds)))], int(g.integers(0, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("B,S,H,D,kind,seed", _random_split_cases())
+def test_random_split_shapes(need_gpu, B, S, H, D, kind, seed):
+    """Random shapes and segment layouts with a ragged last round: the split
+    call against vdx_attn_fwd (unsplit blocks bit for bit when unmasked, at
+    most the split items' blocks differing when masked, split blocks within
+    rounding) and rows of the differing blocks against the oracle."""
+    grid = persistent_grid()
+    n_items = B * H * ((S + 255) // 256)
+    n_split = n_split_items(n_items, grid)
+    if n_split == 0:
+        pytest.skip(f"{n_items} items on a {grid}-workgroup grid leave no ragged round")
+    x = W.make_random(B, S, H, D, seed=seed % 100000)
+    seg = None if kind is None else W.random_segments(B, S, seed % 99991, kind)
+    scale = 1.0 / math.sqrt(D)
+    print(f"case split random B={B} S={S} H={H} D={D} kind={kind} split={n_split}", flush=True)
+    o1, l1 = _run(x, seg, None if seg is None else seg.clone(), scale, split=True)
+    o2, l2 = _run(x, seg, None if seg is None else seg.clone(), scale, split=False)
+    diff = differing_blocks(o1, l1, o2, l2)
+    assert len(diff) <= n_split, (len(diff), n_split)
+    if seg is None:
+        assert set(diff) <= set(split_unmasked_blocks(B, S, H, grid))
+    assert_split_close(o1, l1, o2, l2)
+    if diff:
+        print(_check_against_oracle(x, seg, seg, scale, o1, l1, diff[:12], 6, seed % 1000), flush=True)
