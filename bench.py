@@ -2,10 +2,10 @@
 
 One step = one vdx_attn_fwd_ws call (the forward with a resident workspace;
 the whole hot path: tile scheduling, segment classification, QK^T, masking,
-online softmax, PV, epilogue, and the merge of the split last round's parts)
-over one batch of seeded synthetic input already resident in HBM; with
---plain, one vdx_attn_fwd call (no workspace: unmasked launches never split,
-masked ones run one workgroup per query block).  Steps call the C ABI through the binding with their
+online softmax, PV, epilogue, and the merge of split items' parts) over one
+batch of seeded synthetic input already resident in HBM; with --plain, one
+vdx_attn_fwd call (no workspace: unmasked launches run a static persistent
+grid and never split, masked ones run one workgroup per query block).  Steps call the C ABI through the binding with their
 arguments prepared once (the tensor-level wrappers check them on a first,
 untimed call), and the warm-up runs until the clock has settled (at least 3
 steps and 1 s unless --warmup is given).  The default
@@ -686,7 +686,8 @@ def main():
         line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     elif not args.plain:
         line["roofline"]["scope"] = ("vdx_attn_fwd_ws call (" + ("tile summaries, block counts and order, "
-                                     if w.masked else "") + "the forward, the merge of a split last round)")
+                                     if w.masked else "the pool counter reset, ") + "the forward, the merge of "
+                                     "split items)")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)

@@ -34,8 +34,8 @@
  * the same device give bit-identical outputs (fixed reduction order, no
  * atomics in the arithmetic; the *_ws entry points hand out work items with
  * atomic counters in their workspace, which decides only which workgroup
- * computes an item, and split their last round by a rule fixed by the shape
- * and the device's CU count).
+ * computes an item, and split some items along their keys by a rule fixed
+ * by the shape and the device's CU count).
  */
 #ifndef VDX_ATTN_H
 #define VDX_ATTN_H
@@ -112,7 +112,7 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
 
 /*
  * vdx_attn_fwd_ws -- vdx_attn_fwd with a caller workspace, which the call
- * uses to balance uneven work and to split the last round of a persistent
+ * uses to balance uneven work and to split the last items of a persistent
  * launch; the same operation.
  *
  * The pages motivate it (vidax paper, arXiv:2609.18077, Appendix A, Table 4,
@@ -125,16 +125,29 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
  * from per-XCD work counters and classify tiles from the summaries.  The
  * counters change only which workgroup computes an item, never its result.
  *
- * Split last round (with or without segment IDs): a persistent launch of G
- * workgroups (the CU count rounded down to a multiple of 8; W = G / 8 per
- * XCD) runs the n_x items of each XCD in rounds of W.  When n_x > W and
- * R = n_x mod W leaves room for P = min(8, W / R) >= 2 parts, each of the
- * last R items of the XCD is split along its active key tiles into P parts
- * run side by side, and a last kernel merges each item's parts (their
+ * A persistent launch has G workgroups (the CU count rounded down to a
+ * multiple of 8; W = G / 8 per XCD); an item is one (batch, head, 256-query
+ * block).  Split items: an item is split along its active key tiles into P
+ * parts run side by side, and a last kernel merges each item's parts (their
  * running maxima, sums and unnormalised outputs, added in part order).
  * Every other query block gives vdx_attn_fwd's bits; a split block equals
  * them up to rounding (each part rounds its probabilities to bf16 against
- * its own running maximum), within the same accuracy bound.
+ * its own running maximum), within the same accuracy bound.  Which items
+ * are split:
+ *   - with segment IDs: XCD x runs its n_x items in rounds of W; when
+ *     n_x > W and R = n_x mod W leaves room for P = min(8, W / R) >= 2
+ *     parts, the last R items of the XCD are split;
+ *   - without them, when there are more items n than G (n <= G: no split):
+ *     XCD x owns a contiguous run of items (the first at x per + min(x, rem),
+ *     per + (x < rem) of them, per = n / 8, rem = n mod 8; items numbered
+ *     (b H + h) ceil(S / 256) + block) and runs K of its rounds of W
+ *     (K = per / W - 2 when per / W >= 16, else per / W); the rest of every
+ *     run forms a pool of n - K G items, XCD x's after those of XCDs below
+ *     x, that every workgroup pulls from once its own rounds are done, and
+ *     the pool's last R items (G / 4 when per / W >= 16, else all of them)
+ *     are split into P = min(8, 256 / R, G / R) parts when that is >= 2.
+ *     The XCDs run at different speeds under this load, and the pool lets
+ *     the faster ones take over the slower ones' last items.
  *
  *   q ... scale, stream   exactly as for vdx_attn_fwd.
  *   workspace  device scratch of at least vdx_attn_fwd_workspace_size(B, S,
@@ -142,7 +155,7 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
  *              on entry do not matter and are overwritten (two calls in
  *              flight at once need two workspaces).  Required with segment
  *              IDs.  Without them it may be NULL, and the call is then
- *              vdx_attn_fwd (no split).
+ *              vdx_attn_fwd (no pool, no split).
  * Validation: as vdx_attn_fwd, then the workspace (with segment IDs, or
  * whenever it is not NULL) -> VDX_ERR_WORKSPACE; the first failure is
  * reported before any HIP call.  Results are deterministic.
@@ -155,7 +168,7 @@ int vdx_attn_fwd_ws(const void* q, const void* k, const void* v,
 /* Bytes of workspace vdx_attn_fwd_ws needs for (B, S, H): 256 (work
  * counters) + R(16 * B * ceil(S / 64)) (tile summaries) + R(4 * B *
  * ceil(S / 256)) (block counts) + R(4 * B * ceil(S / 256)) (block orders) +
- * 256 * 256 * 130 * 4 (part records of the split last round: per part the
+ * 256 * 256 * 130 * 4 (part records of the split items: per part the
  * fp32 unnormalised output, maximum and sum of 256 rows at D <= 128), R()
  * rounding up to a multiple of 256.  H does not enter.  0 if B, S or H < 1. */
 size_t vdx_attn_fwd_workspace_size(int B, int S, int H);
@@ -357,8 +370,9 @@ int vdx_rope3d_attn_fwd(const void* q, const void* k, const void* v,
  * vdx_rope3d_attn_fwd_ws -- vdx_rope3d_attn_fwd on the schedule of
  * vdx_attn_fwd_ws (same workspace layout and size,
  * vdx_attn_fwd_workspace_size(B, S, H)): with segment IDs the persistent,
- * longest-first launch, and with or without them the split last round.
- * Without segment IDs the workspace may be NULL (then no split).  Results
+ * longest-first launch, and with or without them the split items (and,
+ * without them, the pool).  Without segment IDs the workspace may be NULL
+ * (then neither).  Results
  * relate to vdx_rope3d_attn_fwd's as vdx_attn_fwd_ws's to vdx_attn_fwd's.
  * Validation: as vdx_rope3d_attn_fwd, then the workspace (with segment IDs,
  * or whenever it is not NULL) -> VDX_ERR_WORKSPACE.

@@ -100,14 +100,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     [B, S] or both None (unmasked).  Returns (out bf16 [B,S,H,D], lse fp32 [B,H,S]).
 
     With segment IDs the call goes to vdx_attn_fwd_ws (work counters, a
-    longest-first block order and the split last round's partial results in
+    longest-first block order and the partial results of split items in
     a workspace; ``workspace``, a uint8 CUDA tensor of at least
     attn_fwd_workspace_size(B, S, H) bytes, or one allocated here on the
     launch stream); ``scheduled=False`` calls vdx_attn_fwd, one workgroup per
     block in index order.  Without segment IDs the call goes to
     vdx_attn_fwd_ws only when a ``workspace`` is given (and ``scheduled``).
     The two entry points give the same bits except on the query blocks whose
-    keys the split last round divides (equal up to rounding).
+    keys vdx_attn_fwd_ws splits (equal up to rounding).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, S, H, D]")

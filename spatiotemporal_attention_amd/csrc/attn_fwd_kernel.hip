@@ -530,12 +530,14 @@ __device__ void rope_stage_q(char* smem, const __bf16* __restrict__ q, const Rop
 struct ItemPos {
     int b, h, qblk;
 };
+__device__ __forceinline__ ItemPos item_at(int lid, int n_qblk, int H) {
+    const int bh = lid / n_qblk;
+    return ItemPos{bh / H, bh % H, lid % n_qblk};
+}
 __device__ __forceinline__ ItemPos decode_item(int w, int n_wg, int n_qblk, int H) {
     const int per = n_wg / kXcds, rem = n_wg % kXcds;
     const int xcd = w % kXcds;
-    const int lid = xcd * per + min(xcd, rem) + w / kXcds;
-    const int bh = lid / n_qblk;
-    return ItemPos{bh / H, bh % H, lid % n_qblk};
+    return item_at(xcd * per + min(xcd, rem) + w / kXcds, n_qblk, H);
 }
 
 // Item j of XCD x in the scheduled order -> batch b, head h and longest-first
@@ -598,6 +600,62 @@ __host__ __device__ inline TailPlan tail_plan(int x, int n_items, int W, bool on
 template <int D>
 constexpr size_t tail_record_floats() { return (size_t)kBq * D + 2 * kBq; }
 static_assert(tail_record_floats<128>() % 64 == 0 && tail_record_floats<64>() % 64 == 0, "records stay 256-byte aligned");
+
+// Unmasked persistent schedule with a shared pool.  XCD x owns a contiguous
+// run of items (the first at x per + min(x, rem), per + (x < rem) of them,
+// per = n / 8, rem = n mod 8) and runs K whole rounds of them, W = G / 8 at
+// a time, in step; the rest of every XCD's run forms a pool of n - K G
+// items, XCD-major (the workgroups that reach it together still stream one
+// head), that every workgroup pulls from through one counter once its own
+// rounds are done.  Long launches keep kPoolRounds rounds per XCD for the
+// pool, because the XCDs do not run the kernel at the same speed (per-item
+// timestamps put the odd-numbered ones 4-5% behind the even ones on two
+// devices, all through the launch) and equal static shares would leave the
+// faster ones idle at the end; the pool's last R = G / 4 items are split
+// into parts along their key tiles and pulled after the whole ones, so the
+// launch ends within about a part.  Shorter launches run every whole round
+// statically (their imbalance is too short to pay for the merge) and pool
+// only the remainder, which is split into P = min(8, G / R) parts when that
+// is at least 2, so that it fills one last round.
+constexpr int kPoolRounds = 2;
+constexpr int kPoolMinRounds = 16;
+struct PoolPlan {
+    int per, rem;  // items of XCD x: per + (x < rem), starting at item x per + min(x, rem)
+    int K;         // whole static rounds of every XCD
+    int n_pool;    // n - K G
+    int R, P;      // pool items split (the last R) and parts per split item (R = 0: none)
+    __host__ __device__ int units() const { return n_pool - R + R * P; }
+};
+__host__ __device__ inline PoolPlan pool_plan(int n_items, int G) {
+    const int W = G / kXcds;
+    PoolPlan p{n_items / kXcds, n_items % kXcds, 0, 0, 0, 1};
+    const int rounds = p.per / W;
+    const bool long_launch = rounds >= kPoolMinRounds;
+    p.K = long_launch ? rounds - kPoolRounds : rounds;
+    p.n_pool = n_items - p.K * G;
+    const int R = long_launch ? min(p.n_pool, G / 4) : p.n_pool % G;
+    const int P = R > 0 ? min(min(kTailMaxParts, kTailRecords / R), G / R) : 1;
+    if (P >= 2) {
+        p.R = R;
+        p.P = P;
+    }
+    return p;
+}
+// Pool item i -> its item number (the b, h, block order of decode_item):
+// XCD x leaves t0 + (x < rem) items after its K W, t0 = per - K W.
+__host__ __device__ inline int pool_item(const PoolPlan& p, int i, int W) {
+    const int t0 = p.per - p.K * W;
+    int x, k;
+    if (i < p.rem * (t0 + 1)) {
+        x = i / (t0 + 1);
+        k = i - x * (t0 + 1);
+    } else {
+        const int i2 = i - p.rem * (t0 + 1);
+        x = p.rem + i2 / max(t0, 1);
+        k = i2 - (x - p.rem) * t0;
+    }
+    return x * p.per + min(x, p.rem) + p.K * W + k;
+}
 
 // What one workgroup of a persistent launch runs: query block it, whole
 // (rec == nullptr) or part p of P of its active key tiles with its partial
@@ -833,23 +891,37 @@ __device__ __forceinline__ void attn_fwd_item(
     }
 }
 
+// Dynamic LDS of a launch: the K/V/segment-ID ring, then (masked) the
+// active-tile list of n_kvt entries and classify_tiles' metadata.
+template <int D, bool SEG>
+constexpr size_t fwd_lds(int n_kvt) {
+    size_t lds = (size_t)Tile<D>::kRingBytes;
+    if (SEG) lds += 2 * (size_t)n_kvt;
+    lds = (lds + 15) & ~(size_t)15;
+    return lds + 32 * sizeof(int);  // meta
+}
+static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(kMaxKvTiles) <= kLdsBytes,
+              "a full active-tile list must fit in the LDS beside the ring");
+
 // Workgroup p takes items p, p + G, p + 2G, ... (G = the grid size: one per
-// item with segment IDs, else a persistent grid, a multiple of 8).  At every step the G/8 workgroups of an XCD
-// then work on consecutive query blocks of one head, streaming the same K/V
-// tiles at the same time, which keeps them in that XCD's L2; with one
-// workgroup per item, CUs that pick up new items at different times drift
-// apart and each re-fetches the tiles.  With part records (recs, a persistent
-// grid only) the last round's items are split (tail_plan): workgroup p then
-// runs local units p / 8, p / 8 + G / 8, ... of its XCD.  Every workgroup's
-// unit count is fixed by G and n_wg, so all waves exit.
-template <int D, bool SEG, bool ROPE, bool SPLIT>
+// item with segment IDs, else a persistent grid, a multiple of 8).  At every
+// step the G/8 workgroups of an XCD then work on consecutive query blocks of
+// one head, streaming the same K/V tiles at the same time, which keeps them
+// in that XCD's L2; with one workgroup per item, CUs that pick up new items
+// at different times drift apart and each re-fetches the tiles.  POOL (a
+// persistent grid with part records recs and a zeroed counter ctr): the
+// workgroups of XCD x run its items up to its last T, then pull pool units
+// (pool_plan) until the counter passes the last one.  Every workgroup's own
+// item count is fixed by G and n_wg and every pull past the pool ends its
+// loop, so all waves exit.
+template <int D, bool SEG, bool ROPE, bool POOL>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
     __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
-    int n_kvt, int n_wg, Rope3DDev rope, float* __restrict__ recs) {
+    int n_kvt, int n_wg, Rope3DDev rope, float* __restrict__ recs, uint32_t* __restrict__ ctr) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    if constexpr (!SPLIT) {
+    if constexpr (!POOL) {
         for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
             attn_fwd_item<D, SEG, ROPE, false, false>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2,
                                                       n_kvt, decode_item(w, n_wg, n_qblk, H), nullptr, rope);
@@ -860,68 +932,89 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     } else {
         // The schedule is recomputed every iteration (the empty asm keeps the
         // compiler from hoisting it), so that only the iteration count is
-        // carried through the item, as in the loop above.
+        // carried through the item, as in the loop above; one call site
+        // serves both the workgroup's own items and the pool's.
+        int* slot = reinterpret_cast<int*>(smem + fwd_lds<D, SEG>(n_kvt) - sizeof(int));
         for (int s = 0;; ++s) {
-            int x = blockIdx.x % kXcds, W = gridDim.x / kXcds;
-            asm volatile("" : "+s"(x), "+s"(W));
-            const TailPlan tp = tail_plan(x, n_wg, W, true);
-            const int n_whole = tp.n_x - tp.R;
-            int j = (int)(blockIdx.x / kXcds) + s * W;
-            if (j >= tp.units()) break;
+            int x = blockIdx.x % kXcds, G = gridDim.x;
+            asm volatile("" : "+s"(x), "+s"(G));
+            const PoolPlan pp = pool_plan(n_wg, G);
+            ItemPos it;
             TailPart part{nullptr, 0, 1};
-            if (j >= n_whole) {
-                const int u = j - n_whole;
-                part = TailPart{recs + (size_t)(x * W + u) * tail_record_floats<D>(), u / tp.R, tp.P};
-                j = n_whole + u % tp.R;
+            if (s < pp.K) {
+                it = decode_item(x + kXcds * ((int)(blockIdx.x / kXcds) + s * (G / kXcds)), n_wg, n_qblk, H);
+            } else {
+                if (threadIdx.x == 0) *slot = (int)atomicAdd(ctr, 1u);
+                __syncthreads();
+                const int u = __builtin_amdgcn_readfirstlane(*slot);
+                __syncthreads();  // every wave has the slot before it is reused
+                if (u >= pp.units()) break;
+                const int n_whole = pp.n_pool - pp.R;
+                int i = u;
+                if (u >= n_whole) {
+                    const int t = u - n_whole;
+                    part = TailPart{recs + (size_t)t * tail_record_floats<D>(), t / pp.R, pp.P};
+                    i = n_whole + t % pp.R;
+                }
+                it = item_at(pool_item(pp, i, G / kXcds), n_qblk, H);
             }
             attn_fwd_item<D, SEG, ROPE, false, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt,
-                                                     decode_item(x + kXcds * j, n_wg, n_qblk, H), nullptr, rope,
-                                                     part);
+                                                     it, nullptr, rope, part);
             __syncthreads();
         }
     }
 }
 
-// Merges the P parts of every split item of XCD blockIdx.y (item
-// blockIdx.x of its R), d columns 32 blockIdx.z .. 32 blockIdx.z + 31: per
-// row, M = the largest reference maximum among the parts with valid keys,
-// L = sum_p l_p 2^(m_p - M), O = sum_p O_p 2^(m_p - M); out = O / L (bf16)
-// and lse = (M + log2 L) ln 2, or +0 / -inf when L = 0.  One thread per row;
-// parts are added in index order, so the result is deterministic.  SCHED: the
-// items are those of attn_fwd_sched_kernel (longest-first block order ord),
-// else those of attn_fwd_kernel.
+// Merges the P parts of every split item, d columns 32 blockIdx.z ..
+// 32 blockIdx.z + 31: per row, M = the largest reference maximum among the
+// parts with valid keys, L = sum_p l_p 2^(m_p - M), O = sum_p O_p 2^(m_p - M);
+// out = O / L (bf16) and lse = (M + log2 L) ln 2, or +0 / -inf when L = 0.
+// One thread per row; parts are added in index order, so the result is
+// deterministic.  SCHED: split item blockIdx.x of XCD blockIdx.y of
+// attn_fwd_sched_kernel's last round (longest-first block order ord; part p
+// in record x W + r + p R); else split item blockIdx.x of attn_fwd_kernel's
+// pool (part p in record r + p R).
 template <int D, bool SCHED>
 __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __restrict__ recs,
                                                                const int* __restrict__ ord,
                                                                __bf16* __restrict__ out, float* __restrict__ lse,
-                                                               int S, int H, int n_qblk, int n_items, int W) {
-    const int x = blockIdx.y, r = blockIdx.x, c0 = 4 * blockIdx.z;
-    const TailPlan tp = tail_plan(x, n_items, W, true);
-    if (r >= tp.R) return;
-    const int j = tp.n_x - tp.R + r;
+                                                               int S, int H, int n_qblk, int n_items, int G) {
+    const int r = blockIdx.x, c0 = 4 * blockIdx.z;
+    constexpr size_t RF = tail_record_floats<D>();
     ItemPos it;
+    const float* rec0;
+    int R, P;
     if (SCHED) {
+        const int x = blockIdx.y, W = G / kXcds;
+        const TailPlan tp = tail_plan(x, n_items, W, true);
+        if (r >= tp.R) return;
         int b, h, rr;
-        sched_coords(x, j, H, n_qblk, n_items, b, h, rr);
+        sched_coords(x, tp.n_x - tp.R + r, H, n_qblk, n_items, b, h, rr);
         const int o = ord[(int64_t)b * n_qblk + rr];
         it = ItemPos{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};
+        rec0 = recs + (size_t)(x * W + r) * RF;
+        R = tp.R;
+        P = tp.P;
     } else {
-        it = decode_item(x + kXcds * j, n_items, n_qblk, H);
+        const PoolPlan pp = pool_plan(n_items, G);
+        if (r >= pp.R) return;
+        it = item_at(pool_item(pp, pp.n_pool - pp.R + r, G / kXcds), n_qblk, H);
+        rec0 = recs + (size_t)r * RF;
+        R = pp.R;
+        P = pp.P;
     }
     const int row = threadIdx.x;
     const int qi = it.qblk * kBq + row;
     if (qi >= S) return;
-    constexpr size_t RF = tail_record_floats<D>();
-    const float* rec0 = recs + (size_t)(x * W + r) * RF;
-    const size_t pstride = (size_t)tp.R * RF;  // part p of this item: record x W + r + p R
+    const size_t pstride = (size_t)R * RF;  // part p of this item: R records further
     float M = -INFINITY;
-    for (int p = 0; p < tp.P; ++p) {
+    for (int p = 0; p < P; ++p) {
         const float* rp = rec0 + p * pstride;
         if (rp[(size_t)kBq * D + kBq + row] > 0.f) M = fmaxf(M, rp[(size_t)kBq * D + row]);
     }
     float L = 0.f;
     float acc[4][8] = {};
-    for (int p = 0; p < tp.P; ++p) {
+    for (int p = 0; p < P; ++p) {
         const float* rp = rec0 + p * pstride;
         const float l = rp[(size_t)kBq * D + kBq + row];
         if (!(l > 0.f)) continue;
@@ -958,18 +1051,6 @@ __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __re
     if (blockIdx.z == 0)
         lse[((int64_t)it.b * H + it.h) * S + qi] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
-
-// Dynamic LDS of a launch: the K/V/segment-ID ring, then (masked) the
-// active-tile list of n_kvt entries and classify_tiles' metadata.
-template <int D, bool SEG>
-constexpr size_t fwd_lds(int n_kvt) {
-    size_t lds = (size_t)Tile<D>::kRingBytes;
-    if (SEG) lds += 2 * (size_t)n_kvt;
-    lds = (lds + 15) & ~(size_t)15;
-    return lds + 32 * sizeof(int);  // meta
-}
-static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(kMaxKvTiles) <= kLdsBytes,
-              "a full active-tile list must fit in the LDS beside the ring");
 
 // ---- scheduled masked forward (caller workspace) -------------------------------------
 // With segment IDs, item lengths differ by up to ~10x (a query block of a
@@ -1166,20 +1247,27 @@ int tail_max_r(int n_items, int grid) {
     return m;
 }
 
+// Zeroes the pool counter of an unmasked persistent launch (a kernel, not a
+// memset, so that the call can be captured in a graph).
+__global__ void attn_fwd_pool_reset_kernel(uint32_t* __restrict__ ctr) {
+    if (threadIdx.x == 0) ctr[0] = 0u;
+}
+
 template <int D, bool SCHED>
 hipError_t launch_combine(const AttnArgs& a, const float* recs, const int* ord, int n_qblk, int n_items, int grid,
                           hipStream_t stream) {
-    const int max_r = tail_max_r(n_items, grid);
+    const int max_r = SCHED ? tail_max_r(n_items, grid) : pool_plan(n_items, grid).R;
     if (max_r == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, kXcds, D / 32), dim3(kBq), 0, stream,
-                       recs, ord, reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, n_qblk, n_items,
-                       grid / kXcds);
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, SCHED ? kXcds : 1, D / 32),
+                       dim3(kBq), 0, stream, recs, ord, reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, n_qblk,
+                       n_items, grid);
     return hipGetLastError();
 }
 
-// recs: part records for a split tail (unmasked calls only), or nullptr.
+// ws: a caller workspace (unmasked calls with more items than the persistent
+// grid then take the pool schedule), or nullptr.
 template <int D, bool SEG, bool ROPE>
-hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream, float* recs = nullptr) {
+hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream, const FwdWs* ws = nullptr) {
     const int n_qblk = (a.S + kBq - 1) / kBq;
     const int n_kvt = (a.S + kBk - 1) / kBk;
     const int64_t n_wg64 = (int64_t)a.B * a.H * n_qblk;
@@ -1191,26 +1279,30 @@ hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream
     // packed clips) and one workgroup per item lets the dispatcher balance them.
     const int64_t pg = persistent_workgroups();
     const int grid = SEG ? n_wg : (int)std::min<int64_t>(n_wg64, pg);
-    // A split tail needs the persistent grid (a multiple of 8) with more than
-    // one round, a record per workgroup, and a ragged last round.
-    if (SEG || n_wg64 <= pg || pg > kTailRecords || tail_max_r(n_wg, grid) == 0) recs = nullptr;
+    // The pool needs the persistent grid (a multiple of 8) with more than one
+    // round, at most one record per workgroup, and items left for it (else the
+    // static rounds are exactly the plain kernel's).
+    const bool pool = !SEG && ws != nullptr && n_wg64 > pg && pg <= kTailRecords && pool_plan(n_wg, grid).n_pool > 0;
     const auto args = std::make_tuple(reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                                       reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
                                       reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, c_log2, n_qblk, n_kvt,
-                                      n_wg, rope, recs);
-    if (recs == nullptr) {
+                                      n_wg, rope, pool ? ws->recs : nullptr, pool ? ws->ctr : nullptr);
+    if (!pool) {
         std::apply([&](auto... x) {
             hipLaunchKernelGGL((attn_fwd_kernel<D, SEG, ROPE, false>), dim3(grid), dim3(kThreads), lds, stream, x...);
         }, args);
         return hipGetLastError();
     }
     if constexpr (!SEG) {
+        hipLaunchKernelGGL(attn_fwd_pool_reset_kernel, dim3(1), dim3(64), 0, stream, ws->ctr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
         std::apply([&](auto... x) {
             hipLaunchKernelGGL((attn_fwd_kernel<D, false, ROPE, true>), dim3(grid), dim3(kThreads), lds, stream, x...);
         }, args);
-        const hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
-        return launch_combine<D, false>(a, recs, nullptr, n_qblk, n_wg, grid, stream);
+        return launch_combine<D, false>(a, ws->recs, nullptr, n_qblk, n_wg, grid, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -1273,8 +1365,8 @@ hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t
     if (a.seg_q == nullptr) {
         if (workspace == nullptr) return launch_attn_fwd(a, stream);
         const FwdWs ws = fwd_ws_layout(workspace, a.B, (a.S + kBk - 1) / kBk, (a.S + kBq - 1) / kBq);
-        return a.D == 128 ? launch_t<128, false, false>(a, none, stream, ws.recs)
-                          : launch_t<64, false, false>(a, none, stream, ws.recs);
+        return a.D == 128 ? launch_t<128, false, false>(a, none, stream, &ws)
+                          : launch_t<64, false, false>(a, none, stream, &ws);
     }
     return a.D == 128 ? launch_sched_t<128, false>(a, none, workspace, stream)
                       : launch_sched_t<64, false>(a, none, workspace, stream);
@@ -1285,8 +1377,8 @@ hipError_t launch_rope3d_attn_fwd_sched(const AttnArgs& a, const Rope3DDev& rope
     if (a.seg_q == nullptr) {
         if (workspace == nullptr) return launch_rope3d_attn_fwd(a, rope, stream);
         const FwdWs ws = fwd_ws_layout(workspace, a.B, (a.S + kBk - 1) / kBk, (a.S + kBq - 1) / kBq);
-        return a.D == 128 ? launch_t<128, false, true>(a, rope, stream, ws.recs)
-                          : launch_t<64, false, true>(a, rope, stream, ws.recs);
+        return a.D == 128 ? launch_t<128, false, true>(a, rope, stream, &ws)
+                          : launch_t<64, false, true>(a, rope, stream, &ws);
     }
     return a.D == 128 ? launch_sched_t<128, true>(a, rope, workspace, stream)
                       : launch_sched_t<64, true>(a, rope, workspace, stream);

@@ -182,10 +182,17 @@ def check_rows(out_g, lse_g, rows, out_o, lse_o, has, sens):
 
 # --- the split last round of vdx_attn_fwd_ws -----------------------------------------
 # The schedule only (which query blocks are split into parts), restated from
-# the library's documented rule: a persistent grid of G workgroups (the CU
-# count rounded down to a multiple of 8, W = G / 8 per XCD) runs the n_x items
-# of XCD x in rounds of W; when more than one round remains ragged, the last
-# R = n_x mod W items are split into P = min(8, W // R) >= 2 parts each.
+# The library's documented rules.  A persistent grid has G workgroups (the CU
+# count rounded down to a multiple of 8, W = G / 8 per XCD).
+# Masked (the scheduled kernel): XCD x runs its n_x items in rounds of W;
+# when more than one round remains ragged, the last R = n_x mod W items are
+# split into P = min(8, W // R) >= 2 parts each.
+# Unmasked with a workspace, more items than G: XCD x owns a contiguous run of
+# items (first x per + min(x, rem), per + (x < rem) of them) and runs K whole
+# rounds of it (K = per // W - 2 when per // W >= 16, else per // W); the
+# rest of every run forms a pool of n - K G items (XCD-major) pulled by every
+# workgroup, whose last R items (G // 4 for the long launches, else the
+# whole pool) are split into P = min(8, 256 // R, G // R) >= 2 parts.
 def persistent_grid():
     return torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
 
@@ -200,28 +207,56 @@ def tail_plan(x, n_items, W):
     return n_x, 0, 1
 
 
-def n_split_items(n_items, grid):
+def pool_plan(n_items, G):
+    """(per, rem, K, n_pool, R, P) of the unmasked pool schedule."""
+    W = G // 8
+    per, rem = n_items // 8, n_items % 8
+    rounds = per // W
+    long_launch = rounds >= 16
+    K = rounds - 2 if long_launch else rounds
+    n_pool = n_items - K * G
+    R = min(n_pool, G // 4) if long_launch else n_pool % G
+    P = min(8, 256 // R, G // R) if R > 0 else 1
+    if P < 2:
+        R, P = 0, 1
+    return per, rem, K, n_pool, R, P
+
+
+def pool_item(n_items, G, i):
+    """Item number of pool item i: XCD x leaves t0 + (x < rem) items after
+    its K W, t0 = per - K W, in XCD order."""
+    per, rem, K, _, _, _ = pool_plan(n_items, G)
+    W = G // 8
+    t0 = per - K * W
+    if i < rem * (t0 + 1):
+        x, k = divmod(i, t0 + 1)
+    else:
+        x, k = divmod(i - rem * (t0 + 1), t0)
+        x += rem
+    return x * per + min(x, rem) + K * W + k
+
+
+def n_split_items(n_items, grid, masked=True):
     if grid > 256:
         return 0
-    return sum(tail_plan(x, n_items, grid // 8)[1] for x in range(8))
+    if masked:
+        return sum(tail_plan(x, n_items, grid // 8)[1] for x in range(8))
+    return pool_plan(n_items, grid)[4] if n_items > grid else 0
 
 
 def split_unmasked_blocks(B, S, H, grid):
     """(b, h, block) of every 256-query block the unmasked vdx_attn_fwd_ws
-    splits: XCD x owns a contiguous run of items (item = (b H + h) n_qblk +
-    block), its local item j being run number x * per + min(x, rem) + j."""
+    splits: the last R items of the pool (item = (b H + h) n_qblk + block)."""
     n_qblk = (S + 255) // 256
     n = B * H * n_qblk
     if n <= grid or grid > 256:
         return []
-    per, rem = n // 8, n % 8
+    _, _, _, n_pool, R, _ = pool_plan(n, grid)
     out = []
-    for x in range(8):
-        n_x, R, _ = tail_plan(x, n, grid // 8)
-        for j in range(n_x - R, n_x):
-            lid = x * per + min(x, rem) + j
-            bh = lid // n_qblk
-            out.append((bh // H, bh % H, lid % n_qblk))
+    for i in range(n_pool - R, n_pool):
+        lid = pool_item(n, grid, i)
+        bh = lid // n_qblk
+        out.append((bh // H, bh % H, lid % n_qblk))
     return out
 
 

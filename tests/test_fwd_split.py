@@ -1,7 +1,9 @@
-"""The split last round of vdx_attn_fwd_ws: when a persistent launch's items
-do not fill its last round, the items of that round are divided along their
-active key tiles into parts that run side by side, and a combine kernel
-merges the parts' (O, m, l).
+"""Split items of vdx_attn_fwd_ws.  With segment IDs, when the scheduled
+persistent launch's items do not fill its last round, the items of that round
+are divided along their active key tiles into parts that run side by side;
+without them, the last items of the shared pool that ends every launch with
+more items than workgroups are divided the same way.  A combine kernel merges
+the parts' (O, m, l).
 
 Against vdx_attn_fwd (which never splits): every query block that is not
 split gives the same bits; the split ones round their probabilities against
@@ -55,12 +57,12 @@ def _check_against_oracle(x, seg_q, seg_kv, scale, o, l, blocks, per_block, seed
 
 @pytest.mark.parametrize("B,S,H,D", [(1, 8192, 9, 128), (1, 8192, 9, 64), (2, 4000, 10, 128), (1, 75600, 40, 128)])
 def test_unmasked_split_blocks(need_gpu, B, S, H, D):
-    """Unmasked: only the blocks the schedule splits differ from vdx_attn_fwd,
+    """Unmasked: only the blocks the pool splits differ from vdx_attn_fwd,
     within rounding; their rows match the oracle."""
     grid = persistent_grid()
     blocks = split_unmasked_blocks(B, S, H, grid)
     if not blocks:
-        pytest.skip(f"{B * H * ((S + 255) // 256)} items on a {grid}-workgroup grid leave no ragged round")
+        pytest.skip(f"{B * H * ((S + 255) // 256)} items on a {grid}-workgroup grid split none")
     if S == 75600:
         w = W.WORKLOADS["dit720p_large"]
         x, scale = W.make_inputs(w), w.scale
@@ -168,17 +170,17 @@ def _rope_run(x, r, seg, scale, split):
 
 @pytest.mark.parametrize("D,kind", [(128, None), (64, None), (128, "packed"), (64, "padded")])
 def test_rope_split_blocks(need_gpu, D, kind):
-    """vdx_rope3d_attn_fwd_ws with a split last round (288 items on a
-    256-workgroup grid) against vdx_rope3d_attn_fwd: at most the split
-    blocks differ, within rounding, and their rows match the oracle
-    (rotation, then attention)."""
+    """vdx_rope3d_attn_fwd_ws with split items (288 items on a 256-workgroup
+    grid: a ragged last round when masked, the pool's last items when not)
+    against vdx_rope3d_attn_fwd: at most the split blocks differ, within
+    rounding, and their rows match the oracle (rotation, then attention)."""
     import oracle
     B, S, H = 1, 8192, 9
     grid = persistent_grid()
     n_items = B * H * ((S + 255) // 256)
-    n_split = n_split_items(n_items, grid)
+    n_split = n_split_items(n_items, grid, masked=kind is not None)
     if n_split == 0:
-        pytest.skip(f"{n_items} items on a {grid}-workgroup grid leave no ragged round")
+        pytest.skip(f"{n_items} items on a {grid}-workgroup grid split none")
     x = W.make_random(B, S, H, D, seed=9000 + D)
     dims = W.ROPE_DIMS[D]
     n = (8, 16, 64)
@@ -249,7 +251,7 @@ def test_split_graph_replays(need_gpu):
 
 def test_rope_split_at_720p_equals_composed_split(need_gpu):
     """At the 720p layer's size, in the launch configuration the benchmark
-    times with --rope: vdx_rope3d_attn_fwd_ws (split last round) equals
+    times with --rope: vdx_rope3d_attn_fwd_ws (the pool and its split items) equals
     vdx_attn_fwd_ws on separately rotated q and k, bit for bit (the same split
     schedule on the same rotated bits)."""
     import spatiotemporal_attention_amd as vdx
@@ -272,7 +274,8 @@ def test_rope_split_at_720p_equals_composed_split(need_gpu):
 
 def _random_split_cases(n=10, seed=2024):
     """Seeded shapes whose item count leaves a ragged last round on a
-    256-workgroup grid (so that the call splits), with random segment kinds."""
+    256-workgroup grid (so that the masked call splits; the unmasked one,
+    with more items than workgroups, always does), with random segment kinds."""
     g = np.random.default_rng(seed)
     kinds = [None, "single", "padded", "packed", "interleaved", "singletons", "negative", "extreme"]
     cases = []
@@ -291,15 +294,15 @@ def _random_split_cases(n=10, seed=2024):
 
 @pytest.mark.parametrize("B,S,H,D,kind,seed", _random_split_cases())
 def test_random_split_shapes(need_gpu, B, S, H, D, kind, seed):
-    """Random shapes and segment layouts with a ragged last round: the split
+    """Random shapes and segment layouts with split items: the split
     call against vdx_attn_fwd (unsplit blocks bit for bit when unmasked, at
     most the split items' blocks differing when masked, split blocks within
     rounding) and rows of the differing blocks against the oracle."""
     grid = persistent_grid()
     n_items = B * H * ((S + 255) // 256)
-    n_split = n_split_items(n_items, grid)
+    n_split = n_split_items(n_items, grid, masked=kind is not None)
     if n_split == 0:
-        pytest.skip(f"{n_items} items on a {grid}-workgroup grid leave no ragged round")
+        pytest.skip(f"{n_items} items on a {grid}-workgroup grid split none")
     x = W.make_random(B, S, H, D, seed=seed % 100000)
     seg = None if kind is None else W.random_segments(B, S, seed % 99991, kind)
     scale = 1.0 / math.sqrt(D)
