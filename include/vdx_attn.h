@@ -133,21 +133,19 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
  * Every other query block gives vdx_attn_fwd's bits; a split block equals
  * them up to rounding (each part rounds its probabilities to bf16 against
  * its own running maximum), within the same accuracy bound.  Which items
- * are split:
- *   - with segment IDs: XCD x runs its n_x items in rounds of W; when
- *     n_x > W and R = n_x mod W leaves room for P = min(8, W / R) >= 2
- *     parts, the last R items of the XCD are split;
- *   - without them, when there are more items n than G (n <= G: no split):
- *     XCD x owns a contiguous run of items (the first at x per + min(x, rem),
- *     per + (x < rem) of them, per = n / 8, rem = n mod 8; items numbered
- *     (b H + h) ceil(S / 256) + block) and runs K of its rounds of W
- *     (K = per / W - 2 when per / W >= 16, else per / W); the rest of every
- *     run forms a pool of n - K G items, XCD x's after those of XCDs below
- *     x, that every workgroup pulls from once its own rounds are done, and
- *     the pool's last R items (G / 4 when per / W >= 16, else all of them)
- *     are split into P = min(8, 256 / R, G / R) parts when that is >= 2.
- *     The XCDs run at different speeds under this load, and the pool lets
- *     the faster ones take over the slower ones' last items.
+ * are split: none when there are no more items n than G.  Otherwise XCD x
+ * holds per + (x < rem) items (per = n / 8, rem = n mod 8) -- without
+ * segment IDs a contiguous run starting at item x per + min(x, rem), items
+ * numbered (b H + h) ceil(S / 256) + block; with them the XCD's
+ * longest-first list -- and runs K rounds' worth of them (K = per / W - 2
+ * when per / W >= L, else per / W; L = 16 without segment IDs, 4 with
+ * them); the rest of every XCD's items forms a pool of n - K G items (XCD
+ * x's after those of XCDs below x) that every workgroup pulls from once its
+ * own items are done, and the pool's last R items (G / 4 when
+ * per / W >= L, else all of them) are split into P = min(8, 256 / R, G / R)
+ * parts when that is >= 2.
+ * The XCDs run at different speeds under this load, and the pool lets the
+ * faster ones take over the slower ones' last items.
  *
  *   q ... scale, stream   exactly as for vdx_attn_fwd.
  *   workspace  device scratch of at least vdx_attn_fwd_workspace_size(B, S,

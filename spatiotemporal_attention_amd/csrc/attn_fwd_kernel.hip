@@ -563,36 +563,12 @@ __device__ __forceinline__ void sched_coords(int x, int j, int H, int n_qblk, in
     }
 }
 
-// ---- split tail of a persistent launch ----------------------------------------------
-// A persistent grid of G workgroups (W = G / 8 per XCD) runs the n_x items of
-// an XCD in rounds of W.  When n_x > W is not a multiple of W, the last round
-// holds R = n_x mod W items and leaves W - R workgroups idle for a whole
-// item's time.  With a workspace for partial results, each of those R items
-// is instead split along its active key tiles into P = min(8, W / R) parts
-// (when that makes at least 2), which the XCD's workgroups run side by side;
-// a combine kernel then merges the parts of each item.  Local index j of an XCD (its j-th item, or unit
-// once split): j < n_x - R is the whole item j; otherwise u = j - (n_x - R)
-// is part u / R of item n_x - R + u % R, with its partial results in record
-// x * W + u.  An XCD runs n_x - R + R * P units.
+// ---- split items of a persistent launch --------------------------------------------
+// With a workspace for partial results, an item can be split along its active
+// key tiles into P parts that run side by side; a combine kernel then merges
+// the parts of each split item.  Which items are split is set by tail_plan.
 constexpr int kTailMaxParts = 8;
 constexpr int kTailRecords = 256;  // part records a workspace holds (one per workgroup of a 256-CU grid)
-struct TailPlan {
-    int n_x;    // items of the XCD
-    int R, P;   // split items and parts per item (R = 0: no split)
-    __host__ __device__ int units() const { return n_x - R + R * P; }
-};
-__host__ __device__ inline TailPlan tail_plan(int x, int n_items, int W, bool on) {
-    TailPlan t{n_items / kXcds + (x < n_items % kXcds ? 1 : 0), 0, 1};
-    if (on && t.n_x > W) {
-        const int R = t.n_x % W;
-        const int P = R > 0 ? min(kTailMaxParts, W / R) : 1;
-        if (P >= 2) {
-            t.R = R;
-            t.P = P;
-        }
-    }
-    return t;
-}
 // Floats of one part record: the unnormalised O^T of the block's kBq rows as
 // [D / 8][kBq][8] (row-contiguous 8-float chunks of d), then the reference
 // maximum m (log2 units of the scaled score) and the key sum l of every row
@@ -601,27 +577,60 @@ template <int D>
 constexpr size_t tail_record_floats() { return (size_t)kBq * D + 2 * kBq; }
 static_assert(tail_record_floats<128>() % 64 == 0 && tail_record_floats<64>() % 64 == 0, "records stay 256-byte aligned");
 
-// Unmasked persistent schedule with a shared pool.  XCD x owns a contiguous
-// run of items (the first at x per + min(x, rem), per + (x < rem) of them,
-// per = n / 8, rem = n mod 8) and runs K whole rounds of them, W = G / 8 at
-// a time, in step; the rest of every XCD's run forms a pool of n - K G
-// items, XCD-major (the workgroups that reach it together still stream one
-// head), that every workgroup pulls from through one counter once its own
-// rounds are done.  Long launches keep kPoolRounds rounds per XCD for the
-// pool, because the XCDs do not run the kernel at the same speed (per-item
-// timestamps put the odd-numbered ones 4-5% behind the even ones on two
-// devices, all through the launch) and equal static shares would leave the
-// faster ones idle at the end; the pool's last R = G / 4 items are split
-// into parts along their key tiles and pulled after the whole ones, so the
-// launch ends within about a part.  Shorter launches run every whole round
-// statically (their imbalance is too short to pay for the merge) and pool
-// only the remainder, which is split into P = min(8, G / R) parts when that
-// is at least 2, so that it fills one last round.
+// Persistent schedules.  XCD x holds n_x = per + (x < rem) items
+// (per = n / 8, rem = n mod 8; unmasked a contiguous run starting at item
+// x per + min(x, rem), masked the XCD's longest-first list of sched_coords),
+// handed out by the XCD's own counter, so that its W = G / 8 workgroups take
+// neighbouring items of one head together and share its K/V in their L2.
+// The XCDs do not run the kernels at the same speed (per-item timestamps put
+// the odd-numbered ones 4-5% behind the even ones on two devices, all
+// through the launch), and equal shares would leave the faster ones idle at
+// the end.  So that the faster XCDs take over the slower ones' last items:
+//   - unmasked (tail_plan, claim_unit): work stealing.  A workgroup whose own
+//     counter has run out takes units from the other XCDs' counters (x + 1,
+//     x + 2, ... in turn) until every counter has, each thief an item of its
+//     victim's current head.  The last R items of each XCD are split into
+//     P = min(8, W / R) parts along their key tiles (when that makes at least
+//     2), after its n_x - R whole ones: R = W / 4 for a long launch
+//     (n_x / W >= kLongRounds), else R = n_x mod W, the ragged last round,
+//     which the parts then fill.  Unit u of XCD x: u < n_x - R is whole item
+//     u; otherwise t = u - (n_x - R) is part t / R of item n_x - R + t % R,
+//     with its partial results in record x W + t.  The shared pool below,
+//     tried here too, balanced as well but cost 50 GB more L2 misses per
+//     720p call, its workgroups leaving their XCD's head for two rounds;
+//   - masked (pool_plan, pool_sched_item): a shared pool.  XCD x's counter
+//     hands out its first K W list positions (K = n_x / W - kPoolRounds for a
+//     long launch, n_x / W >= kLongRoundsSched, else n_x / W); the rest of
+//     every XCD's list forms a pool of n - K G items, XCD-major, pulled
+//     through a ninth counter by any workgroup whose own XCD is done, and the
+//     pool's last R items (G / 4 for a long launch, else all of them) are
+//     split into P = min(8, 256 / R, G / R) parts when that is >= 2, with
+//     part t in record t.  Work stealing measured no faster than no balancing
+//     here (the slower XCDs' remaining items were mostly already running when
+//     the thieves came), the pool 2.4-2.9% faster.
+constexpr int kLongRounds = 16;      // unmasked
+constexpr int kLongRoundsSched = 4;  // masked scheduled kernel
 constexpr int kPoolRounds = 2;
-constexpr int kPoolMinRounds = 16;
+struct TailPlan {
+    int n_x;    // items of the XCD
+    int R, P;   // split items and parts per item (R = 0: no split)
+    __host__ __device__ int units() const { return n_x - R + R * P; }
+};
+__host__ __device__ inline TailPlan tail_plan(int x, int n_items, int W, int long_rounds) {
+    TailPlan t{n_items / kXcds + (x < n_items % kXcds ? 1 : 0), 0, 1};
+    if (t.n_x > W) {
+        const int R = t.n_x / W >= long_rounds ? W / 4 : t.n_x % W;
+        const int P = R > 0 ? min(kTailMaxParts, W / R) : 1;
+        if (P >= 2) {
+            t.R = R;
+            t.P = P;
+        }
+    }
+    return t;
+}
 struct PoolPlan {
-    int per, rem;  // items of XCD x: per + (x < rem), starting at item x per + min(x, rem)
-    int K;         // whole static rounds of every XCD
+    int per, rem;  // items of XCD x: per + (x < rem)
+    int K;         // rounds of every XCD's own items
     int n_pool;    // n - K G
     int R, P;      // pool items split (the last R) and parts per split item (R = 0: none)
     __host__ __device__ int units() const { return n_pool - R + R * P; }
@@ -630,7 +639,7 @@ __host__ __device__ inline PoolPlan pool_plan(int n_items, int G) {
     const int W = G / kXcds;
     PoolPlan p{n_items / kXcds, n_items % kXcds, 0, 0, 0, 1};
     const int rounds = p.per / W;
-    const bool long_launch = rounds >= kPoolMinRounds;
+    const bool long_launch = rounds >= kLongRoundsSched;
     p.K = long_launch ? rounds - kPoolRounds : rounds;
     p.n_pool = n_items - p.K * G;
     const int R = long_launch ? min(p.n_pool, G / 4) : p.n_pool % G;
@@ -641,11 +650,14 @@ __host__ __device__ inline PoolPlan pool_plan(int n_items, int G) {
     }
     return p;
 }
-// Pool item i -> its item number (the b, h, block order of decode_item):
-// XCD x leaves t0 + (x < rem) items after its K W, t0 = per - K W.
-__host__ __device__ inline int pool_item(const PoolPlan& p, int i, int W) {
+// Pool item i -> XCD x and list position j: XCD-major (XCD x's t0 + (x < rem)
+// pool items, t0 = per - K W, after those of the XCDs below it), so that the
+// workgroups that reach the pool together take one XCD's items, one head's
+// K/V in their L2 (interleaving the XCDs' items measured the same time and
+// 40-60% more L2 misses).
+__host__ __device__ inline void pool_sched_item(const PoolPlan& p, int i, int W, int& x, int& j) {
     const int t0 = p.per - p.K * W;
-    int x, k;
+    int k;
     if (i < p.rem * (t0 + 1)) {
         x = i / (t0 + 1);
         k = i - x * (t0 + 1);
@@ -654,7 +666,26 @@ __host__ __device__ inline int pool_item(const PoolPlan& p, int i, int W) {
         x = p.rem + i2 / max(t0, 1);
         k = i2 - (x - p.rem) * t0;
     }
-    return x * p.per + min(x, p.rem) + p.K * W + k;
+    j = p.K * W + k;
+}
+// Claims the next unit for a workgroup of XCD xcd: from its own counter,
+// then (once that has run out) from the others' in turn; v counts the
+// counters found empty, so each is skipped afterwards.  Returns false when
+// every counter has run out.  The slot in the LDS carries thread 0's
+// claim to the whole workgroup; the barriers keep it from being reused
+// early.  Unit u of XCD x is returned.
+template <class Units>
+__device__ __forceinline__ bool claim_unit(uint32_t* __restrict__ ctr, int* slot, int xcd, int& v, int& x, int& u,
+                                           Units units) {
+    for (; v < kXcds; ++v) {
+        x = (xcd + v) % kXcds;
+        if (threadIdx.x == 0) *slot = (int)atomicAdd(ctr + x, 1u);
+        __syncthreads();
+        u = __builtin_amdgcn_readfirstlane(*slot);
+        __syncthreads();  // every wave has the slot before it is reused
+        if (u < units(x)) return true;
+    }
+    return false;
 }
 
 // What one workgroup of a persistent launch runs: query block it, whole
@@ -908,20 +939,19 @@ static_assert(fwd_lds<128, true>(kMaxKvTiles) <= kLdsBytes && fwd_lds<64, true>(
 // step the G/8 workgroups of an XCD then work on consecutive query blocks of
 // one head, streaming the same K/V tiles at the same time, which keeps them
 // in that XCD's L2; with one workgroup per item, CUs that pick up new items
-// at different times drift apart and each re-fetches the tiles.  POOL (a
-// persistent grid with part records recs and a zeroed counter ctr): the
-// workgroups of XCD x run its items up to its last T, then pull pool units
-// (pool_plan) until the counter passes the last one.  Every workgroup's own
-// item count is fixed by G and n_wg and every pull past the pool ends its
-// loop, so all waves exit.
-template <int D, bool SEG, bool ROPE, bool POOL>
+// at different times drift apart and each re-fetches the tiles.  SPLIT (a
+// persistent grid with part records recs and eight zeroed counters ctr): the
+// same items, claimed through the counters with work stealing and the last
+// ones split (tail_plan with kLongRounds, claim_unit); every claim past the
+// last counter ends the loop, so all waves exit.
+template <int D, bool SEG, bool ROPE, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
     __bf16* __restrict__ out, float* __restrict__ lse, int S, int H, float c_log2, int n_qblk,
     int n_kvt, int n_wg, Rope3DDev rope, float* __restrict__ recs, uint32_t* __restrict__ ctr) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    if constexpr (!POOL) {
+    if constexpr (!SPLIT) {
         for (int w = blockIdx.x; w < n_wg; w += gridDim.x) {
             attn_fwd_item<D, SEG, ROPE, false, false>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2,
                                                       n_kvt, decode_item(w, n_wg, n_qblk, H), nullptr, rope);
@@ -931,35 +961,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
         }
     } else {
         // The schedule is recomputed every iteration (the empty asm keeps the
-        // compiler from hoisting it), so that only the iteration count is
-        // carried through the item, as in the loop above; one call site
-        // serves both the workgroup's own items and the pool's.
+        // compiler from hoisting it), so that only the counter position v is
+        // carried through the item, as the loop above carries w.
         int* slot = reinterpret_cast<int*>(smem + fwd_lds<D, SEG>(n_kvt) - sizeof(int));
-        for (int s = 0;; ++s) {
-            int x = blockIdx.x % kXcds, G = gridDim.x;
-            asm volatile("" : "+s"(x), "+s"(G));
-            const PoolPlan pp = pool_plan(n_wg, G);
-            ItemPos it;
+        int vv = 0;
+        for (;;) {
+            int xcd = blockIdx.x % kXcds, G = gridDim.x;
+            asm volatile("" : "+s"(xcd), "+s"(G));
+            const int W = G / kXcds;
+            int x, u;
+            if (!claim_unit(ctr, slot, xcd, vv, x, u,
+                            [&](int y) { return tail_plan(y, n_wg, W, kLongRounds).units(); }))
+                break;
+            const TailPlan tp = tail_plan(x, n_wg, W, kLongRounds);
+            const int n_whole = tp.n_x - tp.R;
+            int j = u;
             TailPart part{nullptr, 0, 1};
-            if (s < pp.K) {
-                it = decode_item(x + kXcds * ((int)(blockIdx.x / kXcds) + s * (G / kXcds)), n_wg, n_qblk, H);
-            } else {
-                if (threadIdx.x == 0) *slot = (int)atomicAdd(ctr, 1u);
-                __syncthreads();
-                const int u = __builtin_amdgcn_readfirstlane(*slot);
-                __syncthreads();  // every wave has the slot before it is reused
-                if (u >= pp.units()) break;
-                const int n_whole = pp.n_pool - pp.R;
-                int i = u;
-                if (u >= n_whole) {
-                    const int t = u - n_whole;
-                    part = TailPart{recs + (size_t)t * tail_record_floats<D>(), t / pp.R, pp.P};
-                    i = n_whole + t % pp.R;
-                }
-                it = item_at(pool_item(pp, i, G / kXcds), n_qblk, H);
+            if (u >= n_whole) {
+                const int t = u - n_whole;
+                part = TailPart{recs + (size_t)(x * W + t) * tail_record_floats<D>(), t / tp.R, tp.P};
+                j = n_whole + t % tp.R;
             }
             attn_fwd_item<D, SEG, ROPE, false, true>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt,
-                                                     it, nullptr, rope, part);
+                                                     decode_item(x + kXcds * j, n_wg, n_qblk, H), nullptr, rope,
+                                                     part);
             __syncthreads();
         }
     }
@@ -970,38 +995,40 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 // parts with valid keys, L = sum_p l_p 2^(m_p - M), O = sum_p O_p 2^(m_p - M);
 // out = O / L (bf16) and lse = (M + log2 L) ln 2, or +0 / -inf when L = 0.
 // One thread per row; parts are added in index order, so the result is
-// deterministic.  SCHED: split item blockIdx.x of XCD blockIdx.y of
-// attn_fwd_sched_kernel's last round (longest-first block order ord; part p
-// in record x W + r + p R); else split item blockIdx.x of attn_fwd_kernel's
-// pool (part p in record r + p R).
+// deterministic.  SCHED: split item r = blockIdx.x of attn_fwd_sched_kernel's
+// pool (pool item n_pool - R + r, longest-first block order ord, part p in
+// record r + p R); else split item r of XCD x = blockIdx.y of
+// attn_fwd_kernel (item n_x - R + r of the XCD, part p in record
+// x W + r + p R).
 template <int D, bool SCHED>
 __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __restrict__ recs,
                                                                const int* __restrict__ ord,
                                                                __bf16* __restrict__ out, float* __restrict__ lse,
                                                                int S, int H, int n_qblk, int n_items, int G) {
-    const int r = blockIdx.x, c0 = 4 * blockIdx.z;
+    const int r = blockIdx.x, c0 = 4 * blockIdx.z, W = G / kXcds;
     constexpr size_t RF = tail_record_floats<D>();
     ItemPos it;
     const float* rec0;
     int R, P;
     if (SCHED) {
-        const int x = blockIdx.y, W = G / kXcds;
-        const TailPlan tp = tail_plan(x, n_items, W, true);
-        if (r >= tp.R) return;
-        int b, h, rr;
-        sched_coords(x, tp.n_x - tp.R + r, H, n_qblk, n_items, b, h, rr);
-        const int o = ord[(int64_t)b * n_qblk + rr];
-        it = ItemPos{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};
-        rec0 = recs + (size_t)(x * W + r) * RF;
-        R = tp.R;
-        P = tp.P;
-    } else {
         const PoolPlan pp = pool_plan(n_items, G);
         if (r >= pp.R) return;
-        it = item_at(pool_item(pp, pp.n_pool - pp.R + r, G / kXcds), n_qblk, H);
+        int x, j, b, h, rr;
+        pool_sched_item(pp, pp.n_pool - pp.R + r, W, x, j);
+        sched_coords(x, j, H, n_qblk, n_items, b, h, rr);
+        const int o = ord[(int64_t)b * n_qblk + rr];
+        it = ItemPos{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};
         rec0 = recs + (size_t)r * RF;
         R = pp.R;
         P = pp.P;
+    } else {
+        const int x = blockIdx.y;
+        const TailPlan tp = tail_plan(x, n_items, W, kLongRounds);
+        if (r >= tp.R) return;
+        it = decode_item(x + kXcds * (tp.n_x - tp.R + r), n_items, n_qblk, H);
+        rec0 = recs + (size_t)(x * W + r) * RF;
+        R = tp.R;
+        P = tp.P;
     }
     const int row = threadIdx.x;
     const int qi = it.qblk * kBq + row;
@@ -1057,19 +1084,20 @@ __global__ __launch_bounds__(kBq) void attn_fwd_combine_kernel(const float* __re
 // short clip skips most key tiles), and the hardware dispatcher, which hands
 // workgroups to the XCDs round-robin in index order, leaves CUs idle behind a
 // long item.  The scheduled path instead runs a persistent grid whose
-// workgroups pull items from eight work counters (one per XCD) in
-// longest-first order, and classifies key tiles from per-tile summaries
-// instead of every workgroup re-reading all of the batch's key IDs.
-// Workspace: eight counters (256 bytes), then int4 tile summaries
-// [B][n_kvt], active-tile counts [B][n_qblk], the longest-first block orders
-// [B][n_qblk] and kTailRecords part records of the split tail (sized for
-// D = 128).  An unmasked call uses only the part records.
+// workgroups pull items from eight work counters (one per XCD, with work
+// stealing) in longest-first order, and classifies key tiles from per-tile
+// summaries instead of every workgroup re-reading all of the batch's key
+// IDs.  Workspace: the eight work counters (256 bytes), then int4 tile
+// summaries [B][n_kvt], active-tile counts [B][n_qblk], the longest-first
+// block orders [B][n_qblk] and kTailRecords part records of split items
+// (sized for D = 128).  An unmasked call uses only the counters and the part
+// records.
 struct FwdWs {
     uint32_t* ctr;
     int4* tsum;
     int* cnt;
     int* ord;
-    float* recs;  // kTailRecords part records of the split tail
+    float* recs;  // kTailRecords part records of split items
 };
 __host__ __device__ inline size_t fwd_ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 FwdWs fwd_ws_layout(void* ws, int64_t B, int64_t n_kvt, int64_t n_qblk) {
@@ -1094,7 +1122,7 @@ FwdWs fwd_ws_layout(void* ws, int64_t B, int64_t n_kvt, int64_t n_qblk) {
 __global__ __launch_bounds__(256) void attn_fwd_tilesum_kernel(const int32_t* __restrict__ seg_kv, int S,
                                                                int n_kvt, int64_t n_all, int4* __restrict__ tsum,
                                                                uint32_t* __restrict__ ctr) {
-    if (blockIdx.x == 0 && threadIdx.x < kXcds) ctr[threadIdx.x] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x <= kXcds) ctr[threadIdx.x] = 0u;  // eight XCD counters and the pool's
     const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int sub = threadIdx.x & 15;
     int mn = INT32_MAX, mx = INT32_MIN, fl = 0;
@@ -1177,12 +1205,16 @@ __global__ __launch_bounds__(kFwdRankThreads) void attn_fwd_rank_kernel(const in
 // workgroups stream one head's K/V at a time; otherwise every eighth item of
 // the list that walks the batches, then the blocks longest first, then the
 // heads.  Either way the XCD takes an eighth of the work, longest first within
-// a head, and its workgroups stay busy until its list runs out.  Every item is
-// pulled exactly once (each counter hands out 0, 1, 2, ...), and a workgroup
-// exits at the first slot past the list, so every wave exits.  Requires a grid
+// a head, and its workgroups stay busy until its list runs out.  POOL
+// (pool_plan): an XCD's counter hands out only its first K W list positions;
+// the rest of every XCD's list forms a pool (pool_sched_item) pulled through
+// a ninth counter by any workgroup whose own XCD is done, its last R items
+// split into parts with records in the workspace.  Every item is pulled
+// exactly once (each counter hands out 0, 1, 2, ...), and a workgroup exits
+// at the first slot past what is left, so every wave exits.  Requires a grid
 // that is a multiple of 8.  ROPE: the queries are rotated in the item
 // prologue, as in attn_fwd_kernel.
-template <int D, bool ROPE, bool SPLIT>
+template <int D, bool ROPE, bool POOL>
 __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_kv,
@@ -1190,30 +1222,47 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_sched_kernel(
     int n_kvt, int n_items, FwdWs ws, Rope3DDev rope) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     int* slot = reinterpret_cast<int*>(smem + fwd_lds<D, true>(n_kvt) - sizeof(int));
+    bool own = true;  // the XCD's own counter may still hold items
     for (;;) {
         // Recomputed every iteration (see attn_fwd_kernel), so that nothing
-        // but the kernel arguments is carried through an item.
-        int xcd = blockIdx.x % kXcds, W = gridDim.x / kXcds;
-        asm volatile("" : "+s"(xcd), "+s"(W));
-        const TailPlan tp = tail_plan(xcd, n_items, W, SPLIT);
-        const int n_whole = tp.n_x - tp.R;
-        if (threadIdx.x == 0) *slot = (int)atomicAdd(ws.ctr + xcd, 1u);
-        __syncthreads();
-        int j = __builtin_amdgcn_readfirstlane(*slot);
-        __syncthreads();  // every wave has the slot before it is reused
-        if (j >= tp.units()) break;
+        // but the kernel arguments and the flag is carried through an item.
+        int xcd = blockIdx.x % kXcds, G = gridDim.x;
+        asm volatile("" : "+s"(xcd), "+s"(G));
+        const int W = G / kXcds;
+        const PoolPlan pp = pool_plan(n_items, G);
+        int x = xcd, j = 0;
         TailPart part{nullptr, 0, 1};
-        if (SPLIT && j >= n_whole) {
-            const int u = j - n_whole;
-            part = TailPart{ws.recs + (size_t)(xcd * W + u) * tail_record_floats<D>(), u / tp.R, tp.P};
-            j = n_whole + u % tp.R;
+        if (own) {
+            if (threadIdx.x == 0) *slot = (int)atomicAdd(ws.ctr + xcd, 1u);
+            __syncthreads();
+            j = __builtin_amdgcn_readfirstlane(*slot);
+            __syncthreads();  // every wave has the slot before it is reused
+            if (j >= (POOL ? pp.K * W : pp.per + (xcd < pp.rem ? 1 : 0))) {
+                if (!POOL) break;
+                own = false;
+            }
+        }
+        if (POOL && !own) {
+            if (threadIdx.x == 0) *slot = (int)atomicAdd(ws.ctr + kXcds, 1u);
+            __syncthreads();
+            const int u = __builtin_amdgcn_readfirstlane(*slot);
+            __syncthreads();
+            if (u >= pp.units()) break;
+            const int n_whole = pp.n_pool - pp.R;
+            int i = u;
+            if (u >= n_whole) {
+                const int t = u - n_whole;
+                part = TailPart{ws.recs + (size_t)t * tail_record_floats<D>(), t / pp.R, pp.P};
+                i = n_whole + t % pp.R;
+            }
+            pool_sched_item(pp, i, W, x, j);
         }
         int b, h, r;
-        sched_coords(xcd, j, H, n_qblk, n_items, b, h, r);
+        sched_coords(x, j, H, n_qblk, n_items, b, h, r);
         const int o = ws.ord[(int64_t)b * n_qblk + r];
         const ItemPos it{b, h, (unsigned)o < (unsigned)n_qblk ? o : 0};  // a permutation; the test keeps it in range
-        attn_fwd_item<D, true, ROPE, true, SPLIT>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
-                                                  ws.tsum + (int64_t)b * n_kvt, rope, part);
+        attn_fwd_item<D, true, ROPE, true, POOL>(smem, q, k, v, seg_q, seg_kv, out, lse, S, H, c_log2, n_kvt, it,
+                                                 ws.tsum + (int64_t)b * n_kvt, rope, part);
         __syncthreads();
     }
 }
@@ -1241,31 +1290,31 @@ int64_t persistent_workgroups() {
 
 // Largest split-item count R over the XCDs of a persistent grid (0: no item
 // is split, and no combine launch is needed).
-int tail_max_r(int n_items, int grid) {
+int tail_max_r(int n_items, int grid, int long_rounds) {
     int m = 0;
-    for (int x = 0; x < kXcds; ++x) m = std::max(m, tail_plan(x, n_items, grid / kXcds, true).R);
+    for (int x = 0; x < kXcds; ++x) m = std::max(m, tail_plan(x, n_items, grid / kXcds, long_rounds).R);
     return m;
 }
 
-// Zeroes the pool counter of an unmasked persistent launch (a kernel, not a
-// memset, so that the call can be captured in a graph).
-__global__ void attn_fwd_pool_reset_kernel(uint32_t* __restrict__ ctr) {
-    if (threadIdx.x == 0) ctr[0] = 0u;
+// Zeroes the eight work counters of an unmasked persistent launch (a
+// kernel, not a memset, so that the call can be captured in a graph).
+__global__ void attn_fwd_ctr_reset_kernel(uint32_t* __restrict__ ctr) {
+    if (threadIdx.x < kXcds) ctr[threadIdx.x] = 0u;
 }
 
 template <int D, bool SCHED>
 hipError_t launch_combine(const AttnArgs& a, const float* recs, const int* ord, int n_qblk, int n_items, int grid,
                           hipStream_t stream) {
-    const int max_r = SCHED ? tail_max_r(n_items, grid) : pool_plan(n_items, grid).R;
+    const int max_r = SCHED ? pool_plan(n_items, grid).R : tail_max_r(n_items, grid, kLongRounds);
     if (max_r == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, SCHED ? kXcds : 1, D / 32),
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<D, SCHED>), dim3((unsigned)max_r, SCHED ? 1 : kXcds, D / 32),
                        dim3(kBq), 0, stream, recs, ord, reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, n_qblk,
                        n_items, grid);
     return hipGetLastError();
 }
 
 // ws: a caller workspace (unmasked calls with more items than the persistent
-// grid then take the pool schedule), or nullptr.
+// grid then take the stealing schedule), or nullptr.
 template <int D, bool SEG, bool ROPE>
 hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream, const FwdWs* ws = nullptr) {
     const int n_qblk = (a.S + kBq - 1) / kBq;
@@ -1279,22 +1328,24 @@ hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream
     // packed clips) and one workgroup per item lets the dispatcher balance them.
     const int64_t pg = persistent_workgroups();
     const int grid = SEG ? n_wg : (int)std::min<int64_t>(n_wg64, pg);
-    // The pool needs the persistent grid (a multiple of 8) with more than one
-    // round, at most one record per workgroup, and items left for it (else the
-    // static rounds are exactly the plain kernel's).
-    const bool pool = !SEG && ws != nullptr && n_wg64 > pg && pg <= kTailRecords && pool_plan(n_wg, grid).n_pool > 0;
+    // Work stealing and split items need the persistent grid (a multiple of
+    // 8) with more than one round, at most one record per workgroup, and a
+    // long launch or a ragged last round (a short launch of whole rounds runs
+    // the plain kernel: stealing measured 0.5% slower there).
+    const bool steal = !SEG && ws != nullptr && n_wg64 > pg && pg <= kTailRecords &&
+                       tail_max_r(n_wg, grid, kLongRounds) > 0;
     const auto args = std::make_tuple(reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                                       reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
                                       reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, c_log2, n_qblk, n_kvt,
-                                      n_wg, rope, pool ? ws->recs : nullptr, pool ? ws->ctr : nullptr);
-    if (!pool) {
+                                      n_wg, rope, steal ? ws->recs : nullptr, steal ? ws->ctr : nullptr);
+    if (!steal) {
         std::apply([&](auto... x) {
             hipLaunchKernelGGL((attn_fwd_kernel<D, SEG, ROPE, false>), dim3(grid), dim3(kThreads), lds, stream, x...);
         }, args);
         return hipGetLastError();
     }
     if constexpr (!SEG) {
-        hipLaunchKernelGGL(attn_fwd_pool_reset_kernel, dim3(1), dim3(64), 0, stream, ws->ctr);
+        hipLaunchKernelGGL(attn_fwd_ctr_reset_kernel, dim3(1), dim3(64), 0, stream, ws->ctr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         std::apply([&](auto... x) {
@@ -1330,7 +1381,9 @@ hipError_t launch_sched_t(const AttnArgs& a, const Rope3DDev& rope, void* worksp
     if (e != hipSuccess) return e;
     // A multiple of 8 (every XCD counter has workgroups), at most one per CU.
     const int64_t grid = std::min<int64_t>(persistent_workgroups(), (n_items64 + kXcds - 1) / kXcds * kXcds);
-    const bool split = grid <= kTailRecords && tail_max_r((int)n_items64, (int)grid) > 0;
+    // The pool needs more items than workgroups and at most one part record
+    // per workgroup (with exactly whole rounds and a short launch it is empty).
+    const bool split = grid <= kTailRecords && n_items64 > grid && pool_plan((int)n_items64, (int)grid).n_pool > 0;
     const auto args = std::make_tuple(reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),
                                       reinterpret_cast<const __bf16*>(a.v), a.seg_q, a.seg_kv,
                                       reinterpret_cast<__bf16*>(a.out), a.lse, a.S, a.H, a.scale * kLog2e, n_qblk,

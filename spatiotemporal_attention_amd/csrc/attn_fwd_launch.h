@@ -35,11 +35,11 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 
 // The forward with a caller workspace of attn_fwd_workspace_bytes(B, S)
 // bytes (16-byte aligned): masked calls run on a persistent grid with per-XCD
-// work counters and longest-first block order, and split a ragged last round
-// along the keys; unmasked calls with more items than the persistent grid end
-// with a pool of items shared by all XCDs, whose last items are split.  The
-// parts are merged by a last kernel.  An unmasked call with a NULL workspace
-// is launch_attn_fwd.
+// work counters and longest-first block order, ending with a pool of items
+// shared by all XCDs; unmasked calls with more items than the persistent grid
+// claim items through per-XCD counters with work stealing.  Either way the
+// last items are split along the keys and merged by a last kernel.  An
+// unmasked call with a NULL workspace is launch_attn_fwd.
 hipError_t launch_attn_fwd_sched(const AttnArgs& a, void* workspace, hipStream_t stream);
 
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t S);

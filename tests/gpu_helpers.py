@@ -183,24 +183,25 @@ def check_rows(out_g, lse_g, rows, out_o, lse_o, has, sens):
 # --- the split last round of vdx_attn_fwd_ws -----------------------------------------
 # The schedule only (which query blocks are split into parts), restated from
 # The library's documented rules.  A persistent grid has G workgroups (the CU
-# count rounded down to a multiple of 8, W = G / 8 per XCD).
-# Masked (the scheduled kernel): XCD x runs its n_x items in rounds of W;
-# when more than one round remains ragged, the last R = n_x mod W items are
-# split into P = min(8, W // R) >= 2 parts each.
-# Unmasked with a workspace, more items than G: XCD x owns a contiguous run of
-# items (first x per + min(x, rem), per + (x < rem) of them) and runs K whole
-# rounds of it (K = per // W - 2 when per // W >= 16, else per // W); the
-# rest of every run forms a pool of n - K G items (XCD-major) pulled by every
-# workgroup, whose last R items (G // 4 for the long launches, else the
-# whole pool) are split into P = min(8, 256 // R, G // R) >= 2 parts.
+# count rounded down to a multiple of 8, W = G / 8 per XCD); with n > G items
+# XCD x holds n_x = per + (x < rem) of them (per = n // 8, rem = n % 8).
+# Unmasked (work stealing): XCD x's items are a contiguous run starting at
+# item x per + min(x, rem) (item = (b H + h) n_qblk + block), and when
+# n_x > W its last R are split into P = min(8, W // R) >= 2 parts, R = W // 4
+# when n_x // W >= 16, else R = n_x % W.  Masked (shared pool): each XCD runs
+# K rounds of its own items (K = per // W - 2 when per // W >= 4, else
+# per // W); the rest forms a pool of n - K G items whose last R (G // 4 for
+# the long launches, else all of them) are split into
+# P = min(8, 256 // R, G // R) >= 2 parts.
 def persistent_grid():
     return torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
 
 
 def tail_plan(x, n_items, W):
+    """(n_x, R, P) of XCD x, unmasked."""
     n_x = n_items // 8 + (1 if x < n_items % 8 else 0)
     if n_x > W:
-        R = n_x % W
+        R = W // 4 if n_x // W >= 16 else n_x % W
         P = min(8, W // R) if R else 1
         if P >= 2:
             return n_x, R, P
@@ -208,11 +209,11 @@ def tail_plan(x, n_items, W):
 
 
 def pool_plan(n_items, G):
-    """(per, rem, K, n_pool, R, P) of the unmasked pool schedule."""
+    """(per, rem, K, n_pool, R, P) of the masked pool."""
     W = G // 8
     per, rem = n_items // 8, n_items % 8
     rounds = per // W
-    long_launch = rounds >= 16
+    long_launch = rounds >= 4
     K = rounds - 2 if long_launch else rounds
     n_pool = n_items - K * G
     R = min(n_pool, G // 4) if long_launch else n_pool % G
@@ -222,41 +223,30 @@ def pool_plan(n_items, G):
     return per, rem, K, n_pool, R, P
 
 
-def pool_item(n_items, G, i):
-    """Item number of pool item i: XCD x leaves t0 + (x < rem) items after
-    its K W, t0 = per - K W, in XCD order."""
-    per, rem, K, _, _, _ = pool_plan(n_items, G)
-    W = G // 8
-    t0 = per - K * W
-    if i < rem * (t0 + 1):
-        x, k = divmod(i, t0 + 1)
-    else:
-        x, k = divmod(i - rem * (t0 + 1), t0)
-        x += rem
-    return x * per + min(x, rem) + K * W + k
-
-
 def n_split_items(n_items, grid, masked=True):
-    if grid > 256:
+    if grid > 256 or n_items <= grid:
         return 0
     if masked:
-        return sum(tail_plan(x, n_items, grid // 8)[1] for x in range(8))
-    return pool_plan(n_items, grid)[4] if n_items > grid else 0
+        return pool_plan(n_items, grid)[4]
+    return sum(tail_plan(x, n_items, grid // 8)[1] for x in range(8))
 
 
 def split_unmasked_blocks(B, S, H, grid):
     """(b, h, block) of every 256-query block the unmasked vdx_attn_fwd_ws
-    splits: the last R items of the pool (item = (b H + h) n_qblk + block)."""
+    splits: XCD x owns a contiguous run of items, its local item j being
+    item x per + min(x, rem) + j, and splits its last R."""
     n_qblk = (S + 255) // 256
     n = B * H * n_qblk
     if n <= grid or grid > 256:
         return []
-    _, _, _, n_pool, R, _ = pool_plan(n, grid)
+    per, rem = n // 8, n % 8
     out = []
-    for i in range(n_pool - R, n_pool):
-        lid = pool_item(n, grid, i)
-        bh = lid // n_qblk
-        out.append((bh // H, bh % H, lid % n_qblk))
+    for x in range(8):
+        n_x, R, _ = tail_plan(x, n, grid // 8)
+        for j in range(n_x - R, n_x):
+            lid = x * per + min(x, rem) + j
+            bh = lid // n_qblk
+            out.append((bh // H, bh % H, lid % n_qblk))
     return out
 
 
@@ -283,14 +273,18 @@ def differing_blocks(o1, l1, o2, l2):
 def assert_split_close(o1, l1, o2, l2):
     """A split block against the same block computed whole.  The parts round
     their probabilities to bf16 against their own reference maxima, so the
-    outputs differ at the level of that rounding (each within the oracle
-    bound, which the callers check on sampled rows): every element within
-    OUT_ATOL of the other and a relative L2 distance within REL_L2.  The
-    sums l are taken from the unrounded probabilities in fp32, so lse agrees
-    to 1e-5 (+1e-6 relative); empty rows (+0.0, -inf) are the same."""
+    two results carry different rounding errors, each within the oracle
+    bound (which the callers check on rows of the split blocks): they may
+    then lie on opposite sides of the exact value, so every element must be
+    within twice max(OUT_ATOL, one bf16 ULP of the larger magnitude) of the
+    other (the ULP term matters from |o| >= 2, as with the peaky N(0, 3^2)
+    scores of packed clips), and the relative L2 distance within REL_L2.
+    The sums l are taken from the unrounded probabilities in fp32, so lse
+    agrees to 1e-5 (+1e-6 relative); empty rows (+0.0, -inf) are the same."""
     a = o1.float().cpu().numpy().astype(np.float64)
     b = o2.float().cpu().numpy().astype(np.float64)
-    assert np.abs(a - b).max() <= OUT_ATOL, float(np.abs(a - b).max())
+    tol = 2.0 * np.maximum(OUT_ATOL, 2.0 * half_ulp_bf16(np.maximum(np.abs(a), np.abs(b))))
+    assert np.all(np.abs(a - b) <= tol), float(np.abs(a - b).max())
     nb = np.linalg.norm(b)
     if nb > 0:
         assert np.linalg.norm(a - b) / nb <= REL_L2

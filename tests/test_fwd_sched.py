@@ -3,18 +3,21 @@
 classified from per-tile summaries) against the plain one (vdx_attn_fwd: one
 workgroup per query block, index order, tiles classified from the IDs): the
 same bits for every segment layout and size, whatever the workspace holds on
-entry, as long as the launch's last round is full or a single round holds
-every item (then no item is split along its keys; the split last round is
-tested in test_fwd_split.py).  Against the oracle it is checked by the
+entry, wherever no item is split along its keys (always when a single round
+holds every item; the split items of longer launches are tested in
+test_fwd_split.py and, at full size, below).  Against the oracle it is checked by the
 parity sweeps, which call attn_fwd and so take this path for every masked
 case.
 """
 import math
 
+import numpy as np
 import pytest
 import torch
 
 import workloads as W
+from gpu_helpers import (assert_split_close, check_rows, differing_blocks, n_split_items, persistent_grid,
+                         run_oracle, valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,29 +83,52 @@ def test_workspace_contents_do_not_matter(need_gpu):
 def test_full_size_scheduled_equals_plain(need_gpu, name):
     """At the workload's full size (thousands of items, so every workgroup of
     the persistent grid runs many), in the launch configuration the benchmark
-    times.  Packed clips' 3,840 items fill 15 whole rounds of 256, so none is
-    split (joint video+text, whose last round is split, is in
+    times.  Packed clips' 3,840 items: 13 rounds of each XCD's own items and
+    a pool of 512 shared by all XCDs, whose last 64 are split; every other
+    block gives the plain call's bits, the split ones agree within the
+    rounding of their parts and match the oracle (joint video+text is in
     test_fwd_split.py)."""
     w = W.WORKLOADS[name]
     x = W.make_inputs(w)
     print(f"case sched full size {name}", flush=True)
-    assert_same_bits(*run_both(x, x["seg_q"], x["seg_kv"], w.scale))
+    (o1, l1), (o2, l2) = run_both(x, x["seg_q"], x["seg_kv"], w.scale)
+    n_split = n_split_items(w.B * w.H * ((w.S + 255) // 256), persistent_grid())
+    diff = differing_blocks(o1, l1, o2, l2)
+    assert len(diff) <= n_split, (len(diff), n_split)
+    assert_split_close(o1, l1, o2, l2)
+    # rows of the split blocks (first, last and two random ones) against the oracle
+    g = np.random.default_rng(17)
+    rows = []
+    for b, h, blk in diff:
+        lo, hi = blk * 256, min(w.S, (blk + 1) * 256)
+        rows += [(b, h, i) for i in sorted({lo, hi - 1} | set(int(i) for i in g.integers(lo, hi, size=2)))]
+    if rows:
+        rows = np.array(rows, dtype=np.int64)
+        oo, lo_, sens = run_oracle(x, x["seg_q"], x["seg_kv"], w.scale, rows=rows)
+        has = valid_rows(x["seg_q"], x["seg_kv"], w.B, w.S)
+        print(check_rows(o1.cpu(), l1.cpu(), rows, oo, lo_, has, sens), flush=True)
 
 
 def test_all_ones_at_480p_size_equals_unmasked(need_gpu):
-    """All IDs 1 at the 480p layer's size: every tile is full, every block has
-    the same count, and the result is the unmasked call's, bit for bit."""
+    """All IDs 1 at the 480p layer's size (1,536 items: 4 rounds of each
+    XCD's own items and a pool of 512, the last 64 split): every tile is
+    full, every block has the same count; the one-workgroup-per-block call
+    gives the unmasked call's bits, and the scheduled one too except on the
+    split items' blocks, which agree within the rounding of their parts."""
     import spatiotemporal_attention_amd as vdx
     w = W.WORKLOADS["dit480p_small"]
     x = W.make_inputs(w)
     ones = torch.ones((w.B, w.S), dtype=torch.int32)
     print("case sched all-ones 480p", flush=True)
     (o1, l1), (o2, l2) = run_both(x, ones, ones.clone(), w.scale)
-    assert_same_bits((o1, l1), (o2, l2))
     d = {n: x[n].cuda() for n in ("q", "k", "v")}
     o3, l3 = vdx.attn_fwd(d["q"], d["k"], d["v"], scale=w.scale)
     torch.cuda.synchronize()
-    assert_same_bits((o1, l1), (o3, l3))
+    assert_same_bits((o2, l2), (o3, l3))
+    n_split = n_split_items(w.B * w.H * ((w.S + 255) // 256), persistent_grid())
+    diff = differing_blocks(o1, l1, o3, l3)
+    assert len(diff) <= n_split, (len(diff), n_split)
+    assert_split_close(o1, l1, o3, l3)
 
 
 def test_graph_replays_reset_the_work_counters(need_gpu):

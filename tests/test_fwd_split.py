@@ -1,9 +1,10 @@
-"""Split items of vdx_attn_fwd_ws.  With segment IDs, when the scheduled
-persistent launch's items do not fill its last round, the items of that round
-are divided along their active key tiles into parts that run side by side;
-without them, the last items of the shared pool that ends every launch with
-more items than workgroups are divided the same way.  A combine kernel merges
-the parts' (O, m, l).
+"""Split items of vdx_attn_fwd_ws.  In a persistent launch with more items
+than workgroups, some items are divided along their active key tiles into
+parts that run side by side: without segment IDs each XCD's last items (a
+quarter round's worth in a long launch, its ragged last round in a short
+one), the XCDs stealing units from each other; with them the last items of
+a pool of items shared by all XCDs.  A combine kernel merges the parts'
+(O, m, l).
 
 Against vdx_attn_fwd (which never splits): every query block that is not
 split gives the same bits; the split ones round their probabilities against
@@ -57,7 +58,7 @@ def _check_against_oracle(x, seg_q, seg_kv, scale, o, l, blocks, per_block, seed
 
 @pytest.mark.parametrize("B,S,H,D", [(1, 8192, 9, 128), (1, 8192, 9, 64), (2, 4000, 10, 128), (1, 75600, 40, 128)])
 def test_unmasked_split_blocks(need_gpu, B, S, H, D):
-    """Unmasked: only the blocks the pool splits differ from vdx_attn_fwd,
+    """Unmasked: only the blocks the schedule splits differ from vdx_attn_fwd,
     within rounding; their rows match the oracle."""
     grid = persistent_grid()
     blocks = split_unmasked_blocks(B, S, H, grid)
@@ -85,8 +86,8 @@ def test_unmasked_split_blocks(need_gpu, B, S, H, D):
 @pytest.mark.parametrize("kind", ["singletons", "packed", "padded", "allpad", "negative"])
 def test_masked_split_blocks(need_gpu, kind):
     """Masked (the scheduled persistent kernel): 288 items on a 256-workgroup
-    grid leave 4 items per XCD for its last round, split 8 ways; with one-
-    token segments a block has about 4 active tiles, so most parts get none.
+    grid leave a pool of 32 items, split 8 ways; with one-token segments a
+    block has about 4 active tiles, so most parts get none.
     At most the split items' blocks differ from vdx_attn_fwd; their rows
     match the oracle and padding rows stay +0.0 / -inf."""
     B, S, H, D = 1, 8192, 9, 128
@@ -94,7 +95,7 @@ def test_masked_split_blocks(need_gpu, kind):
     n_items = B * H * ((S + 255) // 256)
     n_split = n_split_items(n_items, grid)
     if n_split == 0:
-        pytest.skip(f"{n_items} items on a {grid}-workgroup grid leave no ragged round")
+        pytest.skip(f"{n_items} items on a {grid}-workgroup grid split none")
     x = W.make_random(B, S, H, D, seed=7000 + len(kind))
     seg = W.random_segments(B, S, 7100 + len(kind), kind)
     print(f"case split masked kind={kind} items={n_items} split={n_split}", flush=True)
@@ -112,10 +113,10 @@ def test_masked_split_blocks(need_gpu, kind):
 
 
 def test_joint_video_text_split_tail(need_gpu):
-    """The padded joint video+text workload at full size (3,360 items: 13
-    rounds of 256 and 32 items left, split 8 ways): at most 32 blocks differ
-    from vdx_attn_fwd, within rounding, and their rows (text, video and pad
-    rows among them) match the oracle."""
+    """The padded joint video+text workload at full size (3,360 items: 11
+    rounds of 256 and 32 items left; 11 rounds of each XCD's own items, a
+    pool of 544 and its last 64 split 4 ways): at most 64 blocks differ from vdx_attn_fwd, within rounding, and
+    their rows (text, video and pad rows among them) match the oracle."""
     w = W.WORKLOADS["joint_video_text_pad"]
     x = W.make_inputs(w)
     n_items = w.B * w.H * ((w.S + 255) // 256)
@@ -171,7 +172,8 @@ def _rope_run(x, r, seg, scale, split):
 @pytest.mark.parametrize("D,kind", [(128, None), (64, None), (128, "packed"), (64, "padded")])
 def test_rope_split_blocks(need_gpu, D, kind):
     """vdx_rope3d_attn_fwd_ws with split items (288 items on a 256-workgroup
-    grid: a ragged last round when masked, the pool's last items when not)
+    grid: 4 items per XCD split 8 ways unmasked, a pool of 32 items split 8
+    ways masked)
     against vdx_rope3d_attn_fwd: at most the split blocks differ, within
     rounding, and their rows match the oracle (rotation, then attention)."""
     import oracle
@@ -216,7 +218,7 @@ def test_split_graph_replays(need_gpu):
     import spatiotemporal_attention_amd as vdx
     B, S, H, D = 1, 8192, 9, 128
     if n_split_items(B * H * ((S + 255) // 256), persistent_grid()) == 0:
-        pytest.skip("no ragged round on this grid")
+        pytest.skip("no split items on this grid")
     x = W.make_random(B, S, H, D, seed=9100)
     seg = W.random_segments(B, S, 9101, "packed").cuda()
     d = {n: x[n].cuda() for n in ("q", "k", "v")}
@@ -251,7 +253,7 @@ def test_split_graph_replays(need_gpu):
 
 def test_rope_split_at_720p_equals_composed_split(need_gpu):
     """At the 720p layer's size, in the launch configuration the benchmark
-    times with --rope: vdx_rope3d_attn_fwd_ws (the pool and its split items) equals
+    times with --rope: vdx_rope3d_attn_fwd_ws (work stealing and split items) equals
     vdx_attn_fwd_ws on separately rotated q and k, bit for bit (the same split
     schedule on the same rotated bits)."""
     import spatiotemporal_attention_amd as vdx
@@ -273,9 +275,8 @@ def test_rope_split_at_720p_equals_composed_split(need_gpu):
 
 
 def _random_split_cases(n=10, seed=2024):
-    """Seeded shapes whose item count leaves a ragged last round on a
-    256-workgroup grid (so that the masked call splits; the unmasked one,
-    with more items than workgroups, always does), with random segment kinds."""
+    """Seeded shapes whose item count makes the masked call split items on a
+    256-workgroup grid, with random segment kinds."""
     g = np.random.default_rng(seed)
     kinds = [None, "single", "padded", "packed", "interleaved", "singletons", "negative", "extreme"]
     cases = []

@@ -198,10 +198,10 @@ def test_checker_flags_a_planted_hazard():
 def test_no_kernel_spills_to_scratch(asm_text):
     sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm_text)]
     # D in {64, 128} x {unmasked, segment-masked} x {plain, 3D-rotary-embedded queries},
-    # the unmasked ones again with the shared pool, the scheduled masked
+    # the unmasked ones again with work stealing and split items, the scheduled masked
     # kernel for the same D and query variants with and without a split last
     # round, its three set-up kernels (tile summaries, block counts, block
-    # order), the pool counter reset, and the combine kernel of split items
+    # order), the work counters' reset, and the combine kernel of split items
     # for each D and item order
     assert len(sizes) == 28
     assert sizes == [0] * 28

@@ -179,9 +179,10 @@ def test_constant_value_every_row(need_gpu, name):
 
 # Bit canaries at the 480p layer's size (B=1, S=32,760, H=12): 1,536 query
 # blocks, so the unmasked call's persistent grid of 256 workgroups runs six
-# items per workgroup (reusing its LDS and registers after each), while a
-# masked call runs one workgroup per item and a one-head call 128 items on
-# 128 workgroups.  Every route must give the same bits.
+# items per workgroup (reusing its LDS and registers after each), while the
+# masked call through vdx_attn_fwd runs one workgroup per item and a one-head
+# call 128 items on 128 workgroups.  Every route must give the same bits (the
+# scheduled masked route splits some items; test_fwd_sched.py covers it).
 def test_full_size_bit_canaries(need_gpu):
     import spatiotemporal_attention_amd as vdx
     w = W.WORKLOADS["dit480p_small"]
@@ -195,7 +196,7 @@ def test_full_size_bit_canaries(need_gpu):
     assert torch.equal(a_lse.view(torch.int32), b_lse.view(torch.int32)), "repeat run"
     del b_out, b_lse
     ones = torch.ones(w.B, w.S, dtype=torch.int32, device="cuda")
-    c_out, c_lse = vdx.attn_fwd(d["q"], d["k"], d["v"], ones, ones.clone(), scale=w.scale)
+    c_out, c_lse = vdx.attn_fwd(d["q"], d["k"], d["v"], ones, ones.clone(), scale=w.scale, scheduled=False)
     torch.cuda.synchronize()
     assert torch.equal(a_out.view(torch.int16), c_out.view(torch.int16)), "NULL vs all-ones IDs"
     assert torch.equal(a_lse.view(torch.int32), c_lse.view(torch.int32)), "NULL vs all-ones IDs"
