@@ -686,7 +686,7 @@ def main():
         line["roofline"]["rope_key_prepass_ms"] = round(prepass_ms, 4)
     elif not args.plain:
         line["roofline"]["scope"] = ("vdx_attn_fwd_ws call (" + ("tile summaries, block counts and order, "
-                                     if w.masked else "the pool counter reset, ") + "the forward, the merge of "
+                                     if w.masked else "the work counters' reset, ") + "the forward, the merge of "
                                      "split items)")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
