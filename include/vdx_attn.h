@@ -134,17 +134,21 @@ int vdx_attn_fwd(const void* q, const void* k, const void* v,
  * them up to rounding (each part rounds its probabilities to bf16 against
  * its own running maximum), within the same accuracy bound.  Which items
  * are split: none when there are no more items n than G.  Otherwise XCD x
- * holds per + (x < rem) items (per = n / 8, rem = n mod 8) -- without
- * segment IDs a contiguous run starting at item x per + min(x, rem), items
- * numbered (b H + h) ceil(S / 256) + block; with them the XCD's
- * longest-first list -- and runs K rounds' worth of them (K = per / W - 2
- * when per / W >= L, else per / W; L = 16 without segment IDs, 4 with
- * them); the rest of every XCD's items forms a pool of n - K G items (XCD
- * x's after those of XCDs below x) that every workgroup pulls from once its
- * own items are done, and the pool's last R items (G / 4 when
- * per / W >= L, else all of them) are split into P = min(8, 256 / R, G / R)
- * parts when that is >= 2.
- * The XCDs run at different speeds under this load, and the pool lets the
+ * holds n_x = per + (x < rem) items (per = n / 8, rem = n mod 8).
+ *   - Without segment IDs XCD x's items are a contiguous run starting at
+ *     item x per + min(x, rem) (items numbered (b H + h) ceil(S / 256) +
+ *     block); its last R are split into P = min(8, W / R) parts when that is
+ *     >= 2, R = W / 4 when n_x / W >= 4, else R = n_x mod W.  The XCD's
+ *     workgroups claim its units from its own counter, then from the other
+ *     XCDs'.
+ *   - With segment IDs XCD x's items are its longest-first list; its counter
+ *     hands out its first K W (K = per / W - 2 when per / W >= 4, else
+ *     per / W), the rest of every XCD's list forms a pool of n - K G items
+ *     (XCD x's after those of XCDs below x) that every workgroup pulls from
+ *     once its own items are done, and the pool's last R items (G / 4 when
+ *     per / W >= 4, else all of them) are split into P = min(8, 256 / R,
+ *     G / R) parts when that is >= 2.
+ * The XCDs run at different speeds under this load; both schedules let the
  * faster ones take over the slower ones' last items.
  *
  *   q ... scale, stream   exactly as for vdx_attn_fwd.

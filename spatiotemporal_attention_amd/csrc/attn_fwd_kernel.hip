@@ -593,14 +593,16 @@ static_assert(tail_record_floats<128>() % 64 == 0 && tail_record_floats<64>() % 
 //     P = min(8, W / R) parts along their key tiles (when that makes at least
 //     2), after its n_x - R whole ones: R = W / 4 for a long launch
 //     (n_x / W >= kLongRounds), else R = n_x mod W, the ragged last round,
-//     which the parts then fill.  Unit u of XCD x: u < n_x - R is whole item
+//     which the parts then fill (without parts to take, stealing measured
+//     0.5% slower than none on a launch of 6 whole rounds; with them 0.6%
+//     faster).  Unit u of XCD x: u < n_x - R is whole item
 //     u; otherwise t = u - (n_x - R) is part t / R of item n_x - R + t % R,
 //     with its partial results in record x W + t.  The shared pool below,
 //     tried here too, balanced as well but cost 50 GB more L2 misses per
 //     720p call, its workgroups leaving their XCD's head for two rounds;
 //   - masked (pool_plan, pool_sched_item): a shared pool.  XCD x's counter
 //     hands out its first K W list positions (K = n_x / W - kPoolRounds for a
-//     long launch, n_x / W >= kLongRoundsSched, else n_x / W); the rest of
+//     long launch, n_x / W >= kLongRounds, else n_x / W); the rest of
 //     every XCD's list forms a pool of n - K G items, XCD-major, pulled
 //     through a ninth counter by any workgroup whose own XCD is done, and the
 //     pool's last R items (G / 4 for a long launch, else all of them) are
@@ -608,8 +610,7 @@ static_assert(tail_record_floats<128>() % 64 == 0 && tail_record_floats<64>() % 
 //     part t in record t.  Work stealing measured no faster than no balancing
 //     here (the slower XCDs' remaining items were mostly already running when
 //     the thieves came), the pool 2.4-2.9% faster.
-constexpr int kLongRounds = 16;      // unmasked
-constexpr int kLongRoundsSched = 4;  // masked scheduled kernel
+constexpr int kLongRounds = 4;
 constexpr int kPoolRounds = 2;
 struct TailPlan {
     int n_x;    // items of the XCD
@@ -639,7 +640,7 @@ __host__ __device__ inline PoolPlan pool_plan(int n_items, int G) {
     const int W = G / kXcds;
     PoolPlan p{n_items / kXcds, n_items % kXcds, 0, 0, 0, 1};
     const int rounds = p.per / W;
-    const bool long_launch = rounds >= kLongRoundsSched;
+    const bool long_launch = rounds >= kLongRounds;
     p.K = long_launch ? rounds - kPoolRounds : rounds;
     p.n_pool = n_items - p.K * G;
     const int R = long_launch ? min(p.n_pool, G / 4) : p.n_pool % G;
@@ -1331,7 +1332,7 @@ hipError_t launch_t(const AttnArgs& a, const Rope3DDev& rope, hipStream_t stream
     // Work stealing and split items need the persistent grid (a multiple of
     // 8) with more than one round, at most one record per workgroup, and a
     // long launch or a ragged last round (a short launch of whole rounds runs
-    // the plain kernel: stealing measured 0.5% slower there).
+    // the plain kernel).
     const bool steal = !SEG && ws != nullptr && n_wg64 > pg && pg <= kTailRecords &&
                        tail_max_r(n_wg, grid, kLongRounds) > 0;
     const auto args = std::make_tuple(reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const __bf16*>(a.k),

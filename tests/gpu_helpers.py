@@ -188,7 +188,7 @@ def check_rows(out_g, lse_g, rows, out_o, lse_o, has, sens):
 # Unmasked (work stealing): XCD x's items are a contiguous run starting at
 # item x per + min(x, rem) (item = (b H + h) n_qblk + block), and when
 # n_x > W its last R are split into P = min(8, W // R) >= 2 parts, R = W // 4
-# when n_x // W >= 16, else R = n_x % W.  Masked (shared pool): each XCD runs
+# when n_x // W >= 4, else R = n_x % W.  Masked (shared pool): each XCD runs
 # K rounds of its own items (K = per // W - 2 when per // W >= 4, else
 # per // W); the rest forms a pool of n - K G items whose last R (G // 4 for
 # the long launches, else all of them) are split into
@@ -201,7 +201,7 @@ def tail_plan(x, n_items, W):
     """(n_x, R, P) of XCD x, unmasked."""
     n_x = n_items // 8 + (1 if x < n_items % 8 else 0)
     if n_x > W:
-        R = W // 4 if n_x // W >= 16 else n_x % W
+        R = W // 4 if n_x // W >= 4 else n_x % W
         P = min(8, W // R) if R else 1
         if P >= 2:
             return n_x, R, P

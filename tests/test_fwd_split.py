@@ -56,7 +56,8 @@ def _check_against_oracle(x, seg_q, seg_kv, scale, o, l, blocks, per_block, seed
     return check_rows(o.cpu(), l.cpu(), rows, oo, lo, has, sens)
 
 
-@pytest.mark.parametrize("B,S,H,D", [(1, 8192, 9, 128), (1, 8192, 9, 64), (2, 4000, 10, 128), (1, 75600, 40, 128)])
+@pytest.mark.parametrize("B,S,H,D", [(1, 8192, 9, 128), (1, 8192, 9, 64), (2, 4000, 10, 128), (1, 32760, 12, 128),
+                                     (1, 75600, 40, 128)])
 def test_unmasked_split_blocks(need_gpu, B, S, H, D):
     """Unmasked: only the blocks the schedule splits differ from vdx_attn_fwd,
     within rounding; their rows match the oracle."""
@@ -64,8 +65,8 @@ def test_unmasked_split_blocks(need_gpu, B, S, H, D):
     blocks = split_unmasked_blocks(B, S, H, grid)
     if not blocks:
         pytest.skip(f"{B * H * ((S + 255) // 256)} items on a {grid}-workgroup grid split none")
-    if S == 75600:
-        w = W.WORKLOADS["dit720p_large"]
+    if S in (75600, 32760):
+        w = W.WORKLOADS["dit720p_large" if S == 75600 else "dit480p_small"]
         x, scale = W.make_inputs(w), w.scale
     else:
         x, scale = W.make_random(B, S, H, D, seed=S + H + D), 1.0 / math.sqrt(D)
